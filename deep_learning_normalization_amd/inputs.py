@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the norm workloads.
+
+This module only draws random numbers and casts them; it holds none of the normalisation
+arithmetic. The device path and the CPU oracle both receive exactly the tensors made here
+(sampled in fp32 on the CPU, then cast to the storage dtype with round-to-nearest-even).
+
+Every tensor has its own generator, seeded with ``seed + offset``:
+X 0, W 1, B 2, dY 3, R 4, outlier-channel permutation 5, dH 6.
+
+The pages print no data set for these kernels; the shapes follow the workloads they discuss
+(LLM hidden sizes, and the very-large-row regression class named on the page "PyTorch atinge
+desempenho SOTA em normalização com torch.compile", para. 6). Distributions N(a, b) use b as
+the standard deviation.
+"""
+from dataclasses import dataclass, field, replace
+from typing import Optional, Tuple
+
+import numpy as np
+import torch
+
+OFF_X, OFF_W, OFF_B, OFF_DY, OFF_R, OFF_PERM, OFF_DH = 0, 1, 2, 3, 4, 5, 6
+
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+@dataclass(frozen=True)
+class Dist:
+    """A value distribution: ("normal", mean, std), ("uniform", lo, hi) or ("const", v)."""
+    kind: str
+    a: float = 0.0
+    b: float = 1.0
+
+
+def normal(mean, std):
+    return Dist("normal", mean, std)
+
+
+def uniform(lo, hi):
+    return Dist("uniform", lo, hi)
+
+
+def const(v):
+    return Dist("const", v)
+
+
+@dataclass(frozen=True)
+class Workload:
+    """One synthetic problem: kind ("layernorm"/"rmsnorm"), dtype ("f32"/"bf16"), shape,
+    eps, distributions, and which passes and options it exercises."""
+    name: str
+    kind: str
+    dtype: str
+    M: int
+    N: int
+    eps: float
+    x: Dist = normal(0.0, 1.0)
+    w: Dist = normal(1.0, 0.1)
+    b: Optional[Dist] = None          # LayerNorm bias; None means no bias tensor
+    dy: Optional[Dist] = normal(0.0, 1.0)  # None: forward only
+    r: Optional[Dist] = None          # residual input R (residual variant)
+    dh: Optional[Dist] = None         # incoming gradient of the residual output
+    outlier_frac: float = 0.0         # fraction of columns scaled by outlier_scale
+    outlier_scale: float = 20.0
+    seed: int = 0
+    tags: Tuple[str, ...] = field(default_factory=tuple)
+
+    def with_shape(self, M, N, name=None):
+        return replace(self, M=M, N=N, name=name or "%s[%dx%d]" % (self.name, M, N))
+
+
+def _draw(dist: Dist, shape, seed: int) -> torch.Tensor:
+    g = torch.Generator().manual_seed(int(seed))
+    n = int(np.prod(shape)) if len(shape) else 1
+    if dist.kind == "normal":
+        t = torch.randn(n, generator=g, dtype=torch.float32)
+        if dist.b != 1.0:
+            t.mul_(dist.b)
+        if dist.a != 0.0:
+            t.add_(dist.a)
+    elif dist.kind == "uniform":
+        t = torch.empty(n, dtype=torch.float32).uniform_(dist.a, dist.b, generator=g)
+    elif dist.kind == "const":
+        t = torch.full((n,), float(dist.a), dtype=torch.float32)
+    else:
+        raise ValueError("unknown distribution %r" % (dist.kind,))
+    return t.view(*shape)
+
+
+def outlier_columns(N: int, frac: float, seed: int) -> torch.Tensor:
+    """round(frac * N) distinct column indices from a seeded permutation (outlier channels)."""
+    k = int(round(frac * N))
+    g = torch.Generator().manual_seed(int(seed) + OFF_PERM)
+    return torch.randperm(N, generator=g)[:k]
+
+
+def make(w: Workload, M: Optional[int] = None) -> dict:
+    """CPU tensors for a workload, in its storage dtype.
+
+    Keys: X, W, B (None if absent), dY (None if forward-only), R (None unless residual),
+    dH (None unless given). ``M`` overrides the row count (rows are drawn from the same
+    streams, so the first rows match the full-size tensors only when M equals w.M).
+    """
+    M = w.M if M is None else M
+    N = w.N
+    dt = TORCH_DTYPES[w.dtype]
+    s = w.seed
+    X = _draw(w.x, (M, N), s + OFF_X)
+    if w.outlier_frac > 0.0:
+        cols = outlier_columns(N, w.outlier_frac, s)
+        X[:, cols] *= w.outlier_scale
+    out = {
+        "X": X.to(dt),
+        "W": _draw(w.w, (N,), s + OFF_W).to(dt),
+        "B": _draw(w.b, (N,), s + OFF_B).to(dt) if w.b is not None else None,
+        "dY": _draw(w.dy, (M, N), s + OFF_DY).to(dt) if w.dy is not None else None,
+        "R": _draw(w.r, (M, N), s + OFF_R).to(dt) if w.r is not None else None,
+        "dH": _draw(w.dh, (M, N), s + OFF_DH).to(dt) if w.dh is not None else None,
+    }
+    return out
+
+
+def host_bits(t: Optional[torch.Tensor]):
+    """The raw storage bits of a CPU tensor as numpy: uint16 for bf16, float32 for fp32."""
+    if t is None:
+        return None
+    t = t.detach().contiguous().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    if t.dtype == torch.float32:
+        return t.numpy()
+    raise TypeError("unsupported dtype %s" % t.dtype)
+
+
+# ---- the workloads -----------------------------------------------------------------------
+
+# RMSNorm forward, fp32, 2048 x 1024: one row per wavefront.
+RMS_F32_2048x1024 = Workload("rmsnorm_f32_2048x1024_fwd", "rmsnorm", "f32", 2048, 1024, 1e-6,
+                             x=normal(0, 1), w=normal(1, 0.1), dy=None)
+
+# LayerNorm forward + backward, bf16 storage, fp32 accumulation, 16384 x 4096.
+LN_BF16_16384x4096 = Workload("layernorm_bf16_16384x4096", "layernorm", "bf16", 16384, 4096,
+                              1e-5, x=normal(0, 1), w=normal(1, 0.1), b=normal(0, 0.1),
+                              dy=normal(0, 1))
+
+
+# RMSNorm forward + backward, bf16, LLM hidden sizes at 32768 tokens, with 1% of the
+# columns (channels) scaled by 20.
+def rms_hidden(N: int, M: int = 32768) -> Workload:
+    return Workload("rmsnorm_bf16_%dx%d_outliers" % (M, N), "rmsnorm", "bf16", M, N, 1e-6,
+                    x=normal(0, 1), w=normal(1, 0.05), dy=normal(0, 1e-2), outlier_frac=0.01)
+
+
+RMS_HIDDEN_SIZES = (2048, 4096, 5120, 8192)
+
+# Fused residual add + RMSNorm forward + backward, bf16, 65536 x 7168.
+RESID_RMS_BF16_65536x7168 = Workload("resid_rmsnorm_bf16_65536x7168", "rmsnorm", "bf16", 65536,
+                                     7168, 1e-6, x=normal(0, 0.5), r=normal(0, 1),
+                                     w=normal(1, 0.1), dy=normal(0, 1))
+
+
+# Very long rows (split-row class): LayerNorm and RMSNorm forward + backward, bf16.
+def long_rows(kind: str, M: int, N: int) -> Workload:
+    eps = 1e-5 if kind == "layernorm" else 1e-6
+    return Workload("%s_bf16_%dx%d_longrow" % (kind, M, N), kind, "bf16", M, N, eps,
+                    x=uniform(-3, 3), w=normal(1, 0.1),
+                    b=const(0.0) if kind == "layernorm" else None, dy=normal(0, 1))
+
+
+LONG_ROW_SHAPES = ((256, 262144), (4, 4194304))
+
+
+def all_workloads():
+    """Every full-size workload, in a fixed order."""
+    out = [RMS_F32_2048x1024, LN_BF16_16384x4096]
+    out += [rms_hidden(N) for N in RMS_HIDDEN_SIZES]
+    out.append(RESID_RMS_BF16_65536x7168)
+    for M, N in LONG_ROW_SHAPES:
+        out += [long_rows("layernorm", M, N), long_rows("rmsnorm", M, N)]
+    return out

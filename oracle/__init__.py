@@ -1,0 +1,7 @@
+"""Double-precision CPU oracle for row-wise LayerNorm / RMSNorm (test infrastructure only).
+
+Only the test suite, the smoke check and the benchmark's CPU-baseline leg may import this
+package. The HIP library never does.
+"""
+from .oracle import (BF16, F32, LAYERNORM, RMSNORM, Oracle, bwd, decode, default,  # noqa: F401
+                     fwd, num_threads, round_bf16, set_num_threads)

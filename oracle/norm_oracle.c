@@ -1,0 +1,361 @@
+/*
+ * norm_oracle.c -- plain double-precision CPU oracle for row-wise LayerNorm and RMSNorm,
+ * forward and backward, with an optional residual add in front of the norm.
+ *
+ * TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's CPU-baseline
+ * leg may load or call this file. It shares no code, header, table or helper with the HIP
+ * library; the two are compared element by element on identical input bits.
+ *
+ * What is computed is the textbook definition of each operation, evaluated in double
+ * precision on the exact input values (bf16 or fp32 bit patterns widened exactly):
+ *
+ *   Sources (web pages):
+ *   [P1] "PyTorch atinge desempenho SOTA em normalização com torch.compile"
+ *        (matsubara.tec.br):
+ *        para. 2  -- LayerNorm normalises with the mean and the variance taken along one
+ *                    dimension, then scales by the trainable gamma (weight) and shifts by
+ *                    beta (bias); RMSNorm uses the root mean square instead and has no beta.
+ *        para. 3  -- the forward pass is a reduction along the contiguous dimension plus
+ *                    pointwise work.
+ *        para. 7  -- the backward pass produces dX, dW and, for LayerNorm, dB.
+ *        paras. 8-10 -- fusing, splitting and re-ordering these reductions changes only the
+ *                    order of the same sums, not their value; so the oracle is the plain,
+ *                    unsplit definition.
+ *
+ *   Readings taken where the pages say nothing (each is also listed in the design notes):
+ *     - variance is the biased estimator (divide by N);
+ *     - eps is added inside the square root, for both kinds;
+ *     - RMSNorm subtracts no mean and has no bias;
+ *     - the backward takes X and recomputes its own mean and rstd (it never uses a saved
+ *       statistic from the device);
+ *     - residual variant: h = R + X is rounded once to the input dtype (RNE) and the norm is
+ *       applied to that rounded h, because the backward re-reads the stored h; the residual
+ *       gradient equals the input gradient, plus an optional incoming gradient of h.
+ *
+ * Parallelism: rows (forward, dX) and column blocks (dW, dB) are split over OpenMP threads.
+ * Every output value is computed by exactly one thread in the definition's own order (rows
+ * ascending for the column sums), so results do not depend on the thread count.
+ *
+ * Build: gcc -O2 -ffp-contract=off -fopenmp -fPIC -shared (no fast-math).
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+enum { OR_LAYERNORM = 0, OR_RMSNORM = 1 };
+enum { OR_F32 = 0, OR_BF16 = 1 };
+
+enum {
+  OR_OK = 0,
+  OR_BAD_ARG = 1,
+  OR_NO_MEMORY = 2,
+};
+
+/* ---- number formats ---------------------------------------------------------------- */
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double or_bf16_bits_to_double(uint16_t b) {
+  uint32_t u = ((uint32_t)b) << 16;
+  float f;
+  memcpy(&f, &u, sizeof f);
+  return (double)f;
+}
+
+static double or_load(int dtype, const void *base, int64_t idx) {
+  if (dtype == OR_F32) {
+    float f;
+    memcpy(&f, (const char *)base + idx * 4, sizeof f);
+    return (double)f;
+  }
+  uint16_t b;
+  memcpy(&b, (const char *)base + idx * 2, sizeof b);
+  return or_bf16_bits_to_double(b);
+}
+
+/* Round a double to the nearest bf16 value, ties to even, in one step from the double
+ * (no detour through binary32). bf16 keeps 8 significant bits and binary32's exponent range;
+ * the smallest subnormal step is 2^-133 and the largest finite value is (2 - 2^-7) * 2^127. */
+static double or_round_to_bf16(double v) {
+  if (v != v || v == 0.0 || isinf(v)) return v;
+  double a = fabs(v);
+  int e;
+  (void)frexp(a, &e);      /* a = m * 2^e with m in [0.5, 1) */
+  int q = e - 8;           /* weight of the last kept bit */
+  if (q < -133) q = -133;  /* subnormal range: fixed step */
+  double r = nearbyint(ldexp(a, -q)); /* default rounding mode: to nearest, ties to even */
+  double out = ldexp(r, q);
+  if (out > 3.3895313892515355e38) out = INFINITY;
+  return v < 0 ? -out : out;
+}
+
+static double or_round_to_dtype(int dtype, double v) {
+  if (dtype == OR_F32) return (double)(float)v; /* C conversion: round to nearest even */
+  return or_round_to_bf16(v);
+}
+
+/* bit pattern of the bf16 nearest to v (used by tests to pin the rounding rule) */
+static uint16_t or_bf16_bits(double v) {
+  float f = (float)or_round_to_bf16(v); /* exact: the value is a bf16, hence a binary32 */
+  uint32_t u;
+  memcpy(&u, &f, sizeof u);
+  if (v != v) return (uint16_t)0x7FC0;
+  return (uint16_t)(u >> 16);
+}
+
+/* ---- argument checks ----------------------------------------------------------------- */
+
+static int or_check(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64_t r1,
+                    double eps) {
+  if (kind != OR_LAYERNORM && kind != OR_RMSNORM) return OR_BAD_ARG;
+  if (dtype != OR_F32 && dtype != OR_BF16) return OR_BAD_ARG;
+  if (M < 0 || N <= 0) return OR_BAD_ARG;
+  if (r0 < 0 || r1 < r0 || r1 > M) return OR_BAD_ARG;
+  if (!(eps >= 0.0)) return OR_BAD_ARG;
+  return OR_OK;
+}
+
+/* ---- per-row pieces -------------------------------------------------------------------- */
+
+/* Row i of the norm's input, in double: X, or round(R + X) for the residual variant. */
+static void or_input_row(int dtype, int64_t N, int64_t i, const void *X, const void *R,
+                         double *x) {
+  for (int64_t j = 0; j < N; ++j) {
+    double v = or_load(dtype, X, i * N + j);
+    if (R) v = or_round_to_dtype(dtype, or_load(dtype, R, i * N + j) + v);
+    x[j] = v;
+  }
+}
+
+/* Statistics of one row [P1 para. 2]. LayerNorm: mean, then the biased variance as the mean
+ * of squared deviations from that mean (two passes). RMSNorm: mean of squares, mean = 0.
+ * rstd = 1 / sqrt(statistic + eps). */
+static void or_row_stats(int kind, int64_t N, const double *x, double eps, double *mean,
+                         double *rstd) {
+  if (kind == OR_LAYERNORM) {
+    double s = 0.0;
+    for (int64_t j = 0; j < N; ++j) s += x[j];
+    double mu = s / (double)N;
+    double q = 0.0;
+    for (int64_t j = 0; j < N; ++j) q += (x[j] - mu) * (x[j] - mu);
+    double var = q / (double)N;
+    *mean = mu;
+    *rstd = 1.0 / sqrt(var + eps);
+  } else {
+    double q = 0.0;
+    for (int64_t j = 0; j < N; ++j) q += x[j] * x[j];
+    double ms = q / (double)N;
+    *mean = 0.0;
+    *rstd = 1.0 / sqrt(ms + eps);
+  }
+}
+
+/* ---- forward ------------------------------------------------------------------------- */
+
+/*
+ * Forward over rows [r0, r1) of an M x N row-major input.
+ *   X     : input bits (dtype), M*N
+ *   R     : residual bits (dtype), M*N, or NULL
+ *   W     : weight bits (dtype), N
+ *   B     : bias bits (dtype), N, or NULL (LayerNorm only; NULL means zero bias)
+ *   Y     : out, (r1-r0)*N doubles, unrounded
+ *   H     : out, (r1-r0)*N doubles holding round(R + X), or NULL (only with R)
+ *   mean  : out, (r1-r0) doubles, or NULL (0 for RMSNorm)
+ *   rstd  : out, (r1-r0) doubles, or NULL
+ * Returns 0, or nonzero on a bad argument / allocation failure.
+ */
+int oracle_fwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64_t r1,
+                    const void *X, const void *R, const void *W, const void *B, double eps,
+                    double *Y, double *H, double *mean, double *rstd) {
+  int st = or_check(kind, dtype, M, N, r0, r1, eps);
+  if (st) return st;
+  if (!X || !W || !Y) return OR_BAD_ARG;
+  if (kind == OR_RMSNORM && B) return OR_BAD_ARG;
+  if (H && !R) return OR_BAD_ARG;
+  int fail = 0;
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)N * sizeof(double));
+    if (!x) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t i = r0; i < r1; ++i) {
+      if (!x) continue;
+      int64_t o = i - r0;
+      or_input_row(dtype, N, i, X, R, x);
+      if (H)
+        for (int64_t j = 0; j < N; ++j) H[o * N + j] = x[j];
+      double mu, rs;
+      or_row_stats(kind, N, x, eps, &mu, &rs);
+      for (int64_t j = 0; j < N; ++j) {
+        double w = or_load(dtype, W, j);
+        double b = B ? or_load(dtype, B, j) : 0.0;
+        double xhat = (kind == OR_LAYERNORM) ? (x[j] - mu) * rs : x[j] * rs;
+        Y[o * N + j] = (kind == OR_LAYERNORM) ? xhat * w + b : xhat * w;
+      }
+      if (mean) mean[o] = mu;
+      if (rstd) rstd[o] = rs;
+    }
+    free(x);
+  }
+  return fail ? OR_NO_MEMORY : OR_OK;
+}
+
+/* ---- backward ------------------------------------------------------------------------ */
+
+/*
+ * Backward over rows [r0, r1) [P1 para. 7].
+ *   X   : the norm's input bits (for the residual variant: the stored h), M*N
+ *   dY  : gradient of the norm output, M*N
+ *   dH  : optional incoming gradient of the residual output h, M*N, added to dX; or NULL
+ *   W   : weight bits, N
+ *   dX  : out, (r1-r0)*N doubles, or NULL (the residual gradient dR is the same array)
+ *   dW  : out, N doubles: sum over rows r0..r1-1 of dY * xhat, or NULL
+ *   dB  : out, N doubles: sum over rows r0..r1-1 of dY (LayerNorm only), or NULL
+ *
+ * With g = dY * w, xhat the normalised input and rstd the row's 1/sqrt(stat + eps):
+ *   LayerNorm: dX = rstd * (g - mean_j(g) - xhat * mean_j(g * xhat))
+ *   RMSNorm  : dX = rstd * (g - xhat * mean_j(g * xhat))
+ * These are the derivatives of the forward definitions above with the statistics treated
+ * as functions of the row.
+ */
+int oracle_bwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64_t r1,
+                    const void *X, const void *dY, const void *dH, const void *W, double eps,
+                    double *dX, double *dW, double *dB) {
+  int st = or_check(kind, dtype, M, N, r0, r1, eps);
+  if (st) return st;
+  if (!X || !dY || !W) return OR_BAD_ARG;
+  if (kind == OR_RMSNORM && dB) return OR_BAD_ARG;
+  int64_t rows = r1 - r0;
+  double *mu = (double *)malloc((size_t)(rows > 0 ? rows : 1) * sizeof(double));
+  double *rs = (double *)malloc((size_t)(rows > 0 ? rows : 1) * sizeof(double));
+  if (!mu || !rs) {
+    free(mu);
+    free(rs);
+    return OR_NO_MEMORY;
+  }
+  int fail = 0;
+
+  /* per-row statistics and dX */
+#pragma omp parallel
+  {
+    double *x = (double *)malloc((size_t)N * sizeof(double));
+    double *xh = (double *)malloc((size_t)N * sizeof(double));
+    double *g = (double *)malloc((size_t)N * sizeof(double));
+    if (!x || !xh || !g) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t i = r0; i < r1; ++i) {
+      if (!x || !xh || !g) continue;
+      int64_t o = i - r0;
+      or_input_row(dtype, N, i, X, NULL, x);
+      or_row_stats(kind, N, x, eps, &mu[o], &rs[o]);
+      if (!dX) continue;
+      double sg = 0.0, sgx = 0.0;
+      for (int64_t j = 0; j < N; ++j) {
+        xh[j] = (kind == OR_LAYERNORM) ? (x[j] - mu[o]) * rs[o] : x[j] * rs[o];
+        g[j] = or_load(dtype, dY, i * N + j) * or_load(dtype, W, j);
+        sg += g[j];
+        sgx += g[j] * xh[j];
+      }
+      double c1 = sg / (double)N;
+      double c2 = sgx / (double)N;
+      for (int64_t j = 0; j < N; ++j) {
+        double d = (kind == OR_LAYERNORM) ? rs[o] * (g[j] - c1 - xh[j] * c2)
+                                          : rs[o] * (g[j] - xh[j] * c2);
+        if (dH) d += or_load(dtype, dH, i * N + j);
+        dX[o * N + j] = d;
+      }
+    }
+    free(x);
+    free(xh);
+    free(g);
+  }
+
+  /* column sums dW = sum_i dY*xhat and dB = sum_i dY, rows in ascending order */
+  if (!fail && (dW || dB)) {
+#pragma omp parallel
+    {
+      int nt = 1, t = 0;
+#ifdef _OPENMP
+      nt = omp_get_num_threads();
+      t = omp_get_thread_num();
+#endif
+      int64_t per = (N + nt - 1) / nt;
+      int64_t j0 = (int64_t)t * per;
+      int64_t j1 = j0 + per < N ? j0 + per : N;
+      if (j0 < j1) {
+        int64_t w = j1 - j0;
+        double *aw = (double *)calloc((size_t)w, sizeof(double));
+        double *ab = (double *)calloc((size_t)w, sizeof(double));
+        if (!aw || !ab) {
+#pragma omp atomic write
+          fail = 1;
+        } else {
+          for (int64_t i = r0; i < r1; ++i) {
+            int64_t o = i - r0;
+            for (int64_t j = j0; j < j1; ++j) {
+              double x = or_load(dtype, X, i * N + j);
+              double xhat = (kind == OR_LAYERNORM) ? (x - mu[o]) * rs[o] : x * rs[o];
+              double dy = or_load(dtype, dY, i * N + j);
+              aw[j - j0] += dy * xhat;
+              ab[j - j0] += dy;
+            }
+          }
+          for (int64_t j = j0; j < j1; ++j) {
+            if (dW) dW[j] = aw[j - j0];
+            if (dB) dB[j] = ab[j - j0];
+          }
+        }
+        free(aw);
+        free(ab);
+      }
+    }
+  }
+  free(mu);
+  free(rs);
+  return fail ? OR_NO_MEMORY : OR_OK;
+}
+
+/* ---- helpers exposed for pins ---------------------------------------------------------- */
+
+/* Widen count values of the given dtype to double. */
+int oracle_decode(int dtype, const void *bits, int64_t count, double *out) {
+  if ((dtype != OR_F32 && dtype != OR_BF16) || count < 0 || (count && (!bits || !out)))
+    return OR_BAD_ARG;
+  for (int64_t k = 0; k < count; ++k) out[k] = or_load(dtype, bits, k);
+  return OR_OK;
+}
+
+/* Round count doubles to bf16 bit patterns (nearest, ties to even). */
+int oracle_round_bf16(const double *in, int64_t count, uint16_t *out) {
+  if (count < 0 || (count && (!in || !out))) return OR_BAD_ARG;
+  for (int64_t k = 0; k < count; ++k) out[k] = or_bf16_bits(in[k]);
+  return OR_OK;
+}
+
+/* Number of OpenMP threads a parallel region will use (1 without OpenMP). */
+int oracle_num_threads(void) {
+#ifdef _OPENMP
+  return omp_get_max_threads();
+#else
+  return 1;
+#endif
+}
+
+/* Set the OpenMP thread count for later calls (ignored without OpenMP). */
+void oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+  if (n > 0) omp_set_num_threads(n);
+#else
+  (void)n;
+#endif
+}

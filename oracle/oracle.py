@@ -1,0 +1,185 @@
+"""ctypes front end of the double-precision CPU oracle (norm_oracle.c).
+
+TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's CPU-baseline
+leg import this module. It shares nothing with the HIP library: inputs are passed as the same
+bit patterns the device receives (bf16 as uint16, fp32 as float32) and every result comes back
+as unrounded float64.
+
+Definitions followed (web page "PyTorch atinge desempenho SOTA em normalização com
+torch.compile", matsubara.tec.br): para. 2 for what LayerNorm and RMSNorm compute, para. 3 for
+the reduction along the contiguous dimension, para. 7 for the gradients dX, dW and dB.
+"""
+import ctypes
+import os
+
+import numpy as np
+
+from . import build as _build
+
+LAYERNORM, RMSNORM = 0, 1
+F32, BF16 = 0, 1
+
+
+class Oracle:
+    """One loaded copy of the oracle library (a path other than the default is used by the
+    tests that plant mistakes in a copy of the oracle and check that the pins catch them)."""
+
+    def __init__(self, path=None):
+        path = path or _build.LIB
+        if not os.path.exists(path):
+            raise RuntimeError("oracle library missing: build it with oracle/build.py")
+        lib = ctypes.CDLL(path)
+        i64, vp, dbl, dp = ctypes.c_int64, ctypes.c_void_p, ctypes.c_double, ctypes.c_void_p
+        lib.oracle_fwd_rows.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                        vp, vp, vp, vp, dbl, dp, dp, dp, dp]
+        lib.oracle_fwd_rows.restype = ctypes.c_int
+        lib.oracle_bwd_rows.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
+                                        vp, vp, vp, vp, dbl, dp, dp, dp]
+        lib.oracle_bwd_rows.restype = ctypes.c_int
+        lib.oracle_decode.argtypes = [ctypes.c_int, vp, i64, dp]
+        lib.oracle_decode.restype = ctypes.c_int
+        lib.oracle_round_bf16.argtypes = [dp, i64, vp]
+        lib.oracle_round_bf16.restype = ctypes.c_int
+        lib.oracle_num_threads.argtypes = []
+        lib.oracle_num_threads.restype = ctypes.c_int
+        lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
+        lib.oracle_set_num_threads.restype = None
+        self.lib = lib
+        self.path = path
+
+    def fwd(self, kind, dtype, X, W, B=None, R=None, eps=1e-5, rows=None, want_h=False):
+        return _fwd(self.lib, kind, dtype, X, W, B, R, eps, rows, want_h)
+
+    def bwd(self, kind, dtype, X, dY, W, dH=None, eps=1e-5, rows=None, want_dx=True,
+            want_dw=True):
+        return _bwd(self.lib, kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw)
+
+    def decode(self, dtype, bits):
+        return _decode(self.lib, dtype, bits)
+
+    def round_bf16(self, values):
+        return _round_bf16(self.lib, values)
+
+    def num_threads(self):
+        return self.lib.oracle_num_threads()
+
+    def set_num_threads(self, n):
+        self.lib.oracle_set_num_threads(int(n))
+
+
+_default = None
+
+
+def default():
+    """The oracle built from oracle/norm_oracle.c (loaded once)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default
+
+
+def _bits(a, dtype, shape=None):
+    """Validate and return a C-contiguous numpy array of input bits."""
+    if a is None:
+        return None
+    want = np.float32 if dtype == F32 else np.uint16
+    a = np.ascontiguousarray(a)
+    if a.dtype != want:
+        raise TypeError("expected %s bits, got %s" % (np.dtype(want).name, a.dtype))
+    if shape is not None and a.shape != shape:
+        raise ValueError("expected shape %s, got %s" % (shape, a.shape))
+    return a
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+def _fwd(lib, kind, dtype, X, W, B, R, eps, rows, want_h):
+    """Forward over rows [r0, r1) (all rows by default).
+
+    Returns a dict of float64 arrays: y (r x N), mean (r), rstd (r), and h (r x N, the
+    rounded R + X) when want_h is set and R is given.
+    """
+    X = _bits(X, dtype)
+    M, N = X.shape
+    W = _bits(W, dtype, (N,))
+    B = _bits(B, dtype, (N,))
+    R = _bits(R, dtype, (M, N))
+    r0, r1 = (0, M) if rows is None else rows
+    n = r1 - r0
+    y = np.empty((n, N), np.float64)
+    mean = np.empty(n, np.float64)
+    rstd = np.empty(n, np.float64)
+    h = np.empty((n, N), np.float64) if (want_h and R is not None) else None
+    st = lib.oracle_fwd_rows(kind, dtype, M, N, r0, r1, _ptr(X), _ptr(R), _ptr(W), _ptr(B),
+                             float(eps), _ptr(y), _ptr(h), _ptr(mean), _ptr(rstd))
+    if st:
+        raise ValueError("oracle_fwd_rows failed with status %d" % st)
+    return {"y": y, "mean": mean, "rstd": rstd, "h": h}
+
+
+def _bwd(lib, kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw):
+    """Backward over rows [r0, r1) (all rows by default).
+
+    X is the norm's input (the stored h for the residual variant). Returns float64 arrays:
+    dx (r x N, or None), dw (N, summed over the rows given, or None) and db (N, LayerNorm
+    only, or None).
+    """
+    X = _bits(X, dtype)
+    M, N = X.shape
+    dY = _bits(dY, dtype, (M, N))
+    dH = _bits(dH, dtype, (M, N))
+    W = _bits(W, dtype, (N,))
+    r0, r1 = (0, M) if rows is None else rows
+    n = r1 - r0
+    dx = np.empty((n, N), np.float64) if want_dx else None
+    dw = np.empty(N, np.float64) if want_dw else None
+    db = np.empty(N, np.float64) if (want_dw and kind == LAYERNORM) else None
+    st = lib.oracle_bwd_rows(kind, dtype, M, N, r0, r1, _ptr(X), _ptr(dY), _ptr(dH), _ptr(W),
+                             float(eps), _ptr(dx), _ptr(dw), _ptr(db))
+    if st:
+        raise ValueError("oracle_bwd_rows failed with status %d" % st)
+    return {"dx": dx, "dw": dw, "db": db}
+
+
+def _decode(lib, dtype, bits):
+    """Widen an array of bf16 (uint16) or fp32 bits to float64 with the oracle's decoder."""
+    a = _bits(bits, dtype)
+    out = np.empty(a.shape, np.float64)
+    if lib.oracle_decode(dtype, _ptr(a), a.size, _ptr(out)):
+        raise ValueError("oracle_decode failed")
+    return out
+
+
+def _round_bf16(lib, values):
+    """Round float64 values to bf16 bit patterns (nearest, ties to even)."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    if lib.oracle_round_bf16(_ptr(v), v.size, _ptr(out)):
+        raise ValueError("oracle_round_bf16 failed")
+    return out
+
+
+def fwd(kind, dtype, X, W, B=None, R=None, eps=1e-5, rows=None, want_h=False):
+    return default().fwd(kind, dtype, X, W, B, R, eps, rows, want_h)
+
+
+def bwd(kind, dtype, X, dY, W, dH=None, eps=1e-5, rows=None, want_dx=True, want_dw=True):
+    return default().bwd(kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw)
+
+
+def decode(dtype, bits):
+    return default().decode(dtype, bits)
+
+
+def round_bf16(values):
+    return default().round_bf16(values)
+
+
+def num_threads():
+    return default().num_threads()
+
+
+def set_num_threads(n):
+    default().set_num_threads(n)

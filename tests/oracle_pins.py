@@ -1,0 +1,454 @@
+"""Pins for the CPU oracle: checks against things other than the oracle itself.
+
+Each ``pin_*`` function takes an oracle object (``oracle.Oracle``) and raises AssertionError
+on a mismatch. ``test_oracle_pins.py`` runs them on the real oracle; ``test_oracle_mutations.py``
+runs them on copies of the oracle with planted mistakes and requires that some pin fails for
+every mistake.
+
+What pins what:
+  - library routines: torch float64 ``layer_norm`` / ``rms_norm`` and autograd (an
+    implementation independent of the oracle) for Y, statistics, dX, dW, dB;
+  - mathematics: row invariants of the normalised output, shift / scale invariance of the
+    gradient, central finite differences of the oracle's own forward;
+  - hand-derived exact cases in tests/golden/exact_cases.json;
+  - number formats: bf16 widening and round-to-nearest-even against torch's conversions.
+
+Definitions (page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
+matsubara.tec.br): para. 2 (LayerNorm, RMSNorm), para. 3 (reduction along the contiguous
+dimension), para. 7 (gradients dX, dW, dB).
+"""
+import json
+import os
+
+import numpy as np
+import torch
+import torch.nn.functional as F
+
+from deep_learning_normalization_amd import inputs
+
+LN, RMS = 0, 1
+F32, BF16 = 0, 1
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "exact_cases.json")
+
+
+def _rng(seed):
+    return torch.Generator().manual_seed(seed)
+
+
+def _sample(M, N, dtype, seed, scale=1.0, shift=0.0):
+    t = torch.randn(M, N, generator=_rng(seed)) * scale + shift
+    return t.to(torch.bfloat16 if dtype == BF16 else torch.float32)
+
+
+def _vec(N, dtype, seed, mean=1.0, std=0.1):
+    t = torch.randn(N, generator=_rng(seed)) * std + mean
+    return t.to(torch.bfloat16 if dtype == BF16 else torch.float32)
+
+
+def _d(t):
+    return None if t is None else t.double()
+
+
+def _close(got, want, rtol, atol, what):
+    got = np.asarray(got, np.float64)
+    want = np.asarray(want, np.float64)
+    assert got.shape == want.shape, "%s: shape %s vs %s" % (what, got.shape, want.shape)
+    err = np.abs(got - want)
+    bound = atol + rtol * np.abs(want)
+    bad = ~(err <= bound)
+    if bad.any():
+        k = np.flatnonzero(bad.ravel())[0]
+        raise AssertionError("%s: %d mismatches, first at %d: got %r want %r" % (
+            what, int(bad.sum()), k, got.ravel()[k], want.ravel()[k]))
+
+
+def _eps32(eps):
+    """The eps both sides see: the device takes eps as binary32."""
+    return float(np.float32(eps))
+
+
+SHAPES = [(1, 1), (3, 2), (5, 7), (17, 64), (8, 1000), (4, 1025), (2, 4099)]
+
+
+# ---- number formats ------------------------------------------------------------------
+
+def pin_bf16_decode(orc):
+    """Every bf16 bit pattern widens to the value torch gives it."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = orc.decode(BF16, bits)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).double().numpy()
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+
+
+def pin_bf16_rounding(orc):
+    """Round-to-nearest-even to bf16 matches torch's binary32 -> bf16 conversion (a single
+    rounding for binary32 inputs), including exact ties, subnormals and overflow."""
+    g = np.random.default_rng(7)
+    hi = g.integers(0, 1 << 16, 20000, dtype=np.uint32)
+    lo = np.concatenate([g.integers(0, 1 << 16, 10000, dtype=np.uint32),
+                         np.full(5000, 0x8000, np.uint32),          # exact ties
+                         np.full(5000, 0x7FFF, np.uint32)])          # just below a tie
+    u = (hi << 16) | lo
+    f = u.view(np.float32)
+    f = f[np.isfinite(f)]
+    got = orc.round_bf16(f.astype(np.float64))
+    want = torch.from_numpy(f.copy()).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(got, want), "bf16 rounding differs from torch"
+
+
+# ---- forward against torch float64 --------------------------------------------------
+
+def pin_layernorm_forward_vs_torch(orc):
+    for dtype in (F32, BF16):
+        for i, (M, N) in enumerate(SHAPES):
+            for eps in (1e-5, 0.0):
+                if eps == 0.0 and N == 1:
+                    continue
+                X = _sample(M, N, dtype, 100 + i, scale=2.0, shift=0.5)
+                W = _vec(N, dtype, 200 + i)
+                B = _vec(N, dtype, 300 + i, mean=0.0)
+                e = _eps32(eps)
+                for bias in (B, None):
+                    r = orc.fwd(LN, dtype, inputs.host_bits(X), inputs.host_bits(W),
+                                inputs.host_bits(bias), eps=e)
+                    xd = X.double()
+                    want = F.layer_norm(xd, (N,), W.double(), _d(bias), e)
+                    _close(r["y"], want.numpy(), 1e-12, 1e-12, "LN y %s" % ((M, N),))
+                    var, mu = torch.var_mean(xd, dim=1, unbiased=False)
+                    _close(r["mean"], mu.numpy(), 1e-12, 1e-12, "LN mean")
+                    _close(r["rstd"], (1.0 / torch.sqrt(var + e)).numpy(), 1e-12, 0, "LN rstd")
+
+
+def pin_rmsnorm_forward_vs_torch(orc):
+    for dtype in (F32, BF16):
+        for i, (M, N) in enumerate(SHAPES):
+            for eps in (1e-6, 0.0):
+                X = _sample(M, N, dtype, 400 + i, scale=1.5, shift=0.25)
+                W = _vec(N, dtype, 500 + i)
+                e = _eps32(eps)
+                r = orc.fwd(RMS, dtype, inputs.host_bits(X), inputs.host_bits(W), eps=e)
+                xd = X.double()
+                want = F.rms_norm(xd, (N,), W.double(), e)
+                _close(r["y"], want.numpy(), 1e-12, 1e-12, "RMS y %s" % ((M, N),))
+                ms = (xd * xd).mean(dim=1)
+                _close(r["rstd"], (1.0 / torch.sqrt(ms + e)).numpy(), 1e-12, 0, "RMS rstd")
+
+
+# ---- forward invariants -----------------------------------------------------------------
+
+def pin_layernorm_row_invariants(orc):
+    """With unit weight and zero bias, every output row has mean 0 and variance
+    var/(var + eps), which is exactly 1 when eps = 0 (numpy computes var)."""
+    M, N = 16, 333
+    X = _sample(M, N, F32, 11, scale=3.0, shift=-2.0)
+    ones = torch.ones(N)
+    for eps in (1e-5, 0.0):
+        e = _eps32(eps)
+        r = orc.fwd(LN, F32, inputs.host_bits(X), inputs.host_bits(ones), eps=e)
+        y = r["y"]
+        x = X.double().numpy()
+        var = np.var(x, axis=1)
+        _close(y.mean(axis=1), np.zeros(M), 0, 1e-13, "LN row mean")
+        _close(np.var(y, axis=1), var / (var + e), 1e-12, 0, "LN row variance")
+        if eps == 0.0:
+            _close(np.var(y, axis=1), np.ones(M), 1e-12, 0, "LN unit variance")
+    # large-mean rows: |mean| >> std must not lose the variance
+    Xb = _sample(4, 256, F32, 12, scale=1.0, shift=1000.0)
+    r = orc.fwd(LN, F32, inputs.host_bits(Xb), inputs.host_bits(torch.ones(256)), eps=0.0)
+    _close(np.var(r["y"], axis=1), np.ones(4), 1e-9, 0, "LN large-mean variance")
+
+
+def pin_rmsnorm_row_invariants(orc):
+    """With unit weight, every output row has mean square ms/(ms + eps); 1 when eps = 0."""
+    M, N = 16, 333
+    X = _sample(M, N, F32, 13, scale=2.0, shift=0.5)
+    ones = torch.ones(N)
+    for eps in (1e-6, 0.0):
+        e = _eps32(eps)
+        r = orc.fwd(RMS, F32, inputs.host_bits(X), inputs.host_bits(ones), eps=e)
+        x = X.double().numpy()
+        ms = np.mean(x * x, axis=1)
+        _close(np.mean(r["y"] ** 2, axis=1), ms / (ms + e), 1e-12, 0, "RMS row mean square")
+        if eps == 0.0:
+            _close(np.mean(r["y"] ** 2, axis=1), np.ones(M), 1e-12, 0, "RMS unit mean square")
+
+
+# ---- hand-derived exact cases ---------------------------------------------------------
+
+def _f32(a):
+    return np.asarray(a, np.float32)
+
+
+def pin_golden_exact_cases(orc):
+    with open(GOLDEN) as f:
+        gold = json.load(f)
+    for c in gold["cases"]:
+        kind = LN if c["kind"] == "layernorm" else RMS
+        X = _f32(c["X"])
+        W = _f32(c["W"])
+        B = None if c["B"] is None else _f32(c["B"])
+        for dtype in (F32, BF16):
+            # every value in these cases is a short dyadic rational: exact in bf16 too
+            conv = (lambda a: a) if dtype == F32 else (
+                lambda a: None if a is None else
+                torch.from_numpy(np.asarray(a)).to(torch.bfloat16).view(torch.int16).numpy()
+                .view(np.uint16))
+            r = orc.fwd(kind, dtype, conv(X), conv(W), conv(B), eps=c["eps"])
+            _close(r["y"], c["Y"], 0, 1e-15, c["name"] + " Y")
+            _close(r["rstd"], c["rstd"], 0, 1e-15, c["name"] + " rstd")
+            if c["mean"] is not None:
+                _close(r["mean"], c["mean"], 0, 1e-15, c["name"] + " mean")
+            g = orc.bwd(kind, dtype, conv(X), conv(_f32(c["dY"])), conv(W), eps=c["eps"])
+            _close(g["dx"], c["dX"], 0, 1e-15, c["name"] + " dX")
+            _close(g["dw"], c["dW"], 0, 1e-15, c["name"] + " dW")
+            if c["dB"] is not None:
+                _close(g["db"], c["dB"], 0, 1e-15, c["name"] + " dB")
+    for c in gold["residual_cases"]:
+        kind = LN if c["kind"] == "layernorm" else RMS
+        if c["dtype"] == "f32":
+            dtype, conv = F32, (lambda a: _f32(a))
+        else:
+            dtype = BF16
+            conv = (lambda a: torch.tensor(a, dtype=torch.float32).to(torch.bfloat16)
+                    .view(torch.int16).numpy().view(np.uint16))
+        r = orc.fwd(kind, dtype, conv(c["X"]), conv(c["W"]), R=conv(c["R"]), eps=c["eps"],
+                    want_h=True)
+        _close(r["h"], c["H"], 0, 0, c["name"] + " H")
+        if "Y" in c:
+            _close(r["y"], c["Y"], 0, 1e-15, c["name"] + " Y")
+            _close(r["rstd"], c["rstd"], 0, 1e-15, c["name"] + " rstd")
+        if "dX" in c:
+            g = orc.bwd(kind, dtype, conv(c["H"]), conv(c["dY"]), conv(c["W"]),
+                        dH=conv(c["dH"]), eps=c["eps"])
+            _close(g["dx"], c["dX"], 0, 1e-15, c["name"] + " dX")
+            _close(g["dw"], c["dW"], 0, 1e-15, c["name"] + " dW")
+
+
+# ---- backward against torch autograd ------------------------------------------------
+
+def pin_backward_vs_torch_autograd(orc):
+    for dtype in (F32, BF16):
+        for i, (M, N) in enumerate(SHAPES):
+            for kind in (LN, RMS):
+                X = _sample(M, N, dtype, 600 + i, scale=1.5, shift=0.3)
+                W = _vec(N, dtype, 700 + i)
+                B = _vec(N, dtype, 800 + i, mean=0.0) if kind == LN else None
+                dY = _sample(M, N, dtype, 900 + i)
+                e = _eps32(1e-5)
+                xd = X.double().requires_grad_(True)
+                wd = W.double().requires_grad_(True)
+                bd = B.double().requires_grad_(True) if B is not None else None
+                if kind == LN:
+                    y = F.layer_norm(xd, (N,), wd, bd, e)
+                else:
+                    y = F.rms_norm(xd, (N,), wd, e)
+                y.backward(dY.double())
+                g = orc.bwd(kind, dtype, inputs.host_bits(X), inputs.host_bits(dY),
+                            inputs.host_bits(W), eps=e)
+                scale = float(xd.grad.abs().max()) + 1e-300
+                _close(g["dx"], xd.grad.numpy(), 1e-10, 1e-12 * scale, "dX %s" % ((M, N),))
+                _close(g["dw"], wd.grad.numpy(), 1e-10, 1e-10, "dW %s" % ((M, N),))
+                if kind == LN:
+                    _close(g["db"], bd.grad.numpy(), 1e-12, 1e-12, "dB %s" % ((M, N),))
+
+
+def pin_column_sums_by_definition(orc):
+    """dW is the sum over rows of dY times the normalised input (torch's affine-free norm)
+    and dB the sum over rows of dY."""
+    M, N = 37, 96
+    for kind in (LN, RMS):
+        X = _sample(M, N, F32, 21, scale=2.0, shift=1.0)
+        dY = _sample(M, N, F32, 22)
+        W = _vec(N, F32, 23)
+        e = _eps32(1e-5)
+        xd = X.double()
+        xhat = F.layer_norm(xd, (N,), eps=e) if kind == LN else F.rms_norm(xd, (N,), eps=e)
+        g = orc.bwd(kind, F32, inputs.host_bits(X), inputs.host_bits(dY), inputs.host_bits(W),
+                    eps=e)
+        _close(g["dw"], (dY.double() * xhat).sum(0).numpy(), 1e-12, 1e-12, "dW definition")
+        if kind == LN:
+            _close(g["db"], dY.double().sum(0).numpy(), 1e-12, 1e-12, "dB definition")
+
+
+# ---- backward: finite differences of the oracle's own forward ---------------------------
+
+def _dyadic(M, N, seed, lo=-48, hi=48):
+    """Values k/16: exact in binary32, so x +- 2^-12 stays exact."""
+    g = np.random.default_rng(seed)
+    return (g.integers(lo, hi, size=(M, N)) / 16.0).astype(np.float32)
+
+
+def pin_backward_finite_differences(orc):
+    """Central differences of L = sum(dY * Y) (plus sum(dH * H) for the residual variant)
+    through the oracle's forward match its backward. Perturbations of 2^-12 on dyadic inputs
+    are exact in binary32."""
+    h = 2.0 ** -12
+    for kind in (LN, RMS):
+        for (M, N) in ((1, 3), (2, 5), (3, 8)):
+            seed = 31 * M + N + 7 * kind
+            X = _dyadic(M, N, seed)
+            X[:, 0] += 0.5  # no constant rows
+            W = (1.0 + _dyadic(1, N, seed + 1, -8, 8)[0] / 4).astype(np.float32)
+            B = _dyadic(1, N, seed + 2)[0] if kind == LN else None
+            dY = _dyadic(M, N, seed + 3)
+            eps = 0.125
+
+            def loss(Xp, Wp, Bp):
+                return float((orc.fwd(kind, F32, Xp, Wp, Bp, eps=eps)["y"] * dY).sum())
+
+            g = orc.bwd(kind, F32, X, dY, W, eps=eps)
+            fd = np.zeros((M, N))
+            for i in range(M):
+                for j in range(N):
+                    Xp, Xm = X.copy(), X.copy()
+                    Xp[i, j] += h
+                    Xm[i, j] -= h
+                    fd[i, j] = (loss(Xp, W, B) - loss(Xm, W, B)) / (2 * h)
+            _close(g["dx"], fd, 1e-5, 1e-6, "FD dX kind=%d %s" % (kind, (M, N)))
+            fw = np.zeros(N)
+            fb = np.zeros(N)
+            for j in range(N):
+                Wp, Wm = W.copy(), W.copy()
+                Wp[j] += h
+                Wm[j] -= h
+                fw[j] = (loss(X, Wp, B) - loss(X, Wm, B)) / (2 * h)
+                if kind == LN:
+                    Bp, Bm = B.copy(), B.copy()
+                    Bp[j] += h
+                    Bm[j] -= h
+                    fb[j] = (loss(X, W, Bp) - loss(X, W, Bm)) / (2 * h)
+            _close(g["dw"], fw, 1e-6, 1e-6, "FD dW")
+            if kind == LN:
+                _close(g["db"], fb, 1e-6, 1e-6, "FD dB")
+
+
+def pin_residual_finite_differences(orc):
+    """Residual variant in fp32 on dyadic inputs (R + X exact): the gradient with respect to
+    X and to R of L = sum(dY * Y) + sum(dH * H) equals the oracle's dX (plus dH)."""
+    h = 2.0 ** -12
+    M, N = 2, 6
+    X = _dyadic(M, N, 91)
+    R = _dyadic(M, N, 92)
+    R[:, 0] += 0.5
+    W = (1.0 + _dyadic(1, N, 93, -8, 8)[0] / 4).astype(np.float32)
+    dY = _dyadic(M, N, 94)
+    dH = _dyadic(M, N, 95)
+    eps = 0.125
+
+    def loss(Xp, Rp):
+        r = orc.fwd(RMS, F32, Xp, W, R=Rp, eps=eps, want_h=True)
+        return float((r["y"] * dY).sum() + (r["h"] * dH).sum())
+
+    Hbits = (X.astype(np.float64) + R).astype(np.float32)
+    g = orc.bwd(RMS, F32, Hbits, dY, W, dH=dH, eps=eps)
+    for which in ("X", "R"):
+        fd = np.zeros((M, N))
+        for i in range(M):
+            for j in range(N):
+                Ap, Am = (X.copy(), X.copy()) if which == "X" else (R.copy(), R.copy())
+                Ap[i, j] += h
+                Am[i, j] -= h
+                if which == "X":
+                    fd[i, j] = (loss(Ap, R) - loss(Am, R)) / (2 * h)
+                else:
+                    fd[i, j] = (loss(X, Ap) - loss(X, Am)) / (2 * h)
+        _close(g["dx"], fd, 1e-5, 1e-6, "FD residual d%s" % which)
+
+
+# ---- backward: invariances ----------------------------------------------------------------
+
+def pin_backward_invariances(orc):
+    """LayerNorm output is unchanged by adding a constant to a row, so every dX row sums to
+    0 (any eps). With eps = 0 it is also unchanged by scaling the row about its mean, so
+    dX . (x - mean) = 0; RMSNorm with eps = 0 is unchanged by scaling, so dX . x = 0."""
+    M, N = 8, 200
+    X = _sample(M, N, F32, 41, scale=2.0, shift=0.7)
+    dY = _sample(M, N, F32, 42)
+    W = _vec(N, F32, 43)
+    x = X.double().numpy()
+    for eps in (1e-5, 0.0):
+        e = _eps32(eps)
+        g = orc.bwd(LN, F32, inputs.host_bits(X), inputs.host_bits(dY), inputs.host_bits(W),
+                    eps=e)
+        scale = np.abs(g["dx"]).sum(axis=1)
+        _close(g["dx"].sum(axis=1), np.zeros(M), 0, 1e-13 * scale.max(), "LN sum dX")
+        if eps == 0.0:
+            dot = (g["dx"] * (x - x.mean(axis=1, keepdims=True))).sum(axis=1)
+            _close(dot, np.zeros(M), 0, 1e-12 * scale.max() * np.abs(x).max(), "LN dX.(x-mu)")
+            g2 = orc.bwd(RMS, F32, inputs.host_bits(X), inputs.host_bits(dY),
+                         inputs.host_bits(W), eps=e)
+            s2 = np.abs(g2["dx"]).sum(axis=1).max() * np.abs(x).max()
+            _close((g2["dx"] * x).sum(axis=1), np.zeros(M), 0, 1e-12 * s2, "RMS dX.x")
+
+
+# ---- row ranges and threads ----------------------------------------------------------------
+
+def pin_row_ranges_and_threads(orc):
+    """A row range gives the matching slice of the full result; the column sums over two
+    ranges add up to the full sums; one thread and many threads agree bit for bit."""
+    M, N = 50, 130
+    X = _sample(M, N, BF16, 51)
+    dY = _sample(M, N, BF16, 52)
+    W = _vec(N, BF16, 53)
+    B = _vec(N, BF16, 54, mean=0.0)
+    xb, db_, wb, bb = (inputs.host_bits(t) for t in (X, dY, W, B))
+    full = orc.fwd(LN, BF16, xb, wb, bb, eps=1e-5)
+    part = orc.fwd(LN, BF16, xb, wb, bb, eps=1e-5, rows=(13, 29))
+    assert np.array_equal(part["y"], full["y"][13:29])
+    assert np.array_equal(part["rstd"], full["rstd"][13:29])
+    gf = orc.bwd(LN, BF16, xb, db_, wb, eps=1e-5)
+    ga = orc.bwd(LN, BF16, xb, db_, wb, eps=1e-5, rows=(0, 20))
+    gb = orc.bwd(LN, BF16, xb, db_, wb, eps=1e-5, rows=(20, M))
+    assert np.array_equal(gb["dx"], gf["dx"][20:])
+    _close(ga["dw"] + gb["dw"], gf["dw"], 1e-12, 1e-12, "dW split")
+    _close(ga["db"] + gb["db"], gf["db"], 1e-12, 1e-12, "dB split")
+    nt = orc.num_threads()
+    try:
+        orc.set_num_threads(1)
+        g1 = orc.bwd(LN, BF16, xb, db_, wb, eps=1e-5)
+        f1 = orc.fwd(LN, BF16, xb, wb, bb, eps=1e-5)
+    finally:
+        orc.set_num_threads(nt)
+    for k in ("dx", "dw", "db"):
+        assert np.array_equal(g1[k], gf[k]), k
+    assert np.array_equal(f1["y"], full["y"])
+
+
+def pin_residual_rounding_vs_torch(orc):
+    """The residual input h = round_bf16(R + X): on elements where the binary32 sum of the two
+    bf16 values is exact, torch's binary32 -> bf16 conversion is a single rounding and must
+    give the same bits; the output equals the plain norm of that rounded h."""
+    M, N = 64, 257
+    R = _sample(M, N, BF16, 61)
+    X = _sample(M, N, BF16, 62, scale=0.5)
+    W = _vec(N, BF16, 63)
+    r = orc.fwd(RMS, BF16, inputs.host_bits(X), inputs.host_bits(W), R=inputs.host_bits(R),
+                eps=1e-6, want_h=True)
+    s32 = R.float() + X.float()
+    exact = (s32.double() == R.double() + X.double()).numpy()
+    assert exact.mean() > 0.99
+    want = s32.to(torch.bfloat16).double().numpy()
+    assert np.array_equal(r["h"][exact], want[exact])
+    Hb = torch.from_numpy(r["h"]).float().to(torch.bfloat16)  # exact: h holds bf16 values
+    plain = orc.fwd(RMS, BF16, inputs.host_bits(Hb), inputs.host_bits(W), eps=1e-6)
+    assert np.array_equal(plain["y"], r["y"])
+
+
+ALL_PINS = [
+    pin_bf16_decode,
+    pin_bf16_rounding,
+    pin_layernorm_forward_vs_torch,
+    pin_rmsnorm_forward_vs_torch,
+    pin_layernorm_row_invariants,
+    pin_rmsnorm_row_invariants,
+    pin_golden_exact_cases,
+    pin_backward_vs_torch_autograd,
+    pin_column_sums_by_definition,
+    pin_backward_finite_differences,
+    pin_residual_finite_differences,
+    pin_backward_invariances,
+    pin_row_ranges_and_threads,
+    pin_residual_rounding_vs_torch,
+]

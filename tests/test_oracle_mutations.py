@@ -1,0 +1,76 @@
+"""Planted mistakes in copies of the oracle must each fail at least one pin (no GPU).
+
+Every mutation is a plausible slip in the oracle's source: a dropped term, a wrong sign, a
+wrong index, the wrong estimator, a skipped rounding. The copy is compiled with the same
+flags as the real oracle and the pins run on it; the test fails if a mutant passes them all.
+"""
+import os
+import subprocess
+
+import pytest
+
+from oracle import build as obuild
+from oracle.oracle import Oracle
+from tests import oracle_pins
+
+MUTATIONS = [
+    ("unbiased variance", "double var = q / (double)N;",
+     "double var = q / (double)(N > 1 ? N - 1 : 1);"),
+    ("LN eps outside sqrt", "*rstd = 1.0 / sqrt(var + eps);", "*rstd = 1.0 / (sqrt(var) + eps);"),
+    ("RMS eps dropped", "*rstd = 1.0 / sqrt(ms + eps);", "*rstd = 1.0 / sqrt(ms);"),
+    ("RMS mean square off by one", "double ms = q / (double)N;", "double ms = q / (double)(N + 1);"),
+    ("LN mean off by one", "double mu = s / (double)N;", "double mu = s / (double)(N + 1);"),
+    ("bias dropped", "xhat * w + b : xhat * w;", "xhat * w : xhat * w;"),
+    ("bias sign", "xhat * w + b : xhat * w;", "xhat * w - b : xhat * w;"),
+    ("weight index reversed", "double w = or_load(dtype, W, j);",
+     "double w = or_load(dtype, W, N - 1 - j);"),
+    ("LN mean-gradient term dropped", "rs[o] * (g[j] - c1 - xh[j] * c2)", "rs[o] * (g[j] - xh[j] * c2)"),
+    ("LN projection sign", "rs[o] * (g[j] - c1 - xh[j] * c2)", "rs[o] * (g[j] - c1 + xh[j] * c2)"),
+    ("RMS projection dropped", ": rs[o] * (g[j] - xh[j] * c2);", ": rs[o] * g[j];"),
+    ("projection without xhat", "sgx += g[j] * xh[j];", "sgx += g[j];"),
+    ("gradient ignores weight",
+     "g[j] = or_load(dtype, dY, i * N + j) * or_load(dtype, W, j);",
+     "g[j] = or_load(dtype, dY, i * N + j);"),
+    ("dY column index reversed",
+     "g[j] = or_load(dtype, dY, i * N + j) * or_load(dtype, W, j);",
+     "g[j] = or_load(dtype, dY, i * N + (N - 1 - j)) * or_load(dtype, W, j);"),
+    ("dW uses raw input", "aw[j - j0] += dy * xhat;", "aw[j - j0] += dy * x;"),
+    ("dB weighted by xhat", "ab[j - j0] += dy;", "ab[j - j0] += dy * xhat;"),
+    ("dW skips first row",
+     "for (int64_t i = r0; i < r1; ++i) {\n            int64_t o = i - r0;\n            for (int64_t j = j0;",
+     "for (int64_t i = r0 + 1; i < r1; ++i) {\n            int64_t o = i - r0;\n            for (int64_t j = j0;"),
+    ("incoming residual gradient dropped", "if (dH) d += or_load(dtype, dH, i * N + j);",
+     "if (dH) d += 0.0;"),
+    ("residual sum not rounded",
+     "if (R) v = or_round_to_dtype(dtype, or_load(dtype, R, i * N + j) + v);",
+     "if (R) v = or_load(dtype, R, i * N + j) + v;"),
+    ("bf16 ties away from zero", "double r = nearbyint(ldexp(a, -q));",
+     "double r = round(ldexp(a, -q));"),
+    ("bf16 decode shift", "uint32_t u = ((uint32_t)b) << 16;", "uint32_t u = ((uint32_t)b) << 15;"),
+]
+
+
+def _build_mutant(tmp_path, name, old, new):
+    with open(obuild.SRC) as f:
+        src = f.read()
+    assert src.count(old) == 1, "mutation %r: pattern must occur exactly once" % name
+    path = os.path.join(str(tmp_path), "mutant.c")
+    with open(path, "w") as f:
+        f.write(src.replace(old, new))
+    lib = os.path.join(str(tmp_path), "libmutant.so")
+    subprocess.run(["gcc", *obuild.CFLAGS, path, "-o", lib, "-lm"], check=True,
+                   capture_output=True)
+    return lib
+
+
+@pytest.mark.parametrize("name,old,new", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    orc = Oracle(_build_mutant(tmp_path, name, old, new))
+    failures = []
+    for pin in oracle_pins.ALL_PINS:
+        try:
+            pin(orc)
+        except (AssertionError, ValueError) as e:  # a pin mismatch or a rejected result
+            failures.append((pin.__name__, str(e)[:120]))
+            break
+    assert failures, "planted mistake %r passed every pin" % name
