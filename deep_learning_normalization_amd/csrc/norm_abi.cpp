@@ -1,0 +1,275 @@
+// norm_abi.cpp -- the extern "C" entry points declared in include/norm.h.
+//
+// Each call: check arguments (no device access), find the current device's compute-unit count
+// (cached), build the launch plan, check the workspace, queue the kernels on the caller's
+// stream. Nothing here allocates or synchronises.
+#include <atomic>
+#include <new>
+
+#include "norm_internal.hpp"
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_cu_count[kMaxDevices];
+
+norm_status_t current_cu_count(int *cu) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return NORM_ERR_HIP;
+  if (dev < kMaxDevices) {
+    const int cached = g_cu_count[dev].load(std::memory_order_relaxed);
+    if (cached > 0) {
+      *cu = cached;
+      return NORM_OK;
+    }
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return NORM_ERR_HIP;
+  if (dev < kMaxDevices) g_cu_count[dev].store(n, std::memory_order_relaxed);
+  *cu = n;
+  return NORM_OK;
+}
+
+float *ws_region(void *ws, size_t off) {
+  return reinterpret_cast<float *>(static_cast<char *>(ws) + off);
+}
+
+norm_status_t ws_ok(const dln::Plan &p, const void *ws, size_t ws_bytes) {
+  if (p.ws_bytes == 0) return NORM_OK;
+  if (!ws || ws_bytes < p.ws_bytes || ((uintptr_t)ws & 15u)) return NORM_ERR_WORKSPACE;
+  return NORM_OK;
+}
+
+// Plan, workspace check and argument block of the backward's fused pass.
+norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                        const void *W, const float *mean, const float *rstd, float eps,
+                        int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                        void *workspace, size_t workspace_bytes, dln::Plan *plan,
+                        dln::BwdArgs *a) {
+  int cu = 0;
+  norm_status_t st = current_cu_count(&cu);
+  if (st != NORM_OK) return st;
+  const void *ptrs[] = {X, dY, dH, W, dX, dR};
+  const int aligned = dln::all_aligned16(ptrs, 6) ? 1 : 0;
+  st = dln::make_plan(kind, dtype, NORM_PASS_BWD, M, N, 0, aligned, cu, dln::tuning(), plan);
+  if (st != NORM_OK) return st;
+  st = ws_ok(*plan, workspace, workspace_bytes);
+  if (st != NORM_OK) return st;
+  dln::BwdArgs b{};
+  b.x = X;
+  b.dy = dY;
+  b.dh = dH;
+  b.w = W;
+  b.mean = kind == NORM_LAYERNORM ? mean : nullptr;
+  b.rstd = rstd;
+  b.dx = dX;
+  b.dr = (dR == dX) ? nullptr : dR;
+  b.dw = nullptr;
+  b.db = nullptr;
+  b.colpart = ws_region(workspace, plan->off_colpart);
+  b.header = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + plan->off_header);
+  b.rowpart = plan->scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, plan->off_rowpart) : nullptr;
+  b.stats = plan->scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, plan->off_stats) : nullptr;
+  b.M = M;
+  b.N = (int32_t)N;
+  b.nacc = (int32_t)(N / plan->epv);
+  b.chunks = plan->chunks;
+  b.chunk_acc = (int32_t)(plan->chunk_elems / plan->epv);
+  b.partials = plan->partials;
+  b.row_groups = plan->row_groups;
+  b.rows_per_group = plan->rows_per_group;
+  b.layernorm = kind == NORM_LAYERNORM ? 1 : 0;
+  b.want_db = 1;
+  b.eps = eps;
+  b.inv_n = 1.0f / (float)N;
+  *a = b;
+  return NORM_OK;
+}
+
+norm_status_t run_fused(const dln::Plan &p, norm_dtype_t dtype, const dln::BwdArgs &a,
+                        hipStream_t s) {
+  if (p.scheme == NORM_SCHEME_SPLIT) return dln::launch_split_bwd(p, dtype, a, s);
+  return dln::launch_team_bwd(p, dtype, a, s);
+}
+
+// Column reduction of the partials a fused pass left in `workspace` (its header says how many).
+norm_status_t run_reduce(norm_dtype_t dtype, int64_t N, void *dW, void *dB, void *workspace,
+                         size_t workspace_bytes, hipStream_t s) {
+  const size_t row_pair = (size_t)2 * (size_t)N * 4;
+  if (!workspace || ((uintptr_t)workspace & 15u) ||
+      workspace_bytes < dln::kWsHeaderBytes + row_pair)
+    return NORM_ERR_WORKSPACE;
+  dln::ReduceArgs r{};
+  r.header = static_cast<const int64_t *>(workspace);
+  r.colpart = ws_region(workspace, dln::kWsHeaderBytes);
+  r.dw = dW;
+  r.db = dB;
+  r.max_partials = (int64_t)((workspace_bytes - dln::kWsHeaderBytes) / row_pair);
+  r.N = (int32_t)N;
+  return dln::launch_reduce(dtype, r, s);
+}
+
+norm_status_t zero_outputs(int64_t N, norm_dtype_t dtype, void *dW, void *dB, hipStream_t s) {
+  const size_t n = (size_t)N * (dtype == NORM_F32 ? 4 : 2);
+  norm_status_t st = dln::launch_zero(dW, n, s);
+  if (st == NORM_OK && dB) st = dln::launch_zero(dB, n, s);
+  return st;
+}
+
+} // namespace
+
+extern "C" {
+
+norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const void *W,
+                       const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
+                       void *Y, void *H, float *mean, float *rstd, void *workspace,
+                       size_t workspace_bytes, norm_stream_t stream) {
+  dln::FwdCheck c{kind, dtype, X, R, W, B, eps, M, N, Y, H, mean, rstd, workspace,
+                  workspace_bytes};
+  norm_status_t st = dln::check_fwd(c);
+  if (st != NORM_OK || M == 0) return st;
+  int cu = 0;
+  st = current_cu_count(&cu);
+  if (st != NORM_OK) return st;
+  const void *ptrs[] = {X, R, W, B, Y, H};
+  const int aligned = dln::all_aligned16(ptrs, 6) ? 1 : 0;
+  dln::Plan p;
+  st = dln::make_plan(kind, dtype, NORM_PASS_FWD, M, N, R != nullptr, aligned, cu,
+                      dln::tuning(), &p);
+  if (st != NORM_OK) return st;
+  st = ws_ok(p, workspace, workspace_bytes);
+  if (st != NORM_OK) return st;
+  dln::FwdArgs a{};
+  a.x = X;
+  a.r = R;
+  a.w = W;
+  a.b = kind == NORM_LAYERNORM ? B : nullptr;
+  a.y = Y;
+  a.h = H;
+  a.mean = kind == NORM_LAYERNORM ? mean : nullptr;
+  a.rstd = rstd;
+  a.rowpart = p.scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, p.off_rowpart) : nullptr;
+  a.M = M;
+  a.N = (int32_t)N;
+  a.nacc = (int32_t)(N / p.epv);
+  a.chunks = p.chunks;
+  a.chunk_acc = (int32_t)(p.chunk_elems / p.epv);
+  a.layernorm = kind == NORM_LAYERNORM ? 1 : 0;
+  a.eps = eps;
+  a.inv_n = 1.0f / (float)N;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (p.scheme == NORM_SCHEME_SPLIT) return dln::launch_split_fwd(p, dtype, a, s);
+  return dln::launch_team_fwd(p, dtype, a, s);
+}
+
+norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                       const void *W, const float *mean, const float *rstd, float eps,
+                       int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR, void *dW,
+                       void *dB, void *workspace, size_t workspace_bytes, norm_stream_t stream) {
+  dln::BwdCheck c{kind, dtype, X, dY, dH, W, mean, rstd, eps, M, N, dX, dR, dW, dB, workspace,
+                  workspace_bytes, 1, 1};
+  norm_status_t st = dln::check_bwd(c);
+  if (st != NORM_OK) return st;
+  if (kind == NORM_RMSNORM) dB = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) return zero_outputs(N, dtype, dW, dB, s); // empty column sums
+  dln::Plan p;
+  dln::BwdArgs a;
+  st = bwd_setup(kind, X, dY, dH, W, mean, rstd, eps, M, N, dtype, dX, dR, workspace,
+                 workspace_bytes, &p, &a);
+  if (st != NORM_OK) return st;
+  // the split scheme with a single row group writes dW/dB itself, with no reduction pass
+  const bool direct = p.scheme == NORM_SCHEME_SPLIT && p.row_groups == 1;
+  if (direct) {
+    a.dw = dW;
+    a.db = dB;
+  }
+  st = run_fused(p, dtype, a, s);
+  if (st != NORM_OK || direct) return st;
+  return run_reduce(dtype, N, dW, dB, workspace, workspace_bytes, s);
+}
+
+norm_status_t norm_bwd_fused(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                             const void *W, const float *mean, const float *rstd, float eps,
+                             int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                             void *workspace, size_t workspace_bytes, norm_stream_t stream) {
+  dln::BwdCheck c{kind, dtype, X, dY, dH, W, mean, rstd, eps, M, N, dX, dR, nullptr, nullptr,
+                  workspace, workspace_bytes, 1, 0};
+  norm_status_t st = dln::check_bwd(c);
+  if (st != NORM_OK || M == 0) return st;
+  dln::Plan p;
+  dln::BwdArgs a;
+  st = bwd_setup(kind, X, dY, dH, W, mean, rstd, eps, M, N, dtype, dX, dR, workspace,
+                 workspace_bytes, &p, &a);
+  if (st != NORM_OK) return st;
+  return run_fused(p, dtype, a, static_cast<hipStream_t>(stream));
+}
+
+norm_status_t norm_bwd_reduce(norm_kind_t kind, int64_t M, int64_t N, norm_dtype_t dtype,
+                              void *dW, void *dB, void *workspace, size_t workspace_bytes,
+                              norm_stream_t stream) {
+  dln::BwdCheck c{kind, dtype, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, M,
+                  N, nullptr, nullptr, dW, dB, workspace, workspace_bytes, 0, 1};
+  norm_status_t st = dln::check_bwd(c);
+  if (st != NORM_OK) return st;
+  if (kind == NORM_RMSNORM) dB = nullptr;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (M == 0) return zero_outputs(N, dtype, dW, dB, s);
+  return run_reduce(dtype, N, dW, dB, workspace, workspace_bytes, s);
+}
+
+norm_status_t norm_workspace_size(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass,
+                                  int64_t M, int64_t N, int residual, size_t *bytes) {
+  if (!bytes) return NORM_ERR_INVALID_ARG;
+  if (M < 0 || N <= 0) return NORM_ERR_INVALID_ARG;
+  int cu = 0;
+  norm_status_t st = current_cu_count(&cu);
+  if (st != NORM_OK) return st;
+  return dln::workspace_bytes(kind, dtype, pass, M, N, residual, cu, dln::tuning(), bytes);
+}
+
+norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
+                        int64_t N, int residual, int aligned, int cu_count, norm_plan_t *out) {
+  if (!out) return NORM_ERR_INVALID_ARG;
+  dln::Plan p;
+  norm_status_t st =
+      dln::make_plan(kind, dtype, pass, M, N, residual, aligned, cu_count, dln::tuning(), &p);
+  if (st != NORM_OK) return st;
+  norm_plan_t o{};
+  o.scheme = p.scheme;
+  o.vector = p.vector;
+  o.elems_per_access = p.epv;
+  o.threads = p.threads;
+  o.team_threads = p.team_threads;
+  o.accesses_per_thread = p.vpt;
+  o.rows_per_iter = p.rows;
+  o.grid = p.grid;
+  o.chunks = p.chunks;
+  o.chunk_elems = p.chunk_elems;
+  o.row_groups = p.row_groups;
+  o.partials = p.partials;
+  o.workspace_bytes = p.ws_bytes;
+  *out = o;
+  return NORM_OK;
+}
+
+norm_status_t norm_set_tuning(norm_tune_t key, int64_t value) {
+  return dln::set_tuning(key, value);
+}
+
+const char *norm_status_string(norm_status_t status) {
+  switch (status) {
+  case NORM_OK: return "NORM_OK";
+  case NORM_ERR_INVALID_ARG: return "NORM_ERR_INVALID_ARG: invalid argument";
+  case NORM_ERR_UNSUPPORTED: return "NORM_ERR_UNSUPPORTED: shape or option not supported";
+  case NORM_ERR_WORKSPACE: return "NORM_ERR_WORKSPACE: workspace missing or too small";
+  case NORM_ERR_HIP: return "NORM_ERR_HIP: HIP runtime or launch failure";
+  default: return "unknown norm status";
+  }
+}
+
+int norm_version(void) { return 100; }
+
+} // extern "C"

@@ -1,0 +1,203 @@
+// norm_device.hpp -- device building blocks for the gfx950 norm kernels: 16-byte accesses with
+// fp32 unpack/pack, wavefront sums over DPP, and team sums through LDS.
+#pragma once
+
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+namespace dln {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+// bf16 tensors are carried as their raw 16-bit patterns.
+typedef uint16_t bf16_bits;
+
+// Input loads and output stores of the streamed [M, N] tensors. Each element is touched once
+// per pass, so stores bypass the caches' allocate-on-write (nontemporal). Loads stay ordinary:
+// the split scheme re-reads its chunks and wants them cached.
+#ifndef DLN_STORE_NT
+#define DLN_STORE_NT 1
+#endif
+#ifndef DLN_LOAD_NT
+#define DLN_LOAD_NT 0
+#endif
+
+template <typename V> __device__ __forceinline__ V ld_stream(const V *p) {
+#if DLN_LOAD_NT
+  return __builtin_nontemporal_load(p);
+#else
+  return *p;
+#endif
+}
+
+template <typename V> __device__ __forceinline__ void st_stream(V *p, V v) {
+#if DLN_STORE_NT
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+
+__device__ __forceinline__ float bf16_lo(unsigned u) { return __builtin_bit_cast(float, u << 16); }
+__device__ __forceinline__ float bf16_hi(unsigned u) {
+  return __builtin_bit_cast(float, u & 0xffff0000u);
+}
+// Two fp32 values to two bf16 (round to nearest even, gfx950 v_cvt_pk_bf16_f32), packed.
+__device__ __forceinline__ unsigned pack_bf16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, bf16x2));
+}
+__device__ __forceinline__ float round_bf16(float v) {
+  unsigned p = pack_bf16x2(v, 0.0f);
+  return bf16_lo(p);
+}
+
+// Acc<T, VEC>: one memory access of EPV elements of T (16 bytes when VEC, else one element),
+// converted to / from fp32.
+template <typename T, bool VEC> struct Acc;
+
+template <> struct Acc<float, true> {
+  static constexpr int EPV = 4;
+  typedef u32x4 raw;
+  __device__ static raw ld(const float *p) { return ld_stream(reinterpret_cast<const raw *>(p)); }
+  __device__ static raw ld_cached(const float *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static void st(float *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
+  __device__ static void unpack(raw v, float *f) {
+    // Element first into a scalar: this clang's __builtin_bit_cast applied directly to a
+    // vector subscript (v[i]) reads element 0 whatever i is.
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const unsigned u = v[i];
+      f[i] = __builtin_bit_cast(float, u);
+    }
+  }
+  __device__ static raw pack(const float *f) {
+    raw v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(unsigned, f[i]);
+    return v;
+  }
+  __device__ static float round(float v) { return v; }
+  __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
+};
+
+template <> struct Acc<bf16_bits, true> {
+  static constexpr int EPV = 8;
+  typedef u32x4 raw;
+  __device__ static raw ld(const bf16_bits *p) {
+    return ld_stream(reinterpret_cast<const raw *>(p));
+  }
+  __device__ static raw ld_cached(const bf16_bits *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static void st(bf16_bits *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
+  __device__ static void unpack(raw v, float *f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      f[2 * i] = bf16_lo(v[i]);
+      f[2 * i + 1] = bf16_hi(v[i]);
+    }
+  }
+  __device__ static raw pack(const float *f) {
+    raw v;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    return v;
+  }
+  __device__ static float round(float v) { return round_bf16(v); }
+  __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
+};
+
+template <> struct Acc<float, false> {
+  static constexpr int EPV = 1;
+  typedef float raw;
+  __device__ static raw ld(const float *p) { return *p; }
+  __device__ static raw ld_cached(const float *p) { return *p; }
+  __device__ static void st(float *p, raw v) { *p = v; }
+  __device__ static void unpack(raw v, float *f) { f[0] = v; }
+  __device__ static raw pack(const float *f) { return f[0]; }
+  __device__ static float round(float v) { return v; }
+  __device__ static raw zero() { return 0.0f; }
+};
+
+template <> struct Acc<bf16_bits, false> {
+  static constexpr int EPV = 1;
+  typedef bf16_bits raw;
+  __device__ static raw ld(const bf16_bits *p) { return *p; }
+  __device__ static raw ld_cached(const bf16_bits *p) { return *p; }
+  __device__ static void st(bf16_bits *p, raw v) { *p = v; }
+  __device__ static void unpack(raw v, float *f) {
+    f[0] = __builtin_bit_cast(float, ((unsigned)v) << 16);
+  }
+  __device__ static raw pack(const float *f) { return (raw)(pack_bf16x2(f[0], 0.0f) & 0xffffu); }
+  __device__ static float round(float v) { return round_bf16(v); }
+  __device__ static raw zero() { return 0; }
+};
+
+// ---- reductions -------------------------------------------------------------------------
+
+template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, v), CTRL, 0xF, 0xF, true));
+}
+
+__device__ __forceinline__ float read_lane(float v, int lane) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
+}
+
+// Sum over the 64 lanes of a wavefront. Every step pairs lanes symmetrically, so all lanes end
+// with the same bits; the four 16-lane row sums are then combined in a fixed order through
+// scalar registers. All 64 lanes must be active.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v); // row_half_mirror: quad 0 <-> quad 1 within each 8 lanes
+  v += dpp_mov<0x140>(v); // row_mirror: the two 8-lane halves of each 16-lane row
+  float r0 = read_lane(v, 0), r1 = read_lane(v, 16), r2 = read_lane(v, 32), r3 = read_lane(v, 48);
+  return (r0 + r1) + (r2 + r3);
+}
+
+// LDS scratch for team sums: 2 alternating slots x up to 12 values x up to 16 waves.
+constexpr int RED_VALS = 12;
+constexpr int RED_WAVES = 16;
+constexpr int RED_FLOATS = 2 * RED_VALS * RED_WAVES;
+
+// Sums NV values over one team of `waves` consecutive wavefronts of the workgroup (the team's
+// first wave is `wave0`; this thread's wave is `wave`). Every thread of the workgroup must call
+// it with the same slot and NV (it contains one barrier when waves > 1). Alternating the slot
+// between consecutive calls makes one barrier per call enough: a slot is rewritten only after
+// the next call's barrier, by which time every thread has read it.
+template <int NV>
+__device__ __forceinline__ void team_sum(float (&v)[NV], float *red, int slot, int waves,
+                                         int wave0, int wave, int lane) {
+  static_assert(NV <= RED_VALS, "too many values for one team sum");
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
+  if (waves == 1) return;
+  float *base = red + slot * (RED_VALS * RED_WAVES);
+  if (lane == 0) {
+#pragma unroll
+    for (int i = 0; i < NV; ++i) base[i * RED_WAVES + wave] = v[i];
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < NV; ++i) {
+    float s = 0.0f;
+    for (int k = 0; k < waves; ++k) s += base[i * RED_WAVES + wave0 + k];
+    v[i] = s;
+  }
+}
+
+// a * b rounded to fp32 and never fused into a following add (device code is compiled with
+// FMA contraction on). A row mean formed this way is the same fp32 value at every use, which
+// the mean-correction sums rely on.
+__device__ __forceinline__ float mul_rn(float a, float b) {
+#pragma clang fp contract(off)
+  return a * b;
+}
+
+// 1 / sqrt(v): the hardware reciprocal square root (about 1 ulp).
+__device__ __forceinline__ float rsqrt_f32(float v) { return __builtin_amdgcn_rsqf(v); }
+
+} // namespace dln

@@ -1,0 +1,95 @@
+// norm_internal.hpp -- host-side types shared by the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime.h>
+
+#include "norm.h"
+#include "norm_plan.hpp"
+
+namespace dln {
+
+// Launch parameter blocks (passed by value to kernels).
+struct FwdArgs {
+  const void *x;
+  const void *r;      // residual or nullptr
+  const void *w;
+  const void *b;      // bias or nullptr
+  void *y;
+  void *h;            // residual output or nullptr
+  float *mean;        // or nullptr
+  float *rstd;        // or nullptr
+  float *rowpart;     // split: [M][chunks][4]
+  int64_t M;
+  int32_t N;
+  int32_t nacc;       // accesses per row (N / epv)
+  int64_t chunks;     // split
+  int32_t chunk_acc;  // split: accesses per chunk
+  int32_t layernorm;  // 1 LayerNorm, 0 RMSNorm
+  float eps;
+  float inv_n;        // 1 / N
+};
+
+struct BwdArgs {
+  const void *x;
+  const void *dy;
+  const void *dh;     // or nullptr
+  const void *w;
+  const float *mean;  // or nullptr (recompute)
+  const float *rstd;  // or nullptr (recompute)
+  void *dx;
+  void *dr;           // separate dR buffer or nullptr
+  void *dw;           // split scheme with one row group: final dW written directly, else nullptr
+  void *db;           // as dw, for dB
+  float *colpart;     // [2][partials][N]
+  int64_t *header;    // workspace header: magic, partials, N
+  float *rowpart;     // split: [M][chunks][4]
+  float *stats;       // split without saved stats: [2][M]
+  int64_t M;
+  int32_t N;
+  int32_t nacc;
+  int64_t chunks;
+  int32_t chunk_acc;
+  int64_t partials;
+  int64_t row_groups;
+  int64_t rows_per_group;
+  int32_t layernorm;
+  int32_t want_db;
+  float eps;
+  float inv_n;
+};
+
+struct ReduceArgs {
+  const int64_t *header; // written by the fused pass: magic, partials, N
+  const float *colpart;  // [2][partials][N]
+  void *dw;
+  void *db;              // or nullptr
+  int64_t max_partials;  // partial rows the workspace can hold
+  int32_t N;
+};
+
+// Launchers (one translation unit per scheme family). Each returns NORM_OK or
+// NORM_ERR_UNSUPPORTED / NORM_ERR_HIP.
+norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                              hipStream_t s);
+norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
+                              hipStream_t s);
+norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                               hipStream_t s);
+norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
+                               hipStream_t s);
+norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s);
+norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+// First thread of the fused backward pass records the partial count for the reduction.
+__device__ __forceinline__ void write_ws_header(int64_t *h, int64_t partials, int64_t N) {
+  if (h && blockIdx.x == 0 && threadIdx.x == 0) {
+    h[0] = kWsMagic;
+    h[1] = partials;
+    h[2] = N;
+  }
+}
+
+} // namespace dln

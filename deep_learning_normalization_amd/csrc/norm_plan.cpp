@@ -1,0 +1,363 @@
+// norm_plan.cpp -- shape dispatcher and argument checks (host only, no HIP).
+//
+// Scheme choice follows the method's split between short and long reductions (web page
+// "PyTorch atinge desempenho SOTA em normalização com torch.compile", matsubara.tec.br,
+// para. 5: rows of about a thousand elements or fewer are reduced whole, without a loop; para. 6:
+// very large shapes are their own class; paras. 9 and 11: the number of rows each block sums into
+// the workspace trades parallelism against workspace traffic):
+//   N <= 1024                       -> wave scheme (one row per wavefront, registers only)
+//   row fits a team's registers      -> block scheme (one row per team of wavefronts)
+//   otherwise                        -> split scheme (a row spread over several workgroups)
+// The persistent grid size sets how many partial rows the backward writes (its SPLIT_SIZE).
+#include "norm_plan.hpp"
+
+#include <cmath>
+
+namespace dln {
+namespace {
+
+Tuning g_tuning;
+
+constexpr int64_t kMaxN = 2147483647;   // row length fits a 32-bit int
+constexpr int64_t kMaxGrid = 2147483647; // workgroups per launch
+constexpr int kWaveThreads = 256;        // wave scheme: four one-wave teams per workgroup
+constexpr int kSplitThreads = 256;
+constexpr int kWaveMaxRow = 1024;        // wave scheme for rows up to this many elements
+constexpr int kBlockTeamTarget = 512;    // preferred largest team for the block scheme
+
+int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+bool valid_kind(int k) { return k == NORM_LAYERNORM || k == NORM_RMSNORM; }
+bool valid_dtype(int d) { return d == NORM_F32 || d == NORM_BF16; }
+int vec_epv(norm_dtype_t d) { return d == NORM_F32 ? 4 : 8; }
+size_t elem_size(int d) { return d == NORM_F32 ? 4 : 2; }
+int lb_of(int threads) { return threads <= 256 ? 256 : threads <= 512 ? 512 : 1024; }
+
+// Compiled kernel shapes (must match the menus in the kernel sources).
+bool wave_menu(bool vec, int vpt, int rows) {
+  if (!vec) return rows == 1 && (vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16);
+  switch (vpt) {
+  case 1:
+  case 2: return rows == 1 || rows == 2 || rows == 4;
+  case 4: return rows == 1 || rows == 2;
+  case 8: return rows == 1;
+  default: return false;
+  }
+}
+
+bool block_menu(bool vec, int vpt, int rows, int lb) {
+  if (!vec) return lb == 1024 && rows == 1 && (vpt == 4 || vpt == 8);
+  switch (lb) {
+  case 256:
+    return (vpt == 1 && (rows == 1 || rows == 2 || rows == 4)) ||
+           (vpt == 2 && (rows == 1 || rows == 2)) || (vpt == 4 && rows == 1) ||
+           (vpt == 8 && rows == 1);
+  case 512:
+    return (vpt == 1 && (rows == 1 || rows == 2)) || (vpt == 2 && (rows == 1 || rows == 2)) ||
+           (vpt == 4 && rows == 1);
+  case 1024:
+    return (vpt == 1 && (rows == 1 || rows == 2)) || (vpt == 2 && rows == 1);
+  default: return false;
+  }
+}
+
+// Register budget: a 1024-thread workgroup leaves 128 VGPRs per lane, 512 threads 256.
+bool block_fits_registers(bool vec, int vpt, int rows, int lb) {
+  if (!vec) return true; // element-wise: at most 16 floats per array
+  const int slots = vpt * rows;
+  if (lb >= 1024) return slots <= 2;
+  if (lb >= 512) return slots <= 4;
+  return slots <= 8;
+}
+
+bool split_fwd_menu(bool vec, int vpt) { return vec ? (vpt == 1 || vpt == 2 || vpt == 4) : vpt == 8; }
+bool split_bwd_menu(bool vec, int vpt, int rows) {
+  if (!vec) return vpt == 8 && rows == 1;
+  switch (vpt) {
+  case 1:
+  case 2: return rows == 1 || rows == 2 || rows == 4;
+  case 4: return rows == 1 || rows == 2;
+  default: return false;
+  }
+}
+
+} // namespace
+
+const Tuning &tuning() { return g_tuning; }
+
+norm_status_t set_tuning(norm_tune_t key, int64_t v) {
+  switch (key) {
+  case NORM_TUNE_SCHEME:
+    if (v != -1 && v != NORM_SCHEME_WAVE && v != NORM_SCHEME_BLOCK && v != NORM_SCHEME_SPLIT)
+      return NORM_ERR_INVALID_ARG;
+    g_tuning.scheme = (int)v;
+    return NORM_OK;
+  case NORM_TUNE_GRID_PER_CU:
+    if (v != -1 && (v < 1 || v > 64)) return NORM_ERR_INVALID_ARG;
+    g_tuning.grid_per_cu = (int)v;
+    return NORM_OK;
+  case NORM_TUNE_ROWS_PER_ITER:
+    if (v != -1 && v != 1 && v != 2 && v != 4) return NORM_ERR_INVALID_ARG;
+    g_tuning.rows = (int)v;
+    return NORM_OK;
+  case NORM_TUNE_TEAM_THREADS:
+    if (v != -1 && (v < 64 || v > 1024 || v % 64 != 0)) return NORM_ERR_INVALID_ARG;
+    g_tuning.team_threads = (int)v;
+    return NORM_OK;
+  case NORM_TUNE_SPLIT_CHUNK:
+    if (v != -1 && (v < 1 || v > kMaxN)) return NORM_ERR_INVALID_ARG;
+    g_tuning.split_chunk = v;
+    return NORM_OK;
+  case NORM_TUNE_ROW_GROUPS:
+    if (v != -1 && v < 1) return NORM_ERR_INVALID_ARG;
+    g_tuning.row_groups = v;
+    return NORM_OK;
+  default: return NORM_ERR_INVALID_ARG;
+  }
+}
+
+norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
+                        int64_t N, int residual, int aligned, int cu, const Tuning &t,
+                        Plan *out) {
+  (void)residual;
+  if (!out || !valid_kind(kind) || !valid_dtype(dtype) ||
+      (pass != NORM_PASS_FWD && pass != NORM_PASS_BWD) || M < 0 || N <= 0 || N > kMaxN ||
+      cu <= 0)
+    return NORM_ERR_INVALID_ARG;
+  Plan p;
+  const bool bwd = pass == NORM_PASS_BWD;
+  const int ev = vec_epv(dtype);
+  p.vector = (aligned && N % ev == 0) ? 1 : 0;
+  p.epv = p.vector ? ev : 1;
+  const bool vec = p.vector != 0;
+  const int64_t nacc = N / p.epv;
+  const int64_t Mm = M > 0 ? M : 1; // M == 0 launches nothing; size as one row
+
+  int scheme = t.scheme;
+  if (scheme == NORM_SCHEME_AUTO) {
+    if (N <= kWaveMaxRow)
+      scheme = NORM_SCHEME_WAVE;
+    else if (nacc <= (vec ? 2048 : 8192))
+      scheme = NORM_SCHEME_BLOCK;
+    else
+      scheme = NORM_SCHEME_SPLIT;
+  }
+  p.scheme = scheme;
+
+  if (scheme == NORM_SCHEME_WAVE) {
+    static const int menu[] = {1, 2, 4, 8, 16};
+    int vpt = 0;
+    for (int v : menu)
+      if (64LL * v >= nacc && wave_menu(vec, v, 1)) {
+        vpt = v;
+        break;
+      }
+    if (!vpt) return NORM_ERR_UNSUPPORTED;
+    int rows = t.rows > 0 ? t.rows : 1;
+    if (!wave_menu(vec, vpt, rows)) rows = 1;
+    p.vpt = vpt;
+    p.rows = rows;
+    p.threads = kWaveThreads;
+    p.lb = kWaveThreads;
+    p.team_threads = 64;
+    const int64_t groups = cdiv(Mm, (int64_t)(kWaveThreads / 64) * rows);
+    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (bwd ? 2 : 8);
+    p.grid = groups < cu * gpc ? groups : cu * gpc;
+  } else if (scheme == NORM_SCHEME_BLOCK) {
+    static const int vmenu[] = {1, 2, 4, 8};
+    static const int smenu[] = {4, 8};
+    const int *menu = vec ? vmenu : smenu;
+    const int nmenu = vec ? 4 : 2;
+    const int want_rows = t.rows > 0 ? t.rows : 1;
+    int vpt = 0, tt = 0, rows = 1, lb_pick = 1024;
+    // pass 0: the team size override if one is set, else the preferred team size;
+    // pass 1: any team size up to 1024 (an override that cannot hold the row is ignored)
+    for (int pass_i = 0; pass_i < 2 && !vpt; ++pass_i) {
+      const bool use_override = pass_i == 0 && t.team_threads > 0;
+      for (int i = 0; i < nmenu && !vpt; ++i) {
+        const int v = menu[i];
+        int cand = (int)(cdiv(cdiv(nacc, v), 64) * 64);
+        if (use_override) {
+          if ((int64_t)t.team_threads * v < nacc) continue;
+          cand = t.team_threads;
+        }
+        const int limit = (pass_i == 0 && !use_override) ? (vec ? kBlockTeamTarget : 1024) : 1024;
+        if (cand > limit) continue;
+        const int lb = vec ? lb_of(cand) : 1024;
+        int r = want_rows;
+        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, v, r, lb)) r = 1;
+        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, v, r, lb)) continue;
+        vpt = v;
+        tt = cand;
+        rows = r;
+        lb_pick = lb;
+      }
+    }
+    if (!vpt) return NORM_ERR_UNSUPPORTED;
+    p.vpt = vpt;
+    p.rows = rows;
+    p.team_threads = tt;
+    p.threads = tt;
+    p.lb = lb_pick;
+    const int64_t groups = cdiv(Mm, rows);
+    const int64_t per_cu_threads = bwd ? 1024 : 2048;
+    const int64_t gpc_default = per_cu_threads / p.threads > 0 ? per_cu_threads / p.threads : 1;
+    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : gpc_default;
+    p.grid = groups < cu * gpc ? groups : cu * gpc;
+  } else if (scheme == NORM_SCHEME_SPLIT) {
+    int vpt = vec ? 4 : 8;
+    if (t.split_chunk > 0 && vec) { // the element-wise path has one chunk size
+      const int64_t per = (int64_t)kSplitThreads * p.epv;
+      if (t.split_chunk % per) return NORM_ERR_UNSUPPORTED;
+      vpt = (int)(t.split_chunk / per);
+    }
+    if (!split_fwd_menu(vec, vpt)) return NORM_ERR_UNSUPPORTED;
+    const int64_t chunk_acc = (int64_t)kSplitThreads * vpt;
+    p.vpt = vpt;
+    p.threads = kSplitThreads;
+    p.lb = kSplitThreads;
+    p.team_threads = kSplitThreads;
+    p.chunks = cdiv(nacc, chunk_acc);
+    p.chunk_elems = chunk_acc * p.epv;
+    if (Mm * p.chunks > kMaxGrid) return NORM_ERR_UNSUPPORTED;
+    if (!bwd) {
+      p.rows = 1;
+      p.grid = Mm * p.chunks;
+    } else {
+      int64_t G = t.row_groups > 0 ? t.row_groups : cdiv(cu, p.chunks);
+      if (G < 1) G = 1;
+      if (G > Mm) G = Mm;
+      const int64_t rpg = cdiv(Mm, G);
+      G = cdiv(Mm, rpg);
+      int rows = t.rows > 0 ? t.rows : (vpt >= 4 ? 2 : 4);
+      if (!split_bwd_menu(vec, vpt, rows)) rows = 1;
+      if (!split_bwd_menu(vec, vpt, rows)) return NORM_ERR_UNSUPPORTED;
+      p.rows = rows;
+      p.row_groups = G;
+      p.rows_per_group = rpg;
+      p.grid = G * p.chunks;
+    }
+  } else {
+    return NORM_ERR_INVALID_ARG;
+  }
+  if (p.chunk_elems == 0) p.chunk_elems = N;
+
+  size_t off = 0;
+  if (bwd) {
+    p.partials = scheme == NORM_SCHEME_SPLIT ? p.row_groups : p.grid;
+    p.off_header = 0;
+    p.off_colpart = kWsHeaderBytes;
+    off = align256(kWsHeaderBytes + (size_t)2 * (size_t)p.partials * (size_t)N * 4);
+    if (scheme == NORM_SCHEME_SPLIT) {
+      p.off_rowpart = off;
+      off = align256(off + (size_t)Mm * (size_t)p.chunks * 4 * 4);
+      p.off_stats = off;
+      off = align256(off + (size_t)2 * (size_t)Mm * 4);
+    }
+  } else if (scheme == NORM_SCHEME_SPLIT) {
+    p.off_rowpart = 0;
+    off = align256((size_t)Mm * (size_t)p.chunks * 4 * 4);
+  }
+  p.ws_bytes = off;
+  *out = p;
+  return NORM_OK;
+}
+
+norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
+                              int64_t N, int residual, int cu, const Tuning &t, size_t *bytes) {
+  if (!bytes) return NORM_ERR_INVALID_ARG;
+  // Size for both pointer alignments. A tuning override may leave the element-wise variant
+  // without a kernel; a call with such pointers then fails with NORM_ERR_UNSUPPORTED anyway,
+  // so only the 16-byte variant has to plan successfully.
+  Plan p;
+  norm_status_t s = make_plan(kind, dtype, pass, M, N, residual, 1, cu, t, &p);
+  if (s != NORM_OK) return s;
+  size_t best = p.ws_bytes;
+  if (make_plan(kind, dtype, pass, M, N, residual, 0, cu, t, &p) == NORM_OK && p.ws_bytes > best)
+    best = p.ws_bytes;
+  *bytes = best;
+  return NORM_OK;
+}
+
+// ---- argument checks -----------------------------------------------------------------------
+
+namespace {
+
+struct Span {
+  const void *p;
+  size_t n;
+};
+
+bool overlap(Span a, Span b) {
+  if (!a.p || !b.p || !a.n || !b.n) return false;
+  const uintptr_t x = (uintptr_t)a.p, y = (uintptr_t)b.p;
+  return x < y + b.n && y < x + a.n;
+}
+
+// Every output must be disjoint from every input and from every other output.
+bool disjoint(const Span *in, int nin, const Span *outs, int nout) {
+  for (int i = 0; i < nout; ++i) {
+    for (int j = 0; j < nin; ++j)
+      if (overlap(outs[i], in[j])) return false;
+    for (int j = i + 1; j < nout; ++j)
+      if (overlap(outs[i], outs[j])) return false;
+  }
+  return true;
+}
+
+bool sizes_ok(int64_t M, int64_t N) {
+  if (M < 0 || N <= 0 || N > kMaxN) return false;
+  return M <= (INT64_MAX / 16) / N;
+}
+
+} // namespace
+
+norm_status_t check_fwd(const FwdCheck &c) {
+  if (!valid_kind(c.kind) || !valid_dtype(c.dtype)) return NORM_ERR_INVALID_ARG;
+  if (!sizes_ok(c.M, c.N)) return NORM_ERR_INVALID_ARG;
+  if (!(std::isfinite(c.eps) && c.eps >= 0.0f)) return NORM_ERR_INVALID_ARG;
+  if (c.kind == NORM_RMSNORM && (c.B || c.mean)) return NORM_ERR_INVALID_ARG;
+  if ((c.R != nullptr) != (c.H != nullptr)) return NORM_ERR_INVALID_ARG;
+  if (!c.W) return NORM_ERR_INVALID_ARG;
+  if (c.M == 0) return NORM_OK;
+  if (!c.X || !c.Y) return NORM_ERR_INVALID_ARG;
+  const size_t s = elem_size(c.dtype);
+  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * s, m = (size_t)c.M * 4;
+  const Span in[] = {{c.X, mn}, {c.R, mn}, {c.W, n}, {c.B, n}};
+  const Span outs[] = {{c.Y, mn}, {c.H, mn}, {c.mean, m}, {c.rstd, m}, {c.ws, c.ws_bytes}};
+  if (!disjoint(in, 4, outs, 5)) return NORM_ERR_INVALID_ARG;
+  return NORM_OK;
+}
+
+norm_status_t check_bwd(const BwdCheck &c) {
+  if (!valid_kind(c.kind) || !valid_dtype(c.dtype)) return NORM_ERR_INVALID_ARG;
+  if (!sizes_ok(c.M, c.N)) return NORM_ERR_INVALID_ARG;
+  if (c.need_dx) {
+    if (!(std::isfinite(c.eps) && c.eps >= 0.0f)) return NORM_ERR_INVALID_ARG;
+    if (c.kind == NORM_RMSNORM && c.mean) return NORM_ERR_INVALID_ARG;
+    if (c.kind == NORM_LAYERNORM && ((c.mean == nullptr) != (c.rstd == nullptr)))
+      return NORM_ERR_INVALID_ARG;
+    if (!c.W) return NORM_ERR_INVALID_ARG;
+  }
+  if (c.need_dw) {
+    if (!c.dW) return NORM_ERR_INVALID_ARG;
+    if (c.kind == NORM_RMSNORM && c.dB) return NORM_ERR_INVALID_ARG;
+  }
+  if (c.M == 0) return NORM_OK;
+  if (c.need_dx && (!c.X || !c.dY || !c.dX)) return NORM_ERR_INVALID_ARG;
+  const size_t s = elem_size(c.dtype);
+  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * s, m = (size_t)c.M * 4;
+  const void *dr = c.dR == c.dX ? nullptr : c.dR; // dR may alias dX
+  const Span in[] = {{c.X, mn}, {c.dY, mn}, {c.dH, mn}, {c.W, n}, {c.mean, m}, {c.rstd, m}};
+  const Span outs[] = {{c.dX, mn}, {dr, mn}, {c.dW, n}, {c.dB, n}, {c.ws, c.ws_bytes}};
+  if (!disjoint(in, 6, outs, 5)) return NORM_ERR_INVALID_ARG;
+  return NORM_OK;
+}
+
+bool all_aligned16(const void *const *ptrs, int n) {
+  for (int i = 0; i < n; ++i)
+    if (ptrs[i] && ((uintptr_t)ptrs[i] & 15u)) return false;
+  return true;
+}
+
+} // namespace dln

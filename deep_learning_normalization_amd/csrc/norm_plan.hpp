@@ -1,0 +1,93 @@
+// norm_plan.hpp -- host logic of the norm library that needs no GPU: the shape dispatcher
+// (launch plans and workspace layout) and the argument checks. Compiles with any C++17
+// compiler; no HIP header is included.
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include "norm.h"
+
+namespace dln {
+
+// A launch plan: which scheme and kernel shape a (kind, pass, M, N, dtype) call uses, and
+// where its workspace regions live.
+struct Plan {
+  int scheme = NORM_SCHEME_BLOCK;
+  int vector = 1;          // 16-byte accesses (1) or element-wise (0)
+  int epv = 8;             // elements per access
+  int threads = 256;       // workgroup size
+  int lb = 256;            // compiled workgroup-size bound of the kernel (>= threads)
+  int team_threads = 256;  // threads sharing a row (64 for the wave scheme)
+  int vpt = 1;             // accesses per thread per row (per chunk for split)
+  int rows = 1;            // rows a team holds at once
+  int64_t grid = 1;        // workgroups of the main (persistent) kernel
+  int64_t chunks = 1;      // split: chunks per row
+  int64_t chunk_elems = 0; // split: elements per chunk
+  int64_t row_groups = 1;  // split backward: row groups
+  int64_t rows_per_group = 0; // split backward: rows per group
+  int64_t partials = 0;    // rows of fp32 column partials (backward)
+  // workspace layout (bytes from the workspace start; every region 256-byte aligned)
+  size_t off_header = 0;   // backward: kWsHeaderBytes describing the partials (see below)
+  size_t off_colpart = 0;  // [2][partials][N] fp32: dW partials then dB partials
+  size_t off_rowpart = 0;  // split: [M][chunks][4] fp32 per-chunk row partials
+  size_t off_stats = 0;    // split backward without saved stats: [M] mean then [M] rstd
+  size_t ws_bytes = 0;
+};
+
+// The backward's fused pass writes this header at the start of its workspace so that the
+// column reduction (possibly a separate call) knows how many partial rows follow.
+constexpr size_t kWsHeaderBytes = 256;
+constexpr int64_t kWsMagic = 0x4E4F524D50415254LL; // "NORMPART"
+
+struct Tuning {
+  int scheme = NORM_SCHEME_AUTO;
+  int grid_per_cu = -1;
+  int rows = -1;
+  int team_threads = -1;
+  int64_t split_chunk = -1;
+  int64_t row_groups = -1;
+};
+
+const Tuning &tuning();
+norm_status_t set_tuning(norm_tune_t key, int64_t value);
+
+norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
+                        int64_t N, int residual, int aligned, int cu_count, const Tuning &t,
+                        Plan *out);
+
+// Largest workspace any pointer alignment can need for this call on cu_count CUs.
+norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
+                              int64_t N, int residual, int cu_count, const Tuning &t,
+                              size_t *bytes);
+
+// Argument checks (no device access). They return NORM_OK or NORM_ERR_INVALID_ARG.
+struct FwdCheck {
+  int kind, dtype;
+  const void *X, *R, *W, *B;
+  float eps;
+  int64_t M, N;
+  void *Y, *H;
+  float *mean, *rstd;
+  void *ws;
+  size_t ws_bytes;
+};
+norm_status_t check_fwd(const FwdCheck &c);
+
+struct BwdCheck {
+  int kind, dtype;
+  const void *X, *dY, *dH, *W;
+  const float *mean, *rstd;
+  float eps;
+  int64_t M, N;
+  void *dX, *dR, *dW, *dB;
+  void *ws;
+  size_t ws_bytes;
+  int need_dx;  // stage 1 (fused pass) is part of the call
+  int need_dw;  // stage 2 (column reduction) is part of the call
+};
+norm_status_t check_bwd(const BwdCheck &c);
+
+bool all_aligned16(const void *const *ptrs, int n);
+
+} // namespace dln

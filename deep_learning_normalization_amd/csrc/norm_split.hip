@@ -1,0 +1,611 @@
+// norm_split.hip -- split-row scheme for rows too long for one workgroup's registers.
+//
+// A row is cut into chunks of chunk_acc accesses; each chunk belongs to one workgroup.
+//   forward : pass 1 writes per-chunk statistics (chunk mean, sum of squared deviations about
+//             it and the sum of those deviations for LayerNorm; sum of squares for RMSNorm);
+//             pass 2 combines the chunks of its row in a fixed order (the parallel-variance
+//             combination: the row mean from the chunk means, the squared deviation as the
+//             chunk sums plus count * (chunk mean - row mean)^2), re-reads its chunk and
+//             writes the output.
+//   backward: pass 1 walks a group of rows for one column chunk and writes, per (row, chunk),
+//             the partial sums g*(x - mean), g and x - mean; pass 2 combines them per row,
+//             re-reads the chunk, writes dX and accumulates the chunk's dW/dB column partials
+//             over the group; the partials of the row groups are reduced afterwards (or
+//             written directly when there is one group).
+// Pass 2 re-reads what pass 1 read; its order is arranged so that the most recently read data
+// comes back first (forward: block order reversed within each XCD; backward: same blocks,
+// rows in descending order), which is what the L2 and the memory-side cache still hold.
+//
+// Method (web page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
+// matsubara.tec.br): para. 6 names very large shapes as a regression class; paras. 8-10 give
+// the split reduction with a workspace of partial sums, without atomics, consolidated by an
+// extra reduction pass. The page "Towards Free Normalization: Fusing Normalization into GEMM
+// and Attention Kernels" (brifing.si), item 4, names spreading one row's norm over several
+// thread blocks (multi-CTA).
+#include "norm_device.hpp"
+#include "norm_internal.hpp"
+
+namespace dln {
+
+constexpr int SPLIT_LB = 256;
+
+// Bijection on [0, nb) that keeps b % 8 (the XCD a block is dispatched to) and reverses the
+// order of the blocks within each XCD.
+__device__ __forceinline__ int64_t reverse_within_xcd(int64_t b, int64_t nb) {
+  const int64_t x = b & 7, i = b >> 3;
+  const int64_t nx = (nb - x + 7) >> 3;
+  return ((nx - 1 - i) << 3) + x;
+}
+
+// Elements in chunk c of a row of nacc accesses.
+__device__ __forceinline__ float chunk_count(int64_t c, int32_t chunk_acc, int32_t nacc, int E) {
+  const int64_t left = (int64_t)nacc - c * chunk_acc;
+  return (float)((left < chunk_acc ? left : chunk_acc) * E);
+}
+
+// Per-(row, chunk) partials, RP floats each:
+//   forward  LayerNorm: [0] chunk mean m_c, [1] sum (x - m_c)^2, [2] sum (x - m_c)
+//            RMSNorm  : [0] sum x^2
+//   backward LayerNorm: [0] sum g*(x - m), [1] sum g, [2] sum (x - m)   (m: the row's mean)
+//            RMSNorm  : [0] sum g*x
+constexpr int RP = 4;
+
+// Combine the chunk statistics of one row (rp = rowpart + row * C * RP). LayerNorm returns the
+// mean as shift + delta, with shift = chunk 0's mean: every chunk then contributes small,
+// accurately representable terms, n_c (m_c - shift) + sum(x - m_c) to the mean correction
+// and sum (x - m_c)^2 + 2 e_c sum(x - m_c) + n_c e_c^2, e_c = m_c - mean, to the squared
+// deviation (an exact regrouping of sum over the chunk of (x - mean)^2). All threads of the
+// workgroup call it.
+__device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, int32_t chunk_acc,
+                                                  int32_t nacc, int E, int layernorm,
+                                                  float inv_n, float eps, float *red, int &slot,
+                                                  float &shift, float &delta, float &rstd) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+  if (layernorm) {
+    shift = rp[0];
+    float s[1] = {0.0f};
+    for (int64_t c = tid; c < C; c += blockDim.x)
+      s[0] += chunk_count(c, chunk_acc, nacc, E) * (rp[RP * c] - shift) + rp[RP * c + 2];
+    team_sum<1>(s, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    delta = s[0] * inv_n;
+    float q[1] = {0.0f};
+    for (int64_t c = tid; c < C; c += blockDim.x) {
+      const float e = (rp[RP * c] - shift) - delta;
+      q[0] += rp[RP * c + 1] + 2.0f * e * rp[RP * c + 2] + chunk_count(c, chunk_acc, nacc, E) * e * e;
+    }
+    team_sum<1>(q, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    rstd = rsqrt_f32(fmaxf(q[0] * inv_n, 0.0f) + eps);
+  } else {
+    float q[1] = {0.0f};
+    for (int64_t c = tid; c < C; c += blockDim.x) q[0] += rp[RP * c];
+    team_sum<1>(q, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    shift = 0.0f;
+    delta = 0.0f;
+    rstd = rsqrt_f32(q[0] * inv_n + eps);
+  }
+}
+
+// ---- forward pass 1: chunk statistics ---------------------------------------------------
+
+template <typename T, bool VEC, int VPT, bool RESID>
+__global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
+  using A = Acc<T, VEC>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  __shared__ float red[RED_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+  const int64_t C = a.chunks;
+  const int64_t row = (int64_t)blockIdx.x / C;
+  const int64_t c = (int64_t)blockIdx.x - row * C;
+  const int64_t acc0 = c * a.chunk_acc;
+  const int64_t left = (int64_t)a.nacc - acc0;
+  const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
+  const int64_t base = row * (int64_t)a.N + acc0 * E;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + base;
+  const T *__restrict__ Rr = RESID ? static_cast<const T *>(a.r) + base : nullptr;
+  T *__restrict__ H = RESID ? static_cast<T *>(a.h) + base : nullptr;
+
+  float x[VPT][E];
+  {
+    raw rx[VPT], rr[RESID ? VPT : 1];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * SPLIT_LB;
+      rx[k] = A::zero();
+      if (RESID) rr[k] = A::zero();
+      if (v < nin) {
+        rx[k] = A::ld(X + (int64_t)v * E);
+        if (RESID) rr[k] = A::ld(Rr + (int64_t)v * E);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      A::unpack(rx[k], x[k]);
+      if (RESID) {
+        float f[E];
+        A::unpack(rr[k], f);
+#pragma unroll
+        for (int e = 0; e < E; ++e) f[e] += x[k][e];
+        const raw hp = A::pack(f);
+        A::unpack(hp, x[k]);
+        const int v = tid + k * SPLIT_LB;
+        if (v < nin) A::st(H + (int64_t)v * E, hp);
+      }
+    }
+  }
+  const float n_c = (float)(nin * E);
+  float *out = a.rowpart + (row * C + c) * RP;
+  int slot = 0;
+  if (a.layernorm) {
+    float s[1] = {0.0f};
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) s[0] += x[k][e];
+    team_sum<1>(s, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    const float mc = s[0] / n_c;
+    float qc[2] = {0.0f, 0.0f};
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const bool in = tid + k * SPLIT_LB < nin;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float d = in ? x[k][e] - mc : 0.0f;
+        qc[0] += d * d;
+        qc[1] += d;
+      }
+    }
+    team_sum<2>(qc, red, slot, waves, 0, wave, lane);
+    if (tid == 0) {
+      out[0] = mc;
+      out[1] = qc[0];
+      out[2] = qc[1];
+    }
+  } else {
+    float q[1] = {0.0f};
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) q[0] += x[k][e] * x[k][e];
+    team_sum<1>(q, red, slot, waves, 0, wave, lane);
+    if (tid == 0) out[0] = q[0];
+  }
+}
+
+// ---- forward pass 2: combine, normalise the chunk ---------------------------------------
+
+template <typename T, bool VEC, int VPT>
+__global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
+  using A = Acc<T, VEC>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  __shared__ float red[RED_FLOATS];
+  const int tid = threadIdx.x;
+  const int64_t C = a.chunks;
+  const int64_t b = reverse_within_xcd(blockIdx.x, gridDim.x);
+  const int64_t row = b / C;
+  const int64_t c = b - row * C;
+  const int64_t acc0 = c * a.chunk_acc;
+  const int64_t left = (int64_t)a.nacc - acc0;
+  const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
+  const int64_t base = row * (int64_t)a.N + acc0 * E;
+  // the norm's input: the stored h for the residual variant, else X
+  const T *__restrict__ S = static_cast<const T *>(a.r ? a.h : a.x) + base;
+  const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
+  const T *__restrict__ Bb = a.b ? static_cast<const T *>(a.b) + acc0 * E : nullptr;
+  T *__restrict__ Y = static_cast<T *>(a.y) + base;
+
+  raw rx[VPT], rw[VPT], rb[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = tid + k * SPLIT_LB;
+    rx[k] = A::zero();
+    rw[k] = A::zero();
+    rb[k] = A::zero();
+    if (v < nin) {
+      rx[k] = A::ld_cached(S + (int64_t)v * E);
+      rw[k] = A::ld_cached(W + (int64_t)v * E);
+      if (Bb) rb[k] = A::ld_cached(Bb + (int64_t)v * E);
+    }
+  }
+  int slot = 0;
+  float shift, delta, rstd;
+  combine_row_stats(a.rowpart + row * C * RP, C, a.chunk_acc, a.nacc, E, a.layernorm, a.inv_n,
+                    a.eps, red, slot, shift, delta, rstd);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = tid + k * SPLIT_LB;
+    if (v < nin) {
+      float xf[E], wf[E], bf[E], y[E];
+      A::unpack(rx[k], xf);
+      A::unpack(rw[k], wf);
+      A::unpack(rb[k], bf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) y[e] = ((xf[e] - shift) - delta) * rstd * wf[e] + bf[e];
+      A::st(Y + (int64_t)v * E, A::pack(y));
+    }
+  }
+  if (c == 0 && tid == 0) {
+    if (a.mean) a.mean[row] = shift + delta;
+    if (a.rstd) a.rstd[row] = rstd;
+  }
+}
+
+// ---- backward: statistics when the forward's were not kept ------------------------------
+
+__global__ __launch_bounds__(SPLIT_LB) void split_finalize_stats_kernel(BwdArgs a, int E) {
+  __shared__ float red[RED_FLOATS];
+  const int64_t row = blockIdx.x;
+  int slot = 0;
+  float shift, delta, rstd;
+  combine_row_stats(a.rowpart + row * a.chunks * RP, a.chunks, a.chunk_acc, a.nacc, E,
+                    a.layernorm, a.inv_n, a.eps, red, slot, shift, delta, rstd);
+  if (threadIdx.x == 0) {
+    a.stats[row] = shift + delta;
+    a.stats[a.M + row] = rstd;
+  }
+}
+
+// ---- backward pass 1: row partials ---------------------------------------------------------
+
+template <typename T, bool VEC, int VPT, int ROWS, bool LN>
+__global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) {
+  using A = Acc<T, VEC>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  __shared__ float red[RED_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+  const int64_t C = a.chunks;
+  const int64_t g = (int64_t)blockIdx.x / C;
+  const int64_t c = (int64_t)blockIdx.x - g * C;
+  const int64_t acc0 = c * a.chunk_acc;
+  const int64_t left = (int64_t)a.nacc - acc0;
+  const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
+  const int64_t N = a.N;
+  const int64_t r_begin = g * a.rows_per_group;
+  const int64_t r_end = r_begin + a.rows_per_group < a.M ? r_begin + a.rows_per_group : a.M;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + acc0 * E;
+  const T *__restrict__ DY = static_cast<const T *>(a.dy) + acc0 * E;
+  const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
+  const float *mean_p = a.rstd ? a.mean : a.stats;
+
+  float w[VPT][E];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = tid + k * SPLIT_LB;
+    raw rw = A::zero();
+    if (v < nin) rw = A::ld_cached(W + (int64_t)v * E);
+    A::unpack(rw, w[k]);
+  }
+  int slot = 0;
+  for (int64_t row0 = r_begin; row0 < r_end; row0 += ROWS) {
+    raw rx[ROWS][VPT], rdy[ROWS][VPT];
+    float m[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = row0 + r < r_end;
+      const int64_t rowc = rv ? row0 + r : r_end - 1;
+      m[r] = (LN && mean_p) ? mean_p[rowc] : 0.0f;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = tid + k * SPLIT_LB;
+        rx[r][k] = A::zero();
+        rdy[r][k] = A::zero();
+        if (rv && v < nin) {
+          rx[r][k] = A::ld(X + (row0 + r) * N + (int64_t)v * E);
+          rdy[r][k] = A::ld(DY + (row0 + r) * N + (int64_t)v * E);
+        }
+      }
+    }
+    constexpr int NV = LN ? 3 * ROWS : ROWS;
+    float sums[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = row0 + r < r_end;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const bool in = rv && tid + k * SPLIT_LB < nin;
+        float xf[E], df[E];
+        A::unpack(rx[r][k], xf);
+        A::unpack(rdy[r][k], df);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = in ? xf[e] - m[r] : 0.0f;
+          const float gg = df[e] * w[k][e];
+          sums[r] += gg * d;
+          if constexpr (LN) {
+            sums[ROWS + r] += gg;
+            sums[2 * ROWS + r] += d;
+          }
+        }
+      }
+    }
+    team_sum<NV>(sums, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    if (tid == 0) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        if (row0 + r < r_end) {
+          float *out = a.rowpart + ((row0 + r) * C + c) * RP;
+          out[0] = sums[r];
+          if constexpr (LN) {
+            out[1] = sums[ROWS + r];
+            out[2] = sums[2 * ROWS + r];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---- backward pass 2: dX and the column partials -------------------------------------------
+
+template <typename T, bool VEC, int VPT, int ROWS, bool LN>
+__global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
+  using A = Acc<T, VEC>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  __shared__ float red[RED_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
+  const int64_t C = a.chunks;
+  const int64_t g = (int64_t)blockIdx.x / C;
+  const int64_t c = (int64_t)blockIdx.x - g * C;
+  const int64_t acc0 = c * a.chunk_acc;
+  const int64_t left = (int64_t)a.nacc - acc0;
+  const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
+  const int64_t N = a.N;
+  const int64_t r_begin = g * a.rows_per_group;
+  const int64_t r_end = r_begin + a.rows_per_group < a.M ? r_begin + a.rows_per_group : a.M;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + acc0 * E;
+  const T *__restrict__ DY = static_cast<const T *>(a.dy) + acc0 * E;
+  const T *__restrict__ DH = a.dh ? static_cast<const T *>(a.dh) + acc0 * E : nullptr;
+  const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
+  T *__restrict__ DX = static_cast<T *>(a.dx) + acc0 * E;
+  T *__restrict__ DR = a.dr ? static_cast<T *>(a.dr) + acc0 * E : nullptr;
+  const float *mean_p = a.rstd ? a.mean : a.stats;
+  const float *rstd_p = a.rstd ? a.rstd : a.stats + a.M;
+  if (!a.dw) write_ws_header(a.header, a.row_groups, N);
+
+  float w[VPT][E], accw[VPT][E], accb[LN ? VPT : 1][E];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = tid + k * SPLIT_LB;
+    raw rw = A::zero();
+    if (v < nin) rw = A::ld_cached(W + (int64_t)v * E);
+    A::unpack(rw, w[k]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      accw[k][e] = 0.0f;
+      if constexpr (LN) accb[k][e] = 0.0f;
+    }
+  }
+  int slot = 0;
+  const int64_t nrows = r_end - r_begin;
+  const int64_t iters = (nrows + ROWS - 1) / ROWS;
+  // rows in descending order: the last rows pass 1 read are re-read first
+  for (int64_t it = iters - 1; it >= 0; --it) {
+    const int64_t row0 = r_begin + it * ROWS;
+    raw rx[ROWS][VPT], rdy[ROWS][VPT];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = row0 + r < r_end;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = tid + k * SPLIT_LB;
+        rx[r][k] = A::zero();
+        rdy[r][k] = A::zero();
+        if (rv && v < nin) {
+          rx[r][k] = A::ld_cached(X + (row0 + r) * N + (int64_t)v * E);
+          rdy[r][k] = A::ld_cached(DY + (row0 + r) * N + (int64_t)v * E);
+        }
+      }
+    }
+    // combine the row partials of every chunk of these rows
+    constexpr int NV = LN ? 3 * ROWS : ROWS;
+    float sums[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int64_t rowc = row0 + r < r_end ? row0 + r : r_end - 1;
+      const float *rp = a.rowpart + rowc * C * RP;
+      for (int64_t cc = tid; cc < C; cc += blockDim.x) {
+        sums[r] += rp[RP * cc];
+        if constexpr (LN) {
+          sums[ROWS + r] += rp[RP * cc + 1];
+          sums[2 * ROWS + r] += rp[RP * cc + 2];
+        }
+      }
+    }
+    team_sum<NV>(sums, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int64_t row = row0 + r;
+      const bool rv = row < r_end;
+      const int64_t rowc = rv ? row : r_end - 1;
+      const float m = (LN && mean_p) ? mean_p[rowc] : 0.0f;
+      const float rstd = rstd_p[rowc];
+      const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
+      const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
+      const float c2 = LN ? rstd * (sums[r] - delta * sums[ROWS + r]) * a.inv_n
+                          : rstd * sums[r] * a.inv_n;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = tid + k * SPLIT_LB;
+        const bool in = rv && v < nin;
+        float xf[E], df[E], dx[E];
+        A::unpack(rx[r][k], xf);
+        A::unpack(rdy[r][k], df);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float xh = in ? ((xf[e] - m) - delta) * rstd : 0.0f;
+          dx[e] = rstd * (df[e] * w[k][e] - c1 - xh * c2);
+          accw[k][e] += df[e] * xh;
+          if constexpr (LN) accb[k][e] += df[e];
+        }
+        if (in) {
+          const int64_t off = row * N + (int64_t)v * E;
+          if (DH) {
+            float hf[E];
+            A::unpack(A::ld(DH + off), hf);
+#pragma unroll
+            for (int e = 0; e < E; ++e) dx[e] += hf[e];
+          }
+          const raw p = A::pack(dx);
+          A::st(DX + off, p);
+          if (DR) A::st(DR + off, p);
+        }
+      }
+    }
+  }
+  // column partials of this (row group, chunk), or the final dW/dB when the caller asked for
+  // them directly (only ever with a single row group)
+  if (a.dw) {
+    T *dw = static_cast<T *>(a.dw) + acc0 * E;
+    T *db = a.db ? static_cast<T *>(a.db) + acc0 * E : nullptr;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * SPLIT_LB;
+      if (v < nin) {
+        A::st(dw + (int64_t)v * E, A::pack(accw[k]));
+        if constexpr (LN)
+          if (db) A::st(db + (int64_t)v * E, A::pack(accb[k]));
+      }
+    }
+  } else {
+    float *pw = a.colpart + g * N + acc0 * E;
+    float *pb = a.colpart + (a.row_groups + g) * N + acc0 * E;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * SPLIT_LB;
+      if (v < nin) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          pw[(int64_t)v * E + e] = accw[k][e];
+          if constexpr (LN) pb[(int64_t)v * E + e] = accb[k][e];
+        }
+      }
+    }
+  }
+}
+
+// ---- launchers ---------------------------------------------------------------------------------
+
+namespace {
+
+#define DLN_SPLIT_FWD_MENU(X) X(1) X(2) X(4)
+#define DLN_SPLIT_BWD_MENU(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2)
+#define DLN_SPLIT_SCALAR_VPT 8
+
+template <typename T> norm_status_t split_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
+  const bool resid = a.r != nullptr;
+  bool found = false;
+  if (p.vector) {
+#define X(V)                                                                                    \
+  if (!found && p.vpt == V) {                                                                   \
+    found = true;                                                                               \
+    if (resid)                                                                                  \
+      hipLaunchKernelGGL((split_stats_kernel<T, true, V, true>), grid, block, 0, s, a);        \
+    else                                                                                        \
+      hipLaunchKernelGGL((split_stats_kernel<T, true, V, false>), grid, block, 0, s, a);       \
+    hipLaunchKernelGGL((split_norm_kernel<T, true, V>), grid, block, 0, s, a);                  \
+  }
+    DLN_SPLIT_FWD_MENU(X)
+#undef X
+  } else if (p.vpt == DLN_SPLIT_SCALAR_VPT) {
+    found = true;
+    constexpr int V = DLN_SPLIT_SCALAR_VPT;
+    if (resid)
+      hipLaunchKernelGGL((split_stats_kernel<T, false, V, true>), grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL((split_stats_kernel<T, false, V, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((split_norm_kernel<T, false, V>), grid, block, 0, s, a);
+  }
+  if (!found) return NORM_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+template <typename T, bool VEC, int V, int R>
+void split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid), block(SPLIT_LB);
+  if (a.layernorm) {
+    hipLaunchKernelGGL((split_bwd_partial_kernel<T, VEC, V, R, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((split_bwd_dx_kernel<T, VEC, V, R, true>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((split_bwd_partial_kernel<T, VEC, V, R, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((split_bwd_dx_kernel<T, VEC, V, R, false>), grid, block, 0, s, a);
+  }
+}
+
+template <typename T> norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
+  // statistics of the forward, when not supplied: chunk stats, then one combine per row
+  if (a.rstd == nullptr) {
+    FwdArgs f{};
+    f.x = a.x;
+    f.rowpart = a.rowpart;
+    f.M = a.M;
+    f.N = a.N;
+    f.nacc = a.nacc;
+    f.chunks = a.chunks;
+    f.chunk_acc = a.chunk_acc;
+    f.layernorm = a.layernorm;
+    f.eps = a.eps;
+    f.inv_n = a.inv_n;
+    const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
+    bool found = false;
+    if (p.vector) {
+#define X(V)                                                                                    \
+  if (!found && p.vpt == V) {                                                                   \
+    found = true;                                                                               \
+    hipLaunchKernelGGL((split_stats_kernel<T, true, V, false>), grid, block, 0, s, f);         \
+  }
+      DLN_SPLIT_FWD_MENU(X)
+#undef X
+    } else if (p.vpt == DLN_SPLIT_SCALAR_VPT) {
+      found = true;
+      hipLaunchKernelGGL((split_stats_kernel<T, false, DLN_SPLIT_SCALAR_VPT, false>), grid, block,
+                         0, s, f);
+    }
+    if (!found) return NORM_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(split_finalize_stats_kernel, dim3((unsigned)a.M), block, 0, s, a,
+                       p.epv);
+    if (hipGetLastError() != hipSuccess) return NORM_ERR_HIP;
+  }
+  bool found = false;
+  if (p.vector) {
+#define X(V, R)                                                                                 \
+  if (!found && p.vpt == V && p.rows == R) {                                                    \
+    found = true;                                                                               \
+    split_bwd_pair<T, true, V, R>(p, a, s);                                                     \
+  }
+    DLN_SPLIT_BWD_MENU(X)
+#undef X
+  } else if (p.vpt == DLN_SPLIT_SCALAR_VPT && p.rows == 1) {
+    found = true;
+    split_bwd_pair<T, false, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
+  }
+  if (!found) return NORM_ERR_UNSUPPORTED;
+  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+} // namespace
+
+norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                               hipStream_t s) {
+  return dtype == NORM_F32 ? split_fwd_typed<float>(p, a, s) : split_fwd_typed<bf16_bits>(p, a, s);
+}
+
+norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
+                               hipStream_t s) {
+  return dtype == NORM_F32 ? split_bwd_typed<float>(p, a, s) : split_bwd_typed<bf16_bits>(p, a, s);
+}
+
+} // namespace dln

@@ -1,0 +1,692 @@
+// norm_team.hip -- row-resident forward and fused backward kernels, and the column reduction.
+//
+// A "team" of threads owns one row at a time and keeps the whole row in registers:
+//   wave scheme : a team is one 64-lane wavefront; sums stay inside the wavefront (DPP), no LDS
+//                 and no barrier. Used for short rows.
+//   block scheme: a team is several wavefronts; wavefront sums meet in LDS behind one barrier.
+// Kernels are persistent: each workgroup walks row groups with a grid stride, so the weight
+// (and bias) of a thread's columns are loaded once and, in the backward, the dW/dB column sums
+// of all rows a workgroup visits accumulate in registers.
+//
+// Method (web page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
+// matsubara.tec.br):
+//   para. 3  -- forward: reduction along the contiguous dimension, then pointwise work;
+//   para. 5  -- short reduction dimensions are reduced without a loop, the row held on chip;
+//   para. 7  -- backward gradients dX, dW, dB;
+//   paras. 8-10 -- one fused pass produces dX and per-block partial column sums (no atomics;
+//               several rows per block), and a second pass consolidates the partials;
+//   para. 12 -- several rows in flight per team (the software-pipelining knob).
+// Memory: every [M, N] element moves through 16-byte coalesced accesses, exactly once per pass
+// (web page "Otimização de Performance de GPU: Maximizando Throughput para Treinamento e
+// Inferência de LLM", introl.com, sections on memory bandwidth and on kernel fusion), and all
+// arithmetic is fp32 (same page, section on mixed precision).
+#include "norm_device.hpp"
+#include "norm_internal.hpp"
+
+namespace dln {
+
+// Partial column sums of the backward are merged across the teams of a workgroup through
+// LDS in blocks of this many floats.
+constexpr int MERGE_FLOATS = 4096;
+
+struct TeamGeom {
+  int tt;       // threads per team
+  int team;     // team index in the workgroup
+  int t;        // thread index in the team
+  int teams;    // teams per workgroup
+  int waves;    // wavefronts per team
+  int wave0;    // first wavefront of this team in the workgroup
+  int wave;     // this thread's wavefront in the workgroup
+  int lane;
+};
+
+template <bool WAVE> __device__ __forceinline__ TeamGeom team_geom(int team_threads) {
+  TeamGeom g;
+  const int tid = threadIdx.x;
+  g.tt = WAVE ? 64 : team_threads;
+  g.team = tid / g.tt;
+  g.t = tid - g.team * g.tt;
+  g.teams = blockDim.x / g.tt;
+  g.waves = g.tt >> 6;
+  g.wave = tid >> 6;
+  g.wave0 = g.team * g.waves;
+  g.lane = tid & 63;
+  return g;
+}
+
+// ---- forward ------------------------------------------------------------------------------
+
+template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool RESID>
+__global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_threads) {
+  using A = Acc<T, VEC>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  __shared__ float red[RED_FLOATS];
+  const TeamGeom gm = team_geom<WAVE>(team_threads);
+  const int nacc = a.nacc;
+  const int64_t M = a.M;
+  const int64_t N = a.N;
+  const T *__restrict__ X = static_cast<const T *>(a.x);
+  const T *__restrict__ Rr = static_cast<const T *>(a.r);
+  const T *__restrict__ W = static_cast<const T *>(a.w);
+  const T *__restrict__ Bb = static_cast<const T *>(a.b);
+  T *__restrict__ Y = static_cast<T *>(a.y);
+  T *__restrict__ H = static_cast<T *>(a.h);
+
+  float w[VPT][E], b[VPT][E];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = gm.t + k * gm.tt;
+    raw rw = A::zero(), rb = A::zero();
+    if (v < nacc) {
+      rw = A::ld_cached(W + (int64_t)v * E);
+      if (Bb) rb = A::ld_cached(Bb + (int64_t)v * E);
+    }
+    A::unpack(rw, w[k]);
+    A::unpack(rb, b[k]);
+  }
+
+  const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
+  int slot = 0;
+  for (int64_t g = blockIdx.x; g * rows_per_group < M; g += gridDim.x) {
+    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
+    float x[ROWS][VPT][E];
+    {
+      raw rx[ROWS][VPT];
+      raw rr[ROWS][RESID ? VPT : 1];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const bool rv = row0 + r < M;
+        const int64_t base = (row0 + r) * N;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          const int v = gm.t + k * gm.tt;
+          rx[r][k] = A::zero();
+          if (RESID) rr[r][k] = A::zero();
+          if (rv && v < nacc) {
+            rx[r][k] = A::ld(X + base + (int64_t)v * E);
+            if (RESID) rr[r][k] = A::ld(Rr + base + (int64_t)v * E);
+          }
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const bool rv = row0 + r < M;
+        const int64_t base = (row0 + r) * N;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          A::unpack(rx[r][k], x[r][k]);
+          if (RESID) {
+            // h = R + X in fp32, rounded once to the storage type; the norm sees the rounded h
+            float f[E];
+            A::unpack(rr[r][k], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) f[e] += x[r][k][e];
+            const raw hp = A::pack(f);
+            A::unpack(hp, x[r][k]);
+            const int v = gm.t + k * gm.tt;
+            if (rv && v < nacc) A::st(H + base + (int64_t)v * E, hp);
+          }
+        }
+      }
+    }
+
+    // Statistics. LayerNorm: a first pass gives mean1; a second pass sums d = x - mean1 and
+    // d^2. x - mean1 is exact for rows whose values sit near their mean, so sum(d)/N is an
+    // accurate correction even when |mean| >> std and mean1 itself is off by many fp32 ulps of
+    // the variance scale; the normalised value is formed as (x - mean1) - delta.
+    float mean1[ROWS], delta[ROWS], rstd[ROWS];
+    if (a.layernorm) {
+      float s[ROWS];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc += x[r][k][e];
+        s[r] = acc;
+      }
+      team_sum<ROWS>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+      slot ^= 1;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) mean1[r] = mul_rn(s[r], a.inv_n);
+      float qc[2 * ROWS];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float q = 0.0f, c = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k) {
+          const bool in = gm.t + k * gm.tt < nacc;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float d = in ? x[r][k][e] - mean1[r] : 0.0f;
+            q += d * d;
+            c += d;
+          }
+        }
+        qc[r] = q;
+        qc[ROWS + r] = c;
+      }
+      team_sum<2 * ROWS>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+      slot ^= 1;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        delta[r] = qc[ROWS + r] * a.inv_n;
+        const float var = fmaxf(qc[r] * a.inv_n - delta[r] * delta[r], 0.0f);
+        rstd[r] = rsqrt_f32(var + a.eps);
+      }
+    } else {
+      float q[ROWS];
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < VPT; ++k)
+#pragma unroll
+          for (int e = 0; e < E; ++e) acc += x[r][k][e] * x[r][k][e];
+        q[r] = acc;
+      }
+      team_sum<ROWS>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+      slot ^= 1;
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        mean1[r] = 0.0f;
+        delta[r] = 0.0f;
+        rstd[r] = rsqrt_f32(q[r] * a.inv_n + a.eps);
+      }
+    }
+
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int64_t row = row0 + r;
+      if (row >= M) continue;
+      const int64_t base = row * N;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = gm.t + k * gm.tt;
+        if (v < nacc) {
+          float y[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            y[e] = ((x[r][k][e] - mean1[r]) - delta[r]) * rstd[r] * w[k][e] + b[k][e];
+          A::st(Y + base + (int64_t)v * E, A::pack(y));
+        }
+      }
+      if (gm.t == 0) {
+        if (a.mean) a.mean[row] = mean1[r] + delta[r];
+        if (a.rstd) a.rstd[row] = rstd[r];
+      }
+    }
+  }
+}
+
+// ---- backward -----------------------------------------------------------------------------
+
+template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool LN>
+__global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_threads) {
+  using A = Acc<T, VEC>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  __shared__ float red[RED_FLOATS];
+  __shared__ float merge[MERGE_FLOATS];
+  const TeamGeom gm = team_geom<WAVE>(team_threads);
+  const int nacc = a.nacc;
+  const int64_t M = a.M;
+  const int64_t N = a.N;
+  const T *__restrict__ X = static_cast<const T *>(a.x);
+  const T *__restrict__ DY = static_cast<const T *>(a.dy);
+  const T *__restrict__ DH = static_cast<const T *>(a.dh);
+  const T *__restrict__ W = static_cast<const T *>(a.w);
+  T *__restrict__ DX = static_cast<T *>(a.dx);
+  T *__restrict__ DR = static_cast<T *>(a.dr);
+  const bool have_stats = a.rstd != nullptr;
+  write_ws_header(a.header, a.partials, N);
+
+  float w[VPT][E], accw[VPT][E], accb[LN ? VPT : 1][E];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = gm.t + k * gm.tt;
+    raw rw = A::zero();
+    if (v < nacc) rw = A::ld_cached(W + (int64_t)v * E);
+    A::unpack(rw, w[k]);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      accw[k][e] = 0.0f;
+      if constexpr (LN) accb[k][e] = 0.0f;
+    }
+  }
+
+  const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
+  int slot = 0;
+  for (int64_t g = blockIdx.x; g * rows_per_group < M; g += gridDim.x) {
+    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
+    raw rx[ROWS][VPT], rdy[ROWS][VPT];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = row0 + r < M;
+      const int64_t base = (row0 + r) * N;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = gm.t + k * gm.tt;
+        rx[r][k] = A::zero();
+        rdy[r][k] = A::zero();
+        if (rv && v < nacc) {
+          rx[r][k] = A::ld(X + base + (int64_t)v * E);
+          rdy[r][k] = A::ld(DY + base + (int64_t)v * E);
+        }
+      }
+    }
+    // m: the row mean the forward saved (LayerNorm), or a first-pass mean when recomputing.
+    // The reduction below also sums x - m, so the exact mean m + delta is used for xhat.
+    float m[ROWS], rstd[ROWS];
+    if (have_stats) {
+#pragma unroll
+      for (int r = 0; r < ROWS; ++r) {
+        const int64_t row = row0 + r < M ? row0 + r : M - 1;
+        m[r] = LN ? a.mean[row] : 0.0f;
+        rstd[r] = a.rstd[row];
+      }
+    } else {
+      // recompute the forward statistics from the register-resident rows
+      if constexpr (LN) {
+        float s[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < VPT; ++k) {
+            float f[E];
+            A::unpack(rx[r][k], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc += f[e];
+          }
+          s[r] = acc;
+        }
+        team_sum<ROWS>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        slot ^= 1;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) m[r] = mul_rn(s[r], a.inv_n);
+        float qc[2 * ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          float q = 0.0f, c = 0.0f;
+#pragma unroll
+          for (int k = 0; k < VPT; ++k) {
+            const bool in = gm.t + k * gm.tt < nacc; // rows past M are all zeros
+            float f[E];
+            A::unpack(rx[r][k], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) {
+              const float d = in ? f[e] - m[r] : 0.0f;
+              q += d * d;
+              c += d;
+            }
+          }
+          qc[r] = q;
+          qc[ROWS + r] = c;
+        }
+        team_sum<2 * ROWS>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        slot ^= 1;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          const float dl = qc[ROWS + r] * a.inv_n;
+          rstd[r] = rsqrt_f32(fmaxf(qc[r] * a.inv_n - dl * dl, 0.0f) + a.eps);
+        }
+      } else {
+        float q[ROWS];
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int k = 0; k < VPT; ++k) {
+            float f[E];
+            A::unpack(rx[r][k], f);
+#pragma unroll
+            for (int e = 0; e < E; ++e) acc += f[e] * f[e];
+          }
+          q[r] = acc;
+        }
+        team_sum<ROWS>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        slot ^= 1;
+#pragma unroll
+        for (int r = 0; r < ROWS; ++r) {
+          m[r] = 0.0f;
+          rstd[r] = rsqrt_f32(q[r] * a.inv_n + a.eps);
+        }
+      }
+    }
+
+    // One team sum per row group. With g = dY * W and d = x - m:
+    //   LayerNorm: S0 = sum(g*d), S1 = sum(g), S2 = sum(d); delta = S2/N,
+    //              c1 = S1/N, c2 = rstd * (S0 - delta*S1)/N  (= mean(g * xhat))
+    //   RMSNorm  : S0 = sum(g*x), c2 = rstd * S0/N
+    constexpr int NV = LN ? 3 * ROWS : ROWS;
+    float sums[NV];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = row0 + r < M;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const bool in = rv && gm.t + k * gm.tt < nacc;
+        float xf[E], df[E];
+        A::unpack(rx[r][k], xf);
+        A::unpack(rdy[r][k], df);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = in ? xf[e] - m[r] : 0.0f;
+          const float gg = df[e] * w[k][e];
+          sums[r] += gg * d;
+          if constexpr (LN) {
+            sums[ROWS + r] += gg;
+            sums[2 * ROWS + r] += d;
+          }
+        }
+      }
+    }
+    team_sum<NV>(sums, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+    slot ^= 1;
+
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const int64_t row = row0 + r;
+      const bool rv = row < M;
+      const int64_t base = row * N;
+      const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
+      const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
+      const float c2 =
+          LN ? rstd[r] * (sums[r] - delta * sums[ROWS + r]) * a.inv_n : rstd[r] * sums[r] * a.inv_n;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = gm.t + k * gm.tt;
+        const bool in = v < nacc;
+        float xf[E], df[E], dx[E];
+        A::unpack(rx[r][k], xf);
+        A::unpack(rdy[r][k], df);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          // rows past M and columns past N hold zeros and must add nothing (even if rstd is
+          // infinite there, as for eps = 0)
+          const float xh = (rv && in) ? ((xf[e] - m[r]) - delta) * rstd[r] : 0.0f;
+          const float gg = df[e] * w[k][e];
+          dx[e] = rstd[r] * (gg - c1 - xh * c2);
+          accw[k][e] += df[e] * xh;
+          if constexpr (LN) accb[k][e] += df[e];
+        }
+        if (rv && in) {
+          const int64_t off = base + (int64_t)v * E;
+          if (DH) {
+            float hf[E];
+            A::unpack(A::ld(DH + off), hf);
+#pragma unroll
+            for (int e = 0; e < E; ++e) dx[e] += hf[e];
+          }
+          const raw p = A::pack(dx);
+          A::st(DX + off, p);
+          if (DR) A::st(DR + off, p);
+        }
+      }
+    }
+  }
+
+  // Column partials of this workgroup: sum over its teams (fixed order) and write one row
+  // per quantity into the workspace.
+  float *pw = a.colpart + (int64_t)blockIdx.x * N;
+  float *pb = a.colpart + ((int64_t)a.partials + blockIdx.x) * N;
+  if (gm.teams == 1) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = gm.t + k * gm.tt;
+      if (v < nacc) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          pw[(int64_t)v * E + e] = accw[k][e];
+          if constexpr (LN) pb[(int64_t)v * E + e] = accb[k][e];
+        }
+      }
+    }
+    return;
+  }
+  const int cols_per_block = MERGE_FLOATS / gm.teams;
+  for (int q = 0; q < (LN ? 2 : 1); ++q) {
+    float *dst = q == 0 ? pw : pb;
+    for (int64_t c0 = 0; c0 < N; c0 += cols_per_block) {
+      const int64_t c1 = c0 + cols_per_block < N ? c0 + cols_per_block : N;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = gm.t + k * gm.tt;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int64_t col = (int64_t)v * E + e;
+          if (v < nacc && col >= c0 && col < c1)
+            merge[gm.team * cols_per_block + (int)(col - c0)] =
+                q == 0 ? accw[k][e] : accb[LN ? k : 0][e];
+        }
+      }
+      __syncthreads();
+      for (int64_t col = c0 + threadIdx.x; col < c1; col += blockDim.x) {
+        float s = 0.0f;
+        for (int tm = 0; tm < gm.teams; ++tm) s += merge[tm * cols_per_block + (int)(col - c0)];
+        dst[col] = s;
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// ---- column reduction ------------------------------------------------------------------------
+
+// dW[j] (and dB[j]) = sum over p of colpart[q][p][j], in a fixed order: four slices of the
+// partial rows, each summed in ascending p, then the slices in order. One workgroup covers 64
+// columns of one quantity (blockIdx.y: 0 = dW, 1 = dB). The partial count comes from the
+// header the fused pass wrote; a header that does not describe this workspace gives NaN
+// outputs instead of reading past the partials.
+template <typename T>
+__global__ __launch_bounds__(256) void colsum_kernel(ReduceArgs a) {
+  __shared__ float part[4][64];
+  const int lane = threadIdx.x & 63;
+  const int slice = threadIdx.x >> 6;
+  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
+  const int64_t N = a.N;
+  const int64_t P = a.header[1];
+  const bool valid = a.header[0] == kWsMagic && a.header[2] == N && P >= 1 && P <= a.max_partials;
+  const float *src = a.colpart + (int64_t)blockIdx.y * (valid ? P : 0) * N;
+  float s = 0.0f;
+  if (valid && col < N) {
+    int64_t p = slice;
+    for (; p + 12 < P; p += 16) {
+      const float v0 = src[p * N + col];
+      const float v1 = src[(p + 4) * N + col];
+      const float v2 = src[(p + 8) * N + col];
+      const float v3 = src[(p + 12) * N + col];
+      s += v0;
+      s += v1;
+      s += v2;
+      s += v3;
+    }
+    for (; p < P; p += 4) s += src[p * N + col];
+  }
+  part[slice][lane] = s;
+  __syncthreads();
+  if (slice == 0 && col < N) {
+    float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
+    if (!valid) t = __builtin_nanf("");
+    T *dst = static_cast<T *>(blockIdx.y == 0 ? a.dw : a.db);
+    if constexpr (sizeof(T) == 4) {
+      dst[col] = t;
+    } else {
+      dst[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
+    }
+  }
+}
+
+__global__ __launch_bounds__(256) void zero_kernel(unsigned char *p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (size_t)gridDim.x * blockDim.x)
+    p[i] = 0;
+}
+
+// ---- launchers ---------------------------------------------------------------------------------
+
+namespace {
+
+template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
+hipError_t fwd_launch(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s) {
+  dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if (resid)
+    hipLaunchKernelGGL((team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>), grid, block, 0, s,
+                       a, p.team_threads);
+  else
+    hipLaunchKernelGGL((team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>), grid, block, 0, s,
+                       a, p.team_threads);
+  return hipGetLastError();
+}
+
+template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
+hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if (a.layernorm)
+    hipLaunchKernelGGL((team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>), grid, block, 0, s,
+                       a, p.team_threads);
+  else
+    hipLaunchKernelGGL((team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>), grid, block, 0, s,
+                       a, p.team_threads);
+  return hipGetLastError();
+}
+
+// The menu of compiled shapes. Wave scheme: workgroups of 256 threads (4 one-wave teams).
+// Block scheme: teams of up to LB threads. Entries are (VPT, ROWS, LB).
+#define DLN_WAVE_MENU(X)                                                                        \
+  X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(2, 4, 256) X(4, 1, 256)       \
+      X(4, 2, 256) X(8, 1, 256)
+#define DLN_WAVE_MENU_SCALAR(X) X(1, 1, 256) X(2, 1, 256) X(4, 1, 256) X(8, 1, 256) X(16, 1, 256)
+#define DLN_BLOCK_MENU(X)                                                                       \
+  X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(4, 1, 256) X(8, 1, 256)       \
+      X(1, 1, 512) X(1, 2, 512) X(2, 1, 512) X(2, 2, 512) X(4, 1, 512) X(1, 1, 1024)               \
+          X(1, 2, 1024) X(2, 1, 1024)
+#define DLN_BLOCK_MENU_SCALAR(X) X(4, 1, 1024) X(8, 1, 1024)
+
+template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
+  const bool resid = a.r != nullptr;
+  const int lb = p.lb;
+  hipError_t e = hipErrorInvalidConfiguration;
+  bool found = false;
+  if (p.scheme == NORM_SCHEME_WAVE) {
+    if (p.vector) {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = fwd_launch<T, true, V, R, L, true>(p, a, resid, s);                                     \
+  }
+      DLN_WAVE_MENU(X)
+#undef X
+    } else {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = fwd_launch<T, false, V, R, L, true>(p, a, resid, s);                                    \
+  }
+      DLN_WAVE_MENU_SCALAR(X)
+#undef X
+    }
+  } else {
+    if (p.vector) {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = fwd_launch<T, true, V, R, L, false>(p, a, resid, s);                                    \
+  }
+      DLN_BLOCK_MENU(X)
+#undef X
+    } else {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = fwd_launch<T, false, V, R, L, false>(p, a, resid, s);                                   \
+  }
+      DLN_BLOCK_MENU_SCALAR(X)
+#undef X
+    }
+  }
+  if (!found) return NORM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
+  const int lb = p.lb;
+  hipError_t e = hipErrorInvalidConfiguration;
+  bool found = false;
+  if (p.scheme == NORM_SCHEME_WAVE) {
+    if (p.vector) {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = bwd_launch<T, true, V, R, L, true>(p, a, s);                                            \
+  }
+      DLN_WAVE_MENU(X)
+#undef X
+    } else {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = bwd_launch<T, false, V, R, L, true>(p, a, s);                                           \
+  }
+      DLN_WAVE_MENU_SCALAR(X)
+#undef X
+    }
+  } else {
+    if (p.vector) {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = bwd_launch<T, true, V, R, L, false>(p, a, s);                                           \
+  }
+      DLN_BLOCK_MENU(X)
+#undef X
+    } else {
+#define X(V, R, L)                                                                              \
+  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
+    found = true;                                                                               \
+    e = bwd_launch<T, false, V, R, L, false>(p, a, s);                                          \
+  }
+      DLN_BLOCK_MENU_SCALAR(X)
+#undef X
+    }
+  }
+  if (!found) return NORM_ERR_UNSUPPORTED;
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+} // namespace
+
+norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                              hipStream_t s) {
+  return dtype == NORM_F32 ? team_fwd_typed<float>(p, a, s) : team_fwd_typed<bf16_bits>(p, a, s);
+}
+
+norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
+                              hipStream_t s) {
+  return dtype == NORM_F32 ? team_bwd_typed<float>(p, a, s) : team_bwd_typed<bf16_bits>(p, a, s);
+}
+
+norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s) {
+  if (!bytes) return NORM_OK;
+  size_t blocks = (bytes + 255) / 256;
+  if (blocks > 1024) blocks = 1024;
+  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                     static_cast<unsigned char *>(p), bytes);
+  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s) {
+  dim3 grid((unsigned)((a.N + 63) / 64), a.db ? 2u : 1u), block(256);
+  if (dtype == NORM_F32)
+    hipLaunchKernelGGL(colsum_kernel<float>, grid, block, 0, s, a);
+  else
+    hipLaunchKernelGGL(colsum_kernel<bf16_bits>, grid, block, 0, s, a);
+  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+} // namespace dln

@@ -1,0 +1,252 @@
+"""Python binding of the C ABI in include/norm.h (libnorm.so, HIP kernels for gfx950).
+
+Argument marshalling only: every function here takes torch tensors (device memory and streams
+come from PyTorch), checks their shape, dtype, device and contiguity, and passes raw pointers to
+the library. All computation happens in the HIP kernels. If libnorm.so is missing the first call
+raises; there is no fallback path.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libnorm.so")
+
+LAYERNORM, RMSNORM = 0, 1
+F32, BF16 = 0, 1
+PASS_FWD, PASS_BWD = 0, 1
+SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT = -1, 0, 1, 2
+TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
+TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS = 4, 5
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+
+KINDS = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM}
+DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_workspace_size",
+           "norm_plan", "norm_set_tuning", "norm_status_string", "norm_version")
+
+
+class NormError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__("%s: %s" % (where, status_string(status)))
+
+
+class _Plan(ctypes.Structure):
+    _fields_ = [("scheme", ctypes.c_int32), ("vector", ctypes.c_int32),
+                ("elems_per_access", ctypes.c_int32), ("threads", ctypes.c_int32),
+                ("team_threads", ctypes.c_int32), ("accesses_per_thread", ctypes.c_int32),
+                ("rows_per_iter", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("grid", ctypes.c_int64), ("chunks", ctypes.c_int64),
+                ("chunk_elems", ctypes.c_int64), ("row_groups", ctypes.c_int64),
+                ("partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libnorm.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError("libnorm.so is not built (run __graft_entry__.build() or "
+                               "deep_learning_normalization_amd/_build.py)")
+        L = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, f32, sz = (ctypes.c_int, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float,
+                                 ctypes.c_size_t)
+        L.norm_fwd.argtypes = [i32, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, vp, sz,
+                               vp]
+        L.norm_bwd.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp,
+                               vp, sz, vp]
+        L.norm_bwd_fused.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp,
+                                     vp, sz, vp]
+        L.norm_bwd_reduce.argtypes = [i32, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.norm_workspace_size.argtypes = [i32, i32, i32, i64, i64, i32,
+                                          ctypes.POINTER(ctypes.c_size_t)]
+        L.norm_plan.argtypes = [i32, i32, i32, i64, i64, i32, i32, i32, ctypes.POINTER(_Plan)]
+        L.norm_set_tuning.argtypes = [i32, i64]
+        L.norm_status_string.argtypes = [i32]
+        L.norm_status_string.restype = ctypes.c_char_p
+        L.norm_version.argtypes = []
+        for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
+                     "norm_workspace_size", "norm_plan", "norm_set_tuning"):
+            getattr(L, name).restype = ctypes.c_int
+        L.norm_version.restype = ctypes.c_int
+        _lib = L
+    return _lib
+
+
+def status_string(status):
+    return lib().norm_status_string(int(status)).decode()
+
+
+def _kind(kind):
+    return KINDS[kind] if isinstance(kind, str) else int(kind)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr() or None
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check_mat(t, M, N, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype or t.numel() != M * N or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("%s must be a contiguous CUDA %s tensor of %d x %d elements"
+                         % (name, dtype, M, N))
+
+
+def _check_vec(t, n, dtype, name):
+    if t is None:
+        return
+    if t.dtype != dtype or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
+        raise ValueError("%s must be a contiguous CUDA %s tensor of %d elements" % (name, dtype, n))
+
+
+def _raise(st, where):
+    if st != OK:
+        raise NormError(st, where)
+
+
+def _ws(ws):
+    if ws is None:
+        return None, 0
+    return ws.data_ptr(), ws.numel() * ws.element_size()
+
+
+def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=None,
+             stream=None):
+    """Queue the forward. X, R, Y, H are [M, N]; W, B are [N]; mean, rstd are [M] fp32."""
+    M, N = X.shape
+    dt = X.dtype
+    for t, nm in ((X, "X"), (R, "R"), (Y, "Y"), (H, "H")):
+        _check_mat(t, M, N, dt, nm)
+    _check_vec(W, N, dt, "W")
+    _check_vec(B, N, dt, "B")
+    _check_vec(mean, M, torch.float32, "mean")
+    _check_vec(rstd, M, torch.float32, "rstd")
+    wp, wb = _ws(workspace)
+    st = lib().norm_fwd(_kind(kind), _ptr(X), _ptr(R), _ptr(W), _ptr(B), float(eps), M, N,
+                        DTYPES[dt], _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
+                        _stream(stream))
+    _raise(st, "norm_fwd")
+
+
+def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, stream=None):
+    """Queue the backward (fused pass, then the column reduction)."""
+    M, N = X.shape
+    dt = X.dtype
+    for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
+        _check_mat(t, M, N, dt, nm)
+    for t, nm in ((W, "W"), (dW, "dW"), (dB, "dB")):
+        _check_vec(t, N, dt, nm)
+    _check_vec(mean, M, torch.float32, "mean")
+    _check_vec(rstd, M, torch.float32, "rstd")
+    wp, wb = _ws(workspace)
+    st = lib().norm_bwd(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
+                        _ptr(rstd), float(eps), M, N, DTYPES[dt], _ptr(dX), _ptr(dR), _ptr(dW),
+                        _ptr(dB), wp, wb, _stream(stream))
+    _raise(st, "norm_bwd")
+
+
+def norm_bwd_fused(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, workspace, stream=None):
+    """Queue the backward's fused pass: dX (and dR), column partials into the workspace."""
+    M, N = X.shape
+    dt = X.dtype
+    for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
+        _check_mat(t, M, N, dt, nm)
+    _check_vec(W, N, dt, "W")
+    _check_vec(mean, M, torch.float32, "mean")
+    _check_vec(rstd, M, torch.float32, "rstd")
+    wp, wb = _ws(workspace)
+    st = lib().norm_bwd_fused(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
+                              _ptr(rstd), float(eps), M, N, DTYPES[dt], _ptr(dX), _ptr(dR), wp,
+                              wb, _stream(stream))
+    _raise(st, "norm_bwd_fused")
+
+
+def norm_bwd_reduce(kind, M, N, dW, dB, workspace, stream=None):
+    """Queue the column reduction of the partials a fused pass left in the workspace."""
+    dt = dW.dtype
+    _check_vec(dW, N, dt, "dW")
+    _check_vec(dB, N, dt, "dB")
+    wp, wb = _ws(workspace)
+    st = lib().norm_bwd_reduce(_kind(kind), M, N, DTYPES[dt], _ptr(dW), _ptr(dB), wp, wb,
+                               _stream(stream))
+    _raise(st, "norm_bwd_reduce")
+
+
+def norm_workspace_size(kind, dtype, pass_, M, N, residual=False):
+    """Workspace bytes for a call on the current device."""
+    out = ctypes.c_size_t(0)
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    st = lib().norm_workspace_size(_kind(kind), dt, int(pass_), M, N, int(bool(residual)),
+                                   ctypes.byref(out))
+    _raise(st, "norm_workspace_size")
+    return out.value
+
+
+def norm_plan(kind, dtype, pass_, M, N, residual=False, aligned=True, cu_count=256):
+    """The dispatcher's plan for a shape, as a dict (pure host logic, no GPU needed)."""
+    p = _Plan()
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    st = lib().norm_plan(_kind(kind), dt, int(pass_), M, N, int(bool(residual)),
+                         int(bool(aligned)), int(cu_count), ctypes.byref(p))
+    _raise(st, "norm_plan")
+    return {name: getattr(p, name) for name, _ in _Plan._fields_ if name != "reserved"}
+
+
+def norm_set_tuning(key, value):
+    _raise(lib().norm_set_tuning(int(key), int(value)), "norm_set_tuning")
+
+
+def norm_version():
+    return lib().norm_version()
+
+
+# ---- allocating conveniences (torch allocates; the kernels compute) ------------------------
+
+def workspace(kind, dtype, pass_, M, N, residual=False, device="cuda"):
+    n = norm_workspace_size(kind, dtype, pass_, M, N, residual)
+    return torch.empty(max(n, 16), dtype=torch.uint8, device=device)
+
+
+def forward(kind, X, W, B=None, eps=1e-5, R=None, stream=None):
+    """Y, H (or None), mean (LayerNorm, else None), rstd of the forward."""
+    M, N = X.shape
+    k = _kind(kind)
+    Y = torch.empty_like(X)
+    H = torch.empty_like(X) if R is not None else None
+    mean = torch.empty(M, dtype=torch.float32, device=X.device) if k == LAYERNORM else None
+    rstd = torch.empty(M, dtype=torch.float32, device=X.device)
+    ws = workspace(k, X.dtype, PASS_FWD, M, N, R is not None, X.device)
+    norm_fwd(k, X, R, W, B, eps, Y, H, mean, rstd, ws, stream)
+    return Y, H, mean, rstd
+
+
+def backward(kind, X, dY, W, mean=None, rstd=None, eps=1e-5, dH=None, stream=None):
+    """dX, dW, dB (LayerNorm, else None) of the backward."""
+    M, N = X.shape
+    k = _kind(kind)
+    dX = torch.empty_like(X)
+    dW = torch.empty_like(W)
+    dB = torch.empty_like(W) if k == LAYERNORM else None
+    ws = workspace(k, X.dtype, PASS_BWD, M, N, False, X.device)
+    norm_bwd(k, X, dY, dH, W, mean, rstd, eps, dX, None, dW, dB, ws, stream)
+    return dX, dW, dB

@@ -1,0 +1,201 @@
+/*
+ * norm.h -- C ABI of the MI355X (gfx950) row-wise LayerNorm / RMSNorm library.
+ *
+ * What the operations compute. Sources are web pages; each is cited by its title.
+ *   [P1] "PyTorch atinge desempenho SOTA em normalização com torch.compile" (matsubara.tec.br):
+ *     para. 2 -- LayerNorm normalises each row with its mean and variance and applies the
+ *                trainable weight (gamma) and bias (beta); RMSNorm divides by the root mean
+ *                square instead and has no bias.
+ *     para. 3 -- both forwards reduce along the contiguous dimension, then apply pointwise work.
+ *     para. 7 -- the backward produces dX, dW and, for LayerNorm, dB.
+ *     paras. 8-10 -- dX and the dW/dB column reductions are fused in one pass over the data,
+ *                the column sums go through a workspace of per-block partial sums without
+ *                atomics, and an extra reduction pass consolidates that workspace.
+ *
+ * For a row x of N values (in fp32 arithmetic; bf16 inputs are widened exactly):
+ *   LayerNorm: mean = sum(x)/N, var = sum((x-mean)^2)/N (biased), rstd = 1/sqrt(var+eps),
+ *              y = (x-mean)*rstd*W + B
+ *   RMSNorm:   rstd = 1/sqrt(sum(x^2)/N + eps), y = x*rstd*W
+ *   Backward, with g = dY*W and xhat the normalised row:
+ *              LayerNorm dX = rstd*(g - mean(g) - xhat*mean(g*xhat)),
+ *              RMSNorm   dX = rstd*(g - xhat*mean(g*xhat)),
+ *              dW = sum over rows of dY*xhat, dB = sum over rows of dY.
+ *   Residual variant (fused add in front of the norm): h = R + X rounded once to the storage
+ *   dtype is stored in H, and the norm is applied to that stored h; its backward is the plain
+ *   backward on H, plus an optional incoming gradient dH of h, and dR = dX.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers on the current HIP device. X, R, Y, H, dY, dH,
+ *     dX, dR are row-major contiguous [M, N] (row stride N); W, B, dW, dB are [N]; mean and
+ *     rstd are [M] fp32 whatever the dtype; the workspace is raw device memory.
+ *   - dtype is the storage type of every non-statistic tensor; arithmetic is fp32, and each
+ *     output is rounded once (round to nearest even).
+ *   - The caller owns all memory. The library allocates nothing and keeps no state beyond a
+ *     per-device cache of the compute-unit count and the tuning overrides below.
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL = the null stream).
+ *     Nothing synchronises the host. Device faults surface at the caller's next sync.
+ *   - Output buffers must not overlap input buffers (in place is rejected), except that dR
+ *     may be the same pointer as dX.
+ *   - Rows whose start is not 16-byte aligned, or N not a multiple of the 16-byte vector
+ *     width (8 bf16 / 4 fp32), run on a slower element-wise path; results are the same.
+ *   - Arguments are checked before anything is launched; a failed check returns an error and
+ *     launches nothing. M == 0 returns NORM_OK with no launch. No C++ exception crosses the
+ *     ABI and the library never aborts the process.
+ *   - Results are bitwise reproducible run to run on one device (fixed reduction orders, no
+ *     atomics). They can differ in the last bits between devices with different CU counts.
+ */
+#ifndef DLN_NORM_H
+#define DLN_NORM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { NORM_LAYERNORM = 0, NORM_RMSNORM = 1 } norm_kind_t;
+
+typedef enum { NORM_F32 = 0, NORM_BF16 = 1 } norm_dtype_t;
+
+typedef enum {
+  NORM_OK = 0,
+  NORM_ERR_INVALID_ARG = 1, /* a pointer, size, eps, kind or dtype is not acceptable */
+  NORM_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels handle */
+  NORM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than norm_workspace_size() */
+  NORM_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} norm_status_t;
+
+/* Which pass a workspace size or plan is asked for. */
+typedef enum { NORM_PASS_FWD = 0, NORM_PASS_BWD = 1 } norm_pass_t;
+
+/* Kernel scheme chosen for a shape. */
+typedef enum {
+  NORM_SCHEME_AUTO = -1, /* tuning value only: let the dispatcher choose */
+  NORM_SCHEME_WAVE = 0,  /* one row per 64-lane wavefront, registers only (short rows) */
+  NORM_SCHEME_BLOCK = 1, /* one row per team of waves, cross-wave sums through LDS */
+  NORM_SCHEME_SPLIT = 2  /* one row over several workgroups, two passes (very long rows) */
+} norm_scheme_t;
+
+typedef void *norm_stream_t; /* a hipStream_t */
+
+/*
+ * Forward [P1 paras. 2-3].
+ *   kind   LayerNorm or RMSNorm.
+ *   X      [M, N] input. Required.
+ *   R      [M, N] residual added to X before the norm, or NULL.
+ *   W      [N] weight. Required.
+ *   B      [N] bias. LayerNorm: optional (NULL means zero). RMSNorm: must be NULL.
+ *   eps    added to the variance (LayerNorm) or mean square (RMSNorm) inside the square root;
+ *          finite and >= 0.
+ *   M, N   rows (>= 0) and row length (1 <= N <= 2^31 - 1).
+ *   dtype  storage type of X, R, W, B, Y, H.
+ *   Y      [M, N] output. Required.
+ *   H      [M, N] output R + X (rounded to dtype). Required when R is given, else NULL.
+ *   mean   [M] fp32 row means. LayerNorm: optional. RMSNorm: must be NULL.
+ *   rstd   [M] fp32 row 1/sqrt(stat + eps). Optional.
+ *   workspace, workspace_bytes: device scratch of at least
+ *          norm_workspace_size(kind, dtype, NORM_PASS_FWD, M, N, R != NULL) bytes, 256-byte
+ *          aligned; may be NULL when that size is 0.
+ * Returns NORM_OK once the kernels are queued.
+ */
+norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const void *W,
+                       const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
+                       void *Y, void *H, float *mean, float *rstd, void *workspace,
+                       size_t workspace_bytes, norm_stream_t stream);
+
+/*
+ * Backward [P1 paras. 7-10]: dX fused with per-block dW/dB partial sums in one pass over
+ * X and dY, then a column reduction of the partials into dW/dB.
+ *   X      [M, N] the norm's input (for the residual variant: the stored H). Required.
+ *   dY     [M, N] gradient of Y. Required.
+ *   dH     [M, N] incoming gradient of the residual output H, added to dX; or NULL.
+ *   W      [N] weight. Required.
+ *   mean, rstd: the forward's [M] fp32 statistics. LayerNorm: both or neither; RMSNorm: mean
+ *          must be NULL, rstd optional. When absent they are recomputed from X with eps.
+ *   eps, M, N, dtype: as for norm_fwd.
+ *   dX     [M, N] output. Required.
+ *   dR     [M, N] output equal to dX (residual variant); NULL, dX itself, or a separate buffer.
+ *   dW     [N] output. Required.
+ *   dB     [N] output. LayerNorm: optional. RMSNorm: must be NULL.
+ *   workspace: at least norm_workspace_size(kind, dtype, NORM_PASS_BWD, M, N, 0) bytes.
+ */
+norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                       const void *W, const float *mean, const float *rstd, float eps,
+                       int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR, void *dW,
+                       void *dB, void *workspace, size_t workspace_bytes, norm_stream_t stream);
+
+/*
+ * The two stages of norm_bwd, for callers that want them apart (for example to time the
+ * fused pass alone, or to reduce the dW/dB partials later). norm_bwd_fused writes dX (and dR)
+ * and leaves fp32 column partials in the workspace; norm_bwd_reduce turns those partials into
+ * dW (and dB). Both must get the same kind, M, N, dtype, workspace and stream, with nothing
+ * writing the workspace in between. Arguments as for norm_bwd.
+ */
+norm_status_t norm_bwd_fused(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                             const void *W, const float *mean, const float *rstd, float eps,
+                             int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                             void *workspace, size_t workspace_bytes, norm_stream_t stream);
+
+norm_status_t norm_bwd_reduce(norm_kind_t kind, int64_t M, int64_t N, norm_dtype_t dtype,
+                              void *dW, void *dB, void *workspace, size_t workspace_bytes,
+                              norm_stream_t stream);
+
+/*
+ * Workspace bytes a call needs on the CURRENT device (the size depends on its compute-unit
+ * count). pass: NORM_PASS_FWD or NORM_PASS_BWD; residual: nonzero when R is given.
+ * Writes the size to *bytes. Returns NORM_ERR_HIP if no device can be queried.
+ */
+norm_status_t norm_workspace_size(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass,
+                                  int64_t M, int64_t N, int residual, size_t *bytes);
+
+/* Description of the launch plan for a shape, for tests and tuning. */
+typedef struct {
+  int32_t scheme;         /* norm_scheme_t */
+  int32_t vector;         /* 1: 16-byte accesses; 0: element-wise path */
+  int32_t elems_per_access;
+  int32_t threads;        /* threads per workgroup */
+  int32_t team_threads;   /* threads that share one row (64 for the wave scheme) */
+  int32_t accesses_per_thread; /* per row (wave/block) or per chunk (split) */
+  int32_t rows_per_iter;  /* rows a team holds at once */
+  int32_t reserved;
+  int64_t grid;           /* workgroups of the main kernel */
+  int64_t chunks;         /* split scheme: chunks per row (1 otherwise) */
+  int64_t chunk_elems;    /* split scheme: elements per chunk (N otherwise) */
+  int64_t row_groups;     /* split backward: row groups sharing a column partial */
+  int64_t partials;       /* rows of fp32 column partials in the backward workspace */
+  uint64_t workspace_bytes;
+} norm_plan_t;
+
+/*
+ * The plan the dispatcher picks for a shape on a device with cu_count compute units, with
+ * aligned != 0 meaning every pointer is 16-byte aligned. Pure host logic: needs no GPU.
+ */
+norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
+                        int64_t N, int residual, int aligned, int cu_count, norm_plan_t *out);
+
+/* Tuning overrides (process-wide; for tests and offline tuning; not thread-safe with
+ * concurrent calls). Value -1 restores the default. */
+typedef enum {
+  NORM_TUNE_SCHEME = 0,         /* norm_scheme_t to force */
+  NORM_TUNE_GRID_PER_CU = 1,    /* workgroups per compute unit for persistent kernels */
+  NORM_TUNE_ROWS_PER_ITER = 2,  /* rows a team holds at once: 1, 2 or 4 */
+  NORM_TUNE_TEAM_THREADS = 3,   /* threads per row team (multiple of 64); ignored where a team
+                                   of that size cannot hold the row */
+  NORM_TUNE_SPLIT_CHUNK = 4,    /* split scheme: elements per chunk */
+  NORM_TUNE_ROW_GROUPS = 5      /* split backward: number of row groups */
+} norm_tune_t;
+
+norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);
+
+/* Static text for a status code. */
+const char *norm_status_string(norm_status_t status);
+
+/* Library version, major * 10000 + minor * 100 + patch. */
+int norm_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DLN_NORM_H */

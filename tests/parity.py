@@ -1,0 +1,249 @@
+"""GPU-vs-oracle parity helpers shared by the GPU tests.
+
+Inputs come from deep_learning_normalization_amd.inputs (seeded, CPU, storage dtype); the same
+bits go to the HIP library (through the C ABI binding) and to the CPU oracle. The oracle never
+sees a device result: for the residual variant it forms its own h = round(R + X) and runs its
+backward on that.
+
+Tolerances (written out in check_*):
+  fp32 outputs        |d| <= 1e-6 + 1e-5 |ref|
+  bf16 Y, dX, H       |d| <= 1.6e-2 (1 + |ref|)            (1.6e-2 absolute, widened by the bf16
+                                                            spacing beyond |ref| = 1)
+                      |d| <= 1.6e-2 (|ref| + rms(ref))     (scale-aware: small gradients too)
+                      |d| <= 2^-8 |ref| + 1e-5 rms(ref)    (one rounding of an fp32 result)
+  dW, dB              |d_j| <= 1e-2 max(|ref_j|, rms(ref)) (relative, with a floor where a
+                                                            column sum of signed terms is ~0);
+                      1e-4 of that for fp32 storage
+  rstd                |d| <= 1e-5 ref
+  mean                |d| <= 1e-5 (|mean| + std)
+"""
+import dataclasses
+
+import numpy as np
+import torch
+
+import oracle
+from deep_learning_normalization_amd import inputs, normlib as nl
+
+KIND = {"layernorm": oracle.LAYERNORM, "rmsnorm": oracle.RMSNORM}
+DT = {"f32": oracle.F32, "bf16": oracle.BF16}
+
+
+def rms(a):
+    a = np.asarray(a, np.float64)
+    return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
+
+
+def _fail(what, got, ref, bound):
+    d = np.abs(got - ref)
+    bad = ~(d <= bound)
+    k = int(np.flatnonzero(bad)[0])
+    raise AssertionError("%s: %d/%d outside tolerance; first at %d: got %r ref %r (|d|=%g > %g)"
+                         % (what, int(bad.sum()), bad.size, k, got[k], ref[k], d[k], bound[k]))
+
+
+def check_values(what, got, ref, dtype, floor=None):
+    """Y, dX, H against the oracle. `floor` (same shape, optional) is the fp32 arithmetic floor
+    of each value: a result formed by cancelling terms much larger than itself cannot be closer
+    than a few fp32 ulps of those terms (e.g. dX of a one-column RMSNorm row)."""
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    fl = np.zeros_like(ref) if floor is None else np.asarray(floor, np.float64).ravel()
+    assert got.shape == ref.shape, (what, got.shape, ref.shape)
+    if got.size == 0:
+        return
+    assert np.array_equal(np.isnan(got), np.isnan(ref)), what + ": NaN pattern differs"
+    ok = ~np.isnan(ref)
+    got, ref, fl = got[ok], ref[ok], fl[ok]
+    d = np.abs(got - ref)
+    if dtype == "f32":
+        b = 1e-6 + 1e-5 * np.abs(ref) + fl
+        if not (d <= b).all():
+            _fail(what + " [fp32]", got, ref, b)
+        return
+    s = rms(ref)
+    for name, b in (("1.6e-2 abs", 1.6e-2 * (1.0 + np.abs(ref))),
+                    ("1.6e-2 scaled", 1.6e-2 * (np.abs(ref) + s) + fl),
+                    ("bf16 rounding", 2.0 ** -8 * np.abs(ref) + 1e-5 * s + fl)):
+        if not (d <= b).all():
+            _fail("%s [bf16 %s]" % (what, name), got, ref, b)
+
+
+def dx_floor(rows, dY, W, rstd, N):
+    """fp32 floor of dX on the given rows: 8 ulps (2^-24) of the largest term rstd*|dY*W|,
+    times 2 + sqrt(N) (|c1| and |xhat*c2| are at most max|g| and sqrt(N) max|g|)."""
+    g = (dY[rows].double() * W.double()).abs().amax(dim=1).numpy()
+    per_row = 8 * 2.0 ** -24 * np.asarray(rstd) * g * (2.0 + np.sqrt(N))
+    return np.repeat(per_row, N)
+
+
+def check_h(got, ref, dtype):
+    """The residual sum h = round(R + X): the device adds in fp32 and rounds once more, so it
+    may differ from the exactly rounded sum by one unit in the last place, and only rarely (a
+    binary32 sum of two bf16 values is exact unless their exponents differ by more than 16)."""
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    if dtype == "f32":
+        check_values("H", got, ref, dtype)
+        return
+    diff = got != ref
+    if diff.any():
+        r = np.abs(ref[diff])
+        ulp = np.exp2(np.floor(np.log2(np.where(r > 0, r, 2.0 ** -133))) - 7)
+        assert (np.abs(got[diff] - ref[diff]) <= ulp).all(), "H: more than one bf16 ulp off"
+        assert diff.mean() < 1e-4, "H: %d of %d elements differ" % (diff.sum(), diff.size)
+
+
+def check_colsums(what, got, ref, dtype):
+    got = np.asarray(got, np.float64).ravel()
+    ref = np.asarray(ref, np.float64).ravel()
+    floor = np.maximum(np.abs(ref), rms(ref))
+    b = 1e-2 * floor
+    if not (np.abs(got - ref) <= b).all():
+        _fail(what + " [1e-2 rel]", got, ref, b)
+    if dtype == "f32":
+        b = 1e-4 * floor
+        if not (np.abs(got - ref) <= b).all():
+            _fail(what + " [fp32 1e-4 rel]", got, ref, b)
+
+
+def check_stats(got_mean, got_rstd, ref_mean, ref_rstd):
+    r = np.asarray(ref_rstd, np.float64)
+    g = np.asarray(got_rstd, np.float64)
+    b = 1e-5 * r
+    if not (np.abs(g - r) <= b).all():
+        _fail("rstd", g, r, b)
+    if got_mean is not None:
+        m = np.asarray(ref_mean, np.float64)
+        gm = np.asarray(got_mean, np.float64)
+        b = 1e-5 * (np.abs(m) + 1.0 / r)
+        if not (np.abs(gm - m) <= b).all():
+            _fail("mean", gm, m, b)
+
+
+def sample_rows(M, k=24, seed=0):
+    """First, last and seeded random rows (sorted, unique)."""
+    if M <= 3 * k:
+        return np.arange(M)
+    g = np.random.default_rng(seed)
+    rows = set(range(3)) | set(range(M - 3, M)) | set(g.choice(M, k, replace=False).tolist())
+    return np.array(sorted(rows))
+
+
+def _to_dev(t, dev):
+    return None if t is None else t.to(dev)
+
+
+def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stats=True,
+                  dr="none", dh=False, stream=None):
+    """Run forward (and backward) of workload w on the GPU and check every output against the
+    oracle. Rows are checked in full when M*N <= full_limit, else on sampled rows; dW/dB always
+    over all rows.
+
+    dr: "none" (no dR), "alias" (dR is dX), "separate" (its own buffer, must equal dX).
+    dh: add a seeded incoming gradient of H (residual variant).
+    stats: pass the forward's mean/rstd to the backward (else it recomputes them).
+    Returns the device outputs for further checks.
+    """
+    if dh and w.dh is None:
+        w = dataclasses.replace(w, dh=inputs.normal(0, 0.5))
+    t = inputs.make(w, M)
+    M = t["X"].shape[0]
+    N = w.N
+    kind = KIND[w.kind]
+    dtc = DT[w.dtype]
+    eps = float(np.float32(w.eps))
+    X, W, B, R = (_to_dev(t[k], dev) for k in ("X", "W", "B", "R"))
+    Y, H, mean, rstd = nl.forward(w.kind, X, W, B, w.eps, R=R, stream=stream)
+    out = {"Y": Y, "H": H, "mean": mean, "rstd": rstd}
+
+    bits = {k: inputs.host_bits(t[k]) for k in ("X", "W", "B", "R", "dY", "dH")}
+    rows = np.arange(M) if M * N <= full_limit else sample_rows(M)
+    idx = torch.as_tensor(rows, device=dev, dtype=torch.long)
+
+    def take(a):
+        return a.index_select(0, idx).double().cpu().numpy()
+
+    # oracle forward on the sampled rows (contiguous runs)
+    ref = {"y": [], "mean": [], "rstd": [], "h": []}
+    runs = np.split(rows, np.flatnonzero(np.diff(rows) != 1) + 1) if len(rows) else []
+    for run in runs:
+        f = oracle.fwd(kind, dtc, bits["X"], bits["W"], bits["B"], bits["R"], eps=eps,
+                       rows=(int(run[0]), int(run[-1]) + 1), want_h=R is not None)
+        for k in ref:
+            if f[k] is not None:
+                ref[k].append(f[k])
+    cat = {k: (np.concatenate(v) if v else None) for k, v in ref.items()}
+    if M:
+        check_values("Y", take(Y), cat["y"], w.dtype)
+        check_stats(mean.index_select(0, idx).double().cpu().numpy() if mean is not None else None,
+                    rstd.index_select(0, idx).double().cpu().numpy(),
+                    cat["mean"] if w.kind == "layernorm" else None, cat["rstd"])
+        if R is not None:
+            check_h(take(H), cat["h"], w.dtype)
+    if not want_bwd or w.dy is None:
+        return out
+
+    dY, dH = _to_dev(t["dY"], dev), _to_dev(t["dH"], dev)
+    Xin = H if R is not None else X
+    # the oracle's own h (as input bits) for the residual backward, formed block by block
+    if R is not None:
+        xbits = np.empty((M, N), np.uint16 if w.dtype == "bf16" else np.float32)
+        for r0 in range(0, M, 4096):
+            r1 = min(M, r0 + 4096)
+            h = oracle.fwd(kind, dtc, bits["X"], bits["W"], None, bits["R"], eps=eps,
+                           rows=(r0, r1), want_h=True)["h"]
+            xbits[r0:r1] = (oracle.round_bf16(h) if w.dtype == "bf16" else h.astype(np.float32))
+            del h
+    else:
+        xbits = bits["X"]
+
+    dX = torch.empty_like(X)
+    dW = torch.empty_like(W)
+    dB = torch.empty_like(W) if w.kind == "layernorm" else None
+    dR = None
+    if dr == "alias":
+        dR = dX
+    elif dr == "separate":
+        dR = torch.empty_like(X)
+    ws = nl.workspace(w.kind, X.dtype, nl.PASS_BWD, M, N, device=dev)
+    nl.norm_bwd(w.kind, Xin, dY, dH, W, mean if stats else None, rstd if stats else None, w.eps,
+                dX, dR, dW, dB, ws, stream=stream)
+    out.update({"dX": dX, "dW": dW, "dB": dB, "dR": dR, "ws": ws})
+
+    g_full = oracle.bwd(kind, dtc, xbits, bits["dY"], bits["W"], eps=eps, want_dx=False)
+    dx_ref = []
+    for run in runs:
+        g = oracle.bwd(kind, dtc, xbits, bits["dY"], bits["W"], bits["dH"], eps=eps,
+                       rows=(int(run[0]), int(run[-1]) + 1), want_dw=False)
+        dx_ref.append(g["dx"])
+    if M:
+        fl = dx_floor(torch.as_tensor(rows), t["dY"], t["W"], cat["rstd"], N)
+        check_values("dX", take(dX), np.concatenate(dx_ref), w.dtype, floor=fl)
+    check_colsums("dW", dW.double().cpu().numpy(), g_full["dw"], w.dtype)
+    if dB is not None:
+        check_colsums("dB", dB.double().cpu().numpy(), g_full["db"], w.dtype)
+    if dr == "separate" and M:
+        assert torch.equal(dR.view(torch.int16) if dR.dtype == torch.bfloat16 else dR,
+                           dX.view(torch.int16) if dX.dtype == torch.bfloat16 else dX)
+    return out
+
+
+class tuned:
+    """Context manager setting library tuning overrides, restoring defaults afterwards."""
+
+    def __init__(self, **kv):
+        keys = {"scheme": nl.TUNE_SCHEME, "grid_per_cu": nl.TUNE_GRID_PER_CU,
+                "rows": nl.TUNE_ROWS_PER_ITER, "team_threads": nl.TUNE_TEAM_THREADS,
+                "split_chunk": nl.TUNE_SPLIT_CHUNK, "row_groups": nl.TUNE_ROW_GROUPS}
+        self.items = [(keys[k], v) for k, v in kv.items()]
+
+    def __enter__(self):
+        for k, v in self.items:
+            nl.norm_set_tuning(k, v)
+        return self
+
+    def __exit__(self, *exc):
+        for k in range(6):
+            nl.norm_set_tuning(k, -1)
+        return False

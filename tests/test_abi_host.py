@@ -1,0 +1,207 @@
+"""The C ABI library on the host (no GPU): it loads, exports every symbol the header declares,
+rejects bad arguments before touching a device, and its dispatcher picks the documented
+schemes and workspace layouts."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+import torch
+
+from deep_learning_normalization_amd import _build, normlib as nl
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "norm.h")
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib_built():
+    if not os.path.exists(nl.LIB_PATH):
+        _build.build()
+    nl.lib()
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(norm_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_symbols():
+    assert set(_declared_functions()) == set(nl.SYMBOLS)
+
+
+def test_library_exports_every_declared_symbol():
+    out = subprocess.run(["nm", "-D", "--defined-only", nl.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (norm_[a-z_]+)\b", out))
+    missing = set(_declared_functions()) - exported
+    assert not missing, missing
+    lib = ctypes.CDLL(nl.LIB_PATH)
+    for name in _declared_functions():
+        assert hasattr(lib, name)
+
+
+def test_header_compiles_as_c():
+    src = '#include "norm.h"\nint main(void){ norm_plan_t p; (void)p; return NORM_OK; }\n'
+    r = subprocess.run(["gcc", "-x", "c", "-std=c99", "-Wall", "-Werror", "-I",
+                        os.path.dirname(HEADER), "-fsyntax-only", "-"], input=src, text=True,
+                       capture_output=True)
+    assert r.returncode == 0, r.stderr
+
+
+def test_status_strings():
+    for s in range(5):
+        assert nl.status_string(s).startswith("NORM_")
+    assert "unknown" in nl.status_string(99)
+    assert nl.norm_version() >= 100
+
+
+# ---- argument checks (fail before any device access) -------------------------------------
+
+L = None
+FAKE = 1 << 20  # never dereferenced: every call below fails its checks first
+
+
+def _fwd(**kw):
+    a = dict(kind=0, X=FAKE, R=None, W=FAKE * 2, B=None, eps=1e-5, M=4, N=8, dtype=1,
+             Y=FAKE * 3, H=None, mean=None, rstd=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return nl.lib().norm_fwd(a["kind"], a["X"], a["R"], a["W"], a["B"], a["eps"], a["M"], a["N"],
+                             a["dtype"], a["Y"], a["H"], a["mean"], a["rstd"], a["ws"], a["wsb"],
+                             a["stream"])
+
+
+def _bwd(**kw):
+    a = dict(kind=0, X=FAKE, dY=FAKE * 2, dH=None, W=FAKE * 3, mean=None, rstd=None, eps=1e-5,
+             M=4, N=8, dtype=1, dX=FAKE * 4, dR=None, dW=FAKE * 5, dB=None, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return nl.lib().norm_bwd(a["kind"], a["X"], a["dY"], a["dH"], a["W"], a["mean"], a["rstd"],
+                             a["eps"], a["M"], a["N"], a["dtype"], a["dX"], a["dR"], a["dW"],
+                             a["dB"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kind=2), dict(kind=-1), dict(dtype=2), dict(M=-1), dict(N=0), dict(N=-5),
+    dict(N=1 << 31), dict(eps=-1e-5), dict(eps=float("nan")), dict(eps=float("inf")),
+    dict(X=None), dict(W=None), dict(Y=None),
+    dict(kind=1, B=FAKE * 9), dict(kind=1, mean=FAKE * 9),
+    dict(R=FAKE * 9), dict(H=FAKE * 9),                  # R and H go together
+    dict(Y=FAKE),                                        # in place
+    dict(Y=FAKE + 16),                                   # overlapping the input
+    dict(mean=FAKE * 3 + 8),                             # output overlapping an output
+    dict(M=1 << 40, N=1 << 30),                          # size overflow
+], ids=lambda kw: ",".join("%s=%s" % i for i in kw.items()))
+def test_fwd_rejects(kw):
+    assert _fwd(**kw) == nl.ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("kw", [
+    dict(kind=3), dict(dtype=7), dict(M=-2), dict(N=0), dict(eps=-1.0),
+    dict(X=None), dict(dY=None), dict(W=None), dict(dX=None), dict(dW=None),
+    dict(kind=1, dB=FAKE * 9), dict(kind=1, mean=FAKE * 9, rstd=FAKE * 10),
+    dict(mean=FAKE * 9),                                 # LayerNorm: mean and rstd together
+    dict(rstd=FAKE * 9),
+    dict(dX=FAKE * 2),                                   # dX over dY
+    dict(dR=FAKE * 2 + 4),                               # dR over dY
+    dict(dW=FAKE * 3),                                   # dW over W
+    dict(ws=FAKE * 4, wsb=64),                           # workspace over dX
+], ids=lambda kw: ",".join("%s=%s" % i for i in kw.items()))
+def test_bwd_rejects(kw):
+    assert _bwd(**kw) == nl.ERR_INVALID_ARG
+
+
+def test_dr_may_alias_dx_and_zero_rows_need_no_pointers():
+    # dR == dX passes the checks; with no device the call then fails at the device query
+    assert _bwd(dR=FAKE * 4) == nl.ERR_HIP
+    # M == 0: the forward is a no-op that needs no row pointers and no device
+    assert _fwd(M=0, X=None, Y=None) == nl.OK
+
+
+def test_tuning_rejects_bad_values():
+    lib = nl.lib()
+    assert lib.norm_set_tuning(nl.TUNE_SCHEME, 7) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, 3) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_tuning(nl.TUNE_TEAM_THREADS, 100) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_tuning(99, 1) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_tuning(nl.TUNE_SCHEME, -1) == nl.OK
+
+
+# ---- the dispatcher --------------------------------------------------------------------------
+
+BF, F = torch.bfloat16, torch.float32
+
+
+def test_scheme_boundaries():
+    # one row per wavefront up to N = 1024, a team of wavefronts above, split for long rows
+    for dt in (BF, F):
+        assert nl.norm_plan(0, dt, 0, 4096, 1024)["scheme"] == nl.SCHEME_WAVE
+        assert nl.norm_plan(0, dt, 0, 4096, 1025)["scheme"] == nl.SCHEME_BLOCK
+        assert nl.norm_plan(1, dt, 1, 4096, 1024)["scheme"] == nl.SCHEME_WAVE
+        assert nl.norm_plan(1, dt, 1, 4096, 1032)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 0, 256, 262144)["scheme"] == nl.SCHEME_SPLIT
+    assert nl.norm_plan(1, BF, 1, 4, 4194304)["scheme"] == nl.SCHEME_SPLIT
+    assert nl.norm_plan(0, BF, 0, 16384, 16384)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 0, 16384, 16392)["scheme"] == nl.SCHEME_SPLIT
+
+
+def test_vector_path_needs_alignment_and_width():
+    assert nl.norm_plan(0, BF, 0, 64, 4096)["vector"] == 1
+    assert nl.norm_plan(0, BF, 0, 64, 4096, aligned=False)["vector"] == 0
+    assert nl.norm_plan(0, BF, 0, 64, 4100)["vector"] == 0   # 4100 % 8 != 0
+    assert nl.norm_plan(0, F, 0, 64, 4100)["vector"] == 1    # 4100 % 4 == 0
+    assert nl.norm_plan(0, F, 0, 64, 4100)["elems_per_access"] == 4
+
+
+@pytest.mark.parametrize("dt", [BF, F])
+@pytest.mark.parametrize("N", [1, 7, 64, 1000, 1024, 1025, 2048, 4096, 5120, 7168, 8192, 16384,
+                               65535, 262144, 4194304])
+@pytest.mark.parametrize("M", [1, 3, 4, 256, 16384, 65536])
+@pytest.mark.parametrize("pass_", [0, 1])
+def test_plan_covers_every_row_and_column(dt, N, M, pass_):
+    for aligned in (True, False):
+        p = nl.norm_plan(0, dt, pass_, M, N, aligned=aligned)
+        epv = p["elems_per_access"]
+        nacc = -(-N // epv) if not p["vector"] else N // epv
+        assert p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024
+        assert p["grid"] >= 1
+        if p["scheme"] == nl.SCHEME_SPLIT:
+            assert p["chunks"] * p["chunk_elems"] >= N
+            assert (p["chunks"] - 1) * p["chunk_elems"] < N
+            if pass_ == 1:
+                assert p["grid"] == p["chunks"] * p["row_groups"]
+                assert p["partials"] == p["row_groups"] <= M
+        else:
+            # a team's registers cover the whole row
+            assert p["team_threads"] * p["accesses_per_thread"] >= nacc
+            if pass_ == 1:
+                assert p["partials"] == p["grid"]
+        if pass_ == 1:
+            assert p["workspace_bytes"] >= 256 + 2 * p["partials"] * N * 4
+
+
+def test_plan_tuning_overrides():
+    try:
+        nl.norm_set_tuning(nl.TUNE_SCHEME, nl.SCHEME_SPLIT)
+        assert nl.norm_plan(0, BF, 0, 64, 512)["scheme"] == nl.SCHEME_SPLIT
+        nl.norm_set_tuning(nl.TUNE_SCHEME, nl.SCHEME_BLOCK)
+        assert nl.norm_plan(0, BF, 0, 64, 512)["scheme"] == nl.SCHEME_BLOCK
+        nl.norm_set_tuning(nl.TUNE_SCHEME, nl.SCHEME_WAVE)
+        with pytest.raises(nl.NormError):
+            nl.norm_plan(0, BF, 0, 64, 65536)      # a wavefront cannot hold this row
+        nl.norm_set_tuning(nl.TUNE_SCHEME, -1)
+        nl.norm_set_tuning(nl.TUNE_GRID_PER_CU, 1)
+        assert nl.norm_plan(0, BF, 1, 65536, 4096, cu_count=256)["partials"] == 256
+        nl.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, 2)
+        assert nl.norm_plan(0, BF, 0, 65536, 512)["rows_per_iter"] == 2
+    finally:
+        for k in range(6):
+            nl.norm_set_tuning(k, -1)
+
+
+def test_workspace_needs_a_device_here():
+    with pytest.raises(nl.NormError) as e:
+        nl.norm_workspace_size(0, BF, 1, 16, 4096)
+    assert e.value.status == nl.ERR_HIP
