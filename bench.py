@@ -1,0 +1,333 @@
+#!/usr/bin/env python3
+"""Benchmark of the row-wise norm hot path on one MI355X.
+
+Headline workload: LayerNorm forward + backward, bf16 storage with fp32 arithmetic,
+M = 16384 rows x N = 4096, X ~ N(0,1), dY ~ N(0,1), gamma ~ N(1,0.1), beta ~ N(0,0.1),
+eps = 1e-5, synthetic seeded data. One step = norm_fwd on one buffer set, then the backward
+(norm_bwd_fused + norm_bwd_reduce, which is exactly what norm_bwd runs) on another set. Sets
+rotate over more than 1 GiB, so every pass starts with its inputs in HBM, not in the 256 MB
+memory-side cache, and the backward never finds what the forward just touched.
+
+Printed (rank 0, one JSON line): achieved HBM GB/s of forward + backward (algorithmic bytes /
+measured time), with the forward and backward figures, a roofline entry for the dominant
+kernel (the fused backward pass, timed with HIP events around each launch inside the timed
+region) and the CPU oracle timed on this host as a reported baseline.
+
+--sweep also measures every workload shape (forward, backward, both) and writes the table to
+stderr and to --sweep-out.
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+CSRC = os.path.join(ROOT, "deep_learning_normalization_amd", "csrc")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash():
+    """Hash of the HIP sources and the dispatcher: a counter capture is valid only for it."""
+    h = hashlib.sha256()
+    for name in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(name.encode() + b"\0" + f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(workload_name):
+    """HBM bytes per launch of the fused backward from the committed rocprofv3 counter summary,
+    or None if there is none or the kernels changed since it was taken."""
+    path = os.path.join(PROFILES, "traffic_%s.json" % workload_name)
+    if not os.path.exists(path):
+        return None, "no counter summary"
+    with open(path) as f:
+        d = json.load(f)
+    if d.get("kernel_source_hash") != kernel_source_hash():
+        return None, "kernels changed since the counters were taken"
+    return d, None
+
+
+class BufferSet:
+    """One set of device tensors for a workload (inputs copied from host, outputs empty)."""
+
+    def __init__(self, host, dev, torch):
+        self.t = {k: (v.to(dev) if v is not None else None) for k, v in host.items()}
+        X = self.t["X"]
+        M = X.shape[0]
+        self.Y = torch.empty_like(X)
+        self.H = torch.empty_like(X) if self.t["R"] is not None else None
+        self.mean = torch.empty(M, dtype=torch.float32, device=dev)
+        self.rstd = torch.empty(M, dtype=torch.float32, device=dev)
+        self.dX = torch.empty_like(X)
+
+
+def set_bytes(host):
+    n = sum(v.numel() * v.element_size() for v in host.values() if v is not None and v.dim() == 2)
+    X = host["X"]
+    outs = 2 if host["dY"] is not None else 1
+    if host["R"] is not None:
+        outs += 1
+    return n + outs * X.numel() * X.element_size()
+
+
+def timed_workload(w, steps, warmup, torch, nl, traffic, want_bwd=True, min_footprint=1 << 30,
+                   max_sets=64, step_events=True):
+    """Cold-cache timing of one workload: forward on set i, backward on set i + S/2."""
+    from deep_learning_normalization_amd import inputs
+    dev = torch.device("cuda:0")
+    host = inputs.make(w)
+    sb = set_bytes(host)
+    S = max(2, min(max_sets, -(-min_footprint // sb)))
+    if S % 2:
+        S += 1
+    sets = [BufferSet(host, dev, torch) for _ in range(S)]
+    shared = sets[0].t
+    W, B = shared["W"], shared["B"]
+    M, N = w.M, w.N
+    kind = w.kind
+    eps = w.eps
+    want_bwd = want_bwd and w.dy is not None
+    wsf = nl.workspace(kind, host["X"].dtype, nl.PASS_FWD, M, N, w.r is not None)
+    wsb = nl.workspace(kind, host["X"].dtype, nl.PASS_BWD, M, N) if want_bwd else None
+    dW = torch.empty_like(W)
+    dB = torch.empty_like(W) if kind == "layernorm" else None
+    stream = torch.cuda.current_stream()
+
+    def fwd(s):
+        nl.norm_fwd(kind, s.t["X"], s.t["R"], W, B, eps, s.Y, s.H,
+                    s.mean if kind == "layernorm" else None, s.rstd, wsf)
+
+    def bwd_fused(s):
+        Xin = s.H if s.H is not None else s.t["X"]
+        nl.norm_bwd_fused(kind, Xin, s.t["dY"], None, W,
+                          s.mean if kind == "layernorm" else None, s.rstd, eps, s.dX, None, wsb)
+
+    def bwd_reduce():
+        nl.norm_bwd_reduce(kind, M, N, dW, dB, wsb)
+
+    for s in sets:  # every set gets its statistics (and H) before the backward reads them
+        fwd(s)
+    for i in range(warmup):
+        fwd(sets[i % S])
+        if want_bwd:
+            bwd_fused(sets[(i + S // 2) % S])
+            bwd_reduce()
+    torch.cuda.synchronize()
+
+    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    start, end = ev(), ev()
+    fe = [(ev(), ev()) for _ in range(steps)] if step_events else None
+    be = [(ev(), ev()) for _ in range(steps)] if (step_events and want_bwd) else None
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record(stream)
+    for i in range(steps):
+        if fe:
+            fe[i][0].record(stream)
+        fwd(sets[i % S])
+        if fe:
+            fe[i][1].record(stream)
+        if want_bwd:
+            if be:
+                be[i][0].record(stream)
+            bwd_fused(sets[(i + S // 2) % S])
+            if be:
+                be[i][1].record(stream)
+            bwd_reduce()
+    end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = start.elapsed_time(end) / steps
+    out = {"sets": S, "set_bytes": sb, "ms_per_step": ms_step, "wall_s": wall}
+    if fe:
+        f_ms = sorted(a.elapsed_time(b) for a, b in fe)
+        out["fwd_us_median"] = 1e3 * f_ms[len(f_ms) // 2]
+        out["fwd_us_mean"] = 1e3 * sum(f_ms) / len(f_ms)
+    if be:
+        b_ms = sorted(a.elapsed_time(b) for a, b in be)
+        out["bwd_fused_us_median"] = 1e3 * b_ms[len(b_ms) // 2]
+        out["bwd_fused_us_mean"] = 1e3 * sum(b_ms) / len(b_ms)
+    del sets
+    torch.cuda.empty_cache()
+    return out
+
+
+def copy_ceiling(torch, nbytes=1 << 30, iters=20):
+    """Achievable HBM bandwidth of a plain device copy (torch's copy kernel), GB/s moved
+    (read + write). Two buffer pairs alternate so neither copy starts in cache."""
+    n = nbytes // 2
+    bufs = [(torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(),
+             torch.empty(n, dtype=torch.bfloat16, device="cuda")) for _ in range(2)]
+    for s, d in bufs:
+        d.copy_(s)
+    torch.cuda.synchronize()
+    times = []
+    for i in range(iters):
+        s, d = bufs[i % 2]
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        d.copy_(s)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    times.sort()
+    med = times[len(times) // 2]
+    return 2 * nbytes / (med * 1e-3) / 1e9, med * 1e3
+
+
+def cpu_baseline(w):
+    """The CPU oracle (double precision, OpenMP) on this host: forward then backward of the
+    whole workload, median of 3, as GB/s over the same algorithmic bytes as the GPU."""
+    import oracle
+    from deep_learning_normalization_amd import inputs, traffic
+    host = inputs.make(w)
+    bits = {k: inputs.host_bits(host[k]) for k in ("X", "W", "B", "dY")}
+    kind = oracle.LAYERNORM if w.kind == "layernorm" else oracle.RMSNORM
+    dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+    eps = float(w.eps)
+    times = []
+    for _ in range(3):
+        t0 = time.perf_counter()
+        oracle.fwd(kind, dt, bits["X"], bits["W"], bits["B"], eps=eps)
+        oracle.bwd(kind, dt, bits["X"], bits["dY"], bits["W"], eps=eps)
+        times.append(time.perf_counter() - t0)
+    times.sort()
+    t = times[1]
+    nbytes = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N) + traffic.bwd_bytes(w.kind, w.dtype,
+                                                                               w.M, w.N)
+    cpu = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return {"value": round(nbytes / t / 1e9, 3), "unit": "GB/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "whole workload (%d x %d), forward + backward incl. dW/dB, median of 3 runs "
+                      "(%.3f s each); %s" % (w.M, w.N, t, cpu),
+            "seconds": round(t, 4), "rows_per_s": round(w.M / t, 1)}
+
+
+def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
+    from deep_learning_normalization_amd import inputs, traffic
+    rows = []
+    for w in inputs.all_workloads():
+        r = timed_workload(w, steps, warmup, torch, nl, traffic)
+        fb = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=w.r is not None)
+        row = {"workload": w.name, "kind": w.kind, "dtype": w.dtype, "M": w.M, "N": w.N,
+               "residual": w.r is not None, "sets": r["sets"],
+               "fwd_us": round(r["fwd_us_median"], 2),
+               "fwd_GBps": round(fb / (r["fwd_us_median"] * 1e-6) / 1e9, 1)}
+        row["fwd_frac_peak"] = round(row["fwd_GBps"] / PEAK_HBM_GBPS, 4)
+        row["fwd_frac_copy"] = round(row["fwd_GBps"] / copy_gbps, 4)
+        row["fwd_rows_per_s"] = round(w.M / (r["fwd_us_median"] * 1e-6), 1)
+        if w.dy is not None:
+            bb = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N)
+            bfb = traffic.bwd_fused_bytes(w.kind, w.dtype, w.M, w.N)
+            step_us = r["ms_per_step"] * 1e3
+            row.update({"bwd_fused_us": round(r["bwd_fused_us_median"], 2),
+                        "bwd_fused_GBps": round(bfb / (r["bwd_fused_us_median"] * 1e-6) / 1e9, 1),
+                        "step_us": round(step_us, 2),
+                        "fwd_bwd_GBps": round((fb + bb) / (step_us * 1e-6) / 1e9, 1)})
+            row["fwd_bwd_frac_peak"] = round(row["fwd_bwd_GBps"] / PEAK_HBM_GBPS, 4)
+            row["fwd_bwd_frac_copy"] = round(row["fwd_bwd_GBps"] / copy_gbps, 4)
+        rows.append(row)
+        sys.stderr.write(json.dumps(row) + "\n")
+        sys.stderr.flush()
+    if out_path:
+        with open(out_path, "w") as f:
+            json.dump({"copy_ceiling_GBps": copy_gbps, "rows": rows}, f, indent=1)
+    return rows
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--sweep", action="store_true", help="also time every workload shape")
+    ap.add_argument("--sweep-out", default=None)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures a single MI355X only (rows are independent: a multi-GPU run "
+              "would shard rows and all-reduce dW/dB). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from deep_learning_normalization_amd import inputs, normlib as nl, traffic
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    nl.lib()  # fails loudly if libnorm.so is missing
+
+    w = inputs.LN_BF16_16384x4096
+    copy_gbps, copy_us = copy_ceiling(torch)
+    r = timed_workload(w, args.steps, args.warmup, torch, nl, traffic)
+    M, N = w.M, w.N
+    fb = traffic.fwd_bytes(w.kind, w.dtype, M, N)
+    bb = traffic.bwd_bytes(w.kind, w.dtype, M, N)
+    bfb = traffic.bwd_fused_bytes(w.kind, w.dtype, M, N)
+    ms = r["ms_per_step"]
+    value = (fb + bb) / (ms * 1e-3) / 1e9
+    # dominant kernel: the fused backward pass; mean launch duration over the timed steps
+    bwd_us = r["bwd_fused_us_mean"]
+    achieved = bfb / (bwd_us * 1e-6) / 1e9
+    tr, why = load_traffic(w.name)
+    traffic_bytes = None
+    if tr is not None:
+        traffic_bytes = tr["hbm_bytes_per_launch"]
+    line = {
+        "metric": "achieved HBM GB/s (% of peak) for norm fwd and fwd+bwd, bf16, per MxN shape",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; X~N(0,1), dY~N(0,1), gamma~N(1,0.1), beta~N(0,0.1))",
+        "config": {"workload": "layernorm_fwd_bwd_bf16", "kind": "layernorm", "M": M, "N": N,
+                   "eps": w.eps, "pass": "fwd+bwd", "buffer_sets": r["sets"],
+                   "bytes_per_step": fb + bb},
+        "roofline": {"bound": "hbm", "kernel": "team_bwd_kernel (fused dX + dW/dB partials)",
+                     "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_bytes,
+                     "algorithmic_bytes": bfb, "avg_launch_us": round(bwd_us, 3)},
+        "fwd": {"us": round(r["fwd_us_mean"], 3), "GBps": round(fb / (r["fwd_us_mean"] * 1e-6) / 1e9, 1),
+                "frac_peak": round(fb / (r["fwd_us_mean"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                "bytes": fb},
+        "fwd_bwd": {"GBps": round(value, 1), "frac_peak": round(value / PEAK_HBM_GBPS, 4),
+                    "frac_copy_ceiling": round(value / copy_gbps, 4),
+                    "rows_per_s": round(M / (ms * 1e-3), 1)},
+        "copy_ceiling": {"GBps": round(copy_gbps, 1), "us_per_GiB_copy": round(copy_us, 2),
+                         "kernel": "torch copy_ of 1 GiB, read + write counted"},
+    }
+    if traffic_bytes is None:
+        line["roofline"]["traffic_note"] = why
+    if args.sweep:
+        sweep(torch, nl, max(20, args.steps // 4), max(5, args.warmup // 4), args.sweep_out,
+              copy_gbps)
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -158,23 +158,28 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (r0 + r1) + (r2 + r3);
 }
 
-// LDS scratch for team sums: 2 alternating slots x up to 12 values x up to 16 waves.
+// LDS scratch for team sums: 2 alternating slots x up to 12 values x 16 waves, plus one row of
+// padding for the fixed-length reads below.
 constexpr int RED_VALS = 12;
 constexpr int RED_WAVES = 16;
-constexpr int RED_FLOATS = 2 * RED_VALS * RED_WAVES;
+constexpr int RED_FLOATS = 2 * RED_VALS * RED_WAVES + RED_WAVES;
 
 // Sums NV values over one team of `waves` consecutive wavefronts of the workgroup (the team's
-// first wave is `wave0`; this thread's wave is `wave`). Every thread of the workgroup must call
-// it with the same slot and NV (it contains one barrier when waves > 1). Alternating the slot
-// between consecutive calls makes one barrier per call enough: a slot is rewritten only after
-// the next call's barrier, by which time every thread has read it.
-template <int NV>
+// first wave is `wave0`, a multiple of 4; this thread's wave is `wave`). MAXW (compile time)
+// bounds `waves`. Every thread of the workgroup must call it with the same slot and NV (it
+// contains one barrier when waves > 1). Alternating the slot between consecutive calls makes
+// one barrier per call enough: a slot is rewritten only after the next call's barrier, by
+// which time every thread has read it. The read-back is branch-free: MAXW/4 broadcast 16-byte
+// LDS reads per value, adding the team's `waves` partials in wave order (words past the team
+// are read and discarded).
+template <int NV, int MAXW>
 __device__ __forceinline__ void team_sum(float (&v)[NV], float *red, int slot, int waves,
                                          int wave0, int wave, int lane) {
   static_assert(NV <= RED_VALS, "too many values for one team sum");
+  static_assert(MAXW == 1 || MAXW % 4 == 0, "wave bound must be 1 or a multiple of 4");
 #pragma unroll
   for (int i = 0; i < NV; ++i) v[i] = wave_sum(v[i]);
-  if (waves == 1) return;
+  if (MAXW == 1 || waves == 1) return;
   float *base = red + slot * (RED_VALS * RED_WAVES);
   if (lane == 0) {
 #pragma unroll
@@ -183,8 +188,16 @@ __device__ __forceinline__ void team_sum(float (&v)[NV], float *red, int slot, i
   __syncthreads();
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
+    const float4 *q = reinterpret_cast<const float4 *>(base + i * RED_WAVES + wave0);
     float s = 0.0f;
-    for (int k = 0; k < waves; ++k) s += base[i * RED_WAVES + wave0 + k];
+#pragma unroll
+    for (int j = 0; j < (MAXW == 1 ? 1 : MAXW / 4); ++j) {
+      const float4 f = q[j];
+      s += (4 * j + 0 < waves) ? f.x : 0.0f;
+      s += (4 * j + 1 < waves) ? f.y : 0.0f;
+      s += (4 * j + 2 < waves) ? f.z : 0.0f;
+      s += (4 * j + 3 < waves) ? f.w : 0.0f;
+    }
     v[i] = s;
   }
 }

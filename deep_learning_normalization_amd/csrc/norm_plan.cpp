@@ -24,6 +24,7 @@ constexpr int kWaveThreads = 256;        // wave scheme: four one-wave teams per
 constexpr int kSplitThreads = 256;
 constexpr int kWaveMaxRow = 1024;        // wave scheme for rows up to this many elements
 constexpr int kBlockTeamTarget = 512;    // preferred largest team for the block scheme
+constexpr int kBlockTeamTargetBwd = 640; // the backward prefers one access per thread longer
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -61,13 +62,20 @@ bool block_menu(bool vec, int vpt, int rows, int lb) {
   }
 }
 
-// Register budget: a 1024-thread workgroup leaves 128 VGPRs per lane, 512 threads 256.
-bool block_fits_registers(bool vec, int vpt, int rows, int lb) {
-  if (!vec) return true; // element-wise: at most 16 floats per array
+// Register budget: a 1024-thread workgroup leaves 128 VGPRs per lane, 512 threads 256. The
+// backward holds more per access (prefetched X and dY, dW and dB accumulators), so it gets
+// fewer accesses per thread; these limits are the compiled shapes that do not spill.
+bool block_fits_registers(bool vec, bool bwd, int vpt, int rows, int lb) {
   const int slots = vpt * rows;
-  if (lb >= 1024) return slots <= 2;
-  if (lb >= 512) return slots <= 4;
-  return slots <= 8;
+  if (!vec) return !bwd || vpt <= 4;
+  if (!bwd) {
+    if (lb >= 1024) return slots <= 2;
+    if (lb >= 512) return slots <= 4;
+    return slots <= 8;
+  }
+  if (lb >= 1024) return vpt == 1 && slots <= 2;
+  if (lb >= 512) return vpt <= 2 && slots <= 4;
+  return vpt <= 4 && slots <= 8;
 }
 
 bool split_fwd_menu(bool vec, int vpt) { return vec ? (vpt == 1 || vpt == 2 || vpt == 4) : vpt == 8; }
@@ -112,6 +120,10 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
     if (v != -1 && v < 1) return NORM_ERR_INVALID_ARG;
     g_tuning.row_groups = v;
     return NORM_OK;
+  case NORM_TUNE_TEAMS_PER_WG:
+    if (v != -1 && (v < 1 || v > 16)) return NORM_ERR_INVALID_ARG;
+    g_tuning.teams = (int)v;
+    return NORM_OK;
   default: return NORM_ERR_INVALID_ARG;
   }
 }
@@ -137,7 +149,7 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
   if (scheme == NORM_SCHEME_AUTO) {
     if (N <= kWaveMaxRow)
       scheme = NORM_SCHEME_WAVE;
-    else if (nacc <= (vec ? 2048 : 8192))
+    else if (nacc <= (vec ? (bwd ? 1024 : 2048) : (bwd ? 4096 : 8192)))
       scheme = NORM_SCHEME_BLOCK;
     else
       scheme = NORM_SCHEME_SPLIT;
@@ -181,12 +193,14 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
           if ((int64_t)t.team_threads * v < nacc) continue;
           cand = t.team_threads;
         }
-        const int limit = (pass_i == 0 && !use_override) ? (vec ? kBlockTeamTarget : 1024) : 1024;
+        const int limit = (pass_i == 0 && !use_override)
+                              ? (vec ? (bwd ? kBlockTeamTargetBwd : kBlockTeamTarget) : 1024)
+                              : 1024;
         if (cand > limit) continue;
         const int lb = vec ? lb_of(cand) : 1024;
         int r = want_rows;
-        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, v, r, lb)) r = 1;
-        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, v, r, lb)) continue;
+        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, bwd, v, r, lb)) r = 1;
+        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, bwd, v, r, lb)) continue;
         vpt = v;
         tt = cand;
         rows = r;
@@ -194,14 +208,29 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       }
     }
     if (!vpt) return NORM_ERR_UNSUPPORTED;
+    // Backward: several row teams share a workgroup (up to 1024 threads) when the larger
+    // workgroup still fits its registers; their dW/dB partials merge in LDS, so the partial
+    // rows written (and re-read by the column reduction) drop by the team count.
+    // (a team's partial sums sit at a 16-byte aligned LDS offset: team sizes of 4k wavefronts)
+    // Default one team per workgroup: measured on MI355X, separate workgroups (each with its
+    // own barrier) outrun one large workgroup whose barrier waits for every wavefront.
+    int teams = t.teams > 0 ? t.teams : 1;
+    if (tt % 256 != 0) teams = 1;
+    while (teams > 1 && (tt * teams > 1024 || !block_menu(vec, vpt, rows, lb_of(tt * teams)) ||
+                         !block_fits_registers(vec, bwd, vpt, rows, lb_of(tt * teams))))
+      --teams;
+    if (!vec && teams > 1 && tt * teams > 1024) teams = 1;
     p.vpt = vpt;
     p.rows = rows;
     p.team_threads = tt;
-    p.threads = tt;
-    p.lb = lb_pick;
-    const int64_t groups = cdiv(Mm, rows);
-    const int64_t per_cu_threads = bwd ? 1024 : 2048;
-    const int64_t gpc_default = per_cu_threads / p.threads > 0 ? per_cu_threads / p.threads : 1;
+    p.threads = tt * teams;
+    p.lb = vec ? (teams > 1 ? lb_of(p.threads) : lb_pick) : 1024;
+    const int64_t groups = cdiv(Mm, (int64_t)rows * teams);
+    // Workgroups per CU: enough 16-byte accesses in flight per CU (about 2048 for the forward,
+    // 1024 per tensor for the backward, whose workgroups also each write a partial row).
+    const int64_t per_cu = bwd ? 1024 : 2048;
+    const int64_t load = (int64_t)p.threads * vpt * rows;
+    const int64_t gpc_default = per_cu / load > 0 ? per_cu / load : 1;
     const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : gpc_default;
     p.grid = groups < cu * gpc ? groups : cu * gpc;
   } else if (scheme == NORM_SCHEME_SPLIT) {

@@ -47,6 +47,7 @@ struct Tuning {
   int team_threads = -1;
   int64_t split_chunk = -1;
   int64_t row_groups = -1;
+  int teams = -1;
 };
 
 const Tuning &tuning();

@@ -66,7 +66,7 @@ __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, in
     float s[1] = {0.0f};
     for (int64_t c = tid; c < C; c += blockDim.x)
       s[0] += chunk_count(c, chunk_acc, nacc, E) * (rp[RP * c] - shift) + rp[RP * c + 2];
-    team_sum<1>(s, red, slot, waves, 0, wave, lane);
+    team_sum<1, SPLIT_LB / 64>(s, red, slot, waves, 0, wave, lane);
     slot ^= 1;
     delta = s[0] * inv_n;
     float q[1] = {0.0f};
@@ -74,13 +74,13 @@ __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, in
       const float e = (rp[RP * c] - shift) - delta;
       q[0] += rp[RP * c + 1] + 2.0f * e * rp[RP * c + 2] + chunk_count(c, chunk_acc, nacc, E) * e * e;
     }
-    team_sum<1>(q, red, slot, waves, 0, wave, lane);
+    team_sum<1, SPLIT_LB / 64>(q, red, slot, waves, 0, wave, lane);
     slot ^= 1;
     rstd = rsqrt_f32(fmaxf(q[0] * inv_n, 0.0f) + eps);
   } else {
     float q[1] = {0.0f};
     for (int64_t c = tid; c < C; c += blockDim.x) q[0] += rp[RP * c];
-    team_sum<1>(q, red, slot, waves, 0, wave, lane);
+    team_sum<1, SPLIT_LB / 64>(q, red, slot, waves, 0, wave, lane);
     slot ^= 1;
     shift = 0.0f;
     delta = 0.0f;
@@ -95,7 +95,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
   const int64_t C = a.chunks;
   const int64_t row = (int64_t)blockIdx.x / C;
@@ -145,7 +145,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
       for (int e = 0; e < E; ++e) s[0] += x[k][e];
-    team_sum<1>(s, red, slot, waves, 0, wave, lane);
+    team_sum<1, SPLIT_LB / 64>(s, red, slot, waves, 0, wave, lane);
     slot ^= 1;
     const float mc = s[0] / n_c;
     float qc[2] = {0.0f, 0.0f};
@@ -159,7 +159,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
         qc[1] += d;
       }
     }
-    team_sum<2>(qc, red, slot, waves, 0, wave, lane);
+    team_sum<2, SPLIT_LB / 64>(qc, red, slot, waves, 0, wave, lane);
     if (tid == 0) {
       out[0] = mc;
       out[1] = qc[0];
@@ -171,7 +171,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
     for (int k = 0; k < VPT; ++k)
 #pragma unroll
       for (int e = 0; e < E; ++e) q[0] += x[k][e] * x[k][e];
-    team_sum<1>(q, red, slot, waves, 0, wave, lane);
+    team_sum<1, SPLIT_LB / 64>(q, red, slot, waves, 0, wave, lane);
     if (tid == 0) out[0] = q[0];
   }
 }
@@ -183,7 +183,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   const int tid = threadIdx.x;
   const int64_t C = a.chunks;
   const int64_t b = reverse_within_xcd(blockIdx.x, gridDim.x);
@@ -238,7 +238,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
 // ---- backward: statistics when the forward's were not kept ------------------------------
 
 __global__ __launch_bounds__(SPLIT_LB) void split_finalize_stats_kernel(BwdArgs a, int E) {
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   const int64_t row = blockIdx.x;
   int slot = 0;
   float shift, delta, rstd;
@@ -257,7 +257,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
   const int64_t C = a.chunks;
   const int64_t g = (int64_t)blockIdx.x / C;
@@ -326,7 +326,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
         }
       }
     }
-    team_sum<NV>(sums, red, slot, waves, 0, wave, lane);
+    team_sum<NV, SPLIT_LB / 64>(sums, red, slot, waves, 0, wave, lane);
     slot ^= 1;
     if (tid == 0) {
 #pragma unroll
@@ -351,7 +351,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
   const int64_t C = a.chunks;
   const int64_t g = (int64_t)blockIdx.x / C;
@@ -423,7 +423,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
         }
       }
     }
-    team_sum<NV>(sums, red, slot, waves, 0, wave, lane);
+    team_sum<NV, SPLIT_LB / 64>(sums, red, slot, waves, 0, wave, lane);
     slot ^= 1;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   const TeamGeom gm = team_geom<WAVE>(team_threads);
   const int nacc = a.nacc;
   const int64_t M = a.M;
@@ -87,28 +87,44 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   }
 
   const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
+  // Software pipeline: the next row group's loads are issued before the current group is
+  // reduced and written, so every wavefront keeps requests in flight across its barriers.
+  raw px[ROWS][VPT], pr[ROWS][RESID ? VPT : 1];
+  auto issue = [&](int64_t g) {
+    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = row0 + r < M;
+      const int64_t base = (row0 + r) * N;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = gm.t + k * gm.tt;
+        px[r][k] = A::zero();
+        if (RESID) pr[r][k] = A::zero();
+        if (rv && v < nacc) {
+          px[r][k] = A::ld(X + base + (int64_t)v * E);
+          if (RESID) pr[r][k] = A::ld(Rr + base + (int64_t)v * E);
+        }
+      }
+    }
+  };
   int slot = 0;
-  for (int64_t g = blockIdx.x; g * rows_per_group < M; g += gridDim.x) {
+  int64_t g = blockIdx.x;
+  issue(g);
+  for (; g * rows_per_group < M; g += gridDim.x) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
     float x[ROWS][VPT][E];
     {
       raw rx[ROWS][VPT];
       raw rr[ROWS][RESID ? VPT : 1];
 #pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        const bool rv = row0 + r < M;
-        const int64_t base = (row0 + r) * N;
+      for (int r = 0; r < ROWS; ++r)
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
-          const int v = gm.t + k * gm.tt;
-          rx[r][k] = A::zero();
-          if (RESID) rr[r][k] = A::zero();
-          if (rv && v < nacc) {
-            rx[r][k] = A::ld(X + base + (int64_t)v * E);
-            if (RESID) rr[r][k] = A::ld(Rr + base + (int64_t)v * E);
-          }
+          rx[r][k] = px[r][k];
+          if (RESID) rr[r][k] = pr[r][k];
         }
-      }
+      issue(g + gridDim.x);
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         const bool rv = row0 + r < M;
@@ -147,7 +163,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
           for (int e = 0; e < E; ++e) acc += x[r][k][e];
         s[r] = acc;
       }
-      team_sum<ROWS>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+      team_sum<ROWS, (WAVE ? 1 : LB / 64)>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
       slot ^= 1;
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) mean1[r] = mul_rn(s[r], a.inv_n);
@@ -168,7 +184,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
         qc[r] = q;
         qc[ROWS + r] = c;
       }
-      team_sum<2 * ROWS>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+      team_sum<2 * ROWS, (WAVE ? 1 : LB / 64)>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
       slot ^= 1;
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
@@ -187,7 +203,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
           for (int e = 0; e < E; ++e) acc += x[r][k][e] * x[r][k][e];
         q[r] = acc;
       }
-      team_sum<ROWS>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+      team_sum<ROWS, (WAVE ? 1 : LB / 64)>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
       slot ^= 1;
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
@@ -228,7 +244,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
-  __shared__ float red[RED_FLOATS];
+  __shared__ __align__(16) float red[RED_FLOATS];
   __shared__ float merge[MERGE_FLOATS];
   const TeamGeom gm = team_geom<WAVE>(team_threads);
   const int nacc = a.nacc;
@@ -243,13 +259,14 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   const bool have_stats = a.rstd != nullptr;
   write_ws_header(a.header, a.partials, N);
 
-  float w[VPT][E], accw[VPT][E], accb[LN ? VPT : 1][E];
+  // the weight stays in its storage format (half the registers for bf16), unpacked at use
+  raw rw[VPT];
+  float accw[VPT][E], accb[LN ? VPT : 1][E];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = gm.t + k * gm.tt;
-    raw rw = A::zero();
-    if (v < nacc) rw = A::ld_cached(W + (int64_t)v * E);
-    A::unpack(rw, w[k]);
+    rw[k] = A::zero();
+    if (v < nacc) rw[k] = A::ld_cached(W + (int64_t)v * E);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       accw[k][e] = 0.0f;
@@ -258,10 +275,11 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   }
 
   const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
-  int slot = 0;
-  for (int64_t g = blockIdx.x; g * rows_per_group < M; g += gridDim.x) {
+  // Software pipeline: X and dY of the next row group are requested before this group's
+  // reductions and stores.
+  raw px[ROWS][VPT], pdy[ROWS][VPT];
+  auto issue = [&](int64_t g) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
-    raw rx[ROWS][VPT], rdy[ROWS][VPT];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = row0 + r < M;
@@ -269,14 +287,29 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
-        rx[r][k] = A::zero();
-        rdy[r][k] = A::zero();
+        px[r][k] = A::zero();
+        pdy[r][k] = A::zero();
         if (rv && v < nacc) {
-          rx[r][k] = A::ld(X + base + (int64_t)v * E);
-          rdy[r][k] = A::ld(DY + base + (int64_t)v * E);
+          px[r][k] = A::ld(X + base + (int64_t)v * E);
+          pdy[r][k] = A::ld(DY + base + (int64_t)v * E);
         }
       }
     }
+  };
+  int slot = 0;
+  int64_t g = blockIdx.x;
+  issue(g);
+  for (; g * rows_per_group < M; g += gridDim.x) {
+    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
+    raw rx[ROWS][VPT], rdy[ROWS][VPT];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r)
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        rx[r][k] = px[r][k];
+        rdy[r][k] = pdy[r][k];
+      }
+    issue(g + gridDim.x);
     // m: the row mean the forward saved (LayerNorm), or a first-pass mean when recomputing.
     // The reduction below also sums x - m, so the exact mean m + delta is used for xhat.
     float m[ROWS], rstd[ROWS];
@@ -303,7 +336,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           }
           s[r] = acc;
         }
-        team_sum<ROWS>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        team_sum<ROWS, (WAVE ? 1 : LB / 64)>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
         slot ^= 1;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) m[r] = mul_rn(s[r], a.inv_n);
@@ -326,7 +359,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           qc[r] = q;
           qc[ROWS + r] = c;
         }
-        team_sum<2 * ROWS>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        team_sum<2 * ROWS, (WAVE ? 1 : LB / 64)>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
         slot ^= 1;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -347,7 +380,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           }
           q[r] = acc;
         }
-        team_sum<ROWS>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        team_sum<ROWS, (WAVE ? 1 : LB / 64)>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
         slot ^= 1;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -371,13 +404,14 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const bool in = rv && gm.t + k * gm.tt < nacc;
-        float xf[E], df[E];
+        float xf[E], df[E], wf[E];
         A::unpack(rx[r][k], xf);
         A::unpack(rdy[r][k], df);
+        A::unpack(rw[k], wf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float d = in ? xf[e] - m[r] : 0.0f;
-          const float gg = df[e] * w[k][e];
+          const float gg = df[e] * wf[e];
           sums[r] += gg * d;
           if constexpr (LN) {
             sums[ROWS + r] += gg;
@@ -386,7 +420,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         }
       }
     }
-    team_sum<NV>(sums, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+    team_sum<NV, (WAVE ? 1 : LB / 64)>(sums, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
     slot ^= 1;
 
 #pragma unroll
@@ -402,15 +436,16 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
         const bool in = v < nacc;
-        float xf[E], df[E], dx[E];
+        float xf[E], df[E], wf[E], dx[E];
         A::unpack(rx[r][k], xf);
         A::unpack(rdy[r][k], df);
+        A::unpack(rw[k], wf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           // rows past M and columns past N hold zeros and must add nothing (even if rstd is
           // infinite there, as for eps = 0)
           const float xh = (rv && in) ? ((xf[e] - m[r]) - delta) * rstd[r] : 0.0f;
-          const float gg = df[e] * w[k][e];
+          const float gg = df[e] * wf[e];
           dx[e] = rstd[r] * (gg - c1 - xh * c2);
           accw[k][e] += df[e] * xh;
           if constexpr (LN) accb[k][e] += df[e];
@@ -518,6 +553,60 @@ __global__ __launch_bounds__(256) void colsum_kernel(ReduceArgs a) {
       dst[col] = t;
     } else {
       dst[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
+    }
+  }
+}
+
+// The same sum with 16-byte loads, for N % 4 == 0 (every partial row is then 16-byte
+// aligned): a workgroup covers 32 columns of one quantity; its 256 threads are 8 column
+// quads x 32 slices of the partial rows; slice s sums rows s, s + 32, ... in ascending order,
+// then the 32 slice sums of a column are added in slice order.
+template <typename T>
+__global__ __launch_bounds__(256) void colsum4_kernel(ReduceArgs a) {
+  __shared__ float part[32][33];
+  const int q = threadIdx.x & 7;
+  const int slice = threadIdx.x >> 3;
+  const int64_t N = a.N;
+  const int64_t col0 = (int64_t)blockIdx.x * 32 + q * 4;
+  const int64_t P = a.header[1];
+  const bool valid = a.header[0] == kWsMagic && a.header[2] == N && P >= 1 && P <= a.max_partials;
+  const float *src = a.colpart + (int64_t)blockIdx.y * (valid ? P : 0) * N;
+  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+  if (valid && col0 < N) {
+    int64_t p = slice;
+    for (; p + 96 < P; p += 128) {
+      const float4 v0 = *reinterpret_cast<const float4 *>(src + p * N + col0);
+      const float4 v1 = *reinterpret_cast<const float4 *>(src + (p + 32) * N + col0);
+      const float4 v2 = *reinterpret_cast<const float4 *>(src + (p + 64) * N + col0);
+      const float4 v3 = *reinterpret_cast<const float4 *>(src + (p + 96) * N + col0);
+      s0 += v0.x; s1 += v0.y; s2 += v0.z; s3 += v0.w;
+      s0 += v1.x; s1 += v1.y; s2 += v1.z; s3 += v1.w;
+      s0 += v2.x; s1 += v2.y; s2 += v2.z; s3 += v2.w;
+      s0 += v3.x; s1 += v3.y; s2 += v3.z; s3 += v3.w;
+    }
+    for (; p < P; p += 32) {
+      const float4 v = *reinterpret_cast<const float4 *>(src + p * N + col0);
+      s0 += v.x; s1 += v.y; s2 += v.z; s3 += v.w;
+    }
+  }
+  part[slice][q * 4 + 0] = s0;
+  part[slice][q * 4 + 1] = s1;
+  part[slice][q * 4 + 2] = s2;
+  part[slice][q * 4 + 3] = s3;
+  __syncthreads();
+  if (threadIdx.x < 32) {
+    const int c = threadIdx.x;
+    const int64_t col = (int64_t)blockIdx.x * 32 + c;
+    float t = 0.0f;
+    for (int sl = 0; sl < 32; ++sl) t += part[sl][c];
+    if (!valid) t = __builtin_nanf("");
+    if (col < N) {
+      T *dst = static_cast<T *>(blockIdx.y == 0 ? a.dw : a.db);
+      if constexpr (sizeof(T) == 4) {
+        dst[col] = t;
+      } else {
+        dst[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
+      }
     }
   }
 }
@@ -681,11 +770,20 @@ norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s) {
 }
 
 norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)((a.N + 63) / 64), a.db ? 2u : 1u), block(256);
-  if (dtype == NORM_F32)
-    hipLaunchKernelGGL(colsum_kernel<float>, grid, block, 0, s, a);
-  else
-    hipLaunchKernelGGL(colsum_kernel<bf16_bits>, grid, block, 0, s, a);
+  const unsigned q = a.db ? 2u : 1u;
+  if (a.N % 4 == 0) {
+    dim3 grid((unsigned)((a.N + 31) / 32), q), block(256);
+    if (dtype == NORM_F32)
+      hipLaunchKernelGGL(colsum4_kernel<float>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(colsum4_kernel<bf16_bits>, grid, block, 0, s, a);
+  } else {
+    dim3 grid((unsigned)((a.N + 63) / 64), q), block(256);
+    if (dtype == NORM_F32)
+      hipLaunchKernelGGL(colsum_kernel<float>, grid, block, 0, s, a);
+    else
+      hipLaunchKernelGGL(colsum_kernel<bf16_bits>, grid, block, 0, s, a);
+  }
   return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 

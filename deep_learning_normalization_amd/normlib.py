@@ -18,7 +18,7 @@ F32, BF16 = 0, 1
 PASS_FWD, PASS_BWD = 0, 1
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT = -1, 0, 1, 2
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
-TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS = 4, 5
+TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG = 4, 5, 6
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 

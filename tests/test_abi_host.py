@@ -145,6 +145,9 @@ def test_scheme_boundaries():
     assert nl.norm_plan(1, BF, 1, 4, 4194304)["scheme"] == nl.SCHEME_SPLIT
     assert nl.norm_plan(0, BF, 0, 16384, 16384)["scheme"] == nl.SCHEME_BLOCK
     assert nl.norm_plan(0, BF, 0, 16384, 16392)["scheme"] == nl.SCHEME_SPLIT
+    # the backward holds twice the state per element: its block rows end at 8192 bf16
+    assert nl.norm_plan(0, BF, 1, 16384, 8192)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 1, 16384, 8200)["scheme"] == nl.SCHEME_SPLIT
 
 
 def test_vector_path_needs_alignment_and_width():
@@ -197,7 +200,7 @@ def test_plan_tuning_overrides():
         nl.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, 2)
         assert nl.norm_plan(0, BF, 0, 65536, 512)["rows_per_iter"] == 2
     finally:
-        for k in range(6):
+        for k in range(7):
             nl.norm_set_tuning(k, -1)
 
 

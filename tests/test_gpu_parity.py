@@ -86,8 +86,8 @@ def test_forced_scheme(name, scheme, Ns, dt, kind):
     for N in Ns:
         if name == "wave" and N * esize > 64 * 8 * 16:
             continue  # longer than one wavefront's registers
-        if name == "block" and N * esize > 2048 * 16:
-            continue  # longer than a team's registers (2048 16-byte accesses)
+        if name == "block" and N * esize > 1024 * 16:
+            continue  # longer than a backward team's registers (1024 16-byte accesses)
         for M in (1, 5, 300):
             _say("forced %s %s %s %dx%d" % (name, kind, dt, M, N))
             with tuned(scheme=scheme):
@@ -103,6 +103,7 @@ KNOBS = [
     dict(scheme=nl.SCHEME_SPLIT, split_chunk=2048), dict(scheme=nl.SCHEME_SPLIT, split_chunk=4096),
     dict(scheme=nl.SCHEME_SPLIT, row_groups=1), dict(scheme=nl.SCHEME_SPLIT, row_groups=7),
     dict(scheme=nl.SCHEME_SPLIT, rows=1), dict(scheme=nl.SCHEME_SPLIT, rows=4),
+    dict(teams=2), dict(team_threads=256, teams=4), dict(team_threads=512, teams=2, rows=2),
 ]
 
 
