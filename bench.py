@@ -10,14 +10,14 @@ memory-side cache, and the backward never finds what the forward just touched.
 
 Printed (rank 0, one JSON line): achieved HBM GB/s of forward + backward (algorithmic bytes /
 measured time), with the forward and backward figures, a roofline entry for the dominant
-kernel (the fused backward pass, timed with HIP events around each launch inside the timed
-region) and the CPU oracle timed on this host as a reported baseline.
+kernel (the fused backward pass: on every launch inside the timed region, HIP events take the
+kernel's own start and end timestamps) and the CPU oracle timed on this host as a reported
+baseline.
 
 --sweep also measures every workload shape (forward, backward, both) and writes the table to
 stderr and to --sweep-out.
 """
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -28,17 +28,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
-CSRC = os.path.join(ROOT, "deep_learning_normalization_amd", "csrc")
 PROFILES = os.path.join(ROOT, "profiles")
-
-
-def kernel_source_hash():
-    """Hash of the HIP sources and the dispatcher: a counter capture is valid only for it."""
-    h = hashlib.sha256()
-    for name in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
-    return h.hexdigest()[:16]
 
 
 def load_traffic(workload_name):
@@ -49,6 +39,7 @@ def load_traffic(workload_name):
         return None, "no counter summary"
     with open(path) as f:
         d = json.load(f)
+    from deep_learning_normalization_amd.profiling import kernel_source_hash
     if d.get("kernel_source_hash") != kernel_source_hash():
         return None, "kernels changed since the counters were taken"
     return d, None
@@ -77,9 +68,13 @@ def set_bytes(host):
     return n + outs * X.numel() * X.element_size()
 
 
-def timed_workload(w, steps, warmup, torch, nl, traffic, want_bwd=True, min_footprint=1 << 30,
-                   max_sets=64, step_events=True):
-    """Cold-cache timing of one workload: forward on set i, backward on set i + S/2."""
+def timed_workload(w, steps, warmup, torch, nl, min_footprint=1 << 30, max_sets=64):
+    """Cold-cache timing of one workload. Buffer sets rotate over more than min_footprint
+    bytes; the backward of a step uses a different set than its forward. Three loops:
+      step : forward, fused backward (its kernels' own timestamps recorded into HIP events on
+             every launch, norm_set_launch_events), column reduce;
+      fwd  : forward only;   bwd : fused backward + column reduce only.
+    Each loop is bracketed by a synchronize and a pair of events on the launch stream."""
     from deep_learning_normalization_amd import inputs
     dev = torch.device("cuda:0")
     host = inputs.make(w)
@@ -93,7 +88,7 @@ def timed_workload(w, steps, warmup, torch, nl, traffic, want_bwd=True, min_foot
     M, N = w.M, w.N
     kind = w.kind
     eps = w.eps
-    want_bwd = want_bwd and w.dy is not None
+    want_bwd = w.dy is not None
     wsf = nl.workspace(kind, host["X"].dtype, nl.PASS_FWD, M, N, w.r is not None)
     wsb = nl.workspace(kind, host["X"].dtype, nl.PASS_BWD, M, N) if want_bwd else None
     dW = torch.empty_like(W)
@@ -114,46 +109,56 @@ def timed_workload(w, steps, warmup, torch, nl, traffic, want_bwd=True, min_foot
 
     for s in sets:  # every set gets its statistics (and H) before the backward reads them
         fwd(s)
-    for i in range(warmup):
-        fwd(sets[i % S])
-        if want_bwd:
-            bwd_fused(sets[(i + S // 2) % S])
-            bwd_reduce()
-    torch.cuda.synchronize()
-
     ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-    start, end = ev(), ev()
-    fe = [(ev(), ev()) for _ in range(steps)] if step_events else None
-    be = [(ev(), ev()) for _ in range(steps)] if (step_events and want_bwd) else None
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    start.record(stream)
-    for i in range(steps):
-        if fe:
-            fe[i][0].record(stream)
+
+    def run(body, n, timed_kernels=False):
+        for i in range(warmup):
+            body(i, None)
+        torch.cuda.synchronize()
+        marks = [nl.KernelTimer() for _ in range(n)] if timed_kernels else [None] * n
+        start, end = ev(), ev()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        start.record(stream)
+        for i in range(n):
+            body(i, marks[i])
+        end.record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return start.elapsed_time(end) / n, wall, marks
+
+    out = {"sets": S, "set_bytes": sb}
+
+    def step(i, timer):
         fwd(sets[i % S])
-        if fe:
-            fe[i][1].record(stream)
         if want_bwd:
-            if be:
-                be[i][0].record(stream)
+            if timer:
+                timer.arm()  # the fused kernel's own start/end timestamps, no extra packets
             bwd_fused(sets[(i + S // 2) % S])
-            if be:
-                be[i][1].record(stream)
             bwd_reduce()
-    end.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = start.elapsed_time(end) / steps
-    out = {"sets": S, "set_bytes": sb, "ms_per_step": ms_step, "wall_s": wall}
-    if fe:
-        f_ms = sorted(a.elapsed_time(b) for a, b in fe)
-        out["fwd_us_median"] = 1e3 * f_ms[len(f_ms) // 2]
-        out["fwd_us_mean"] = 1e3 * sum(f_ms) / len(f_ms)
-    if be:
-        b_ms = sorted(a.elapsed_time(b) for a, b in be)
-        out["bwd_fused_us_median"] = 1e3 * b_ms[len(b_ms) // 2]
-        out["bwd_fused_us_mean"] = 1e3 * sum(b_ms) / len(b_ms)
+
+    # the GPU clock settles within a few hundred ms of load: run steps for >= 0.3 s first
+    t_end = time.perf_counter() + 0.3
+    i = 0
+    while time.perf_counter() < t_end or i < warmup:
+        step(i, None)
+        i += 1
+        if i % 50 == 0:
+            torch.cuda.synchronize()
+    ms, wall, marks = run(step, steps, timed_kernels=want_bwd)
+    out["ms_per_step"], out["wall_s"] = ms, wall
+    if want_bwd:
+        b = [m.elapsed_ms() for m in marks]
+        out["bwd_fused_us_mean"] = 1e3 * sum(b) / len(b)
+        out["bwd_fused_us_median"] = 1e3 * sorted(b)[len(b) // 2]
+    ms, _, _ = run(lambda i, mk: fwd(sets[i % S]), steps)
+    out["fwd_us"] = ms * 1e3
+    if want_bwd:
+        def bwd(i, mk):
+            bwd_fused(sets[i % S])
+            bwd_reduce()
+        ms, _, _ = run(bwd, steps)
+        out["bwd_us"] = ms * 1e3
     del sets
     torch.cuda.empty_cache()
     return out
@@ -178,6 +183,8 @@ def copy_ceiling(torch, nbytes=1 << 30, iters=20):
         b.record()
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b))
+    del bufs
+    torch.cuda.empty_cache()
     times.sort()
     med = times[len(times) // 2]
     return 2 * nbytes / (med * 1e-3) / 1e9, med * 1e3
@@ -223,25 +230,25 @@ def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
     from deep_learning_normalization_amd import inputs, traffic
     rows = []
     for w in inputs.all_workloads():
-        r = timed_workload(w, steps, warmup, torch, nl, traffic)
-        fb = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=w.r is not None)
+        r = timed_workload(w, steps, warmup, torch, nl)
+        res = w.r is not None
+        fb = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res)
         row = {"workload": w.name, "kind": w.kind, "dtype": w.dtype, "M": w.M, "N": w.N,
-               "residual": w.r is not None, "sets": r["sets"],
-               "fwd_us": round(r["fwd_us_median"], 2),
-               "fwd_GBps": round(fb / (r["fwd_us_median"] * 1e-6) / 1e9, 1)}
+               "residual": res, "sets": r["sets"], "fwd_us": round(r["fwd_us"], 2),
+               "fwd_GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1)}
         row["fwd_frac_peak"] = round(row["fwd_GBps"] / PEAK_HBM_GBPS, 4)
-        row["fwd_frac_copy"] = round(row["fwd_GBps"] / copy_gbps, 4)
-        row["fwd_rows_per_s"] = round(w.M / (r["fwd_us_median"] * 1e-6), 1)
+        row["fwd_rows_per_s"] = round(w.M / (r["fwd_us"] * 1e-6), 1)
         if w.dy is not None:
             bb = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N)
             bfb = traffic.bwd_fused_bytes(w.kind, w.dtype, w.M, w.N)
             step_us = r["ms_per_step"] * 1e3
-            row.update({"bwd_fused_us": round(r["bwd_fused_us_median"], 2),
-                        "bwd_fused_GBps": round(bfb / (r["bwd_fused_us_median"] * 1e-6) / 1e9, 1),
+            row.update({"bwd_us": round(r["bwd_us"], 2),
+                        "bwd_GBps": round(bb / (r["bwd_us"] * 1e-6) / 1e9, 1),
+                        "bwd_fused_event_us": round(r["bwd_fused_us_mean"], 2),
+                        "bwd_fused_GBps": round(bfb / (r["bwd_fused_us_mean"] * 1e-6) / 1e9, 1),
                         "step_us": round(step_us, 2),
                         "fwd_bwd_GBps": round((fb + bb) / (step_us * 1e-6) / 1e9, 1)})
             row["fwd_bwd_frac_peak"] = round(row["fwd_bwd_GBps"] / PEAK_HBM_GBPS, 4)
-            row["fwd_bwd_frac_copy"] = round(row["fwd_bwd_GBps"] / copy_gbps, 4)
         rows.append(row)
         sys.stderr.write(json.dumps(row) + "\n")
         sys.stderr.flush()
@@ -275,8 +282,8 @@ def main():
     nl.lib()  # fails loudly if libnorm.so is missing
 
     w = inputs.LN_BF16_16384x4096
+    r = timed_workload(w, args.steps, args.warmup, torch, nl)
     copy_gbps, copy_us = copy_ceiling(torch)
-    r = timed_workload(w, args.steps, args.warmup, torch, nl, traffic)
     M, N = w.M, w.N
     fb = traffic.fwd_bytes(w.kind, w.dtype, M, N)
     bb = traffic.bwd_bytes(w.kind, w.dtype, M, N)
@@ -310,14 +317,16 @@ def main():
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_bytes,
                      "algorithmic_bytes": bfb, "avg_launch_us": round(bwd_us, 3)},
-        "fwd": {"us": round(r["fwd_us_mean"], 3), "GBps": round(fb / (r["fwd_us_mean"] * 1e-6) / 1e9, 1),
-                "frac_peak": round(fb / (r["fwd_us_mean"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+        "fwd": {"us": round(r["fwd_us"], 3), "GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1),
+                "frac_peak": round(fb / (r["fwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                 "bytes": fb},
+        "bwd": {"us": round(r["bwd_us"], 3), "GBps": round(bb / (r["bwd_us"] * 1e-6) / 1e9, 1),
+                "frac_peak": round(bb / (r["bwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                "bytes": bb},
         "fwd_bwd": {"GBps": round(value, 1), "frac_peak": round(value / PEAK_HBM_GBPS, 4),
-                    "frac_copy_ceiling": round(value / copy_gbps, 4),
                     "rows_per_s": round(M / (ms * 1e-3), 1)},
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "us_per_GiB_copy": round(copy_us, 2),
-                         "kernel": "torch copy_ of 1 GiB, read + write counted"},
+                         "kernel": "HIP runtime device copy of 1 GiB, read + write counted"},
     }
     if traffic_bytes is None:
         line["roofline"]["traffic_note"] = why

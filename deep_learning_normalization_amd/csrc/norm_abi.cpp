@@ -10,6 +10,13 @@
 
 namespace {
 
+thread_local dln::LaunchEvents tl_events{nullptr, nullptr};
+
+// Disarms the timing events when an entry point returns.
+struct EventsDisarm {
+  ~EventsDisarm() { tl_events = dln::LaunchEvents{nullptr, nullptr}; }
+};
+
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_cu_count[kMaxDevices];
 
@@ -120,12 +127,15 @@ norm_status_t zero_outputs(int64_t N, norm_dtype_t dtype, void *dW, void *dB, hi
 
 } // namespace
 
+dln::LaunchEvents &dln::launch_events() { return tl_events; }
+
 extern "C" {
 
 norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const void *W,
                        const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
                        void *Y, void *H, float *mean, float *rstd, void *workspace,
                        size_t workspace_bytes, norm_stream_t stream) {
+  const EventsDisarm disarm;
   dln::FwdCheck c{kind, dtype, X, R, W, B, eps, M, N, Y, H, mean, rstd, workspace,
                   workspace_bytes};
   norm_status_t st = dln::check_fwd(c);
@@ -168,6 +178,7 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
                        const void *W, const float *mean, const float *rstd, float eps,
                        int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR, void *dW,
                        void *dB, void *workspace, size_t workspace_bytes, norm_stream_t stream) {
+  const EventsDisarm disarm;
   dln::BwdCheck c{kind, dtype, X, dY, dH, W, mean, rstd, eps, M, N, dX, dR, dW, dB, workspace,
                   workspace_bytes, 1, 1};
   norm_status_t st = dln::check_bwd(c);
@@ -195,6 +206,7 @@ norm_status_t norm_bwd_fused(norm_kind_t kind, const void *X, const void *dY, co
                              const void *W, const float *mean, const float *rstd, float eps,
                              int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
                              void *workspace, size_t workspace_bytes, norm_stream_t stream) {
+  const EventsDisarm disarm;
   dln::BwdCheck c{kind, dtype, X, dY, dH, W, mean, rstd, eps, M, N, dX, dR, nullptr, nullptr,
                   workspace, workspace_bytes, 1, 0};
   norm_status_t st = dln::check_bwd(c);
@@ -210,6 +222,7 @@ norm_status_t norm_bwd_fused(norm_kind_t kind, const void *X, const void *dY, co
 norm_status_t norm_bwd_reduce(norm_kind_t kind, int64_t M, int64_t N, norm_dtype_t dtype,
                               void *dW, void *dB, void *workspace, size_t workspace_bytes,
                               norm_stream_t stream) {
+  const EventsDisarm disarm;
   dln::BwdCheck c{kind, dtype, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, M,
                   N, nullptr, nullptr, dW, dB, workspace, workspace_bytes, 0, 1};
   norm_status_t st = dln::check_bwd(c);
@@ -257,6 +270,16 @@ norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value) {
   return dln::set_tuning(key, value);
+}
+
+norm_status_t norm_set_launch_events(void *start_event, void *stop_event) {
+  if ((start_event == nullptr) != (stop_event == nullptr)) {
+    tl_events = dln::LaunchEvents{nullptr, nullptr};
+    return NORM_ERR_INVALID_ARG;
+  }
+  tl_events = dln::LaunchEvents{static_cast<hipEvent_t>(start_event),
+                                static_cast<hipEvent_t>(stop_event)};
+  return NORM_OK;
 }
 
 const char *norm_status_string(norm_status_t status) {

@@ -4,6 +4,10 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <tuple>
+#include <utility>
+
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 
 #include "norm.h"
@@ -82,6 +86,37 @@ norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs 
                                hipStream_t s);
 norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s);
 norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s);
+
+// Events armed by norm_set_launch_events for the calling thread's next entry point: start is
+// attached to the first kernel that call launches, stop to every kernel (the last one wins), so
+// the pair brackets exactly the GPU time of the call's kernels.
+struct LaunchEvents {
+  hipEvent_t start;
+  hipEvent_t stop;
+};
+LaunchEvents &launch_events();
+
+template <typename... P, typename Tup, size_t... I>
+hipError_t launch_tuple(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, Tup &t,
+                        std::index_sequence<I...>) {
+  void *argv[sizeof...(P) + 1] = {static_cast<void *>(&std::get<I>(t))..., nullptr};
+  LaunchEvents &ev = launch_events();
+  if (ev.stop) {
+    const hipError_t e = hipExtLaunchKernel(reinterpret_cast<const void *>(k), grid, block, argv,
+                                            0, s, ev.start, ev.stop, 0);
+    ev.start = nullptr;
+    return e;
+  }
+  return hipLaunchKernel(reinterpret_cast<const void *>(k), grid, block, argv, 0, s);
+}
+
+// Every kernel of the library is launched through here (no dynamic LDS).
+template <typename... P, typename... A>
+hipError_t launch(void (*k)(P...), dim3 grid, dim3 block, hipStream_t s, A... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "kernel argument count");
+  std::tuple<P...> t{static_cast<P>(a)...};
+  return launch_tuple(k, grid, block, s, t, std::index_sequence_for<P...>{});
+}
 
 // First thread of the fused backward pass records the partial count for the reduction.
 __device__ __forceinline__ void write_ws_header(int64_t *h, int64_t partials, int64_t N) {

@@ -508,41 +508,41 @@ template <typename T> norm_status_t split_fwd_typed(const Plan &p, const FwdArgs
   const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
   const bool resid = a.r != nullptr;
   bool found = false;
+  hipError_t e = hipSuccess;
+  auto keep = [&e](hipError_t r) { e = e == hipSuccess ? r : e; };
   if (p.vector) {
 #define X(V)                                                                                    \
   if (!found && p.vpt == V) {                                                                   \
     found = true;                                                                               \
-    if (resid)                                                                                  \
-      hipLaunchKernelGGL((split_stats_kernel<T, true, V, true>), grid, block, 0, s, a);        \
-    else                                                                                        \
-      hipLaunchKernelGGL((split_stats_kernel<T, true, V, false>), grid, block, 0, s, a);       \
-    hipLaunchKernelGGL((split_norm_kernel<T, true, V>), grid, block, 0, s, a);                  \
+    keep(resid ? launch(split_stats_kernel<T, true, V, true>, grid, block, s, a)                \
+               : launch(split_stats_kernel<T, true, V, false>, grid, block, s, a));             \
+    keep(launch(split_norm_kernel<T, true, V>, grid, block, s, a));                             \
   }
     DLN_SPLIT_FWD_MENU(X)
 #undef X
   } else if (p.vpt == DLN_SPLIT_SCALAR_VPT) {
     found = true;
     constexpr int V = DLN_SPLIT_SCALAR_VPT;
-    if (resid)
-      hipLaunchKernelGGL((split_stats_kernel<T, false, V, true>), grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL((split_stats_kernel<T, false, V, false>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((split_norm_kernel<T, false, V>), grid, block, 0, s, a);
+    keep(resid ? launch(split_stats_kernel<T, false, V, true>, grid, block, s, a)
+               : launch(split_stats_kernel<T, false, V, false>, grid, block, s, a));
+    keep(launch(split_norm_kernel<T, false, V>, grid, block, s, a));
   }
   if (!found) return NORM_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
 template <typename T, bool VEC, int V, int R>
-void split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
+hipError_t split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)p.grid), block(SPLIT_LB);
+  hipError_t e;
   if (a.layernorm) {
-    hipLaunchKernelGGL((split_bwd_partial_kernel<T, VEC, V, R, true>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((split_bwd_dx_kernel<T, VEC, V, R, true>), grid, block, 0, s, a);
+    e = launch(split_bwd_partial_kernel<T, VEC, V, R, true>, grid, block, s, a);
+    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, true>, grid, block, s, a);
   } else {
-    hipLaunchKernelGGL((split_bwd_partial_kernel<T, VEC, V, R, false>), grid, block, 0, s, a);
-    hipLaunchKernelGGL((split_bwd_dx_kernel<T, VEC, V, R, false>), grid, block, 0, s, a);
+    e = launch(split_bwd_partial_kernel<T, VEC, V, R, false>, grid, block, s, a);
+    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, false>, grid, block, s, a);
   }
+  return e;
 }
 
 template <typename T> norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
@@ -561,39 +561,40 @@ template <typename T> norm_status_t split_bwd_typed(const Plan &p, const BwdArgs
     f.inv_n = a.inv_n;
     const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
     bool found = false;
+    hipError_t e = hipSuccess;
     if (p.vector) {
 #define X(V)                                                                                    \
   if (!found && p.vpt == V) {                                                                   \
     found = true;                                                                               \
-    hipLaunchKernelGGL((split_stats_kernel<T, true, V, false>), grid, block, 0, s, f);         \
+    e = launch(split_stats_kernel<T, true, V, false>, grid, block, s, f);                      \
   }
       DLN_SPLIT_FWD_MENU(X)
 #undef X
     } else if (p.vpt == DLN_SPLIT_SCALAR_VPT) {
       found = true;
-      hipLaunchKernelGGL((split_stats_kernel<T, false, DLN_SPLIT_SCALAR_VPT, false>), grid, block,
-                         0, s, f);
+      e = launch(split_stats_kernel<T, false, DLN_SPLIT_SCALAR_VPT, false>, grid, block, s, f);
     }
     if (!found) return NORM_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(split_finalize_stats_kernel, dim3((unsigned)a.M), block, 0, s, a,
-                       p.epv);
-    if (hipGetLastError() != hipSuccess) return NORM_ERR_HIP;
+    if (e == hipSuccess)
+      e = launch(split_finalize_stats_kernel, dim3((unsigned)a.M), block, s, a, p.epv);
+    if (e != hipSuccess) return NORM_ERR_HIP;
   }
   bool found = false;
+  hipError_t e = hipSuccess;
   if (p.vector) {
 #define X(V, R)                                                                                 \
   if (!found && p.vpt == V && p.rows == R) {                                                    \
     found = true;                                                                               \
-    split_bwd_pair<T, true, V, R>(p, a, s);                                                     \
+    e = split_bwd_pair<T, true, V, R>(p, a, s);                                                 \
   }
     DLN_SPLIT_BWD_MENU(X)
 #undef X
   } else if (p.vpt == DLN_SPLIT_SCALAR_VPT && p.rows == 1) {
     found = true;
-    split_bwd_pair<T, false, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
+    e = split_bwd_pair<T, false, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
   }
   if (!found) return NORM_ERR_UNSUPPORTED;
-  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
 } // namespace

@@ -625,24 +625,20 @@ template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
 hipError_t fwd_launch(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s) {
   dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
   if (resid)
-    hipLaunchKernelGGL((team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>), grid, block, 0, s,
-                       a, p.team_threads);
-  else
-    hipLaunchKernelGGL((team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>), grid, block, 0, s,
-                       a, p.team_threads);
-  return hipGetLastError();
+    return launch(team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
+                  p.team_threads);
+  return launch(team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
+                p.team_threads);
 }
 
 template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
 hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
   if (a.layernorm)
-    hipLaunchKernelGGL((team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>), grid, block, 0, s,
-                       a, p.team_threads);
-  else
-    hipLaunchKernelGGL((team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>), grid, block, 0, s,
-                       a, p.team_threads);
-  return hipGetLastError();
+    return launch(team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
+                  p.team_threads);
+  return launch(team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
+                p.team_threads);
 }
 
 // The menu of compiled shapes. Wave scheme: workgroups of 256 threads (4 one-wave teams).
@@ -764,27 +760,24 @@ norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s) {
   if (!bytes) return NORM_OK;
   size_t blocks = (bytes + 255) / 256;
   if (blocks > 1024) blocks = 1024;
-  hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                     static_cast<unsigned char *>(p), bytes);
-  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+  const hipError_t e = launch(zero_kernel, dim3((unsigned)blocks), dim3(256), s,
+                              static_cast<unsigned char *>(p), bytes);
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
 norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s) {
   const unsigned q = a.db ? 2u : 1u;
+  hipError_t e;
   if (a.N % 4 == 0) {
-    dim3 grid((unsigned)((a.N + 31) / 32), q), block(256);
-    if (dtype == NORM_F32)
-      hipLaunchKernelGGL(colsum4_kernel<float>, grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL(colsum4_kernel<bf16_bits>, grid, block, 0, s, a);
+    const dim3 grid((unsigned)((a.N + 31) / 32), q), block(256);
+    e = dtype == NORM_F32 ? launch(colsum4_kernel<float>, grid, block, s, a)
+                          : launch(colsum4_kernel<bf16_bits>, grid, block, s, a);
   } else {
-    dim3 grid((unsigned)((a.N + 63) / 64), q), block(256);
-    if (dtype == NORM_F32)
-      hipLaunchKernelGGL(colsum_kernel<float>, grid, block, 0, s, a);
-    else
-      hipLaunchKernelGGL(colsum_kernel<bf16_bits>, grid, block, 0, s, a);
+    const dim3 grid((unsigned)((a.N + 63) / 64), q), block(256);
+    e = dtype == NORM_F32 ? launch(colsum_kernel<float>, grid, block, s, a)
+                          : launch(colsum_kernel<bf16_bits>, grid, block, s, a);
   }
-  return hipGetLastError() == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
 } // namespace dln

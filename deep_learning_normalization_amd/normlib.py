@@ -26,7 +26,8 @@ KINDS = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM}
 DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
 
 SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_workspace_size",
-           "norm_plan", "norm_set_tuning", "norm_status_string", "norm_version")
+           "norm_plan", "norm_set_tuning", "norm_set_launch_events", "norm_status_string",
+           "norm_version")
 
 
 class NormError(RuntimeError):
@@ -69,11 +70,13 @@ def lib():
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.norm_plan.argtypes = [i32, i32, i32, i64, i64, i32, i32, i32, ctypes.POINTER(_Plan)]
         L.norm_set_tuning.argtypes = [i32, i64]
+        L.norm_set_launch_events.argtypes = [vp, vp]
         L.norm_status_string.argtypes = [i32]
         L.norm_status_string.restype = ctypes.c_char_p
         L.norm_version.argtypes = []
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
-                     "norm_workspace_size", "norm_plan", "norm_set_tuning"):
+                     "norm_workspace_size", "norm_plan", "norm_set_tuning",
+                     "norm_set_launch_events"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
         _lib = L
@@ -216,8 +219,58 @@ def norm_set_tuning(key, value):
     _raise(lib().norm_set_tuning(int(key), int(value)), "norm_set_tuning")
 
 
+def norm_set_launch_events(start, stop):
+    """Arm two raw hipEvent_t handles (ints) for this thread's next entry-point call."""
+    _raise(lib().norm_set_launch_events(start or None, stop or None), "norm_set_launch_events")
+
+
 def norm_version():
     return lib().norm_version()
+
+
+class KernelTimer:
+    """HIP events that take the kernels' own start and end timestamps (see
+    norm_set_launch_events): `arm()` before an entry-point call, `elapsed_ms()` after the
+    stream has passed it. Events come from the HIP runtime the library is linked against."""
+
+    _hip = None
+
+    @classmethod
+    def _rt(cls):
+        if cls._hip is None:
+            lib()  # the runtime libnorm.so loaded
+            h = ctypes.CDLL("libamdhip64.so.7")
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                              ctypes.c_void_p]
+            for f in ("hipEventCreateWithFlags", "hipEventDestroy", "hipEventElapsedTime"):
+                getattr(h, f).restype = ctypes.c_int
+            cls._hip = h
+        return cls._hip
+
+    def __init__(self):
+        h = self._rt()
+        self.start, self.stop = ctypes.c_void_p(), ctypes.c_void_p()
+        for e in (self.start, self.stop):
+            if h.hipEventCreateWithFlags(ctypes.byref(e), 0) != 0:
+                raise RuntimeError("hipEventCreateWithFlags failed")
+
+    def arm(self):
+        norm_set_launch_events(self.start.value, self.stop.value)
+
+    def elapsed_ms(self):
+        ms = ctypes.c_float()
+        if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.start, self.stop) != 0:
+            raise RuntimeError("hipEventElapsedTime failed (events not recorded?)")
+        return ms.value
+
+    def __del__(self):
+        h = self._hip
+        if h is not None:
+            for e in (self.start, self.stop):
+                if e.value:
+                    h.hipEventDestroy(e)
 
 
 # ---- allocating conveniences (torch allocates; the kernels compute) ------------------------

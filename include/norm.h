@@ -190,6 +190,19 @@ typedef enum {
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);
 
+/*
+ * Kernel timing for profilers and benchmarks. Arms two HIP events (hipEvent_t, created by the
+ * caller on the device of the stream that will be used) for the calling thread's next call of
+ * norm_fwd, norm_bwd, norm_bwd_fused or norm_bwd_reduce: `start_event` takes the start
+ * timestamp of the first kernel that call launches and `stop_event` the end timestamp of its
+ * last one (hipExtLaunchKernel; no extra packets are queued, so the stream runs as it would
+ * without timing). hipEventElapsedTime of the pair is then the GPU time of that call's kernels.
+ * The events are disarmed when that call returns, whatever its status; a call that launches no
+ * kernel leaves them unrecorded. Both NULL disarms; exactly one NULL is NORM_ERR_INVALID_ARG
+ * (and disarms). The library does not own the events.
+ */
+norm_status_t norm_set_launch_events(void *start_event, void *stop_event);
+
 /* Static text for a status code. */
 const char *norm_status_string(norm_status_t status);
 

@@ -208,3 +208,14 @@ def test_workspace_needs_a_device_here():
     with pytest.raises(nl.NormError) as e:
         nl.norm_workspace_size(0, BF, 1, 16, 4096)
     assert e.value.status == nl.ERR_HIP
+
+
+def test_launch_events_arm_and_disarm():
+    lib = nl.lib()
+    assert lib.norm_set_launch_events(None, None) == nl.OK
+    assert lib.norm_set_launch_events(FAKE, None) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_launch_events(None, FAKE) == nl.ERR_INVALID_ARG
+    # armed with handles that are never used: the call fails its checks and disarms them
+    assert lib.norm_set_launch_events(FAKE, FAKE * 2) == nl.OK
+    assert _fwd(kind=9) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_launch_events(None, None) == nl.OK
