@@ -89,6 +89,7 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   b.rows_per_group = plan->rows_per_group;
   b.layernorm = kind == NORM_LAYERNORM ? 1 : 0;
   b.want_db = 1;
+  b.blocked = plan->row_order;
   b.eps = eps;
   b.inv_n = 1.0f / (float)N;
   *a = b;
@@ -167,6 +168,7 @@ norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const voi
   a.chunks = p.chunks;
   a.chunk_acc = (int32_t)(p.chunk_elems / p.epv);
   a.layernorm = kind == NORM_LAYERNORM ? 1 : 0;
+  a.blocked = p.row_order;
   a.eps = eps;
   a.inv_n = 1.0f / (float)N;
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -258,6 +260,7 @@ norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
   o.team_threads = p.team_threads;
   o.accesses_per_thread = p.vpt;
   o.rows_per_iter = p.rows;
+  o.row_order = p.row_order;
   o.grid = p.grid;
   o.chunks = p.chunks;
   o.chunk_elems = p.chunk_elems;

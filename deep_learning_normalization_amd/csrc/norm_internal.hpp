@@ -32,6 +32,7 @@ struct FwdArgs {
   int64_t chunks;     // split
   int32_t chunk_acc;  // split: accesses per chunk
   int32_t layernorm;  // 1 LayerNorm, 0 RMSNorm
+  int32_t blocked;    // wave/block: contiguous row blocks per workgroup (else interleaved)
   float eps;
   float inv_n;        // 1 / N
 };
@@ -61,6 +62,7 @@ struct BwdArgs {
   int64_t rows_per_group;
   int32_t layernorm;
   int32_t want_db;
+  int32_t blocked;    // wave/block: contiguous row blocks per workgroup (else interleaved)
   float eps;
   float inv_n;
 };

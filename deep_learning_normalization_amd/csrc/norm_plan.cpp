@@ -124,6 +124,10 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
     if (v != -1 && (v < 1 || v > 16)) return NORM_ERR_INVALID_ARG;
     g_tuning.teams = (int)v;
     return NORM_OK;
+  case NORM_TUNE_ROW_ORDER:
+    if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
+    g_tuning.row_order = (int)v;
+    return NORM_OK;
   default: return NORM_ERR_INVALID_ARG;
   }
 }
@@ -175,12 +179,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     const int64_t groups = cdiv(Mm, (int64_t)(kWaveThreads / 64) * rows);
     const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (bwd ? 2 : 8);
     p.grid = groups < cu * gpc ? groups : cu * gpc;
+    p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_BLOCK) {
     static const int vmenu[] = {1, 2, 4, 8};
     static const int smenu[] = {4, 8};
     const int *menu = vec ? vmenu : smenu;
     const int nmenu = vec ? 4 : 2;
-    const int want_rows = t.rows > 0 ? t.rows : 1;
     int vpt = 0, tt = 0, rows = 1, lb_pick = 1024;
     // pass 0: the team size override if one is set, else the preferred team size;
     // pass 1: any team size up to 1024 (an override that cannot hold the row is ignored)
@@ -198,7 +202,10 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
                               : 1024;
         if (cand > limit) continue;
         const int lb = vec ? lb_of(cand) : 1024;
-        int r = want_rows;
+        // Backward teams of up to 512 threads with one access per thread hold two rows at
+        // once by default (measured on MI355X, with the saved statistics prefetched as well:
+        // fewer, fuller workgroups; wider teams or more accesses per thread do better with one)
+        int r = t.rows > 0 ? t.rows : ((bwd && v == 1 && cand <= 512) ? 2 : 1);
         if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, bwd, v, r, lb)) r = 1;
         if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, bwd, v, r, lb)) continue;
         vpt = v;
@@ -233,6 +240,7 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     const int64_t gpc_default = per_cu / load > 0 ? per_cu / load : 1;
     const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : gpc_default;
     p.grid = groups < cu * gpc ? groups : cu * gpc;
+    p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_SPLIT) {
     int vpt = vec ? 4 : 8;
     if (t.split_chunk > 0 && vec) { // the element-wise path has one chunk size

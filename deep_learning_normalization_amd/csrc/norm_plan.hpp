@@ -21,6 +21,7 @@ struct Plan {
   int team_threads = 256;  // threads sharing a row (64 for the wave scheme)
   int vpt = 1;             // accesses per thread per row (per chunk for split)
   int rows = 1;            // rows a team holds at once
+  int row_order = 0;       // wave/block: 0 interleaved row groups, 1 contiguous blocks
   int64_t grid = 1;        // workgroups of the main (persistent) kernel
   int64_t chunks = 1;      // split: chunks per row
   int64_t chunk_elems = 0; // split: elements per chunk
@@ -48,6 +49,7 @@ struct Tuning {
   int64_t split_chunk = -1;
   int64_t row_groups = -1;
   int teams = -1;
+  int row_order = -1;
 };
 
 const Tuning &tuning();

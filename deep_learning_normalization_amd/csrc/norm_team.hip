@@ -54,6 +54,21 @@ template <bool WAVE> __device__ __forceinline__ TeamGeom team_geom(int team_thre
   return g;
 }
 
+// Row groups of this workgroup: first, first + step, ... below end. Interleaved: group g goes
+// to workgroup g mod grid. Blocked: workgroup b takes the contiguous groups
+// [b * per, (b + 1) * per), per = ceil(groups / grid), so its rows stream from one region.
+struct GroupRange {
+  int64_t first, step, end;
+};
+__device__ __forceinline__ GroupRange group_range(int64_t M, int64_t rows_per_group,
+                                                  int blocked) {
+  const int64_t groups = (M + rows_per_group - 1) / rows_per_group;
+  if (!blocked) return GroupRange{(int64_t)blockIdx.x, (int64_t)gridDim.x, groups};
+  const int64_t per = (groups + gridDim.x - 1) / gridDim.x;
+  const int64_t first = (int64_t)blockIdx.x * per;
+  return GroupRange{first, 1, first + per < groups ? first + per : groups};
+}
+
 // ---- forward ------------------------------------------------------------------------------
 
 template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool RESID>
@@ -90,11 +105,11 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   // Software pipeline: the next row group's loads are issued before the current group is
   // reduced and written, so every wavefront keeps requests in flight across its barriers.
   raw px[ROWS][VPT], pr[ROWS][RESID ? VPT : 1];
-  auto issue = [&](int64_t g) {
+  auto issue = [&](int64_t g, bool live) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      const bool rv = row0 + r < M;
+      const bool rv = live && row0 + r < M;
       const int64_t base = (row0 + r) * N;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
@@ -109,9 +124,10 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
     }
   };
   int slot = 0;
-  int64_t g = blockIdx.x;
-  issue(g);
-  for (; g * rows_per_group < M; g += gridDim.x) {
+  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
+  int64_t g = gr.first;
+  issue(g, g < gr.end);
+  for (; g < gr.end; g += gr.step) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
     float x[ROWS][VPT][E];
     {
@@ -124,7 +140,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
           rx[r][k] = px[r][k];
           if (RESID) rr[r][k] = pr[r][k];
         }
-      issue(g + gridDim.x);
+      issue(g + gr.step, g + gr.step < gr.end);
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         const bool rv = row0 + r < M;
@@ -275,15 +291,23 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   }
 
   const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
-  // Software pipeline: X and dY of the next row group are requested before this group's
-  // reductions and stores.
+  // Software pipeline: X, dY and the saved statistics of the next row group are requested
+  // before this group's reductions and stores.
   raw px[ROWS][VPT], pdy[ROWS][VPT];
-  auto issue = [&](int64_t g) {
+  float pm[ROWS], pr[ROWS];
+  auto issue = [&](int64_t g, bool live) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      const bool rv = row0 + r < M;
+      const bool rv = live && row0 + r < M;
       const int64_t base = (row0 + r) * N;
+      pm[r] = 0.0f;
+      pr[r] = 0.0f;
+      if (have_stats) {
+        const int64_t row = rv ? row0 + r : M - 1;
+        if constexpr (LN) pm[r] = a.mean[row];
+        pr[r] = a.rstd[row];
+      }
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
@@ -297,30 +321,27 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
     }
   };
   int slot = 0;
-  int64_t g = blockIdx.x;
-  issue(g);
-  for (; g * rows_per_group < M; g += gridDim.x) {
+  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
+  int64_t g = gr.first;
+  issue(g, g < gr.end);
+  for (; g < gr.end; g += gr.step) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
     raw rx[ROWS][VPT], rdy[ROWS][VPT];
+    // m: the row mean the forward saved (LayerNorm), or a first-pass mean when recomputing.
+    // The reduction below also sums x - m, so the exact mean m + delta is used for xhat.
+    float m[ROWS], rstd[ROWS];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r)
+    for (int r = 0; r < ROWS; ++r) {
+      m[r] = pm[r];
+      rstd[r] = pr[r];
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         rx[r][k] = px[r][k];
         rdy[r][k] = pdy[r][k];
       }
-    issue(g + gridDim.x);
-    // m: the row mean the forward saved (LayerNorm), or a first-pass mean when recomputing.
-    // The reduction below also sums x - m, so the exact mean m + delta is used for xhat.
-    float m[ROWS], rstd[ROWS];
-    if (have_stats) {
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        const int64_t row = row0 + r < M ? row0 + r : M - 1;
-        m[r] = LN ? a.mean[row] : 0.0f;
-        rstd[r] = a.rstd[row];
-      }
-    } else {
+    }
+    issue(g + gr.step, g + gr.step < gr.end);
+    if (!have_stats) {
       // recompute the forward statistics from the register-resident rows
       if constexpr (LN) {
         float s[ROWS];
@@ -513,101 +534,140 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 
 // ---- column reduction ------------------------------------------------------------------------
 
-// dW[j] (and dB[j]) = sum over p of colpart[q][p][j], in a fixed order: four slices of the
-// partial rows, each summed in ascending p, then the slices in order. One workgroup covers 64
-// columns of one quantity (blockIdx.y: 0 = dW, 1 = dB). The partial count comes from the
-// header the fused pass wrote; a header that does not describe this workspace gives NaN
-// outputs instead of reading past the partials.
+// dW[j] (and dB[j]) = sum over p of colpart[q][p][j] (blockIdx.y: 0 = dW, 1 = dB) in a fixed
+// order for a given partial count P, which comes from the header the fused pass wrote (a
+// header that does not describe this workspace gives NaN outputs instead of reading past the
+// partials). Few partial rows (P <= kNarrowP): every thread owns its columns and adds the P
+// rows in ascending order. Otherwise a tile of columns is shared by slices of the partial
+// rows: slice s adds rows s, s + S, ... in ascending order, then the S slice sums of a column
+// are added in slice order. Workgroups stride over the column tiles, so the grid stays small
+// for very long rows.
+constexpr int64_t kNarrowP = 32;
+
+template <typename T> __device__ __forceinline__ void store_col(void *dst, int64_t col, float t) {
+  T *d = static_cast<T *>(dst);
+  if constexpr (sizeof(T) == 4)
+    d[col] = t;
+  else
+    d[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
+}
+
+struct ColsumSrc {
+  const float *src;
+  int64_t P;
+  bool valid;
+};
+__device__ __forceinline__ ColsumSrc colsum_src(const ReduceArgs &a) {
+  const int64_t P = a.header[1];
+  const bool valid =
+      a.header[0] == kWsMagic && a.header[2] == a.N && P >= 1 && P <= a.max_partials;
+  return ColsumSrc{a.colpart + (int64_t)blockIdx.y * (valid ? P : 0) * a.N, P, valid};
+}
+
+// Element-wise version (any N): wide tiles are 64 columns x 4 slices.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum_kernel(ReduceArgs a) {
   __shared__ float part[4][64];
+  const int64_t N = a.N;
+  const ColsumSrc c = colsum_src(a);
+  void *dst = blockIdx.y == 0 ? a.dw : a.db;
+  if (!c.valid || c.P <= kNarrowP) {
+    for (int64_t col = (int64_t)blockIdx.x * 256 + threadIdx.x; col < N;
+         col += (int64_t)gridDim.x * 256) {
+      float s = 0.0f;
+      for (int64_t p = 0; c.valid && p < c.P; ++p) s += c.src[p * N + col];
+      store_col<T>(dst, col, c.valid ? s : __builtin_nanf(""));
+    }
+    return;
+  }
   const int lane = threadIdx.x & 63;
   const int slice = threadIdx.x >> 6;
-  const int64_t col = (int64_t)blockIdx.x * 64 + lane;
-  const int64_t N = a.N;
-  const int64_t P = a.header[1];
-  const bool valid = a.header[0] == kWsMagic && a.header[2] == N && P >= 1 && P <= a.max_partials;
-  const float *src = a.colpart + (int64_t)blockIdx.y * (valid ? P : 0) * N;
-  float s = 0.0f;
-  if (valid && col < N) {
-    int64_t p = slice;
-    for (; p + 12 < P; p += 16) {
-      const float v0 = src[p * N + col];
-      const float v1 = src[(p + 4) * N + col];
-      const float v2 = src[(p + 8) * N + col];
-      const float v3 = src[(p + 12) * N + col];
-      s += v0;
-      s += v1;
-      s += v2;
-      s += v3;
+  for (int64_t tile = blockIdx.x; tile * 64 < N; tile += gridDim.x) {
+    const int64_t col = tile * 64 + lane;
+    float s = 0.0f;
+    if (col < N) {
+      int64_t p = slice;
+      for (; p + 12 < c.P; p += 16) {
+        const float v0 = c.src[p * N + col];
+        const float v1 = c.src[(p + 4) * N + col];
+        const float v2 = c.src[(p + 8) * N + col];
+        const float v3 = c.src[(p + 12) * N + col];
+        s += v0;
+        s += v1;
+        s += v2;
+        s += v3;
+      }
+      for (; p < c.P; p += 4) s += c.src[p * N + col];
     }
-    for (; p < P; p += 4) s += src[p * N + col];
-  }
-  part[slice][lane] = s;
-  __syncthreads();
-  if (slice == 0 && col < N) {
-    float t = (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]);
-    if (!valid) t = __builtin_nanf("");
-    T *dst = static_cast<T *>(blockIdx.y == 0 ? a.dw : a.db);
-    if constexpr (sizeof(T) == 4) {
-      dst[col] = t;
-    } else {
-      dst[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
-    }
+    part[slice][lane] = s;
+    __syncthreads();
+    if (slice == 0 && col < N)
+      store_col<T>(dst, col, (part[0][lane] + part[1][lane]) + (part[2][lane] + part[3][lane]));
+    __syncthreads();
   }
 }
 
-// The same sum with 16-byte loads, for N % 4 == 0 (every partial row is then 16-byte
-// aligned): a workgroup covers 32 columns of one quantity; its 256 threads are 8 column
-// quads x 32 slices of the partial rows; slice s sums rows s, s + 32, ... in ascending order,
-// then the 32 slice sums of a column are added in slice order.
+// 16-byte version for N % 4 == 0 (every partial row is then 16-byte aligned): wide tiles are
+// 32 columns (8 quads) x 32 slices.
 template <typename T>
 __global__ __launch_bounds__(256) void colsum4_kernel(ReduceArgs a) {
   __shared__ float part[32][33];
+  const int64_t N = a.N;
+  const ColsumSrc c = colsum_src(a);
+  void *dst = blockIdx.y == 0 ? a.dw : a.db;
+  if (!c.valid || c.P <= kNarrowP) {
+    for (int64_t col0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4; col0 < N;
+         col0 += (int64_t)gridDim.x * 1024) {
+      float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+      for (int64_t p = 0; c.valid && p < c.P; ++p) {
+        const float4 v = *reinterpret_cast<const float4 *>(c.src + p * N + col0);
+        s0 += v.x;
+        s1 += v.y;
+        s2 += v.z;
+        s3 += v.w;
+      }
+      if (!c.valid) s0 = s1 = s2 = s3 = __builtin_nanf("");
+      store_col<T>(dst, col0, s0);
+      store_col<T>(dst, col0 + 1, s1);
+      store_col<T>(dst, col0 + 2, s2);
+      store_col<T>(dst, col0 + 3, s3);
+    }
+    return;
+  }
   const int q = threadIdx.x & 7;
   const int slice = threadIdx.x >> 3;
-  const int64_t N = a.N;
-  const int64_t col0 = (int64_t)blockIdx.x * 32 + q * 4;
-  const int64_t P = a.header[1];
-  const bool valid = a.header[0] == kWsMagic && a.header[2] == N && P >= 1 && P <= a.max_partials;
-  const float *src = a.colpart + (int64_t)blockIdx.y * (valid ? P : 0) * N;
-  float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
-  if (valid && col0 < N) {
-    int64_t p = slice;
-    for (; p + 96 < P; p += 128) {
-      const float4 v0 = *reinterpret_cast<const float4 *>(src + p * N + col0);
-      const float4 v1 = *reinterpret_cast<const float4 *>(src + (p + 32) * N + col0);
-      const float4 v2 = *reinterpret_cast<const float4 *>(src + (p + 64) * N + col0);
-      const float4 v3 = *reinterpret_cast<const float4 *>(src + (p + 96) * N + col0);
-      s0 += v0.x; s1 += v0.y; s2 += v0.z; s3 += v0.w;
-      s0 += v1.x; s1 += v1.y; s2 += v1.z; s3 += v1.w;
-      s0 += v2.x; s1 += v2.y; s2 += v2.z; s3 += v2.w;
-      s0 += v3.x; s1 += v3.y; s2 += v3.z; s3 += v3.w;
-    }
-    for (; p < P; p += 32) {
-      const float4 v = *reinterpret_cast<const float4 *>(src + p * N + col0);
-      s0 += v.x; s1 += v.y; s2 += v.z; s3 += v.w;
-    }
-  }
-  part[slice][q * 4 + 0] = s0;
-  part[slice][q * 4 + 1] = s1;
-  part[slice][q * 4 + 2] = s2;
-  part[slice][q * 4 + 3] = s3;
-  __syncthreads();
-  if (threadIdx.x < 32) {
-    const int c = threadIdx.x;
-    const int64_t col = (int64_t)blockIdx.x * 32 + c;
-    float t = 0.0f;
-    for (int sl = 0; sl < 32; ++sl) t += part[sl][c];
-    if (!valid) t = __builtin_nanf("");
-    if (col < N) {
-      T *dst = static_cast<T *>(blockIdx.y == 0 ? a.dw : a.db);
-      if constexpr (sizeof(T) == 4) {
-        dst[col] = t;
-      } else {
-        dst[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
+  for (int64_t tile = blockIdx.x; tile * 32 < N; tile += gridDim.x) {
+    const int64_t col0 = tile * 32 + q * 4;
+    float s0 = 0.0f, s1 = 0.0f, s2 = 0.0f, s3 = 0.0f;
+    if (col0 < N) {
+      int64_t p = slice;
+      for (; p + 96 < c.P; p += 128) {
+        const float4 v0 = *reinterpret_cast<const float4 *>(c.src + p * N + col0);
+        const float4 v1 = *reinterpret_cast<const float4 *>(c.src + (p + 32) * N + col0);
+        const float4 v2 = *reinterpret_cast<const float4 *>(c.src + (p + 64) * N + col0);
+        const float4 v3 = *reinterpret_cast<const float4 *>(c.src + (p + 96) * N + col0);
+        s0 += v0.x; s1 += v0.y; s2 += v0.z; s3 += v0.w;
+        s0 += v1.x; s1 += v1.y; s2 += v1.z; s3 += v1.w;
+        s0 += v2.x; s1 += v2.y; s2 += v2.z; s3 += v2.w;
+        s0 += v3.x; s1 += v3.y; s2 += v3.z; s3 += v3.w;
+      }
+      for (; p < c.P; p += 32) {
+        const float4 v = *reinterpret_cast<const float4 *>(c.src + p * N + col0);
+        s0 += v.x; s1 += v.y; s2 += v.z; s3 += v.w;
       }
     }
+    part[slice][q * 4 + 0] = s0;
+    part[slice][q * 4 + 1] = s1;
+    part[slice][q * 4 + 2] = s2;
+    part[slice][q * 4 + 3] = s3;
+    __syncthreads();
+    if (threadIdx.x < 32) {
+      const int64_t col = tile * 32 + threadIdx.x;
+      float t = 0.0f;
+      for (int sl = 0; sl < 32; ++sl) t += part[sl][threadIdx.x];
+      if (col < N) store_col<T>(dst, col, t);
+    }
+    __syncthreads();
   }
 }
 
@@ -766,14 +826,18 @@ norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s) {
 }
 
 norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s) {
+  // one workgroup per wide tile up to kReduceGrid workgroups per quantity; they stride beyond
+  constexpr int64_t kReduceGrid = 2048;
   const unsigned q = a.db ? 2u : 1u;
   hipError_t e;
   if (a.N % 4 == 0) {
-    const dim3 grid((unsigned)((a.N + 31) / 32), q), block(256);
+    const int64_t tiles = (a.N + 31) / 32;
+    const dim3 grid((unsigned)(tiles < kReduceGrid ? tiles : kReduceGrid), q), block(256);
     e = dtype == NORM_F32 ? launch(colsum4_kernel<float>, grid, block, s, a)
                           : launch(colsum4_kernel<bf16_bits>, grid, block, s, a);
   } else {
-    const dim3 grid((unsigned)((a.N + 63) / 64), q), block(256);
+    const int64_t tiles = (a.N + 63) / 64;
+    const dim3 grid((unsigned)(tiles < kReduceGrid ? tiles : kReduceGrid), q), block(256);
     e = dtype == NORM_F32 ? launch(colsum_kernel<float>, grid, block, s, a)
                           : launch(colsum_kernel<bf16_bits>, grid, block, s, a);
   }

@@ -18,7 +18,8 @@ F32, BF16 = 0, 1
 PASS_FWD, PASS_BWD = 0, 1
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT = -1, 0, 1, 2
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
-TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG = 4, 5, 6
+TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
+N_TUNE_KEYS = 8
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
@@ -40,7 +41,7 @@ class _Plan(ctypes.Structure):
     _fields_ = [("scheme", ctypes.c_int32), ("vector", ctypes.c_int32),
                 ("elems_per_access", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("team_threads", ctypes.c_int32), ("accesses_per_thread", ctypes.c_int32),
-                ("rows_per_iter", ctypes.c_int32), ("reserved", ctypes.c_int32),
+                ("rows_per_iter", ctypes.c_int32), ("row_order", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("chunks", ctypes.c_int64),
                 ("chunk_elems", ctypes.c_int64), ("row_groups", ctypes.c_int64),
                 ("partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
@@ -212,7 +213,7 @@ def norm_plan(kind, dtype, pass_, M, N, residual=False, aligned=True, cu_count=2
     st = lib().norm_plan(_kind(kind), dt, int(pass_), M, N, int(bool(residual)),
                          int(bool(aligned)), int(cu_count), ctypes.byref(p))
     _raise(st, "norm_plan")
-    return {name: getattr(p, name) for name, _ in _Plan._fields_ if name != "reserved"}
+    return {name: getattr(p, name) for name, _ in _Plan._fields_}
 
 
 def norm_set_tuning(key, value):

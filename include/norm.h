@@ -158,7 +158,7 @@ typedef struct {
   int32_t team_threads;   /* threads that share one row (64 for the wave scheme) */
   int32_t accesses_per_thread; /* per row (wave/block) or per chunk (split) */
   int32_t rows_per_iter;  /* rows a team holds at once */
-  int32_t reserved;
+  int32_t row_order;      /* wave/block: 0 interleaved row groups, 1 contiguous blocks */
   int64_t grid;           /* workgroups of the main kernel */
   int64_t chunks;         /* split scheme: chunks per row (1 otherwise) */
   int64_t chunk_elems;    /* split scheme: elements per chunk (N otherwise) */
@@ -184,8 +184,10 @@ typedef enum {
                                    of that size cannot hold the row */
   NORM_TUNE_SPLIT_CHUNK = 4,    /* split scheme: elements per chunk */
   NORM_TUNE_ROW_GROUPS = 5,     /* split backward: number of row groups */
-  NORM_TUNE_TEAMS_PER_WG = 6    /* block scheme: row teams per workgroup (their dW/dB partials
+  NORM_TUNE_TEAMS_PER_WG = 6,   /* block scheme: row teams per workgroup (their dW/dB partials
                                    are merged in LDS, so fewer partial rows are written) */
+  NORM_TUNE_ROW_ORDER = 7       /* wave/block schemes: 0 = row groups interleaved across the
+                                   workgroups, 1 = each workgroup takes a contiguous block */
 } norm_tune_t;
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);

@@ -236,7 +236,7 @@ class tuned:
         keys = {"scheme": nl.TUNE_SCHEME, "grid_per_cu": nl.TUNE_GRID_PER_CU,
                 "rows": nl.TUNE_ROWS_PER_ITER, "team_threads": nl.TUNE_TEAM_THREADS,
                 "split_chunk": nl.TUNE_SPLIT_CHUNK, "row_groups": nl.TUNE_ROW_GROUPS,
-                "teams": nl.TUNE_TEAMS_PER_WG}
+                "teams": nl.TUNE_TEAMS_PER_WG, "row_order": nl.TUNE_ROW_ORDER}
         self.items = [(keys[k], v) for k, v in kv.items()]
 
     def __enter__(self):
@@ -245,6 +245,6 @@ class tuned:
         return self
 
     def __exit__(self, *exc):
-        for k in range(7):
+        for k in range(nl.N_TUNE_KEYS):
             nl.norm_set_tuning(k, -1)
         return False

@@ -126,6 +126,7 @@ def test_tuning_rejects_bad_values():
     assert lib.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, 3) == nl.ERR_INVALID_ARG
     assert lib.norm_set_tuning(nl.TUNE_TEAM_THREADS, 100) == nl.ERR_INVALID_ARG
     assert lib.norm_set_tuning(99, 1) == nl.ERR_INVALID_ARG
+    assert lib.norm_set_tuning(nl.TUNE_ROW_ORDER, 2) == nl.ERR_INVALID_ARG
     assert lib.norm_set_tuning(nl.TUNE_SCHEME, -1) == nl.OK
 
 
@@ -199,8 +200,12 @@ def test_plan_tuning_overrides():
         assert nl.norm_plan(0, BF, 1, 65536, 4096, cu_count=256)["partials"] == 256
         nl.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, 2)
         assert nl.norm_plan(0, BF, 0, 65536, 512)["rows_per_iter"] == 2
+        assert nl.norm_plan(0, BF, 0, 65536, 4096)["row_order"] == 0
+        nl.norm_set_tuning(nl.TUNE_ROW_ORDER, 1)
+        assert nl.norm_plan(0, BF, 0, 65536, 4096)["row_order"] == 1
+        assert nl.norm_plan(0, BF, 1, 65536, 512)["row_order"] == 1
     finally:
-        for k in range(7):
+        for k in range(nl.N_TUNE_KEYS):
             nl.norm_set_tuning(k, -1)
 
 

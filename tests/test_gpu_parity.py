@@ -104,6 +104,9 @@ KNOBS = [
     dict(scheme=nl.SCHEME_SPLIT, row_groups=1), dict(scheme=nl.SCHEME_SPLIT, row_groups=7),
     dict(scheme=nl.SCHEME_SPLIT, rows=1), dict(scheme=nl.SCHEME_SPLIT, rows=4),
     dict(teams=2), dict(team_threads=256, teams=4), dict(team_threads=512, teams=2, rows=2),
+    dict(rows=1), dict(row_order=1), dict(row_order=1, rows=1),
+    dict(row_order=1, grid_per_cu=16),         # more workgroups than row groups: some idle
+    dict(row_order=1, team_threads=256, teams=4),
 ]
 
 
