@@ -51,11 +51,11 @@ bool block_menu(bool vec, int vpt, int rows, int lb) {
   switch (lb) {
   case 256:
     return (vpt == 1 && (rows == 1 || rows == 2 || rows == 4)) ||
-           (vpt == 2 && (rows == 1 || rows == 2)) || (vpt == 4 && rows == 1) ||
+           (vpt == 2 && (rows == 1 || rows == 2 || rows == 4)) || (vpt == 4 && rows == 1) ||
            (vpt == 8 && rows == 1);
   case 512:
-    return (vpt == 1 && (rows == 1 || rows == 2)) || (vpt == 2 && (rows == 1 || rows == 2)) ||
-           (vpt == 4 && rows == 1);
+    return (vpt == 1 && (rows == 1 || rows == 2 || rows == 4)) ||
+           (vpt == 2 && (rows == 1 || rows == 2)) || (vpt == 4 && rows == 1);
   case 1024:
     return (vpt == 1 && (rows == 1 || rows == 2)) || (vpt == 2 && rows == 1);
   default: return false;
@@ -261,12 +261,13 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       p.rows = 1;
       p.grid = Mm * p.chunks;
     } else {
-      int64_t G = t.row_groups > 0 ? t.row_groups : cdiv(cu, p.chunks);
+      // about two (row group, chunk) workgroups per CU for the second pass
+      int64_t G = t.row_groups > 0 ? t.row_groups : cdiv(2 * (int64_t)cu, p.chunks);
       if (G < 1) G = 1;
       if (G > Mm) G = Mm;
       const int64_t rpg = cdiv(Mm, G);
       G = cdiv(Mm, rpg);
-      int rows = t.rows > 0 ? t.rows : (vpt >= 4 ? 2 : 4);
+      int rows = t.rows > 0 ? t.rows : (vpt >= 4 ? 1 : 2);
       if (!split_bwd_menu(vec, vpt, rows)) rows = 1;
       if (!split_bwd_menu(vec, vpt, rows)) return NORM_ERR_UNSUPPORTED;
       p.rows = rows;

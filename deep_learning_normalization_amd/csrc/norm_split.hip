@@ -252,7 +252,9 @@ __global__ __launch_bounds__(SPLIT_LB) void split_finalize_stats_kernel(BwdArgs 
 
 // ---- backward pass 1: row partials ---------------------------------------------------------
 
-template <typename T, bool VEC, int VPT, int ROWS, bool LN>
+// One workgroup per (row, chunk), like the forward's statistics pass: the whole grid streams X
+// and dY once, with no loop-carried latency.
+template <typename T, bool VEC, int VPT, bool LN>
 __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
@@ -260,92 +262,70 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
   __shared__ __align__(16) float red[RED_FLOATS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
   const int64_t C = a.chunks;
-  const int64_t g = (int64_t)blockIdx.x / C;
-  const int64_t c = (int64_t)blockIdx.x - g * C;
+  const int64_t row = (int64_t)blockIdx.x / C;
+  const int64_t c = (int64_t)blockIdx.x - row * C;
   const int64_t acc0 = c * a.chunk_acc;
   const int64_t left = (int64_t)a.nacc - acc0;
   const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
-  const int64_t N = a.N;
-  const int64_t r_begin = g * a.rows_per_group;
-  const int64_t r_end = r_begin + a.rows_per_group < a.M ? r_begin + a.rows_per_group : a.M;
-  const T *__restrict__ X = static_cast<const T *>(a.x) + acc0 * E;
-  const T *__restrict__ DY = static_cast<const T *>(a.dy) + acc0 * E;
+  const int64_t base = row * (int64_t)a.N + acc0 * E;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + base;
+  const T *__restrict__ DY = static_cast<const T *>(a.dy) + base;
   const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
   const float *mean_p = a.rstd ? a.mean : a.stats;
 
-  float w[VPT][E];
+  raw rx[VPT], rdy[VPT], rw[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
-    raw rw = A::zero();
-    if (v < nin) rw = A::ld_cached(W + (int64_t)v * E);
-    A::unpack(rw, w[k]);
+    rx[k] = A::zero();
+    rdy[k] = A::zero();
+    rw[k] = A::zero();
+    if (v < nin) {
+      rx[k] = A::ld(X + (int64_t)v * E);
+      rdy[k] = A::ld(DY + (int64_t)v * E);
+      rw[k] = A::ld_cached(W + (int64_t)v * E);
+    }
+  }
+  const float m = (LN && mean_p) ? mean_p[row] : 0.0f;
+  constexpr int NV = LN ? 3 : 1;
+  float sums[NV];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const bool in = tid + k * SPLIT_LB < nin;
+    float xf[E], df[E], wf[E];
+    A::unpack(rx[k], xf);
+    A::unpack(rdy[k], df);
+    A::unpack(rw[k], wf);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float d = in ? xf[e] - m : 0.0f;
+      const float gg = df[e] * wf[e];
+      sums[0] += gg * d;
+      if constexpr (LN) {
+        sums[1] += gg;
+        sums[2] += d;
+      }
+    }
   }
   int slot = 0;
-  for (int64_t row0 = r_begin; row0 < r_end; row0 += ROWS) {
-    raw rx[ROWS][VPT], rdy[ROWS][VPT];
-    float m[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const bool rv = row0 + r < r_end;
-      const int64_t rowc = rv ? row0 + r : r_end - 1;
-      m[r] = (LN && mean_p) ? mean_p[rowc] : 0.0f;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int v = tid + k * SPLIT_LB;
-        rx[r][k] = A::zero();
-        rdy[r][k] = A::zero();
-        if (rv && v < nin) {
-          rx[r][k] = A::ld(X + (row0 + r) * N + (int64_t)v * E);
-          rdy[r][k] = A::ld(DY + (row0 + r) * N + (int64_t)v * E);
-        }
-      }
-    }
-    constexpr int NV = LN ? 3 * ROWS : ROWS;
-    float sums[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const bool rv = row0 + r < r_end;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const bool in = rv && tid + k * SPLIT_LB < nin;
-        float xf[E], df[E];
-        A::unpack(rx[r][k], xf);
-        A::unpack(rdy[r][k], df);
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float d = in ? xf[e] - m[r] : 0.0f;
-          const float gg = df[e] * w[k][e];
-          sums[r] += gg * d;
-          if constexpr (LN) {
-            sums[ROWS + r] += gg;
-            sums[2 * ROWS + r] += d;
-          }
-        }
-      }
-    }
-    team_sum<NV, SPLIT_LB / 64>(sums, red, slot, waves, 0, wave, lane);
-    slot ^= 1;
-    if (tid == 0) {
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        if (row0 + r < r_end) {
-          float *out = a.rowpart + ((row0 + r) * C + c) * RP;
-          out[0] = sums[r];
-          if constexpr (LN) {
-            out[1] = sums[ROWS + r];
-            out[2] = sums[2 * ROWS + r];
-          }
-        }
-      }
+  team_sum<NV, SPLIT_LB / 64>(sums, red, slot, waves, 0, wave, lane);
+  if (tid == 0) {
+    float *out = a.rowpart + (row * C + c) * RP;
+    out[0] = sums[0];
+    if constexpr (LN) {
+      out[1] = sums[1];
+      out[2] = sums[2];
     }
   }
 }
 
 // ---- backward pass 2: dX and the column partials -------------------------------------------
 
+// One workgroup per (row group, chunk). Rows are visited in descending order (the last rows
+// pass 1 read come back first) and the next row group's X and dY are requested before the
+// current one is combined and written.
 template <typename T, bool VEC, int VPT, int ROWS, bool LN>
 __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   using A = Acc<T, VEC>;
@@ -372,40 +352,53 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   const float *rstd_p = a.rstd ? a.rstd : a.stats + a.M;
   if (!a.dw) write_ws_header(a.header, a.row_groups, N);
 
-  float w[VPT][E], accw[VPT][E], accb[LN ? VPT : 1][E];
+  // the weight stays packed (half the registers for bf16), unpacked at use
+  raw rw[VPT];
+  float accw[VPT][E], accb[LN ? VPT : 1][E];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
-    raw rw = A::zero();
-    if (v < nin) rw = A::ld_cached(W + (int64_t)v * E);
-    A::unpack(rw, w[k]);
+    rw[k] = A::zero();
+    if (v < nin) rw[k] = A::ld_cached(W + (int64_t)v * E);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       accw[k][e] = 0.0f;
       if constexpr (LN) accb[k][e] = 0.0f;
     }
   }
-  int slot = 0;
-  const int64_t nrows = r_end - r_begin;
+  const int64_t nrows = r_end > r_begin ? r_end - r_begin : 0;
   const int64_t iters = (nrows + ROWS - 1) / ROWS;
-  // rows in descending order: the last rows pass 1 read are re-read first
+  raw px[ROWS][VPT], pdy[ROWS][VPT];
+  auto issue = [&](int64_t it) {
+    const int64_t row0 = r_begin + it * ROWS;
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      const bool rv = it >= 0 && row0 + r < r_end;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const int v = tid + k * SPLIT_LB;
+        px[r][k] = A::zero();
+        pdy[r][k] = A::zero();
+        if (rv && v < nin) {
+          px[r][k] = A::ld(X + (row0 + r) * N + (int64_t)v * E);
+          pdy[r][k] = A::ld(DY + (row0 + r) * N + (int64_t)v * E);
+        }
+      }
+    }
+  };
+  int slot = 0;
+  issue(iters - 1);
   for (int64_t it = iters - 1; it >= 0; --it) {
     const int64_t row0 = r_begin + it * ROWS;
     raw rx[ROWS][VPT], rdy[ROWS][VPT];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const bool rv = row0 + r < r_end;
+    for (int r = 0; r < ROWS; ++r)
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
-        const int v = tid + k * SPLIT_LB;
-        rx[r][k] = A::zero();
-        rdy[r][k] = A::zero();
-        if (rv && v < nin) {
-          rx[r][k] = A::ld_cached(X + (row0 + r) * N + (int64_t)v * E);
-          rdy[r][k] = A::ld_cached(DY + (row0 + r) * N + (int64_t)v * E);
-        }
+        rx[r][k] = px[r][k];
+        rdy[r][k] = pdy[r][k];
       }
-    }
+    issue(it - 1);
     // combine the row partials of every chunk of these rows
     constexpr int NV = LN ? 3 * ROWS : ROWS;
     float sums[NV];
@@ -440,13 +433,14 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
       for (int k = 0; k < VPT; ++k) {
         const int v = tid + k * SPLIT_LB;
         const bool in = rv && v < nin;
-        float xf[E], df[E], dx[E];
+        float xf[E], df[E], wf[E], dx[E];
         A::unpack(rx[r][k], xf);
         A::unpack(rdy[r][k], df);
+        A::unpack(rw[k], wf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float xh = in ? ((xf[e] - m) - delta) * rstd : 0.0f;
-          dx[e] = rstd * (df[e] * w[k][e] - c1 - xh * c2);
+          dx[e] = rstd * (df[e] * wf[e] - c1 - xh * c2);
           accw[k][e] += df[e] * xh;
           if constexpr (LN) accb[k][e] += df[e];
         }
@@ -533,14 +527,14 @@ template <typename T> norm_status_t split_fwd_typed(const Plan &p, const FwdArgs
 
 template <typename T, bool VEC, int V, int R>
 hipError_t split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)p.grid), block(SPLIT_LB);
+  const dim3 grid1((unsigned)(a.M * a.chunks)), grid2((unsigned)p.grid), block(SPLIT_LB);
   hipError_t e;
   if (a.layernorm) {
-    e = launch(split_bwd_partial_kernel<T, VEC, V, R, true>, grid, block, s, a);
-    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, true>, grid, block, s, a);
+    e = launch(split_bwd_partial_kernel<T, VEC, V, true>, grid1, block, s, a);
+    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, true>, grid2, block, s, a);
   } else {
-    e = launch(split_bwd_partial_kernel<T, VEC, V, R, false>, grid, block, s, a);
-    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, false>, grid, block, s, a);
+    e = launch(split_bwd_partial_kernel<T, VEC, V, false>, grid1, block, s, a);
+    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, false>, grid2, block, s, a);
   }
   return e;
 }

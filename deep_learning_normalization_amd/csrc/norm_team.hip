@@ -708,9 +708,9 @@ hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
       X(4, 2, 256) X(8, 1, 256)
 #define DLN_WAVE_MENU_SCALAR(X) X(1, 1, 256) X(2, 1, 256) X(4, 1, 256) X(8, 1, 256) X(16, 1, 256)
 #define DLN_BLOCK_MENU(X)                                                                       \
-  X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(4, 1, 256) X(8, 1, 256)       \
-      X(1, 1, 512) X(1, 2, 512) X(2, 1, 512) X(2, 2, 512) X(4, 1, 512) X(1, 1, 1024)               \
-          X(1, 2, 1024) X(2, 1, 1024)
+  X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(2, 4, 256) X(4, 1, 256)       \
+      X(8, 1, 256) X(1, 1, 512) X(1, 2, 512) X(1, 4, 512) X(2, 1, 512) X(2, 2, 512) X(4, 1, 512)   \
+          X(1, 1, 1024) X(1, 2, 1024) X(2, 1, 1024)
 #define DLN_BLOCK_MENU_SCALAR(X) X(4, 1, 1024) X(8, 1, 1024)
 
 template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
