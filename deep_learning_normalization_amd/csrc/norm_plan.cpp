@@ -261,8 +261,8 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       p.rows = 1;
       p.grid = Mm * p.chunks;
     } else {
-      // about two (row group, chunk) workgroups per CU for the second pass
-      int64_t G = t.row_groups > 0 ? t.row_groups : cdiv(2 * (int64_t)cu, p.chunks);
+      // one (row group, chunk) workgroup per CU for the second pass
+      int64_t G = t.row_groups > 0 ? t.row_groups : cdiv((int64_t)cu, p.chunks);
       if (G < 1) G = 1;
       if (G > Mm) G = Mm;
       const int64_t rpg = cdiv(Mm, G);

@@ -368,12 +368,27 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   }
   const int64_t nrows = r_end > r_begin ? r_end - r_begin : 0;
   const int64_t iters = (nrows + ROWS - 1) / ROWS;
+  // Prefetched with the next rows: X, dY, the row statistics, and the row partials of up to
+  // RPF chunks per thread (the rest, for rows of more than RPF * 256 chunks, are read at use).
+  constexpr int RPF = 2;
+  constexpr int NQ = LN ? 3 : 1;
   raw px[ROWS][VPT], pdy[ROWS][VPT];
+  float pm[ROWS], prs[ROWS], pq[ROWS][RPF][NQ];
   auto issue = [&](int64_t it) {
     const int64_t row0 = r_begin + it * ROWS;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = it >= 0 && row0 + r < r_end;
+      const int64_t rowc = rv ? row0 + r : r_end - 1;
+      pm[r] = (LN && mean_p) ? mean_p[rowc] : 0.0f;
+      prs[r] = rstd_p[rowc];
+      const float *rp = a.rowpart + rowc * C * RP;
+#pragma unroll
+      for (int j = 0; j < RPF; ++j) {
+        const int64_t cc = tid + (int64_t)j * SPLIT_LB;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) pq[r][j][q] = cc < C ? rp[RP * cc + q] : 0.0f;
+      }
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = tid + k * SPLIT_LB;
@@ -391,29 +406,36 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   for (int64_t it = iters - 1; it >= 0; --it) {
     const int64_t row0 = r_begin + it * ROWS;
     raw rx[ROWS][VPT], rdy[ROWS][VPT];
+    float m_r[ROWS], rs_r[ROWS];
+    // combine the row partials of every chunk of these rows: this thread's chunks in
+    // ascending order, then the team sum
+    constexpr int NV = LN ? 3 * ROWS : ROWS;
+    float sums[NV];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r)
+    for (int r = 0; r < ROWS; ++r) {
+      m_r[r] = pm[r];
+      rs_r[r] = prs[r];
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int j = 0; j < RPF; ++j) acc += pq[r][j][q];
+        sums[q * ROWS + r] = acc;
+      }
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         rx[r][k] = px[r][k];
         rdy[r][k] = pdy[r][k];
       }
+    }
     issue(it - 1);
-    // combine the row partials of every chunk of these rows
-    constexpr int NV = LN ? 3 * ROWS : ROWS;
-    float sums[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int64_t rowc = row0 + r < r_end ? row0 + r : r_end - 1;
       const float *rp = a.rowpart + rowc * C * RP;
-      for (int64_t cc = tid; cc < C; cc += blockDim.x) {
-        sums[r] += rp[RP * cc];
-        if constexpr (LN) {
-          sums[ROWS + r] += rp[RP * cc + 1];
-          sums[2 * ROWS + r] += rp[RP * cc + 2];
-        }
+      for (int64_t cc = tid + (int64_t)RPF * SPLIT_LB; cc < C; cc += SPLIT_LB) {
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) sums[q * ROWS + r] += rp[RP * cc + q];
       }
     }
     team_sum<NV, SPLIT_LB / 64>(sums, red, slot, waves, 0, wave, lane);
@@ -422,9 +444,8 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
     for (int r = 0; r < ROWS; ++r) {
       const int64_t row = row0 + r;
       const bool rv = row < r_end;
-      const int64_t rowc = rv ? row : r_end - 1;
-      const float m = (LN && mean_p) ? mean_p[rowc] : 0.0f;
-      const float rstd = rstd_p[rowc];
+      const float m = m_r[r];
+      const float rstd = rs_r[r];
       const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
       const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
       const float c2 = LN ? rstd * (sums[r] - delta * sums[ROWS + r]) * a.inv_n
