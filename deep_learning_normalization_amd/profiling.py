@@ -1,8 +1,17 @@
-"""Summaries of rocprofv3 output for the norm kernels (kernel durations and HBM traffic).
+"""rocprofv3 support for the norm kernels: a workload driver and summaries of kernel durations
+and HBM traffic.
 
+    python -m deep_learning_normalization_amd.profiling drive --workload NAME [--steps K]
     python -m deep_learning_normalization_amd.profiling stats --trace DIR --out FILE --cmd "..."
     python -m deep_learning_normalization_amd.profiling traffic --fetch DIR --write DIR \\
         --workload NAME --kernel SUBSTR --algo-bytes N --out FILE --cmd "..."
+    python -m deep_learning_normalization_amd.profiling workloads --root DIR --out FILE --cmd "..."
+
+`drive` runs one workload's forward and backward K times on two rotating buffer sets (run it
+under rocprofv3); it first makes the 1 GiB device copies the counter calibration uses.
+`workloads` summarises, for every workload, the three runs <root>/<name>/{trace,fetch,write}
+of `drive`: per kernel, its average duration, its calibrated HBM bytes and those bytes over
+the pass's algorithmic bytes.
 
 `stats` reads <DIR>/*_kernel_stats.csv and *_kernel_trace.csv (rocprofv3 --kernel-trace --stats
 --output-format csv) and writes the per-kernel average durations plus the idle gaps between
@@ -118,6 +127,115 @@ def traffic(fetch_dir, write_dir, workload, kernel, algo_bytes, out, cmd):
     return d
 
 
+# ---- workload driver -------------------------------------------------------------------------
+
+def drive(name, steps):
+    """Forward then backward of one workload, `steps` times over two buffer sets."""
+    import torch
+    from deep_learning_normalization_amd import inputs, normlib as nl
+    w = {x.name: x for x in inputs.all_workloads()}[name]
+    nl.lib()
+    # calibration: 1 GiB device-to-device copies of known size
+    a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+    b = torch.empty_like(a)
+    for _ in range(4):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    del a, b
+    torch.cuda.empty_cache()
+    host = inputs.make(w)
+    dev = [{k: (v.cuda() if v is not None else None) for k, v in host.items()} for _ in range(2)]
+    ln = w.kind == "layernorm"
+    M, N = w.M, w.N
+    outs = []
+    for d in dev:
+        X = d["X"]
+        outs.append({"Y": torch.empty_like(X),
+                     "H": torch.empty_like(X) if d["R"] is not None else None,
+                     "mean": torch.empty(M, device="cuda") if ln else None,
+                     "rstd": torch.empty(M, device="cuda"), "dX": torch.empty_like(X)})
+    W, B = dev[0]["W"], dev[0]["B"]
+    dW = torch.empty_like(W)
+    dB = torch.empty_like(W) if ln else None
+    wsf = nl.workspace(w.kind, host["X"].dtype, nl.PASS_FWD, M, N, w.r is not None)
+    wsb = nl.workspace(w.kind, host["X"].dtype, nl.PASS_BWD, M, N)
+    for i in range(steps):
+        d, o = dev[i % 2], outs[i % 2]
+        nl.norm_fwd(w.kind, d["X"], d["R"], W, B, w.eps, o["Y"], o["H"], o["mean"], o["rstd"],
+                    wsf)
+        if w.dy is not None:
+            Xin = o["H"] if o["H"] is not None else d["X"]
+            nl.norm_bwd(w.kind, Xin, d["dY"], None, W, o["mean"], o["rstd"], w.eps, o["dX"],
+                        None, dW, dB, wsb)
+    torch.cuda.synchronize()
+
+
+def _kernel_rows(trace_dir):
+    rows = list(csv.DictReader(open(_one(trace_dir, "_kernel_trace.csv"))))
+    per = {}
+    for r in rows:
+        if "dln::" not in r["Kernel_Name"]:
+            continue
+        per.setdefault(_short(r["Kernel_Name"]), []).append(
+            (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    return per
+
+
+def workloads(root, out, cmd):
+    """Markdown table over every workload directory under root."""
+    from deep_learning_normalization_amd import inputs, traffic
+    lines = ["# Norm kernels per workload: duration and HBM traffic (rocprofv3)", "",
+             "command (per workload NAME): %s" % cmd, "",
+             "HBM bytes = FETCH_SIZE x fetch calibration + WRITE_SIZE x write calibration, the "
+             "factors taken from 1 GiB device copies in the same run. 'algorithmic' is the "
+             "pass's minimum traffic; the backward's dW/dB partials are extra by design.", "",
+             "| workload | kernel | launches | avg us | HBM MB/launch | pass | algorithmic MB | "
+             "HBM / algorithmic | GB/s (HBM) |", "|---|---|---|---|---|---|---|---|---|"]
+    for w in inputs.all_workloads():
+        d = os.path.join(root, w.name)
+        if not os.path.isdir(d):
+            continue
+        dur = _kernel_rows(os.path.join(d, "trace"))
+        fetch = _counter(os.path.join(d, "fetch"), "FETCH_SIZE")
+        write = _counter(os.path.join(d, "write"), "WRITE_SIZE")
+        cf = sorted(fetch.get(COPY_KERNEL, []))[-4:]
+        cw = sorted(write.get(COPY_KERNEL, []))[-4:]
+        f_factor = COPY_BYTES / (statistics.median(cf) * 1024.0)
+        w_factor = COPY_BYTES / (statistics.median(cw) * 1024.0)
+        res = w.r is not None
+        fwd_alg = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res)
+        bwd_alg = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N) if w.dy is not None else 0
+        names = {_short(n): n for n in fetch if "dln::" in n}
+        for short in sorted(names, key=lambda k: (("bwd" in k or "colsum" in k or "dx" in k
+                                                   or "partial" in k), k)):
+            full = names[short]
+            fb = statistics.median(fetch[full]) * 1024.0 * f_factor
+            wb = statistics.median(write.get(full, [0.0])) * 1024.0 * w_factor
+            us = statistics.mean(dur.get(short, [float("nan")]))
+            bwd_kernel = any(t in short for t in ("bwd", "colsum", "partial", "dx_kernel"))
+            alg = bwd_alg if bwd_kernel else fwd_alg
+            lines.append("| %s | %s | %d | %.2f | %.1f | %s | %.1f | | %.0f |" % (
+                w.name, short, len(dur.get(short, [])), us, (fb + wb) / 1e6,
+                "bwd" if bwd_kernel else "fwd", alg / 1e6, (fb + wb) / (us * 1e-6) / 1e9))
+        # per pass totals: all kernels of the pass
+        for pname, alg, sel in (("fwd", fwd_alg, False), ("bwd", bwd_alg, True)):
+            if not alg:
+                continue
+            tot_b = tot_us = 0.0
+            for short, full in names.items():
+                bk = any(t in short for t in ("bwd", "colsum", "partial", "dx_kernel"))
+                if bk != sel:
+                    continue
+                tot_b += (statistics.median(fetch[full]) * f_factor +
+                          statistics.median(write.get(full, [0.0])) * w_factor) * 1024.0
+                tot_us += statistics.mean(dur.get(short, [0.0]))
+            lines.append("| %s | **%s pass, all kernels** | | %.2f | %.1f | %s | %.1f | %.3f | "
+                         "%.0f |" % (w.name, pname, tot_us, tot_b / 1e6, pname, alg / 1e6,
+                                     tot_b / alg, alg / (tot_us * 1e-6) / 1e9))
+    with open(out, "w") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -133,8 +251,19 @@ def main():
     t.add_argument("--algo-bytes", type=int, required=True)
     t.add_argument("--out", required=True)
     t.add_argument("--cmd", required=True)
+    d = sub.add_parser("drive")
+    d.add_argument("--workload", required=True)
+    d.add_argument("--steps", type=int, default=20)
+    wk = sub.add_parser("workloads")
+    wk.add_argument("--root", required=True)
+    wk.add_argument("--out", required=True)
+    wk.add_argument("--cmd", required=True)
     a = ap.parse_args()
-    if a.what == "stats":
+    if a.what == "drive":
+        drive(a.workload, a.steps)
+    elif a.what == "workloads":
+        workloads(a.root, a.out, a.cmd)
+    elif a.what == "stats":
         stats(a.trace, a.out, a.cmd)
     else:
         print(json.dumps(traffic(a.fetch, a.write, a.workload, a.kernel, a.algo_bytes, a.out,
