@@ -23,7 +23,7 @@ constexpr int64_t kMaxGrid = 2147483647; // workgroups per launch
 constexpr int kWaveThreads = 256;        // wave scheme: four one-wave teams per workgroup
 constexpr int kSplitThreads = 256;
 constexpr int kWaveMaxRow = 1024;        // wave scheme for rows up to this many elements
-constexpr int kBlockTeamTarget = 512;    // preferred largest team for the block scheme
+constexpr int kBlockTeamTarget = 256;    // preferred largest team for the block scheme
 constexpr int kBlockTeamTargetBwd = 640; // the backward prefers one access per thread longer
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -101,7 +101,7 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
     g_tuning.scheme = (int)v;
     return NORM_OK;
   case NORM_TUNE_GRID_PER_CU:
-    if (v != -1 && (v < 1 || v > 64)) return NORM_ERR_INVALID_ARG;
+    if (v != -1 && (v < 1 || v > 4096)) return NORM_ERR_INVALID_ARG;
     g_tuning.grid_per_cu = (int)v;
     return NORM_OK;
   case NORM_TUNE_ROWS_PER_ITER:
@@ -135,7 +135,6 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
 norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
                         int64_t N, int residual, int aligned, int cu, const Tuning &t,
                         Plan *out) {
-  (void)residual;
   if (!out || !valid_kind(kind) || !valid_dtype(dtype) ||
       (pass != NORM_PASS_FWD && pass != NORM_PASS_BWD) || M < 0 || N <= 0 || N > kMaxN ||
       cu <= 0)
@@ -233,13 +232,20 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.threads = tt * teams;
     p.lb = vec ? (teams > 1 ? lb_of(p.threads) : lb_pick) : 1024;
     const int64_t groups = cdiv(Mm, (int64_t)rows * teams);
-    // Workgroups per CU: enough 16-byte accesses in flight per CU (about 2048 for the forward,
-    // 1024 per tensor for the backward, whose workgroups also each write a partial row).
-    const int64_t per_cu = bwd ? 1024 : 2048;
-    const int64_t load = (int64_t)p.threads * vpt * rows;
-    const int64_t gpc_default = per_cu / load > 0 ? per_cu / load : 1;
-    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : gpc_default;
-    p.grid = groups < cu * gpc ? groups : cu * gpc;
+    if (bwd) {
+      // Backward: persistent, about 1024 16-byte accesses per tensor in flight per CU; every
+      // workgroup writes one partial row, so fewer, longer-lived workgroups.
+      const int64_t load = (int64_t)p.threads * vpt * rows;
+      const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1);
+      p.grid = groups < cu * gpc ? groups : cu * gpc;
+    } else if (t.grid_per_cu > 0) {
+      p.grid = groups < cu * t.grid_per_cu ? groups : cu * t.grid_per_cu;
+    } else {
+      // Forward (measured on MI355X): short-lived workgroups of two row groups each (the second
+      // group's loads overlap the first's reductions), one for the residual variant, whose
+      // four streams per row already keep enough requests in flight.
+      p.grid = residual ? groups : cdiv(groups, 2);
+    }
     p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_SPLIT) {
     int vpt = vec ? 4 : 8;
