@@ -146,16 +146,25 @@ __device__ __forceinline__ float read_lane(float v, int lane) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
-// Sum over the 64 lanes of a wavefront. Every step pairs lanes symmetrically, so all lanes end
-// with the same bits; the four 16-lane row sums are then combined in a fixed order through
-// scalar registers. All 64 lanes must be active.
+// DPP move into the rows of ROWMASK only; the other rows get 0.
+template <int CTRL, int ROWMASK> __device__ __forceinline__ float dpp_rows(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                               CTRL, ROWMASK, 0xF, false));
+}
+
+// Sum over the 64 lanes of a wavefront, returned as a wave-uniform value. Four symmetric
+// steps leave every lane of each 16-lane row with that row's sum r0..r3; two row broadcasts
+// (lane 15 of a row into the next row, then lane 31 into rows 2 and 3) leave
+// (r3 + r2) + (r1 + r0) in lane 63, which is read out. The order is fixed, so the result is
+// the same bits on every call with the same inputs. All 64 lanes must be active.
 __device__ __forceinline__ float wave_sum(float v) {
-  v += dpp_mov<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
-  v += dpp_mov<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
-  v += dpp_mov<0x141>(v); // row_half_mirror: quad 0 <-> quad 1 within each 8 lanes
-  v += dpp_mov<0x140>(v); // row_mirror: the two 8-lane halves of each 16-lane row
-  float r0 = read_lane(v, 0), r1 = read_lane(v, 16), r2 = read_lane(v, 32), r3 = read_lane(v, 48);
-  return (r0 + r1) + (r2 + r3);
+  v += dpp_mov<0xB1>(v);         // quad_perm [1,0,3,2]: lane ^ 1
+  v += dpp_mov<0x4E>(v);         // quad_perm [2,3,0,1]: lane ^ 2
+  v += dpp_mov<0x141>(v);        // row_half_mirror: quad 0 <-> quad 1 within each 8 lanes
+  v += dpp_mov<0x140>(v);        // row_mirror: the two 8-lane halves of each 16-lane row
+  v += dpp_rows<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_rows<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return read_lane(v, 63);
 }
 
 // LDS scratch for team sums: 2 alternating slots x up to 12 values x 16 waves, plus one row of
@@ -186,6 +195,24 @@ __device__ __forceinline__ void team_sum(float (&v)[NV], float *red, int slot, i
     for (int i = 0; i < NV; ++i) base[i * RED_WAVES + wave] = v[i];
   }
   __syncthreads();
+  if (waves == MAXW) {
+    // the whole workgroup is one team: every word read is a partial (same order, no selects)
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+      const float4 *q = reinterpret_cast<const float4 *>(base + i * RED_WAVES);
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < (MAXW == 1 ? 1 : MAXW / 4); ++j) {
+        const float4 f = q[j];
+        s += f.x;
+        s += f.y;
+        s += f.z;
+        s += f.w;
+      }
+      v[i] = s;
+    }
+    return;
+  }
 #pragma unroll
   for (int i = 0; i < NV; ++i) {
     const float4 *q = reinterpret_cast<const float4 *>(base + i * RED_WAVES + wave0);

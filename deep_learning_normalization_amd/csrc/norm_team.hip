@@ -255,11 +255,18 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 
 // ---- backward -----------------------------------------------------------------------------
 
+// Per element: unpack x, dY (and W once per row group), d = x - m, g = dY * W, the row sums;
+// after the team sum, with per-row constants a = rstd, nd = -delta * rstd,
+// B = -rstd * c2, C = -rstd * c1: xhat = d * a + nd, dX = g * a + (xhat * B + C), and the
+// dW / dB column sums. d, g and dY stay in registers across the team sum when the thread holds
+// at most 16 elements of the row group (else they are formed again from the packed data).
 template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool LN>
 __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_threads) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
+  constexpr int MAXW = WAVE ? 1 : LB / 64;
+  constexpr bool KEEP = VPT * ROWS * E <= 16;
   __shared__ __align__(16) float red[RED_FLOATS];
   __shared__ float merge[MERGE_FLOATS];
   const TeamGeom gm = team_geom<WAVE>(team_threads);
@@ -357,7 +364,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           }
           s[r] = acc;
         }
-        team_sum<ROWS, (WAVE ? 1 : LB / 64)>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        team_sum<ROWS, MAXW>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
         slot ^= 1;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) m[r] = mul_rn(s[r], a.inv_n);
@@ -367,20 +374,21 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           float q = 0.0f, c = 0.0f;
 #pragma unroll
           for (int k = 0; k < VPT; ++k) {
-            const bool in = gm.t + k * gm.tt < nacc; // rows past M are all zeros
-            float f[E];
-            A::unpack(rx[r][k], f);
+            if (gm.t + k * gm.tt < nacc) { // rows past M are all zeros
+              float f[E];
+              A::unpack(rx[r][k], f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) {
-              const float d = in ? f[e] - m[r] : 0.0f;
-              q += d * d;
-              c += d;
+              for (int e = 0; e < E; ++e) {
+                const float d = f[e] - m[r];
+                q = __builtin_fmaf(d, d, q);
+                c += d;
+              }
             }
           }
           qc[r] = q;
           qc[ROWS + r] = c;
         }
-        team_sum<2 * ROWS, (WAVE ? 1 : LB / 64)>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        team_sum<2 * ROWS, MAXW>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
         slot ^= 1;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -397,11 +405,11 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
             float f[E];
             A::unpack(rx[r][k], f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc += f[e] * f[e];
+            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
           }
           q[r] = acc;
         }
-        team_sum<ROWS, (WAVE ? 1 : LB / 64)>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+        team_sum<ROWS, MAXW>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
         slot ^= 1;
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
@@ -419,70 +427,98 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
     float sums[NV];
 #pragma unroll
     for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
+    float kd[KEEP ? ROWS : 1][KEEP ? VPT : 1][E], kg[KEEP ? ROWS : 1][KEEP ? VPT : 1][E],
+        kdy[KEEP ? ROWS : 1][KEEP ? VPT : 1][E];
 #pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const bool rv = row0 + r < M;
+    for (int k = 0; k < VPT; ++k) {
+      float wf[E];
+      A::unpack(rw[k], wf);
+      const bool in = gm.t + k * gm.tt < nacc;
 #pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const bool in = rv && gm.t + k * gm.tt < nacc;
-        float xf[E], df[E], wf[E];
+      for (int r = 0; r < ROWS; ++r) {
+        float xf[E], df[E];
         A::unpack(rx[r][k], xf);
         A::unpack(rdy[r][k], df);
-        A::unpack(rw[k], wf);
+        float d[E], gg[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const float d = in ? xf[e] - m[r] : 0.0f;
-          const float gg = df[e] * wf[e];
-          sums[r] += gg * d;
-          if constexpr (LN) {
-            sums[ROWS + r] += gg;
-            sums[2 * ROWS + r] += d;
+          d[e] = LN ? xf[e] - m[r] : xf[e];
+          gg[e] = df[e] * wf[e];
+          // columns past N hold x = dY = 0: g * d adds nothing there
+          sums[r] = __builtin_fmaf(gg[e], d[e], sums[r]);
+          if constexpr (LN) sums[ROWS + r] += gg[e];
+        }
+        if constexpr (LN) {
+          if (in) {
+#pragma unroll
+            for (int e = 0; e < E; ++e) sums[2 * ROWS + r] += d[e];
+          }
+        }
+        if constexpr (KEEP) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            kd[KEEP ? r : 0][KEEP ? k : 0][e] = d[e];
+            kg[KEEP ? r : 0][KEEP ? k : 0][e] = gg[e];
+            kdy[KEEP ? r : 0][KEEP ? k : 0][e] = df[e];
           }
         }
       }
     }
-    team_sum<NV, (WAVE ? 1 : LB / 64)>(sums, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
+    team_sum<NV, MAXW>(sums, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
     slot ^= 1;
 
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const int64_t row = row0 + r;
-      const bool rv = row < M;
+      if (row >= M) continue; // rows past M add nothing to dW / dB and write nothing
       const int64_t base = row * N;
       const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
       const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
       const float c2 =
           LN ? rstd[r] * (sums[r] - delta * sums[ROWS + r]) * a.inv_n : rstd[r] * sums[r] * a.inv_n;
+      const float ra = rstd[r], nd = -delta * rstd[r];
+      const float cB = -rstd[r] * c2, cC = -rstd[r] * c1;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
-        const bool in = v < nacc;
-        float xf[E], df[E], wf[E], dx[E];
-        A::unpack(rx[r][k], xf);
-        A::unpack(rdy[r][k], df);
-        A::unpack(rw[k], wf);
+        if (v >= nacc) continue; // columns past N: nothing to add or write
+        float d[E], gg[E], df[E];
+        if constexpr (KEEP) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            d[e] = kd[KEEP ? r : 0][KEEP ? k : 0][e];
+            gg[e] = kg[KEEP ? r : 0][KEEP ? k : 0][e];
+            df[e] = kdy[KEEP ? r : 0][KEEP ? k : 0][e];
+          }
+        } else {
+          float xf[E], wf[E];
+          A::unpack(rx[r][k], xf);
+          A::unpack(rdy[r][k], df);
+          A::unpack(rw[k], wf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            d[e] = LN ? xf[e] - m[r] : xf[e];
+            gg[e] = df[e] * wf[e];
+          }
+        }
+        float dx[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          // rows past M and columns past N hold zeros and must add nothing (even if rstd is
-          // infinite there, as for eps = 0)
-          const float xh = (rv && in) ? ((xf[e] - m[r]) - delta) * rstd[r] : 0.0f;
-          const float gg = df[e] * wf[e];
-          dx[e] = rstd[r] * (gg - c1 - xh * c2);
-          accw[k][e] += df[e] * xh;
+          const float xh = __builtin_fmaf(d[e], ra, nd);
+          dx[e] = __builtin_fmaf(gg[e], ra, __builtin_fmaf(xh, cB, cC));
+          accw[k][e] = __builtin_fmaf(df[e], xh, accw[k][e]);
           if constexpr (LN) accb[k][e] += df[e];
         }
-        if (rv && in) {
-          const int64_t off = base + (int64_t)v * E;
-          if (DH) {
-            float hf[E];
-            A::unpack(A::ld(DH + off), hf);
+        const int64_t off = base + (int64_t)v * E;
+        if (DH) {
+          float hf[E];
+          A::unpack(A::ld(DH + off), hf);
 #pragma unroll
-            for (int e = 0; e < E; ++e) dx[e] += hf[e];
-          }
-          const raw p = A::pack(dx);
-          A::st(DX + off, p);
-          if (DR) A::st(DR + off, p);
+          for (int e = 0; e < E; ++e) dx[e] += hf[e];
         }
+        const raw p = A::pack(dx);
+        A::st(DX + off, p);
+        if (DR) A::st(DR + off, p);
       }
     }
   }
