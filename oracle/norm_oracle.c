@@ -48,7 +48,9 @@
 #endif
 
 enum { OR_LAYERNORM = 0, OR_RMSNORM = 1 };
-enum { OR_F32 = 0, OR_BF16 = 1 };
+/* dtype: the storage type of every tensor, or OR_BF16_F32W = bf16 activations and gradients
+ * (X, R, dY, dH) with fp32 weight and bias (their gradients are then fp32 too). */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_BF16_F32W = 2 };
 
 enum {
   OR_OK = 0,
@@ -93,6 +95,10 @@ static double or_round_to_bf16(double v) {
   return v < 0 ? -out : out;
 }
 
+/* storage type of the activations, and of the weight and bias, for a call's dtype */
+static int or_act(int dtype) { return dtype == OR_BF16_F32W ? OR_BF16 : dtype; }
+static int or_wt(int dtype) { return dtype == OR_BF16_F32W ? OR_F32 : dtype; }
+
 static double or_round_to_dtype(int dtype, double v) {
   if (dtype == OR_F32) return (double)(float)v; /* C conversion: round to nearest even */
   return or_round_to_bf16(v);
@@ -112,7 +118,7 @@ static uint16_t or_bf16_bits(double v) {
 static int or_check(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64_t r1,
                     double eps) {
   if (kind != OR_LAYERNORM && kind != OR_RMSNORM) return OR_BAD_ARG;
-  if (dtype != OR_F32 && dtype != OR_BF16) return OR_BAD_ARG;
+  if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_BF16_F32W) return OR_BAD_ARG;
   if (M < 0 || N <= 0) return OR_BAD_ARG;
   if (r0 < 0 || r1 < r0 || r1 > M) return OR_BAD_ARG;
   if (!(eps >= 0.0)) return OR_BAD_ARG;
@@ -158,10 +164,10 @@ static void or_row_stats(int kind, int64_t N, const double *x, double eps, doubl
 
 /*
  * Forward over rows [r0, r1) of an M x N row-major input.
- *   X     : input bits (dtype), M*N
- *   R     : residual bits (dtype), M*N, or NULL
- *   W     : weight bits (dtype), N
- *   B     : bias bits (dtype), N, or NULL (LayerNorm only; NULL means zero bias)
+ *   X     : input bits (the activation type of dtype), M*N
+ *   R     : residual bits (activation type), M*N, or NULL
+ *   W     : weight bits (the weight type of dtype), N
+ *   B     : bias bits (weight type), N, or NULL (LayerNorm only; NULL means zero bias)
  *   Y     : out, (r1-r0)*N doubles, unrounded
  *   H     : out, (r1-r0)*N doubles holding round(R + X), or NULL (only with R)
  *   mean  : out, (r1-r0) doubles, or NULL (0 for RMSNorm)
@@ -188,14 +194,14 @@ int oracle_fwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64
     for (int64_t i = r0; i < r1; ++i) {
       if (!x) continue;
       int64_t o = i - r0;
-      or_input_row(dtype, N, i, X, R, x);
+      or_input_row(or_act(dtype), N, i, X, R, x);
       if (H)
         for (int64_t j = 0; j < N; ++j) H[o * N + j] = x[j];
       double mu, rs;
       or_row_stats(kind, N, x, eps, &mu, &rs);
       for (int64_t j = 0; j < N; ++j) {
-        double w = or_load(dtype, W, j);
-        double b = B ? or_load(dtype, B, j) : 0.0;
+        double w = or_load(or_wt(dtype), W, j);
+        double b = B ? or_load(or_wt(dtype), B, j) : 0.0;
         double xhat = (kind == OR_LAYERNORM) ? (x[j] - mu) * rs : x[j] * rs;
         Y[o * N + j] = (kind == OR_LAYERNORM) ? xhat * w + b : xhat * w;
       }
@@ -256,13 +262,13 @@ int oracle_bwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64
     for (int64_t i = r0; i < r1; ++i) {
       if (!x || !xh || !g) continue;
       int64_t o = i - r0;
-      or_input_row(dtype, N, i, X, NULL, x);
+      or_input_row(or_act(dtype), N, i, X, NULL, x);
       or_row_stats(kind, N, x, eps, &mu[o], &rs[o]);
       if (!dX) continue;
       double sg = 0.0, sgx = 0.0;
       for (int64_t j = 0; j < N; ++j) {
         xh[j] = (kind == OR_LAYERNORM) ? (x[j] - mu[o]) * rs[o] : x[j] * rs[o];
-        g[j] = or_load(dtype, dY, i * N + j) * or_load(dtype, W, j);
+        g[j] = or_load(or_act(dtype), dY, i * N + j) * or_load(or_wt(dtype), W, j);
         sg += g[j];
         sgx += g[j] * xh[j];
       }
@@ -271,7 +277,7 @@ int oracle_bwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64
       for (int64_t j = 0; j < N; ++j) {
         double d = (kind == OR_LAYERNORM) ? rs[o] * (g[j] - c1 - xh[j] * c2)
                                           : rs[o] * (g[j] - xh[j] * c2);
-        if (dH) d += or_load(dtype, dH, i * N + j);
+        if (dH) d += or_load(or_act(dtype), dH, i * N + j);
         dX[o * N + j] = d;
       }
     }
@@ -303,9 +309,9 @@ int oracle_bwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64
           for (int64_t i = r0; i < r1; ++i) {
             int64_t o = i - r0;
             for (int64_t j = j0; j < j1; ++j) {
-              double x = or_load(dtype, X, i * N + j);
+              double x = or_load(or_act(dtype), X, i * N + j);
               double xhat = (kind == OR_LAYERNORM) ? (x - mu[o]) * rs[o] : x * rs[o];
-              double dy = or_load(dtype, dY, i * N + j);
+              double dy = or_load(or_act(dtype), dY, i * N + j);
               aw[j - j0] += dy * xhat;
               ab[j - j0] += dy;
             }

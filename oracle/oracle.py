@@ -17,7 +17,19 @@ import numpy as np
 from . import build as _build
 
 LAYERNORM, RMSNORM = 0, 1
-F32, BF16 = 0, 1
+# storage types: every tensor fp32, every tensor bf16, or bf16 activations and gradients with
+# fp32 weight and bias
+F32, BF16, BF16_F32W = 0, 1, 2
+
+
+def act_dtype(dtype):
+    """Storage type of X, R, dY, dH for a call's dtype."""
+    return BF16 if dtype == BF16_F32W else dtype
+
+
+def weight_dtype(dtype):
+    """Storage type of W and B (and of dW, dB) for a call's dtype."""
+    return F32 if dtype == BF16_F32W else dtype
 
 
 class Oracle:
@@ -101,11 +113,11 @@ def _fwd(lib, kind, dtype, X, W, B, R, eps, rows, want_h):
     Returns a dict of float64 arrays: y (r x N), mean (r), rstd (r), and h (r x N, the
     rounded R + X) when want_h is set and R is given.
     """
-    X = _bits(X, dtype)
+    X = _bits(X, act_dtype(dtype))
     M, N = X.shape
-    W = _bits(W, dtype, (N,))
-    B = _bits(B, dtype, (N,))
-    R = _bits(R, dtype, (M, N))
+    W = _bits(W, weight_dtype(dtype), (N,))
+    B = _bits(B, weight_dtype(dtype), (N,))
+    R = _bits(R, act_dtype(dtype), (M, N))
     r0, r1 = (0, M) if rows is None else rows
     n = r1 - r0
     y = np.empty((n, N), np.float64)
@@ -126,11 +138,11 @@ def _bwd(lib, kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw):
     dx (r x N, or None), dw (N, summed over the rows given, or None) and db (N, LayerNorm
     only, or None).
     """
-    X = _bits(X, dtype)
+    X = _bits(X, act_dtype(dtype))
     M, N = X.shape
-    dY = _bits(dY, dtype, (M, N))
-    dH = _bits(dH, dtype, (M, N))
-    W = _bits(W, dtype, (N,))
+    dY = _bits(dY, act_dtype(dtype), (M, N))
+    dH = _bits(dH, act_dtype(dtype), (M, N))
+    W = _bits(W, weight_dtype(dtype), (N,))
     r0, r1 = (0, M) if rows is None else rows
     n = r1 - r0
     dx = np.empty((n, N), np.float64) if want_dx else None

@@ -22,25 +22,32 @@ MUTATIONS = [
     ("LN mean off by one", "double mu = s / (double)N;", "double mu = s / (double)(N + 1);"),
     ("bias dropped", "xhat * w + b : xhat * w;", "xhat * w : xhat * w;"),
     ("bias sign", "xhat * w + b : xhat * w;", "xhat * w - b : xhat * w;"),
-    ("weight index reversed", "double w = or_load(dtype, W, j);",
-     "double w = or_load(dtype, W, N - 1 - j);"),
+    ("weight index reversed", "double w = or_load(or_wt(dtype), W, j);",
+     "double w = or_load(or_wt(dtype), W, N - 1 - j);"),
     ("LN mean-gradient term dropped", "rs[o] * (g[j] - c1 - xh[j] * c2)", "rs[o] * (g[j] - xh[j] * c2)"),
     ("LN projection sign", "rs[o] * (g[j] - c1 - xh[j] * c2)", "rs[o] * (g[j] - c1 + xh[j] * c2)"),
     ("RMS projection dropped", ": rs[o] * (g[j] - xh[j] * c2);", ": rs[o] * g[j];"),
     ("projection without xhat", "sgx += g[j] * xh[j];", "sgx += g[j];"),
     ("gradient ignores weight",
-     "g[j] = or_load(dtype, dY, i * N + j) * or_load(dtype, W, j);",
-     "g[j] = or_load(dtype, dY, i * N + j);"),
+     "g[j] = or_load(or_act(dtype), dY, i * N + j) * or_load(or_wt(dtype), W, j);",
+     "g[j] = or_load(or_act(dtype), dY, i * N + j);"),
     ("dY column index reversed",
-     "g[j] = or_load(dtype, dY, i * N + j) * or_load(dtype, W, j);",
-     "g[j] = or_load(dtype, dY, i * N + (N - 1 - j)) * or_load(dtype, W, j);"),
+     "g[j] = or_load(or_act(dtype), dY, i * N + j) * or_load(or_wt(dtype), W, j);",
+     "g[j] = or_load(or_act(dtype), dY, i * N + (N - 1 - j)) * or_load(or_wt(dtype), W, j);"),
     ("dW uses raw input", "aw[j - j0] += dy * xhat;", "aw[j - j0] += dy * x;"),
     ("dB weighted by xhat", "ab[j - j0] += dy;", "ab[j - j0] += dy * xhat;"),
     ("dW skips first row",
      "for (int64_t i = r0; i < r1; ++i) {\n            int64_t o = i - r0;\n            for (int64_t j = j0;",
      "for (int64_t i = r0 + 1; i < r1; ++i) {\n            int64_t o = i - r0;\n            for (int64_t j = j0;"),
-    ("incoming residual gradient dropped", "if (dH) d += or_load(dtype, dH, i * N + j);",
+    ("incoming residual gradient dropped", "if (dH) d += or_load(or_act(dtype), dH, i * N + j);",
      "if (dH) d += 0.0;"),
+    ("forward weight read as the activation type", "double w = or_load(or_wt(dtype), W, j);",
+     "double w = or_load(or_act(dtype), W, j);"),
+    ("backward weight read as the activation type",
+     "g[j] = or_load(or_act(dtype), dY, i * N + j) * or_load(or_wt(dtype), W, j);",
+     "g[j] = or_load(or_act(dtype), dY, i * N + j) * or_load(or_act(dtype), W, j);"),
+    ("bias read as the activation type", "double b = B ? or_load(or_wt(dtype), B, j) : 0.0;",
+     "double b = B ? or_load(or_act(dtype), B, j) : 0.0;"),
     ("residual sum not rounded",
      "if (R) v = or_round_to_dtype(dtype, or_load(dtype, R, i * N + j) + v);",
      "if (R) v = or_load(dtype, R, i * N + j) + v;"),
