@@ -120,7 +120,7 @@ norm_status_t run_reduce(norm_dtype_t dtype, int64_t N, void *dW, void *dB, void
 }
 
 norm_status_t zero_outputs(int64_t N, norm_dtype_t dtype, void *dW, void *dB, hipStream_t s) {
-  const size_t n = (size_t)N * (dtype == NORM_F32 ? 4 : 2);
+  const size_t n = (size_t)N * (dtype == NORM_BF16 ? 2 : 4); // dW, dB in the weight type
   norm_status_t st = dln::launch_zero(dW, n, s);
   if (st == NORM_OK && dB) st = dln::launch_zero(dB, n, s);
   return st;
@@ -194,7 +194,10 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
                  workspace_bytes, &p, &a);
   if (st != NORM_OK) return st;
   // the split scheme with a single row group writes dW/dB itself, with no reduction pass
-  const bool direct = p.scheme == NORM_SCHEME_SPLIT && p.row_groups == 1;
+  // (its vector stores need dW and dB 16-byte aligned, like every other vector access)
+  const void *outs[] = {dW, dB};
+  const bool direct = p.scheme == NORM_SCHEME_SPLIT && p.row_groups == 1 &&
+                      (!p.vector || dln::all_aligned16(outs, 2));
   if (direct) {
     a.dw = dW;
     a.db = dB;

@@ -135,6 +135,65 @@ template <> struct Acc<bf16_bits, false> {
   __device__ static raw zero() { return 0; }
 };
 
+// WAcc<T, TW, VEC>: the weight (or bias) values of one access of T, stored as TW. With the same
+// storage type as the activations they stay packed; fp32 weights next to bf16 activations are
+// E fp32 values (two 16-byte loads for E = 8). get() gives fp32; store() writes E fp32 sums as
+// TW (the final dW / dB).
+template <typename T, typename TW, bool VEC> struct WAcc;
+
+template <typename T, bool VEC> struct WAcc<T, T, VEC> {
+  using A = Acc<T, VEC>;
+  static constexpr int E = A::EPV;
+  typename A::raw r;
+  __device__ void zero() { r = A::zero(); }
+  __device__ void load(const T *p) { r = A::ld_cached(p); }
+  __device__ void get(float *f) const { A::unpack(r, f); }
+  __device__ static void store(T *p, const float *f) { A::st(p, A::pack(f)); }
+};
+
+template <bool VEC> struct WAcc<bf16_bits, float, VEC> {
+  static constexpr int E = Acc<bf16_bits, VEC>::EPV;
+  float w[E];
+  __device__ void zero() {
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[e] = 0.0f;
+  }
+  __device__ void load(const float *p) {
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i) {
+        const u32x4 v = *reinterpret_cast<const u32x4 *>(p + 4 * i);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const unsigned u = v[j];
+          w[4 * i + j] = __builtin_bit_cast(float, u);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) w[e] = p[e];
+    }
+  }
+  __device__ void get(float *f) const {
+#pragma unroll
+    for (int e = 0; e < E; ++e) f[e] = w[e];
+  }
+  __device__ static void store(float *p, const float *f) {
+    if constexpr (E % 4 == 0) {
+#pragma unroll
+      for (int i = 0; i < E / 4; ++i) {
+        u32x4 v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = __builtin_bit_cast(unsigned, f[4 * i + j]);
+        *reinterpret_cast<u32x4 *>(p + 4 * i) = v;
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < E; ++e) p[e] = f[e];
+    }
+  }
+};
+
 // ---- reductions -------------------------------------------------------------------------
 
 template <int CTRL> __device__ __forceinline__ float dpp_mov(float v) {

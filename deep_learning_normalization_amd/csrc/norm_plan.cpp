@@ -29,9 +29,11 @@ constexpr int kBlockTeamTargetBwd = 640; // the backward prefers one access per 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool valid_kind(int k) { return k == NORM_LAYERNORM || k == NORM_RMSNORM; }
-bool valid_dtype(int d) { return d == NORM_F32 || d == NORM_BF16; }
+bool valid_dtype(int d) { return d == NORM_F32 || d == NORM_BF16 || d == NORM_BF16_F32W; }
 int vec_epv(norm_dtype_t d) { return d == NORM_F32 ? 4 : 8; }
+// bytes per element of the activations (X, R, Y, H, dY, dH, dX, dR) and of W, B, dW, dB
 size_t elem_size(int d) { return d == NORM_F32 ? 4 : 2; }
+size_t weight_size(int d) { return d == NORM_BF16 ? 2 : 4; }
 int lb_of(int threads) { return threads <= 256 ? 256 : threads <= 512 ? 512 : 1024; }
 
 // Compiled kernel shapes (must match the menus in the kernel sources).
@@ -366,7 +368,8 @@ norm_status_t check_fwd(const FwdCheck &c) {
   if (c.M == 0) return NORM_OK;
   if (!c.X || !c.Y) return NORM_ERR_INVALID_ARG;
   const size_t s = elem_size(c.dtype);
-  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * s, m = (size_t)c.M * 4;
+  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * weight_size(c.dtype),
+               m = (size_t)c.M * 4;
   const Span in[] = {{c.X, mn}, {c.R, mn}, {c.W, n}, {c.B, n}};
   const Span outs[] = {{c.Y, mn}, {c.H, mn}, {c.mean, m}, {c.rstd, m}, {c.ws, c.ws_bytes}};
   if (!disjoint(in, 4, outs, 5)) return NORM_ERR_INVALID_ARG;
@@ -390,7 +393,8 @@ norm_status_t check_bwd(const BwdCheck &c) {
   if (c.M == 0) return NORM_OK;
   if (c.need_dx && (!c.X || !c.dY || !c.dX)) return NORM_ERR_INVALID_ARG;
   const size_t s = elem_size(c.dtype);
-  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * s, m = (size_t)c.M * 4;
+  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * weight_size(c.dtype),
+               m = (size_t)c.M * 4;
   const void *dr = c.dR == c.dX ? nullptr : c.dR; // dR may alias dX
   const Span in[] = {{c.X, mn}, {c.dY, mn}, {c.dH, mn}, {c.W, n}, {c.mean, m}, {c.rstd, m}};
   const Span outs[] = {{c.dX, mn}, {dr, mn}, {c.dW, n}, {c.dB, n}, {c.ws, c.ws_bytes}};

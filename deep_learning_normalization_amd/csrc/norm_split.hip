@@ -178,7 +178,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
 
 // ---- forward pass 2: combine, normalise the chunk ---------------------------------------
 
-template <typename T, bool VEC, int VPT>
+template <typename T, typename TW, bool VEC, int VPT>
 __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
@@ -195,21 +195,22 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
   const int64_t base = row * (int64_t)a.N + acc0 * E;
   // the norm's input: the stored h for the residual variant, else X
   const T *__restrict__ S = static_cast<const T *>(a.r ? a.h : a.x) + base;
-  const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
-  const T *__restrict__ Bb = a.b ? static_cast<const T *>(a.b) + acc0 * E : nullptr;
+  const TW *__restrict__ W = static_cast<const TW *>(a.w) + acc0 * E;
+  const TW *__restrict__ Bb = a.b ? static_cast<const TW *>(a.b) + acc0 * E : nullptr;
   T *__restrict__ Y = static_cast<T *>(a.y) + base;
 
-  raw rx[VPT], rw[VPT], rb[VPT];
+  raw rx[VPT];
+  WAcc<T, TW, VEC> rw[VPT], rb[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
     rx[k] = A::zero();
-    rw[k] = A::zero();
-    rb[k] = A::zero();
+    rw[k].zero();
+    rb[k].zero();
     if (v < nin) {
       rx[k] = A::ld_cached(S + (int64_t)v * E);
-      rw[k] = A::ld_cached(W + (int64_t)v * E);
-      if (Bb) rb[k] = A::ld_cached(Bb + (int64_t)v * E);
+      rw[k].load(W + (int64_t)v * E);
+      if (Bb) rb[k].load(Bb + (int64_t)v * E);
     }
   }
   int slot = 0;
@@ -222,8 +223,8 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
     if (v < nin) {
       float xf[E], wf[E], bf[E], y[E];
       A::unpack(rx[k], xf);
-      A::unpack(rw[k], wf);
-      A::unpack(rb[k], bf);
+      rw[k].get(wf);
+      rb[k].get(bf);
 #pragma unroll
       for (int e = 0; e < E; ++e) y[e] = ((xf[e] - shift) - delta) * rstd * wf[e] + bf[e];
       A::st(Y + (int64_t)v * E, A::pack(y));
@@ -254,7 +255,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_finalize_stats_kernel(BwdArgs 
 
 // One workgroup per (row, chunk), like the forward's statistics pass: the whole grid streams X
 // and dY once, with no loop-carried latency.
-template <typename T, bool VEC, int VPT, bool LN>
+template <typename T, typename TW, bool VEC, int VPT, bool LN>
 __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
@@ -270,20 +271,21 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
   const int64_t base = row * (int64_t)a.N + acc0 * E;
   const T *__restrict__ X = static_cast<const T *>(a.x) + base;
   const T *__restrict__ DY = static_cast<const T *>(a.dy) + base;
-  const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
+  const TW *__restrict__ W = static_cast<const TW *>(a.w) + acc0 * E;
   const float *mean_p = a.rstd ? a.mean : a.stats;
 
-  raw rx[VPT], rdy[VPT], rw[VPT];
+  raw rx[VPT], rdy[VPT];
+  WAcc<T, TW, VEC> rw[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
     rx[k] = A::zero();
     rdy[k] = A::zero();
-    rw[k] = A::zero();
+    rw[k].zero();
     if (v < nin) {
       rx[k] = A::ld(X + (int64_t)v * E);
       rdy[k] = A::ld(DY + (int64_t)v * E);
-      rw[k] = A::ld_cached(W + (int64_t)v * E);
+      rw[k].load(W + (int64_t)v * E);
     }
   }
   const float m = (LN && mean_p) ? mean_p[row] : 0.0f;
@@ -297,7 +299,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
     float xf[E], df[E], wf[E];
     A::unpack(rx[k], xf);
     A::unpack(rdy[k], df);
-    A::unpack(rw[k], wf);
+    rw[k].get(wf);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const float d = in ? xf[e] - m : 0.0f;
@@ -326,7 +328,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
 // One workgroup per (row group, chunk). Rows are visited in descending order (the last rows
 // pass 1 read come back first) and the next row group's X and dY are requested before the
 // current one is combined and written.
-template <typename T, bool VEC, int VPT, int ROWS, bool LN>
+template <typename T, typename TW, bool VEC, int VPT, int ROWS, bool LN>
 __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
@@ -345,7 +347,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   const T *__restrict__ X = static_cast<const T *>(a.x) + acc0 * E;
   const T *__restrict__ DY = static_cast<const T *>(a.dy) + acc0 * E;
   const T *__restrict__ DH = a.dh ? static_cast<const T *>(a.dh) + acc0 * E : nullptr;
-  const T *__restrict__ W = static_cast<const T *>(a.w) + acc0 * E;
+  const TW *__restrict__ W = static_cast<const TW *>(a.w) + acc0 * E;
   T *__restrict__ DX = static_cast<T *>(a.dx) + acc0 * E;
   T *__restrict__ DR = a.dr ? static_cast<T *>(a.dr) + acc0 * E : nullptr;
   const float *mean_p = a.rstd ? a.mean : a.stats;
@@ -353,13 +355,13 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   if (!a.dw) write_ws_header(a.header, a.row_groups, N);
 
   // the weight stays packed (half the registers for bf16), unpacked at use
-  raw rw[VPT];
+  WAcc<T, TW, VEC> rw[VPT];
   float accw[VPT][E], accb[LN ? VPT : 1][E];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
-    rw[k] = A::zero();
-    if (v < nin) rw[k] = A::ld_cached(W + (int64_t)v * E);
+    rw[k].zero();
+    if (v < nin) rw[k].load(W + (int64_t)v * E);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       accw[k][e] = 0.0f;
@@ -457,7 +459,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
         float xf[E], df[E], wf[E], dx[E];
         A::unpack(rx[r][k], xf);
         A::unpack(rdy[r][k], df);
-        A::unpack(rw[k], wf);
+        rw[k].get(wf);
 #pragma unroll
         for (int e = 0; e < E; ++e) {
           const float xh = in ? ((xf[e] - m) - delta) * rstd : 0.0f;
@@ -483,15 +485,15 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   // column partials of this (row group, chunk), or the final dW/dB when the caller asked for
   // them directly (only ever with a single row group)
   if (a.dw) {
-    T *dw = static_cast<T *>(a.dw) + acc0 * E;
-    T *db = a.db ? static_cast<T *>(a.db) + acc0 * E : nullptr;
+    TW *dw = static_cast<TW *>(a.dw) + acc0 * E;
+    TW *db = a.db ? static_cast<TW *>(a.db) + acc0 * E : nullptr;
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       const int v = tid + k * SPLIT_LB;
       if (v < nin) {
-        A::st(dw + (int64_t)v * E, A::pack(accw[k]));
+        WAcc<T, TW, VEC>::store(dw + (int64_t)v * E, accw[k]);
         if constexpr (LN)
-          if (db) A::st(db + (int64_t)v * E, A::pack(accb[k]));
+          if (db) WAcc<T, TW, VEC>::store(db + (int64_t)v * E, accb[k]);
       }
     }
   } else {
@@ -519,7 +521,8 @@ namespace {
 #define DLN_SPLIT_BWD_MENU(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2)
 #define DLN_SPLIT_SCALAR_VPT 8
 
-template <typename T> norm_status_t split_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
+template <typename T, typename TW>
+norm_status_t split_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
   const bool resid = a.r != nullptr;
   bool found = false;
@@ -531,7 +534,7 @@ template <typename T> norm_status_t split_fwd_typed(const Plan &p, const FwdArgs
     found = true;                                                                               \
     keep(resid ? launch(split_stats_kernel<T, true, V, true>, grid, block, s, a)                \
                : launch(split_stats_kernel<T, true, V, false>, grid, block, s, a));             \
-    keep(launch(split_norm_kernel<T, true, V>, grid, block, s, a));                             \
+    keep(launch(split_norm_kernel<T, TW, true, V>, grid, block, s, a));                         \
   }
     DLN_SPLIT_FWD_MENU(X)
 #undef X
@@ -540,27 +543,30 @@ template <typename T> norm_status_t split_fwd_typed(const Plan &p, const FwdArgs
     constexpr int V = DLN_SPLIT_SCALAR_VPT;
     keep(resid ? launch(split_stats_kernel<T, false, V, true>, grid, block, s, a)
                : launch(split_stats_kernel<T, false, V, false>, grid, block, s, a));
-    keep(launch(split_norm_kernel<T, false, V>, grid, block, s, a));
+    keep(launch(split_norm_kernel<T, TW, false, V>, grid, block, s, a));
   }
   if (!found) return NORM_ERR_UNSUPPORTED;
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
-template <typename T, bool VEC, int V, int R>
+template <typename T, typename TW, bool VEC, int V, int R>
 hipError_t split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
   const dim3 grid1((unsigned)(a.M * a.chunks)), grid2((unsigned)p.grid), block(SPLIT_LB);
   hipError_t e;
   if (a.layernorm) {
-    e = launch(split_bwd_partial_kernel<T, VEC, V, true>, grid1, block, s, a);
-    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, true>, grid2, block, s, a);
+    e = launch(split_bwd_partial_kernel<T, TW, VEC, V, true>, grid1, block, s, a);
+    if (e == hipSuccess)
+      e = launch(split_bwd_dx_kernel<T, TW, VEC, V, R, true>, grid2, block, s, a);
   } else {
-    e = launch(split_bwd_partial_kernel<T, VEC, V, false>, grid1, block, s, a);
-    if (e == hipSuccess) e = launch(split_bwd_dx_kernel<T, VEC, V, R, false>, grid2, block, s, a);
+    e = launch(split_bwd_partial_kernel<T, TW, VEC, V, false>, grid1, block, s, a);
+    if (e == hipSuccess)
+      e = launch(split_bwd_dx_kernel<T, TW, VEC, V, R, false>, grid2, block, s, a);
   }
   return e;
 }
 
-template <typename T> norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
+template <typename T, typename TW>
+norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   // statistics of the forward, when not supplied: chunk stats, then one combine per row
   if (a.rstd == nullptr) {
     FwdArgs f{};
@@ -600,13 +606,13 @@ template <typename T> norm_status_t split_bwd_typed(const Plan &p, const BwdArgs
 #define X(V, R)                                                                                 \
   if (!found && p.vpt == V && p.rows == R) {                                                    \
     found = true;                                                                               \
-    e = split_bwd_pair<T, true, V, R>(p, a, s);                                                 \
+    e = split_bwd_pair<T, TW, true, V, R>(p, a, s);                                             \
   }
     DLN_SPLIT_BWD_MENU(X)
 #undef X
   } else if (p.vpt == DLN_SPLIT_SCALAR_VPT && p.rows == 1) {
     found = true;
-    e = split_bwd_pair<T, false, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
+    e = split_bwd_pair<T, TW, false, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
   }
   if (!found) return NORM_ERR_UNSUPPORTED;
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
@@ -616,12 +622,22 @@ template <typename T> norm_status_t split_bwd_typed(const Plan &p, const BwdArgs
 
 norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                                hipStream_t s) {
-  return dtype == NORM_F32 ? split_fwd_typed<float>(p, a, s) : split_fwd_typed<bf16_bits>(p, a, s);
+  switch (dtype) {
+  case NORM_F32: return split_fwd_typed<float, float>(p, a, s);
+  case NORM_BF16: return split_fwd_typed<bf16_bits, bf16_bits>(p, a, s);
+  case NORM_BF16_F32W: return split_fwd_typed<bf16_bits, float>(p, a, s);
+  default: return NORM_ERR_UNSUPPORTED;
+  }
 }
 
 norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                                hipStream_t s) {
-  return dtype == NORM_F32 ? split_bwd_typed<float>(p, a, s) : split_bwd_typed<bf16_bits>(p, a, s);
+  switch (dtype) {
+  case NORM_F32: return split_bwd_typed<float, float>(p, a, s);
+  case NORM_BF16: return split_bwd_typed<bf16_bits, bf16_bits>(p, a, s);
+  case NORM_BF16_F32W: return split_bwd_typed<bf16_bits, float>(p, a, s);
+  default: return NORM_ERR_UNSUPPORTED;
+  }
 }
 
 } // namespace dln

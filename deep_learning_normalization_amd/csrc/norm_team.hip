@@ -71,7 +71,7 @@ __device__ __forceinline__ GroupRange group_range(int64_t M, int64_t rows_per_gr
 
 // ---- forward ------------------------------------------------------------------------------
 
-template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool RESID>
+template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool RESID>
 __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_threads) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
@@ -83,8 +83,8 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   const int64_t N = a.N;
   const T *__restrict__ X = static_cast<const T *>(a.x);
   const T *__restrict__ Rr = static_cast<const T *>(a.r);
-  const T *__restrict__ W = static_cast<const T *>(a.w);
-  const T *__restrict__ Bb = static_cast<const T *>(a.b);
+  const TW *__restrict__ W = static_cast<const TW *>(a.w);
+  const TW *__restrict__ Bb = static_cast<const TW *>(a.b);
   T *__restrict__ Y = static_cast<T *>(a.y);
   T *__restrict__ H = static_cast<T *>(a.h);
 
@@ -92,13 +92,15 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = gm.t + k * gm.tt;
-    raw rw = A::zero(), rb = A::zero();
+    WAcc<T, TW, VEC> rw, rb;
+    rw.zero();
+    rb.zero();
     if (v < nacc) {
-      rw = A::ld_cached(W + (int64_t)v * E);
-      if (Bb) rb = A::ld_cached(Bb + (int64_t)v * E);
+      rw.load(W + (int64_t)v * E);
+      if (Bb) rb.load(Bb + (int64_t)v * E);
     }
-    A::unpack(rw, w[k]);
-    A::unpack(rb, b[k]);
+    rw.get(w[k]);
+    rb.get(b[k]);
   }
 
   const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 // B = -rstd * c2, C = -rstd * c1: xhat = d * a + nd, dX = g * a + (xhat * B + C), and the
 // dW / dB column sums. d, g and dY stay in registers across the team sum when the thread holds
 // at most 16 elements of the row group (else they are formed again from the packed data).
-template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool LN>
+template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool LN>
 __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_threads) {
   using A = Acc<T, VEC>;
   using raw = typename A::raw;
@@ -276,20 +278,20 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   const T *__restrict__ X = static_cast<const T *>(a.x);
   const T *__restrict__ DY = static_cast<const T *>(a.dy);
   const T *__restrict__ DH = static_cast<const T *>(a.dh);
-  const T *__restrict__ W = static_cast<const T *>(a.w);
+  const TW *__restrict__ W = static_cast<const TW *>(a.w);
   T *__restrict__ DX = static_cast<T *>(a.dx);
   T *__restrict__ DR = static_cast<T *>(a.dr);
   const bool have_stats = a.rstd != nullptr;
   write_ws_header(a.header, a.partials, N);
 
   // the weight stays in its storage format (half the registers for bf16), unpacked at use
-  raw rw[VPT];
+  WAcc<T, TW, VEC> rw[VPT];
   float accw[VPT][E], accb[LN ? VPT : 1][E];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = gm.t + k * gm.tt;
-    rw[k] = A::zero();
-    if (v < nacc) rw[k] = A::ld_cached(W + (int64_t)v * E);
+    rw[k].zero();
+    if (v < nacc) rw[k].load(W + (int64_t)v * E);
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       accw[k][e] = 0.0f;
@@ -432,7 +434,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       float wf[E];
-      A::unpack(rw[k], wf);
+      rw[k].get(wf);
       const bool in = gm.t + k * gm.tt < nacc;
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           float xf[E], wf[E];
           A::unpack(rx[r][k], xf);
           A::unpack(rdy[r][k], df);
-          A::unpack(rw[k], wf);
+          rw[k].get(wf);
 #pragma unroll
           for (int e = 0; e < E; ++e) {
             d[e] = LN ? xf[e] - m[r] : xf[e];
@@ -717,23 +719,23 @@ __global__ __launch_bounds__(256) void zero_kernel(unsigned char *p, size_t n) {
 
 namespace {
 
-template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
+template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
 hipError_t fwd_launch(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s) {
   dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
   if (resid)
-    return launch(team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
+    return launch(team_fwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
                   p.team_threads);
-  return launch(team_fwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
+  return launch(team_fwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
                 p.team_threads);
 }
 
-template <typename T, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
+template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
 hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
   if (a.layernorm)
-    return launch(team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
+    return launch(team_bwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
                   p.team_threads);
-  return launch(team_bwd_kernel<T, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
+  return launch(team_bwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
                 p.team_threads);
 }
 
@@ -749,7 +751,8 @@ hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
           X(1, 1, 1024) X(1, 2, 1024) X(2, 1, 1024)
 #define DLN_BLOCK_MENU_SCALAR(X) X(4, 1, 1024) X(8, 1, 1024)
 
-template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
+template <typename T, typename TW>
+norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
   const bool resid = a.r != nullptr;
   const int lb = p.lb;
   hipError_t e = hipErrorInvalidConfiguration;
@@ -759,7 +762,7 @@ template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, true, V, R, L, true>(p, a, resid, s);                                     \
+    e = fwd_launch<T, TW, true, V, R, L, true>(p, a, resid, s);                                 \
   }
       DLN_WAVE_MENU(X)
 #undef X
@@ -767,7 +770,7 @@ template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, false, V, R, L, true>(p, a, resid, s);                                    \
+    e = fwd_launch<T, TW, false, V, R, L, true>(p, a, resid, s);                                \
   }
       DLN_WAVE_MENU_SCALAR(X)
 #undef X
@@ -777,7 +780,7 @@ template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, true, V, R, L, false>(p, a, resid, s);                                    \
+    e = fwd_launch<T, TW, true, V, R, L, false>(p, a, resid, s);                                \
   }
       DLN_BLOCK_MENU(X)
 #undef X
@@ -785,7 +788,7 @@ template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, false, V, R, L, false>(p, a, resid, s);                                   \
+    e = fwd_launch<T, TW, false, V, R, L, false>(p, a, resid, s);                               \
   }
       DLN_BLOCK_MENU_SCALAR(X)
 #undef X
@@ -795,7 +798,8 @@ template <typename T> norm_status_t team_fwd_typed(const Plan &p, const FwdArgs 
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
-template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
+template <typename T, typename TW>
+norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   const int lb = p.lb;
   hipError_t e = hipErrorInvalidConfiguration;
   bool found = false;
@@ -804,7 +808,7 @@ template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, true, V, R, L, true>(p, a, s);                                            \
+    e = bwd_launch<T, TW, true, V, R, L, true>(p, a, s);                                        \
   }
       DLN_WAVE_MENU(X)
 #undef X
@@ -812,7 +816,7 @@ template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, false, V, R, L, true>(p, a, s);                                           \
+    e = bwd_launch<T, TW, false, V, R, L, true>(p, a, s);                                       \
   }
       DLN_WAVE_MENU_SCALAR(X)
 #undef X
@@ -822,7 +826,7 @@ template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, true, V, R, L, false>(p, a, s);                                           \
+    e = bwd_launch<T, TW, true, V, R, L, false>(p, a, s);                                       \
   }
       DLN_BLOCK_MENU(X)
 #undef X
@@ -830,7 +834,7 @@ template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs 
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, false, V, R, L, false>(p, a, s);                                          \
+    e = bwd_launch<T, TW, false, V, R, L, false>(p, a, s);                                      \
   }
       DLN_BLOCK_MENU_SCALAR(X)
 #undef X
@@ -844,12 +848,22 @@ template <typename T> norm_status_t team_bwd_typed(const Plan &p, const BwdArgs 
 
 norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                               hipStream_t s) {
-  return dtype == NORM_F32 ? team_fwd_typed<float>(p, a, s) : team_fwd_typed<bf16_bits>(p, a, s);
+  switch (dtype) {
+  case NORM_F32: return team_fwd_typed<float, float>(p, a, s);
+  case NORM_BF16: return team_fwd_typed<bf16_bits, bf16_bits>(p, a, s);
+  case NORM_BF16_F32W: return team_fwd_typed<bf16_bits, float>(p, a, s);
+  default: return NORM_ERR_UNSUPPORTED;
+  }
 }
 
 norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                               hipStream_t s) {
-  return dtype == NORM_F32 ? team_bwd_typed<float>(p, a, s) : team_bwd_typed<bf16_bits>(p, a, s);
+  switch (dtype) {
+  case NORM_F32: return team_bwd_typed<float, float>(p, a, s);
+  case NORM_BF16: return team_bwd_typed<bf16_bits, bf16_bits>(p, a, s);
+  case NORM_BF16_F32W: return team_bwd_typed<bf16_bits, float>(p, a, s);
+  default: return NORM_ERR_UNSUPPORTED;
+  }
 }
 
 norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s) {
@@ -869,13 +883,13 @@ norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t
   if (a.N % 4 == 0) {
     const int64_t tiles = (a.N + 31) / 32;
     const dim3 grid((unsigned)(tiles < kReduceGrid ? tiles : kReduceGrid), q), block(256);
-    e = dtype == NORM_F32 ? launch(colsum4_kernel<float>, grid, block, s, a)
-                          : launch(colsum4_kernel<bf16_bits>, grid, block, s, a);
+    e = dtype == NORM_BF16 ? launch(colsum4_kernel<bf16_bits>, grid, block, s, a)
+                           : launch(colsum4_kernel<float>, grid, block, s, a);
   } else {
     const int64_t tiles = (a.N + 63) / 64;
     const dim3 grid((unsigned)(tiles < kReduceGrid ? tiles : kReduceGrid), q), block(256);
-    e = dtype == NORM_F32 ? launch(colsum_kernel<float>, grid, block, s, a)
-                          : launch(colsum_kernel<bf16_bits>, grid, block, s, a);
+    e = dtype == NORM_BF16 ? launch(colsum_kernel<bf16_bits>, grid, block, s, a)
+                           : launch(colsum_kernel<float>, grid, block, s, a);
   }
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }

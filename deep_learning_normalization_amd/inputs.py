@@ -59,6 +59,7 @@ class Workload:
     dy: Optional[Dist] = normal(0.0, 1.0)  # None: forward only
     r: Optional[Dist] = None          # residual input R (residual variant)
     dh: Optional[Dist] = None         # incoming gradient of the residual output
+    wdtype: Optional[str] = None      # storage of W, B (and dW, dB); None: the same as dtype
     outlier_frac: float = 0.0         # fraction of columns scaled by outlier_scale
     outlier_scale: float = 20.0
     seed: int = 0
@@ -103,6 +104,7 @@ def make(w: Workload, M: Optional[int] = None) -> dict:
     M = w.M if M is None else M
     N = w.N
     dt = TORCH_DTYPES[w.dtype]
+    wdt = TORCH_DTYPES[w.wdtype or w.dtype]
     s = w.seed
     X = _draw(w.x, (M, N), s + OFF_X)
     if w.outlier_frac > 0.0:
@@ -110,8 +112,8 @@ def make(w: Workload, M: Optional[int] = None) -> dict:
         X[:, cols] *= w.outlier_scale
     out = {
         "X": X.to(dt),
-        "W": _draw(w.w, (N,), s + OFF_W).to(dt),
-        "B": _draw(w.b, (N,), s + OFF_B).to(dt) if w.b is not None else None,
+        "W": _draw(w.w, (N,), s + OFF_W).to(wdt),
+        "B": _draw(w.b, (N,), s + OFF_B).to(wdt) if w.b is not None else None,
         "dY": _draw(w.dy, (M, N), s + OFF_DY).to(dt) if w.dy is not None else None,
         "R": _draw(w.r, (M, N), s + OFF_R).to(dt) if w.r is not None else None,
         "dH": _draw(w.dh, (M, N), s + OFF_DH).to(dt) if w.dh is not None else None,

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnorm.so")
 
 LAYERNORM, RMSNORM = 0, 1
-F32, BF16 = 0, 1
+F32, BF16, BF16_F32W = 0, 1, 2
 PASS_FWD, PASS_BWD = 0, 1
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT = -1, 0, 1, 2
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
@@ -25,6 +25,17 @@ OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 KINDS = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM}
 DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+
+
+def dtype_code(act, weight=None):
+    """norm_dtype_t for activations of torch dtype `act` and weights of `weight` (default: the
+    same): fp32/fp32, bf16/bf16, or bf16 activations with fp32 weights."""
+    weight = act if weight is None else weight
+    if act == weight:
+        return DTYPES[act]
+    if act == torch.bfloat16 and weight == torch.float32:
+        return BF16_F32W
+    raise ValueError("unsupported dtype pair: activations %s, weights %s" % (act, weight))
 
 SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_workspace_size",
            "norm_plan", "norm_set_tuning", "norm_set_launch_events", "norm_status_string",
@@ -138,16 +149,16 @@ def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=N
              stream=None):
     """Queue the forward. X, R, Y, H are [M, N]; W, B are [N]; mean, rstd are [M] fp32."""
     M, N = X.shape
-    dt = X.dtype
+    dt, wdt = X.dtype, W.dtype
     for t, nm in ((X, "X"), (R, "R"), (Y, "Y"), (H, "H")):
         _check_mat(t, M, N, dt, nm)
-    _check_vec(W, N, dt, "W")
-    _check_vec(B, N, dt, "B")
+    _check_vec(W, N, wdt, "W")
+    _check_vec(B, N, wdt, "B")
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
     st = lib().norm_fwd(_kind(kind), _ptr(X), _ptr(R), _ptr(W), _ptr(B), float(eps), M, N,
-                        DTYPES[dt], _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
+                        dtype_code(dt, wdt), _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
                         _stream(stream))
     _raise(st, "norm_fwd")
 
@@ -155,38 +166,39 @@ def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=N
 def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, stream=None):
     """Queue the backward (fused pass, then the column reduction)."""
     M, N = X.shape
-    dt = X.dtype
+    dt, wdt = X.dtype, W.dtype
     for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
         _check_mat(t, M, N, dt, nm)
     for t, nm in ((W, "W"), (dW, "dW"), (dB, "dB")):
-        _check_vec(t, N, dt, nm)
+        _check_vec(t, N, wdt, nm)
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
     st = lib().norm_bwd(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
-                        _ptr(rstd), float(eps), M, N, DTYPES[dt], _ptr(dX), _ptr(dR), _ptr(dW),
-                        _ptr(dB), wp, wb, _stream(stream))
+                        _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX), _ptr(dR),
+                        _ptr(dW), _ptr(dB), wp, wb, _stream(stream))
     _raise(st, "norm_bwd")
 
 
 def norm_bwd_fused(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, workspace, stream=None):
     """Queue the backward's fused pass: dX (and dR), column partials into the workspace."""
     M, N = X.shape
-    dt = X.dtype
+    dt, wdt = X.dtype, W.dtype
     for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
         _check_mat(t, M, N, dt, nm)
-    _check_vec(W, N, dt, "W")
+    _check_vec(W, N, wdt, "W")
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
     st = lib().norm_bwd_fused(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
-                              _ptr(rstd), float(eps), M, N, DTYPES[dt], _ptr(dX), _ptr(dR), wp,
-                              wb, _stream(stream))
+                              _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX),
+                              _ptr(dR), wp, wb, _stream(stream))
     _raise(st, "norm_bwd_fused")
 
 
 def norm_bwd_reduce(kind, M, N, dW, dB, workspace, stream=None):
-    """Queue the column reduction of the partials a fused pass left in the workspace."""
+    """Queue the column reduction of the partials a fused pass left in the workspace (the
+    outputs' dtype selects the store type: fp32 dW, dB for F32 and BF16_F32W)."""
     dt = dW.dtype
     _check_vec(dW, N, dt, "dW")
     _check_vec(dB, N, dt, "dB")
@@ -199,7 +211,7 @@ def norm_bwd_reduce(kind, M, N, dW, dB, workspace, stream=None):
 def norm_workspace_size(kind, dtype, pass_, M, N, residual=False):
     """Workspace bytes for a call on the current device."""
     out = ctypes.c_size_t(0)
-    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
+    dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)  # int: norm_dtype_t
     st = lib().norm_workspace_size(_kind(kind), dt, int(pass_), M, N, int(bool(residual)),
                                    ctypes.byref(out))
     _raise(st, "norm_workspace_size")

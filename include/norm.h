@@ -28,8 +28,9 @@
  *   - All tensor pointers are DEVICE pointers on the current HIP device. X, R, Y, H, dY, dH,
  *     dX, dR are row-major contiguous [M, N] (row stride N); W, B, dW, dB are [N]; mean and
  *     rstd are [M] fp32 whatever the dtype; the workspace is raw device memory.
- *   - dtype is the storage type of every non-statistic tensor; arithmetic is fp32, and each
- *     output is rounded once (round to nearest even).
+ *   - dtype gives the storage types of the non-statistic tensors (norm_dtype_t: one type for
+ *     all, or bf16 activations with fp32 W, B, dW, dB); arithmetic is fp32, and each output
+ *     is rounded once (round to nearest even).
  *   - The caller owns all memory. The library allocates nothing and keeps no state beyond a
  *     per-device cache of the compute-unit count and the tuning overrides below.
  *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL = the null stream).
@@ -56,7 +57,14 @@ extern "C" {
 
 typedef enum { NORM_LAYERNORM = 0, NORM_RMSNORM = 1 } norm_kind_t;
 
-typedef enum { NORM_F32 = 0, NORM_BF16 = 1 } norm_dtype_t;
+/*
+ * Storage types. NORM_F32 and NORM_BF16: every tensor in that type. NORM_BF16_F32W: X, R, Y,
+ * H, dY, dH, dX, dR in bf16 and W, B, dW, dB in fp32, the mixed-precision layout in which the
+ * parameters keep fp32 master copies ([P2] "Otimização de Performance de GPU: Maximizando
+ * Throughput para Treinamento e Inferência de LLM", section on mixed-precision training).
+ * mean and rstd are fp32 always; all arithmetic is fp32.
+ */
+typedef enum { NORM_F32 = 0, NORM_BF16 = 1, NORM_BF16_F32W = 2 } norm_dtype_t;
 
 typedef enum {
   NORM_OK = 0,

@@ -29,6 +29,14 @@ KIND = {"layernorm": oracle.LAYERNORM, "rmsnorm": oracle.RMSNORM}
 DT = {"f32": oracle.F32, "bf16": oracle.BF16}
 
 
+def oracle_dtype(w):
+    """The oracle's storage code for a workload: one type, or bf16 with fp32 weights."""
+    if w.wdtype and w.wdtype != w.dtype:
+        assert (w.dtype, w.wdtype) == ("bf16", "f32"), (w.dtype, w.wdtype)
+        return oracle.BF16_F32W
+    return DT[w.dtype]
+
+
 def rms(a):
     a = np.asarray(a, np.float64)
     return float(np.sqrt(np.mean(a * a))) if a.size else 0.0
@@ -151,7 +159,7 @@ def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stat
     M = t["X"].shape[0]
     N = w.N
     kind = KIND[w.kind]
-    dtc = DT[w.dtype]
+    dtc = oracle_dtype(w)
     eps = float(np.float32(w.eps))
     X, W, B, R = (_to_dev(t[k], dev) for k in ("X", "W", "B", "R"))
     Y, H, mean, rstd = nl.forward(w.kind, X, W, B, w.eps, R=R, stream=stream)
@@ -220,9 +228,9 @@ def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stat
     if M:
         fl = dx_floor(torch.as_tensor(rows), t["dY"], t["W"], cat["rstd"], N)
         check_values("dX", take(dX), np.concatenate(dx_ref), w.dtype, floor=fl)
-    check_colsums("dW", dW.double().cpu().numpy(), g_full["dw"], w.dtype)
+    check_colsums("dW", dW.double().cpu().numpy(), g_full["dw"], w.wdtype or w.dtype)
     if dB is not None:
-        check_colsums("dB", dB.double().cpu().numpy(), g_full["db"], w.dtype)
+        check_colsums("dB", dB.double().cpu().numpy(), g_full["db"], w.wdtype or w.dtype)
     if dr == "separate" and M:
         assert torch.equal(dR.view(torch.int16) if dR.dtype == torch.bfloat16 else dR,
                            dX.view(torch.int16) if dX.dtype == torch.bfloat16 else dX)

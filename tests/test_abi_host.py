@@ -84,7 +84,7 @@ def _bwd(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(kind=2), dict(kind=-1), dict(dtype=2), dict(M=-1), dict(N=0), dict(N=-5),
+    dict(kind=2), dict(kind=-1), dict(dtype=3), dict(M=-1), dict(N=0), dict(N=-5),
     dict(N=1 << 31), dict(eps=-1e-5), dict(eps=float("nan")), dict(eps=float("inf")),
     dict(X=None), dict(W=None), dict(Y=None),
     dict(kind=1, B=FAKE * 9), dict(kind=1, mean=FAKE * 9),
@@ -224,3 +224,22 @@ def test_launch_events_arm_and_disarm():
     assert lib.norm_set_launch_events(FAKE, FAKE * 2) == nl.OK
     assert _fwd(kind=9) == nl.ERR_INVALID_ARG
     assert lib.norm_set_launch_events(None, None) == nl.OK
+
+
+def test_mixed_weight_dtype_on_the_host():
+    # bf16 activations with fp32 weights plan like bf16 and size spans with 4-byte weights
+    for pass_ in (0, 1):
+        a = nl.norm_plan(0, nl.BF16_F32W, pass_, 4096, 4096)
+        b = nl.norm_plan(0, BF, pass_, 4096, 4096)
+        assert a == b
+    assert nl.lib().norm_set_tuning(nl.TUNE_SCHEME, -1) == nl.OK
+    with pytest.raises(nl.NormError):
+        nl.norm_plan(0, 3, 0, 16, 16)                      # no such dtype
+    # W holds N fp32 values: an output placed inside them overlaps
+    assert _fwd(dtype=2, W=FAKE * 2, Y=FAKE * 2 + 16) == nl.ERR_INVALID_ARG
+    assert _fwd(dtype=2, W=FAKE * 2, mean=FAKE * 2 + 16, M=4, N=8) == nl.ERR_INVALID_ARG
+    # with bf16 weights the same output starts after W's 16 bytes: accepted (then no device)
+    assert _fwd(dtype=1, W=FAKE * 2, mean=FAKE * 2 + 16, M=4, N=8) == nl.ERR_HIP
+    assert nl.dtype_code(torch.bfloat16, torch.float32) == nl.BF16_F32W
+    with pytest.raises(ValueError):
+        nl.dtype_code(torch.float32, torch.bfloat16)

@@ -95,6 +95,81 @@ def test_forced_scheme(name, scheme, Ns, dt, kind):
                 run_and_check(_small(kind, dt, M, N, seed=3 * M + N + 1), stats=False)
 
 
+# ---- bf16 activations with fp32 weight, bias, dW, dB --------------------------------------------
+
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("N", [8, 512, 1000, 4096, 5120, 20000, 300000])
+def test_mixed_weight_type(kind, N):
+    Ms = (1, 5, 300) if N <= 20000 else (1, 3)
+    for M in Ms:
+        _say("mixed weights %s %dx%d" % (kind, M, N))
+        w = dataclasses.replace(_small(kind, "bf16", M, N, seed=M + N), wdtype="f32")
+        run_and_check(w)
+        run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
+
+
+@pytest.mark.parametrize("name,scheme,N", [("wave", nl.SCHEME_WAVE, 1024),
+                                           ("block", nl.SCHEME_BLOCK, 4104),
+                                           ("split", nl.SCHEME_SPLIT, 20000)],
+                         ids=["wave", "block", "split"])
+def test_mixed_weight_type_forced_schemes(name, scheme, N):
+    for kind in ("layernorm", "rmsnorm"):
+        _say("mixed weights forced %s %s N=%d" % (name, kind, N))
+        with tuned(scheme=scheme):
+            w = dataclasses.replace(_small(kind, "bf16", 77, N, seed=N), wdtype="f32")
+            run_and_check(w)
+
+
+@pytest.mark.parametrize("dr", ["alias", "separate"])
+def test_mixed_weight_type_residual(dr):
+    for N in (1024, 7168, 40000):
+        _say("mixed weights residual dr=%s N=%d" % (dr, N))
+        w = dataclasses.replace(_small("rmsnorm", "bf16", 33, N, seed=N, r=inputs.normal(0, 1)),
+                                wdtype="f32")
+        run_and_check(w, dr=dr, dh=True)
+
+
+def test_mixed_weight_type_unaligned():
+    # N % 8 != 0: the element-wise path with fp32 weights
+    for kind in ("layernorm", "rmsnorm"):
+        for N in (100, 4100):
+            _say("mixed weights element-wise %s N=%d" % (kind, N))
+            w = dataclasses.replace(_small(kind, "bf16", 9, N, seed=N), wdtype="f32")
+            run_and_check(w)
+
+
+@pytest.mark.parametrize("wdtype", [None, "f32"])
+def test_split_direct_dw_unaligned_outputs(wdtype):
+    # one row group in the split scheme writes dW, dB itself; outputs that are not 16-byte
+    # aligned take the reduction pass instead
+    w = dataclasses.replace(_small("layernorm", "bf16", 2, 300000, seed=3), wdtype=wdtype)
+    t = inputs.make(w)
+    dev = "cuda"
+    X, W, B, dY = (t[k].to(dev) for k in ("X", "W", "B", "dY"))
+    _say("split direct dW, unaligned outputs, wdtype=%s" % wdtype)
+    Y, _, mean, rstd = nl.forward("layernorm", X, W, B, w.eps)
+    ref_dx, ref_dw, ref_db = nl.backward("layernorm", X, dY, W, mean, rstd, w.eps)
+    big_w = torch.zeros(w.N + 1, dtype=W.dtype, device=dev)
+    big_b = torch.zeros(w.N + 1, dtype=W.dtype, device=dev)
+    dX = torch.empty_like(X)
+    dW, dB = big_w[1:], big_b[1:]                  # one element past an aligned start
+    ws = nl.workspace("layernorm", X.dtype, nl.PASS_BWD, w.M, w.N, device=dev)
+    nl.norm_bwd("layernorm", X, dY, None, W, mean, rstd, w.eps, dX, None, dW, dB, ws)
+    torch.cuda.synchronize()
+    assert torch.equal(dX, ref_dx)
+    # the same column sums in another order: within the dW/dB tolerance of each other
+    check_colsums("dW", dW.double().cpu().numpy(), ref_dw.double().cpu().numpy(), "f32")
+    check_colsums("dB", dB.double().cpu().numpy(), ref_db.double().cpu().numpy(), "f32")
+
+
+def test_full_size_mixed_weight_type():
+    w = dataclasses.replace(inputs.LN_BF16_16384x4096, name="layernorm_bf16_f32w_16384x4096",
+                            wdtype="f32")
+    _say("full size %s" % w.name)
+    run_and_check(w)
+    torch.cuda.synchronize()
+
+
 # ---- tuning knobs ----------------------------------------------------------------------------
 
 KNOBS = [
