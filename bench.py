@@ -244,14 +244,15 @@ def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
     for w in inputs.all_workloads():
         r = timed_workload(w, steps, warmup, torch, nl, two_stage=False)
         res = w.r is not None
-        fb = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res)
-        row = {"workload": w.name, "kind": w.kind, "dtype": w.dtype, "M": w.M, "N": w.N,
+        fb = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res, wdtype=w.wdtype)
+        row = {"workload": w.name, "kind": w.kind, "dtype": w.dtype,
+               "weight_dtype": w.wdtype or w.dtype, "M": w.M, "N": w.N,
                "residual": res, "sets": r["sets"], "fwd_us": round(r["fwd_us"], 2),
                "fwd_GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1)}
         row["fwd_frac_peak"] = round(row["fwd_GBps"] / PEAK_HBM_GBPS, 4)
         row["fwd_rows_per_s"] = round(w.M / (r["fwd_us"] * 1e-6), 1)
         if w.dy is not None:
-            bb = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N)
+            bb = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N, wdtype=w.wdtype)
             step_us = r["ms_per_step"] * 1e3
             row.update({"bwd_us": round(r["bwd_us"], 2),
                         "bwd_GBps": round(bb / (r["bwd_us"] * 1e-6) / 1e9, 1),

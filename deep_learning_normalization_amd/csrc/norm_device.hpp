@@ -139,6 +139,19 @@ template <> struct Acc<bf16_bits, false> {
 // storage type as the activations they stay packed; fp32 weights next to bf16 activations are
 // E fp32 values (two 16-byte loads for E = 8). get() gives fp32; store() writes E fp32 sums as
 // TW (the final dW / dB).
+// Settle a value loaded from memory at this point: an empty asm that takes it in VGPRs and may
+// rewrite it, so the wait for its load is placed here. Kernels settle the weight and bias once,
+// after the first row group's loads are issued; left to itself the compiler may place that wait
+// inside the row loop, behind the loads issued for the next row group, and then every
+// iteration drains the software pipeline.
+__device__ __forceinline__ void settle(float &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void settle(u32x4 &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void settle(bf16_bits &v) {
+  unsigned u = v;
+  asm volatile("" : "+v"(u));
+  v = (bf16_bits)u;
+}
+
 template <typename T, typename TW, bool VEC> struct WAcc;
 
 template <typename T, bool VEC> struct WAcc<T, T, VEC> {
@@ -148,6 +161,7 @@ template <typename T, bool VEC> struct WAcc<T, T, VEC> {
   __device__ void zero() { r = A::zero(); }
   __device__ void load(const T *p) { r = A::ld_cached(p); }
   __device__ void get(float *f) const { A::unpack(r, f); }
+  __device__ void settle() { dln::settle(r); }
   __device__ static void store(T *p, const float *f) { A::st(p, A::pack(f)); }
 };
 
@@ -177,6 +191,10 @@ template <bool VEC> struct WAcc<bf16_bits, float, VEC> {
   __device__ void get(float *f) const {
 #pragma unroll
     for (int e = 0; e < E; ++e) f[e] = w[e];
+  }
+  __device__ void settle() {
+#pragma unroll
+    for (int e = 0; e < E; ++e) dln::settle(w[e]);
   }
   __device__ static void store(float *p, const float *f) {
     if constexpr (E % 4 == 0) {

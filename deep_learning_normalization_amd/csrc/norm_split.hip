@@ -405,6 +405,8 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   };
   int slot = 0;
   issue(iters - 1);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) rw[k].settle();
   for (int64_t it = iters - 1; it >= 0; --it) {
     const int64_t row0 = r_begin + it * ROWS;
     raw rx[ROWS][VPT], rdy[ROWS][VPT];

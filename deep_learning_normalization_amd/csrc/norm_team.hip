@@ -129,6 +129,13 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   const GroupRange gr = group_range(M, rows_per_group, a.blocked);
   int64_t g = gr.first;
   issue(g, g < gr.end);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k)
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      settle(w[k][e]);
+      settle(b[k][e]);
+    }
   for (; g < gr.end; g += gr.step) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
     float x[ROWS][VPT][E];
@@ -333,6 +340,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   const GroupRange gr = group_range(M, rows_per_group, a.blocked);
   int64_t g = gr.first;
   issue(g, g < gr.end);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) rw[k].settle();
   for (; g < gr.end; g += gr.step) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
     raw rx[ROWS][VPT], rdy[ROWS][VPT];

@@ -144,6 +144,10 @@ LN_BF16_16384x4096 = Workload("layernorm_bf16_16384x4096", "layernorm", "bf16", 
                               1e-5, x=normal(0, 1), w=normal(1, 0.1), b=normal(0, 0.1),
                               dy=normal(0, 1))
 
+# The same LayerNorm with fp32 weight, bias, dW and dB beside the bf16 activations.
+LN_BF16_F32W_16384x4096 = replace(LN_BF16_16384x4096,
+                                  name="layernorm_bf16_f32w_16384x4096", wdtype="f32")
+
 
 # RMSNorm forward + backward, bf16, LLM hidden sizes at 32768 tokens, with 1% of the
 # columns (channels) scaled by 20.
@@ -173,7 +177,7 @@ LONG_ROW_SHAPES = ((256, 262144), (4, 4194304))
 
 def all_workloads():
     """Every full-size workload, in a fixed order."""
-    out = [RMS_F32_2048x1024, LN_BF16_16384x4096]
+    out = [RMS_F32_2048x1024, LN_BF16_16384x4096, LN_BF16_F32W_16384x4096]
     out += [rms_hidden(N) for N in RMS_HIDDEN_SIZES]
     out.append(RESID_RMS_BF16_65536x7168)
     for M, N in LONG_ROW_SHAPES:

@@ -6,6 +6,7 @@ and HBM traffic.
     python -m deep_learning_normalization_amd.profiling traffic --fetch DIR --write DIR \\
         --workload NAME --kernel SUBSTR --algo-bytes N --out FILE --cmd "..."
     python -m deep_learning_normalization_amd.profiling workloads --root DIR --out FILE --cmd "..."
+    python -m deep_learning_normalization_amd.profiling summarize --root DIR --out DIR
 
 `drive` runs one workload's forward and backward K times on two rotating buffer sets (run it
 under rocprofv3); it first makes the 1 GiB device copies the counter calibration uses.
@@ -203,8 +204,9 @@ def workloads(root, out, cmd):
         f_factor = COPY_BYTES / (statistics.median(cf) * 1024.0)
         w_factor = COPY_BYTES / (statistics.median(cw) * 1024.0)
         res = w.r is not None
-        fwd_alg = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res)
-        bwd_alg = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N) if w.dy is not None else 0
+        fwd_alg = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res, wdtype=w.wdtype)
+        bwd_alg = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N, wdtype=w.wdtype) \
+            if w.dy is not None else 0
         names = {_short(n): n for n in fetch if "dln::" in n}
         for short in sorted(names, key=lambda k: (("bwd" in k or "colsum" in k or "dx" in k
                                                    or "partial" in k), k)):
@@ -236,6 +238,38 @@ def workloads(root, out, cmd):
         f.write("\n".join(lines) + "\n")
 
 
+HEADLINE_TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_trace "
+                      "-o trace --output-format csv -- python3 $REPO/bench.py --steps 50 --warmup 10 "
+                      "--no-cpu-baseline")
+HEADLINE_PMC_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/prof_fetch -o fetch "
+                    "--output-format csv -- python3 $REPO/bench.py --steps 20 --warmup 5 "
+                    "--no-cpu-baseline; the same with --pmc WRITE_SIZE -d $REPO/gpurun_out/prof_write "
+                    "-o write")
+WORKLOAD_CMD = ("cd /tmp && PYTHONPATH=$REPO rocprofv3 {--kernel-trace | --pmc FETCH_SIZE | --pmc "
+                "WRITE_SIZE} -d $REPO/gpurun_out/wl/NAME/{trace|fetch|write} -o run --output-format csv "
+                "-- python3 -m deep_learning_normalization_amd.profiling drive --workload NAME")
+
+
+def summarize(root, out):
+    """Every committed summary from one capture: the headline command's kernel statistics and
+    its fused backward's and forward's traffic (under root/prof_{trace,fetch,write}), and the
+    per-workload table (under root/wl)."""
+    from deep_learning_normalization_amd import inputs, traffic as model
+    w = inputs.LN_BF16_16384x4096
+    stats(os.path.join(root, "prof_trace"), os.path.join(out, "kernel_stats_%s.md" % w.name),
+          HEADLINE_TRACE_CMD)
+    fetch, write = os.path.join(root, "prof_fetch"), os.path.join(root, "prof_write")
+    traffic(fetch, write, w.name, "team_bwd_kernel",
+            model.bwd_fused_bytes(w.kind, w.dtype, w.M, w.N),
+            os.path.join(out, "traffic_%s.json" % w.name), HEADLINE_PMC_CMD)
+    traffic(fetch, write, w.name, "team_fwd_kernel",
+            model.fwd_bytes(w.kind, w.dtype, w.M, w.N),
+            os.path.join(out, "traffic_%s_fwd.json" % w.name),
+            "the same two runs as traffic_%s.json" % w.name)
+    workloads(os.path.join(root, "wl"), os.path.join(out, "kernels_all_workloads.md"),
+              WORKLOAD_CMD)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="what", required=True)
@@ -258,8 +292,13 @@ def main():
     wk.add_argument("--root", required=True)
     wk.add_argument("--out", required=True)
     wk.add_argument("--cmd", required=True)
+    sm = sub.add_parser("summarize")
+    sm.add_argument("--root", required=True, help="the capture's output folder")
+    sm.add_argument("--out", required=True, help="where the summaries go")
     a = ap.parse_args()
-    if a.what == "drive":
+    if a.what == "summarize":
+        summarize(a.root, a.out)
+    elif a.what == "drive":
         drive(a.workload, a.steps)
     elif a.what == "workloads":
         workloads(a.root, a.out, a.cmd)

@@ -162,14 +162,6 @@ def test_split_direct_dw_unaligned_outputs(wdtype):
     check_colsums("dB", dB.double().cpu().numpy(), ref_db.double().cpu().numpy(), "f32")
 
 
-def test_full_size_mixed_weight_type():
-    w = dataclasses.replace(inputs.LN_BF16_16384x4096, name="layernorm_bf16_f32w_16384x4096",
-                            wdtype="f32")
-    _say("full size %s" % w.name)
-    run_and_check(w)
-    torch.cuda.synchronize()
-
-
 # ---- tuning knobs ----------------------------------------------------------------------------
 
 KNOBS = [
