@@ -59,8 +59,8 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   norm_status_t st = current_cu_count(&cu);
   if (st != NORM_OK) return st;
   const void *ptrs[] = {X, dY, dH, W, dX, dR};
-  const int aligned = dln::all_aligned16(ptrs, 6) ? 1 : 0;
-  st = dln::make_plan(kind, dtype, NORM_PASS_BWD, M, N, 0, aligned, cu, dln::tuning(), plan);
+  const int align = dln::common_align(ptrs, 6);
+  st = dln::make_plan(kind, dtype, NORM_PASS_BWD, M, N, 0, align, cu, dln::tuning(), plan);
   if (st != NORM_OK) return st;
   st = ws_ok(*plan, workspace, workspace_bytes);
   if (st != NORM_OK) return st;
@@ -145,9 +145,9 @@ norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const voi
   st = current_cu_count(&cu);
   if (st != NORM_OK) return st;
   const void *ptrs[] = {X, R, W, B, Y, H};
-  const int aligned = dln::all_aligned16(ptrs, 6) ? 1 : 0;
+  const int align = dln::common_align(ptrs, 6);
   dln::Plan p;
-  st = dln::make_plan(kind, dtype, NORM_PASS_FWD, M, N, R != nullptr, aligned, cu,
+  st = dln::make_plan(kind, dtype, NORM_PASS_FWD, M, N, R != nullptr, align, cu,
                       dln::tuning(), &p);
   if (st != NORM_OK) return st;
   st = ws_ok(p, workspace, workspace_bytes);
@@ -194,10 +194,10 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
                  workspace_bytes, &p, &a);
   if (st != NORM_OK) return st;
   // the split scheme with a single row group writes dW/dB itself, with no reduction pass
-  // (its vector stores need dW and dB 16-byte aligned, like every other vector access)
+  // (its vector stores of dW and dB need the alignment of the weight loads of its width)
   const void *outs[] = {dW, dB};
   const bool direct = p.scheme == NORM_SCHEME_SPLIT && p.row_groups == 1 &&
-                      (!p.vector || dln::all_aligned16(outs, 2));
+                      (size_t)dln::common_align(outs, 2) >= dln::weight_align_need(dtype, p.epv);
   if (direct) {
     a.dw = dW;
     a.db = dB;
@@ -249,15 +249,15 @@ norm_status_t norm_workspace_size(norm_kind_t kind, norm_dtype_t dtype, norm_pas
 }
 
 norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
-                        int64_t N, int residual, int aligned, int cu_count, norm_plan_t *out) {
+                        int64_t N, int residual, int align, int cu_count, norm_plan_t *out) {
   if (!out) return NORM_ERR_INVALID_ARG;
   dln::Plan p;
   norm_status_t st =
-      dln::make_plan(kind, dtype, pass, M, N, residual, aligned, cu_count, dln::tuning(), &p);
+      dln::make_plan(kind, dtype, pass, M, N, residual, align, cu_count, dln::tuning(), &p);
   if (st != NORM_OK) return st;
   norm_plan_t o{};
   o.scheme = p.scheme;
-  o.vector = p.vector;
+  o.access_bytes = p.access_bytes;
   o.elems_per_access = p.epv;
   o.threads = p.threads;
   o.team_threads = p.team_threads;

@@ -55,61 +55,70 @@ __device__ __forceinline__ float round_bf16(float v) {
   return bf16_lo(p);
 }
 
-// Acc<T, VEC>: one memory access of EPV elements of T (16 bytes when VEC, else one element),
-// converted to / from fp32.
-template <typename T, bool VEC> struct Acc;
+// Acc<T, E>: one memory access of E elements of T, converted to / from fp32. E * sizeof(T) is
+// 16, 8 or 4 bytes on the vector paths (whole 32-bit words, E = full_epv<T>() and its halves
+// down to two elements); E = 1 is the element-wise path.
+template <typename T> constexpr int full_epv() { return 16 / (int)sizeof(T); }
 
-template <> struct Acc<float, true> {
-  static constexpr int EPV = 4;
-  typedef u32x4 raw;
-  __device__ static raw ld(const float *p) { return ld_stream(reinterpret_cast<const raw *>(p)); }
-  __device__ static raw ld_cached(const float *p) { return *reinterpret_cast<const raw *>(p); }
-  __device__ static void st(float *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
+typedef unsigned u32x2 __attribute__((ext_vector_type(2)));
+template <int NW> struct Words;
+template <> struct Words<4> { typedef u32x4 type; };
+template <> struct Words<2> { typedef u32x2 type; };
+template <> struct Words<1> { typedef unsigned type; };
+// Word i of a raw access, read into a scalar first: this clang's __builtin_bit_cast applied
+// directly to a vector subscript (v[i]) reads element 0 whatever i is.
+__device__ __forceinline__ unsigned word(u32x4 v, int i) { const unsigned u = v[i]; return u; }
+__device__ __forceinline__ unsigned word(u32x2 v, int i) { const unsigned u = v[i]; return u; }
+__device__ __forceinline__ unsigned word(unsigned v, int) { return v; }
+__device__ __forceinline__ void set_word(u32x4 &v, int i, unsigned u) { v[i] = u; }
+__device__ __forceinline__ void set_word(u32x2 &v, int i, unsigned u) { v[i] = u; }
+__device__ __forceinline__ void set_word(unsigned &v, int, unsigned u) { v = u; }
+
+template <typename T, int E> struct Acc {
+  static_assert(E >= 2 && E <= full_epv<T>() && (E & (E - 1)) == 0, "whole-word accesses");
+  static constexpr int EPV = E;
+  static constexpr int NW = E * (int)sizeof(T) / 4;
+  static constexpr bool BF16 = sizeof(T) == 2;
+  typedef typename Words<NW>::type raw;
+  __device__ static raw ld(const T *p) { return ld_stream(reinterpret_cast<const raw *>(p)); }
+  __device__ static raw ld_cached(const T *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static void st(T *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
   __device__ static void unpack(raw v, float *f) {
-    // Element first into a scalar: this clang's __builtin_bit_cast applied directly to a
-    // vector subscript (v[i]) reads element 0 whatever i is.
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned u = v[i];
-      f[i] = __builtin_bit_cast(float, u);
+    for (int i = 0; i < NW; ++i) {
+      const unsigned u = word(v, i);
+      if constexpr (BF16) {
+        f[2 * i] = bf16_lo(u);
+        f[2 * i + 1] = bf16_hi(u);
+      } else {
+        f[i] = __builtin_bit_cast(float, u);
+      }
     }
   }
   __device__ static raw pack(const float *f) {
     raw v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __builtin_bit_cast(unsigned, f[i]);
+    for (int i = 0; i < NW; ++i) {
+      if constexpr (BF16)
+        set_word(v, i, pack_bf16x2(f[2 * i], f[2 * i + 1]));
+      else
+        set_word(v, i, __builtin_bit_cast(unsigned, f[i]));
+    }
     return v;
   }
-  __device__ static float round(float v) { return v; }
-  __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
-};
-
-template <> struct Acc<bf16_bits, true> {
-  static constexpr int EPV = 8;
-  typedef u32x4 raw;
-  __device__ static raw ld(const bf16_bits *p) {
-    return ld_stream(reinterpret_cast<const raw *>(p));
+  __device__ static float round(float v) {
+    if constexpr (BF16) return round_bf16(v);
+    return v;
   }
-  __device__ static raw ld_cached(const bf16_bits *p) { return *reinterpret_cast<const raw *>(p); }
-  __device__ static void st(bf16_bits *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
-  __device__ static void unpack(raw v, float *f) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      f[2 * i] = bf16_lo(v[i]);
-      f[2 * i + 1] = bf16_hi(v[i]);
-    }
-  }
-  __device__ static raw pack(const float *f) {
+  __device__ static raw zero() {
     raw v;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = pack_bf16x2(f[2 * i], f[2 * i + 1]);
+    for (int i = 0; i < NW; ++i) set_word(v, i, 0u);
     return v;
   }
-  __device__ static float round(float v) { return round_bf16(v); }
-  __device__ static raw zero() { return raw{0u, 0u, 0u, 0u}; }
 };
 
-template <> struct Acc<float, false> {
+template <> struct Acc<float, 1> {
   static constexpr int EPV = 1;
   typedef float raw;
   __device__ static raw ld(const float *p) { return *p; }
@@ -121,7 +130,7 @@ template <> struct Acc<float, false> {
   __device__ static raw zero() { return 0.0f; }
 };
 
-template <> struct Acc<bf16_bits, false> {
+template <> struct Acc<bf16_bits, 1> {
   static constexpr int EPV = 1;
   typedef bf16_bits raw;
   __device__ static raw ld(const bf16_bits *p) { return *p; }
@@ -135,16 +144,14 @@ template <> struct Acc<bf16_bits, false> {
   __device__ static raw zero() { return 0; }
 };
 
-// WAcc<T, TW, VEC>: the weight (or bias) values of one access of T, stored as TW. With the same
-// storage type as the activations they stay packed; fp32 weights next to bf16 activations are
-// E fp32 values (two 16-byte loads for E = 8). get() gives fp32; store() writes E fp32 sums as
-// TW (the final dW / dB).
 // Settle a value loaded from memory at this point: an empty asm that takes it in VGPRs and may
 // rewrite it, so the wait for its load is placed here. Kernels settle the weight and bias once,
 // after the first row group's loads are issued; left to itself the compiler may place that wait
 // inside the row loop, behind the loads issued for the next row group, and then every
 // iteration drains the software pipeline.
 __device__ __forceinline__ void settle(float &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void settle(unsigned &v) { asm volatile("" : "+v"(v)); }
+__device__ __forceinline__ void settle(u32x2 &v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void settle(u32x4 &v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ void settle(bf16_bits &v) {
   unsigned u = v;
@@ -152,10 +159,14 @@ __device__ __forceinline__ void settle(bf16_bits &v) {
   v = (bf16_bits)u;
 }
 
-template <typename T, typename TW, bool VEC> struct WAcc;
+// WAcc<T, TW, E>: the weight (or bias) values of one access of E elements of T, stored as TW.
+// With the same storage type as the activations they stay packed; fp32 weights next to bf16
+// activations are E fp32 values (E * 4 bytes: two 16-byte loads for E = 8, one 8-byte load for
+// E = 2). get() gives fp32; store() writes E fp32 sums as TW (the final dW / dB).
+template <typename T, typename TW, int E> struct WAcc;
 
-template <typename T, bool VEC> struct WAcc<T, T, VEC> {
-  using A = Acc<T, VEC>;
+template <typename T, int EV> struct WAcc<T, T, EV> {
+  using A = Acc<T, EV>;
   static constexpr int E = A::EPV;
   typename A::raw r;
   __device__ void zero() { r = A::zero(); }
@@ -165,27 +176,22 @@ template <typename T, bool VEC> struct WAcc<T, T, VEC> {
   __device__ static void store(T *p, const float *f) { A::st(p, A::pack(f)); }
 };
 
-template <bool VEC> struct WAcc<bf16_bits, float, VEC> {
-  static constexpr int E = Acc<bf16_bits, VEC>::EPV;
+template <int EV> struct WAcc<bf16_bits, float, EV> {
+  static constexpr int E = EV;
+  // words per load: 16-byte loads when E is a multiple of 4, else one E-word load
+  static constexpr int LW = E % 4 == 0 ? 4 : E;
+  typedef typename Words<LW>::type raw;
   float w[E];
   __device__ void zero() {
 #pragma unroll
     for (int e = 0; e < E; ++e) w[e] = 0.0f;
   }
   __device__ void load(const float *p) {
-    if constexpr (E % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < E / 4; ++i) {
-        const u32x4 v = *reinterpret_cast<const u32x4 *>(p + 4 * i);
+    for (int i = 0; i < E / LW; ++i) {
+      const raw v = *reinterpret_cast<const raw *>(p + LW * i);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const unsigned u = v[j];
-          w[4 * i + j] = __builtin_bit_cast(float, u);
-        }
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) w[e] = p[e];
+      for (int j = 0; j < LW; ++j) w[LW * i + j] = __builtin_bit_cast(float, word(v, j));
     }
   }
   __device__ void get(float *f) const {
@@ -197,17 +203,12 @@ template <bool VEC> struct WAcc<bf16_bits, float, VEC> {
     for (int e = 0; e < E; ++e) dln::settle(w[e]);
   }
   __device__ static void store(float *p, const float *f) {
-    if constexpr (E % 4 == 0) {
 #pragma unroll
-      for (int i = 0; i < E / 4; ++i) {
-        u32x4 v;
+    for (int i = 0; i < E / LW; ++i) {
+      raw v;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) v[j] = __builtin_bit_cast(unsigned, f[4 * i + j]);
-        *reinterpret_cast<u32x4 *>(p + 4 * i) = v;
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < E; ++e) p[e] = f[e];
+      for (int j = 0; j < LW; ++j) set_word(v, j, __builtin_bit_cast(unsigned, f[LW * i + j]));
+      *reinterpret_cast<raw *>(p + LW * i) = v;
     }
   }
 };

@@ -82,6 +82,11 @@ norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &
                               hipStream_t s);
 norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                               hipStream_t s);
+// 8- and 4-byte accesses (plans with scale > 1), instantiated apart from the full-width ones
+norm_status_t launch_team_fwd_narrow(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                                     hipStream_t s);
+norm_status_t launch_team_bwd_narrow(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
+                                     hipStream_t s);
 norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                                hipStream_t s);
 norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,

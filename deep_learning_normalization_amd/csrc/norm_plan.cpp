@@ -34,11 +34,23 @@ int vec_epv(norm_dtype_t d) { return d == NORM_F32 ? 4 : 8; }
 // bytes per element of the activations (X, R, Y, H, dY, dH, dX, dR) and of W, B, dW, dB
 size_t elem_size(int d) { return d == NORM_F32 ? 4 : 2; }
 size_t weight_size(int d) { return d == NORM_BF16 ? 2 : 4; }
+// Pointer alignment an access of e elements needs: e activation elements in one load, and the
+// matching e weights (read 16 bytes at a time when they span 16 bytes or more).
+size_t access_align(int d, int e) {
+  const size_t act = (size_t)e * elem_size(d), w = (size_t)e * weight_size(d);
+  const size_t wneed = w < 16 ? w : 16;
+  return act > wneed ? act : wneed;
+}
 int lb_of(int threads) { return threads <= 256 ? 256 : threads <= 512 ? 512 : 1024; }
 
+// Access width classes: element-wise, full (16-byte) vectors, narrow (8- or 4-byte) vectors.
+// Narrow shapes are given in full-width units: the kernel runs vpt * scale narrow accesses.
+enum Width { kElem = 0, kFull = 1, kNarrow = 2 };
+
 // Compiled kernel shapes (must match the menus in the kernel sources).
-bool wave_menu(bool vec, int vpt, int rows) {
-  if (!vec) return rows == 1 && (vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16);
+bool wave_menu(int wc, int vpt, int rows) {
+  if (wc == kElem) return rows == 1 && (vpt == 1 || vpt == 2 || vpt == 4 || vpt == 8 || vpt == 16);
+  if (wc == kNarrow) return rows == 1 && (vpt == 1 || vpt == 2 || vpt == 4);
   switch (vpt) {
   case 1:
   case 2: return rows == 1 || rows == 2 || rows == 4;
@@ -48,8 +60,26 @@ bool wave_menu(bool vec, int vpt, int rows) {
   }
 }
 
-bool block_menu(bool vec, int vpt, int rows, int lb) {
-  if (!vec) return lb == 1024 && rows == 1 && (vpt == 4 || vpt == 8);
+// 4-byte accesses (scale 4) need an address register pair per access once the accesses of a
+// thread span more than the load's immediate offset; shapes that then spill are left out: the
+// residual forward beyond 4 full-width accesses per 256 threads, and 1024-thread backwards.
+bool narrow_spills(int sc, bool bwd, bool resid, int vpt, int lb) {
+  if (sc < 4) return false;
+  if (bwd) return lb >= 1024;
+  return resid && vpt * (lb / 256) > 4;
+}
+
+bool block_menu(int wc, bool bwd, int vpt, int rows, int lb, int sc = 1, bool resid = false) {
+  if (wc == kElem) return lb == 1024 && rows == 1 && (vpt == 4 || vpt == 8);
+  if (wc == kNarrow) {
+    if (rows != 1 || narrow_spills(sc, bwd, resid, vpt, lb)) return false;
+    switch (lb) {
+    case 256: return vpt == 1 || vpt == 2 || vpt == 4 || (!bwd && vpt == 8);
+    case 512: return vpt == 1 || vpt == 2 || (!bwd && vpt == 4);
+    case 1024: return vpt == 1 || (!bwd && vpt == 2);
+    default: return false;
+    }
+  }
   switch (lb) {
   case 256:
     return (vpt == 1 && (rows == 1 || rows == 2 || rows == 4)) ||
@@ -67,9 +97,9 @@ bool block_menu(bool vec, int vpt, int rows, int lb) {
 // Register budget: a 1024-thread workgroup leaves 128 VGPRs per lane, 512 threads 256. The
 // backward holds more per access (prefetched X and dY, dW and dB accumulators), so it gets
 // fewer accesses per thread; these limits are the compiled shapes that do not spill.
-bool block_fits_registers(bool vec, bool bwd, int vpt, int rows, int lb) {
+bool block_fits_registers(int wc, bool bwd, int vpt, int rows, int lb) {
   const int slots = vpt * rows;
-  if (!vec) return !bwd || vpt <= 4;
+  if (wc == kElem) return !bwd || vpt <= 4;
   if (!bwd) {
     if (lb >= 1024) return slots <= 2;
     if (lb >= 512) return slots <= 4;
@@ -80,9 +110,14 @@ bool block_fits_registers(bool vec, bool bwd, int vpt, int rows, int lb) {
   return vpt <= 4 && slots <= 8;
 }
 
-bool split_fwd_menu(bool vec, int vpt) { return vec ? (vpt == 1 || vpt == 2 || vpt == 4) : vpt == 8; }
-bool split_bwd_menu(bool vec, int vpt, int rows) {
-  if (!vec) return vpt == 8 && rows == 1;
+bool split_fwd_menu(int wc, int vpt) {
+  if (wc == kElem) return vpt == 8;
+  if (wc == kNarrow) return vpt == 4;
+  return vpt == 1 || vpt == 2 || vpt == 4;
+}
+bool split_bwd_menu(int wc, int vpt, int rows) {
+  if (wc == kElem) return vpt == 8 && rows == 1;
+  if (wc == kNarrow) return vpt == 4 && rows == 1;
   switch (vpt) {
   case 1:
   case 2: return rows == 1 || rows == 2 || rows == 4;
@@ -135,7 +170,7 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
 }
 
 norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
-                        int64_t N, int residual, int aligned, int cu, const Tuning &t,
+                        int64_t N, int residual, int align, int cu, const Tuning &t,
                         Plan *out) {
   if (!out || !valid_kind(kind) || !valid_dtype(dtype) ||
       (pass != NORM_PASS_FWD && pass != NORM_PASS_BWD) || M < 0 || N <= 0 || N > kMaxN ||
@@ -143,18 +178,32 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     return NORM_ERR_INVALID_ARG;
   Plan p;
   const bool bwd = pass == NORM_PASS_BWD;
+  // The widest whole-word access (16, 8, then 4 bytes; at least two elements) that divides the
+  // row length and that every pointer's alignment allows; else one element per access.
   const int ev = vec_epv(dtype);
-  p.vector = (aligned && N % ev == 0) ? 1 : 0;
-  p.epv = p.vector ? ev : 1;
+  p.epv = 1;
+  for (int e = ev; e >= 2; e /= 2)
+    if (N % e == 0 && align > 0 && (size_t)align >= access_align(dtype, e)) {
+      p.epv = e;
+      break;
+    }
+  p.vector = p.epv > 1 ? 1 : 0;
+  p.scale = p.vector ? ev / p.epv : 1;
+  p.access_bytes = (int)((size_t)p.epv * elem_size(dtype));
   const bool vec = p.vector != 0;
+  const int wc = !vec ? kElem : p.scale == 1 ? kFull : kNarrow;
+  const int sc = p.scale;
   const int64_t nacc = N / p.epv;
+  // accesses per row in full-width units: the narrow paths size teams and pick schemes as the
+  // 16-byte path would for the same row
+  const int64_t nacc_eq = cdiv(nacc, sc);
   const int64_t Mm = M > 0 ? M : 1; // M == 0 launches nothing; size as one row
 
   int scheme = t.scheme;
   if (scheme == NORM_SCHEME_AUTO) {
     if (N <= kWaveMaxRow)
       scheme = NORM_SCHEME_WAVE;
-    else if (nacc <= (vec ? (bwd ? 1024 : 2048) : (bwd ? 4096 : 8192)))
+    else if (nacc_eq <= (!vec ? (bwd ? 4096 : 8192) : (bwd || (sc == 4 && residual)) ? 1024 : 2048))
       scheme = NORM_SCHEME_BLOCK;
     else
       scheme = NORM_SCHEME_SPLIT;
@@ -165,14 +214,14 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     static const int menu[] = {1, 2, 4, 8, 16};
     int vpt = 0;
     for (int v : menu)
-      if (64LL * v >= nacc && wave_menu(vec, v, 1)) {
+      if (64LL * v * sc >= nacc && wave_menu(wc, v, 1)) {
         vpt = v;
         break;
       }
     if (!vpt) return NORM_ERR_UNSUPPORTED;
     int rows = t.rows > 0 ? t.rows : 1;
-    if (!wave_menu(vec, vpt, rows)) rows = 1;
-    p.vpt = vpt;
+    if (!wave_menu(wc, vpt, rows)) rows = 1;
+    p.vpt = vpt * sc;
     p.rows = rows;
     p.threads = kWaveThreads;
     p.lb = kWaveThreads;
@@ -193,9 +242,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       const bool use_override = pass_i == 0 && t.team_threads > 0;
       for (int i = 0; i < nmenu && !vpt; ++i) {
         const int v = menu[i];
-        int cand = (int)(cdiv(cdiv(nacc, v), 64) * 64);
+        int cand = (int)(cdiv(cdiv(nacc, (int64_t)v * sc), 64) * 64);
         if (use_override) {
-          if ((int64_t)t.team_threads * v < nacc) continue;
+          if ((int64_t)t.team_threads * v * sc < nacc) continue;
           cand = t.team_threads;
         }
         const int limit = (pass_i == 0 && !use_override)
@@ -207,8 +256,13 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
         // once by default (measured on MI355X, with the saved statistics prefetched as well:
         // fewer, fuller workgroups; wider teams or more accesses per thread do better with one)
         int r = t.rows > 0 ? t.rows : ((bwd && v == 1 && cand <= 512) ? 2 : 1);
-        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, bwd, v, r, lb)) r = 1;
-        if (!block_menu(vec, v, r, lb) || !block_fits_registers(vec, bwd, v, r, lb)) continue;
+        const bool res = residual != 0;
+        auto ok = [&](int rr) {
+          return block_menu(wc, bwd, v, rr, lb, sc, res) &&
+                 block_fits_registers(wc, bwd, v, rr, lb);
+        };
+        if (!ok(r)) r = 1;
+        if (!ok(r)) continue;
         vpt = v;
         tt = cand;
         rows = r;
@@ -224,11 +278,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // own barrier) outrun one large workgroup whose barrier waits for every wavefront.
     int teams = t.teams > 0 ? t.teams : 1;
     if (tt % 256 != 0) teams = 1;
-    while (teams > 1 && (tt * teams > 1024 || !block_menu(vec, vpt, rows, lb_of(tt * teams)) ||
-                         !block_fits_registers(vec, bwd, vpt, rows, lb_of(tt * teams))))
+    while (teams > 1 && (tt * teams > 1024 ||
+                         !block_menu(wc, bwd, vpt, rows, lb_of(tt * teams), sc, residual != 0) ||
+                         !block_fits_registers(wc, bwd, vpt, rows, lb_of(tt * teams))))
       --teams;
     if (!vec && teams > 1 && tt * teams > 1024) teams = 1;
-    p.vpt = vpt;
+    p.vpt = vpt * sc;
     p.rows = rows;
     p.team_threads = tt;
     p.threads = tt * teams;
@@ -237,7 +292,7 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     if (bwd) {
       // Backward: persistent, about 1024 16-byte accesses per tensor in flight per CU; every
       // workgroup writes one partial row, so fewer, longer-lived workgroups.
-      const int64_t load = (int64_t)p.threads * vpt * rows;
+      const int64_t load = (int64_t)p.threads * vpt * rows; // full-width units
       const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1);
       p.grid = groups < cu * gpc ? groups : cu * gpc;
     } else if (t.grid_per_cu > 0) {
@@ -250,15 +305,15 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     }
     p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_SPLIT) {
-    int vpt = vec ? 4 : 8;
-    if (t.split_chunk > 0 && vec) { // the element-wise path has one chunk size
+    int vpt = vec ? 4 : 8; // full-width units on the vector paths
+    if (t.split_chunk > 0 && wc == kFull) { // the other widths have one chunk size
       const int64_t per = (int64_t)kSplitThreads * p.epv;
       if (t.split_chunk % per) return NORM_ERR_UNSUPPORTED;
       vpt = (int)(t.split_chunk / per);
     }
-    if (!split_fwd_menu(vec, vpt)) return NORM_ERR_UNSUPPORTED;
-    const int64_t chunk_acc = (int64_t)kSplitThreads * vpt;
-    p.vpt = vpt;
+    if (!split_fwd_menu(wc, vpt)) return NORM_ERR_UNSUPPORTED;
+    const int64_t chunk_acc = (int64_t)kSplitThreads * vpt * sc;
+    p.vpt = vpt * sc;
     p.threads = kSplitThreads;
     p.lb = kSplitThreads;
     p.team_threads = kSplitThreads;
@@ -276,8 +331,8 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       const int64_t rpg = cdiv(Mm, G);
       G = cdiv(Mm, rpg);
       int rows = t.rows > 0 ? t.rows : (vpt >= 4 ? 1 : 2);
-      if (!split_bwd_menu(vec, vpt, rows)) rows = 1;
-      if (!split_bwd_menu(vec, vpt, rows)) return NORM_ERR_UNSUPPORTED;
+      if (!split_bwd_menu(wc, vpt, rows)) rows = 1;
+      if (!split_bwd_menu(wc, vpt, rows)) return NORM_ERR_UNSUPPORTED;
       p.rows = rows;
       p.row_groups = G;
       p.rows_per_group = rpg;
@@ -312,15 +367,17 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
 norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
                               int64_t N, int residual, int cu, const Tuning &t, size_t *bytes) {
   if (!bytes) return NORM_ERR_INVALID_ARG;
-  // Size for both pointer alignments. A tuning override may leave the element-wise variant
-  // without a kernel; a call with such pointers then fails with NORM_ERR_UNSUPPORTED anyway,
-  // so only the 16-byte variant has to plan successfully.
+  // Size for every pointer alignment (each may pick another access width). A tuning override
+  // may leave a narrower width without a kernel; a call with such pointers then fails with
+  // NORM_ERR_UNSUPPORTED anyway, so only the 16-byte-aligned plan has to succeed.
   Plan p;
-  norm_status_t s = make_plan(kind, dtype, pass, M, N, residual, 1, cu, t, &p);
+  norm_status_t s = make_plan(kind, dtype, pass, M, N, residual, 16, cu, t, &p);
   if (s != NORM_OK) return s;
   size_t best = p.ws_bytes;
-  if (make_plan(kind, dtype, pass, M, N, residual, 0, cu, t, &p) == NORM_OK && p.ws_bytes > best)
-    best = p.ws_bytes;
+  for (int align : {8, 4, 2, 1})
+    if (make_plan(kind, dtype, pass, M, N, residual, align, cu, t, &p) == NORM_OK &&
+        p.ws_bytes > best)
+      best = p.ws_bytes;
   *bytes = best;
   return NORM_OK;
 }
@@ -402,10 +459,18 @@ norm_status_t check_bwd(const BwdCheck &c) {
   return NORM_OK;
 }
 
-bool all_aligned16(const void *const *ptrs, int n) {
+bool all_aligned16(const void *const *ptrs, int n) { return common_align(ptrs, n) >= 16; }
+
+int common_align(const void *const *ptrs, int n) {
+  uintptr_t bits = 16;
   for (int i = 0; i < n; ++i)
-    if (ptrs[i] && ((uintptr_t)ptrs[i] & 15u)) return false;
-  return true;
+    if (ptrs[i]) bits |= (uintptr_t)ptrs[i];
+  return (int)(bits & (~bits + 1)); // lowest set bit, at most 16
+}
+
+size_t weight_align_need(norm_dtype_t d, int epv) {
+  const size_t w = (size_t)epv * weight_size(d);
+  return w < 16 ? w : 16;
 }
 
 } // namespace dln

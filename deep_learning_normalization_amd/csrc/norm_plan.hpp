@@ -14,8 +14,10 @@ namespace dln {
 // where its workspace regions live.
 struct Plan {
   int scheme = NORM_SCHEME_BLOCK;
-  int vector = 1;          // 16-byte accesses (1) or element-wise (0)
+  int vector = 1;          // vector accesses of whole 32-bit words (1) or element-wise (0)
   int epv = 8;             // elements per access
+  int scale = 1;           // full-width elements (16 bytes) / epv on the vector paths: 1, 2, 4
+  int access_bytes = 16;   // bytes per access: 16, 8 or 4, or the element size
   int threads = 256;       // workgroup size
   int lb = 256;            // compiled workgroup-size bound of the kernel (>= threads)
   int team_threads = 256;  // threads sharing a row (64 for the wave scheme)
@@ -55,8 +57,10 @@ struct Tuning {
 const Tuning &tuning();
 norm_status_t set_tuning(norm_tune_t key, int64_t value);
 
+// align: the largest power of two, up to 16, that divides the address of every tensor the call
+// touches (16 for buffers from an allocator; 1 when unknown or odd).
 norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
-                        int64_t N, int residual, int aligned, int cu_count, const Tuning &t,
+                        int64_t N, int residual, int align, int cu_count, const Tuning &t,
                         Plan *out);
 
 // Largest workspace any pointer alignment can need for this call on cu_count CUs.
@@ -92,5 +96,10 @@ struct BwdCheck {
 norm_status_t check_bwd(const BwdCheck &c);
 
 bool all_aligned16(const void *const *ptrs, int n);
+// The largest power of two, at most 16, dividing every non-null pointer (16 if all are null).
+int common_align(const void *const *ptrs, int n);
+// Alignment the weight-sized outputs (dW, dB) need for the vector stores of an access of epv
+// elements.
+size_t weight_align_need(norm_dtype_t d, int epv);
 
 } // namespace dln

@@ -72,7 +72,8 @@ __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, in
     float q[1] = {0.0f};
     for (int64_t c = tid; c < C; c += blockDim.x) {
       const float e = (rp[RP * c] - shift) - delta;
-      q[0] += rp[RP * c + 1] + 2.0f * e * rp[RP * c + 2] + chunk_count(c, chunk_acc, nacc, E) * e * e;
+      q[0] += rp[RP * c + 1] + 2.0f * e * rp[RP * c + 2] +
+              chunk_count(c, chunk_acc, nacc, E) * e * e;
     }
     team_sum<1, SPLIT_LB / 64>(q, red, slot, waves, 0, wave, lane);
     slot ^= 1;
@@ -90,9 +91,9 @@ __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, in
 
 // ---- forward pass 1: chunk statistics ---------------------------------------------------
 
-template <typename T, bool VEC, int VPT, bool RESID>
+template <typename T, int EV, int VPT, bool RESID>
 __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
-  using A = Acc<T, VEC>;
+  using A = Acc<T, EV>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
   __shared__ __align__(16) float red[RED_FLOATS];
@@ -178,9 +179,9 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
 
 // ---- forward pass 2: combine, normalise the chunk ---------------------------------------
 
-template <typename T, typename TW, bool VEC, int VPT>
+template <typename T, typename TW, int EV, int VPT>
 __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
-  using A = Acc<T, VEC>;
+  using A = Acc<T, EV>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
   __shared__ __align__(16) float red[RED_FLOATS];
@@ -200,7 +201,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
   T *__restrict__ Y = static_cast<T *>(a.y) + base;
 
   raw rx[VPT];
-  WAcc<T, TW, VEC> rw[VPT], rb[VPT];
+  WAcc<T, TW, EV> rw[VPT], rb[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
@@ -255,9 +256,9 @@ __global__ __launch_bounds__(SPLIT_LB) void split_finalize_stats_kernel(BwdArgs 
 
 // One workgroup per (row, chunk), like the forward's statistics pass: the whole grid streams X
 // and dY once, with no loop-carried latency.
-template <typename T, typename TW, bool VEC, int VPT, bool LN>
+template <typename T, typename TW, int EV, int VPT, bool LN>
 __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) {
-  using A = Acc<T, VEC>;
+  using A = Acc<T, EV>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
   __shared__ __align__(16) float red[RED_FLOATS];
@@ -275,7 +276,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
   const float *mean_p = a.rstd ? a.mean : a.stats;
 
   raw rx[VPT], rdy[VPT];
-  WAcc<T, TW, VEC> rw[VPT];
+  WAcc<T, TW, EV> rw[VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * SPLIT_LB;
@@ -328,9 +329,9 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
 // One workgroup per (row group, chunk). Rows are visited in descending order (the last rows
 // pass 1 read come back first) and the next row group's X and dY are requested before the
 // current one is combined and written.
-template <typename T, typename TW, bool VEC, int VPT, int ROWS, bool LN>
+template <typename T, typename TW, int EV, int VPT, int ROWS, bool LN>
 __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
-  using A = Acc<T, VEC>;
+  using A = Acc<T, EV>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
   __shared__ __align__(16) float red[RED_FLOATS];
@@ -355,7 +356,7 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
   if (!a.dw) write_ws_header(a.header, a.row_groups, N);
 
   // the weight stays packed (half the registers for bf16), unpacked at use
-  WAcc<T, TW, VEC> rw[VPT];
+  WAcc<T, TW, EV> rw[VPT];
   float accw[VPT][E], accb[LN ? VPT : 1][E];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
@@ -493,9 +494,9 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
     for (int k = 0; k < VPT; ++k) {
       const int v = tid + k * SPLIT_LB;
       if (v < nin) {
-        WAcc<T, TW, VEC>::store(dw + (int64_t)v * E, accw[k]);
+        WAcc<T, TW, EV>::store(dw + (int64_t)v * E, accw[k]);
         if constexpr (LN)
-          if (db) WAcc<T, TW, VEC>::store(db + (int64_t)v * E, accb[k]);
+          if (db) WAcc<T, TW, EV>::store(db + (int64_t)v * E, accb[k]);
       }
     }
   } else {
@@ -522,53 +523,100 @@ namespace {
 #define DLN_SPLIT_FWD_MENU(X) X(1) X(2) X(4)
 #define DLN_SPLIT_BWD_MENU(X) X(1, 1) X(1, 2) X(1, 4) X(2, 1) X(2, 2) X(2, 4) X(4, 1) X(4, 2)
 #define DLN_SPLIT_SCALAR_VPT 8
+// 8- and 4-byte accesses: the full-width chunk (4 accesses of 16 bytes per thread) in narrower
+// accesses, one row at a time in the backward's second pass
+#define DLN_SPLIT_NARROW_VPT_FULL 4
+
+template <typename T, int EV, int V>
+hipError_t split_stats_launch(const FwdArgs &a, bool resid, hipStream_t s) {
+  const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
+  return resid ? launch(split_stats_kernel<T, EV, V, true>, grid, block, s, a)
+               : launch(split_stats_kernel<T, EV, V, false>, grid, block, s, a);
+}
+
+template <typename T, typename TW, int EV, int V>
+hipError_t split_fwd_pair(const FwdArgs &a, hipStream_t s) {
+  const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
+  hipError_t e = split_stats_launch<T, EV, V>(a, a.r != nullptr, s);
+  if (e == hipSuccess) e = launch(split_norm_kernel<T, TW, EV, V>, grid, block, s, a);
+  return e;
+}
+
+template <typename T, typename TW, int EV, int V, int R>
+hipError_t split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
+  const dim3 grid1((unsigned)(a.M * a.chunks)), grid2((unsigned)p.grid), block(SPLIT_LB);
+  hipError_t e;
+  if (a.layernorm) {
+    e = launch(split_bwd_partial_kernel<T, TW, EV, V, true>, grid1, block, s, a);
+    if (e == hipSuccess)
+      e = launch(split_bwd_dx_kernel<T, TW, EV, V, R, true>, grid2, block, s, a);
+  } else {
+    e = launch(split_bwd_partial_kernel<T, TW, EV, V, false>, grid1, block, s, a);
+    if (e == hipSuccess)
+      e = launch(split_bwd_dx_kernel<T, TW, EV, V, R, false>, grid2, block, s, a);
+  }
+  return e;
+}
+
+// The statistics pass of every width: hipErrorInvalidConfiguration when the plan's width and
+// chunk have no kernel (reported as NORM_ERR_UNSUPPORTED by the callers).
+template <typename T>
+hipError_t split_stats_any(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s,
+                           bool *found) {
+  constexpr int F = full_epv<T>();
+  *found = true;
+  if (p.epv == F) {
+#define X(V)                                                                                    \
+  if (p.vpt == V) return split_stats_launch<T, F, V>(a, resid, s);
+    DLN_SPLIT_FWD_MENU(X)
+#undef X
+  } else if (p.epv == F / 2 && p.vpt == DLN_SPLIT_NARROW_VPT_FULL * 2) {
+    return split_stats_launch<T, F / 2, DLN_SPLIT_NARROW_VPT_FULL * 2>(a, resid, s);
+  } else if (p.epv == F / 4 && p.vpt == DLN_SPLIT_NARROW_VPT_FULL * 4) {
+    if constexpr (F / 4 >= 2)
+      return split_stats_launch<T, F / 4, DLN_SPLIT_NARROW_VPT_FULL * 4>(a, resid, s);
+  } else if (p.epv == 1 && p.vpt == DLN_SPLIT_SCALAR_VPT) {
+    return split_stats_launch<T, 1, DLN_SPLIT_SCALAR_VPT>(a, resid, s);
+  }
+  *found = false;
+  return hipErrorInvalidConfiguration;
+}
 
 template <typename T, typename TW>
 norm_status_t split_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
-  const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
-  const bool resid = a.r != nullptr;
-  bool found = false;
-  hipError_t e = hipSuccess;
-  auto keep = [&e](hipError_t r) { e = e == hipSuccess ? r : e; };
-  if (p.vector) {
+  constexpr int F = full_epv<T>();
+  constexpr int NV = DLN_SPLIT_NARROW_VPT_FULL;
+  hipError_t e = hipErrorInvalidConfiguration;
+  bool found = true;
+  if (p.epv == F) {
+    found = false;
 #define X(V)                                                                                    \
   if (!found && p.vpt == V) {                                                                   \
     found = true;                                                                               \
-    keep(resid ? launch(split_stats_kernel<T, true, V, true>, grid, block, s, a)                \
-               : launch(split_stats_kernel<T, true, V, false>, grid, block, s, a));             \
-    keep(launch(split_norm_kernel<T, TW, true, V>, grid, block, s, a));                         \
+    e = split_fwd_pair<T, TW, F, V>(a, s);                                                      \
   }
     DLN_SPLIT_FWD_MENU(X)
 #undef X
-  } else if (p.vpt == DLN_SPLIT_SCALAR_VPT) {
-    found = true;
-    constexpr int V = DLN_SPLIT_SCALAR_VPT;
-    keep(resid ? launch(split_stats_kernel<T, false, V, true>, grid, block, s, a)
-               : launch(split_stats_kernel<T, false, V, false>, grid, block, s, a));
-    keep(launch(split_norm_kernel<T, TW, false, V>, grid, block, s, a));
+  } else if (p.epv == F / 2 && p.vpt == NV * 2) {
+    e = split_fwd_pair<T, TW, F / 2, NV * 2>(a, s);
+  } else if (p.epv == F / 4 && p.vpt == NV * 4) {
+    if constexpr (F / 4 >= 2)
+      e = split_fwd_pair<T, TW, F / 4, NV * 4>(a, s);
+    else
+      found = false;
+  } else if (p.epv == 1 && p.vpt == DLN_SPLIT_SCALAR_VPT) {
+    e = split_fwd_pair<T, TW, 1, DLN_SPLIT_SCALAR_VPT>(a, s);
+  } else {
+    found = false;
   }
   if (!found) return NORM_ERR_UNSUPPORTED;
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 
-template <typename T, typename TW, bool VEC, int V, int R>
-hipError_t split_bwd_pair(const Plan &p, const BwdArgs &a, hipStream_t s) {
-  const dim3 grid1((unsigned)(a.M * a.chunks)), grid2((unsigned)p.grid), block(SPLIT_LB);
-  hipError_t e;
-  if (a.layernorm) {
-    e = launch(split_bwd_partial_kernel<T, TW, VEC, V, true>, grid1, block, s, a);
-    if (e == hipSuccess)
-      e = launch(split_bwd_dx_kernel<T, TW, VEC, V, R, true>, grid2, block, s, a);
-  } else {
-    e = launch(split_bwd_partial_kernel<T, TW, VEC, V, false>, grid1, block, s, a);
-    if (e == hipSuccess)
-      e = launch(split_bwd_dx_kernel<T, TW, VEC, V, R, false>, grid2, block, s, a);
-  }
-  return e;
-}
-
 template <typename T, typename TW>
 norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
+  constexpr int F = full_epv<T>();
+  constexpr int NV = DLN_SPLIT_NARROW_VPT_FULL;
   // statistics of the forward, when not supplied: chunk stats, then one combine per row
   if (a.rstd == nullptr) {
     FwdArgs f{};
@@ -582,39 +630,35 @@ norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
     f.layernorm = a.layernorm;
     f.eps = a.eps;
     f.inv_n = a.inv_n;
-    const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
     bool found = false;
-    hipError_t e = hipSuccess;
-    if (p.vector) {
-#define X(V)                                                                                    \
-  if (!found && p.vpt == V) {                                                                   \
-    found = true;                                                                               \
-    e = launch(split_stats_kernel<T, true, V, false>, grid, block, s, f);                      \
-  }
-      DLN_SPLIT_FWD_MENU(X)
-#undef X
-    } else if (p.vpt == DLN_SPLIT_SCALAR_VPT) {
-      found = true;
-      e = launch(split_stats_kernel<T, false, DLN_SPLIT_SCALAR_VPT, false>, grid, block, s, f);
-    }
+    hipError_t e = split_stats_any<T>(p, f, false, s, &found);
     if (!found) return NORM_ERR_UNSUPPORTED;
     if (e == hipSuccess)
-      e = launch(split_finalize_stats_kernel, dim3((unsigned)a.M), block, s, a, p.epv);
+      e = launch(split_finalize_stats_kernel, dim3((unsigned)a.M), dim3(SPLIT_LB), s, a, p.epv);
     if (e != hipSuccess) return NORM_ERR_HIP;
   }
-  bool found = false;
-  hipError_t e = hipSuccess;
-  if (p.vector) {
+  bool found = true;
+  hipError_t e = hipErrorInvalidConfiguration;
+  if (p.epv == F) {
+    found = false;
 #define X(V, R)                                                                                 \
   if (!found && p.vpt == V && p.rows == R) {                                                    \
     found = true;                                                                               \
-    e = split_bwd_pair<T, TW, true, V, R>(p, a, s);                                             \
+    e = split_bwd_pair<T, TW, F, V, R>(p, a, s);                                                \
   }
     DLN_SPLIT_BWD_MENU(X)
 #undef X
-  } else if (p.vpt == DLN_SPLIT_SCALAR_VPT && p.rows == 1) {
-    found = true;
-    e = split_bwd_pair<T, TW, false, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
+  } else if (p.epv == F / 2 && p.vpt == NV * 2 && p.rows == 1) {
+    e = split_bwd_pair<T, TW, F / 2, NV * 2, 1>(p, a, s);
+  } else if (p.epv == F / 4 && p.vpt == NV * 4 && p.rows == 1) {
+    if constexpr (F / 4 >= 2)
+      e = split_bwd_pair<T, TW, F / 4, NV * 4, 1>(p, a, s);
+    else
+      found = false;
+  } else if (p.epv == 1 && p.vpt == DLN_SPLIT_SCALAR_VPT && p.rows == 1) {
+    e = split_bwd_pair<T, TW, 1, DLN_SPLIT_SCALAR_VPT, 1>(p, a, s);
+  } else {
+    found = false;
   }
   if (!found) return NORM_ERR_UNSUPPORTED;
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;

@@ -1,583 +1,12 @@
-// norm_team.hip -- row-resident forward and fused backward kernels, and the column reduction.
+// norm_team.hip -- the team kernels' full-width (16-byte) and element-wise instantiations and
+// their dispatch, the column reduction of the backward's partials, and a zero fill.
 //
-// A "team" of threads owns one row at a time and keeps the whole row in registers:
-//   wave scheme : a team is one 64-lane wavefront; sums stay inside the wavefront (DPP), no LDS
-//                 and no barrier. Used for short rows.
-//   block scheme: a team is several wavefronts; wavefront sums meet in LDS behind one barrier.
-// Kernels are persistent: each workgroup walks row groups with a grid stride, so the weight
-// (and bias) of a thread's columns are loaded once and, in the backward, the dW/dB column sums
-// of all rows a workgroup visits accumulate in registers.
-//
-// Method (web page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
-// matsubara.tec.br):
-//   para. 3  -- forward: reduction along the contiguous dimension, then pointwise work;
-//   para. 5  -- short reduction dimensions are reduced without a loop, the row held on chip;
-//   para. 7  -- backward gradients dX, dW, dB;
-//   paras. 8-10 -- one fused pass produces dX and per-block partial column sums (no atomics;
-//               several rows per block), and a second pass consolidates the partials;
-//   para. 12 -- several rows in flight per team (the software-pipelining knob).
-// Memory: every [M, N] element moves through 16-byte coalesced accesses, exactly once per pass
-// (web page "Otimização de Performance de GPU: Maximizando Throughput para Treinamento e
-// Inferência de LLM", introl.com, sections on memory bandwidth and on kernel fusion), and all
-// arithmetic is fp32 (same page, section on mixed precision).
-#include "norm_device.hpp"
-#include "norm_internal.hpp"
+// The kernels themselves (norm_team_kernels.hpp) hold a row per team of threads in registers;
+// 8- and 4-byte accesses for rows whose length or pointers rule out 16-byte ones are
+// instantiated in norm_team_narrow.hip.
+#include "norm_team_kernels.hpp"
 
 namespace dln {
-
-// Partial column sums of the backward are merged across the teams of a workgroup through
-// LDS in blocks of this many floats.
-constexpr int MERGE_FLOATS = 4096;
-
-struct TeamGeom {
-  int tt;       // threads per team
-  int team;     // team index in the workgroup
-  int t;        // thread index in the team
-  int teams;    // teams per workgroup
-  int waves;    // wavefronts per team
-  int wave0;    // first wavefront of this team in the workgroup
-  int wave;     // this thread's wavefront in the workgroup
-  int lane;
-};
-
-template <bool WAVE> __device__ __forceinline__ TeamGeom team_geom(int team_threads) {
-  TeamGeom g;
-  const int tid = threadIdx.x;
-  g.tt = WAVE ? 64 : team_threads;
-  g.team = tid / g.tt;
-  g.t = tid - g.team * g.tt;
-  g.teams = blockDim.x / g.tt;
-  g.waves = g.tt >> 6;
-  g.wave = tid >> 6;
-  g.wave0 = g.team * g.waves;
-  g.lane = tid & 63;
-  return g;
-}
-
-// Row groups of this workgroup: first, first + step, ... below end. Interleaved: group g goes
-// to workgroup g mod grid. Blocked: workgroup b takes the contiguous groups
-// [b * per, (b + 1) * per), per = ceil(groups / grid), so its rows stream from one region.
-struct GroupRange {
-  int64_t first, step, end;
-};
-__device__ __forceinline__ GroupRange group_range(int64_t M, int64_t rows_per_group,
-                                                  int blocked) {
-  const int64_t groups = (M + rows_per_group - 1) / rows_per_group;
-  if (!blocked) return GroupRange{(int64_t)blockIdx.x, (int64_t)gridDim.x, groups};
-  const int64_t per = (groups + gridDim.x - 1) / gridDim.x;
-  const int64_t first = (int64_t)blockIdx.x * per;
-  return GroupRange{first, 1, first + per < groups ? first + per : groups};
-}
-
-// ---- forward ------------------------------------------------------------------------------
-
-template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool RESID>
-__global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_threads) {
-  using A = Acc<T, VEC>;
-  using raw = typename A::raw;
-  constexpr int E = A::EPV;
-  __shared__ __align__(16) float red[RED_FLOATS];
-  const TeamGeom gm = team_geom<WAVE>(team_threads);
-  const int nacc = a.nacc;
-  const int64_t M = a.M;
-  const int64_t N = a.N;
-  const T *__restrict__ X = static_cast<const T *>(a.x);
-  const T *__restrict__ Rr = static_cast<const T *>(a.r);
-  const TW *__restrict__ W = static_cast<const TW *>(a.w);
-  const TW *__restrict__ Bb = static_cast<const TW *>(a.b);
-  T *__restrict__ Y = static_cast<T *>(a.y);
-  T *__restrict__ H = static_cast<T *>(a.h);
-
-  float w[VPT][E], b[VPT][E];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int v = gm.t + k * gm.tt;
-    WAcc<T, TW, VEC> rw, rb;
-    rw.zero();
-    rb.zero();
-    if (v < nacc) {
-      rw.load(W + (int64_t)v * E);
-      if (Bb) rb.load(Bb + (int64_t)v * E);
-    }
-    rw.get(w[k]);
-    rb.get(b[k]);
-  }
-
-  const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
-  // Software pipeline: the next row group's loads are issued before the current group is
-  // reduced and written, so every wavefront keeps requests in flight across its barriers.
-  raw px[ROWS][VPT], pr[ROWS][RESID ? VPT : 1];
-  auto issue = [&](int64_t g, bool live) {
-    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const bool rv = live && row0 + r < M;
-      const int64_t base = (row0 + r) * N;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int v = gm.t + k * gm.tt;
-        px[r][k] = A::zero();
-        if (RESID) pr[r][k] = A::zero();
-        if (rv && v < nacc) {
-          px[r][k] = A::ld(X + base + (int64_t)v * E);
-          if (RESID) pr[r][k] = A::ld(Rr + base + (int64_t)v * E);
-        }
-      }
-    }
-  };
-  int slot = 0;
-  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
-  int64_t g = gr.first;
-  issue(g, g < gr.end);
-#pragma unroll
-  for (int k = 0; k < VPT; ++k)
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      settle(w[k][e]);
-      settle(b[k][e]);
-    }
-  for (; g < gr.end; g += gr.step) {
-    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
-    float x[ROWS][VPT][E];
-    {
-      raw rx[ROWS][VPT];
-      raw rr[ROWS][RESID ? VPT : 1];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r)
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-          rx[r][k] = px[r][k];
-          if (RESID) rr[r][k] = pr[r][k];
-        }
-      issue(g + gr.step, g + gr.step < gr.end);
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        const bool rv = row0 + r < M;
-        const int64_t base = (row0 + r) * N;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-          A::unpack(rx[r][k], x[r][k]);
-          if (RESID) {
-            // h = R + X in fp32, rounded once to the storage type; the norm sees the rounded h
-            float f[E];
-            A::unpack(rr[r][k], f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) f[e] += x[r][k][e];
-            const raw hp = A::pack(f);
-            A::unpack(hp, x[r][k]);
-            const int v = gm.t + k * gm.tt;
-            if (rv && v < nacc) A::st(H + base + (int64_t)v * E, hp);
-          }
-        }
-      }
-    }
-
-    // Statistics. LayerNorm: a first pass gives mean1; a second pass sums d = x - mean1 and
-    // d^2. x - mean1 is exact for rows whose values sit near their mean, so sum(d)/N is an
-    // accurate correction even when |mean| >> std and mean1 itself is off by many fp32 ulps of
-    // the variance scale; the normalised value is formed as (x - mean1) - delta.
-    float mean1[ROWS], delta[ROWS], rstd[ROWS];
-    if (a.layernorm) {
-      float s[ROWS];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k)
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc += x[r][k][e];
-        s[r] = acc;
-      }
-      team_sum<ROWS, (WAVE ? 1 : LB / 64)>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-      slot ^= 1;
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) mean1[r] = mul_rn(s[r], a.inv_n);
-      float qc[2 * ROWS];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float q = 0.0f, c = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k) {
-          const bool in = gm.t + k * gm.tt < nacc;
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float d = in ? x[r][k][e] - mean1[r] : 0.0f;
-            q += d * d;
-            c += d;
-          }
-        }
-        qc[r] = q;
-        qc[ROWS + r] = c;
-      }
-      team_sum<2 * ROWS, (WAVE ? 1 : LB / 64)>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-      slot ^= 1;
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        delta[r] = qc[ROWS + r] * a.inv_n;
-        const float var = fmaxf(qc[r] * a.inv_n - delta[r] * delta[r], 0.0f);
-        rstd[r] = rsqrt_f32(var + a.eps);
-      }
-    } else {
-      float q[ROWS];
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float acc = 0.0f;
-#pragma unroll
-        for (int k = 0; k < VPT; ++k)
-#pragma unroll
-          for (int e = 0; e < E; ++e) acc += x[r][k][e] * x[r][k][e];
-        q[r] = acc;
-      }
-      team_sum<ROWS, (WAVE ? 1 : LB / 64)>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-      slot ^= 1;
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        mean1[r] = 0.0f;
-        delta[r] = 0.0f;
-        rstd[r] = rsqrt_f32(q[r] * a.inv_n + a.eps);
-      }
-    }
-
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const int64_t row = row0 + r;
-      if (row >= M) continue;
-      const int64_t base = row * N;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int v = gm.t + k * gm.tt;
-        if (v < nacc) {
-          float y[E];
-#pragma unroll
-          for (int e = 0; e < E; ++e)
-            y[e] = ((x[r][k][e] - mean1[r]) - delta[r]) * rstd[r] * w[k][e] + b[k][e];
-          A::st(Y + base + (int64_t)v * E, A::pack(y));
-        }
-      }
-      if (gm.t == 0) {
-        if (a.mean) a.mean[row] = mean1[r] + delta[r];
-        if (a.rstd) a.rstd[row] = rstd[r];
-      }
-    }
-  }
-}
-
-// ---- backward -----------------------------------------------------------------------------
-
-// Per element: unpack x, dY (and W once per row group), d = x - m, g = dY * W, the row sums;
-// after the team sum, with per-row constants a = rstd, nd = -delta * rstd,
-// B = -rstd * c2, C = -rstd * c1: xhat = d * a + nd, dX = g * a + (xhat * B + C), and the
-// dW / dB column sums. d, g and dY stay in registers across the team sum when the thread holds
-// at most 16 elements of the row group (else they are formed again from the packed data).
-template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE, bool LN>
-__global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_threads) {
-  using A = Acc<T, VEC>;
-  using raw = typename A::raw;
-  constexpr int E = A::EPV;
-  constexpr int MAXW = WAVE ? 1 : LB / 64;
-  constexpr bool KEEP = VPT * ROWS * E <= 16;
-  __shared__ __align__(16) float red[RED_FLOATS];
-  __shared__ float merge[MERGE_FLOATS];
-  const TeamGeom gm = team_geom<WAVE>(team_threads);
-  const int nacc = a.nacc;
-  const int64_t M = a.M;
-  const int64_t N = a.N;
-  const T *__restrict__ X = static_cast<const T *>(a.x);
-  const T *__restrict__ DY = static_cast<const T *>(a.dy);
-  const T *__restrict__ DH = static_cast<const T *>(a.dh);
-  const TW *__restrict__ W = static_cast<const TW *>(a.w);
-  T *__restrict__ DX = static_cast<T *>(a.dx);
-  T *__restrict__ DR = static_cast<T *>(a.dr);
-  const bool have_stats = a.rstd != nullptr;
-  write_ws_header(a.header, a.partials, N);
-
-  // the weight stays in its storage format (half the registers for bf16), unpacked at use
-  WAcc<T, TW, VEC> rw[VPT];
-  float accw[VPT][E], accb[LN ? VPT : 1][E];
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) {
-    const int v = gm.t + k * gm.tt;
-    rw[k].zero();
-    if (v < nacc) rw[k].load(W + (int64_t)v * E);
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      accw[k][e] = 0.0f;
-      if constexpr (LN) accb[k][e] = 0.0f;
-    }
-  }
-
-  const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
-  // Software pipeline: X, dY and the saved statistics of the next row group are requested
-  // before this group's reductions and stores.
-  raw px[ROWS][VPT], pdy[ROWS][VPT];
-  float pm[ROWS], pr[ROWS];
-  auto issue = [&](int64_t g, bool live) {
-    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const bool rv = live && row0 + r < M;
-      const int64_t base = (row0 + r) * N;
-      pm[r] = 0.0f;
-      pr[r] = 0.0f;
-      if (have_stats) {
-        const int64_t row = rv ? row0 + r : M - 1;
-        if constexpr (LN) pm[r] = a.mean[row];
-        pr[r] = a.rstd[row];
-      }
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int v = gm.t + k * gm.tt;
-        px[r][k] = A::zero();
-        pdy[r][k] = A::zero();
-        if (rv && v < nacc) {
-          px[r][k] = A::ld(X + base + (int64_t)v * E);
-          pdy[r][k] = A::ld(DY + base + (int64_t)v * E);
-        }
-      }
-    }
-  };
-  int slot = 0;
-  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
-  int64_t g = gr.first;
-  issue(g, g < gr.end);
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) rw[k].settle();
-  for (; g < gr.end; g += gr.step) {
-    const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
-    raw rx[ROWS][VPT], rdy[ROWS][VPT];
-    // m: the row mean the forward saved (LayerNorm), or a first-pass mean when recomputing.
-    // The reduction below also sums x - m, so the exact mean m + delta is used for xhat.
-    float m[ROWS], rstd[ROWS];
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      m[r] = pm[r];
-      rstd[r] = pr[r];
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        rx[r][k] = px[r][k];
-        rdy[r][k] = pdy[r][k];
-      }
-    }
-    issue(g + gr.step, g + gr.step < gr.end);
-    if (!have_stats) {
-      // recompute the forward statistics from the register-resident rows
-      if constexpr (LN) {
-        float s[ROWS];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          float acc = 0.0f;
-#pragma unroll
-          for (int k = 0; k < VPT; ++k) {
-            float f[E];
-            A::unpack(rx[r][k], f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc += f[e];
-          }
-          s[r] = acc;
-        }
-        team_sum<ROWS, MAXW>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-        slot ^= 1;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) m[r] = mul_rn(s[r], a.inv_n);
-        float qc[2 * ROWS];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          float q = 0.0f, c = 0.0f;
-#pragma unroll
-          for (int k = 0; k < VPT; ++k) {
-            if (gm.t + k * gm.tt < nacc) { // rows past M are all zeros
-              float f[E];
-              A::unpack(rx[r][k], f);
-#pragma unroll
-              for (int e = 0; e < E; ++e) {
-                const float d = f[e] - m[r];
-                q = __builtin_fmaf(d, d, q);
-                c += d;
-              }
-            }
-          }
-          qc[r] = q;
-          qc[ROWS + r] = c;
-        }
-        team_sum<2 * ROWS, MAXW>(qc, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-        slot ^= 1;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          const float dl = qc[ROWS + r] * a.inv_n;
-          rstd[r] = rsqrt_f32(fmaxf(qc[r] * a.inv_n - dl * dl, 0.0f) + a.eps);
-        }
-      } else {
-        float q[ROWS];
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          float acc = 0.0f;
-#pragma unroll
-          for (int k = 0; k < VPT; ++k) {
-            float f[E];
-            A::unpack(rx[r][k], f);
-#pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
-          }
-          q[r] = acc;
-        }
-        team_sum<ROWS, MAXW>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-        slot ^= 1;
-#pragma unroll
-        for (int r = 0; r < ROWS; ++r) {
-          m[r] = 0.0f;
-          rstd[r] = rsqrt_f32(q[r] * a.inv_n + a.eps);
-        }
-      }
-    }
-
-    // One team sum per row group. With g = dY * W and d = x - m:
-    //   LayerNorm: S0 = sum(g*d), S1 = sum(g), S2 = sum(d); delta = S2/N,
-    //              c1 = S1/N, c2 = rstd * (S0 - delta*S1)/N  (= mean(g * xhat))
-    //   RMSNorm  : S0 = sum(g*x), c2 = rstd * S0/N
-    constexpr int NV = LN ? 3 * ROWS : ROWS;
-    float sums[NV];
-#pragma unroll
-    for (int i = 0; i < NV; ++i) sums[i] = 0.0f;
-    float kd[KEEP ? ROWS : 1][KEEP ? VPT : 1][E], kg[KEEP ? ROWS : 1][KEEP ? VPT : 1][E],
-        kdy[KEEP ? ROWS : 1][KEEP ? VPT : 1][E];
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      float wf[E];
-      rw[k].get(wf);
-      const bool in = gm.t + k * gm.tt < nacc;
-#pragma unroll
-      for (int r = 0; r < ROWS; ++r) {
-        float xf[E], df[E];
-        A::unpack(rx[r][k], xf);
-        A::unpack(rdy[r][k], df);
-        float d[E], gg[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          d[e] = LN ? xf[e] - m[r] : xf[e];
-          gg[e] = df[e] * wf[e];
-          // columns past N hold x = dY = 0: g * d adds nothing there
-          sums[r] = __builtin_fmaf(gg[e], d[e], sums[r]);
-          if constexpr (LN) sums[ROWS + r] += gg[e];
-        }
-        if constexpr (LN) {
-          if (in) {
-#pragma unroll
-            for (int e = 0; e < E; ++e) sums[2 * ROWS + r] += d[e];
-          }
-        }
-        if constexpr (KEEP) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            kd[KEEP ? r : 0][KEEP ? k : 0][e] = d[e];
-            kg[KEEP ? r : 0][KEEP ? k : 0][e] = gg[e];
-            kdy[KEEP ? r : 0][KEEP ? k : 0][e] = df[e];
-          }
-        }
-      }
-    }
-    team_sum<NV, MAXW>(sums, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
-    slot ^= 1;
-
-#pragma unroll
-    for (int r = 0; r < ROWS; ++r) {
-      const int64_t row = row0 + r;
-      if (row >= M) continue; // rows past M add nothing to dW / dB and write nothing
-      const int64_t base = row * N;
-      const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
-      const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
-      const float c2 =
-          LN ? rstd[r] * (sums[r] - delta * sums[ROWS + r]) * a.inv_n : rstd[r] * sums[r] * a.inv_n;
-      const float ra = rstd[r], nd = -delta * rstd[r];
-      const float cB = -rstd[r] * c2, cC = -rstd[r] * c1;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int v = gm.t + k * gm.tt;
-        if (v >= nacc) continue; // columns past N: nothing to add or write
-        float d[E], gg[E], df[E];
-        if constexpr (KEEP) {
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            d[e] = kd[KEEP ? r : 0][KEEP ? k : 0][e];
-            gg[e] = kg[KEEP ? r : 0][KEEP ? k : 0][e];
-            df[e] = kdy[KEEP ? r : 0][KEEP ? k : 0][e];
-          }
-        } else {
-          float xf[E], wf[E];
-          A::unpack(rx[r][k], xf);
-          A::unpack(rdy[r][k], df);
-          rw[k].get(wf);
-#pragma unroll
-          for (int e = 0; e < E; ++e) {
-            d[e] = LN ? xf[e] - m[r] : xf[e];
-            gg[e] = df[e] * wf[e];
-          }
-        }
-        float dx[E];
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float xh = __builtin_fmaf(d[e], ra, nd);
-          dx[e] = __builtin_fmaf(gg[e], ra, __builtin_fmaf(xh, cB, cC));
-          accw[k][e] = __builtin_fmaf(df[e], xh, accw[k][e]);
-          if constexpr (LN) accb[k][e] += df[e];
-        }
-        const int64_t off = base + (int64_t)v * E;
-        if (DH) {
-          float hf[E];
-          A::unpack(A::ld(DH + off), hf);
-#pragma unroll
-          for (int e = 0; e < E; ++e) dx[e] += hf[e];
-        }
-        const raw p = A::pack(dx);
-        A::st(DX + off, p);
-        if (DR) A::st(DR + off, p);
-      }
-    }
-  }
-
-  // Column partials of this workgroup: sum over its teams (fixed order) and write one row
-  // per quantity into the workspace.
-  float *pw = a.colpart + (int64_t)blockIdx.x * N;
-  float *pb = a.colpart + ((int64_t)a.partials + blockIdx.x) * N;
-  if (gm.teams == 1) {
-#pragma unroll
-    for (int k = 0; k < VPT; ++k) {
-      const int v = gm.t + k * gm.tt;
-      if (v < nacc) {
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          pw[(int64_t)v * E + e] = accw[k][e];
-          if constexpr (LN) pb[(int64_t)v * E + e] = accb[k][e];
-        }
-      }
-    }
-    return;
-  }
-  const int cols_per_block = MERGE_FLOATS / gm.teams;
-  for (int q = 0; q < (LN ? 2 : 1); ++q) {
-    float *dst = q == 0 ? pw : pb;
-    for (int64_t c0 = 0; c0 < N; c0 += cols_per_block) {
-      const int64_t c1 = c0 + cols_per_block < N ? c0 + cols_per_block : N;
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        const int v = gm.t + k * gm.tt;
-#pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const int64_t col = (int64_t)v * E + e;
-          if (v < nacc && col >= c0 && col < c1)
-            merge[gm.team * cols_per_block + (int)(col - c0)] =
-                q == 0 ? accw[k][e] : accb[LN ? k : 0][e];
-        }
-      }
-      __syncthreads();
-      for (int64_t col = c0 + threadIdx.x; col < c1; col += blockDim.x) {
-        float s = 0.0f;
-        for (int tm = 0; tm < gm.teams; ++tm) s += merge[tm * cols_per_block + (int)(col - c0)];
-        dst[col] = s;
-      }
-      __syncthreads();
-    }
-  }
-}
 
 // ---- column reduction ------------------------------------------------------------------------
 
@@ -728,26 +157,6 @@ __global__ __launch_bounds__(256) void zero_kernel(unsigned char *p, size_t n) {
 
 namespace {
 
-template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
-hipError_t fwd_launch(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s) {
-  dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
-  if (resid)
-    return launch(team_fwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
-                  p.team_threads);
-  return launch(team_fwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
-                p.team_threads);
-}
-
-template <typename T, typename TW, bool VEC, int VPT, int ROWS, int LB, bool WAVE>
-hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
-  dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
-  if (a.layernorm)
-    return launch(team_bwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
-                  p.team_threads);
-  return launch(team_bwd_kernel<T, TW, VEC, VPT, ROWS, LB, WAVE, false>, grid, block, s, a,
-                p.team_threads);
-}
-
 // The menu of compiled shapes. Wave scheme: workgroups of 256 threads (4 one-wave teams).
 // Block scheme: teams of up to LB threads. Entries are (VPT, ROWS, LB).
 #define DLN_WAVE_MENU(X)                                                                        \
@@ -771,7 +180,7 @@ norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, TW, true, V, R, L, true>(p, a, resid, s);                                 \
+    e = fwd_launch<T, TW, full_epv<T>(), V, R, L, true>(p, a, resid, s);                           \
   }
       DLN_WAVE_MENU(X)
 #undef X
@@ -779,7 +188,7 @@ norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, TW, false, V, R, L, true>(p, a, resid, s);                                \
+    e = fwd_launch<T, TW, 1, V, R, L, true>(p, a, resid, s);                                \
   }
       DLN_WAVE_MENU_SCALAR(X)
 #undef X
@@ -789,7 +198,7 @@ norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, TW, true, V, R, L, false>(p, a, resid, s);                                \
+    e = fwd_launch<T, TW, full_epv<T>(), V, R, L, false>(p, a, resid, s);                          \
   }
       DLN_BLOCK_MENU(X)
 #undef X
@@ -797,7 +206,7 @@ norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = fwd_launch<T, TW, false, V, R, L, false>(p, a, resid, s);                               \
+    e = fwd_launch<T, TW, 1, V, R, L, false>(p, a, resid, s);                               \
   }
       DLN_BLOCK_MENU_SCALAR(X)
 #undef X
@@ -817,7 +226,7 @@ norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, TW, true, V, R, L, true>(p, a, s);                                        \
+    e = bwd_launch<T, TW, full_epv<T>(), V, R, L, true>(p, a, s);                                  \
   }
       DLN_WAVE_MENU(X)
 #undef X
@@ -825,7 +234,7 @@ norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, TW, false, V, R, L, true>(p, a, s);                                       \
+    e = bwd_launch<T, TW, 1, V, R, L, true>(p, a, s);                                       \
   }
       DLN_WAVE_MENU_SCALAR(X)
 #undef X
@@ -835,7 +244,7 @@ norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, TW, true, V, R, L, false>(p, a, s);                                       \
+    e = bwd_launch<T, TW, full_epv<T>(), V, R, L, false>(p, a, s);                                 \
   }
       DLN_BLOCK_MENU(X)
 #undef X
@@ -843,7 +252,7 @@ norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
 #define X(V, R, L)                                                                              \
   if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
     found = true;                                                                               \
-    e = bwd_launch<T, TW, false, V, R, L, false>(p, a, s);                                      \
+    e = bwd_launch<T, TW, 1, V, R, L, false>(p, a, s);                                      \
   }
       DLN_BLOCK_MENU_SCALAR(X)
 #undef X
@@ -857,6 +266,7 @@ norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
 
 norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                               hipStream_t s) {
+  if (p.scale > 1) return launch_team_fwd_narrow(p, dtype, a, s);
   switch (dtype) {
   case NORM_F32: return team_fwd_typed<float, float>(p, a, s);
   case NORM_BF16: return team_fwd_typed<bf16_bits, bf16_bits>(p, a, s);
@@ -867,6 +277,7 @@ norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &
 
 norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                               hipStream_t s) {
+  if (p.scale > 1) return launch_team_bwd_narrow(p, dtype, a, s);
   switch (dtype) {
   case NORM_F32: return team_bwd_typed<float, float>(p, a, s);
   case NORM_BF16: return team_bwd_typed<bf16_bits, bf16_bits>(p, a, s);

@@ -49,7 +49,7 @@ class NormError(RuntimeError):
 
 
 class _Plan(ctypes.Structure):
-    _fields_ = [("scheme", ctypes.c_int32), ("vector", ctypes.c_int32),
+    _fields_ = [("scheme", ctypes.c_int32), ("access_bytes", ctypes.c_int32),
                 ("elems_per_access", ctypes.c_int32), ("threads", ctypes.c_int32),
                 ("team_threads", ctypes.c_int32), ("accesses_per_thread", ctypes.c_int32),
                 ("rows_per_iter", ctypes.c_int32), ("row_order", ctypes.c_int32),
@@ -218,12 +218,13 @@ def norm_workspace_size(kind, dtype, pass_, M, N, residual=False):
     return out.value
 
 
-def norm_plan(kind, dtype, pass_, M, N, residual=False, aligned=True, cu_count=256):
-    """The dispatcher's plan for a shape, as a dict (pure host logic, no GPU needed)."""
+def norm_plan(kind, dtype, pass_, M, N, residual=False, align=16, cu_count=256):
+    """The dispatcher's plan for a shape, as a dict (pure host logic, no GPU needed). align:
+    the largest power of two (up to 16) dividing every tensor's address."""
     p = _Plan()
     dt = DTYPES[dtype] if isinstance(dtype, torch.dtype) else int(dtype)
     st = lib().norm_plan(_kind(kind), dt, int(pass_), M, N, int(bool(residual)),
-                         int(bool(aligned)), int(cu_count), ctypes.byref(p))
+                         int(align), int(cu_count), ctypes.byref(p))
     _raise(st, "norm_plan")
     return {name: getattr(p, name) for name, _ in _Plan._fields_}
 

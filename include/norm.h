@@ -37,8 +37,12 @@
  *     Nothing synchronises the host. Device faults surface at the caller's next sync.
  *   - Output buffers must not overlap input buffers (in place is rejected), except that dR
  *     may be the same pointer as dX.
- *   - Rows whose start is not 16-byte aligned, or N not a multiple of the 16-byte vector
- *     width (8 bf16 / 4 fp32), run on a slower element-wise path; results are the same.
+ *   - Accesses are the widest of 16, 8 and 4 bytes (at least two elements) that divides the
+ *     row length in bytes and that the alignment common to every tensor pointer allows. An
+ *     access of E elements needs E * element size bytes; with fp32 W, B, dW, dB beside bf16
+ *     activations it needs min(16, 4 E) bytes, for the weights read with it. Rows of an odd
+ *     number of elements, or pointers aligned to one element only, run on a slower
+ *     element-wise path. Results are the same on every path up to rounding order.
  *   - Arguments are checked before anything is launched; a failed check returns an error and
  *     launches nothing. M == 0 returns NORM_OK with no launch. No C++ exception crosses the
  *     ABI and the library never aborts the process.
@@ -160,7 +164,7 @@ norm_status_t norm_workspace_size(norm_kind_t kind, norm_dtype_t dtype, norm_pas
 /* Description of the launch plan for a shape, for tests and tuning. */
 typedef struct {
   int32_t scheme;         /* norm_scheme_t */
-  int32_t vector;         /* 1: 16-byte accesses; 0: element-wise path */
+  int32_t access_bytes;   /* bytes per access: 16, 8 or 4, or the element size (element-wise) */
   int32_t elems_per_access;
   int32_t threads;        /* threads per workgroup */
   int32_t team_threads;   /* threads that share one row (64 for the wave scheme) */
@@ -176,11 +180,13 @@ typedef struct {
 } norm_plan_t;
 
 /*
- * The plan the dispatcher picks for a shape on a device with cu_count compute units, with
- * aligned != 0 meaning every pointer is 16-byte aligned. Pure host logic: needs no GPU.
+ * The plan the dispatcher picks for a shape on a device with cu_count compute units. align is
+ * the largest power of two, up to 16, that divides the address of every tensor of the call
+ * (16 for buffers straight from an allocator; values above 16 count as 16; 0 or 1 when
+ * unknown). Pure host logic: needs no GPU.
  */
 norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
-                        int64_t N, int residual, int aligned, int cu_count, norm_plan_t *out);
+                        int64_t N, int residual, int align, int cu_count, norm_plan_t *out);
 
 /* Tuning overrides (process-wide; for tests and offline tuning; not thread-safe with
  * concurrent calls). Value -1 restores the default. */

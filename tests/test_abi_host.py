@@ -133,6 +133,7 @@ def test_tuning_rejects_bad_values():
 # ---- the dispatcher --------------------------------------------------------------------------
 
 BF, F = torch.bfloat16, torch.float32
+BF32W = nl.BF16_F32W
 
 
 def test_scheme_boundaries():
@@ -151,12 +152,29 @@ def test_scheme_boundaries():
     assert nl.norm_plan(0, BF, 1, 16384, 8200)["scheme"] == nl.SCHEME_SPLIT
 
 
-def test_vector_path_needs_alignment_and_width():
-    assert nl.norm_plan(0, BF, 0, 64, 4096)["vector"] == 1
-    assert nl.norm_plan(0, BF, 0, 64, 4096, aligned=False)["vector"] == 0
-    assert nl.norm_plan(0, BF, 0, 64, 4100)["vector"] == 0   # 4100 % 8 != 0
-    assert nl.norm_plan(0, F, 0, 64, 4100)["vector"] == 1    # 4100 % 4 == 0
-    assert nl.norm_plan(0, F, 0, 64, 4100)["elems_per_access"] == 4
+def test_access_width_follows_row_length_and_alignment():
+    def width(dt, N, align=16, pass_=0):
+        p = nl.norm_plan(0, dt, pass_, 64, N, align=align)
+        assert p["access_bytes"] == p["elems_per_access"] * (4 if dt == F else 2)
+        return p["access_bytes"]
+    # bf16: 16 bytes when N % 8 == 0, else 8 (N % 4 == 0), else 4 (N even), else one element
+    assert [width(BF, N) for N in (4096, 4100, 4098, 4097)] == [16, 8, 4, 2]
+    # fp32: 16 bytes when N % 4 == 0, else 8 (N even), else one element
+    assert [width(F, N) for N in (4096, 4098, 4097)] == [16, 8, 4]
+    # the pointers' common alignment caps the width
+    assert [width(BF, 4096, a) for a in (16, 8, 4, 2, 1, 0)] == [16, 8, 4, 2, 2, 2]
+    assert [width(F, 4096, a) for a in (16, 8, 4)] == [16, 8, 4]
+    # fp32 weights beside bf16 activations: 4 bf16 need 16-byte weight loads, 2 need 8 bytes
+    assert [width(BF32W, N) for N in (4096, 4100, 4098)] == [16, 8, 4]
+    assert [width(BF32W, 4100, a) for a in (16, 8, 4)] == [8, 4, 2]
+    # the narrow paths size their teams like the 16-byte path: same scheme, same threads
+    for pass_ in (0, 1):
+        full = nl.norm_plan(0, BF, pass_, 16384, 4096)
+        for N in (4100, 4098):
+            narrow = nl.norm_plan(0, BF, pass_, 16384, N)
+            assert narrow["scheme"] == full["scheme"] == nl.SCHEME_BLOCK
+            assert narrow["team_threads"] * narrow["accesses_per_thread"] * \
+                narrow["elems_per_access"] >= N
 
 
 @pytest.mark.parametrize("dt", [BF, F])
@@ -165,10 +183,11 @@ def test_vector_path_needs_alignment_and_width():
 @pytest.mark.parametrize("M", [1, 3, 4, 256, 16384, 65536])
 @pytest.mark.parametrize("pass_", [0, 1])
 def test_plan_covers_every_row_and_column(dt, N, M, pass_):
-    for aligned in (True, False):
-        p = nl.norm_plan(0, dt, pass_, M, N, aligned=aligned)
+    for align in (16, 8, 4, 2, 1):
+        p = nl.norm_plan(0, dt, pass_, M, N, align=align)
         epv = p["elems_per_access"]
-        nacc = -(-N // epv) if not p["vector"] else N // epv
+        assert N % epv == 0 and p["access_bytes"] <= max(align, 4 if dt == F else 2)
+        nacc = N // epv
         assert p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024
         assert p["grid"] >= 1
         if p["scheme"] == nl.SCHEME_SPLIT:

@@ -130,10 +130,11 @@ def test_mixed_weight_type_residual(dr):
 
 
 def test_mixed_weight_type_unaligned():
-    # N % 8 != 0: the element-wise path with fp32 weights
+    # N % 8 != 0: 8-byte (N % 4 == 0), 4-byte (N even) and element-wise (N odd) accesses with
+    # fp32 weights
     for kind in ("layernorm", "rmsnorm"):
-        for N in (100, 4100):
-            _say("mixed weights element-wise %s N=%d" % (kind, N))
+        for N in (100, 4100, 102, 4098, 101, 4097):
+            _say("mixed weights narrow or element-wise %s N=%d" % (kind, N))
             w = dataclasses.replace(_small(kind, "bf16", 9, N, seed=N), wdtype="f32")
             run_and_check(w)
 
@@ -160,6 +161,62 @@ def test_split_direct_dw_unaligned_outputs(wdtype):
     # the same column sums in another order: within the dW/dB tolerance of each other
     check_colsums("dW", dW.double().cpu().numpy(), ref_dw.double().cpu().numpy(), "f32")
     check_colsums("dB", dB.double().cpu().numpy(), ref_db.double().cpu().numpy(), "f32")
+
+
+# ---- 8- and 4-byte accesses ---------------------------------------------------------------------
+
+# Even row lengths that are not a multiple of the 16-byte vector (bf16: N % 8 != 0; fp32:
+# N % 4 != 0), across the wave, block and split schemes.
+NARROW_N = [2, 6, 10, 12, 100, 1002, 1004, 1026, 1028, 2050, 4098, 4100, 5122, 7170, 8194, 8196,
+            16386, 16388, 20002, 262146]
+
+
+def _narrow_cases():
+    out = []
+    for N in NARROW_N:
+        for kind in ("layernorm", "rmsnorm"):
+            for dt, wdt in (("bf16", None), ("bf16", "f32"), ("f32", None)):
+                if dt == "f32" and N % 4 == 0:
+                    continue  # 16-byte accesses
+                out.append((kind, dt, wdt, 129 if N <= 20002 else 9, N))
+    return out
+
+
+def _access_bytes(kind, dt, wdt, M, N, residual=False, align=16):
+    code = nl.BF16_F32W if wdt == "f32" else inputs.TORCH_DTYPES[dt]
+    return nl.norm_plan(kind, code, 0, M, N, residual, align=align)["access_bytes"]
+
+
+@pytest.mark.parametrize("kind,dt,wdt,M,N", _narrow_cases(), ids=lambda v: str(v))
+def test_narrow_access_widths(kind, dt, wdt, M, N):
+    width = _access_bytes(kind, dt, wdt, M, N)
+    assert width == (8 if (dt == "f32" or N % 4 == 0) else 4)
+    _say("narrow %d-byte %s %s w=%s %dx%d" % (width, kind, dt, wdt, M, N))
+    w = dataclasses.replace(_small(kind, dt, M, N, seed=M + N), wdtype=wdt)
+    run_and_check(w)
+    run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
+
+
+@pytest.mark.parametrize("N", [1002, 4098, 4100, 7170, 8194, 16386])
+@pytest.mark.parametrize("kind", ["rmsnorm", "layernorm"])
+def test_narrow_residual(kind, N):
+    _say("narrow residual %s N=%d" % (kind, N))
+    w = _small(kind, "bf16", 65, N, seed=N, x=inputs.normal(0, 0.5), r=inputs.normal(0, 1))
+    run_and_check(w, dr="alias", dh=True)
+    run_and_check(dataclasses.replace(w, seed=N + 1), dr="separate")
+
+
+@pytest.mark.parametrize("N", [4098, 4100, 8196])
+@pytest.mark.parametrize("knob", [dict(scheme=nl.SCHEME_SPLIT), dict(scheme=nl.SCHEME_BLOCK),
+                                  dict(team_threads=1024), dict(grid_per_cu=1)],
+                         ids=lambda k: str(k))
+def test_narrow_forced(knob, N):
+    if knob.get("scheme") == nl.SCHEME_BLOCK and N * 2 > 1024 * 16:
+        pytest.skip("longer than a backward team's registers (1024 16-byte accesses)")
+    for kind in ("layernorm", "rmsnorm"):
+        _say("narrow knob %s %s N=%d" % (knob, kind, N))
+        with tuned(**knob):
+            run_and_check(_small(kind, "bf16", 77, N, seed=N))
 
 
 # ---- tuning knobs ----------------------------------------------------------------------------
@@ -216,49 +273,62 @@ def test_backward_without_saved_stats(kind, N):
     run_and_check(_small(kind, "bf16", 37, N, seed=N), stats=False)
 
 
-# ---- element-wise path: unaligned rows ------------------------------------------------------------
+# ---- pointer alignment sets the access width -------------------------------------------------
 
-@pytest.mark.parametrize("dt", ["bf16", "f32"])
+# (dtype, weight dtype, shift of every tensor in elements of its own type, expected access bytes)
+# A shift of s elements leaves a pointer aligned to s * element size bytes. The plan sees the
+# alignment common to all pointers; fp32 weights beside bf16 activations need min(16, 4 E)
+# bytes for an access of E elements, so 4-byte alignment leaves them element-wise and 8-byte
+# alignment allows two elements per access.
+SHIFTS = [("bf16", None, 1, 2), ("bf16", None, 2, 4), ("bf16", None, 4, 8),
+          ("f32", None, 1, 4), ("f32", None, 2, 8),
+          ("bf16", "f32", 1, 2), ("bf16", "f32", 2, 2), ("bf16", "f32", 4, 4)]
+
+
+@pytest.mark.parametrize("dt,wdt,shift,width", SHIFTS, ids=lambda v: str(v))
 @pytest.mark.parametrize("N", [100, 1000, 4096, 9000])
-def test_unaligned_pointers_take_elementwise_path(dt, N):
-    """Tensors placed one element past a 16-byte boundary run on the element-wise path and
-    still match the oracle."""
+def test_pointer_alignment_sets_width(dt, wdt, shift, width, N):
+    """Every tensor placed `shift` elements past a 16-byte boundary: the plan takes the widest
+    access that alignment allows, and the results still match the oracle."""
     kind = "layernorm"
-    w = _small(kind, dt, 61, N, seed=N)
+    w = dataclasses.replace(_small(kind, dt, 61, N, seed=N), wdtype=wdt)
     t = inputs.make(w)
-    tdt = inputs.TORCH_DTYPES[dt]
 
     def shifted(src):
-        buf = torch.empty(src.numel() + 16, dtype=tdt, device="cuda")
-        v = buf[1:1 + src.numel()].view(src.shape)
+        buf = torch.empty(src.numel() + 16, dtype=src.dtype, device="cuda")
+        v = buf[shift:shift + src.numel()].view(src.shape)
         v.copy_(src.to("cuda"))
         return v
 
     X, W, B, dY = (shifted(t[k]) for k in ("X", "W", "B", "dY"))
-    assert X.data_ptr() % 16 != 0
-    p = nl.norm_plan(kind, tdt, 0, 61, N, aligned=False)
-    assert p["vector"] == 0
-    Y = shifted(torch.zeros(61, N, dtype=tdt))
+    align = X.data_ptr() & -X.data_ptr()
+    assert align == shift * X.element_size()
+    # row length and alignment together: N = 100 holds 4-element accesses at most
+    expect = min(width, (N & -N) * X.element_size())
+    if expect < 4:
+        expect = X.element_size()
+    assert _access_bytes(kind, dt, wdt, 61, N, align=min(align, W.data_ptr() & -W.data_ptr())) \
+        == expect
+    _say("pointer shift %d (%s, w=%s) N=%d: %d-byte accesses" % (shift, dt, wdt, N, expect))
+    Y = shifted(torch.zeros(61, N, dtype=X.dtype))
     mean = torch.empty(61, dtype=torch.float32, device="cuda")
     rstd = torch.empty(61, dtype=torch.float32, device="cuda")
-    ws = nl.workspace(kind, tdt, nl.PASS_FWD, 61, N)
+    ws = nl.workspace(kind, X.dtype, nl.PASS_FWD, 61, N)
     nl.norm_fwd(kind, X, None, W, B, w.eps, Y, None, mean, rstd, ws)
-    dX = shifted(torch.zeros(61, N, dtype=tdt))
-    dW = shifted(torch.zeros(N, dtype=tdt))
-    dB = shifted(torch.zeros(N, dtype=tdt))
-    wsb = nl.workspace(kind, tdt, nl.PASS_BWD, 61, N)
+    dX = shifted(torch.zeros(61, N, dtype=X.dtype))
+    dW = shifted(torch.zeros(N, dtype=W.dtype))
+    dB = shifted(torch.zeros(N, dtype=W.dtype))
+    wsb = nl.workspace(kind, X.dtype, nl.PASS_BWD, 61, N)
     nl.norm_bwd(kind, X, dY, None, W, mean, rstd, w.eps, dX, None, dW, dB, wsb)
     bits = {k: inputs.host_bits(t[k]) for k in ("X", "W", "B", "dY")}
     eps = float(np.float32(w.eps))
-    f = oracle.fwd(oracle.LAYERNORM, oracle.F32 if dt == "f32" else oracle.BF16, bits["X"],
-                   bits["W"], bits["B"], eps=eps)
-    g = oracle.bwd(oracle.LAYERNORM, oracle.F32 if dt == "f32" else oracle.BF16, bits["X"],
-                   bits["dY"], bits["W"], eps=eps)
+    code = {"f32": oracle.F32, "bf16": oracle.BF16}[dt] if wdt is None else oracle.BF16_F32W
+    f = oracle.fwd(oracle.LAYERNORM, code, bits["X"], bits["W"], bits["B"], eps=eps)
+    g = oracle.bwd(oracle.LAYERNORM, code, bits["X"], bits["dY"], bits["W"], eps=eps)
     check_values("Y", Y.double().cpu().numpy(), f["y"], dt)
     check_values("dX", dX.double().cpu().numpy(), g["dx"], dt)
-    check_colsums("dW", dW.double().cpu().numpy(), g["dw"], dt)
-    check_colsums("dB", dB.double().cpu().numpy(), g["db"], dt)
-
+    check_colsums("dW", dW.double().cpu().numpy(), g["dw"], wdt or dt)
+    check_colsums("dB", dB.double().cpu().numpy(), g["db"], wdt or dt)
 
 # ---- numerically hard rows ---------------------------------------------------------------------
 
@@ -435,7 +505,12 @@ def test_workspace_too_small_is_rejected():
     M, N = 1024, 4096
     X = torch.randn(M, N, device="cuda").to(torch.bfloat16)
     W = torch.ones(N, device="cuda", dtype=torch.bfloat16)
-    need = nl.norm_workspace_size("layernorm", torch.bfloat16, nl.PASS_BWD, M, N)
+    # what this call's plan needs (norm_workspace_size covers every pointer alignment and can be
+    # larger)
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    need = nl.norm_plan("layernorm", torch.bfloat16, nl.PASS_BWD, M, N,
+                        cu_count=cu)["workspace_bytes"]
+    assert need <= nl.norm_workspace_size("layernorm", torch.bfloat16, nl.PASS_BWD, M, N)
     small = torch.empty(need - 256, dtype=torch.uint8, device="cuda")
     with pytest.raises(nl.NormError) as e:
         nl.norm_bwd("layernorm", X, X, None, W, None, None, 1e-5, torch.empty_like(X), None,
