@@ -99,6 +99,7 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
 norm_status_t run_fused(const dln::Plan &p, norm_dtype_t dtype, const dln::BwdArgs &a,
                         hipStream_t s) {
   if (p.scheme == NORM_SCHEME_SPLIT) return dln::launch_split_bwd(p, dtype, a, s);
+  if (p.scheme == NORM_SCHEME_LOOP) return dln::launch_looped_bwd(p, dtype, a, s);
   return dln::launch_team_bwd(p, dtype, a, s);
 }
 

@@ -87,6 +87,9 @@ norm_status_t launch_team_fwd_narrow(const Plan &p, norm_dtype_t dtype, const Fw
                                      hipStream_t s);
 norm_status_t launch_team_bwd_narrow(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                                      hipStream_t s);
+// rows of 1024-2048 full-width accesses: two sweeps per row, the second from the L2
+norm_status_t launch_looped_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
+                                hipStream_t s);
 norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                                hipStream_t s);
 norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,

@@ -16,7 +16,7 @@ LIB_PATH = os.path.join(_HERE, "libnorm.so")
 LAYERNORM, RMSNORM = 0, 1
 F32, BF16, BF16_F32W = 0, 1, 2
 PASS_FWD, PASS_BWD = 0, 1
-SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT = -1, 0, 1, 2
+SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT, SCHEME_LOOP = -1, 0, 1, 2, 3
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
 TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
 N_TUNE_KEYS = 8

@@ -86,7 +86,10 @@ typedef enum {
   NORM_SCHEME_AUTO = -1, /* tuning value only: let the dispatcher choose */
   NORM_SCHEME_WAVE = 0,  /* one row per 64-lane wavefront, registers only (short rows) */
   NORM_SCHEME_BLOCK = 1, /* one row per team of waves, cross-wave sums through LDS */
-  NORM_SCHEME_SPLIT = 2  /* one row over several workgroups, two passes (very long rows) */
+  NORM_SCHEME_SPLIT = 2, /* one row over several workgroups, two passes (very long rows) */
+  NORM_SCHEME_LOOP = 3   /* backward only: one row per workgroup in two sweeps, the second
+                            from the L2 (rows of 1024-2048 16-byte accesses); forcing it
+                            leaves the forward to the dispatcher */
 } norm_scheme_t;
 
 typedef void *norm_stream_t; /* a hipStream_t */

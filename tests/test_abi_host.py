@@ -147,9 +147,28 @@ def test_scheme_boundaries():
     assert nl.norm_plan(1, BF, 1, 4, 4194304)["scheme"] == nl.SCHEME_SPLIT
     assert nl.norm_plan(0, BF, 0, 16384, 16384)["scheme"] == nl.SCHEME_BLOCK
     assert nl.norm_plan(0, BF, 0, 16384, 16392)["scheme"] == nl.SCHEME_SPLIT
-    # the backward holds twice the state per element: its block rows end at 8192 bf16
+    # the backward holds twice the state per element: its block rows end at 8192 bf16; the
+    # looped backward (two sweeps, the second from the L2) takes rows up to 16384 bf16 / 8192
+    # fp32 with 16- or 8-byte accesses, and the split scheme what is longer
     assert nl.norm_plan(0, BF, 1, 16384, 8192)["scheme"] == nl.SCHEME_BLOCK
-    assert nl.norm_plan(0, BF, 1, 16384, 8200)["scheme"] == nl.SCHEME_SPLIT
+    assert nl.norm_plan(0, BF, 1, 16384, 8200)["scheme"] == nl.SCHEME_LOOP
+    assert nl.norm_plan(0, BF, 1, 16384, 16384)["scheme"] == nl.SCHEME_LOOP
+    assert nl.norm_plan(0, BF, 1, 16384, 16380)["scheme"] == nl.SCHEME_LOOP   # 8-byte
+    assert nl.norm_plan(0, BF, 1, 16384, 16382)["scheme"] == nl.SCHEME_SPLIT  # 4-byte
+    assert nl.norm_plan(0, BF, 1, 16384, 16392)["scheme"] == nl.SCHEME_SPLIT
+    assert nl.norm_plan(0, F, 1, 16384, 8192)["scheme"] == nl.SCHEME_LOOP
+    assert nl.norm_plan(0, F, 1, 16384, 8196)["scheme"] == nl.SCHEME_SPLIT
+    assert nl.norm_plan(0, BF, 1, 16384, 4095)["scheme"] == nl.SCHEME_BLOCK   # element-wise
+    assert nl.norm_plan(0, BF, 1, 16384, 4097)["scheme"] == nl.SCHEME_SPLIT   # element-wise
+    # forcing the looped scheme leaves the forward to the dispatcher
+    try:
+        nl.norm_set_tuning(nl.TUNE_SCHEME, nl.SCHEME_LOOP)
+        assert nl.norm_plan(0, BF, 0, 64, 4096)["scheme"] == nl.SCHEME_BLOCK
+        assert nl.norm_plan(0, BF, 1, 64, 4096)["scheme"] == nl.SCHEME_LOOP
+        with pytest.raises(nl.NormError):
+            nl.norm_plan(0, BF, 1, 64, 4098)    # 4-byte accesses: no looped kernel
+    finally:
+        nl.norm_set_tuning(nl.TUNE_SCHEME, -1)
 
 
 def test_access_width_follows_row_length_and_alignment():

@@ -75,6 +75,7 @@ FORCED = [
     ("wave", nl.SCHEME_WAVE, [8, 200, 512, 1024, 2048, 4096]),
     ("block", nl.SCHEME_BLOCK, [8, 64, 200, 1000, 1024, 4104, 16384]),
     ("split", nl.SCHEME_SPLIT, [8, 200, 1024, 4096, 8200, 20000]),
+    ("loop", nl.SCHEME_LOOP, [8, 200, 1000, 4100, 4104, 12288, 16384]),
 ]
 
 
@@ -88,6 +89,8 @@ def test_forced_scheme(name, scheme, Ns, dt, kind):
             continue  # longer than one wavefront's registers
         if name == "block" and N * esize > 1024 * 16:
             continue  # longer than a backward team's registers (1024 16-byte accesses)
+        if name == "loop" and (N * esize > 2048 * 16 or N * esize % 8):
+            continue  # beyond 512 threads x 4 16-byte accesses, or narrower than 8 bytes
         for M in (1, 5, 300):
             _say("forced %s %s %s %dx%d" % (name, kind, dt, M, N))
             with tuned(scheme=scheme):
@@ -208,11 +211,14 @@ def test_narrow_residual(kind, N):
 
 @pytest.mark.parametrize("N", [4098, 4100, 8196])
 @pytest.mark.parametrize("knob", [dict(scheme=nl.SCHEME_SPLIT), dict(scheme=nl.SCHEME_BLOCK),
-                                  dict(team_threads=1024), dict(grid_per_cu=1)],
+                                  dict(scheme=nl.SCHEME_LOOP), dict(team_threads=1024),
+                                  dict(grid_per_cu=1)],
                          ids=lambda k: str(k))
 def test_narrow_forced(knob, N):
     if knob.get("scheme") == nl.SCHEME_BLOCK and N * 2 > 1024 * 16:
         pytest.skip("longer than a backward team's registers (1024 16-byte accesses)")
+    if knob.get("scheme") == nl.SCHEME_LOOP and N % 4:
+        pytest.skip("the looped backward has no 4-byte kernels")
     for kind in ("layernorm", "rmsnorm"):
         _say("narrow knob %s %s N=%d" % (knob, kind, N))
         with tuned(**knob):
@@ -231,6 +237,7 @@ KNOBS = [
     dict(rows=1), dict(row_order=1), dict(row_order=1, rows=1),
     dict(row_order=1, grid_per_cu=16),         # more workgroups than row groups: some idle
     dict(row_order=1, team_threads=256, teams=4),
+    dict(scheme=nl.SCHEME_LOOP), dict(scheme=nl.SCHEME_LOOP, grid_per_cu=3),
 ]
 
 
@@ -238,7 +245,8 @@ KNOBS = [
 @pytest.mark.parametrize("kind,dt,M,N", [("layernorm", "bf16", 1000, 4096),
                                         ("rmsnorm", "bf16", 777, 1024),
                                         ("rmsnorm", "f32", 333, 7168),
-                                        ("layernorm", "f32", 65, 520)])
+                                        ("layernorm", "f32", 65, 520),
+                                        ("layernorm", "bf16", 300, 12288)])
 def test_tuning_knobs(knob, kind, dt, M, N):
     _say("knob %s %s %s %dx%d" % (knob, kind, dt, M, N))
     with tuned(**knob):
@@ -250,7 +258,7 @@ def test_tuning_knobs(knob, kind, dt, M, N):
 @pytest.mark.parametrize("dr", ["none", "alias", "separate"])
 @pytest.mark.parametrize("dh", [False, True])
 @pytest.mark.parametrize("kind", ["rmsnorm", "layernorm"])
-@pytest.mark.parametrize("N", [512, 7168, 20000])
+@pytest.mark.parametrize("N", [512, 7168, 12288, 20000])
 def test_residual(dr, dh, kind, N):
     _say("residual %s N=%d dr=%s dh=%s" % (kind, N, dr, dh))
     w = _small(kind, "bf16", 129, N, seed=N, x=inputs.normal(0, 0.5), r=inputs.normal(0, 1))
@@ -267,7 +275,7 @@ def test_residual_full_shape_sample():
 # ---- statistics recomputed in the backward -----------------------------------------------------
 
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
-@pytest.mark.parametrize("N", [256, 4096, 300000])
+@pytest.mark.parametrize("N", [256, 4096, 12288, 300000])
 def test_backward_without_saved_stats(kind, N):
     _say("no saved stats %s N=%d" % (kind, N))
     run_and_check(_small(kind, "bf16", 37, N, seed=N), stats=False)
