@@ -175,6 +175,14 @@ def long_rows(kind: str, M: int, N: int) -> Workload:
 LONG_ROW_SHAPES = ((256, 262144), (4, 4194304))
 
 
+# Beyond the shapes above: a row length that rules out 16-byte accesses (LayerNorm 16384 x
+# 4100, 8-byte accesses) and a hidden size whose backward rows no longer fit a team's
+# registers (RMSNorm 16384 x 16384, the looped backward), with the same draws as their
+# neighbours.
+LN_BF16_16384x4100 = LN_BF16_16384x4096.with_shape(16384, 4100, "layernorm_bf16_16384x4100")
+RMS_BF16_16384x16384 = rms_hidden(16384, M=16384)
+
+
 def all_workloads():
     """Every full-size workload, in a fixed order."""
     out = [RMS_F32_2048x1024, LN_BF16_16384x4096, LN_BF16_F32W_16384x4096]
@@ -182,4 +190,5 @@ def all_workloads():
     out.append(RESID_RMS_BF16_65536x7168)
     for M, N in LONG_ROW_SHAPES:
         out += [long_rows("layernorm", M, N), long_rows("rmsnorm", M, N)]
+    out += [LN_BF16_16384x4100, RMS_BF16_16384x16384]
     return out
