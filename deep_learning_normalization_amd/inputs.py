@@ -20,7 +20,7 @@ import torch
 
 OFF_X, OFF_W, OFF_B, OFF_DY, OFF_R, OFF_PERM, OFF_DH = 0, 1, 2, 3, 4, 5, 6
 
-TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16}
+TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
 
 @dataclass(frozen=True)
@@ -122,11 +122,12 @@ def make(w: Workload, M: Optional[int] = None) -> dict:
 
 
 def host_bits(t: Optional[torch.Tensor]):
-    """The raw storage bits of a CPU tensor as numpy: uint16 for bf16, float32 for fp32."""
+    """The raw storage bits of a CPU tensor as numpy: uint16 for bf16 and fp16, float32 for
+    fp32."""
     if t is None:
         return None
     t = t.detach().contiguous().cpu()
-    if t.dtype == torch.bfloat16:
+    if t.dtype in (torch.bfloat16, torch.float16):
         return t.view(torch.int16).numpy().view(np.uint16)
     if t.dtype == torch.float32:
         return t.numpy()

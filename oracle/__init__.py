@@ -3,6 +3,6 @@
 Only the test suite, the smoke check and the benchmark's CPU-baseline leg may import this
 package. The HIP library never does.
 """
-from .oracle import (BF16, BF16_F32W, F32, LAYERNORM, RMSNORM, Oracle, act_dtype,  # noqa: F401
-                     weight_dtype, bwd, decode, default,
-                     fwd, num_threads, round_bf16, set_num_threads)
+from .oracle import (BF16, BF16_F32W, F16, F16_F32W, F32, LAYERNORM, RMSNORM,  # noqa: F401
+                     Oracle, act_dtype, weight_dtype, bwd, decode, default, fwd, num_threads,
+                     round_bf16, round_f16, set_num_threads)

@@ -7,7 +7,7 @@
  * library; the two are compared element by element on identical input bits.
  *
  * What is computed is the textbook definition of each operation, evaluated in double
- * precision on the exact input values (bf16 or fp32 bit patterns widened exactly):
+ * precision on the exact input values (bf16, fp16 or fp32 bit patterns widened exactly):
  *
  *   Sources (web pages):
  *   [P1] "PyTorch atinge desempenho SOTA em normalização com torch.compile"
@@ -48,9 +48,10 @@
 #endif
 
 enum { OR_LAYERNORM = 0, OR_RMSNORM = 1 };
-/* dtype: the storage type of every tensor, or OR_BF16_F32W = bf16 activations and gradients
- * (X, R, dY, dH) with fp32 weight and bias (their gradients are then fp32 too). */
-enum { OR_F32 = 0, OR_BF16 = 1, OR_BF16_F32W = 2 };
+/* dtype: the storage type of every tensor, or OR_BF16_F32W / OR_F16_F32W = bf16 / fp16
+ * activations and gradients (X, R, dY, dH) with fp32 weight and bias (their gradients are then
+ * fp32 too). */
+enum { OR_F32 = 0, OR_BF16 = 1, OR_BF16_F32W = 2, OR_F16 = 3, OR_F16_F32W = 4 };
 
 enum {
   OR_OK = 0,
@@ -68,6 +69,20 @@ static double or_bf16_bits_to_double(uint16_t b) {
   return (double)f;
 }
 
+/* IEEE binary16: 1 sign bit, 5 exponent bits (bias 15), 10 fraction bits. Normal values are
+ * (1024 + f) * 2^(e - 25), subnormals f * 2^-24; e = 31 holds the infinities and NaNs. */
+static double or_f16_bits_to_double(uint16_t b) {
+  const int sign = b >> 15, e = (b >> 10) & 31, f = b & 1023;
+  double v;
+  if (e == 31)
+    v = f ? NAN : INFINITY;
+  else if (e == 0)
+    v = ldexp((double)f, -24);
+  else
+    v = ldexp((double)(1024 + f), e - 25);
+  return sign ? -v : v;
+}
+
 static double or_load(int dtype, const void *base, int64_t idx) {
   if (dtype == OR_F32) {
     float f;
@@ -76,7 +91,7 @@ static double or_load(int dtype, const void *base, int64_t idx) {
   }
   uint16_t b;
   memcpy(&b, (const char *)base + idx * 2, sizeof b);
-  return or_bf16_bits_to_double(b);
+  return dtype == OR_F16 ? or_f16_bits_to_double(b) : or_bf16_bits_to_double(b);
 }
 
 /* Round a double to the nearest bf16 value, ties to even, in one step from the double
@@ -95,13 +110,47 @@ static double or_round_to_bf16(double v) {
   return v < 0 ? -out : out;
 }
 
+/* Round a double to the nearest fp16 value, ties to even, in one step from the double. fp16
+ * keeps 11 significant bits; the smallest subnormal step is 2^-24 and the largest finite value
+ * 65504 = (2 - 2^-10) * 2^15; what rounds beyond it becomes infinity. */
+static double or_round_to_f16(double v) {
+  if (v != v || v == 0.0 || isinf(v)) return v;
+  double a = fabs(v);
+  int e;
+  (void)frexp(a, &e);     /* a = m * 2^e with m in [0.5, 1) */
+  int q = e - 11;         /* weight of the last kept bit */
+  if (q < -24) q = -24;   /* subnormal range: fixed step */
+  double k = nearbyint(ldexp(a, -q));
+  double out = ldexp(k, q);
+  if (out > 65504.0) out = INFINITY;
+  return v < 0 ? -out : out;
+}
+
 /* storage type of the activations, and of the weight and bias, for a call's dtype */
-static int or_act(int dtype) { return dtype == OR_BF16_F32W ? OR_BF16 : dtype; }
-static int or_wt(int dtype) { return dtype == OR_BF16_F32W ? OR_F32 : dtype; }
+static int or_act(int dtype) {
+  return dtype == OR_BF16_F32W ? OR_BF16 : dtype == OR_F16_F32W ? OR_F16 : dtype;
+}
+static int or_wt(int dtype) {
+  return (dtype == OR_BF16_F32W || dtype == OR_F16_F32W) ? OR_F32 : dtype;
+}
 
 static double or_round_to_dtype(int dtype, double v) {
   if (dtype == OR_F32) return (double)(float)v; /* C conversion: round to nearest even */
+  if (dtype == OR_F16) return or_round_to_f16(v);
   return or_round_to_bf16(v);
+}
+
+/* bit pattern of the fp16 nearest to v (used by tests to pin the rounding rule) */
+static uint16_t or_f16_bits(double v) {
+  if (v != v) return (uint16_t)0x7E00;
+  const double r = or_round_to_f16(v);
+  const uint16_t sign = signbit(r) ? 0x8000 : 0;
+  const double a = fabs(r);
+  if (isinf(a)) return sign | 0x7C00;
+  if (a < ldexp(1.0, -14)) return sign | (uint16_t)ldexp(a, 24); /* subnormal or zero */
+  int e;
+  const double m = frexp(a, &e); /* a = m * 2^e, m in [0.5, 1): biased exponent e + 14 */
+  return sign | (uint16_t)((e + 14) << 10) | (uint16_t)(ldexp(m, 11) - 1024.0);
 }
 
 /* bit pattern of the bf16 nearest to v (used by tests to pin the rounding rule) */
@@ -118,7 +167,7 @@ static uint16_t or_bf16_bits(double v) {
 static int or_check(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64_t r1,
                     double eps) {
   if (kind != OR_LAYERNORM && kind != OR_RMSNORM) return OR_BAD_ARG;
-  if (dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_BF16_F32W) return OR_BAD_ARG;
+  if (dtype < OR_F32 || dtype > OR_F16_F32W) return OR_BAD_ARG;
   if (M < 0 || N <= 0) return OR_BAD_ARG;
   if (r0 < 0 || r1 < r0 || r1 > M) return OR_BAD_ARG;
   if (!(eps >= 0.0)) return OR_BAD_ARG;
@@ -335,7 +384,8 @@ int oracle_bwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64
 
 /* Widen count values of the given dtype to double. */
 int oracle_decode(int dtype, const void *bits, int64_t count, double *out) {
-  if ((dtype != OR_F32 && dtype != OR_BF16) || count < 0 || (count && (!bits || !out)))
+  if ((dtype != OR_F32 && dtype != OR_BF16 && dtype != OR_F16) || count < 0 ||
+      (count && (!bits || !out)))
     return OR_BAD_ARG;
   for (int64_t k = 0; k < count; ++k) out[k] = or_load(dtype, bits, k);
   return OR_OK;
@@ -345,6 +395,13 @@ int oracle_decode(int dtype, const void *bits, int64_t count, double *out) {
 int oracle_round_bf16(const double *in, int64_t count, uint16_t *out) {
   if (count < 0 || (count && (!in || !out))) return OR_BAD_ARG;
   for (int64_t k = 0; k < count; ++k) out[k] = or_bf16_bits(in[k]);
+  return OR_OK;
+}
+
+/* Round count doubles to fp16 bit patterns (nearest, ties to even). */
+int oracle_round_f16(const double *in, int64_t count, uint16_t *out) {
+  if (count < 0 || (count && (!in || !out))) return OR_BAD_ARG;
+  for (int64_t k = 0; k < count; ++k) out[k] = or_f16_bits(in[k]);
   return OR_OK;
 }
 

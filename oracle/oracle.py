@@ -2,8 +2,8 @@
 
 TEST INFRASTRUCTURE. Only the test suite, the smoke check and the benchmark's CPU-baseline
 leg import this module. It shares nothing with the HIP library: inputs are passed as the same
-bit patterns the device receives (bf16 as uint16, fp32 as float32) and every result comes back
-as unrounded float64.
+bit patterns the device receives (bf16 and fp16 as uint16, fp32 as float32) and every result
+comes back as unrounded float64.
 
 Definitions followed (web page "PyTorch atinge desempenho SOTA em normalização com
 torch.compile", matsubara.tec.br): para. 2 for what LayerNorm and RMSNorm compute, para. 3 for
@@ -17,19 +17,19 @@ import numpy as np
 from . import build as _build
 
 LAYERNORM, RMSNORM = 0, 1
-# storage types: every tensor fp32, every tensor bf16, or bf16 activations and gradients with
-# fp32 weight and bias
-F32, BF16, BF16_F32W = 0, 1, 2
+# storage types: every tensor fp32, bf16 or fp16, or bf16 / fp16 activations and gradients
+# with fp32 weight and bias
+F32, BF16, BF16_F32W, F16, F16_F32W = 0, 1, 2, 3, 4
 
 
 def act_dtype(dtype):
     """Storage type of X, R, dY, dH for a call's dtype."""
-    return BF16 if dtype == BF16_F32W else dtype
+    return {BF16_F32W: BF16, F16_F32W: F16}.get(dtype, dtype)
 
 
 def weight_dtype(dtype):
     """Storage type of W and B (and of dW, dB) for a call's dtype."""
-    return F32 if dtype == BF16_F32W else dtype
+    return F32 if dtype in (BF16_F32W, F16_F32W) else dtype
 
 
 class Oracle:
@@ -52,6 +52,8 @@ class Oracle:
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [dp, i64, vp]
         lib.oracle_round_bf16.restype = ctypes.c_int
+        lib.oracle_round_f16.argtypes = [dp, i64, vp]
+        lib.oracle_round_f16.restype = ctypes.c_int
         lib.oracle_num_threads.argtypes = []
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
@@ -71,6 +73,9 @@ class Oracle:
 
     def round_bf16(self, values):
         return _round_bf16(self.lib, values)
+
+    def round_f16(self, values):
+        return _round_f16(self.lib, values)
 
     def num_threads(self):
         return self.lib.oracle_num_threads()
@@ -156,7 +161,8 @@ def _bwd(lib, kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw):
 
 
 def _decode(lib, dtype, bits):
-    """Widen an array of bf16 (uint16) or fp32 bits to float64 with the oracle's decoder."""
+    """Widen an array of bf16 or fp16 (uint16) or fp32 bits to float64 with the oracle's
+    decoder."""
     a = _bits(bits, dtype)
     out = np.empty(a.shape, np.float64)
     if lib.oracle_decode(dtype, _ptr(a), a.size, _ptr(out)):
@@ -170,6 +176,15 @@ def _round_bf16(lib, values):
     out = np.empty(v.shape, np.uint16)
     if lib.oracle_round_bf16(_ptr(v), v.size, _ptr(out)):
         raise ValueError("oracle_round_bf16 failed")
+    return out
+
+
+def _round_f16(lib, values):
+    """Round float64 values to fp16 bit patterns (nearest, ties to even)."""
+    v = np.ascontiguousarray(values, dtype=np.float64)
+    out = np.empty(v.shape, np.uint16)
+    if lib.oracle_round_f16(_ptr(v), v.size, _ptr(out)):
+        raise ValueError("oracle_round_f16 failed")
     return out
 
 
@@ -187,6 +202,10 @@ def decode(dtype, bits):
 
 def round_bf16(values):
     return default().round_bf16(values)
+
+
+def round_f16(values):
+    return default().round_f16(values)
 
 
 def num_threads():

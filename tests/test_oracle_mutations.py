@@ -54,6 +54,21 @@ MUTATIONS = [
     ("bf16 ties away from zero", "double r = nearbyint(ldexp(a, -q));",
      "double r = round(ldexp(a, -q));"),
     ("bf16 decode shift", "uint32_t u = ((uint32_t)b) << 16;", "uint32_t u = ((uint32_t)b) << 15;"),
+    ("fp16 ties away from zero", "double k = nearbyint(ldexp(a, -q));",
+     "double k = round(ldexp(a, -q));"),
+    ("fp16 decode exponent bias", "v = ldexp((double)(1024 + f), e - 25);",
+     "v = ldexp((double)(1024 + f), e - 24);"),
+    ("fp16 subnormal step", "if (q < -24) q = -24;", "if (q < -25) q = -25;"),
+    ("fp16 overflow threshold", "if (out > 65504.0) out = INFINITY;",
+     "if (out > 65536.0) out = INFINITY;"),
+    ("fp16 read as bf16",
+     "return dtype == OR_F16 ? or_f16_bits_to_double(b) : or_bf16_bits_to_double(b);",
+     "return or_bf16_bits_to_double(b);"),
+    ("fp16 residual rounded as bf16", "if (dtype == OR_F16) return or_round_to_f16(v);",
+     "if (dtype == OR_F16) return or_round_to_bf16(v);"),
+    ("fp16 mixed activations read as bf16",
+     "return dtype == OR_BF16_F32W ? OR_BF16 : dtype == OR_F16_F32W ? OR_F16 : dtype;",
+     "return dtype == OR_BF16_F32W ? OR_BF16 : dtype == OR_F16_F32W ? OR_BF16 : dtype;"),
 ]
 
 
