@@ -18,8 +18,9 @@ LIB = os.path.join(PKG, "libnorm.so")
 
 ARCH = os.environ.get("DLN_OFFLOAD_ARCH", "gfx950")
 SOURCES = [
-    "norm_team.hip", "norm_team_narrow.hip", "norm_looped.hip", "norm_split.hip", "norm_abi.cpp",
-    "norm_plan.cpp",
+    "norm_team.hip", "norm_team_f32.hip", "norm_team_bf16.hip", "norm_team_bf16w.hip",
+    "norm_team_f16.hip", "norm_team_f16w.hip", "norm_looped.hip", "norm_split.hip",
+    "norm_abi.cpp", "norm_plan.cpp",
 ]
 
 # -packed-fp32-ops: keep the compiler from forming packed fp32 VALU ops (v_pk_*_f32).

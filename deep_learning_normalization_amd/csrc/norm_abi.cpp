@@ -121,7 +121,7 @@ norm_status_t run_reduce(norm_dtype_t dtype, int64_t N, void *dW, void *dB, void
 }
 
 norm_status_t zero_outputs(int64_t N, norm_dtype_t dtype, void *dW, void *dB, hipStream_t s) {
-  const size_t n = (size_t)N * (dtype == NORM_BF16 ? 2 : 4); // dW, dB in the weight type
+  const size_t n = (size_t)N * ((dtype == NORM_BF16 || dtype == NORM_F16) ? 2 : 4); // dW, dB
   norm_status_t st = dln::launch_zero(dW, n, s);
   if (st == NORM_OK && dB) st = dln::launch_zero(dB, n, s);
   return st;

@@ -11,9 +11,12 @@ namespace dln {
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
-// bf16 tensors are carried as their raw 16-bit patterns.
+// bf16 tensors are carried as their raw 16-bit patterns; fp16 tensors as the compiler's
+// binary16 type (conversions to and from fp32 are the hardware's, round to nearest even).
 typedef uint16_t bf16_bits;
+typedef _Float16 f16_t;
 
 // Input loads and output stores of the streamed [M, N] tensors. Each element is touched once
 // per pass, so stores bypass the caches' allocate-on-write (nontemporal). Loads stay ordinary:
@@ -55,6 +58,37 @@ __device__ __forceinline__ float round_bf16(float v) {
   return bf16_lo(p);
 }
 
+// The same for fp16 (IEEE binary16).
+__device__ __forceinline__ float f16_lo(unsigned u) {
+  return (float)__builtin_bit_cast(f16_t, (uint16_t)(u & 0xffffu));
+}
+__device__ __forceinline__ float f16_hi(unsigned u) {
+  return (float)__builtin_bit_cast(f16_t, (uint16_t)(u >> 16));
+}
+__device__ __forceinline__ unsigned pack_f16x2(float lo, float hi) {
+  f32x2 f = {lo, hi};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(f, f16x2));
+}
+__device__ __forceinline__ float round_f16(float v) { return (float)(f16_t)v; }
+
+// Two 16-bit values of type T (bf16_bits or f16_t) in one 32-bit word, to and from fp32.
+template <typename T> __device__ __forceinline__ float lo16(unsigned u) {
+  if constexpr (__is_same(T, f16_t)) return f16_lo(u);
+  else return bf16_lo(u);
+}
+template <typename T> __device__ __forceinline__ float hi16(unsigned u) {
+  if constexpr (__is_same(T, f16_t)) return f16_hi(u);
+  else return bf16_hi(u);
+}
+template <typename T> __device__ __forceinline__ unsigned pack16x2(float lo, float hi) {
+  if constexpr (__is_same(T, f16_t)) return pack_f16x2(lo, hi);
+  else return pack_bf16x2(lo, hi);
+}
+template <typename T> __device__ __forceinline__ float round16(float v) {
+  if constexpr (__is_same(T, f16_t)) return round_f16(v);
+  else return round_bf16(v);
+}
+
 // Acc<T, E>: one memory access of E elements of T, converted to / from fp32. E * sizeof(T) is
 // 16, 8 or 4 bytes on the vector paths (whole 32-bit words, E = full_epv<T>() and its halves
 // down to two elements); E = 1 is the element-wise path.
@@ -78,7 +112,7 @@ template <typename T, int E> struct Acc {
   static_assert(E >= 2 && E <= full_epv<T>() && (E & (E - 1)) == 0, "whole-word accesses");
   static constexpr int EPV = E;
   static constexpr int NW = E * (int)sizeof(T) / 4;
-  static constexpr bool BF16 = sizeof(T) == 2;
+  static constexpr bool B16 = sizeof(T) == 2; // bf16 or fp16
   typedef typename Words<NW>::type raw;
   __device__ static raw ld(const T *p) { return ld_stream(reinterpret_cast<const raw *>(p)); }
   __device__ static raw ld_cached(const T *p) { return *reinterpret_cast<const raw *>(p); }
@@ -87,9 +121,9 @@ template <typename T, int E> struct Acc {
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
       const unsigned u = word(v, i);
-      if constexpr (BF16) {
-        f[2 * i] = bf16_lo(u);
-        f[2 * i + 1] = bf16_hi(u);
+      if constexpr (B16) {
+        f[2 * i] = lo16<T>(u);
+        f[2 * i + 1] = hi16<T>(u);
       } else {
         f[i] = __builtin_bit_cast(float, u);
       }
@@ -99,15 +133,15 @@ template <typename T, int E> struct Acc {
     raw v;
 #pragma unroll
     for (int i = 0; i < NW; ++i) {
-      if constexpr (BF16)
-        set_word(v, i, pack_bf16x2(f[2 * i], f[2 * i + 1]));
+      if constexpr (B16)
+        set_word(v, i, pack16x2<T>(f[2 * i], f[2 * i + 1]));
       else
         set_word(v, i, __builtin_bit_cast(unsigned, f[i]));
     }
     return v;
   }
   __device__ static float round(float v) {
-    if constexpr (BF16) return round_bf16(v);
+    if constexpr (B16) return round16<T>(v);
     return v;
   }
   __device__ static raw zero() {
@@ -144,6 +178,18 @@ template <> struct Acc<bf16_bits, 1> {
   __device__ static raw zero() { return 0; }
 };
 
+template <> struct Acc<f16_t, 1> {
+  static constexpr int EPV = 1;
+  typedef uint16_t raw; // the element's bits
+  __device__ static raw ld(const f16_t *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static raw ld_cached(const f16_t *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static void st(f16_t *p, raw v) { *reinterpret_cast<raw *>(p) = v; }
+  __device__ static void unpack(raw v, float *f) { f[0] = (float)__builtin_bit_cast(f16_t, v); }
+  __device__ static raw pack(const float *f) { return __builtin_bit_cast(raw, (f16_t)f[0]); }
+  __device__ static float round(float v) { return round_f16(v); }
+  __device__ static raw zero() { return 0; }
+};
+
 // Settle a value loaded from memory at this point: an empty asm that takes it in VGPRs and may
 // rewrite it, so the wait for its load is placed here. Kernels settle the weight and bias once,
 // after the first row group's loads are issued; left to itself the compiler may place that wait
@@ -160,8 +206,8 @@ __device__ __forceinline__ void settle(bf16_bits &v) {
 }
 
 // WAcc<T, TW, E>: the weight (or bias) values of one access of E elements of T, stored as TW.
-// With the same storage type as the activations they stay packed; fp32 weights next to bf16
-// activations are E fp32 values (E * 4 bytes: two 16-byte loads for E = 8, one 8-byte load for
+// With the same storage type as the activations they stay packed; fp32 weights next to bf16 or
+// fp16 activations are E fp32 values (E * 4 bytes: two 16-byte loads for E = 8, one 8-byte load for
 // E = 2). get() gives fp32; store() writes E fp32 sums as TW (the final dW / dB).
 template <typename T, typename TW, int E> struct WAcc;
 
@@ -176,7 +222,7 @@ template <typename T, int EV> struct WAcc<T, T, EV> {
   __device__ static void store(T *p, const float *f) { A::st(p, A::pack(f)); }
 };
 
-template <int EV> struct WAcc<bf16_bits, float, EV> {
+template <int EV> struct WAccF32 {
   static constexpr int E = EV;
   // words per load: 16-byte loads when E is a multiple of 4, else one E-word load
   static constexpr int LW = E % 4 == 0 ? 4 : E;
@@ -212,6 +258,8 @@ template <int EV> struct WAcc<bf16_bits, float, EV> {
     }
   }
 };
+template <int EV> struct WAcc<bf16_bits, float, EV> : WAccF32<EV> {};
+template <int EV> struct WAcc<f16_t, float, EV> : WAccF32<EV> {};
 
 // ---- reductions -------------------------------------------------------------------------
 

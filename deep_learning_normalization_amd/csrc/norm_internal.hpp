@@ -82,11 +82,16 @@ norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &
                               hipStream_t s);
 norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                               hipStream_t s);
-// 8- and 4-byte accesses (plans with scale > 1), instantiated apart from the full-width ones
-norm_status_t launch_team_fwd_narrow(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
-                                     hipStream_t s);
-norm_status_t launch_team_bwd_narrow(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
-                                     hipStream_t s);
+// the team kernels of one storage combination, every access width (norm_team_<type>.hip)
+#define DLN_TEAM_TYPE_LAUNCHERS(tag)                                                            \
+  norm_status_t launch_team_fwd_##tag(const Plan &p, const FwdArgs &a, hipStream_t s);          \
+  norm_status_t launch_team_bwd_##tag(const Plan &p, const BwdArgs &a, hipStream_t s);
+DLN_TEAM_TYPE_LAUNCHERS(f32)
+DLN_TEAM_TYPE_LAUNCHERS(bf16)
+DLN_TEAM_TYPE_LAUNCHERS(bf16w)
+DLN_TEAM_TYPE_LAUNCHERS(f16)
+DLN_TEAM_TYPE_LAUNCHERS(f16w)
+#undef DLN_TEAM_TYPE_LAUNCHERS
 // rows of 1024-2048 full-width accesses: two sweeps per row, the second from the L2
 norm_status_t launch_looped_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                                 hipStream_t s);

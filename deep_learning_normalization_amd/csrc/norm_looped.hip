@@ -244,6 +244,8 @@ norm_status_t launch_looped_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs
   case NORM_F32: return looped_width<float, float>(p, a, s);
   case NORM_BF16: return looped_width<bf16_bits, bf16_bits>(p, a, s);
   case NORM_BF16_F32W: return looped_width<bf16_bits, float>(p, a, s);
+  case NORM_F16: return looped_width<f16_t, f16_t>(p, a, s);
+  case NORM_F16_F32W: return looped_width<f16_t, float>(p, a, s);
   default: return NORM_ERR_UNSUPPORTED;
   }
 }

@@ -32,11 +32,14 @@ constexpr int kLoopMaxEq = kLoopThreads * kLoopSegFull; // longest row, full-wid
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool valid_kind(int k) { return k == NORM_LAYERNORM || k == NORM_RMSNORM; }
-bool valid_dtype(int d) { return d == NORM_F32 || d == NORM_BF16 || d == NORM_BF16_F32W; }
+bool valid_dtype(int d) {
+  return d == NORM_F32 || d == NORM_BF16 || d == NORM_BF16_F32W || d == NORM_F16 ||
+         d == NORM_F16_F32W;
+}
 int vec_epv(norm_dtype_t d) { return d == NORM_F32 ? 4 : 8; }
 // bytes per element of the activations (X, R, Y, H, dY, dH, dX, dR) and of W, B, dW, dB
 size_t elem_size(int d) { return d == NORM_F32 ? 4 : 2; }
-size_t weight_size(int d) { return d == NORM_BF16 ? 2 : 4; }
+size_t weight_size(int d) { return (d == NORM_BF16 || d == NORM_F16) ? 2 : 4; }
 // Pointer alignment an access of e elements needs: e activation elements in one load, and the
 // matching e weights (read 16 bytes at a time when they span 16 bytes or more).
 size_t access_align(int d, int e) {

@@ -672,6 +672,8 @@ norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs 
   case NORM_F32: return split_fwd_typed<float, float>(p, a, s);
   case NORM_BF16: return split_fwd_typed<bf16_bits, bf16_bits>(p, a, s);
   case NORM_BF16_F32W: return split_fwd_typed<bf16_bits, float>(p, a, s);
+  case NORM_F16: return split_fwd_typed<f16_t, f16_t>(p, a, s);
+  case NORM_F16_F32W: return split_fwd_typed<f16_t, float>(p, a, s);
   default: return NORM_ERR_UNSUPPORTED;
   }
 }
@@ -682,6 +684,8 @@ norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs 
   case NORM_F32: return split_bwd_typed<float, float>(p, a, s);
   case NORM_BF16: return split_bwd_typed<bf16_bits, bf16_bits>(p, a, s);
   case NORM_BF16_F32W: return split_bwd_typed<bf16_bits, float>(p, a, s);
+  case NORM_F16: return split_bwd_typed<f16_t, f16_t>(p, a, s);
+  case NORM_F16_F32W: return split_bwd_typed<f16_t, float>(p, a, s);
   default: return NORM_ERR_UNSUPPORTED;
   }
 }

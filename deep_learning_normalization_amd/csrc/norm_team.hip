@@ -1,9 +1,9 @@
-// norm_team.hip -- the team kernels' full-width (16-byte) and element-wise instantiations and
-// their dispatch, the column reduction of the backward's partials, and a zero fill.
+// norm_team.hip -- the column reduction of the backward's partials, a zero fill, and the
+// team kernels' dispatch by storage type.
 //
-// The kernels themselves (norm_team_kernels.hpp) hold a row per team of threads in registers;
-// 8- and 4-byte accesses for rows whose length or pointers rule out 16-byte ones are
-// instantiated in norm_team_narrow.hip.
+// The team kernels (norm_team_kernels.hpp) hold a row per team of threads in registers; each
+// storage combination's shapes are instantiated in its own translation unit
+// (norm_team_<type>.hip, from the menus in norm_team_menu.hpp).
 #include "norm_team_kernels.hpp"
 
 namespace dln {
@@ -24,6 +24,8 @@ template <typename T> __device__ __forceinline__ void store_col(void *dst, int64
   T *d = static_cast<T *>(dst);
   if constexpr (sizeof(T) == 4)
     d[col] = t;
+  else if constexpr (__is_same(T, f16_t))
+    d[col] = (f16_t)t;
   else
     d[col] = (T)(pack_bf16x2(t, 0.0f) & 0xffffu);
 }
@@ -155,133 +157,26 @@ __global__ __launch_bounds__(256) void zero_kernel(unsigned char *p, size_t n) {
 
 // ---- launchers ---------------------------------------------------------------------------------
 
-namespace {
-
-// The menu of compiled shapes. Wave scheme: workgroups of 256 threads (4 one-wave teams).
-// Block scheme: teams of up to LB threads. Entries are (VPT, ROWS, LB).
-#define DLN_WAVE_MENU(X)                                                                        \
-  X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(2, 4, 256) X(4, 1, 256)       \
-      X(4, 2, 256) X(8, 1, 256)
-#define DLN_WAVE_MENU_SCALAR(X) X(1, 1, 256) X(2, 1, 256) X(4, 1, 256) X(8, 1, 256) X(16, 1, 256)
-#define DLN_BLOCK_MENU(X)                                                                       \
-  X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(2, 4, 256) X(4, 1, 256)       \
-      X(8, 1, 256) X(1, 1, 512) X(1, 2, 512) X(1, 4, 512) X(2, 1, 512) X(2, 2, 512) X(4, 1, 512)   \
-          X(1, 1, 1024) X(1, 2, 1024) X(2, 1, 1024)
-#define DLN_BLOCK_MENU_SCALAR(X) X(4, 1, 1024) X(8, 1, 1024)
-
-template <typename T, typename TW>
-norm_status_t team_fwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
-  const bool resid = a.r != nullptr;
-  const int lb = p.lb;
-  hipError_t e = hipErrorInvalidConfiguration;
-  bool found = false;
-  if (p.scheme == NORM_SCHEME_WAVE) {
-    if (p.vector) {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = fwd_launch<T, TW, full_epv<T>(), V, R, L, true>(p, a, resid, s);                           \
-  }
-      DLN_WAVE_MENU(X)
-#undef X
-    } else {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = fwd_launch<T, TW, 1, V, R, L, true>(p, a, resid, s);                                \
-  }
-      DLN_WAVE_MENU_SCALAR(X)
-#undef X
-    }
-  } else {
-    if (p.vector) {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = fwd_launch<T, TW, full_epv<T>(), V, R, L, false>(p, a, resid, s);                          \
-  }
-      DLN_BLOCK_MENU(X)
-#undef X
-    } else {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = fwd_launch<T, TW, 1, V, R, L, false>(p, a, resid, s);                               \
-  }
-      DLN_BLOCK_MENU_SCALAR(X)
-#undef X
-    }
-  }
-  if (!found) return NORM_ERR_UNSUPPORTED;
-  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
-}
-
-template <typename T, typename TW>
-norm_status_t team_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
-  const int lb = p.lb;
-  hipError_t e = hipErrorInvalidConfiguration;
-  bool found = false;
-  if (p.scheme == NORM_SCHEME_WAVE) {
-    if (p.vector) {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = bwd_launch<T, TW, full_epv<T>(), V, R, L, true>(p, a, s);                                  \
-  }
-      DLN_WAVE_MENU(X)
-#undef X
-    } else {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = bwd_launch<T, TW, 1, V, R, L, true>(p, a, s);                                       \
-  }
-      DLN_WAVE_MENU_SCALAR(X)
-#undef X
-    }
-  } else {
-    if (p.vector) {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = bwd_launch<T, TW, full_epv<T>(), V, R, L, false>(p, a, s);                                 \
-  }
-      DLN_BLOCK_MENU(X)
-#undef X
-    } else {
-#define X(V, R, L)                                                                              \
-  if (!found && p.vpt == V && p.rows == R && lb == L) {                                         \
-    found = true;                                                                               \
-    e = bwd_launch<T, TW, 1, V, R, L, false>(p, a, s);                                      \
-  }
-      DLN_BLOCK_MENU_SCALAR(X)
-#undef X
-    }
-  }
-  if (!found) return NORM_ERR_UNSUPPORTED;
-  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
-}
-
-} // namespace
-
 norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                               hipStream_t s) {
-  if (p.scale > 1) return launch_team_fwd_narrow(p, dtype, a, s);
   switch (dtype) {
-  case NORM_F32: return team_fwd_typed<float, float>(p, a, s);
-  case NORM_BF16: return team_fwd_typed<bf16_bits, bf16_bits>(p, a, s);
-  case NORM_BF16_F32W: return team_fwd_typed<bf16_bits, float>(p, a, s);
+  case NORM_F32: return launch_team_fwd_f32(p, a, s);
+  case NORM_BF16: return launch_team_fwd_bf16(p, a, s);
+  case NORM_BF16_F32W: return launch_team_fwd_bf16w(p, a, s);
+  case NORM_F16: return launch_team_fwd_f16(p, a, s);
+  case NORM_F16_F32W: return launch_team_fwd_f16w(p, a, s);
   default: return NORM_ERR_UNSUPPORTED;
   }
 }
 
 norm_status_t launch_team_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                               hipStream_t s) {
-  if (p.scale > 1) return launch_team_bwd_narrow(p, dtype, a, s);
   switch (dtype) {
-  case NORM_F32: return team_bwd_typed<float, float>(p, a, s);
-  case NORM_BF16: return team_bwd_typed<bf16_bits, bf16_bits>(p, a, s);
-  case NORM_BF16_F32W: return team_bwd_typed<bf16_bits, float>(p, a, s);
+  case NORM_F32: return launch_team_bwd_f32(p, a, s);
+  case NORM_BF16: return launch_team_bwd_bf16(p, a, s);
+  case NORM_BF16_F32W: return launch_team_bwd_bf16w(p, a, s);
+  case NORM_F16: return launch_team_bwd_f16(p, a, s);
+  case NORM_F16_F32W: return launch_team_bwd_f16w(p, a, s);
   default: return NORM_ERR_UNSUPPORTED;
   }
 }
@@ -303,13 +198,16 @@ norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t
   if (a.N % 4 == 0) {
     const int64_t tiles = (a.N + 31) / 32;
     const dim3 grid((unsigned)(tiles < kReduceGrid ? tiles : kReduceGrid), q), block(256);
-    e = dtype == NORM_BF16 ? launch(colsum4_kernel<bf16_bits>, grid, block, s, a)
-                           : launch(colsum4_kernel<float>, grid, block, s, a);
+    // dW, dB are stored like W: bf16, fp16 or fp32
+    e = dtype == NORM_BF16  ? launch(colsum4_kernel<bf16_bits>, grid, block, s, a)
+        : dtype == NORM_F16 ? launch(colsum4_kernel<f16_t>, grid, block, s, a)
+                            : launch(colsum4_kernel<float>, grid, block, s, a);
   } else {
     const int64_t tiles = (a.N + 63) / 64;
     const dim3 grid((unsigned)(tiles < kReduceGrid ? tiles : kReduceGrid), q), block(256);
-    e = dtype == NORM_BF16 ? launch(colsum_kernel<bf16_bits>, grid, block, s, a)
-                           : launch(colsum_kernel<float>, grid, block, s, a);
+    e = dtype == NORM_BF16  ? launch(colsum_kernel<bf16_bits>, grid, block, s, a)
+        : dtype == NORM_F16 ? launch(colsum_kernel<f16_t>, grid, block, s, a)
+                            : launch(colsum_kernel<float>, grid, block, s, a);
   }
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }

@@ -14,7 +14,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libnorm.so")
 
 LAYERNORM, RMSNORM = 0, 1
-F32, BF16, BF16_F32W = 0, 1, 2
+F32, BF16, BF16_F32W, F16, F16_F32W = 0, 1, 2, 3, 4
 PASS_FWD, PASS_BWD = 0, 1
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT, SCHEME_LOOP = -1, 0, 1, 2, 3
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
@@ -24,17 +24,19 @@ N_TUNE_KEYS = 8
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
 KINDS = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM}
-DTYPES = {torch.float32: F32, torch.bfloat16: BF16}
+DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
+MIXED = {torch.bfloat16: BF16_F32W, torch.float16: F16_F32W}
 
 
 def dtype_code(act, weight=None):
     """norm_dtype_t for activations of torch dtype `act` and weights of `weight` (default: the
-    same): fp32/fp32, bf16/bf16, or bf16 activations with fp32 weights."""
+    same): one type for both (fp32, bf16, fp16), or bf16 / fp16 activations with fp32
+    weights."""
     weight = act if weight is None else weight
     if act == weight:
         return DTYPES[act]
-    if act == torch.bfloat16 and weight == torch.float32:
-        return BF16_F32W
+    if act in MIXED and weight == torch.float32:
+        return MIXED[act]
     raise ValueError("unsupported dtype pair: activations %s, weights %s" % (act, weight))
 
 SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_workspace_size",
@@ -198,7 +200,7 @@ def norm_bwd_fused(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, workspace, strea
 
 def norm_bwd_reduce(kind, M, N, dW, dB, workspace, stream=None):
     """Queue the column reduction of the partials a fused pass left in the workspace (the
-    outputs' dtype selects the store type: fp32 dW, dB for F32 and BF16_F32W)."""
+    outputs' dtype selects the store type: fp32 dW, dB for F32 and the fp32-weight types)."""
     dt = dW.dtype
     _check_vec(dW, N, dt, "dW")
     _check_vec(dB, N, dt, "dB")

@@ -9,7 +9,7 @@ Throughput para Treinamento e Inferência de LLM", introl.com, section on kernel
 
 
 def elem_size(dtype):
-    return {"bf16": 2, "f32": 4}[dtype]
+    return {"bf16": 2, "f16": 2, "f32": 4}[dtype]
 
 
 def fwd_bytes(kind, dtype, M, N, residual=False, bias=None, wdtype=None):

@@ -29,7 +29,7 @@
  *     dX, dR are row-major contiguous [M, N] (row stride N); W, B, dW, dB are [N]; mean and
  *     rstd are [M] fp32 whatever the dtype; the workspace is raw device memory.
  *   - dtype gives the storage types of the non-statistic tensors (norm_dtype_t: one type for
- *     all, or bf16 activations with fp32 W, B, dW, dB); arithmetic is fp32, and each output
+ *     all, or 16-bit activations with fp32 W, B, dW, dB); arithmetic is fp32, and each output
  *     is rounded once (round to nearest even).
  *   - The caller owns all memory. The library allocates nothing and keeps no state beyond a
  *     per-device cache of the compute-unit count and the tuning overrides below.
@@ -40,7 +40,7 @@
  *   - Accesses are the widest of 16, 8 and 4 bytes (at least two elements) that divides the
  *     row length in bytes and that the alignment common to every tensor pointer allows. An
  *     access of E elements needs E * element size bytes; with fp32 W, B, dW, dB beside bf16
- *     activations it needs min(16, 4 E) bytes, for the weights read with it. Rows of an odd
+ *     or fp16 activations it needs min(16, 4 E) bytes, for the weights read with it. Rows of an odd
  *     number of elements, or pointers aligned to one element only, run on a slower
  *     element-wise path. Results are the same on every path up to rounding order.
  *   - Arguments are checked before anything is launched; a failed check returns an error and
@@ -62,13 +62,21 @@ extern "C" {
 typedef enum { NORM_LAYERNORM = 0, NORM_RMSNORM = 1 } norm_kind_t;
 
 /*
- * Storage types. NORM_F32 and NORM_BF16: every tensor in that type. NORM_BF16_F32W: X, R, Y,
- * H, dY, dH, dX, dR in bf16 and W, B, dW, dB in fp32, the mixed-precision layout in which the
- * parameters keep fp32 master copies ([P2] "Otimização de Performance de GPU: Maximizando
- * Throughput para Treinamento e Inferência de LLM", section on mixed-precision training).
- * mean and rstd are fp32 always; all arithmetic is fp32.
+ * Storage types. NORM_F32, NORM_BF16 and NORM_F16 (IEEE binary16): every tensor in that type.
+ * NORM_BF16_F32W / NORM_F16_F32W: X, R, Y, H, dY, dH, dX, dR in bf16 / fp16 and W, B, dW, dB
+ * in fp32, the mixed-precision layout in which the parameters keep fp32 master copies ([P2]
+ * "Otimização de Performance de GPU: Maximizando Throughput para Treinamento e Inferência de
+ * LLM", section on mixed-precision training, which trains in FP16 with FP32 master weights).
+ * mean and rstd are fp32 always; all arithmetic is fp32; outputs are rounded to nearest even
+ * (fp16 values beyond 65504 round to infinity).
  */
-typedef enum { NORM_F32 = 0, NORM_BF16 = 1, NORM_BF16_F32W = 2 } norm_dtype_t;
+typedef enum {
+  NORM_F32 = 0,
+  NORM_BF16 = 1,
+  NORM_BF16_F32W = 2,
+  NORM_F16 = 3,      /* IEEE binary16 */
+  NORM_F16_F32W = 4  /* fp16 activations, fp32 W, B, dW, dB */
+} norm_dtype_t;
 
 typedef enum {
   NORM_OK = 0,

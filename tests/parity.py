@@ -11,6 +11,9 @@ Tolerances (written out in check_*):
                                                             spacing beyond |ref| = 1)
                       |d| <= 1.6e-2 (|ref| + rms(ref))     (scale-aware: small gradients too)
                       |d| <= 2^-8 |ref| + 1e-5 rms(ref)    (one rounding of an fp32 result)
+  fp16 Y, dX, H       the same three with 2 fp16 ulps at 1.0 (2^-9) in place of 1.6e-2 and
+                      half an fp16 ulp (2^-11 |ref|) for the rounding, each plus half the
+                      subnormal step (2^-25); values rounding past 65504 must be +-inf
   dW, dB              |d_j| <= 1e-2 max(|ref_j|, rms(ref)) (relative, with a floor where a
                                                             column sum of signed terms is ~0);
                       1e-4 of that for fp32 storage
@@ -26,14 +29,15 @@ import oracle
 from deep_learning_normalization_amd import inputs, normlib as nl
 
 KIND = {"layernorm": oracle.LAYERNORM, "rmsnorm": oracle.RMSNORM}
-DT = {"f32": oracle.F32, "bf16": oracle.BF16}
+DT = {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}
+MIXED = {"bf16": oracle.BF16_F32W, "f16": oracle.F16_F32W}
 
 
 def oracle_dtype(w):
-    """The oracle's storage code for a workload: one type, or bf16 with fp32 weights."""
+    """The oracle's storage code for a workload: one type, or bf16 / fp16 with fp32 weights."""
     if w.wdtype and w.wdtype != w.dtype:
-        assert (w.dtype, w.wdtype) == ("bf16", "f32"), (w.dtype, w.wdtype)
-        return oracle.BF16_F32W
+        assert w.dtype in MIXED and w.wdtype == "f32", (w.dtype, w.wdtype)
+        return MIXED[w.dtype]
     return DT[w.dtype]
 
 
@@ -62,6 +66,11 @@ def check_values(what, got, ref, dtype, floor=None):
         return
     assert np.array_equal(np.isnan(got), np.isnan(ref)), what + ": NaN pattern differs"
     ok = ~np.isnan(ref)
+    if dtype == "f16":
+        # values that round beyond 65504 are stored as infinity of their sign
+        big = np.abs(ref) >= 65520.0
+        assert np.array_equal(got[big], np.copysign(np.inf, ref[big])), what + ": fp16 overflow"
+        ok &= ~big
     got, ref, fl = got[ok], ref[ok], fl[ok]
     d = np.abs(got - ref)
     if dtype == "f32":
@@ -70,11 +79,21 @@ def check_values(what, got, ref, dtype, floor=None):
             _fail(what + " [fp32]", got, ref, b)
         return
     s = rms(ref)
-    for name, b in (("1.6e-2 abs", 1.6e-2 * (1.0 + np.abs(ref))),
-                    ("1.6e-2 scaled", 1.6e-2 * (np.abs(ref) + s) + fl),
-                    ("bf16 rounding", 2.0 ** -8 * np.abs(ref) + 1e-5 * s + fl)):
+    if dtype == "f16":
+        # fp16: 2 ulps at 1.0 (2^-9), scale-aware; then the rounding itself: half an ulp
+        # (2^-11 relative) plus the fp32 arithmetic before it. Below 2^-14 the spacing is a
+        # fixed 2^-24, so every bound also allows half of that step (2^-25).
+        sub = 2.0 ** -25
+        checks = (("2^-9 abs", 2.0 ** -9 * (1.0 + np.abs(ref)) + sub),
+                  ("2^-9 scaled", 2.0 ** -9 * (np.abs(ref) + s) + sub + fl),
+                  ("fp16 rounding", 2.0 ** -11 * np.abs(ref) + sub + 1e-5 * s + fl))
+    else:
+        checks = (("1.6e-2 abs", 1.6e-2 * (1.0 + np.abs(ref))),
+                  ("1.6e-2 scaled", 1.6e-2 * (np.abs(ref) + s) + fl),
+                  ("bf16 rounding", 2.0 ** -8 * np.abs(ref) + 1e-5 * s + fl))
+    for name, b in checks:
         if not (d <= b).all():
-            _fail("%s [bf16 %s]" % (what, name), got, ref, b)
+            _fail("%s [%s %s]" % (what, dtype, name), got, ref, b)
 
 
 def dx_floor(rows, dY, W, rstd, N):
@@ -97,8 +116,9 @@ def check_h(got, ref, dtype):
     diff = got != ref
     if diff.any():
         r = np.abs(ref[diff])
-        ulp = np.exp2(np.floor(np.log2(np.where(r > 0, r, 2.0 ** -133))) - 7)
-        assert (np.abs(got[diff] - ref[diff]) <= ulp).all(), "H: more than one bf16 ulp off"
+        bits, tiny = (10, 2.0 ** -24) if dtype == "f16" else (7, 2.0 ** -133)
+        ulp = np.maximum(np.exp2(np.floor(np.log2(np.where(r > 0, r, tiny))) - bits), tiny)
+        assert (np.abs(got[diff] - ref[diff]) <= ulp).all(), "H: more than one %s ulp off" % dtype
         assert diff.mean() < 1e-4, "H: %d of %d elements differ" % (diff.sum(), diff.size)
 
 
@@ -196,12 +216,13 @@ def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stat
     Xin = H if R is not None else X
     # the oracle's own h (as input bits) for the residual backward, formed block by block
     if R is not None:
-        xbits = np.empty((M, N), np.uint16 if w.dtype == "bf16" else np.float32)
+        xbits = np.empty((M, N), np.float32 if w.dtype == "f32" else np.uint16)
         for r0 in range(0, M, 4096):
             r1 = min(M, r0 + 4096)
             h = oracle.fwd(kind, dtc, bits["X"], bits["W"], None, bits["R"], eps=eps,
                            rows=(r0, r1), want_h=True)["h"]
-            xbits[r0:r1] = (oracle.round_bf16(h) if w.dtype == "bf16" else h.astype(np.float32))
+            xbits[r0:r1] = (oracle.round_bf16(h) if w.dtype == "bf16" else
+                            oracle.round_f16(h) if w.dtype == "f16" else h.astype(np.float32))
             del h
     else:
         xbits = bits["X"]

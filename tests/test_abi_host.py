@@ -84,7 +84,7 @@ def _bwd(**kw):
 
 
 @pytest.mark.parametrize("kw", [
-    dict(kind=2), dict(kind=-1), dict(dtype=3), dict(M=-1), dict(N=0), dict(N=-5),
+    dict(kind=2), dict(kind=-1), dict(dtype=5), dict(M=-1), dict(N=0), dict(N=-5),
     dict(N=1 << 31), dict(eps=-1e-5), dict(eps=float("nan")), dict(eps=float("inf")),
     dict(X=None), dict(W=None), dict(Y=None),
     dict(kind=1, B=FAKE * 9), dict(kind=1, mean=FAKE * 9),
@@ -272,7 +272,7 @@ def test_mixed_weight_dtype_on_the_host():
         assert a == b
     assert nl.lib().norm_set_tuning(nl.TUNE_SCHEME, -1) == nl.OK
     with pytest.raises(nl.NormError):
-        nl.norm_plan(0, 3, 0, 16, 16)                      # no such dtype
+        nl.norm_plan(0, 5, 0, 16, 16)                      # no such dtype
     # W holds N fp32 values: an output placed inside them overlaps
     assert _fwd(dtype=2, W=FAKE * 2, Y=FAKE * 2 + 16) == nl.ERR_INVALID_ARG
     assert _fwd(dtype=2, W=FAKE * 2, mean=FAKE * 2 + 16, M=4, N=8) == nl.ERR_INVALID_ARG
@@ -281,3 +281,20 @@ def test_mixed_weight_dtype_on_the_host():
     assert nl.dtype_code(torch.bfloat16, torch.float32) == nl.BF16_F32W
     with pytest.raises(ValueError):
         nl.dtype_code(torch.float32, torch.bfloat16)
+
+
+def test_fp16_dtypes_on_the_host():
+    # fp16 plans like bf16 (two-byte elements); fp16 activations with fp32 weights like the
+    # bf16 mixed layout, and their weight spans are 4 bytes per element
+    HF = torch.float16
+    for pass_ in (0, 1):
+        for N in (1000, 4096, 4100, 4098, 12288, 262144):
+            assert nl.norm_plan(0, HF, pass_, 4096, N) == nl.norm_plan(0, BF, pass_, 4096, N)
+            assert nl.norm_plan(0, nl.F16_F32W, pass_, 4096, N) == \
+                nl.norm_plan(0, nl.BF16_F32W, pass_, 4096, N)
+    assert nl.dtype_code(HF) == nl.F16 == 3
+    assert nl.dtype_code(HF, torch.float32) == nl.F16_F32W == 4
+    with pytest.raises(ValueError):
+        nl.dtype_code(HF, torch.bfloat16)
+    assert _fwd(dtype=4, W=FAKE * 2, Y=FAKE * 2 + 16) == nl.ERR_INVALID_ARG
+    assert _fwd(dtype=3, W=FAKE * 2, mean=FAKE * 2 + 16, M=4, N=8) == nl.ERR_HIP

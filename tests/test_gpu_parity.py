@@ -166,6 +166,66 @@ def test_split_direct_dw_unaligned_outputs(wdtype):
     check_colsums("dB", dB.double().cpu().numpy(), ref_db.double().cpu().numpy(), "f32")
 
 
+# ---- fp16 storage, and fp16 activations with fp32 weights ---------------------------------------
+
+F16_N = [1, 7, 64, 1000, 1024, 1025, 1002, 4096, 4100, 4098, 5120, 8192, 12288, 16384, 20000,
+         262144]
+
+
+def _f16_cases():
+    out = []
+    for N in F16_N:
+        for kind in ("layernorm", "rmsnorm"):
+            for wdt in (None, "f32"):
+                out.append((kind, wdt, 129 if N <= 20000 else 5, N))
+    return out
+
+
+@pytest.mark.parametrize("kind,wdt,M,N", _f16_cases(), ids=lambda v: str(v))
+def test_fp16(kind, wdt, M, N):
+    _say("fp16 %s w=%s %dx%d" % (kind, wdt, M, N))
+    w = dataclasses.replace(_small(kind, "f16", M, N, seed=M + N), wdtype=wdt)
+    run_and_check(w)
+    run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
+
+
+@pytest.mark.parametrize("name,scheme,N", [("wave", nl.SCHEME_WAVE, 512),
+                                           ("block", nl.SCHEME_BLOCK, 4096),
+                                           ("loop", nl.SCHEME_LOOP, 4096),
+                                           ("split", nl.SCHEME_SPLIT, 4096)],
+                         ids=lambda v: str(v))
+def test_fp16_forced_schemes(name, scheme, N):
+    for kind in ("layernorm", "rmsnorm"):
+        for wdt in (None, "f32"):
+            _say("fp16 forced %s %s w=%s N=%d" % (name, kind, wdt, N))
+            with tuned(scheme=scheme):
+                run_and_check(dataclasses.replace(_small(kind, "f16", 77, N, seed=N), wdtype=wdt))
+
+
+@pytest.mark.parametrize("N", [512, 7168, 4098])
+def test_fp16_residual(N):
+    for kind in ("rmsnorm", "layernorm"):
+        _say("fp16 residual %s N=%d" % (kind, N))
+        w = _small(kind, "f16", 65, N, seed=N, x=inputs.normal(0, 0.5), r=inputs.normal(0, 1))
+        run_and_check(w, dr="alias", dh=True)
+        run_and_check(dataclasses.replace(w, seed=N + 1, wdtype="f32"), dr="separate")
+
+
+def test_fp16_overflow_and_subnormal_outputs():
+    """Outputs beyond fp16's range round to infinity, tiny ones to subnormals, on both sides:
+    a weight of 2^15 scales normalised values beyond 2 past 65504, one of 2^-20 into the
+    subnormals."""
+    for wscale in (2.0 ** 15, 2.0 ** -20):
+        w = _small("rmsnorm", "f16", 33, 1000, seed=5, w=inputs.const(wscale))
+        _say("fp16 range, weight %g" % wscale)
+        out = run_and_check(w, want_bwd=False)
+        y = out["Y"].float()
+        if wscale > 1:
+            assert torch.isinf(y).any()
+        else:
+            assert ((y != 0) & (y.abs() < 2.0 ** -14)).any()
+
+
 # ---- 8- and 4-byte accesses ---------------------------------------------------------------------
 
 # Even row lengths that are not a multiple of the 16-byte vector (bf16: N % 8 != 0; fp32:
