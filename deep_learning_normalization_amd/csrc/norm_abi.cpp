@@ -49,17 +49,31 @@ norm_status_t ws_ok(const dln::Plan &p, const void *ws, size_t ws_bytes) {
   return NORM_OK;
 }
 
+// Row strides of one call in elements, each resolved (0 or no struct: N, contiguous rows).
+struct Strides {
+  int64_t x, r, y, h, dy, dh, dx, dr;
+};
+
+Strides resolve(const norm_row_strides_t *ld, int64_t N) {
+  auto pick = [N](int64_t v) { return v ? v : N; };
+  if (!ld) return Strides{N, N, N, N, N, N, N, N};
+  return Strides{pick(ld->x),  pick(ld->r),  pick(ld->y),  pick(ld->h),
+                 pick(ld->dy), pick(ld->dh), pick(ld->dx), pick(ld->dr)};
+}
+
 // Plan, workspace check and argument block of the backward's fused pass.
 norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const void *dH,
                         const void *W, const float *mean, const float *rstd, float eps,
                         int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
-                        void *workspace, size_t workspace_bytes, dln::Plan *plan,
-                        dln::BwdArgs *a) {
+                        void *workspace, size_t workspace_bytes, const Strides &ld,
+                        dln::Plan *plan, dln::BwdArgs *a) {
   int cu = 0;
   norm_status_t st = current_cu_count(&cu);
   if (st != NORM_OK) return st;
   const void *ptrs[] = {X, dY, dH, W, dX, dR};
-  const int align = dln::common_align(ptrs, 6);
+  const int64_t lds[] = {ld.x, ld.dy, dH ? ld.dh : N, ld.dx, dR ? ld.dr : N};
+  const int align = dln::fold_stride_align(dln::common_align(ptrs, 6), lds, 5,
+                                           dln::act_elem_size(dtype));
   st = dln::make_plan(kind, dtype, NORM_PASS_BWD, M, N, 0, align, cu, dln::tuning(), plan);
   if (st != NORM_OK) return st;
   st = ws_ok(*plan, workspace, workspace_bytes);
@@ -79,6 +93,11 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   b.header = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + plan->off_header);
   b.rowpart = plan->scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, plan->off_rowpart) : nullptr;
   b.stats = plan->scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, plan->off_stats) : nullptr;
+  b.ldx = ld.x;
+  b.lddy = ld.dy;
+  b.lddh = ld.dh;
+  b.lddx = ld.dx;
+  b.lddr = ld.dr;
   b.M = M;
   b.N = (int32_t)N;
   b.nacc = (int32_t)(N / plan->epv);
@@ -137,16 +156,29 @@ norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const voi
                        const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
                        void *Y, void *H, float *mean, float *rstd, void *workspace,
                        size_t workspace_bytes, norm_stream_t stream) {
+  return norm_fwd_ex(kind, X, R, W, B, eps, M, N, dtype, Y, H, mean, rstd, workspace,
+                     workspace_bytes, nullptr, stream);
+}
+
+norm_status_t norm_fwd_ex(norm_kind_t kind, const void *X, const void *R, const void *W,
+                          const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
+                          void *Y, void *H, float *mean, float *rstd, void *workspace,
+                          size_t workspace_bytes, const norm_row_strides_t *row_strides,
+                          norm_stream_t stream) {
   const EventsDisarm disarm;
+  if (N <= 0) return NORM_ERR_INVALID_ARG;
+  const Strides ld = resolve(row_strides, N);
   dln::FwdCheck c{kind, dtype, X, R, W, B, eps, M, N, Y, H, mean, rstd, workspace,
-                  workspace_bytes};
+                  workspace_bytes, ld.x, ld.r, ld.y, ld.h};
   norm_status_t st = dln::check_fwd(c);
   if (st != NORM_OK || M == 0) return st;
   int cu = 0;
   st = current_cu_count(&cu);
   if (st != NORM_OK) return st;
   const void *ptrs[] = {X, R, W, B, Y, H};
-  const int align = dln::common_align(ptrs, 6);
+  const int64_t lds[] = {ld.x, R ? ld.r : N, ld.y, H ? ld.h : N};
+  const int align = dln::fold_stride_align(dln::common_align(ptrs, 6), lds, 4,
+                                           dln::act_elem_size(dtype));
   dln::Plan p;
   st = dln::make_plan(kind, dtype, NORM_PASS_FWD, M, N, R != nullptr, align, cu,
                       dln::tuning(), &p);
@@ -163,6 +195,10 @@ norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const voi
   a.mean = kind == NORM_LAYERNORM ? mean : nullptr;
   a.rstd = rstd;
   a.rowpart = p.scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, p.off_rowpart) : nullptr;
+  a.ldx = ld.x;
+  a.ldr = ld.r;
+  a.ldy = ld.y;
+  a.ldh = ld.h;
   a.M = M;
   a.N = (int32_t)N;
   a.nacc = (int32_t)(N / p.epv);
@@ -181,9 +217,21 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
                        const void *W, const float *mean, const float *rstd, float eps,
                        int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR, void *dW,
                        void *dB, void *workspace, size_t workspace_bytes, norm_stream_t stream) {
+  return norm_bwd_ex(kind, X, dY, dH, W, mean, rstd, eps, M, N, dtype, dX, dR, dW, dB,
+                     workspace, workspace_bytes, nullptr, stream);
+}
+
+norm_status_t norm_bwd_ex(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                          const void *W, const float *mean, const float *rstd, float eps,
+                          int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                          void *dW, void *dB, void *workspace, size_t workspace_bytes,
+                          const norm_row_strides_t *row_strides, norm_stream_t stream) {
   const EventsDisarm disarm;
-  dln::BwdCheck c{kind, dtype, X, dY, dH, W, mean, rstd, eps, M, N, dX, dR, dW, dB, workspace,
-                  workspace_bytes, 1, 1};
+  if (N <= 0) return NORM_ERR_INVALID_ARG;
+  const Strides ld = resolve(row_strides, N);
+  dln::BwdCheck c{kind,   dtype, X,  dY, dH,    W,     mean,     rstd,  eps,
+                  M,      N,     dX, dR, dW,    dB,    workspace, workspace_bytes,
+                  1,      1,     ld.x, ld.dy, ld.dh, ld.dx, ld.dr};
   norm_status_t st = dln::check_bwd(c);
   if (st != NORM_OK) return st;
   if (kind == NORM_RMSNORM) dB = nullptr;
@@ -192,7 +240,7 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
   dln::Plan p;
   dln::BwdArgs a;
   st = bwd_setup(kind, X, dY, dH, W, mean, rstd, eps, M, N, dtype, dX, dR, workspace,
-                 workspace_bytes, &p, &a);
+                 workspace_bytes, ld, &p, &a);
   if (st != NORM_OK) return st;
   // the split scheme with a single row group writes dW/dB itself, with no reduction pass
   // (its vector stores of dW and dB need the alignment of the weight loads of its width)
@@ -212,15 +260,27 @@ norm_status_t norm_bwd_fused(norm_kind_t kind, const void *X, const void *dY, co
                              const void *W, const float *mean, const float *rstd, float eps,
                              int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
                              void *workspace, size_t workspace_bytes, norm_stream_t stream) {
+  return norm_bwd_fused_ex(kind, X, dY, dH, W, mean, rstd, eps, M, N, dtype, dX, dR, workspace,
+                           workspace_bytes, nullptr, stream);
+}
+
+norm_status_t norm_bwd_fused_ex(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                                const void *W, const float *mean, const float *rstd, float eps,
+                                int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                                void *workspace, size_t workspace_bytes,
+                                const norm_row_strides_t *row_strides, norm_stream_t stream) {
   const EventsDisarm disarm;
-  dln::BwdCheck c{kind, dtype, X, dY, dH, W, mean, rstd, eps, M, N, dX, dR, nullptr, nullptr,
-                  workspace, workspace_bytes, 1, 0};
+  if (N <= 0) return NORM_ERR_INVALID_ARG;
+  const Strides ld = resolve(row_strides, N);
+  dln::BwdCheck c{kind,   dtype, X,       dY,      dH,    W,     mean,      rstd,
+                  eps,    M,     N,       dX,      dR,    nullptr, nullptr, workspace,
+                  workspace_bytes, 1, 0,  ld.x,    ld.dy, ld.dh, ld.dx,     ld.dr};
   norm_status_t st = dln::check_bwd(c);
   if (st != NORM_OK || M == 0) return st;
   dln::Plan p;
   dln::BwdArgs a;
   st = bwd_setup(kind, X, dY, dH, W, mean, rstd, eps, M, N, dtype, dX, dR, workspace,
-                 workspace_bytes, &p, &a);
+                 workspace_bytes, ld, &p, &a);
   if (st != NORM_OK) return st;
   return run_fused(p, dtype, a, static_cast<hipStream_t>(stream));
 }
@@ -230,7 +290,8 @@ norm_status_t norm_bwd_reduce(norm_kind_t kind, int64_t M, int64_t N, norm_dtype
                               norm_stream_t stream) {
   const EventsDisarm disarm;
   dln::BwdCheck c{kind, dtype, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr, 0.0f, M,
-                  N, nullptr, nullptr, dW, dB, workspace, workspace_bytes, 0, 1};
+                  N, nullptr, nullptr, dW, dB, workspace, workspace_bytes, 0, 1,
+                  N, N, N, N, N};
   norm_status_t st = dln::check_bwd(c);
   if (st != NORM_OK) return st;
   if (kind == NORM_RMSNORM) dB = nullptr;

@@ -26,6 +26,7 @@ struct FwdArgs {
   float *mean;        // or nullptr
   float *rstd;        // or nullptr
   float *rowpart;     // split: [M][chunks][4]
+  int64_t ldx, ldr, ldy, ldh; // elements between row starts of X, R, Y, H (N when contiguous)
   int64_t M;
   int32_t N;
   int32_t nacc;       // accesses per row (N / epv)
@@ -52,6 +53,7 @@ struct BwdArgs {
   int64_t *header;    // workspace header: magic, partials, N
   float *rowpart;     // split: [M][chunks][4]
   float *stats;       // split without saved stats: [2][M]
+  int64_t ldx, lddy, lddh, lddx, lddr; // elements between row starts (N when contiguous)
   int64_t M;
   int32_t N;
   int32_t nacc;

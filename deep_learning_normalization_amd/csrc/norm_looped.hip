@@ -63,9 +63,8 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
   int slot = 0;
   for (int64_t row = blockIdx.x; row < M; row += gridDim.x) {
     // the row is uniform across the workgroup: scalar row pointers, 32-bit element offsets
-    const int64_t base = row * N;
-    const T *xr = X + base;
-    const T *dyr = DY + base;
+    const T *xr = X + row * a.ldx;
+    const T *dyr = DY + row * a.lddy;
     float m = 0.0f, rstd = 0.0f;
     if (have_stats) {
       if constexpr (LN) m = a.mean[row];
@@ -184,13 +183,13 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
         }
         if (DH) {
           float hf[E];
-          A::unpack(A::ld(DH + base + off), hf);
+          A::unpack(A::ld(DH + row * a.lddh + off), hf);
 #pragma unroll
           for (int e = 0; e < E; ++e) dx[e] += hf[e];
         }
         const typename A::raw p = A::pack(dx);
-        A::st(DX + base + off, p);
-        if (DR) A::st(DR + base + off, p);
+        A::st(DX + row * a.lddx + off, p);
+        if (DR) A::st(DR + row * a.lddr + off, p);
       }
     }
   }

@@ -442,6 +442,17 @@ bool sizes_ok(int64_t M, int64_t N) {
   return M <= (INT64_MAX / 16) / N;
 }
 
+// A row stride is at least N and keeps (M - 1) * ld + N elements addressable.
+bool stride_ok(int64_t M, int64_t N, int64_t ld) {
+  if (ld < N) return false;
+  return M <= (INT64_MAX / 16) / ld;
+}
+
+// bytes an [M, N] tensor with row stride ld spans
+size_t span(int64_t M, int64_t N, int64_t ld, size_t s) {
+  return M > 0 ? ((size_t)(M - 1) * (size_t)ld + (size_t)N) * s : 0;
+}
+
 } // namespace
 
 norm_status_t check_fwd(const FwdCheck &c) {
@@ -453,11 +464,16 @@ norm_status_t check_fwd(const FwdCheck &c) {
   if (!c.W) return NORM_ERR_INVALID_ARG;
   if (c.M == 0) return NORM_OK;
   if (!c.X || !c.Y) return NORM_ERR_INVALID_ARG;
+  // the strides of the tensors the call has (R and H are optional)
+  if (!stride_ok(c.M, c.N, c.ldx) || !stride_ok(c.M, c.N, c.ldy) ||
+      (c.R && !stride_ok(c.M, c.N, c.ldr)) || (c.H && !stride_ok(c.M, c.N, c.ldh)))
+    return NORM_ERR_INVALID_ARG;
   const size_t s = elem_size(c.dtype);
-  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * weight_size(c.dtype),
-               m = (size_t)c.M * 4;
-  const Span in[] = {{c.X, mn}, {c.R, mn}, {c.W, n}, {c.B, n}};
-  const Span outs[] = {{c.Y, mn}, {c.H, mn}, {c.mean, m}, {c.rstd, m}, {c.ws, c.ws_bytes}};
+  const size_t n = (size_t)c.N * weight_size(c.dtype), m = (size_t)c.M * 4;
+  const Span in[] = {{c.X, span(c.M, c.N, c.ldx, s)}, {c.R, span(c.M, c.N, c.ldr, s)},
+                     {c.W, n}, {c.B, n}};
+  const Span outs[] = {{c.Y, span(c.M, c.N, c.ldy, s)}, {c.H, span(c.M, c.N, c.ldh, s)},
+                       {c.mean, m}, {c.rstd, m}, {c.ws, c.ws_bytes}};
   if (!disjoint(in, 4, outs, 5)) return NORM_ERR_INVALID_ARG;
   return NORM_OK;
 }
@@ -478,12 +494,25 @@ norm_status_t check_bwd(const BwdCheck &c) {
   }
   if (c.M == 0) return NORM_OK;
   if (c.need_dx && (!c.X || !c.dY || !c.dX)) return NORM_ERR_INVALID_ARG;
+  if (c.need_dx) {
+    // the strides of the tensors the call has (dH and dR are optional)
+    if (!stride_ok(c.M, c.N, c.ldx) || !stride_ok(c.M, c.N, c.lddy) ||
+        !stride_ok(c.M, c.N, c.lddx) || (c.dH && !stride_ok(c.M, c.N, c.lddh)) ||
+        (c.dR && !stride_ok(c.M, c.N, c.lddr)))
+      return NORM_ERR_INVALID_ARG;
+    if (c.dR && c.dR == c.dX && c.lddr != c.lddx) return NORM_ERR_INVALID_ARG;
+  }
   const size_t s = elem_size(c.dtype);
-  const size_t mn = (size_t)c.M * (size_t)c.N * s, n = (size_t)c.N * weight_size(c.dtype),
-               m = (size_t)c.M * 4;
+  const size_t n = (size_t)c.N * weight_size(c.dtype), m = (size_t)c.M * 4;
   const void *dr = c.dR == c.dX ? nullptr : c.dR; // dR may alias dX
-  const Span in[] = {{c.X, mn}, {c.dY, mn}, {c.dH, mn}, {c.W, n}, {c.mean, m}, {c.rstd, m}};
-  const Span outs[] = {{c.dX, mn}, {dr, mn}, {c.dW, n}, {c.dB, n}, {c.ws, c.ws_bytes}};
+  const bool dx = c.need_dx != 0;
+  const Span in[] = {{c.X, dx ? span(c.M, c.N, c.ldx, s) : 0},
+                     {c.dY, dx ? span(c.M, c.N, c.lddy, s) : 0},
+                     {c.dH, dx ? span(c.M, c.N, c.lddh, s) : 0},
+                     {c.W, n}, {c.mean, m}, {c.rstd, m}};
+  const Span outs[] = {{c.dX, dx ? span(c.M, c.N, c.lddx, s) : 0},
+                       {dr, dx ? span(c.M, c.N, c.lddr, s) : 0},
+                       {c.dW, n}, {c.dB, n}, {c.ws, c.ws_bytes}};
   if (!disjoint(in, 6, outs, 5)) return NORM_ERR_INVALID_ARG;
   return NORM_OK;
 }
@@ -496,6 +525,14 @@ int common_align(const void *const *ptrs, int n) {
     if (ptrs[i]) bits |= (uintptr_t)ptrs[i];
   return (int)(bits & (~bits + 1)); // lowest set bit, at most 16
 }
+
+int fold_stride_align(int align, const int64_t *ld, int n, size_t elem_bytes) {
+  uintptr_t bits = (uintptr_t)(align > 0 ? align : 1);
+  for (int i = 0; i < n; ++i) bits |= (uintptr_t)((size_t)ld[i] * elem_bytes);
+  return (int)(bits & (~bits + 1));
+}
+
+size_t act_elem_size(norm_dtype_t d) { return elem_size(d); }
 
 size_t weight_align_need(norm_dtype_t d, int epv) {
   const size_t w = (size_t)epv * weight_size(d);

@@ -78,6 +78,7 @@ struct FwdCheck {
   float *mean, *rstd;
   void *ws;
   size_t ws_bytes;
+  int64_t ldx, ldr, ldy, ldh; // row strides in elements (each >= N)
 };
 norm_status_t check_fwd(const FwdCheck &c);
 
@@ -92,12 +93,18 @@ struct BwdCheck {
   size_t ws_bytes;
   int need_dx;  // stage 1 (fused pass) is part of the call
   int need_dw;  // stage 2 (column reduction) is part of the call
+  int64_t ldx, lddy, lddh, lddx, lddr; // row strides in elements (each >= N)
 };
 norm_status_t check_bwd(const BwdCheck &c);
 
 bool all_aligned16(const void *const *ptrs, int n);
 // The largest power of two, at most 16, dividing every non-null pointer (16 if all are null).
 int common_align(const void *const *ptrs, int n);
+// align lowered to the largest power of two that also divides each row stride in bytes (the
+// row starts of a strided tensor are aligned only that far)
+int fold_stride_align(int align, const int64_t *ld, int n, size_t elem_bytes);
+// bytes per element of the [M, N] tensors of a dtype
+size_t act_elem_size(norm_dtype_t d);
 // Alignment the weight-sized outputs (dW, dB) need for the vector stores of an access of epv
 // elements.
 size_t weight_align_need(norm_dtype_t d, int epv);

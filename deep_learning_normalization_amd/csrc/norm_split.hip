@@ -104,10 +104,10 @@ __global__ __launch_bounds__(SPLIT_LB) void split_stats_kernel(FwdArgs a) {
   const int64_t acc0 = c * a.chunk_acc;
   const int64_t left = (int64_t)a.nacc - acc0;
   const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
-  const int64_t base = row * (int64_t)a.N + acc0 * E;
-  const T *__restrict__ X = static_cast<const T *>(a.x) + base;
-  const T *__restrict__ Rr = RESID ? static_cast<const T *>(a.r) + base : nullptr;
-  T *__restrict__ H = RESID ? static_cast<T *>(a.h) + base : nullptr;
+  const int64_t col0 = acc0 * E;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + row * a.ldx + col0;
+  const T *__restrict__ Rr = RESID ? static_cast<const T *>(a.r) + row * a.ldr + col0 : nullptr;
+  T *__restrict__ H = RESID ? static_cast<T *>(a.h) + row * a.ldh + col0 : nullptr;
 
   float x[VPT][E];
   {
@@ -193,12 +193,13 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
   const int64_t acc0 = c * a.chunk_acc;
   const int64_t left = (int64_t)a.nacc - acc0;
   const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
-  const int64_t base = row * (int64_t)a.N + acc0 * E;
+  const int64_t col0 = acc0 * E;
   // the norm's input: the stored h for the residual variant, else X
-  const T *__restrict__ S = static_cast<const T *>(a.r ? a.h : a.x) + base;
+  const T *__restrict__ S = static_cast<const T *>(a.r ? a.h : a.x) + row * (a.r ? a.ldh : a.ldx) +
+                            col0;
   const TW *__restrict__ W = static_cast<const TW *>(a.w) + acc0 * E;
   const TW *__restrict__ Bb = a.b ? static_cast<const TW *>(a.b) + acc0 * E : nullptr;
-  T *__restrict__ Y = static_cast<T *>(a.y) + base;
+  T *__restrict__ Y = static_cast<T *>(a.y) + row * a.ldy + col0;
 
   raw rx[VPT];
   WAcc<T, TW, EV> rw[VPT], rb[VPT];
@@ -269,9 +270,9 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_partial_kernel(BwdArgs a) 
   const int64_t acc0 = c * a.chunk_acc;
   const int64_t left = (int64_t)a.nacc - acc0;
   const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
-  const int64_t base = row * (int64_t)a.N + acc0 * E;
-  const T *__restrict__ X = static_cast<const T *>(a.x) + base;
-  const T *__restrict__ DY = static_cast<const T *>(a.dy) + base;
+  const int64_t col0 = acc0 * E;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + row * a.ldx + col0;
+  const T *__restrict__ DY = static_cast<const T *>(a.dy) + row * a.lddy + col0;
   const TW *__restrict__ W = static_cast<const TW *>(a.w) + acc0 * E;
   const float *mean_p = a.rstd ? a.mean : a.stats;
 
@@ -398,8 +399,8 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
         px[r][k] = A::zero();
         pdy[r][k] = A::zero();
         if (rv && v < nin) {
-          px[r][k] = A::ld(X + (row0 + r) * N + (int64_t)v * E);
-          pdy[r][k] = A::ld(DY + (row0 + r) * N + (int64_t)v * E);
+          px[r][k] = A::ld(X + (row0 + r) * a.ldx + (int64_t)v * E);
+          pdy[r][k] = A::ld(DY + (row0 + r) * a.lddy + (int64_t)v * E);
         }
       }
     }
@@ -471,16 +472,16 @@ __global__ __launch_bounds__(SPLIT_LB) void split_bwd_dx_kernel(BwdArgs a) {
           if constexpr (LN) accb[k][e] += df[e];
         }
         if (in) {
-          const int64_t off = row * N + (int64_t)v * E;
+          const int64_t off = (int64_t)v * E;
           if (DH) {
             float hf[E];
-            A::unpack(A::ld(DH + off), hf);
+            A::unpack(A::ld(DH + row * a.lddh + off), hf);
 #pragma unroll
             for (int e = 0; e < E; ++e) dx[e] += hf[e];
           }
           const raw p = A::pack(dx);
-          A::st(DX + off, p);
-          if (DR) A::st(DR + off, p);
+          A::st(DX + row * a.lddx + off, p);
+          if (DR) A::st(DR + row * a.lddr + off, p);
         }
       }
     }
@@ -621,6 +622,7 @@ norm_status_t split_bwd_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   if (a.rstd == nullptr) {
     FwdArgs f{};
     f.x = a.x;
+    f.ldx = a.ldx;
     f.rowpart = a.rowpart;
     f.M = a.M;
     f.N = a.N;

@@ -83,7 +83,6 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   const TeamGeom gm = team_geom<WAVE>(team_threads);
   const int nacc = a.nacc;
   const int64_t M = a.M;
-  const int64_t N = a.N;
   const T *__restrict__ X = static_cast<const T *>(a.x);
   const T *__restrict__ Rr = static_cast<const T *>(a.r);
   const TW *__restrict__ W = static_cast<const TW *>(a.w);
@@ -115,15 +114,15 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = live && row0 + r < M;
-      const int64_t base = (row0 + r) * N;
+      const int64_t row = row0 + r;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
         px[r][k] = A::zero();
         if (RESID) pr[r][k] = A::zero();
         if (rv && v < nacc) {
-          px[r][k] = A::ld(X + base + (int64_t)v * E);
-          if (RESID) pr[r][k] = A::ld(Rr + base + (int64_t)v * E);
+          px[r][k] = A::ld(X + row * a.ldx + (int64_t)v * E);
+          if (RESID) pr[r][k] = A::ld(Rr + row * a.ldr + (int64_t)v * E);
         }
       }
     }
@@ -156,7 +155,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         const bool rv = row0 + r < M;
-        const int64_t base = (row0 + r) * N;
+        const int64_t hbase = (row0 + r) * a.ldh;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
           A::unpack(rx[r][k], x[r][k]);
@@ -169,7 +168,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
             const raw hp = A::pack(f);
             A::unpack(hp, x[r][k]);
             const int v = gm.t + k * gm.tt;
-            if (rv && v < nacc) A::st(H + base + (int64_t)v * E, hp);
+            if (rv && v < nacc) A::st(H + hbase + (int64_t)v * E, hp);
           }
         }
       }
@@ -245,7 +244,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
     for (int r = 0; r < ROWS; ++r) {
       const int64_t row = row0 + r;
       if (row >= M) continue;
-      const int64_t base = row * N;
+      const int64_t ybase = row * a.ldy;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
@@ -254,7 +253,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
           for (int e = 0; e < E; ++e)
             y[e] = ((x[r][k][e] - mean1[r]) - delta[r]) * rstd[r] * w[k][e] + b[k][e];
-          A::st(Y + base + (int64_t)v * E, A::pack(y));
+          A::st(Y + ybase + (int64_t)v * E, A::pack(y));
         }
       }
       if (gm.t == 0) {
@@ -319,7 +318,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = live && row0 + r < M;
-      const int64_t base = (row0 + r) * N;
+      const int64_t row = row0 + r;
       pm[r] = 0.0f;
       pr[r] = 0.0f;
       if (have_stats) {
@@ -333,8 +332,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         px[r][k] = A::zero();
         pdy[r][k] = A::zero();
         if (rv && v < nacc) {
-          px[r][k] = A::ld(X + base + (int64_t)v * E);
-          pdy[r][k] = A::ld(DY + base + (int64_t)v * E);
+          px[r][k] = A::ld(X + row * a.ldx + (int64_t)v * E);
+          pdy[r][k] = A::ld(DY + row * a.lddy + (int64_t)v * E);
         }
       }
     }
@@ -485,7 +484,6 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
     for (int r = 0; r < ROWS; ++r) {
       const int64_t row = row0 + r;
       if (row >= M) continue; // rows past M add nothing to dW / dB and write nothing
-      const int64_t base = row * N;
       const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
       const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
       const float c2 =
@@ -523,16 +521,16 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           accw[k][e] = __builtin_fmaf(df[e], xh, accw[k][e]);
           if constexpr (LN) accb[k][e] += df[e];
         }
-        const int64_t off = base + (int64_t)v * E;
+        const int64_t off = (int64_t)v * E;
         if (DH) {
           float hf[E];
-          A::unpack(A::ld(DH + off), hf);
+          A::unpack(A::ld(DH + row * a.lddh + off), hf);
 #pragma unroll
           for (int e = 0; e < E; ++e) dx[e] += hf[e];
         }
         const raw p = A::pack(dx);
-        A::st(DX + off, p);
-        if (DR) A::st(DR + off, p);
+        A::st(DX + row * a.lddx + off, p);
+        if (DR) A::st(DR + row * a.lddr + off, p);
       }
     }
   }

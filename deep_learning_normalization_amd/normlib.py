@@ -39,15 +39,20 @@ def dtype_code(act, weight=None):
         return MIXED[act]
     raise ValueError("unsupported dtype pair: activations %s, weights %s" % (act, weight))
 
-SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_workspace_size",
-           "norm_plan", "norm_set_tuning", "norm_set_launch_events", "norm_status_string",
-           "norm_version")
+SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fwd_ex",
+           "norm_bwd_ex", "norm_bwd_fused_ex", "norm_workspace_size", "norm_plan",
+           "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version")
 
 
 class NormError(RuntimeError):
     def __init__(self, status, where):
         self.status = status
         super().__init__("%s: %s" % (where, status_string(status)))
+
+
+class RowStrides(ctypes.Structure):
+    """norm_row_strides_t: elements between row starts of each [M, N] tensor (0: N)."""
+    _fields_ = [(name, ctypes.c_int64) for name in ("x", "r", "y", "h", "dy", "dh", "dx", "dr")]
 
 
 class _Plan(ctypes.Structure):
@@ -80,6 +85,10 @@ def lib():
         L.norm_bwd_fused.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp,
                                      vp, sz, vp]
         L.norm_bwd_reduce.argtypes = [i32, i64, i64, i32, vp, vp, vp, sz, vp]
+        ld = ctypes.POINTER(RowStrides)
+        L.norm_fwd_ex.argtypes = L.norm_fwd.argtypes[:-1] + [ld, vp]
+        L.norm_bwd_ex.argtypes = L.norm_bwd.argtypes[:-1] + [ld, vp]
+        L.norm_bwd_fused_ex.argtypes = L.norm_bwd_fused.argtypes[:-1] + [ld, vp]
         L.norm_workspace_size.argtypes = [i32, i32, i32, i64, i64, i32,
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.norm_plan.argtypes = [i32, i32, i32, i64, i64, i32, i32, i32, ctypes.POINTER(_Plan)]
@@ -89,8 +98,8 @@ def lib():
         L.norm_status_string.restype = ctypes.c_char_p
         L.norm_version.argtypes = []
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
-                     "norm_workspace_size", "norm_plan", "norm_set_tuning",
-                     "norm_set_launch_events"):
+                     "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_workspace_size",
+                     "norm_plan", "norm_set_tuning", "norm_set_launch_events"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
         _lib = L
@@ -122,11 +131,25 @@ def _stream(stream):
 
 
 def _check_mat(t, M, N, dtype, name):
+    """A CUDA [M, N] tensor of `dtype` whose rows are contiguous (row stride >= N allowed)."""
     if t is None:
         return
-    if t.dtype != dtype or t.numel() != M * N or not t.is_contiguous() or not t.is_cuda:
-        raise ValueError("%s must be a contiguous CUDA %s tensor of %d x %d elements"
+    if (t.dtype != dtype or tuple(t.shape) != (M, N) or not t.is_cuda or
+            (M > 1 and t.stride(0) < N) or (N > 1 and t.stride(1) != 1)):
+        raise ValueError("%s must be a CUDA %s tensor of %d x %d elements with contiguous rows"
                          % (name, dtype, M, N))
+
+
+def _strides(**mats):
+    """RowStrides for the named [M, N] tensors, or None when every row stride is N."""
+    ld = RowStrides()
+    strided = False
+    for name, t in mats.items():
+        if t is None or t.shape[0] <= 1:
+            continue
+        setattr(ld, name, t.stride(0))
+        strided |= t.stride(0) != t.shape[1]
+    return ctypes.byref(ld) if strided else None
 
 
 def _check_vec(t, n, dtype, name):
@@ -159,9 +182,9 @@ def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=N
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
-    st = lib().norm_fwd(_kind(kind), _ptr(X), _ptr(R), _ptr(W), _ptr(B), float(eps), M, N,
-                        dtype_code(dt, wdt), _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
-                        _stream(stream))
+    st = lib().norm_fwd_ex(_kind(kind), _ptr(X), _ptr(R), _ptr(W), _ptr(B), float(eps), M, N,
+                           dtype_code(dt, wdt), _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
+                           _strides(x=X, r=R, y=Y, h=H), _stream(stream))
     _raise(st, "norm_fwd")
 
 
@@ -176,9 +199,10 @@ def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, str
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
-    st = lib().norm_bwd(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
-                        _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX), _ptr(dR),
-                        _ptr(dW), _ptr(dB), wp, wb, _stream(stream))
+    st = lib().norm_bwd_ex(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
+                           _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX), _ptr(dR),
+                           _ptr(dW), _ptr(dB), wp, wb,
+                           _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR), _stream(stream))
     _raise(st, "norm_bwd")
 
 
@@ -192,9 +216,10 @@ def norm_bwd_fused(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, workspace, strea
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
-    st = lib().norm_bwd_fused(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
-                              _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX),
-                              _ptr(dR), wp, wb, _stream(stream))
+    st = lib().norm_bwd_fused_ex(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
+                                 _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX),
+                                 _ptr(dR), wp, wb, _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR),
+                                 _stream(stream))
     _raise(st, "norm_bwd_fused")
 
 

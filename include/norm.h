@@ -149,6 +149,38 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
                        void *dB, void *workspace, size_t workspace_bytes, norm_stream_t stream);
 
 /*
+ * Row strides for the _ex variants below: the number of elements between the starts of
+ * consecutive rows of each [M, N] tensor, so a tensor may be a row-strided view (for example
+ * the query rows inside a fused query/key/value buffer). 0 means N (contiguous rows); any other
+ * value must be >= N, and rows must not overlap one another or any other tensor of the call
+ * (overlap is judged on the span (M - 1) * stride + N). Forward: x (X), r (R), y (Y), h (H).
+ * Backward: x (its X), dy, dh, dx, dr; dR may alias dX only with the same stride.
+ * Accesses are sized by the alignment common to the pointers and to every stride in bytes.
+ */
+typedef struct {
+  int64_t x, r, y, h;
+  int64_t dy, dh, dx, dr;
+} norm_row_strides_t;
+
+/* norm_fwd, norm_bwd and norm_bwd_fused with row strides (row_strides NULL: contiguous, the
+ * same as the calls above). Everything else is as documented there. */
+norm_status_t norm_fwd_ex(norm_kind_t kind, const void *X, const void *R, const void *W,
+                          const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
+                          void *Y, void *H, float *mean, float *rstd, void *workspace,
+                          size_t workspace_bytes, const norm_row_strides_t *row_strides,
+                          norm_stream_t stream);
+norm_status_t norm_bwd_ex(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                          const void *W, const float *mean, const float *rstd, float eps,
+                          int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                          void *dW, void *dB, void *workspace, size_t workspace_bytes,
+                          const norm_row_strides_t *row_strides, norm_stream_t stream);
+norm_status_t norm_bwd_fused_ex(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                                const void *W, const float *mean, const float *rstd, float eps,
+                                int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                                void *workspace, size_t workspace_bytes,
+                                const norm_row_strides_t *row_strides, norm_stream_t stream);
+
+/*
  * The two stages of norm_bwd, for callers that want them apart (for example to time the
  * fused pass alone, or to reduce the dW/dB partials later). norm_bwd_fused writes dX (and dR)
  * and leaves fp32 column partials in the workspace; norm_bwd_reduce turns those partials into

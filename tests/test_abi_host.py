@@ -113,6 +113,55 @@ def test_bwd_rejects(kw):
     assert _bwd(**kw) == nl.ERR_INVALID_ARG
 
 
+def _strides(**kw):
+    ld = nl.RowStrides()
+    for k, v in kw.items():
+        setattr(ld, k, v)
+    return ctypes.byref(ld)
+
+
+def _fwd_ex(ld, **kw):
+    a = dict(kind=0, X=FAKE, R=None, W=FAKE * 2, B=None, eps=1e-5, M=4, N=8, dtype=1,
+             Y=FAKE * 3, H=None, mean=None, rstd=None, ws=None, wsb=0, stream=None)
+    a.update(kw)
+    return nl.lib().norm_fwd_ex(a["kind"], a["X"], a["R"], a["W"], a["B"], a["eps"], a["M"],
+                                a["N"], a["dtype"], a["Y"], a["H"], a["mean"], a["rstd"], a["ws"],
+                                a["wsb"], ld, a["stream"])
+
+
+def _bwd_ex(ld, **kw):
+    a = dict(kind=0, X=FAKE, dY=FAKE * 2, dH=None, W=FAKE * 3, mean=None, rstd=None, eps=1e-5,
+             M=4, N=8, dtype=1, dX=FAKE * 4, dR=None, dW=FAKE * 5, dB=None, ws=None, wsb=0,
+             stream=None)
+    a.update(kw)
+    return nl.lib().norm_bwd_ex(a["kind"], a["X"], a["dY"], a["dH"], a["W"], a["mean"],
+                                a["rstd"], a["eps"], a["M"], a["N"], a["dtype"], a["dX"], a["dR"],
+                                a["dW"], a["dB"], a["ws"], a["wsb"], ld, a["stream"])
+
+
+def test_row_strides_on_the_host():
+    # a NULL struct and all-zero strides are the contiguous call
+    assert _fwd_ex(None) == _fwd() == nl.ERR_HIP
+    assert _fwd_ex(_strides()) == nl.ERR_HIP
+    # a stride below N is rejected; N or more is accepted (then no device)
+    assert _fwd_ex(_strides(x=7)) == nl.ERR_INVALID_ARG
+    assert _fwd_ex(_strides(y=-8)) == nl.ERR_INVALID_ARG
+    assert _fwd_ex(_strides(x=24, y=9)) == nl.ERR_HIP
+    # spans grow with the stride: X rows 3 x 64 elements apart (bf16) now reach Y at FAKE * 3
+    # only if (M - 1) * ld + N elements cover 2 MiB: M = 4, ld = 2^19 does
+    assert _fwd_ex(_strides(x=1 << 19)) == nl.ERR_INVALID_ARG
+    assert _fwd_ex(_strides(x=1 << 17)) == nl.ERR_HIP
+    # a residual stride is checked only with R
+    assert _fwd_ex(_strides(r=3)) == nl.ERR_HIP
+    assert _fwd_ex(_strides(r=3), R=FAKE * 5, H=FAKE * 6) == nl.ERR_INVALID_ARG
+    # backward: dR may alias dX only with the same stride
+    assert _bwd_ex(_strides(dx=16, dr=16), dR=FAKE * 4) == nl.ERR_HIP
+    assert _bwd_ex(_strides(dx=16, dr=8), dR=FAKE * 4) == nl.ERR_INVALID_ARG
+    assert _bwd_ex(_strides(dy=5)) == nl.ERR_INVALID_ARG
+    # a stride overflowing the addressable span
+    assert _fwd_ex(_strides(x=1 << 60)) == nl.ERR_INVALID_ARG
+
+
 def test_dr_may_alias_dx_and_zero_rows_need_no_pointers():
     # dR == dX passes the checks; with no device the call then fails at the device query
     assert _bwd(dR=FAKE * 4) == nl.ERR_HIP

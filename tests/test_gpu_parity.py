@@ -17,7 +17,8 @@ import torch
 
 import oracle
 from deep_learning_normalization_amd import inputs, normlib as nl
-from tests.parity import (check_colsums, check_values, dx_floor, run_and_check, tuned)
+from tests.parity import (check_colsums, check_h, check_values, dx_floor, run_and_check,
+                          tuned)
 
 pytestmark = pytest.mark.gpu
 
@@ -339,6 +340,110 @@ def test_residual_full_shape_sample():
 def test_backward_without_saved_stats(kind, N):
     _say("no saved stats %s N=%d" % (kind, N))
     run_and_check(_small(kind, "bf16", 37, N, seed=N), stats=False)
+
+
+# ---- row-strided tensors -----------------------------------------------------------------------
+
+def _strided_like(src, ld, col0, fill):
+    """A CUDA view with src's values, row stride ld, starting col0 elements into each row of a
+    [M, ld] buffer filled with `fill` (whose other columns must stay untouched)."""
+    M, N = src.shape
+    buf = torch.full((M, ld), fill, dtype=src.dtype, device="cuda")
+    v = buf[:, col0:col0 + N]
+    v.copy_(src.to("cuda"))
+    return buf, v
+
+
+# (kind, N, input stride, input column offset, output stride): the query rows of a fused
+# [M, 3N] projection (stride 3N, offset 0 or N), padded rows, and strides that only allow
+# narrower accesses (4100 bf16 elements: 8 bytes)
+STRIDED = [("layernorm", 512, 1536, 512, 520), ("rmsnorm", 512, 1536, 0, 512),
+           ("layernorm", 4096, 12288, 4096, 4100), ("rmsnorm", 4096, 4104, 8, 4096),
+           ("rmsnorm", 12288, 36864, 12288, 12296), ("layernorm", 20000, 20008, 0, 20004),
+           ("layernorm", 4100, 4108, 4, 4100)]
+
+
+@pytest.mark.parametrize("kind,N,ldi,col0,ldo", STRIDED, ids=lambda v: str(v))
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_row_strided_tensors(kind, N, ldi, col0, ldo, dt):
+    """Inputs and outputs as row-strided views: results match the oracle on the contiguous
+    values, and the columns between the rows of every output keep their fill."""
+    M = 37 if N <= 12288 else 9
+    w = _small(kind, dt, M, N, seed=N + ldi)
+    t = inputs.make(w)
+    sentinel = -7.0
+    _, X = _strided_like(t["X"], ldi, col0, 0.0)
+    _, dY = _strided_like(t["dY"], ldi, col0, 0.0)
+    W = t["W"].cuda()
+    B = t["B"].cuda() if t["B"] is not None else None
+    ybuf, Y = _strided_like(torch.zeros(M, N, dtype=X.dtype), ldo, ldo - N, sentinel)
+    xbuf, dX = _strided_like(torch.zeros(M, N, dtype=X.dtype), ldo, 0, sentinel)
+    mean = torch.empty(M, dtype=torch.float32, device="cuda") if kind == "layernorm" else None
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    _say("strided %s %s N=%d in ld %d (+%d) out ld %d" % (kind, dt, N, ldi, col0, ldo))
+    nl.norm_fwd(kind, X, None, W, B, w.eps, Y, None, mean, rstd,
+                nl.workspace(kind, X.dtype, nl.PASS_FWD, M, N))
+    dW = torch.empty_like(W)
+    dB = torch.empty_like(W) if kind == "layernorm" else None
+    nl.norm_bwd(kind, X, dY, None, W, mean, rstd, w.eps, dX, None, dW, dB,
+                nl.workspace(kind, X.dtype, nl.PASS_BWD, M, N))
+    torch.cuda.synchronize()
+    bits = {k: inputs.host_bits(t[k]) for k in ("X", "W", "B", "dY")}
+    code = oracle.F32 if dt == "f32" else oracle.BF16
+    k = oracle.LAYERNORM if kind == "layernorm" else oracle.RMSNORM
+    eps = float(np.float32(w.eps))
+    f = oracle.fwd(k, code, bits["X"], bits["W"], bits["B"], eps=eps)
+    g = oracle.bwd(k, code, bits["X"], bits["dY"], bits["W"], eps=eps)
+    check_values("Y", Y.double().cpu().numpy(), f["y"], dt)
+    floor = dx_floor(np.arange(M), t["dY"], t["W"], f["rstd"], N).reshape(M, N)
+    check_values("dX", dX.double().cpu().numpy(), g["dx"], dt, floor)
+    check_colsums("dW", dW.double().cpu().numpy(), g["dw"], dt)
+    if dB is not None:
+        check_colsums("dB", dB.double().cpu().numpy(), g["db"], dt)
+    # the gaps between output rows are untouched
+    for buf, c0 in ((ybuf, ldo - N), (xbuf, 0)):
+        gap = torch.ones(ldo, dtype=torch.bool, device="cuda")
+        gap[c0:c0 + N] = False
+        assert (buf[:, gap] == sentinel).all()
+
+
+@pytest.mark.parametrize("N", [512, 4096, 7168])
+def test_row_strided_residual(N):
+    """Residual RMSNorm with R, X, H, dY, dH, dX and dR all row-strided views."""
+    M = 33
+    w = _small("rmsnorm", "bf16", M, N, seed=N, x=inputs.normal(0, 0.5), r=inputs.normal(0, 1),
+               dh=inputs.normal(0, 0.5))
+    t = inputs.make(w)
+    ld = N + 24
+    _, X = _strided_like(t["X"], 3 * N, N, 0.0)
+    _, R = _strided_like(t["R"], 3 * N, 0, 0.0)
+    _, dY = _strided_like(t["dY"], ld, 8, 0.0)
+    _, dH = _strided_like(t["dH"], ld, 16, 0.0)
+    W = t["W"].cuda()
+    _, Y = _strided_like(torch.zeros(M, N, dtype=X.dtype), ld, 0, 0.0)
+    _, H = _strided_like(torch.zeros(M, N, dtype=X.dtype), ld, 24, 0.0)
+    _, dX = _strided_like(torch.zeros(M, N, dtype=X.dtype), ld, 8, 0.0)
+    _, dR = _strided_like(torch.zeros(M, N, dtype=X.dtype), ld + 8, 0, 0.0)
+    rstd = torch.empty(M, dtype=torch.float32, device="cuda")
+    _say("strided residual N=%d" % N)
+    nl.norm_fwd("rmsnorm", X, R, W, None, w.eps, Y, H, None, rstd,
+                nl.workspace("rmsnorm", X.dtype, nl.PASS_FWD, M, N, True))
+    dW = torch.empty_like(W)
+    nl.norm_bwd("rmsnorm", H, dY, dH, W, None, rstd, w.eps, dX, dR, dW, None,
+                nl.workspace("rmsnorm", X.dtype, nl.PASS_BWD, M, N))
+    torch.cuda.synchronize()
+    bits = {k: inputs.host_bits(t[k]) for k in ("X", "W", "R", "dY", "dH")}
+    eps = float(np.float32(w.eps))
+    f = oracle.fwd(oracle.RMSNORM, oracle.BF16, bits["X"], bits["W"], None, bits["R"], eps=eps,
+                   want_h=True)
+    check_h(H.double().cpu().numpy(), f["h"], "bf16")
+    check_values("Y", Y.double().cpu().numpy(), f["y"], "bf16")
+    hbits = oracle.round_bf16(f["h"])
+    g = oracle.bwd(oracle.RMSNORM, oracle.BF16, hbits, bits["dY"], bits["W"], dH=bits["dH"],
+                   eps=eps)
+    check_values("dX", dX.double().cpu().numpy(), g["dx"], "bf16")
+    assert torch.equal(dR, dX)
+    check_colsums("dW", dW.double().cpu().numpy(), g["dw"], "bf16")
 
 
 # ---- pointer alignment sets the access width -------------------------------------------------
