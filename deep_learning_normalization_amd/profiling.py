@@ -30,7 +30,9 @@ import glob
 import hashlib
 import json
 import os
+import shutil
 import statistics
+import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
@@ -54,6 +56,25 @@ def _one(directory, suffix):
     return hits[0]
 
 
+_demangled = {}
+
+
+def _name(raw):
+    """A kernel name as rocprofv3 reports it, demangled where it left it mangled (it does not
+    demangle _Float16 template arguments, DF16_; they are shown as 'half')."""
+    if not raw.startswith("_Z"):
+        return raw
+    if raw not in _demangled:
+        tool = shutil.which("c++filt")
+        out = raw
+        if tool:
+            r = subprocess.run([tool], input=raw.replace("DF16_", "Dh"), capture_output=True,
+                               text=True)
+            out = r.stdout.strip() or raw
+        _demangled[raw] = out if out != raw.replace("DF16_", "Dh") else raw
+    return _demangled[raw]
+
+
 def _short(name):
     """Kernel name without the argument list; torch kernels cut to their first words."""
     base = name.split("(")[0] if "dln::" in name else name[:60]
@@ -63,6 +84,10 @@ def _short(name):
 def stats(trace_dir, out, cmd):
     rows = list(csv.DictReader(open(_one(trace_dir, "_kernel_stats.csv"))))
     trace = list(csv.DictReader(open(_one(trace_dir, "_kernel_trace.csv"))))
+    for r in rows:
+        r["Name"] = _name(r["Name"])
+    for r in trace:
+        r["Kernel_Name"] = _name(r["Kernel_Name"])
     trace.sort(key=lambda r: int(r["Start_Timestamp"]))
     ours = [r for r in trace if "dln::" in r["Kernel_Name"]]
     gaps = {}
@@ -93,7 +118,7 @@ def _counter(directory, counter):
     for r in csv.DictReader(open(path)):
         if r["Counter_Name"] != counter:
             continue
-        per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+        per.setdefault(_name(r["Kernel_Name"]), []).append(float(r["Counter_Value"]))
     return per
 
 
@@ -175,9 +200,10 @@ def _kernel_rows(trace_dir):
     rows = list(csv.DictReader(open(_one(trace_dir, "_kernel_trace.csv"))))
     per = {}
     for r in rows:
-        if "dln::" not in r["Kernel_Name"]:
+        name = _name(r["Kernel_Name"])
+        if "dln::" not in name:
             continue
-        per.setdefault(_short(r["Kernel_Name"]), []).append(
+        per.setdefault(_short(name), []).append(
             (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
     return per
 
