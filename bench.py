@@ -172,6 +172,36 @@ def timed_workload(w, steps, warmup, torch, nl, min_footprint=1 << 30, max_sets=
     return out
 
 
+def stats_only(w, torch, nl, steps, warmup):
+    """The statistics pass alone (norm_stats) on the workload's X: mean (LayerNorm) and rstd,
+    no Y. X sets rotate over more than 1 GiB so every pass starts from HBM. Returns the mean
+    loop time per call (launch gaps included) and its algorithmic bytes."""
+    from deep_learning_normalization_amd import inputs
+    X0 = inputs.make(w)["X"].cuda()
+    M, N = w.M, w.N
+    nsets = max(2, -(-(1 << 30) // (X0.numel() * X0.element_size())))
+    xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
+    ln = w.kind == "layernorm"
+    mean = torch.empty(M, device="cuda") if ln else None
+    rstd = torch.empty(M, device="cuda")
+    ws = nl.workspace(w.kind, X0.dtype, nl.PASS_FWD, M, N)
+    for i in range(warmup):
+        nl.norm_stats(w.kind, xs[i % nsets], None, w.eps, None, mean, rstd, ws)
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for i in range(steps):
+        nl.norm_stats(w.kind, xs[i % nsets], None, w.eps, None, mean, rstd, ws)
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / steps * 1e3
+    nbytes = M * N * X0.element_size() + (8 if ln else 4) * M
+    del xs
+    torch.cuda.empty_cache()
+    return us, nbytes
+
+
 def copy_ceiling(torch, nbytes=1 << 30, iters=20):
     """Achievable HBM bandwidth of a plain device copy (torch's copy kernel), GB/s moved
     (read + write). Two buffer pairs alternate so neither copy starts in cache."""
@@ -295,6 +325,7 @@ def main():
     w = inputs.LN_BF16_16384x4096
     r = timed_workload(w, args.steps, args.warmup, torch, nl)
     copy_gbps, copy_us = copy_ceiling(torch)
+    st_us, st_bytes = stats_only(w, torch, nl, args.steps, args.warmup)
     M, N = w.M, w.N
     fb = traffic.fwd_bytes(w.kind, w.dtype, M, N)
     bb = traffic.bwd_bytes(w.kind, w.dtype, M, N)
@@ -338,6 +369,9 @@ def main():
                     "rows_per_s": round(M / (ms * 1e-3), 1)},
         "copy_ceiling": {"GBps": round(copy_gbps, 1), "us_per_GiB_copy": round(copy_us, 2),
                          "kernel": "HIP runtime device copy of 1 GiB, read + write counted"},
+        "stats_only": {"us": round(st_us, 3), "GBps": round(st_bytes / (st_us * 1e-6) / 1e9, 1),
+                       "bytes": st_bytes,
+                       "what": "norm_stats: mean and rstd without Y (loop time per call)"},
     }
     if traffic_bytes is None:
         line["roofline"]["traffic_note"] = why

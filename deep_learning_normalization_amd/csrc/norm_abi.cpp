@@ -61,6 +61,12 @@ Strides resolve(const norm_row_strides_t *ld, int64_t N) {
                  pick(ld->dy), pick(ld->dh), pick(ld->dx), pick(ld->dr)};
 }
 
+norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const void *W,
+                         const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
+                         void *Y, void *H, float *mean, float *rstd, void *workspace,
+                         size_t workspace_bytes, const Strides &ld, norm_pass_t pass,
+                         norm_stream_t stream);
+
 // Plan, workspace check and argument block of the backward's fused pass.
 norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const void *dH,
                         const void *W, const float *mean, const float *rstd, float eps,
@@ -169,9 +175,39 @@ norm_status_t norm_fwd_ex(norm_kind_t kind, const void *X, const void *R, const 
   if (N <= 0) return NORM_ERR_INVALID_ARG;
   const Strides ld = resolve(row_strides, N);
   dln::FwdCheck c{kind, dtype, X, R, W, B, eps, M, N, Y, H, mean, rstd, workspace,
-                  workspace_bytes, ld.x, ld.r, ld.y, ld.h};
+                  workspace_bytes, ld.x, ld.r, ld.y, ld.h, 0};
   norm_status_t st = dln::check_fwd(c);
   if (st != NORM_OK || M == 0) return st;
+  return fwd_launch(kind, X, R, W, B, eps, M, N, dtype, Y, H, mean, rstd, workspace,
+                    workspace_bytes, ld, NORM_PASS_FWD, stream);
+}
+
+norm_status_t norm_stats(norm_kind_t kind, const void *X, const void *R, float eps, int64_t M,
+                         int64_t N, norm_dtype_t dtype, void *H, float *mean, float *rstd,
+                         void *workspace, size_t workspace_bytes,
+                         const norm_row_strides_t *row_strides, norm_stream_t stream) {
+  const EventsDisarm disarm;
+  if (N <= 0) return NORM_ERR_INVALID_ARG;
+  const Strides ld = resolve(row_strides, N);
+  dln::FwdCheck c{kind, dtype, X, R, nullptr, nullptr, eps, M, N, nullptr, H, mean, rstd,
+                  workspace, workspace_bytes, ld.x, ld.r, ld.y, ld.h, 1};
+  norm_status_t st = dln::check_fwd(c);
+  if (st != NORM_OK || M == 0) return st;
+  return fwd_launch(kind, X, R, nullptr, nullptr, eps, M, N, dtype, nullptr, H, mean, rstd,
+                    workspace, workspace_bytes, ld, NORM_PASS_STATS, stream);
+}
+
+} // extern "C"
+
+namespace {
+
+// Plan and queue a checked forward (Y and W NULL: the statistics pass alone).
+norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const void *W,
+                         const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
+                         void *Y, void *H, float *mean, float *rstd, void *workspace,
+                         size_t workspace_bytes, const Strides &ld, norm_pass_t pass,
+                         norm_stream_t stream) {
+  norm_status_t st;
   int cu = 0;
   st = current_cu_count(&cu);
   if (st != NORM_OK) return st;
@@ -180,8 +216,7 @@ norm_status_t norm_fwd_ex(norm_kind_t kind, const void *X, const void *R, const 
   const int align = dln::fold_stride_align(dln::common_align(ptrs, 6), lds, 4,
                                            dln::act_elem_size(dtype));
   dln::Plan p;
-  st = dln::make_plan(kind, dtype, NORM_PASS_FWD, M, N, R != nullptr, align, cu,
-                      dln::tuning(), &p);
+  st = dln::make_plan(kind, dtype, pass, M, N, R != nullptr, align, cu, dln::tuning(), &p);
   if (st != NORM_OK) return st;
   st = ws_ok(p, workspace, workspace_bytes);
   if (st != NORM_OK) return st;
@@ -212,6 +247,10 @@ norm_status_t norm_fwd_ex(norm_kind_t kind, const void *X, const void *R, const 
   if (p.scheme == NORM_SCHEME_SPLIT) return dln::launch_split_fwd(p, dtype, a, s);
   return dln::launch_team_fwd(p, dtype, a, s);
 }
+
+} // namespace
+
+extern "C" {
 
 norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const void *dH,
                        const void *W, const float *mean, const float *rstd, float eps,

@@ -79,6 +79,7 @@ struct FwdCheck {
   void *ws;
   size_t ws_bytes;
   int64_t ldx, ldr, ldy, ldh; // row strides in elements (each >= N)
+  int stats_only;             // the statistics pass alone: no W, B, Y; some output required
 };
 norm_status_t check_fwd(const FwdCheck &c);
 

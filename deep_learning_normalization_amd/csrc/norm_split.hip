@@ -238,6 +238,21 @@ __global__ __launch_bounds__(SPLIT_LB) void split_norm_kernel(FwdArgs a) {
   }
 }
 
+// ---- statistics-only forward: combine the chunk statistics, write mean and rstd ------------
+
+__global__ __launch_bounds__(SPLIT_LB) void split_stats_combine_kernel(FwdArgs a, int E) {
+  __shared__ __align__(16) float red[RED_FLOATS];
+  const int64_t row = blockIdx.x;
+  int slot = 0;
+  float shift, delta, rstd;
+  combine_row_stats(a.rowpart + row * a.chunks * RP, a.chunks, a.chunk_acc, a.nacc, E,
+                    a.layernorm, a.inv_n, a.eps, red, slot, shift, delta, rstd);
+  if (threadIdx.x == 0) {
+    if (a.mean) a.mean[row] = shift + delta;
+    if (a.rstd) a.rstd[row] = rstd;
+  }
+}
+
 // ---- backward: statistics when the forward's were not kept ------------------------------
 
 __global__ __launch_bounds__(SPLIT_LB) void split_finalize_stats_kernel(BwdArgs a, int E) {
@@ -539,8 +554,10 @@ template <typename T, typename TW, int EV, int V>
 hipError_t split_fwd_pair(const FwdArgs &a, hipStream_t s) {
   const dim3 grid((unsigned)(a.M * a.chunks)), block(SPLIT_LB);
   hipError_t e = split_stats_launch<T, EV, V>(a, a.r != nullptr, s);
-  if (e == hipSuccess) e = launch(split_norm_kernel<T, TW, EV, V>, grid, block, s, a);
-  return e;
+  if (e != hipSuccess) return e;
+  if (!a.y) // statistics only: one combine per row, no second pass over X
+    return launch(split_stats_combine_kernel, dim3((unsigned)a.M), block, s, a, EV);
+  return launch(split_norm_kernel<T, TW, EV, V>, grid, block, s, a);
 }
 
 template <typename T, typename TW, int EV, int V, int R>

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
     WAcc<T, TW, EV> rw, rb;
     rw.zero();
     rb.zero();
-    if (v < nacc) {
+    if (W && v < nacc) { // no weight: the statistics-only pass
       rw.load(W + (int64_t)v * E);
       if (Bb) rb.load(Bb + (int64_t)v * E);
     }
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
-        if (v < nacc) {
+        if (Y && v < nacc) { // no Y: the statistics-only pass
           float y[E];
 #pragma unroll
           for (int e = 0; e < E; ++e)

@@ -15,7 +15,7 @@ LIB_PATH = os.path.join(_HERE, "libnorm.so")
 
 LAYERNORM, RMSNORM = 0, 1
 F32, BF16, BF16_F32W, F16, F16_F32W = 0, 1, 2, 3, 4
-PASS_FWD, PASS_BWD = 0, 1
+PASS_FWD, PASS_BWD, PASS_STATS = 0, 1, 2
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT, SCHEME_LOOP = -1, 0, 1, 2, 3
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
 TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
@@ -40,7 +40,7 @@ def dtype_code(act, weight=None):
     raise ValueError("unsupported dtype pair: activations %s, weights %s" % (act, weight))
 
 SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fwd_ex",
-           "norm_bwd_ex", "norm_bwd_fused_ex", "norm_workspace_size", "norm_plan",
+           "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats", "norm_workspace_size", "norm_plan",
            "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version")
 
 
@@ -89,6 +89,7 @@ def lib():
         L.norm_fwd_ex.argtypes = L.norm_fwd.argtypes[:-1] + [ld, vp]
         L.norm_bwd_ex.argtypes = L.norm_bwd.argtypes[:-1] + [ld, vp]
         L.norm_bwd_fused_ex.argtypes = L.norm_bwd_fused.argtypes[:-1] + [ld, vp]
+        L.norm_stats.argtypes = [i32, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, sz, ld, vp]
         L.norm_workspace_size.argtypes = [i32, i32, i32, i64, i64, i32,
                                           ctypes.POINTER(ctypes.c_size_t)]
         L.norm_plan.argtypes = [i32, i32, i32, i64, i64, i32, i32, i32, ctypes.POINTER(_Plan)]
@@ -98,7 +99,8 @@ def lib():
         L.norm_status_string.restype = ctypes.c_char_p
         L.norm_version.argtypes = []
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
-                     "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_workspace_size",
+                     "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats",
+                     "norm_workspace_size",
                      "norm_plan", "norm_set_tuning", "norm_set_launch_events"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
@@ -186,6 +188,21 @@ def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=N
                            dtype_code(dt, wdt), _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
                            _strides(x=X, r=R, y=Y, h=H), _stream(stream))
     _raise(st, "norm_fwd")
+
+
+def norm_stats(kind, X, R, eps, H=None, mean=None, rstd=None, workspace=None, stream=None):
+    """Queue the statistics pass alone: mean (LayerNorm) and rstd, and H = R + X with R."""
+    M, N = X.shape
+    dt = X.dtype
+    for t, nm in ((X, "X"), (R, "R"), (H, "H")):
+        _check_mat(t, M, N, dt, nm)
+    _check_vec(mean, M, torch.float32, "mean")
+    _check_vec(rstd, M, torch.float32, "rstd")
+    wp, wb = _ws(workspace)
+    st = lib().norm_stats(_kind(kind), _ptr(X), _ptr(R), float(eps), M, N, DTYPES[dt], _ptr(H),
+                          _ptr(mean), _ptr(rstd), wp, wb, _strides(x=X, r=R, h=H),
+                          _stream(stream))
+    _raise(st, "norm_stats")
 
 
 def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, stream=None):

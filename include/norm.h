@@ -87,7 +87,11 @@ typedef enum {
 } norm_status_t;
 
 /* Which pass a workspace size or plan is asked for. */
-typedef enum { NORM_PASS_FWD = 0, NORM_PASS_BWD = 1 } norm_pass_t;
+typedef enum {
+  NORM_PASS_FWD = 0,
+  NORM_PASS_BWD = 1,
+  NORM_PASS_STATS = 2 /* norm_stats: the forward's statistics alone (workspace as the forward) */
+} norm_pass_t;
 
 /* Kernel scheme chosen for a shape. */
 typedef enum {
@@ -161,6 +165,21 @@ typedef struct {
   int64_t x, r, y, h;
   int64_t dy, dh, dx, dr;
 } norm_row_strides_t;
+
+/*
+ * The forward's statistics pass alone [P1 paras. 2-3, 6]: mean (LayerNorm) and rstd per row,
+ * and H = R + X when R is given, without normalising (no W, B or Y; about half the forward's
+ * HBM traffic). The statistics a consumer needs to apply the norm later, for example in the
+ * epilogue of a following matrix product ([P3] "Towards Free Normalization", items 3-4 and
+ * 9-10). Very long rows use the split scheme's per-chunk statistics over several workgroups
+ * and one combine per row.
+ *   Arguments as for norm_fwd; at least one of mean, rstd and H must be given; row_strides
+ *   may be NULL (contiguous). Workspace: norm_workspace_size(..., NORM_PASS_FWD, ...).
+ */
+norm_status_t norm_stats(norm_kind_t kind, const void *X, const void *R, float eps, int64_t M,
+                         int64_t N, norm_dtype_t dtype, void *H, float *mean, float *rstd,
+                         void *workspace, size_t workspace_bytes,
+                         const norm_row_strides_t *row_strides, norm_stream_t stream);
 
 /* norm_fwd, norm_bwd and norm_bwd_fused with row strides (row_strides NULL: contiguous, the
  * same as the calls above). Everything else is as documented there. */

@@ -162,6 +162,38 @@ def test_row_strides_on_the_host():
     assert _fwd_ex(_strides(x=1 << 60)) == nl.ERR_INVALID_ARG
 
 
+def _stats(**kw):
+    a = dict(kind=0, X=FAKE, R=None, eps=1e-5, M=4, N=8, dtype=1, H=None, mean=FAKE * 3,
+             rstd=FAKE * 4, ws=None, wsb=0, ld=None, stream=None)
+    a.update(kw)
+    return nl.lib().norm_stats(a["kind"], a["X"], a["R"], a["eps"], a["M"], a["N"], a["dtype"],
+                               a["H"], a["mean"], a["rstd"], a["ws"], a["wsb"], a["ld"],
+                               a["stream"])
+
+
+def test_stats_only_on_the_host():
+    assert _stats() == nl.ERR_HIP                              # valid: then no device
+    assert _stats(mean=None) == nl.ERR_HIP                     # rstd alone
+    assert _stats(mean=None, rstd=None) == nl.ERR_INVALID_ARG  # nothing to compute
+    assert _stats(mean=None, rstd=None, R=FAKE * 5, H=FAKE * 6) == nl.ERR_HIP  # H alone
+    assert _stats(kind=1) == nl.ERR_INVALID_ARG                # RMSNorm has no mean
+    assert _stats(kind=1, mean=None) == nl.ERR_HIP
+    assert _stats(R=FAKE * 5) == nl.ERR_INVALID_ARG            # R without H
+    assert _stats(X=None) == nl.ERR_INVALID_ARG
+    assert _stats(mean=FAKE + 8) == nl.ERR_INVALID_ARG         # an output inside X
+    assert _stats(eps=-1.0) == nl.ERR_INVALID_ARG
+    assert _stats(M=0, X=None) == nl.OK
+    # its plan: the forward's shapes on a persistent grid (8 workgroups per CU), the forward's
+    # workspace
+    for N in (512, 4096, 8192, 262144):
+        f = nl.norm_plan(0, BF, nl.PASS_FWD, 16384, N, cu_count=256)
+        st = nl.norm_plan(0, BF, nl.PASS_STATS, 16384, N, cu_count=256)
+        for k in ("scheme", "team_threads", "accesses_per_thread", "workspace_bytes"):
+            assert f[k] == st[k], (N, k)
+        if st["scheme"] == nl.SCHEME_BLOCK:
+            assert st["grid"] == min(16384, 256 * 8)
+
+
 def test_dr_may_alias_dx_and_zero_rows_need_no_pointers():
     # dR == dX passes the checks; with no device the call then fails at the device query
     assert _bwd(dR=FAKE * 4) == nl.ERR_HIP

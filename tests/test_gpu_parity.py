@@ -342,6 +342,53 @@ def test_backward_without_saved_stats(kind, N):
     run_and_check(_small(kind, "bf16", 37, N, seed=N), stats=False)
 
 
+# ---- the statistics pass alone ------------------------------------------------------------------
+
+# wave, block, split, 8-byte, element-wise and fp16 rows, and the residual variant
+STATS_CASES = [("layernorm", "bf16", 300, 512, False), ("rmsnorm", "bf16", 300, 512, False),
+               ("layernorm", "bf16", 129, 4096, False), ("rmsnorm", "f32", 129, 8192, False),
+               ("layernorm", "bf16", 5, 262144, False), ("rmsnorm", "bf16", 3, 300000, False),
+               ("layernorm", "bf16", 129, 4100, False), ("layernorm", "bf16", 65, 4097, False),
+               ("layernorm", "f16", 129, 4096, False), ("rmsnorm", "bf16", 129, 7168, True),
+               ("layernorm", "bf16", 9, 262144, True)]
+
+
+@pytest.mark.parametrize("kind,dt,M,N,resid", STATS_CASES, ids=lambda v: str(v))
+def test_stats_only(kind, dt, M, N, resid):
+    """norm_stats gives the oracle's mean and rstd (and H), bit for bit the statistics that
+    norm_fwd writes on the same inputs."""
+    extra = dict(x=inputs.normal(0, 0.5), r=inputs.normal(0, 1)) if resid else {}
+    w = _small(kind, dt, M, N, seed=N + M, **extra)
+    t = inputs.make(w)
+    X = t["X"].cuda()
+    R = t["R"].cuda() if resid else None
+    ln = kind == "layernorm"
+    mean = torch.full((M,), float("nan"), device="cuda") if ln else None
+    rstd = torch.full((M,), float("nan"), device="cuda")
+    H = torch.empty_like(X) if resid else None
+    _say("stats only %s %s %dx%d resid=%s" % (kind, dt, M, N, resid))
+    ws = nl.workspace(kind, X.dtype, nl.PASS_FWD, M, N, resid)
+    nl.norm_stats(kind, X, R, w.eps, H, mean, rstd, ws)
+    Y, H2, mean2, rstd2 = nl.forward(kind, X, t["W"].cuda(), t["B"].cuda() if ln else None,
+                                     w.eps, R=R)
+    torch.cuda.synchronize()
+    assert torch.equal(rstd, rstd2)
+    if ln:
+        assert torch.equal(mean, mean2)
+    if resid:
+        assert torch.equal(H, H2)
+    bits = {k: inputs.host_bits(t[k]) for k in ("X", "W", "B", "R")}
+    code = {"f32": oracle.F32, "bf16": oracle.BF16, "f16": oracle.F16}[dt]
+    k = oracle.LAYERNORM if ln else oracle.RMSNORM
+    f = oracle.fwd(k, code, bits["X"], bits["W"], bits["B"], bits["R"],
+                   eps=float(np.float32(w.eps)), want_h=resid)
+    from tests.parity import check_stats
+    check_stats(mean.double().cpu().numpy() if ln else None, rstd.double().cpu().numpy(),
+                f["mean"] if ln else None, f["rstd"])
+    if resid:
+        check_h(H.double().cpu().numpy(), f["h"], dt)
+
+
 # ---- row-strided tensors -----------------------------------------------------------------------
 
 def _strided_like(src, ld, col0, fill):
