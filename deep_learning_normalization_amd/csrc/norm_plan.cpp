@@ -240,7 +240,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.lb = kWaveThreads;
     p.team_threads = 64;
     const int64_t groups = cdiv(Mm, (int64_t)(kWaveThreads / 64) * rows);
-    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (bwd ? 2 : 8);
+    // 8- and 4-byte forwards stream better from 16 workgroups per CU (measured on MI355X:
+    // LayerNorm 65536 x 1002 57.8 -> 53.4 us)
+    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (bwd ? 2 : sc > 1 ? 16 : 8);
     p.grid = groups < cu * gpc ? groups : cu * gpc;
     p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_BLOCK) {
@@ -311,10 +313,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       const int64_t load = (int64_t)p.threads * vpt * rows; // full-width units
       const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1);
       p.grid = groups < cu * gpc ? groups : cu * gpc;
-    } else if (t.grid_per_cu > 0 || stats) {
+    } else if (t.grid_per_cu > 0 || stats || sc > 1) {
       // the statistics pass alone, with no stores to overlap, streams best from a persistent
-      // grid of 8 workgroups per CU (measured on MI355X: LayerNorm 16384 x 4096 30.6 -> 28.7 us)
-      const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : 8;
+      // grid of 8 workgroups per CU (measured on MI355X: LayerNorm 16384 x 4096 30.6 -> 28.7 us);
+      // 8- and 4-byte forwards from 16 (LayerNorm 16384 x 4100 54.4 -> 49.8 us, 16384 x 4098
+      // 68.8 -> 60.4 us)
+      const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : stats ? 8 : 16;
       p.grid = groups < cu * gpc ? groups : cu * gpc;
     } else {
       // Forward (measured on MI355X): short-lived workgroups of two row groups each (the second
@@ -328,8 +332,15 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // ones; 4-byte accesses are not compiled for it); one resident workgroup per CU, each
     // writing one partial row
     if (!vec || sc > 2 || nacc_eq > kLoopMaxEq) return NORM_ERR_UNSUPPORTED;
+    // Teams of the full 512 threads even where fewer would cover the row (the last segments
+    // are then partly empty): with one resident workgroup per CU the team size is the CU's
+    // whole parallelism (measured on MI355X: RMSNorm 16384 x 12288 297 -> 253 us, fp32
+    // 32768 x 4098 705 -> 519 us). A smaller override is taken where it still covers the row.
     const int seg = kLoopSegFull * sc;
-    const int tt = (int)(cdiv(cdiv(nacc, seg), 64) * 64);
+    const int need = (int)(cdiv(cdiv(nacc, seg), 64) * 64);
+    int tt = kLoopThreads;
+    if (t.team_threads > 0 && t.team_threads <= kLoopThreads && t.team_threads >= need)
+      tt = t.team_threads;
     p.vpt = seg;
     p.rows = 1;
     p.team_threads = tt;
