@@ -202,6 +202,49 @@ def stats_only(w, torch, nl, steps, warmup):
     return us, nbytes
 
 
+def graph_fwd_us(w, torch, nl, replays=10):
+    """Forward calls replayed from a captured graph: one forward per buffer set, the sets
+    rotating over more than 1 GiB so that every call starts from HBM as in the eager loops,
+    replayed `replays` times; microseconds per forward. For shapes bound by the launch rather
+    than by HBM."""
+    from deep_learning_normalization_amd import inputs
+    host = inputs.make(w)
+    ln = w.kind == "layernorm"
+    set_bytes = 2 * host["X"].numel() * host["X"].element_size()
+    calls = max(20, -(-(1 << 30) // set_bytes))
+    sets = []
+    for _ in range(calls):
+        X = host["X"].cuda()
+        sets.append((X, torch.empty_like(X), torch.empty(w.M, device="cuda") if ln else None,
+                     torch.empty(w.M, device="cuda")))
+    W = host["W"].cuda()
+    B = host["B"].cuda() if ln and host["B"] is not None else None
+    ws = nl.workspace(w.kind, sets[0][0].dtype, nl.PASS_FWD, w.M, w.N)
+
+    def body():
+        for i in range(calls):
+            X, Y, mean, rstd = sets[i]
+            nl.norm_fwd(w.kind, X, None, W, B, w.eps, Y, None, mean, rstd, ws)
+    body()
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        body()
+    g.replay()
+    torch.cuda.synchronize()
+    a = torch.cuda.Event(enable_timing=True)
+    b = torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(replays):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / (replays * calls)
+    del g, sets
+    torch.cuda.empty_cache()
+    return us
+
+
 def copy_ceiling(torch, nbytes=1 << 30, iters=20):
     """Achievable HBM bandwidth of a plain device copy (torch's copy kernel), GB/s moved
     (read + write). Two buffer pairs alternate so neither copy starts in cache."""
@@ -280,6 +323,10 @@ def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
                "residual": res, "sets": r["sets"], "fwd_us": round(r["fwd_us"], 2),
                "fwd_GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1)}
         row["fwd_frac_peak"] = round(row["fwd_GBps"] / PEAK_HBM_GBPS, 4)
+        if w.M * w.N <= (1 << 22):  # launch-bound sizes: the rate from a replayed graph
+            gu = graph_fwd_us(w, torch, nl)
+            row["fwd_graph_us"] = round(gu, 2)
+            row["fwd_graph_GBps"] = round(fb / (gu * 1e-6) / 1e9, 1)
         row["fwd_rows_per_s"] = round(w.M / (r["fwd_us"] * 1e-6), 1)
         if w.dy is not None:
             bb = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N, wdtype=w.wdtype)
