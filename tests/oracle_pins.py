@@ -253,12 +253,16 @@ def pin_golden_exact_cases(orc):
         X = _f32(c["X"])
         W = _f32(c["W"])
         B = None if c["B"] is None else _f32(c["B"])
-        for dtype in (F32, BF16):
-            # every value in these cases is a short dyadic rational: exact in bf16 too
+        for dtype in (F32, BF16, F16):
+            # every value in these cases is a short dyadic rational: exact in bf16 and fp16 too
             conv = (lambda a: a) if dtype == F32 else (
-                lambda a: None if a is None else
-                torch.from_numpy(np.asarray(a)).to(torch.bfloat16).view(torch.int16).numpy()
-                .view(np.uint16))
+                lambda a, t=TORCH[dtype]: None if a is None else
+                torch.from_numpy(np.asarray(a)).to(t).view(torch.int16).numpy().view(np.uint16))
+            if dtype != F32:
+                for a in (X, W, B):
+                    if a is not None:  # the conversion is exact, or the case is not this type's
+                        assert np.array_equal(torch.from_numpy(np.asarray(a)).to(
+                            TORCH[dtype]).float().numpy(), a), c["name"]
             r = orc.fwd(kind, dtype, conv(X), conv(W), conv(B), eps=c["eps"])
             _close(r["y"], c["Y"], 0, 1e-15, c["name"] + " Y")
             _close(r["rstd"], c["rstd"], 0, 1e-15, c["name"] + " rstd")
