@@ -4,5 +4,5 @@ Only the test suite, the smoke check and the benchmark's CPU-baseline leg may im
 package. The HIP library never does.
 """
 from .oracle import (BF16, BF16_F32W, F16, F16_F32W, F32, LAYERNORM, RMSNORM,  # noqa: F401
-                     Oracle, act_dtype, weight_dtype, bwd, decode, default, fwd, num_threads,
-                     round_bf16, round_f16, set_num_threads)
+                     Oracle, act_dtype, weight_dtype, bwd, decode, default, fwd, norm_linear,
+                     num_threads, round_bf16, round_f16, set_num_threads)

@@ -22,6 +22,10 @@
  *                    order of the same sums, not their value; so the oracle is the plain,
  *                    unsplit definition.
  *
+ *   [P3] "Towards Free Normalization: Fusing Normalization into GEMM and Attention Kernels"
+ *        (brifing.si): items 3-4 and 9-10 -- a norm whose output is the input of a matrix
+ *        product, fused into that product; the oracle evaluates the unfused composition.
+ *
  *   Readings taken where the pages say nothing (each is also listed in the design notes):
  *     - variance is the biased estimator (divide by N);
  *     - eps is added inside the square root, for both kinds;
@@ -378,6 +382,49 @@ int oracle_bwd_rows(int kind, int dtype, int64_t M, int64_t N, int64_t r0, int64
   free(mu);
   free(rs);
   return fail ? OR_NO_MEMORY : OR_OK;
+}
+
+/* ---- the norm followed by a linear projection ---------------------------------------- */
+
+/*
+ * out = Norm(X) * L^T + c over rows [r0, r1): a pre-norm projection, the operation that a
+ * normalisation fused into the following matrix product ("Towards Free Normalization: Fusing
+ * Normalization into GEMM and Attention Kernels", brifing.si, items 3-4 and 9-10) has to
+ * reproduce. Evaluated as its definition: the row's normalised output in double (the forward
+ * above, with gamma and beta, unrounded), then one dot product with each row of L.
+ *   X     : M*K input bits (the activation type of dtype)
+ *   W, B  : the norm's gamma and beta (the weight type of dtype), K each; B may be NULL
+ *   L     : Nout*K projection bits (the activation type of dtype), row j = output column j
+ *   c     : Nout fp32 projection bias, or NULL (zero)
+ *   out   : (r1-r0)*Nout doubles, unrounded
+ */
+int oracle_norm_linear_rows(int kind, int dtype, int64_t M, int64_t K, int64_t Nout,
+                            int64_t r0, int64_t r1, const void *X, const void *W,
+                            const void *B, const void *L, const float *c, double eps,
+                            double *out) {
+  int st = or_check(kind, dtype, M, K, r0, r1, eps);
+  if (st) return st;
+  if (Nout <= 0 || !X || !W || !L || !out) return OR_BAD_ARG;
+  if (kind == OR_RMSNORM && B) return OR_BAD_ARG;
+  const int64_t n = r1 - r0;
+  double *y = (double *)malloc((size_t)(n ? n : 1) * (size_t)K * sizeof(double));
+  if (!y) return OR_NO_MEMORY;
+  st = oracle_fwd_rows(kind, dtype, M, K, r0, r1, X, NULL, W, B, eps, y, NULL, NULL, NULL);
+  if (st) {
+    free(y);
+    return st;
+  }
+  const int act = or_act(dtype);
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < Nout; ++j) {
+    for (int64_t o = 0; o < n; ++o) {
+      double acc = 0.0;
+      for (int64_t k = 0; k < K; ++k) acc += y[o * K + k] * or_load(act, L, j * K + k);
+      out[o * Nout + j] = acc + (c ? (double)c[j] : 0.0);
+    }
+  }
+  free(y);
+  return OR_OK;
 }
 
 /* ---- helpers exposed for pins ---------------------------------------------------------- */

@@ -7,7 +7,9 @@ comes back as unrounded float64.
 
 Definitions followed (web page "PyTorch atinge desempenho SOTA em normalização com
 torch.compile", matsubara.tec.br): para. 2 for what LayerNorm and RMSNorm compute, para. 3 for
-the reduction along the contiguous dimension, para. 7 for the gradients dX, dW and dB.
+the reduction along the contiguous dimension, para. 7 for the gradients dX, dW and dB; and
+(web page "Towards Free Normalization: Fusing Normalization into GEMM and Attention Kernels",
+brifing.si) items 3-4 and 9-10 for a norm whose output feeds a matrix product.
 """
 import ctypes
 import os
@@ -48,6 +50,9 @@ class Oracle:
         lib.oracle_bwd_rows.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, i64,
                                         vp, vp, vp, vp, dbl, dp, dp, dp]
         lib.oracle_bwd_rows.restype = ctypes.c_int
+        lib.oracle_norm_linear_rows.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
+                                                i64, i64, vp, vp, vp, vp, vp, dbl, dp]
+        lib.oracle_norm_linear_rows.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_int, vp, i64, dp]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [dp, i64, vp]
@@ -67,6 +72,9 @@ class Oracle:
     def bwd(self, kind, dtype, X, dY, W, dH=None, eps=1e-5, rows=None, want_dx=True,
             want_dw=True):
         return _bwd(self.lib, kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw)
+
+    def norm_linear(self, kind, dtype, X, W, B, L, c=None, eps=1e-5, rows=None):
+        return _norm_linear(self.lib, kind, dtype, X, W, B, L, c, eps, rows)
 
     def decode(self, dtype, bits):
         return _decode(self.lib, dtype, bits)
@@ -160,6 +168,36 @@ def _bwd(lib, kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw):
     return {"dx": dx, "dw": dw, "db": db}
 
 
+def _norm_linear(lib, kind, dtype, X, W, B, L, c, eps, rows):
+    """Norm(X) @ L.T + c over rows [r0, r1) (all rows by default), unrounded float64.
+
+    X is M x K, W and B (gamma, beta) K each, L the Nout x K projection in the activation
+    type, c an Nout fp32 projection bias or None. Returns an (r1-r0) x Nout float64 array.
+    Definition: the page "Towards Free Normalization: Fusing Normalization into GEMM and
+    Attention Kernels" (brifing.si), items 3-4 and 9-10: a norm whose output feeds a matrix
+    product.
+    """
+    X = _bits(X, act_dtype(dtype))
+    M, K = X.shape
+    W = _bits(W, weight_dtype(dtype), (K,))
+    B = _bits(B, weight_dtype(dtype), (K,))
+    L = _bits(L, act_dtype(dtype))
+    if L.ndim != 2 or L.shape[1] != K:
+        raise ValueError("projection must be Nout x %d, got %s" % (K, L.shape))
+    Nout = L.shape[0]
+    if c is not None:
+        c = np.ascontiguousarray(c, dtype=np.float32)
+        if c.shape != (Nout,):
+            raise ValueError("projection bias must have %d entries" % Nout)
+    r0, r1 = (0, M) if rows is None else rows
+    out = np.empty((r1 - r0, Nout), np.float64)
+    st = lib.oracle_norm_linear_rows(kind, dtype, M, K, Nout, r0, r1, _ptr(X), _ptr(W), _ptr(B),
+                                     _ptr(L), _ptr(c), float(eps), _ptr(out))
+    if st:
+        raise ValueError("oracle_norm_linear_rows failed with status %d" % st)
+    return out
+
+
 def _decode(lib, dtype, bits):
     """Widen an array of bf16 or fp16 (uint16) or fp32 bits to float64 with the oracle's
     decoder."""
@@ -194,6 +232,10 @@ def fwd(kind, dtype, X, W, B=None, R=None, eps=1e-5, rows=None, want_h=False):
 
 def bwd(kind, dtype, X, dY, W, dH=None, eps=1e-5, rows=None, want_dx=True, want_dw=True):
     return default().bwd(kind, dtype, X, dY, W, dH, eps, rows, want_dx, want_dw)
+
+
+def norm_linear(kind, dtype, X, W, B, L, c=None, eps=1e-5, rows=None):
+    return default().norm_linear(kind, dtype, X, W, B, L, c, eps, rows)
 
 
 def decode(dtype, bits):

@@ -547,6 +547,82 @@ def pin_residual_rounding_vs_torch(orc):
         assert np.array_equal(plain["y"], r["y"])
 
 
+# ---- a norm followed by a linear projection ------------------------------------------------
+
+NL_SHAPES = [(1, 1, 1), (3, 8, 5), (17, 64, 33), (5, 1000, 7), (2, 4099, 3)]
+
+
+def _norm_linear_case(kind, dtype, M, K, Nout, seed):
+    act = BF16 if dtype in (BF16, BF16_F32W) else (F16 if dtype in (F16, F16_F32W) else F32)
+    wt = F32 if dtype in (BF16_F32W, F16_F32W) else act
+    X = _sample(M, K, act, seed, scale=1.5, shift=0.3)
+    W = _vec(K, wt, seed + 1)
+    B = _vec(K, wt, seed + 2, mean=0.0) if kind == LN else None
+    L = (torch.randn(Nout, K, generator=_rng(seed + 3)) * K ** -0.5).to(TORCH[act])
+    c = (torch.randn(Nout, generator=_rng(seed + 4)) * 0.1).float()
+    return X, W, B, L, c
+
+
+def pin_norm_linear_vs_torch(orc):
+    """Norm(X) @ L^T + c against torch float64 layer_norm / rms_norm followed by linear."""
+    for kind in (LN, RMS):
+        for dtype in (F32, BF16, BF16_F32W, F16):
+            for i, (M, K, Nout) in enumerate(NL_SHAPES):
+                X, W, B, L, c = _norm_linear_case(kind, dtype, M, K, Nout, 700 + 10 * i)
+                for bias in (c, None):
+                    e = _eps32(1e-5)
+                    got = orc.norm_linear(kind, dtype, inputs.host_bits(X), inputs.host_bits(W),
+                                          inputs.host_bits(B), inputs.host_bits(L),
+                                          None if bias is None else bias.numpy(), eps=e)
+                    xd = X.double()
+                    y = (F.layer_norm(xd, (K,), W.double(), _d(B), e) if kind == LN
+                         else F.rms_norm(xd, (K,), W.double(), e))
+                    want = F.linear(y, L.double(), _d(bias)).numpy()
+                    scale = (y.abs() @ L.double().abs().T).numpy() + 1.0
+                    _close(got / scale, want / scale, 0, 1e-13, "norm_linear %s" % ((M, K, Nout),))
+
+
+def pin_norm_linear_permutation(orc):
+    """With L a permutation matrix every output column is one normalised column (plus c),
+    exactly: the other K - 1 products are exact zeros."""
+    for kind in (LN, RMS):
+        K = 37
+        X, W, B, _, c = _norm_linear_case(kind, BF16, 6, K, K, 900)
+        perm = torch.randperm(K, generator=_rng(901))
+        L = torch.zeros(K, K)
+        L[torch.arange(K), perm] = 1.0
+        Lb = inputs.host_bits(L.to(torch.bfloat16))
+        y = orc.fwd(kind, BF16, inputs.host_bits(X), inputs.host_bits(W), inputs.host_bits(B),
+                    eps=1e-5)["y"]
+        got = orc.norm_linear(kind, BF16, inputs.host_bits(X), inputs.host_bits(W),
+                              inputs.host_bits(B), Lb, c.numpy(), eps=1e-5)
+        assert np.array_equal(got, y[:, perm.numpy()] + c.numpy().astype(np.float64))
+        got0 = orc.norm_linear(kind, BF16, inputs.host_bits(X), inputs.host_bits(W),
+                               inputs.host_bits(B), Lb, None, eps=1e-5)
+        assert np.array_equal(got0, y[:, perm.numpy()])
+
+
+def pin_norm_linear_deferred_form(orc):
+    """The deferred (lazy) form the fused product evaluates, in float64 from the decoded
+    inputs: rstd * ((X - mean) @ (L * gamma)^T) + beta @ L^T + c equals the definition; for
+    RMSNorm the mean and beta terms vanish."""
+    for kind in (LN, RMS):
+        for dtype in (BF16, BF16_F32W):
+            M, K, Nout = 9, 130, 11
+            X, W, B, L, c = _norm_linear_case(kind, dtype, M, K, Nout, 950)
+            st = orc.fwd(kind, dtype, inputs.host_bits(X), inputs.host_bits(W),
+                         inputs.host_bits(B), eps=1e-5)
+            xd, wd, ld = X.double().numpy(), W.double().numpy(), L.double().numpy()
+            lg = ld * wd[None, :]
+            lazy = st["rstd"][:, None] * (xd @ lg.T - st["mean"][:, None] * lg.sum(axis=1)[None, :])
+            if B is not None:
+                lazy = lazy + (ld @ B.double().numpy())[None, :]
+            lazy = lazy + c.double().numpy()[None, :]
+            got = orc.norm_linear(kind, dtype, inputs.host_bits(X), inputs.host_bits(W),
+                                  inputs.host_bits(B), inputs.host_bits(L), c.numpy(), eps=1e-5)
+            _close(got, lazy, 1e-11, 1e-11, "deferred form")
+
+
 ALL_PINS = [
     pin_bf16_decode,
     pin_bf16_rounding,
@@ -565,4 +641,7 @@ ALL_PINS = [
     pin_backward_invariances,
     pin_row_ranges_and_threads,
     pin_residual_rounding_vs_torch,
+    pin_norm_linear_vs_torch,
+    pin_norm_linear_permutation,
+    pin_norm_linear_deferred_form,
 ]

@@ -69,6 +69,15 @@ MUTATIONS = [
     ("fp16 mixed activations read as bf16",
      "return dtype == OR_BF16_F32W ? OR_BF16 : dtype == OR_F16_F32W ? OR_F16 : dtype;",
      "return dtype == OR_BF16_F32W ? OR_BF16 : dtype == OR_F16_F32W ? OR_BF16 : dtype;"),
+    ("projection bias dropped", "out[o * Nout + j] = acc + (c ? (double)c[j] : 0.0);",
+     "out[o * Nout + j] = acc;"),
+    ("projection transposed", "acc += y[o * K + k] * or_load(act, L, j * K + k);",
+     "acc += y[o * K + k] * or_load(act, L, k * Nout + j);"),
+    ("norm beta dropped before the projection",
+     "st = oracle_fwd_rows(kind, dtype, M, K, r0, r1, X, NULL, W, B, eps, y, NULL, NULL, NULL);",
+     "st = oracle_fwd_rows(kind, dtype, M, K, r0, r1, X, NULL, W, NULL, eps, y, NULL, NULL, NULL);"),
+    ("projection of the first row only", "acc += y[o * K + k] * or_load(act, L, j * K + k);",
+     "acc += y[k] * or_load(act, L, j * K + k);"),
 ]
 
 
