@@ -197,6 +197,64 @@ norm_status_t norm_stats(norm_kind_t kind, const void *X, const void *R, float e
                     workspace, workspace_bytes, ld, NORM_PASS_STATS, stream);
 }
 
+norm_status_t norm_fold_projection(norm_kind_t kind, norm_dtype_t dtype, const void *L,
+                                   int64_t ldl, const void *gamma, const void *beta,
+                                   const float *c, int64_t Nout, int64_t K, void *G, int64_t ldg,
+                                   float *s, float *t, norm_stream_t stream) {
+  const EventsDisarm disarm;
+  const dln::FoldCheck fc{kind, dtype, L, gamma, beta, c, Nout, K, ldl, ldg, G, s, t};
+  const norm_status_t st = dln::check_fold(fc);
+  if (st != NORM_OK) return st;
+  dln::FoldArgs a{};
+  a.l = static_cast<const uint16_t *>(L);
+  a.gamma = gamma;
+  a.beta = beta;
+  a.c = c;
+  a.g = static_cast<uint16_t *>(G);
+  a.s = kind == NORM_LAYERNORM ? s : nullptr;
+  a.t = t;
+  a.K = K;
+  a.ldl = ldl;
+  a.ldg = ldg;
+  return dln::launch_fold_projection(dtype == NORM_BF16_F32W, a, Nout,
+                                     static_cast<hipStream_t>(stream));
+}
+
+norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int64_t M,
+                               int64_t K, float eps, const void *G, int64_t ldg, int64_t Nout,
+                               const float *s, const float *t, const float *mean_in,
+                               const float *rstd_in, float *mean_out, float *rstd_out, void *Y,
+                               int64_t ldy, norm_stream_t stream) {
+  const EventsDisarm disarm;
+  const dln::LazyCheck lc{kind, X, ldx, M, K, eps, G, ldg, Nout, s, t, mean_in, rstd_in,
+                          mean_out, rstd_out, Y, ldy};
+  const norm_status_t st = dln::check_lazy(lc);
+  if (st != NORM_OK || M == 0) return st;
+  dln::LazyArgs a{};
+  a.x = static_cast<const uint16_t *>(X);
+  a.g = static_cast<const uint16_t *>(G);
+  a.s = s;
+  a.t = t;
+  a.mean_in = mean_in;
+  a.rstd_in = rstd_in;
+  a.mean_out = mean_out;
+  a.rstd_out = rstd_out;
+  a.y = static_cast<uint16_t *>(Y);
+  a.M = M;
+  a.N = Nout;
+  a.K = K;
+  a.ldx = ldx;
+  a.ldg = ldg;
+  a.ldy = ldy;
+  const int64_t tm = (M + 127) / 128, tn = (Nout + 127) / 128;
+  if (tm > 0x7fffffff || tn > 0x7fffffff) return NORM_ERR_UNSUPPORTED;
+  a.tiles_m = (int32_t)tm;
+  a.tiles_n = (int32_t)tn;
+  a.eps = eps;
+  a.inv_k = 1.0f / (float)K;
+  return dln::launch_lazy_linear(kind == NORM_LAYERNORM, a, static_cast<hipStream_t>(stream));
+}
+
 } // extern "C"
 
 namespace {

@@ -5,7 +5,7 @@ arithmetic. The device path and the CPU oracle both receive exactly the tensors 
 (sampled in fp32 on the CPU, then cast to the storage dtype with round-to-nearest-even).
 
 Every tensor has its own generator, seeded with ``seed + offset``:
-X 0, W 1, B 2, dY 3, R 4, outlier-channel permutation 5, dH 6.
+X 0, W 1, B 2, dY 3, R 4, outlier-channel permutation 5, dH 6, projection L 7, its bias c 8.
 
 The pages print no data set for these kernels; the shapes follow the workloads they discuss
 (LLM hidden sizes, and the very-large-row regression class named on the page "PyTorch atinge
@@ -18,7 +18,7 @@ from typing import Optional, Tuple
 import numpy as np
 import torch
 
-OFF_X, OFF_W, OFF_B, OFF_DY, OFF_R, OFF_PERM, OFF_DH = 0, 1, 2, 3, 4, 5, 6
+OFF_X, OFF_W, OFF_B, OFF_DY, OFF_R, OFF_PERM, OFF_DH, OFF_L, OFF_C = 0, 1, 2, 3, 4, 5, 6, 7, 8
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -184,6 +184,39 @@ LN_BF16_16384x4100 = LN_BF16_16384x4096.with_shape(16384, 4100, "layernorm_bf16_
 # The LayerNorm in fp16 storage.
 LN_F16_16384x4096 = replace(LN_BF16_16384x4096, name="layernorm_f16_16384x4096", dtype="f16")
 RMS_BF16_16384x16384 = rms_hidden(16384, M=16384)
+
+
+@dataclass(frozen=True)
+class Projection:
+    """A norm (the workload `norm`, M x K with K = norm.N) followed by a linear projection
+    L [Nout, K] (bf16, row j = output column j) with bias c [Nout] (fp32, or None)."""
+    name: str
+    norm: Workload
+    Nout: int
+    l: Dist = normal(0.0, 1.0)  # scaled by K ** -0.5 when drawn
+    c: Optional[Dist] = normal(0.0, 0.1)
+
+
+def make_projection(p: Projection) -> dict:
+    """CPU tensors L (bf16, N(0, 1/K) when l is N(0, 1): outputs of unit scale) and c."""
+    K = p.norm.N
+    s = p.norm.seed
+    L = _draw(p.l, (p.Nout, K), s + OFF_L)
+    L.mul_(K ** -0.5)
+    return {"L": L.to(torch.bfloat16),
+            "c": _draw(p.c, (p.Nout,), s + OFF_C) if p.c is not None else None}
+
+
+# LayerNorm 16384 x 4096 (bf16, the draws of the LayerNorm workload above) into a 4096 x 4096
+# projection: a pre-norm block's first matrix product at 16384 tokens.
+LN_LINEAR_BF16_16384x4096x4096 = Projection(
+    "layernorm_linear_bf16_16384x4096x4096",
+    replace(LN_BF16_16384x4096, name="layernorm_bf16_16384x4096_proj", dy=None), 4096)
+# The RMSNorm variant (hidden 4096, the outlier-channel draws) into the same projection.
+RMS_LINEAR_BF16_16384x4096x4096 = Projection(
+    "rmsnorm_linear_bf16_16384x4096x4096",
+    replace(rms_hidden(4096, M=16384), name="rmsnorm_bf16_16384x4096_proj", dy=None), 4096,
+    c=None)
 
 
 def all_workloads():

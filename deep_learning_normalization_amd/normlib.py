@@ -41,7 +41,8 @@ def dtype_code(act, weight=None):
 
 SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fwd_ex",
            "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats", "norm_workspace_size", "norm_plan",
-           "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version")
+           "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version",
+           "norm_fold_projection", "norm_lazy_linear")
 
 
 class NormError(RuntimeError):
@@ -98,10 +99,14 @@ def lib():
         L.norm_status_string.argtypes = [i32]
         L.norm_status_string.restype = ctypes.c_char_p
         L.norm_version.argtypes = []
+        L.norm_fold_projection.argtypes = [i32, i32, vp, i64, vp, vp, vp, i64, i64, vp, i64, vp,
+                                           vp, vp]
+        L.norm_lazy_linear.argtypes = [i32, vp, i64, i64, i64, f32, vp, i64, i64, vp, vp, vp,
+                                       vp, vp, vp, vp, i64, vp]
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
                      "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats",
-                     "norm_workspace_size",
-                     "norm_plan", "norm_set_tuning", "norm_set_launch_events"):
+                     "norm_workspace_size", "norm_plan", "norm_set_tuning",
+                     "norm_set_launch_events", "norm_fold_projection", "norm_lazy_linear"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
         _lib = L
@@ -203,6 +208,54 @@ def norm_stats(kind, X, R, eps, H=None, mean=None, rstd=None, workspace=None, st
                           _ptr(mean), _ptr(rstd), wp, wb, _strides(x=X, r=R, h=H),
                           _stream(stream))
     _raise(st, "norm_stats")
+
+
+def _check_rows(t, rows, cols, dtype, name):
+    """A CUDA [rows, cols] tensor of `dtype` with contiguous rows (any row stride >= cols)."""
+    if (t.dtype != dtype or tuple(t.shape) != (rows, cols) or not t.is_cuda or
+            (cols > 1 and t.stride(1) != 1) or (rows > 1 and t.stride(0) < cols)):
+        raise ValueError("%s must be a CUDA %s tensor of %d x %d elements with contiguous rows"
+                         % (name, dtype, rows, cols))
+
+
+def _ld(t):
+    return t.stride(0) if t.shape[0] > 1 else t.shape[1]
+
+
+def norm_fold_projection(kind, L, gamma, beta, c, G, s, t, stream=None):
+    """Queue the fold of the norm's gamma (and beta) into a projection L [Nout, K] (bf16):
+    G = bf16(L * gamma), s = row sums of G (LayerNorm), t = L beta + c."""
+    Nout, K = L.shape
+    _check_rows(L, Nout, K, torch.bfloat16, "L")
+    _check_rows(G, Nout, K, torch.bfloat16, "G")
+    wdt = gamma.dtype
+    _check_vec(gamma, K, wdt, "gamma")
+    _check_vec(beta, K, wdt, "beta")
+    for v, nm in ((c, "c"), (s, "s"), (t, "t")):
+        _check_vec(v, Nout, torch.float32, nm)
+    st = lib().norm_fold_projection(_kind(kind), dtype_code(torch.bfloat16, wdt), _ptr(L),
+                                    _ld(L), _ptr(gamma), _ptr(beta), _ptr(c), Nout, K, _ptr(G),
+                                    _ld(G), _ptr(s), _ptr(t), _stream(stream))
+    _raise(st, "norm_fold_projection")
+
+
+def norm_lazy_linear(kind, X, eps, G, s, t, Y, mean_in=None, rstd_in=None, mean_out=None,
+                     rstd_out=None, stream=None):
+    """Queue Y = rstd * (X G^T - mean * s) + t (bf16): the norm applied in the projection's
+    epilogue, with given statistics (rstd_in) or statistics formed from X's tiles."""
+    M, K = X.shape
+    Nout = G.shape[0]
+    _check_rows(X, M, K, torch.bfloat16, "X")
+    _check_rows(G, Nout, K, torch.bfloat16, "G")
+    _check_rows(Y, M, Nout, torch.bfloat16, "Y")
+    for v, n, nm in ((s, Nout, "s"), (t, Nout, "t"), (mean_in, M, "mean_in"),
+                     (rstd_in, M, "rstd_in"), (mean_out, M, "mean_out"), (rstd_out, M, "rstd_out")):
+        _check_vec(v, n, torch.float32, nm)
+    st = lib().norm_lazy_linear(_kind(kind), _ptr(X), _ld(X), M, K, float(eps), _ptr(G), _ld(G),
+                                Nout, _ptr(s), _ptr(t), _ptr(mean_in), _ptr(rstd_in),
+                                _ptr(mean_out), _ptr(rstd_out), _ptr(Y), _ld(Y),
+                                _stream(stream))
+    _raise(st, "norm_lazy_linear")
 
 
 def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, stream=None):
@@ -349,6 +402,26 @@ def forward(kind, X, W, B=None, eps=1e-5, R=None, stream=None):
     ws = workspace(k, X.dtype, PASS_FWD, M, N, R is not None, X.device)
     norm_fwd(k, X, R, W, B, eps, Y, H, mean, rstd, ws, stream)
     return Y, H, mean, rstd
+
+
+def fold_projection(kind, L, gamma, beta=None, c=None, stream=None):
+    """G, s (LayerNorm, else None), t (or None) for a projection L [Nout, K] after the norm."""
+    Nout, K = L.shape
+    k = _kind(kind)
+    G = torch.empty_like(L)
+    s = torch.empty(Nout, dtype=torch.float32, device=L.device) if k == LAYERNORM else None
+    t = (torch.empty(Nout, dtype=torch.float32, device=L.device)
+         if (beta is not None or c is not None) else None)
+    norm_fold_projection(k, L, gamma, beta, c, G, s, t, stream)
+    return G, s, t
+
+
+def lazy_linear(kind, X, eps, G, s=None, t=None, mean=None, rstd=None, stream=None):
+    """Norm(X) L^T + c as bf16 [M, Nout] from the fold's G, s, t; statistics from `rstd` (and
+    `mean`) when given, else formed inside the product."""
+    Y = torch.empty(X.shape[0], G.shape[0], dtype=torch.bfloat16, device=X.device)
+    norm_lazy_linear(kind, X, eps, G, s, t, Y, mean, rstd, None, None, stream)
+    return Y
 
 
 def backward(kind, X, dY, W, mean=None, rstd=None, eps=1e-5, dH=None, stream=None):

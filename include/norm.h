@@ -269,6 +269,58 @@ typedef enum {
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);
 
 /*
+ * A norm whose output feeds a linear projection, with the normalisation deferred past the
+ * matrix product ([P3] "Towards Free Normalization: Fusing Normalization into GEMM and
+ * Attention Kernels", items 3-4 and 9-10; the page names "Lazy Pre-Norm" without giving its
+ * algebra, so the form below is this library's reading). For X [M, K], the norm's gamma and
+ * beta [K], a projection L [Nout, K] (row j gives output column j) and its bias c [Nout]:
+ *     out = Norm(X) L^T + c
+ *         = rstd * (X G^T - mean * s) + t          (row-wise rstd and mean, column-wise s, t)
+ * with G = L * gamma (gamma folded into each row of L, rounded once to bf16), s[j] = sum_k
+ * G[j,k] and t[j] = sum_k beta[k] L[j,k] + c[j]. The product then reads the raw X: it tiles
+ * both of its dimensions freely, and the per-row statistics enter only its epilogue (the tiling
+ * conflict between a row-wise norm and a 2-D tiled product that the page's item 9 describes).
+ * RMSNorm has no mean and no beta: out = rstd * (X G^T) + t.
+ *
+ * norm_fold_projection: G, s and t from L, gamma, beta and c, once per projection weight.
+ *   dtype   NORM_BF16 (gamma, beta bf16) or NORM_BF16_F32W (gamma, beta fp32); L and G bf16.
+ *   L       [Nout, K] row stride ldl (elements); gamma [K]; beta [K] or NULL (LayerNorm only);
+ *           c [Nout] fp32 or NULL.
+ *   G       [Nout, K] bf16 out, row stride ldg: G[j,k] = bf16(L[j,k] * gamma[k]) (the fp32
+ *           product, rounded to nearest even).
+ *   s       [Nout] fp32 out, the sums of G's rows as stored (LayerNorm: required; RMSNorm:
+ *           NULL or ignored).
+ *   t       [Nout] fp32 out, or NULL when there is neither beta nor c.
+ *   One workgroup per row of G; the sums are formed in a fixed order (the same bits on every
+ *   call). G must not overlap L.
+ *
+ * norm_lazy_linear: Y = out above, rounded once to bf16.
+ *   X       [M, K] bf16, row stride ldx; G [Nout, K] bf16, row stride ldg (from the fold).
+ *   s, t    from the fold (t may be NULL: zero).
+ *   Statistics: with rstd_in given, mean_in (LayerNorm) and rstd_in [M] fp32 are used as they
+ *           are (for example from norm_stats or a forward). With rstd_in NULL the product
+ *           forms them itself from the X tiles it reads anyway, in fp32 (sums shifted by the
+ *           row's first element; var = E[(x-x0)^2] - E[x-x0]^2, clamped at 0; rstd =
+ *           1/sqrt(var + eps)) and, when mean_out / rstd_out are given, stores them [M] fp32.
+ *   Y       [M, Nout] bf16 out, row stride ldy.
+ *   Requirements: K a multiple of 8; ldx and ldg multiples of 8; X and G 16-byte aligned (the
+ *   product reads 16-byte chunks of 8 values); ldy >= Nout. Otherwise NORM_ERR_UNSUPPORTED
+ *   (alignment) or NORM_ERR_INVALID_ARG (sizes, NULL pointers, eps). M == 0: NORM_OK, nothing
+ *   launched. Y must not overlap X, G, s, t or the statistics.
+ *   The product runs on the matrix cores (bf16 inputs, fp32 accumulation) in 128 x 128 output
+ *   tiles.
+ */
+norm_status_t norm_fold_projection(norm_kind_t kind, norm_dtype_t dtype, const void *L,
+                                   int64_t ldl, const void *gamma, const void *beta,
+                                   const float *c, int64_t Nout, int64_t K, void *G, int64_t ldg,
+                                   float *s, float *t, norm_stream_t stream);
+norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int64_t M,
+                               int64_t K, float eps, const void *G, int64_t ldg, int64_t Nout,
+                               const float *s, const float *t, const float *mean_in,
+                               const float *rstd_in, float *mean_out, float *rstd_out, void *Y,
+                               int64_t ldy, norm_stream_t stream);
+
+/*
  * Kernel timing for profilers and benchmarks. Arms two HIP events (hipEvent_t, created by the
  * caller on the device of the stream that will be used) for the calling thread's next call of
  * norm_fwd, norm_bwd, norm_bwd_fused or norm_bwd_reduce: `start_event` takes the start

@@ -379,3 +379,59 @@ def test_fp16_dtypes_on_the_host():
         nl.dtype_code(HF, torch.bfloat16)
     assert _fwd(dtype=4, W=FAKE * 2, Y=FAKE * 2 + 16) == nl.ERR_INVALID_ARG
     assert _fwd(dtype=3, W=FAKE * 2, mean=FAKE * 2 + 16, M=4, N=8) == nl.ERR_HIP
+
+
+# ---- the norm deferred into a projection: argument checks --------------------------------
+
+def _fold(**kw):
+    a = dict(kind=0, dtype=1, L=FAKE, ldl=64, gamma=FAKE * 2, beta=FAKE * 3, c=None, Nout=32,
+             K=64, G=FAKE * 4, ldg=64, s=FAKE * 5, t=FAKE * 6, stream=None)
+    a.update(kw)
+    return nl.lib().norm_fold_projection(*a.values())
+
+
+def _lazy(**kw):
+    a = dict(kind=0, X=FAKE, ldx=64, M=16, K=64, eps=1e-5, G=FAKE * 2, ldg=64, Nout=32,
+             s=FAKE * 3, t=FAKE * 4, mean_in=None, rstd_in=None, mean_out=None, rstd_out=None,
+             Y=FAKE * 5, ldy=32, stream=None)
+    a.update(kw)
+    return nl.lib().norm_lazy_linear(*a.values())
+
+
+def test_fold_projection_checks():
+    assert _fold() == nl.ERR_HIP                           # valid: reaches the launch
+    assert _fold(dtype=2, kind=1, beta=None, s=None, t=None) == nl.ERR_HIP
+    for kw in (dict(dtype=0), dict(dtype=3), dict(kind=2), dict(L=None), dict(G=None),
+               dict(gamma=None), dict(Nout=0), dict(K=0), dict(ldl=63), dict(ldg=8),
+               dict(s=None),                               # LayerNorm needs s
+               dict(t=None),                               # beta given: t needed
+               dict(kind=1, s=None),                       # RMSNorm has no beta
+               dict(G=FAKE + 64),                          # G over L
+               dict(s=FAKE * 2),                           # s over gamma
+               dict(t=FAKE * 5 + 4),                       # t over s
+               dict(L=FAKE + 1)):                          # misaligned bf16
+        assert _fold(**kw) == nl.ERR_INVALID_ARG, kw
+
+
+def test_lazy_linear_checks():
+    assert _lazy() == nl.ERR_HIP                           # statistics formed in the product
+    assert _lazy(mean_out=FAKE * 6, rstd_out=FAKE * 7) == nl.ERR_HIP
+    assert _lazy(mean_in=FAKE * 6, rstd_in=FAKE * 7) == nl.ERR_HIP
+    assert _lazy(kind=1, s=None, t=None, rstd_in=FAKE * 7) == nl.ERR_HIP
+    assert _lazy(M=0) == nl.OK                             # nothing to launch
+    for kw in (dict(kind=2), dict(X=None), dict(G=None), dict(Y=None), dict(M=-1), dict(K=0),
+               dict(Nout=0), dict(eps=-1.0), dict(eps=float("nan")), dict(ldx=32),
+               dict(ldy=16), dict(s=None),
+               dict(rstd_in=FAKE * 7),                     # LayerNorm: mean_in too
+               dict(mean_in=FAKE * 6),                     # mean without rstd
+               dict(mean_in=FAKE * 6, rstd_in=FAKE * 7, rstd_out=FAKE * 8),
+               dict(kind=1, mean_out=FAKE * 6),            # RMSNorm has no mean
+               dict(kind=1, rstd_in=FAKE * 7, mean_in=FAKE * 6),
+               dict(Y=FAKE + 64),                          # Y over X
+               dict(rstd_out=FAKE * 5),                    # statistics over Y
+               dict(Y=FAKE * 5 + 1)):                      # misaligned bf16
+        assert _lazy(**kw) == nl.ERR_INVALID_ARG, kw
+    for kw in (dict(K=60, ldx=64, ldg=64),                 # K not a multiple of 8
+               dict(ldx=68), dict(ldg=72 + 4),             # row strides not multiples of 8
+               dict(X=FAKE + 8), dict(G=FAKE * 2 + 2)):    # not 16-byte aligned
+        assert _lazy(**kw) == nl.ERR_UNSUPPORTED, kw
