@@ -7,6 +7,7 @@
 #include <new>
 
 #include "norm_internal.hpp"
+#include "norm_lazy.hpp"
 
 namespace {
 

@@ -78,36 +78,6 @@ struct ReduceArgs {
   int32_t N;
 };
 
-// The norm deferred into a following projection (norm_lazy.hip).
-struct FoldArgs {
-  const uint16_t *l;  // [Nout, K] bf16, row stride ldl
-  const void *gamma;  // [K] bf16 or fp32
-  const void *beta;   // [K] or nullptr
-  const float *c;     // [Nout] or nullptr
-  uint16_t *g;        // [Nout, K] bf16 out, row stride ldg
-  float *s;           // [Nout] out or nullptr
-  float *t;           // [Nout] out or nullptr
-  int64_t K, ldl, ldg;
-};
-
-struct LazyArgs {
-  const uint16_t *x;  // [M, K] bf16, row stride ldx
-  const uint16_t *g;  // [Nout, K] bf16, row stride ldg
-  const float *s;     // [Nout] (LayerNorm)
-  const float *t;     // [Nout] or nullptr
-  const float *mean_in, *rstd_in;  // given statistics, or nullptr
-  float *mean_out, *rstd_out;      // formed statistics to store, or nullptr
-  uint16_t *y;        // [M, Nout] bf16, row stride ldy
-  int64_t M, N, K;    // N = Nout
-  int64_t ldx, ldg, ldy;
-  int32_t tiles_m, tiles_n;
-  float eps, inv_k;
-};
-
-norm_status_t launch_fold_projection(bool f32_weights, const FoldArgs &a, int64_t nout,
-                                     hipStream_t s);
-norm_status_t launch_lazy_linear(bool layernorm, const LazyArgs &a, hipStream_t s);
-
 // Launchers (one translation unit per scheme family). Each returns NORM_OK or
 // NORM_ERR_UNSUPPORTED / NORM_ERR_HIP.
 norm_status_t launch_team_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,

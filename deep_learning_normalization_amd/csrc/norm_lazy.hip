@@ -15,7 +15,7 @@
 // 2 x 2 MFMA 32x32x16 bf16 blocks with fp32 accumulators), K in steps of 64 staged through
 // double-buffered LDS. Global loads of step k+1 are in flight while step k multiplies.
 #include "norm_device.hpp"
-#include "norm_internal.hpp"
+#include "norm_lazy.hpp"
 
 namespace dln {
 namespace {

@@ -98,32 +98,6 @@ struct BwdCheck {
 };
 norm_status_t check_bwd(const BwdCheck &c);
 
-// norm_fold_projection and norm_lazy_linear (NORM_OK, NORM_ERR_INVALID_ARG, or
-// NORM_ERR_UNSUPPORTED for a layout the product does not read).
-struct FoldCheck {
-  int kind, dtype;
-  const void *L, *gamma, *beta;
-  const float *c;
-  int64_t Nout, K, ldl, ldg;
-  const void *G;
-  const float *s, *t;
-};
-norm_status_t check_fold(const FoldCheck &c);
-
-struct LazyCheck {
-  int kind;
-  const void *X;
-  int64_t ldx, M, K;
-  float eps;
-  const void *G;
-  int64_t ldg, Nout;
-  const float *s, *t, *mean_in, *rstd_in;
-  const float *mean_out, *rstd_out;
-  const void *Y;
-  int64_t ldy;
-};
-norm_status_t check_lazy(const LazyCheck &c);
-
 bool all_aligned16(const void *const *ptrs, int n);
 // The largest power of two, at most 16, dividing every non-null pointer (16 if all are null).
 int common_align(const void *const *ptrs, int n);

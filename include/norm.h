@@ -305,8 +305,9 @@ norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);
  *   Y       [M, Nout] bf16 out, row stride ldy.
  *   Requirements: K a multiple of 8; ldx and ldg multiples of 8; X and G 16-byte aligned (the
  *   product reads 16-byte chunks of 8 values); ldy >= Nout. Otherwise NORM_ERR_UNSUPPORTED
- *   (alignment) or NORM_ERR_INVALID_ARG (sizes, NULL pointers, eps). M == 0: NORM_OK, nothing
- *   launched. Y must not overlap X, G, s, t or the statistics.
+ *   (alignment) or NORM_ERR_INVALID_ARG (sizes, NULL pointers, eps). M == 0: NORM_OK once the
+ *   sizes and eps pass, nothing launched and no pointer read. Y must not overlap X, G, s, t
+ *   or the statistics.
  *   The product runs on the matrix cores (bf16 inputs, fp32 accumulation) in 128 x 128 output
  *   tiles.
  */

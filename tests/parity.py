@@ -277,3 +277,67 @@ class tuned:
         for k in range(nl.N_TUNE_KEYS):
             nl.norm_set_tuning(k, -1)
         return False
+
+
+# ---- the norm deferred into a following projection ---------------------------------------
+
+def norm_linear_bound(kind, xd, gd, bd, Ld, c, eps, x0=None):
+    """Per-element bound on |device - definition| for rstd * (X G^T - mean * s) + t in bf16.
+
+    xd [r, K] the rows (float64), gd / bd gamma / beta [K] (bd None for RMSNorm), Ld the
+    projection [Nout, K], c [Nout] or None; x0 [r] the shift of the formed statistics (each
+    row's first value; None for given statistics). Terms, with u = 2^-8 (one bf16 rounding,
+    half an ulp is 2^-9, doubled to cover a preceding fp32 rounding) and gK = (K/16 + 32)
+    2^-23 (twice the first-order bound of the product's fp32 sums: exact bf16 products, 16 per
+    matrix-core step, K/16 steps accumulated in turn; the fold's sums of K/256 terms per
+    thread and a tree of 8 levels are shorter):
+      G rounding             u * sum_k |xhat_k gamma_k L_jk|
+      product, s and the
+      mean correction        gK * rstd * (sum_k |x_k gamma_k L_jk| + |mean| sum_k |gamma_k L_jk|)
+      statistics             e_r * sum_k |xhat_k gamma_k L_jk| + e_m * sum_k |gamma_k L_jk|,
+                             e_r the relative error of rstd and e_m that of mean times rstd:
+                             4 (K/8 + 8) 2^-24 (1 + (x0 - mean)^2 rstd^2) for formed sums of
+                             8 partials of K/8 shifted terms; 1e-5 for given ones
+      t                      gK * sum_k |beta_k L_jk| + 2^-23 |c_j|
+    The output rounding (u |ref|) is added by check_norm_linear."""
+    K = xd.shape[1]
+    u = 2.0 ** -8
+    gK = (K / 16 + 32) * 2.0 ** -23
+    ln = kind == oracle.LAYERNORM
+    mean = xd.mean(axis=1) if ln else np.zeros(xd.shape[0])
+    var = ((xd - mean[:, None]) ** 2).mean(axis=1) if ln else (xd * xd).mean(axis=1)
+    rstd = 1.0 / np.sqrt(var + eps)
+    xh = (xd - mean[:, None]) * rstd[:, None]
+    aGL = np.abs(Ld * gd[None, :])
+    xgl = np.abs(xh) @ aGL.T
+    colsum = aGL.sum(axis=1)[None, :]
+    b = u * xgl + gK * rstd[:, None] * (np.abs(xd) @ aGL.T + np.abs(mean)[:, None] * colsum)
+    if x0 is None:
+        er = np.full(xd.shape[0], 1e-5)
+    else:
+        er = 4 * (K / 8 + 8) * 2.0 ** -24 * (1 + ((x0 - mean) * rstd) ** 2)
+    em = er * (1 + np.abs(mean) * rstd) if ln else np.zeros_like(er)
+    b = b + er[:, None] * xgl + em[:, None] * colsum
+    if bd is not None:
+        b = b + gK * (np.abs(Ld) @ np.abs(bd))[None, :]
+    if c is not None:
+        b = b + 2.0 ** -23 * np.abs(c)[None, :]
+    return b
+
+
+def check_norm_linear(what, got_bits, ref, bound):
+    """Device bf16 rows (uint16 bits) against the oracle's float64 rows: every element within
+    bound + u |ref|; and, since worst-case bounds over K terms leave room for a wrong term of
+    moderate size, the mean and root-mean-square errors within u times the mean and rms
+    magnitudes (the expected errors, one output rounding plus a random walk of the fold's
+    roundings, are well below that)."""
+    got = torch.from_numpy(np.ascontiguousarray(got_bits).view(np.int16)).view(
+        torch.bfloat16).double().numpy()
+    b = bound + 2.0 ** -8 * np.abs(ref) + 1e-30
+    d = np.abs(got - ref)
+    if not (d <= b).all():
+        _fail(what, got.ravel(), ref.ravel(), b.ravel())
+    assert d.mean() <= 2.0 ** -8 * np.abs(ref).mean() + 1e-12, (
+        "%s: mean error %g against mean magnitude %g" % (what, d.mean(), np.abs(ref).mean()))
+    assert rms(d) <= 2.0 ** -8 * rms(ref) + 1e-12, (
+        "%s: rms error %g against rms magnitude %g" % (what, rms(d), rms(ref)))

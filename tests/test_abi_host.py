@@ -419,6 +419,8 @@ def test_lazy_linear_checks():
     assert _lazy(mean_in=FAKE * 6, rstd_in=FAKE * 7) == nl.ERR_HIP
     assert _lazy(kind=1, s=None, t=None, rstd_in=FAKE * 7) == nl.ERR_HIP
     assert _lazy(M=0) == nl.OK                             # nothing to launch
+    assert _lazy(M=0, X=None, Y=None) == nl.OK
+    assert _lazy(M=0, K=0) == nl.ERR_INVALID_ARG
     for kw in (dict(kind=2), dict(X=None), dict(G=None), dict(Y=None), dict(M=-1), dict(K=0),
                dict(Nout=0), dict(eps=-1.0), dict(eps=float("nan")), dict(ldx=32),
                dict(ldy=16), dict(s=None),
