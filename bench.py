@@ -16,6 +16,11 @@ baseline.
 
 --sweep also measures every workload shape (forward, backward, both) and writes the table to
 stderr and to --sweep-out.
+
+--projection instead measures the norm deferred into a following projection (norm_lazy_linear
+after norm_fold_projection) on its two workloads, next to the unfused pair (norm_fwd, then
+torch's 2-D product with the bias, which is hipBLASLt) and the bare hipBLASLt product, and
+prints one JSON line per workload with a matrix-core roofline for the product kernel.
 """
 import argparse
 import json
@@ -28,6 +33,7 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E, published
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 matrix cores, published (no sparsity)
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -346,6 +352,116 @@ def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
     return rows
 
 
+def projection(p, torch, nl, steps, warmup):
+    """One projection workload: the fused product (statistics formed from the X tiles), the
+    statistics pass plus the product with given statistics, the unfused pair (norm_fwd to a
+    bf16 Y, then torch's 2-D product with the bias in bf16, i.e. hipBLASLt) and that product
+    alone. Two
+    buffer sets alternate (X, Y: 2 x 256 MiB at 16384 x 4096, beyond the memory-side cache).
+    Times are loop times per call over `steps` calls after `warmup`; the product kernel's own
+    duration is taken from HIP events on every launch (norm_set_launch_events)."""
+    from deep_learning_normalization_amd import inputs
+    w = p.norm
+    host = inputs.make(w)
+    ph = inputs.make_projection(p)
+    M, K, Nout = w.M, w.N, p.Nout
+    ln = w.kind == "layernorm"
+    Xs = [host["X"].cuda() for _ in range(2)]
+    g = host["W"].cuda()
+    b = host["B"].cuda() if host["B"] is not None else None
+    L = ph["L"].cuda()
+    c = ph["c"].cuda() if ph["c"] is not None else None
+    cb = c.to(torch.bfloat16) if c is not None else None
+    Lt = L.t()
+    Ys = [torch.empty(M, Nout, dtype=torch.bfloat16, device="cuda") for _ in range(2)]
+    Ns = [torch.empty_like(Xs[0]) for _ in range(2)]
+    mean = torch.empty(M, device="cuda") if ln else None
+    rstd = torch.empty(M, device="cuda")
+    ws = nl.workspace(w.kind, torch.bfloat16, nl.PASS_FWD, M, K)
+    G, sv, tv = nl.fold_projection(w.kind, L, g, b, c)
+
+    def fold(i):
+        nl.norm_fold_projection(w.kind, L, g, b, c, G, sv, tv)
+
+    def fused(i):
+        nl.norm_lazy_linear(w.kind, Xs[i % 2], w.eps, G, sv, tv, Ys[i % 2])
+
+    def given(i):
+        nl.norm_stats(w.kind, Xs[i % 2], None, w.eps, None, mean, rstd, ws)
+        nl.norm_lazy_linear(w.kind, Xs[i % 2], w.eps, G, sv, tv, Ys[i % 2], mean_in=mean,
+                            rstd_in=rstd)
+
+    def stats(i):
+        nl.norm_stats(w.kind, Xs[i % 2], None, w.eps, None, mean, rstd, ws)
+
+    def norm(i):
+        nl.norm_fwd(w.kind, Xs[i % 2], None, g, b, w.eps, Ns[i % 2], None, mean, rstd, ws)
+
+    def product(A, Y):
+        # hipBLASLt through torch: the 2-D product with L transposed, bias in its epilogue
+        if cb is None:
+            torch.mm(A, Lt, out=Y)
+        else:
+            torch.addmm(cb, A, Lt, out=Y)
+
+    def unfused(i):
+        norm(i)
+        product(Ns[i % 2], Ys[i % 2])
+
+    def linear(i):
+        product(Xs[i % 2], Ys[i % 2])
+
+    def loop(body, n, timers=None):
+        for i in range(warmup):
+            body(i)
+        torch.cuda.synchronize()
+        a = torch.cuda.Event(enable_timing=True)
+        e = torch.cuda.Event(enable_timing=True)
+        a.record()
+        for i in range(n):
+            if timers is not None:
+                timers[i].arm()
+            body(i)
+        e.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(e) / n * 1e3
+
+    # settle the clock under load
+    t_end = time.perf_counter() + 0.3
+    while time.perf_counter() < t_end:
+        fused(0)
+        torch.cuda.synchronize()
+    timers = [nl.KernelTimer() for _ in range(steps)]
+    r = {"fused_us": loop(fused, steps, timers)}
+    k_us = 1e3 * sum(t.elapsed_ms() for t in timers) / steps
+    r["given_us"] = loop(given, steps)
+    r["stats_us"] = loop(stats, steps)
+    r["norm_fwd_us"] = loop(norm, steps)
+    r["unfused_us"] = loop(unfused, steps)
+    r["hipblaslt_linear_us"] = loop(linear, steps)
+    r["fold_us"] = loop(fold, max(5, steps // 4))
+    flops = 2.0 * M * K * Nout
+    achieved = flops / (k_us * 1e-6) / 1e12
+    out = {
+        "workload": p.name, "kind": w.kind, "M": M, "K": K, "Nout": Nout, "dtype": "bf16",
+        "what": "Norm(X) L^T + c: rstd * (X G^T - mean * s) + t on the matrix cores, G = "
+                "bf16(L * gamma) from norm_fold_projection",
+        "flops_per_call": flops,
+    }
+    out.update({k: round(v, 2) for k, v in r.items()})
+    out["lazy_kernel_us"] = round(k_us, 2)
+    out["roofline"] = {"bound": "mfma", "kernel": "lazy_linear_kernel", "achieved":
+                       round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                       "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    out["hipblaslt_TFLOPs"] = round(flops / (r["hipblaslt_linear_us"] * 1e-6) / 1e12, 1)
+    # what the norm adds on top of the bare product, unfused and fused
+    out["norm_cost_unfused_us"] = round(r["unfused_us"] - r["hipblaslt_linear_us"], 2)
+    out["norm_cost_fused_us"] = round(r["fused_us"] - r["hipblaslt_linear_us"], 2)
+    del Xs, Ys, Ns
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -354,6 +470,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--sweep", action="store_true", help="also time every workload shape")
     ap.add_argument("--sweep-out", default=None)
+    ap.add_argument("--projection", action="store_true",
+                    help="measure the norm deferred into a following projection instead")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -368,6 +486,11 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     nl.lib()  # fails loudly if libnorm.so is missing
+
+    if args.projection:
+        for p in (inputs.LN_LINEAR_BF16_16384x4096x4096, inputs.RMS_LINEAR_BF16_16384x4096x4096):
+            print(json.dumps(projection(p, torch, nl, args.steps, args.warmup)), flush=True)
+        return
 
     w = inputs.LN_BF16_16384x4096
     r = timed_workload(w, args.steps, args.warmup, torch, nl)
