@@ -100,6 +100,11 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   b.header = reinterpret_cast<int64_t *>(static_cast<char *>(workspace) + plan->off_header);
   b.rowpart = plan->scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, plan->off_rowpart) : nullptr;
   b.stats = plan->scheme == NORM_SCHEME_SPLIT ? ws_region(workspace, plan->off_stats) : nullptr;
+  // the split scheme's single-pass exchange form needs the forward's statistics
+  const bool xchg = plan->xchg && rstd && (kind != NORM_LAYERNORM || mean) &&
+                    dln::xsplit_ready(dtype, kind == NORM_LAYERNORM, true);
+  b.xpart = xchg ? reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + plan->off_xpart)
+                 : nullptr;
   b.ldx = ld.x;
   b.lddy = ld.dy;
   b.lddh = ld.dh;
@@ -111,7 +116,7 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   b.chunks = plan->chunks;
   b.chunk_acc = (int32_t)(plan->chunk_elems / plan->epv);
   b.partials = plan->partials;
-  b.row_groups = plan->row_groups;
+  b.row_groups = xchg ? plan->xrow_groups : plan->row_groups;
   b.rows_per_group = plan->rows_per_group;
   b.layernorm = kind == NORM_LAYERNORM ? 1 : 0;
   b.want_db = 1;
@@ -124,7 +129,8 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
 
 norm_status_t run_fused(const dln::Plan &p, norm_dtype_t dtype, const dln::BwdArgs &a,
                         hipStream_t s) {
-  if (p.scheme == NORM_SCHEME_SPLIT) return dln::launch_split_bwd(p, dtype, a, s);
+  if (p.scheme == NORM_SCHEME_SPLIT)
+    return a.xpart ? dln::launch_xsplit_bwd(dtype, a, s) : dln::launch_split_bwd(p, dtype, a, s);
   if (p.scheme == NORM_SCHEME_LOOP) return dln::launch_looped_bwd(p, dtype, a, s);
   return dln::launch_team_bwd(p, dtype, a, s);
 }
@@ -303,7 +309,15 @@ norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const v
   a.eps = eps;
   a.inv_n = 1.0f / (float)N;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (p.scheme == NORM_SCHEME_SPLIT) return dln::launch_split_fwd(p, dtype, a, s);
+  if (p.scheme == NORM_SCHEME_SPLIT) {
+    // the single-pass exchange form where the plan allows it and Y is written
+    if (p.xchg && Y && !R && dln::xsplit_ready(dtype, kind == NORM_LAYERNORM, false)) {
+      a.xpart = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + p.off_xpart);
+      a.xgroups = p.xrow_groups;
+      return dln::launch_xsplit_fwd(p, dtype, a, s);
+    }
+    return dln::launch_split_fwd(p, dtype, a, s);
+  }
   return dln::launch_team_fwd(p, dtype, a, s);
 }
 
@@ -343,7 +357,7 @@ norm_status_t norm_bwd_ex(norm_kind_t kind, const void *X, const void *dY, const
   // the split scheme with a single row group writes dW/dB itself, with no reduction pass
   // (its vector stores of dW and dB need the alignment of the weight loads of its width)
   const void *outs[] = {dW, dB};
-  const bool direct = p.scheme == NORM_SCHEME_SPLIT && p.row_groups == 1 &&
+  const bool direct = p.scheme == NORM_SCHEME_SPLIT && a.row_groups == 1 &&
                       (size_t)dln::common_align(outs, 2) >= dln::weight_align_need(dtype, p.epv);
   if (direct) {
     a.dw = dW;
@@ -430,6 +444,7 @@ norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
   o.row_groups = p.row_groups;
   o.partials = p.partials;
   o.workspace_bytes = p.ws_bytes;
+  o.exchange_row_groups = p.xchg ? p.xrow_groups : 0;
   *out = o;
   return NORM_OK;
 }

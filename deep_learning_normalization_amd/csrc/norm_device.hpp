@@ -366,4 +366,22 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
 // 1 / sqrt(v): the hardware reciprocal square root (about 1 ulp).
 __device__ __forceinline__ float rsqrt_f32(float v) { return __builtin_amdgcn_rsqf(v); }
 
+// LayerNorm statistics of a row from its chunks' partials (the split scheme, both forms): chunk
+// c has n_c elements, mean m_c, q_c = sum (x - m_c)^2 and s_c = sum (x - m_c). With d_c = m_c -
+// shift (shift: chunk 0's mean), A = sum n_c d_c + s_c gives the row mean shift + A / N, and
+// B = sum q_c + 2 d_c s_c + n_c d_c^2 the squared deviation B - A^2 / N: an exact regrouping of
+// sum_c q_c + 2 (m_c - mean) s_c + n_c (m_c - mean)^2, whose terms stay small and positive.
+__device__ __forceinline__ void ln_chunk_terms(float n, float mc, float q, float s, float shift,
+                                               float &A, float &B) {
+  const float d = mc - shift;
+  A += n * d + s;
+  B += q + 2.0f * d * s + n * d * d;
+}
+// From the team-summed A and B: delta = A / N (the mean is shift + delta) and rstd.
+__device__ __forceinline__ float ln_combined_rstd(float A, float B, float inv_n, float eps,
+                                                  float &delta) {
+  delta = A * inv_n;
+  return rsqrt_f32(fmaxf((B - delta * A) * inv_n, 0.0f) + eps);
+}
+
 } // namespace dln

@@ -26,6 +26,8 @@ struct FwdArgs {
   float *mean;        // or nullptr
   float *rstd;        // or nullptr
   float *rowpart;     // split: [M][chunks][4]
+  uint64_t *xpart;    // split exchange form: [M][chunks][4] exchange words
+  int64_t xgroups;    // split exchange form: row groups
   int64_t ldx, ldr, ldy, ldh; // elements between row starts of X, R, Y, H (N when contiguous)
   int64_t M;
   int32_t N;
@@ -53,6 +55,8 @@ struct BwdArgs {
   int64_t *header;    // workspace header: magic, partials, N
   float *rowpart;     // split: [M][chunks][4]
   float *stats;       // split without saved stats: [2][M]
+  uint64_t *xpart;    // split exchange form: [M][chunks][4] exchange words, or nullptr when
+                      // the two-pass form runs
   int64_t ldx, lddy, lddh, lddx, lddr; // elements between row starts (N when contiguous)
   int64_t M;
   int32_t N;
@@ -101,6 +105,12 @@ norm_status_t launch_split_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs 
                                hipStream_t s);
 norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs &a,
                                hipStream_t s);
+// the split scheme in one pass, chunk partials exchanged between the workgroups of a row;
+// xsplit_ready: whether the device keeps its kernels resident as the plan assumes
+bool xsplit_ready(norm_dtype_t dtype, bool layernorm, bool bwd);
+norm_status_t launch_xsplit_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                                hipStream_t s);
+norm_status_t launch_xsplit_bwd(norm_dtype_t dtype, const BwdArgs &a, hipStream_t s);
 norm_status_t launch_reduce(norm_dtype_t dtype, const ReduceArgs &a, hipStream_t s);
 norm_status_t launch_zero(void *p, size_t bytes, hipStream_t s);
 

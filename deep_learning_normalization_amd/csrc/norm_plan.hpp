@@ -30,11 +30,14 @@ struct Plan {
   int64_t row_groups = 1;  // split backward: row groups
   int64_t rows_per_group = 0; // split backward: rows per group
   int64_t partials = 0;    // rows of fp32 column partials (backward)
+  int xchg = 0;            // split: the single-pass exchange form may run (norm_xsplit.hip)
+  int64_t xrow_groups = 0; // split exchange form: row groups (its grid is xrow_groups x chunks)
   // workspace layout (bytes from the workspace start; every region 256-byte aligned)
   size_t off_header = 0;   // backward: kWsHeaderBytes describing the partials (see below)
   size_t off_colpart = 0;  // [2][partials][N] fp32: dW partials then dB partials
   size_t off_rowpart = 0;  // split: [M][chunks][4] fp32 per-chunk row partials
   size_t off_stats = 0;    // split backward without saved stats: [M] mean then [M] rstd
+  size_t off_xpart = 0;    // split exchange form: [M][chunks][4] 64-bit exchange words
   size_t ws_bytes = 0;
 };
 
@@ -42,6 +45,12 @@ struct Plan {
 // column reduction (possibly a separate call) knows how many partial rows follow.
 constexpr size_t kWsHeaderBytes = 256;
 constexpr int64_t kWsMagic = 0x4E4F524D50415254LL; // "NORMPART"
+
+// Split exchange form: workgroups per CU its kernels are compiled to keep resident (their
+// launch bounds), which bounds its grid, and the most chunks per row it exchanges.
+constexpr int kXchgFwdPerCu = 3;
+constexpr int kXchgBwdPerCu = 2;
+constexpr int64_t kXchgMaxChunks = 512;
 
 struct Tuning {
   int scheme = NORM_SCHEME_AUTO;
@@ -52,6 +61,7 @@ struct Tuning {
   int64_t row_groups = -1;
   int teams = -1;
   int row_order = -1;
+  int xchg = -1;
 };
 
 const Tuning &tuning();

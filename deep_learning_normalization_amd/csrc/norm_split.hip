@@ -52,10 +52,9 @@ constexpr int RP = 4;
 
 // Combine the chunk statistics of one row (rp = rowpart + row * C * RP). LayerNorm returns the
 // mean as shift + delta, with shift = chunk 0's mean: every chunk then contributes small,
-// accurately representable terms, n_c (m_c - shift) + sum(x - m_c) to the mean correction
-// and sum (x - m_c)^2 + 2 e_c sum(x - m_c) + n_c e_c^2, e_c = m_c - mean, to the squared
-// deviation (an exact regrouping of sum over the chunk of (x - mean)^2). All threads of the
-// workgroup call it.
+// accurately representable terms (ln_chunk_terms), one team sum for both. All threads of the
+// workgroup call it. The single-pass form (norm_xsplit.hip) combines in the same order with
+// the same terms, so both forms give the same statistics bit for bit.
 __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, int32_t chunk_acc,
                                                   int32_t nacc, int E, int layernorm,
                                                   float inv_n, float eps, float *red, int &slot,
@@ -63,21 +62,13 @@ __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, in
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = blockDim.x >> 6;
   if (layernorm) {
     shift = rp[0];
-    float s[1] = {0.0f};
+    float ab[2] = {0.0f, 0.0f};
     for (int64_t c = tid; c < C; c += blockDim.x)
-      s[0] += chunk_count(c, chunk_acc, nacc, E) * (rp[RP * c] - shift) + rp[RP * c + 2];
-    team_sum<1, SPLIT_LB / 64>(s, red, slot, waves, 0, wave, lane);
+      ln_chunk_terms(chunk_count(c, chunk_acc, nacc, E), rp[RP * c], rp[RP * c + 1],
+                     rp[RP * c + 2], shift, ab[0], ab[1]);
+    team_sum<2, SPLIT_LB / 64>(ab, red, slot, waves, 0, wave, lane);
     slot ^= 1;
-    delta = s[0] * inv_n;
-    float q[1] = {0.0f};
-    for (int64_t c = tid; c < C; c += blockDim.x) {
-      const float e = (rp[RP * c] - shift) - delta;
-      q[0] += rp[RP * c + 1] + 2.0f * e * rp[RP * c + 2] +
-              chunk_count(c, chunk_acc, nacc, E) * e * e;
-    }
-    team_sum<1, SPLIT_LB / 64>(q, red, slot, waves, 0, wave, lane);
-    slot ^= 1;
-    rstd = rsqrt_f32(fmaxf(q[0] * inv_n, 0.0f) + eps);
+    rstd = ln_combined_rstd(ab[0], ab[1], inv_n, eps, delta);
   } else {
     float q[1] = {0.0f};
     for (int64_t c = tid; c < C; c += blockDim.x) q[0] += rp[RP * c];

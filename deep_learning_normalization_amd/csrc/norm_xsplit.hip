@@ -1,0 +1,610 @@
+// norm_xsplit.hip -- the split-row scheme in a single pass over the data ("exchange" form).
+//
+// Rows too long for one workgroup are cut into chunks, as in norm_split.hip, but every chunk
+// stays in its workgroup's registers from load to output: the workgroups that share a row swap
+// their chunk partials through the workspace instead of re-reading the row in a second pass.
+// X (and dY) cross HBM once, which is the traffic of the single-workgroup schemes.
+//
+//   grid      G row groups x C chunks. Workgroup (g, c) owns column chunk c (its weight and
+//             bias stay in registers) and walks rows g, g + G, g + 2G, ...; the next row's
+//             inputs are requested before the current row is reduced.
+//   exchange  per (row, chunk) four 64-bit words: bit 32 marks the word as published, the low
+//             half holds an fp32 partial. They are written and read with relaxed atomics at
+//             agent scope, which the compiler makes coherent across the XCDs' separate L2s;
+//             each word carries its own valid bit, so no fence orders anything. The launcher
+//             zeroes the words with a kernel before every call (no memset, so graph replays
+//             start clean too).
+//   progress  workgroup (g, c) only waits for the other C - 1 workgroups of row group g, whose
+//             ids are adjacent to its own. Workgroups are dispatched in id order, so every
+//             group below the highest dispatched one is complete on the device and can finish;
+//             the plan keeps C within what the device holds at once (C <= G * C <= resident
+//             workgroups), so the group being dispatched fits too. The wait is bounded anyway:
+//             after kSpinLimit polls (a second or so) the workgroup gives up, writes NaN for the
+//             row and stops waiting for later rows, so a broken assumption shows up as NaN
+//             outputs, never as a hang.
+//
+// Method (web page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
+// matsubara.tec.br): para. 6, very large shapes as a regression class; paras. 8-10, the split
+// reduction with a workspace of partial sums and no atomics in the arithmetic. The page
+// "Towards Free Normalization: Fusing Normalization into GEMM and Attention Kernels"
+// (brifing.si), item 4: one row's norm spread over several thread blocks (multi-CTA). The
+// chunk combination is the parallel-variance one: the row mean from the chunk means, the
+// squared deviation from the chunk sums plus count * (chunk mean - row mean)^2.
+#include "norm_device.hpp"
+#include "norm_internal.hpp"
+
+namespace dln {
+namespace {
+
+constexpr int XLB = 256;                // threads per workgroup
+constexpr int XMAXCH = 2;               // chunks per thread in the exchange (C <= 512)
+constexpr unsigned kSpinLimit = 1u << 19;
+constexpr int kWordsPerChunk = 4;
+
+__device__ __forceinline__ void publish(uint64_t *p, float v) {
+  const uint64_t w = (1ull << 32) | (uint64_t)__builtin_bit_cast(unsigned, v);
+  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint64_t peek(uint64_t *p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ float word_value(uint64_t w) {
+  return __builtin_bit_cast(float, (unsigned)(w & 0xffffffffull));
+}
+
+// Elements in chunk c of a row of nacc accesses of E elements.
+__device__ __forceinline__ float chunk_elems(int64_t c, int32_t chunk_acc, int32_t nacc, int E) {
+  const int64_t left = (int64_t)nacc - c * chunk_acc;
+  return (float)((left < chunk_acc ? left : chunk_acc) * E);
+}
+
+// Wait until the NQ words of every chunk of one row (xp: the row's words) are published and
+// return this thread's chunks tid + XLB * j in v[j] (zeros past C), plus chunk 0's first word
+// in v0. Every thread of the workgroup calls it. Returns false, with NaN in every value, once a
+// wait has given up (`failed` then stays set and later calls return at once).
+template <int NQ>
+__device__ bool gather_row(uint64_t *xp, int64_t C, float (&v)[XMAXCH][NQ], float &v0,
+                           bool &failed) {
+  const int tid = threadIdx.x;
+  if (!failed) {
+    for (unsigned spin = 0;; ++spin) {
+      int ok = 1;
+      const uint64_t w0 = peek(xp);
+      ok &= (int)(w0 >> 32);
+      v0 = word_value(w0);
+#pragma unroll
+      for (int j = 0; j < XMAXCH; ++j) {
+        const int64_t cc = tid + (int64_t)j * XLB;
+#pragma unroll
+        for (int q = 0; q < NQ; ++q) {
+          v[j][q] = 0.0f;
+          if (cc < C) {
+            const uint64_t w = peek(xp + cc * kWordsPerChunk + q);
+            ok &= (int)(w >> 32);
+            v[j][q] = word_value(w);
+          }
+        }
+      }
+      if (__syncthreads_and(ok)) return true;
+      if (spin >= kSpinLimit) break;
+      __builtin_amdgcn_s_sleep(4);
+    }
+    failed = true;
+  }
+  const float nan = __builtin_nanf("");
+  v0 = nan;
+#pragma unroll
+  for (int j = 0; j < XMAXCH; ++j)
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) v[j][q] = nan;
+  return false;
+}
+
+// ---- forward -------------------------------------------------------------------------------
+
+// Chunk partials (published as words 0..2):
+//   LayerNorm: chunk mean m_c, sum (x - m_c)^2, sum (x - m_c)
+//   RMSNorm  : sum x^2
+// Two rows are in hand at a time: the partials of row r + G are published before the wait for
+// row r's, so the wait overlaps the other workgroups' progress on row r; the inputs of row
+// r + 2G are in flight meanwhile.
+template <typename T, typename TW, int EV, int VPT, bool LN>
+__global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs a) {
+  using A = Acc<T, EV>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  constexpr int NQ = LN ? 3 : 1;
+  __shared__ __align__(16) float red[RED_FLOATS];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = XLB / 64;
+  const int64_t C = a.chunks, G = a.xgroups, M = a.M;
+  const int64_t g = (int64_t)blockIdx.x / C;
+  const int64_t c = (int64_t)blockIdx.x - g * C;
+  const int64_t acc0 = c * a.chunk_acc;
+  const int64_t left = (int64_t)a.nacc - acc0;
+  const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
+  const int64_t col0 = acc0 * E;
+  const float n_c = (float)(nin * E);
+  const T *__restrict__ X = static_cast<const T *>(a.x) + col0;
+  T *__restrict__ Y = static_cast<T *>(a.y) + col0;
+  const TW *__restrict__ W = static_cast<const TW *>(a.w) + col0;
+  const TW *__restrict__ Bb = a.b ? static_cast<const TW *>(a.b) + col0 : nullptr;
+
+  WAcc<T, TW, EV> rw[VPT], rb[VPT];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = tid + k * XLB;
+    rw[k].zero();
+    rb[k].zero();
+    if (v < nin) {
+      rw[k].load(W + (int64_t)v * E);
+      if (Bb) rb[k].load(Bb + (int64_t)v * E);
+    }
+  }
+  raw px[VPT], ra[VPT], rn[VPT];
+  auto issue = [&](int64_t row) {
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * XLB;
+      px[k] = A::zero();
+      if (row < M && v < nin) px[k] = A::ld(X + row * a.ldx + (int64_t)v * E);
+    }
+  };
+  int slot = 0;
+  // this chunk's partials of one row (accesses past the chunk's end hold zeros), published
+  auto publish_partials = [&](raw (&r)[VPT], int64_t row) {
+    uint64_t *xc = a.xpart + (row * C + c) * kWordsPerChunk;
+    if constexpr (LN) {
+      float s[1] = {0.0f};
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        float xf[E];
+        A::unpack(r[k], xf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s[0] += xf[e];
+      }
+      team_sum<1, XLB / 64>(s, red, slot, waves, 0, wave, lane);
+      slot ^= 1;
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) settle(r[k]);
+      const float mc = s[0] / n_c;
+      float qc[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        const bool in = tid + k * XLB < nin;
+        float xf[E];
+        A::unpack(r[k], xf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float d = in ? xf[e] - mc : 0.0f;
+          qc[0] += d * d;
+          qc[1] += d;
+        }
+      }
+      team_sum<2, XLB / 64>(qc, red, slot, waves, 0, wave, lane);
+      slot ^= 1;
+      if (tid == 0) {
+        publish(xc + 0, mc);
+        publish(xc + 1, qc[0]);
+        publish(xc + 2, qc[1]);
+      }
+    } else {
+      float q[1] = {0.0f};
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        float xf[E];
+        A::unpack(r[k], xf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) q[0] += xf[e] * xf[e];
+      }
+      team_sum<1, XLB / 64>(q, red, slot, waves, 0, wave, lane);
+      slot ^= 1;
+      if (tid == 0) publish(xc, q[0]);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) settle(r[k]);
+  };
+
+  issue(g); // g < M: the plan makes G at most M
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    rw[k].settle();
+    rb[k].settle();
+    ra[k] = px[k];
+  }
+  issue(g + G);
+  publish_partials(ra, g);
+  bool failed = false;
+  for (int64_t row = g; row < M; row += G) {
+    const int64_t next = row + G;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) rn[k] = px[k];
+    issue(next + G);
+    if (next < M) publish_partials(rn, next);
+
+    // the row's statistics from every chunk's partials, in chunk order per thread, then the
+    // team sum (a fixed order; the two-pass form combines in the same order with the same
+    // terms, ln_chunk_terms, so both forms give the same bits)
+    float pv[XMAXCH][NQ], m0;
+    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, pv, m0, failed);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) settle(ra[k]);
+    float shift = 0.0f, delta = 0.0f, rstd;
+    if constexpr (LN) {
+      shift = m0;
+      float ab[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int j = 0; j < XMAXCH; ++j) {
+        const int64_t cc = tid + (int64_t)j * XLB;
+        if (cc < C)
+          ln_chunk_terms(chunk_elems(cc, a.chunk_acc, a.nacc, E), pv[j][0], pv[j][1], pv[j][2],
+                         shift, ab[0], ab[1]);
+      }
+      team_sum<2, XLB / 64>(ab, red, slot, waves, 0, wave, lane);
+      slot ^= 1;
+      rstd = ln_combined_rstd(ab[0], ab[1], a.inv_n, a.eps, delta);
+    } else {
+      float q[1] = {0.0f};
+#pragma unroll
+      for (int j = 0; j < XMAXCH; ++j) q[0] += pv[j][0];
+      team_sum<1, XLB / 64>(q, red, slot, waves, 0, wave, lane);
+      slot ^= 1;
+      rstd = rsqrt_f32(q[0] * a.inv_n + a.eps);
+    }
+
+    // normalise the chunk held in registers
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * XLB;
+      if (v < nin) {
+        float xf[E], wf[E], bf[E], y[E];
+        A::unpack(ra[k], xf);
+        rw[k].get(wf);
+        rb[k].get(bf);
+#pragma unroll
+        for (int e = 0; e < E; ++e) y[e] = ((xf[e] - shift) - delta) * rstd * wf[e] + bf[e];
+        A::st(Y + row * a.ldy + (int64_t)v * E, A::pack(y));
+      }
+    }
+    if (c == 0 && tid == 0) {
+      if (a.mean) a.mean[row] = shift + delta;
+      if (a.rstd) a.rstd[row] = rstd;
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) ra[k] = rn[k];
+  }
+}
+
+// ---- backward ------------------------------------------------------------------------------
+
+// Chunk partials, around the row's saved mean m:
+//   LayerNorm: sum g*(x - m), sum g, sum (x - m)    (g = dY * w)
+//   RMSNorm  : sum g*x
+// After the exchange each workgroup writes dX for its chunk from registers and keeps the
+// chunk's dW (and dB) column sums over its rows; they are written once at the end as partial
+// row g (or as the final dW/dB when there is one row group). Rows are pipelined as in the
+// forward: row r + G's partials are published before the wait for row r's. The dB sums live
+// in LDS (each thread owns one column of it, so no barrier guards them), which leaves the
+// registers for three rows of X and dY.
+template <typename T, typename TW, int EV, int VPT, bool LN>
+__global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs a) {
+  using A = Acc<T, EV>;
+  using raw = typename A::raw;
+  constexpr int E = A::EPV;
+  constexpr int NQ = LN ? 3 : 1;
+  __shared__ __align__(16) float red[RED_FLOATS];
+  // dB sums: element (k, e) of thread t at sdb[k * E + e][t]
+  __shared__ float sdb[LN ? VPT * E : 1][XLB];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = XLB / 64;
+  const int64_t C = a.chunks, G = a.row_groups, M = a.M;
+  const int64_t g = (int64_t)blockIdx.x / C;
+  const int64_t c = (int64_t)blockIdx.x - g * C;
+  const int64_t acc0 = c * a.chunk_acc;
+  const int64_t left = (int64_t)a.nacc - acc0;
+  const int nin = (int)(left < a.chunk_acc ? left : a.chunk_acc);
+  const int64_t col0 = acc0 * E;
+  const int64_t N = a.N;
+  const T *__restrict__ X = static_cast<const T *>(a.x) + col0;
+  const T *__restrict__ DY = static_cast<const T *>(a.dy) + col0;
+  const T *__restrict__ DH = a.dh ? static_cast<const T *>(a.dh) + col0 : nullptr;
+  const TW *__restrict__ W = static_cast<const TW *>(a.w) + col0;
+  T *__restrict__ DX = static_cast<T *>(a.dx) + col0;
+  T *__restrict__ DR = a.dr ? static_cast<T *>(a.dr) + col0 : nullptr;
+  if (!a.dw) write_ws_header(a.header, G, N);
+
+  WAcc<T, TW, EV> rw[VPT];
+  float accw[VPT][E];
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    const int v = tid + k * XLB;
+    rw[k].zero();
+    if (v < nin) rw[k].load(W + (int64_t)v * E);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      accw[k][e] = 0.0f;
+      if constexpr (LN) sdb[k * E + e][tid] = 0.0f;
+    }
+  }
+  // px/pdy: in flight; xa/dya: the row being finished; xn/dyn: the next row (published)
+  raw px[VPT], pdy[VPT], xa[VPT], dya[VPT], xn[VPT], dyn[VPT];
+  float pm = 0.0f, prs = 0.0f, ma, rsa, mn, rsn;
+  auto issue = [&](int64_t row) {
+    const bool rv = row < M;
+    const int64_t rowc = rv ? row : M - 1;
+    pm = LN ? a.mean[rowc] : 0.0f;
+    prs = a.rstd[rowc];
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * XLB;
+      px[k] = A::zero();
+      pdy[k] = A::zero();
+      if (rv && v < nin) {
+        px[k] = A::ld(X + row * a.ldx + (int64_t)v * E);
+        pdy[k] = A::ld(DY + row * a.lddy + (int64_t)v * E);
+      }
+    }
+  };
+  int slot = 0;
+  auto publish_partials = [&](raw (&rx)[VPT], raw (&rdy)[VPT], float m, int64_t row) {
+    float sums[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) sums[q] = 0.0f;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const bool in = tid + k * XLB < nin;
+      float xf[E], df[E], wf[E];
+      A::unpack(rx[k], xf);
+      A::unpack(rdy[k], df);
+      rw[k].get(wf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float d = in ? xf[e] - m : 0.0f;
+        const float gg = df[e] * wf[e];
+        sums[0] += gg * d;
+        if constexpr (LN) {
+          sums[1] += gg;
+          sums[2] += d;
+        }
+      }
+    }
+    team_sum<NQ, XLB / 64>(sums, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    if (tid == 0) {
+      uint64_t *xc = a.xpart + (row * C + c) * kWordsPerChunk;
+#pragma unroll
+      for (int q = 0; q < NQ; ++q) publish(xc + q, sums[q]);
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      settle(rx[k]);
+      settle(rdy[k]);
+    }
+  };
+
+  issue(g); // g < M: the plan makes G at most M
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) {
+    rw[k].settle();
+    xa[k] = px[k];
+    dya[k] = pdy[k];
+  }
+  ma = pm;
+  rsa = prs;
+  issue(g + G);
+  publish_partials(xa, dya, ma, g);
+  bool failed = false;
+  for (int64_t row = g; row < M; row += G) {
+    const int64_t next = row + G;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      xn[k] = px[k];
+      dyn[k] = pdy[k];
+    }
+    mn = pm;
+    rsn = prs;
+    issue(next + G);
+    if (next < M) publish_partials(xn, dyn, mn, next);
+
+    float pv[XMAXCH][NQ], unused;
+    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, pv, unused, failed);
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      settle(xa[k]);
+      settle(dya[k]);
+    }
+    float tot[NQ];
+#pragma unroll
+    for (int q = 0; q < NQ; ++q) {
+      float s = 0.0f;
+#pragma unroll
+      for (int j = 0; j < XMAXCH; ++j) s += pv[j][q];
+      tot[q] = s;
+    }
+    team_sum<NQ, XLB / 64>(tot, red, slot, waves, 0, wave, lane);
+    slot ^= 1;
+    const float m = ma, rstd = rsa;
+    const float delta = LN ? tot[2] * a.inv_n : 0.0f;
+    const float c1 = LN ? tot[1] * a.inv_n : 0.0f;
+    const float c2 = LN ? rstd * (tot[0] - delta * tot[1]) * a.inv_n : rstd * tot[0] * a.inv_n;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * XLB;
+      const bool in = v < nin;
+      float xf[E], df[E], wf[E], dx[E];
+      A::unpack(xa[k], xf);
+      A::unpack(dya[k], df);
+      rw[k].get(wf);
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const float xh = in ? ((xf[e] - m) - delta) * rstd : 0.0f;
+        dx[e] = rstd * (df[e] * wf[e] - c1 - xh * c2);
+        accw[k][e] += df[e] * xh;
+        if constexpr (LN) sdb[k * E + e][tid] += df[e];
+      }
+      if (in) {
+        const int64_t off = (int64_t)v * E;
+        if (DH) {
+          float hf[E];
+          A::unpack(A::ld(DH + row * a.lddh + off), hf);
+#pragma unroll
+          for (int e = 0; e < E; ++e) dx[e] += hf[e];
+        }
+        const raw p = A::pack(dx);
+        A::st(DX + row * a.lddx + off, p);
+        if (DR) A::st(DR + row * a.lddr + off, p);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      xa[k] = xn[k];
+      dya[k] = dyn[k];
+    }
+    ma = mn;
+    rsa = rsn;
+  }
+  if (a.dw) {
+    TW *dw = static_cast<TW *>(a.dw) + col0;
+    TW *db = a.db ? static_cast<TW *>(a.db) + col0 : nullptr;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * XLB;
+      if (v < nin) {
+        WAcc<T, TW, EV>::store(dw + (int64_t)v * E, accw[k]);
+        if constexpr (LN) {
+          float bsum[E];
+#pragma unroll
+          for (int e = 0; e < E; ++e) bsum[e] = sdb[k * E + e][tid];
+          if (db) WAcc<T, TW, EV>::store(db + (int64_t)v * E, bsum);
+        }
+      }
+    }
+  } else {
+    float *pw = a.colpart + g * N + col0;
+    float *pb = a.colpart + (G + g) * N + col0;
+#pragma unroll
+    for (int k = 0; k < VPT; ++k) {
+      const int v = tid + k * XLB;
+      if (v < nin) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          pw[(int64_t)v * E + e] = accw[k][e];
+          if constexpr (LN) pb[(int64_t)v * E + e] = sdb[k * E + e][tid];
+        }
+      }
+    }
+  }
+}
+
+// ---- launchers -------------------------------------------------------------------------------
+
+// Clears n 16-byte units of exchange words (the region is 256-byte aligned and a multiple of 32
+// bytes long). One kernel name per pass, so that profiles attribute it.
+__device__ __forceinline__ void clear16(u32x4 *p, int64_t n) {
+  const u32x4 z = {0u, 0u, 0u, 0u};
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    p[i] = z;
+}
+__global__ __launch_bounds__(256) void xclear_fwd_kernel(u32x4 *p, int64_t n) { clear16(p, n); }
+__global__ __launch_bounds__(256) void xclear_bwd_kernel(u32x4 *p, int64_t n) { clear16(p, n); }
+
+norm_status_t clear_words(uint64_t *words, int64_t M, int64_t C, bool bwd, hipStream_t s) {
+  const int64_t n = M * C * kWordsPerChunk / 2;
+  const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
+  const hipError_t e = launch(bwd ? xclear_bwd_kernel : xclear_fwd_kernel,
+                              dim3((unsigned)blocks), dim3(256), s,
+                              reinterpret_cast<u32x4 *>(words), n);
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+// Resident workgroups per CU of one kernel, asked of the runtime once per process (every
+// device of a process is the same gfx950 part).
+template <typename K> int resident_per_cu(K kernel) {
+  int n = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, kernel, XLB, 0) != hipSuccess) n = 0;
+  return n;
+}
+
+template <typename T, typename TW, bool LN> int fwd_resident() {
+  static const int n = resident_per_cu(xsplit_fwd_kernel<T, TW, full_epv<T>(), 4, LN>);
+  return n;
+}
+template <typename T, typename TW, bool LN> int bwd_resident() {
+  static const int n = resident_per_cu(xsplit_bwd_kernel<T, TW, full_epv<T>(), 4, LN>);
+  return n;
+}
+
+template <typename T, typename TW>
+norm_status_t xfwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
+  constexpr int F = full_epv<T>();
+  const int need = (int)kXchgFwdPerCu;
+  const int have = a.layernorm ? fwd_resident<T, TW, true>() : fwd_resident<T, TW, false>();
+  if (have < need) return NORM_ERR_UNSUPPORTED;
+  norm_status_t st = clear_words(a.xpart, a.M, a.chunks, false, s);
+  if (st != NORM_OK) return st;
+  const dim3 grid((unsigned)(a.xgroups * a.chunks)), block(XLB);
+  const hipError_t e = a.layernorm
+                           ? launch(xsplit_fwd_kernel<T, TW, F, 4, true>, grid, block, s, a)
+                           : launch(xsplit_fwd_kernel<T, TW, F, 4, false>, grid, block, s, a);
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+template <typename T, typename TW>
+norm_status_t xbwd_typed(const BwdArgs &a, hipStream_t s) {
+  constexpr int F = full_epv<T>();
+  const int need = (int)kXchgBwdPerCu;
+  const int have = a.layernorm ? bwd_resident<T, TW, true>() : bwd_resident<T, TW, false>();
+  if (have < need) return NORM_ERR_UNSUPPORTED;
+  norm_status_t st = clear_words(a.xpart, a.M, a.chunks, true, s);
+  if (st != NORM_OK) return st;
+  const dim3 grid((unsigned)(a.row_groups * a.chunks)), block(XLB);
+  const hipError_t e = a.layernorm
+                           ? launch(xsplit_bwd_kernel<T, TW, F, 4, true>, grid, block, s, a)
+                           : launch(xsplit_bwd_kernel<T, TW, F, 4, false>, grid, block, s, a);
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+} // namespace
+
+bool xsplit_ready(norm_dtype_t dtype, bool layernorm, bool bwd) {
+  const int need = bwd ? (int)kXchgBwdPerCu : (int)kXchgFwdPerCu;
+  int have = 0;
+#define DLN_XR(T, TW)                                                                           \
+  have = bwd ? (layernorm ? bwd_resident<T, TW, true>() : bwd_resident<T, TW, false>())          \
+             : (layernorm ? fwd_resident<T, TW, true>() : fwd_resident<T, TW, false>());
+  switch (dtype) {
+  case NORM_F32: DLN_XR(float, float) break;
+  case NORM_BF16: DLN_XR(bf16_bits, bf16_bits) break;
+  case NORM_BF16_F32W: DLN_XR(bf16_bits, float) break;
+  case NORM_F16: DLN_XR(f16_t, f16_t) break;
+  case NORM_F16_F32W: DLN_XR(f16_t, float) break;
+  default: return false;
+  }
+#undef DLN_XR
+  return have >= need;
+}
+
+norm_status_t launch_xsplit_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
+                                hipStream_t s) {
+  switch (dtype) {
+  case NORM_F32: return xfwd_typed<float, float>(p, a, s);
+  case NORM_BF16: return xfwd_typed<bf16_bits, bf16_bits>(p, a, s);
+  case NORM_BF16_F32W: return xfwd_typed<bf16_bits, float>(p, a, s);
+  case NORM_F16: return xfwd_typed<f16_t, f16_t>(p, a, s);
+  case NORM_F16_F32W: return xfwd_typed<f16_t, float>(p, a, s);
+  default: return NORM_ERR_UNSUPPORTED;
+  }
+}
+
+norm_status_t launch_xsplit_bwd(norm_dtype_t dtype, const BwdArgs &a, hipStream_t s) {
+  switch (dtype) {
+  case NORM_F32: return xbwd_typed<float, float>(a, s);
+  case NORM_BF16: return xbwd_typed<bf16_bits, bf16_bits>(a, s);
+  case NORM_BF16_F32W: return xbwd_typed<bf16_bits, float>(a, s);
+  case NORM_F16: return xbwd_typed<f16_t, f16_t>(a, s);
+  case NORM_F16_F32W: return xbwd_typed<f16_t, float>(a, s);
+  default: return NORM_ERR_UNSUPPORTED;
+  }
+}
+
+} // namespace dln

@@ -19,7 +19,8 @@ PASS_FWD, PASS_BWD, PASS_STATS = 0, 1, 2
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT, SCHEME_LOOP = -1, 0, 1, 2, 3
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
 TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
-N_TUNE_KEYS = 8
+TUNE_SPLIT_EXCHANGE = 8
+N_TUNE_KEYS = 9
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 
@@ -63,7 +64,8 @@ class _Plan(ctypes.Structure):
                 ("rows_per_iter", ctypes.c_int32), ("row_order", ctypes.c_int32),
                 ("grid", ctypes.c_int64), ("chunks", ctypes.c_int64),
                 ("chunk_elems", ctypes.c_int64), ("row_groups", ctypes.c_int64),
-                ("partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64)]
+                ("partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
+                ("exchange_row_groups", ctypes.c_int64)]
 
 
 _lib = None

@@ -46,6 +46,7 @@ NORM_KERNEL_SOURCES = ("norm_device.hpp", "norm_internal.hpp", "norm_team_kernel
                        "norm_team_menu.hpp", "norm_team.hip", "norm_team_f32.hip",
                        "norm_team_bf16.hip", "norm_team_bf16w.hip", "norm_team_f16.hip",
                        "norm_team_f16w.hip", "norm_looped.hip", "norm_split.hip",
+                       "norm_xsplit.hip",
                        "norm_plan.cpp", "norm_plan.hpp")
 
 

@@ -98,7 +98,12 @@ typedef enum {
   NORM_SCHEME_AUTO = -1, /* tuning value only: let the dispatcher choose */
   NORM_SCHEME_WAVE = 0,  /* one row per 64-lane wavefront, registers only (short rows) */
   NORM_SCHEME_BLOCK = 1, /* one row per team of waves, cross-wave sums through LDS */
-  NORM_SCHEME_SPLIT = 2, /* one row over several workgroups, two passes (very long rows) */
+  NORM_SCHEME_SPLIT = 2, /* one row over several workgroups (very long rows): a single pass
+                            in which the row's workgroups exchange their chunk partials through
+                            the workspace, each chunk held in registers throughout (16-byte
+                            accesses, no residual input, up to 1024 chunks, saved statistics
+                            for the backward), else two passes, the second re-reading its
+                            chunk */
   NORM_SCHEME_LOOP = 3   /* backward only: one row per workgroup in two sweeps, the second
                             from the L2 (rows of 1024-2048 16-byte accesses); forcing it
                             leaves the forward to the dispatcher */
@@ -239,6 +244,9 @@ typedef struct {
   int64_t row_groups;     /* split backward: row groups sharing a column partial */
   int64_t partials;       /* rows of fp32 column partials in the backward workspace */
   uint64_t workspace_bytes;
+  int64_t exchange_row_groups; /* split scheme: row groups of the single-pass exchange form
+                                  when it applies (the backward's also needs the saved
+                                  statistics), else 0 */
 } norm_plan_t;
 
 /*
@@ -262,8 +270,10 @@ typedef enum {
   NORM_TUNE_ROW_GROUPS = 5,     /* split backward: number of row groups */
   NORM_TUNE_TEAMS_PER_WG = 6,   /* block scheme: row teams per workgroup (their dW/dB partials
                                    are merged in LDS, so fewer partial rows are written) */
-  NORM_TUNE_ROW_ORDER = 7       /* wave/block schemes: 0 = row groups interleaved across the
+  NORM_TUNE_ROW_ORDER = 7,      /* wave/block schemes: 0 = row groups interleaved across the
                                    workgroups, 1 = each workgroup takes a contiguous block */
+  NORM_TUNE_SPLIT_EXCHANGE = 8  /* split scheme: 1 = the single-pass exchange form where it
+                                   applies (the default), 0 = always the two-pass form */
 } norm_tune_t;
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);

@@ -265,7 +265,8 @@ class tuned:
         keys = {"scheme": nl.TUNE_SCHEME, "grid_per_cu": nl.TUNE_GRID_PER_CU,
                 "rows": nl.TUNE_ROWS_PER_ITER, "team_threads": nl.TUNE_TEAM_THREADS,
                 "split_chunk": nl.TUNE_SPLIT_CHUNK, "row_groups": nl.TUNE_ROW_GROUPS,
-                "teams": nl.TUNE_TEAMS_PER_WG, "row_order": nl.TUNE_ROW_ORDER}
+                "teams": nl.TUNE_TEAMS_PER_WG, "row_order": nl.TUNE_ROW_ORDER,
+                "exchange": nl.TUNE_SPLIT_EXCHANGE}
         self.items = [(keys[k], v) for k, v in kv.items()]
 
     def __enter__(self):

@@ -295,7 +295,8 @@ def test_plan_covers_every_row_and_column(dt, N, M, pass_):
             assert (p["chunks"] - 1) * p["chunk_elems"] < N
             if pass_ == 1:
                 assert p["grid"] == p["chunks"] * p["row_groups"]
-                assert p["partials"] == p["row_groups"] <= M
+                assert p["partials"] == max(p["row_groups"], p["exchange_row_groups"])
+                assert p["partials"] <= M
         else:
             # a team's registers cover the whole row
             assert p["team_threads"] * p["accesses_per_thread"] >= nacc
@@ -323,6 +324,51 @@ def test_plan_tuning_overrides():
         nl.norm_set_tuning(nl.TUNE_ROW_ORDER, 1)
         assert nl.norm_plan(0, BF, 0, 65536, 4096)["row_order"] == 1
         assert nl.norm_plan(0, BF, 1, 65536, 512)["row_order"] == 1
+    finally:
+        for k in range(nl.N_TUNE_KEYS):
+            nl.norm_set_tuning(k, -1)
+
+
+def test_split_exchange_plan():
+    """The single-pass split form: 16-byte accesses, the default chunk, no residual input, at
+    most 512 chunks, and a grid (row groups x chunks) the device keeps resident: 3 workgroups
+    per CU forward (with room for two row groups), 2 backward."""
+    cu = 256
+    try:
+        for kind, pass_, per_cu in ((0, 0, 3), (1, 0, 3), (0, 1, 2), (1, 1, 2)):
+            for M, N in ((256, 262144), (4, 4194304), (3, 20000), (1000, 65536)):
+                # more chunks than the device holds at once (forward: twice over)
+                if N // 8192 * (2 if pass_ == 0 else 1) > cu * per_cu:
+                    assert nl.norm_plan(kind, BF, pass_, M, N,
+                                        cu_count=cu)["exchange_row_groups"] == 0
+                    continue
+                p = nl.norm_plan(kind, BF, pass_, M, N, cu_count=cu)
+                assert p["scheme"] == nl.SCHEME_SPLIT and p["chunk_elems"] == 8192
+                G = p["exchange_row_groups"]
+                assert G == min(M, cu * per_cu // p["chunks"]) >= 1
+                assert G * p["chunks"] <= cu * per_cu
+                if pass_ == 1:
+                    assert p["partials"] >= G
+            # residual input, narrower accesses, the statistics pass, or a tuned chunk: two passes
+            assert nl.norm_plan(1, BF, pass_, 64, 262144, residual=1,
+                                cu_count=cu)["exchange_row_groups"] == 0
+            assert nl.norm_plan(0, BF, pass_, 64, 262148, cu_count=cu)["exchange_row_groups"] == 0
+            nl.norm_set_tuning(nl.TUNE_SPLIT_CHUNK, 4096)
+            assert nl.norm_plan(0, BF, pass_, 64, 262144, cu_count=cu)["exchange_row_groups"] == 0
+            nl.norm_set_tuning(nl.TUNE_SPLIT_CHUNK, -1)
+            nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, 0)
+            assert nl.norm_plan(0, BF, pass_, 64, 262144, cu_count=cu)["exchange_row_groups"] == 0
+            nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, -1)
+        # the statistics pass shares the forward's plan and workspace (it runs two passes)
+        assert (nl.norm_plan(0, BF, 2, 64, 262144, cu_count=cu)["workspace_bytes"] ==
+                nl.norm_plan(0, BF, 0, 64, 262144, cu_count=cu)["workspace_bytes"])
+        # more chunks than 512, or than the device holds at once
+        assert nl.norm_plan(0, BF, 0, 2, 8192 * 513, cu_count=cu)["exchange_row_groups"] == 0
+        assert nl.norm_plan(0, BF, 1, 4, 4194304, cu_count=128)["exchange_row_groups"] == 0
+        # the backward's row-group knob lowers its row groups
+        nl.norm_set_tuning(nl.TUNE_ROW_GROUPS, 5)
+        assert nl.norm_plan(0, BF, 1, 256, 262144, cu_count=cu)["exchange_row_groups"] == 5
+        assert nl.lib().norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, 2) == nl.ERR_INVALID_ARG
     finally:
         for k in range(nl.N_TUNE_KEYS):
             nl.norm_set_tuning(k, -1)

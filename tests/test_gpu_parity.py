@@ -99,6 +99,65 @@ def test_forced_scheme(name, scheme, Ns, dt, kind):
                 run_and_check(_small(kind, dt, M, N, seed=3 * M + N + 1), stats=False)
 
 
+# ---- the split scheme's two forms -----------------------------------------------------------------
+# Single pass (the workgroups of a row exchange chunk partials, each chunk stays in registers)
+# and two passes (the second re-reads its chunk). The backward's single pass needs the saved
+# statistics; with stats=False it recomputes them and runs two passes either way.
+
+SPLIT_FORMS = [("exchange", 1), ("two_pass", 0)]
+
+
+def _split_form(kind, dt, pass_, M, N):
+    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], pass_, M, N,
+                     cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
+    return p["exchange_row_groups"]
+
+
+@pytest.mark.parametrize("form,flag", SPLIT_FORMS, ids=[f[0] for f in SPLIT_FORMS])
+@pytest.mark.parametrize("dt", ["bf16", "f32", "f16"])
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_split_forms(form, flag, dt, kind):
+    for N in (8200, 20000, 65536, 262144):
+        for M in ((1, 3, 300) if N <= 65536 else (1, 17)):
+            _say("split form %s %s %s %dx%d" % (form, kind, dt, M, N))
+            with tuned(scheme=nl.SCHEME_SPLIT, exchange=flag):
+                if flag and N % 8 == 0:
+                    assert _split_form(kind, dt, nl.PASS_FWD, M, N) > 0
+                    assert _split_form(kind, dt, nl.PASS_BWD, M, N) > 0
+                run_and_check(_small(kind, dt, M, N, seed=5 * M + N))
+                run_and_check(_small(kind, dt, M, N, seed=5 * M + N + 1), stats=False)
+
+
+@pytest.mark.parametrize("knob", [dict(row_groups=1), dict(row_groups=7), dict()],
+                         ids=["one_group", "seven_groups", "default"])
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_split_exchange_many_rows_per_group(kind, knob):
+    """Each row group walks many rows: the prefetch of the next row, the exchange words of
+    every row, and the column partials kept over the group's rows (one group writes dW and dB
+    itself)."""
+    M, N = 2000, 65536
+    _say("split exchange %s %dx%d %s" % (kind, M, N, knob))
+    with tuned(exchange=1, **knob):
+        assert _split_form(kind, "bf16", nl.PASS_BWD, M, N) > 0
+        run_and_check(_small(kind, "bf16", M, N, seed=M))
+
+
+def test_split_exchange_mixed_weights_and_residual():
+    for kind in ("layernorm", "rmsnorm"):
+        for N in (20000, 262144):
+            _say("split exchange fp32 weights %s N=%d" % (kind, N))
+            w = dataclasses.replace(_small(kind, "bf16", 9, N, seed=N), wdtype="f32")
+            with tuned(exchange=1):
+                run_and_check(w)
+    # the residual variant: its forward takes two passes, its backward (with dH) one
+    for dr in ("alias", "separate"):
+        _say("split exchange residual dr=%s" % dr)
+        w = dataclasses.replace(_small("rmsnorm", "bf16", 9, 40000, seed=3,
+                                       r=inputs.normal(0, 1)), wdtype="f32")
+        with tuned(exchange=1):
+            run_and_check(w, dr=dr, dh=True)
+
+
 # ---- bf16 activations with fp32 weight, bias, dW, dB --------------------------------------------
 
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
@@ -643,6 +702,8 @@ def test_zero_rows():
 @pytest.mark.parametrize("kind,dt,M,N", [("layernorm", "bf16", 4096, 4096),
                                         ("rmsnorm", "bf16", 3000, 1024),
                                         ("layernorm", "bf16", 64, 100000),
+                                        ("layernorm", "f16", 17, 262144),
+                                        ("rmsnorm", "bf16", 4, 1048576),
                                         ("rmsnorm", "f32", 513, 7168)])
 def test_bitwise_deterministic(kind, dt, M, N):
     """No atomics and fixed reduction orders: repeated runs, also on another stream, give the
