@@ -498,22 +498,20 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
 
 // ---- launchers -------------------------------------------------------------------------------
 
-// Clears n 16-byte units of exchange words (the region is 256-byte aligned and a multiple of 32
-// bytes long). One kernel name per pass, so that profiles attribute it.
-__device__ __forceinline__ void clear16(u32x4 *p, int64_t n) {
-  const u32x4 z = {0u, 0u, 0u, 0u};
+// Clears n exchange words, with the same agent-scope stores that publish them. One kernel name
+// per pass, so that profiles attribute it.
+__device__ __forceinline__ void clear_n(uint64_t *p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
-    p[i] = z;
+    __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__global__ __launch_bounds__(256) void xclear_fwd_kernel(u32x4 *p, int64_t n) { clear16(p, n); }
-__global__ __launch_bounds__(256) void xclear_bwd_kernel(u32x4 *p, int64_t n) { clear16(p, n); }
+__global__ __launch_bounds__(256) void xclear_fwd_kernel(uint64_t *p, int64_t n) { clear_n(p, n); }
+__global__ __launch_bounds__(256) void xclear_bwd_kernel(uint64_t *p, int64_t n) { clear_n(p, n); }
 
 norm_status_t clear_words(uint64_t *words, int64_t M, int64_t C, bool bwd, hipStream_t s) {
-  const int64_t n = M * C * kWordsPerChunk / 2;
+  const int64_t n = M * C * kWordsPerChunk;
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
   const hipError_t e = launch(bwd ? xclear_bwd_kernel : xclear_fwd_kernel,
-                              dim3((unsigned)blocks), dim3(256), s,
-                              reinterpret_cast<u32x4 *>(words), n);
+                              dim3((unsigned)blocks), dim3(256), s, words, n);
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }
 

@@ -86,7 +86,9 @@ def _name(raw):
 
 
 def _short(name):
-    """Kernel name without the argument list; torch kernels cut to their first words."""
+    """Kernel name without the argument list or namespaces' anonymous part; torch kernels cut to
+    their first words."""
+    name = name.replace("(anonymous namespace)::", "")
     base = name.split("(")[0] if "dln::" in name else name[:60]
     return base.replace("void dln::", "").strip()
 
