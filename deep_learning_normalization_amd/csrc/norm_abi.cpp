@@ -105,6 +105,9 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
                     dln::xsplit_ready(dtype, kind == NORM_LAYERNORM, true);
   b.xpart = xchg ? reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + plan->off_xpart)
                  : nullptr;
+  b.polls = (uint32_t)(dln::tuning().xchg_polls > 0 ? dln::tuning().xchg_polls
+                                                     : dln::kXchgPollsDefault);
+  b.withhold = dln::tuning().xchg_withhold == 1 ? 1 : 0;
   b.ldx = ld.x;
   b.lddy = ld.dy;
   b.lddh = ld.dh;
@@ -314,6 +317,9 @@ norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const v
     if (p.xchg && Y && !R && dln::xsplit_ready(dtype, kind == NORM_LAYERNORM, false)) {
       a.xpart = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + p.off_xpart);
       a.xgroups = p.xrow_groups;
+      a.polls = (uint32_t)(dln::tuning().xchg_polls > 0 ? dln::tuning().xchg_polls
+                                                         : dln::kXchgPollsDefault);
+      a.withhold = dln::tuning().xchg_withhold == 1 ? 1 : 0;
       return dln::launch_xsplit_fwd(p, dtype, a, s);
     }
     return dln::launch_split_fwd(p, dtype, a, s);

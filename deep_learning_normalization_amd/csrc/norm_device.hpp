@@ -366,6 +366,10 @@ __device__ __forceinline__ float mul_rn(float a, float b) {
 // 1 / sqrt(v): the hardware reciprocal square root (about 1 ulp).
 __device__ __forceinline__ float rsqrt_f32(float v) { return __builtin_amdgcn_rsqf(v); }
 
+// A variance formed by subtraction, with a negative rounding residue set to 0. A NaN passes
+// through (fmaxf would turn it into 0 and give a NaN row the finite rstd eps^-1/2).
+__device__ __forceinline__ float clamp_var(float v) { return v < 0.0f ? 0.0f : v; }
+
 // LayerNorm statistics of a row from its chunks' partials (the split scheme, both forms): chunk
 // c has n_c elements, mean m_c, q_c = sum (x - m_c)^2 and s_c = sum (x - m_c). With d_c = m_c -
 // shift (shift: chunk 0's mean), A = sum n_c d_c + s_c gives the row mean shift + A / N, and
@@ -381,7 +385,7 @@ __device__ __forceinline__ void ln_chunk_terms(float n, float mc, float q, float
 __device__ __forceinline__ float ln_combined_rstd(float A, float B, float inv_n, float eps,
                                                   float &delta) {
   delta = A * inv_n;
-  return rsqrt_f32(fmaxf((B - delta * A) * inv_n, 0.0f) + eps);
+  return rsqrt_f32(clamp_var((B - delta * A) * inv_n) + eps);
 }
 
 } // namespace dln

@@ -28,6 +28,8 @@ struct FwdArgs {
   float *rowpart;     // split: [M][chunks][4]
   uint64_t *xpart;    // split exchange form: [M][chunks][4] exchange words
   int64_t xgroups;    // split exchange form: row groups
+  uint32_t polls;     // split exchange form: polls before a row is given up
+  int32_t withhold;   // split exchange form, tests only: chunk 0 publishes nothing
   int64_t ldx, ldr, ldy, ldh; // elements between row starts of X, R, Y, H (N when contiguous)
   int64_t M;
   int32_t N;
@@ -57,6 +59,8 @@ struct BwdArgs {
   float *stats;       // split without saved stats: [2][M]
   uint64_t *xpart;    // split exchange form: [M][chunks][4] exchange words, or nullptr when
                       // the two-pass form runs
+  uint32_t polls;     // split exchange form: polls before a row is given up
+  int32_t withhold;   // split exchange form, tests only: chunk 0 publishes nothing
   int64_t ldx, lddy, lddh, lddx, lddr; // elements between row starts (N when contiguous)
   int64_t M;
   int32_t N;

@@ -178,7 +178,7 @@ __global__ __launch_bounds__(kThreads, 2) void lazy_linear_kernel(LazyArgs a) {
         if constexpr (LN) {
           const float d = s1[q] * a.inv_k;
           mean = sh[q] + d;
-          rstd = rsqrt_f32(fmaxf(s2[q] * a.inv_k - d * d, 0.0f) + a.eps);
+          rstd = rsqrt_f32(clamp_var(s2[q] * a.inv_k - d * d) + a.eps);
         } else {
           rstd = rsqrt_f32(s2[q] * a.inv_k + a.eps);
         }

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
       team_sum<2, MAXW>(qc, red, slot, waves, 0, wave, lane);
       slot ^= 1;
       const float dl = qc[1] * a.inv_n;
-      rstd = rsqrt_f32(fmaxf(qc[0] * a.inv_n - dl * dl, 0.0f) + a.eps);
+      rstd = rsqrt_f32(clamp_var(qc[0] * a.inv_n - dl * dl) + a.eps);
       reload_barrier();
     } else {
       float q[1] = {0.0f};

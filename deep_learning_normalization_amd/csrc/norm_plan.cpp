@@ -176,6 +176,14 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
     if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
     g_tuning.xchg = (int)v;
     return NORM_OK;
+  case NORM_TUNE_EXCHANGE_POLLS:
+    if (v != -1 && (v < 1 || v > kXchgPollsMax)) return NORM_ERR_INVALID_ARG;
+    g_tuning.xchg_polls = v;
+    return NORM_OK;
+  case NORM_TUNE_EXCHANGE_WITHHOLD:
+    if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
+    g_tuning.xchg_withhold = (int)v;
+    return NORM_OK;
   default: return NORM_ERR_INVALID_ARG;
   }
 }

@@ -50,6 +50,8 @@ constexpr int64_t kWsMagic = 0x4E4F524D50415254LL; // "NORMPART"
 // launch bounds), which bounds its grid, and the most chunks per row it exchanges.
 constexpr int kXchgFwdPerCu = 3;
 constexpr int kXchgBwdPerCu = 2;
+constexpr int64_t kXchgPollsDefault = 1 << 19;
+constexpr int64_t kXchgPollsMax = 1 << 24;
 constexpr int64_t kXchgMaxChunks = 512;
 
 struct Tuning {
@@ -62,6 +64,8 @@ struct Tuning {
   int teams = -1;
   int row_order = -1;
   int xchg = -1;
+  int64_t xchg_polls = -1;
+  int xchg_withhold = -1;
 };
 
 const Tuning &tuning();

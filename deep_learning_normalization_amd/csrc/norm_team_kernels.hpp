@@ -216,7 +216,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         delta[r] = qc[ROWS + r] * a.inv_n;
-        const float var = fmaxf(qc[r] * a.inv_n - delta[r] * delta[r], 0.0f);
+        const float var = clamp_var(qc[r] * a.inv_n - delta[r] * delta[r]);
         rstd[r] = rsqrt_f32(var + a.eps);
       }
     } else {
@@ -406,7 +406,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
         for (int r = 0; r < ROWS; ++r) {
           const float dl = qc[ROWS + r] * a.inv_n;
-          rstd[r] = rsqrt_f32(fmaxf(qc[r] * a.inv_n - dl * dl, 0.0f) + a.eps);
+          rstd[r] = rsqrt_f32(clamp_var(qc[r] * a.inv_n - dl * dl) + a.eps);
         }
       } else {
         float q[ROWS];

@@ -19,9 +19,9 @@
 //             group below the highest dispatched one is complete on the device and can finish;
 //             the plan keeps C within what the device holds at once (C <= G * C <= resident
 //             workgroups), so the group being dispatched fits too. The wait is bounded anyway:
-//             after kSpinLimit polls (a second or so) the workgroup gives up, writes NaN for the
-//             row and stops waiting for later rows, so a broken assumption shows up as NaN
-//             outputs, never as a hang.
+//             after a set number of polls (2^19 by default, a second or so) the workgroup gives
+//             up, writes NaN for the row and stops waiting for later rows, so a broken
+//             assumption shows up as NaN outputs, never as a hang.
 //
 // Method (web page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
 // matsubara.tec.br): para. 6, very large shapes as a regression class; paras. 8-10, the split
@@ -38,7 +38,6 @@ namespace {
 
 constexpr int XLB = 256;                // threads per workgroup
 constexpr int XMAXCH = 2;               // chunks per thread in the exchange (C <= 512)
-constexpr unsigned kSpinLimit = 1u << 19;
 constexpr int kWordsPerChunk = 4;
 
 __device__ __forceinline__ void publish(uint64_t *p, float v) {
@@ -63,10 +62,11 @@ __device__ __forceinline__ float chunk_elems(int64_t c, int32_t chunk_acc, int32
 // Wait until the NQ words of every chunk of one row (xp: the row's words) are published and
 // return this thread's chunks tid + XLB * j in v[j] (zeros past C), plus chunk 0's first word
 // in v0. Every thread of the workgroup calls it. Returns false, with NaN in every value, once a
-// wait has given up (`failed` then stays set and later calls return at once).
+// wait has given up after `polls` polls (`failed` then stays set and later calls return at
+// once).
 template <int NQ>
-__device__ bool gather_row(uint64_t *xp, int64_t C, float (&v)[XMAXCH][NQ], float &v0,
-                           bool &failed) {
+__device__ bool gather_row(uint64_t *xp, int64_t C, unsigned polls, float (&v)[XMAXCH][NQ],
+                           float &v0, bool &failed) {
   const int tid = threadIdx.x;
   if (!failed) {
     for (unsigned spin = 0;; ++spin) {
@@ -88,7 +88,7 @@ __device__ bool gather_row(uint64_t *xp, int64_t C, float (&v)[XMAXCH][NQ], floa
         }
       }
       if (__syncthreads_and(ok)) return true;
-      if (spin >= kSpinLimit) break;
+      if (spin + 1 >= polls) break;
       __builtin_amdgcn_s_sleep(4);
     }
     failed = true;
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
       }
       team_sum<2, XLB / 64>(qc, red, slot, waves, 0, wave, lane);
       slot ^= 1;
-      if (tid == 0) {
+      if (tid == 0 && !(a.withhold && c == 0)) {
         publish(xc + 0, mc);
         publish(xc + 1, qc[0]);
         publish(xc + 2, qc[1]);
@@ -200,7 +200,7 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
       }
       team_sum<1, XLB / 64>(q, red, slot, waves, 0, wave, lane);
       slot ^= 1;
-      if (tid == 0) publish(xc, q[0]);
+      if (tid == 0 && !(a.withhold && c == 0)) publish(xc, q[0]);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) settle(r[k]);
@@ -227,7 +227,7 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
     // team sum (a fixed order; the two-pass form combines in the same order with the same
     // terms, ln_chunk_terms, so both forms give the same bits)
     float pv[XMAXCH][NQ], m0;
-    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, pv, m0, failed);
+    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, a.polls, pv, m0, failed);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) settle(ra[k]);
     float shift = 0.0f, delta = 0.0f, rstd;
@@ -370,7 +370,7 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
     }
     team_sum<NQ, XLB / 64>(sums, red, slot, waves, 0, wave, lane);
     slot ^= 1;
-    if (tid == 0) {
+    if (tid == 0 && !(a.withhold && c == 0)) {
       uint64_t *xc = a.xpart + (row * C + c) * kWordsPerChunk;
 #pragma unroll
       for (int q = 0; q < NQ; ++q) publish(xc + q, sums[q]);
@@ -407,7 +407,7 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
     if (next < M) publish_partials(xn, dyn, mn, next);
 
     float pv[XMAXCH][NQ], unused;
-    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, pv, unused, failed);
+    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, a.polls, pv, unused, failed);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       settle(xa[k]);
@@ -462,6 +462,18 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
     }
     ma = mn;
     rsa = rsn;
+  }
+  // a wait that gave up poisons the column sums too (RMSNorm's dW does not depend on the
+  // exchanged values and would otherwise come out finite)
+  if (failed) {
+    const float nan = __builtin_nanf("");
+#pragma unroll
+    for (int k = 0; k < VPT; ++k)
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        accw[k][e] = nan;
+        if constexpr (LN) sdb[k * E + e][tid] = nan;
+      }
   }
   if (a.dw) {
     TW *dw = static_cast<TW *>(a.dw) + col0;

@@ -19,8 +19,8 @@ PASS_FWD, PASS_BWD, PASS_STATS = 0, 1, 2
 SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT, SCHEME_LOOP = -1, 0, 1, 2, 3
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
 TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
-TUNE_SPLIT_EXCHANGE = 8
-N_TUNE_KEYS = 9
+TUNE_SPLIT_EXCHANGE, TUNE_EXCHANGE_POLLS, TUNE_EXCHANGE_WITHHOLD = 8, 9, 10
+N_TUNE_KEYS = 11
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
 

@@ -128,8 +128,13 @@ typedef void *norm_stream_t; /* a hipStream_t */
  *   rstd   [M] fp32 row 1/sqrt(stat + eps). Optional.
  *   workspace, workspace_bytes: device scratch of at least
  *          norm_workspace_size(kind, dtype, NORM_PASS_FWD, M, N, R != NULL) bytes, 256-byte
- *          aligned; may be NULL when that size is 0.
+ *          aligned; may be NULL when that size is 0. Calls that share a workspace must not
+ *          overlap in time.
  * Returns NORM_OK once the kernels are queued.
+ * Very long rows (the split scheme's single-pass form) are spread over workgroups that wait
+ * for each other's partial sums; the wait is bounded (NORM_TUNE_EXCHANGE_POLLS) and a wait that
+ * gives up writes NaN into the call's outputs for the rows it could not finish, never hangs.
+ * It can only give up if the device does not keep the call's workgroups resident.
  */
 norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const void *W,
                        const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
@@ -151,6 +156,8 @@ norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const voi
  *   dW     [N] output. Required.
  *   dB     [N] output. LayerNorm: optional. RMSNorm: must be NULL.
  *   workspace: at least norm_workspace_size(kind, dtype, NORM_PASS_BWD, M, N, 0) bytes.
+ * Very long rows with saved statistics take the split scheme's single-pass form, with the
+ * bounded wait described at norm_fwd (a wait that gives up leaves NaN in dX, dW and dB).
  */
 norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const void *dH,
                        const void *W, const float *mean, const float *rstd, float eps,
@@ -272,8 +279,14 @@ typedef enum {
                                    are merged in LDS, so fewer partial rows are written) */
   NORM_TUNE_ROW_ORDER = 7,      /* wave/block schemes: 0 = row groups interleaved across the
                                    workgroups, 1 = each workgroup takes a contiguous block */
-  NORM_TUNE_SPLIT_EXCHANGE = 8  /* split scheme: 1 = the single-pass exchange form where it
+  NORM_TUNE_SPLIT_EXCHANGE = 8, /* split scheme: 1 = the single-pass exchange form where it
                                    applies (the default), 0 = always the two-pass form */
+  NORM_TUNE_EXCHANGE_POLLS = 9, /* single-pass split form: polls of a row's exchange words
+                                   before a workgroup gives up on the row and writes NaN for
+                                   it and for its later rows (1 .. 2^24; default 2^19, about a
+                                   second) */
+  NORM_TUNE_EXCHANGE_WITHHOLD = 10 /* for tests of that bounded wait only: 1 = chunk 0 never
+                                      publishes its partials, so every row gives up */
 } norm_tune_t;
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);

@@ -266,7 +266,8 @@ class tuned:
                 "rows": nl.TUNE_ROWS_PER_ITER, "team_threads": nl.TUNE_TEAM_THREADS,
                 "split_chunk": nl.TUNE_SPLIT_CHUNK, "row_groups": nl.TUNE_ROW_GROUPS,
                 "teams": nl.TUNE_TEAMS_PER_WG, "row_order": nl.TUNE_ROW_ORDER,
-                "exchange": nl.TUNE_SPLIT_EXCHANGE}
+                "exchange": nl.TUNE_SPLIT_EXCHANGE, "polls": nl.TUNE_EXCHANGE_POLLS,
+                "withhold": nl.TUNE_EXCHANGE_WITHHOLD}
         self.items = [(keys[k], v) for k, v in kv.items()]
 
     def __enter__(self):

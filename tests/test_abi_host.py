@@ -369,6 +369,10 @@ def test_split_exchange_plan():
         nl.norm_set_tuning(nl.TUNE_ROW_GROUPS, 5)
         assert nl.norm_plan(0, BF, 1, 256, 262144, cu_count=cu)["exchange_row_groups"] == 5
         assert nl.lib().norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, 2) == nl.ERR_INVALID_ARG
+        for bad in (0, (1 << 24) + 1):
+            assert nl.lib().norm_set_tuning(nl.TUNE_EXCHANGE_POLLS, bad) == nl.ERR_INVALID_ARG
+        assert nl.lib().norm_set_tuning(nl.TUNE_EXCHANGE_POLLS, 1) == nl.OK
+        assert nl.lib().norm_set_tuning(nl.TUNE_EXCHANGE_WITHHOLD, 2) == nl.ERR_INVALID_ARG
     finally:
         for k in range(nl.N_TUNE_KEYS):
             nl.norm_set_tuning(k, -1)

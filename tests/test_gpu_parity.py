@@ -158,6 +158,64 @@ def test_split_exchange_mixed_weights_and_residual():
             run_and_check(w, dr=dr, dh=True)
 
 
+@pytest.mark.parametrize("N,knob", [(512, dict()), (4096, dict()), (4100, dict()),
+                                    (12288, dict()), (65536, dict(exchange=1)),
+                                    (65536, dict(exchange=0))],
+                         ids=["wave", "block", "block8", "loop", "split1", "split2"])
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_nan_row_propagates(kind, N, knob):
+    """A NaN in one row makes that row's statistics, output and dX NaN (and the column sums it
+    enters) and leaves the other rows alone, on every scheme, the statistics pass included."""
+    M = 5
+    _say("nan row %s N=%d %s" % (kind, N, knob))
+    w = _small(kind, "bf16", M, N, seed=N)
+    t = inputs.make(w)
+    t["X"][2, N // 3] = float("nan")
+    X, W, B, dY = (t[k].cuda() if t[k] is not None else None for k in ("X", "W", "B", "dY"))
+    with tuned(**knob):
+        Y, _, mean, rstd = nl.forward(kind, X, W, B, w.eps)
+        dX, dW, _ = nl.backward(kind, X, dY, W, mean, rstd, w.eps)
+        dX2, _, _ = nl.backward(kind, X, dY, W, None, None, w.eps)
+        ws = nl.workspace(kind, torch.bfloat16, nl.PASS_STATS, M, N)
+        m3 = torch.empty(M, device="cuda") if kind == "layernorm" else None
+        r3 = torch.empty(M, device="cuda")
+        nl.norm_stats(kind, X, None, w.eps, None, m3, r3, ws)
+        torch.cuda.synchronize()
+    others = [0, 1, 3, 4]
+    for r in (rstd, r3):
+        assert torch.isnan(r[2]) and torch.isfinite(r[others]).all()
+    for a in (Y, dX, dX2):
+        assert torch.isnan(a[2].float()).all() and torch.isfinite(a[others].float()).all()
+    assert torch.isnan(dW.float()).all()
+
+
+def test_split_exchange_wait_is_bounded():
+    """The exchange's wait gives up rather than hangs: with chunk 0 withholding its partials
+    (a test-only flag) and a poll limit of 8, every row of the call comes out NaN, the kernels
+    finish, and the next call without the flag is correct again."""
+    M, N = 64, 65536
+    for kind in ("layernorm", "rmsnorm"):
+        _say("split exchange bounded wait %s %dx%d" % (kind, M, N))
+        w = _small(kind, "bf16", M, N, seed=9)
+        t = inputs.make(w)
+        X, W, B, dY = (t[k].cuda() if t[k] is not None else None for k in ("X", "W", "B", "dY"))
+        with tuned(exchange=1):
+            Y0, _, mean0, rstd0 = nl.forward(kind, X, W, B, w.eps)
+            assert _split_form(kind, "bf16", nl.PASS_FWD, M, N) > 0
+        with tuned(exchange=1, polls=8, withhold=1):
+            Y, _, _, rstd = nl.forward(kind, X, W, B, w.eps)
+            dX, dW, dB = nl.backward(kind, X, dY, W, mean0, rstd0, w.eps)
+            torch.cuda.synchronize()
+        assert torch.isnan(Y.float()).all() and torch.isnan(rstd).all()
+        assert torch.isnan(dX.float()).all() and torch.isnan(dW.float()).all()
+        with tuned(exchange=1):
+            Y2, _, _, rstd2 = nl.forward(kind, X, W, B, w.eps)
+            torch.cuda.synchronize()
+        assert torch.equal(Y2.view(torch.int16), Y0.view(torch.int16))
+        assert torch.equal(rstd2, rstd0)
+        run_and_check(w)
+
+
 # ---- bf16 activations with fp32 weight, bias, dW, dB --------------------------------------------
 
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
