@@ -294,8 +294,11 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
   constexpr int E = A::EPV;
   constexpr int NQ = LN ? 3 : 1;
   __shared__ __align__(16) float red[RED_FLOATS];
-  // dB sums: element (k, e) of thread t at sdb[k * E + e][t]
-  __shared__ float sdb[LN ? VPT * E : 1][XLB];
+  // dB sums, 16-byte LDS accesses: elements 4h .. 4h + 3 of access k of thread t at
+  // sdb[k * (E / 4) + h][t]
+  static_assert(E % 4 == 0, "16-byte accesses of 2- or 4-byte elements");
+  constexpr int E4 = E / 4;
+  __shared__ float4 sdb[LN ? VPT * E4 : 1][XLB];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, waves = XLB / 64;
   const int64_t C = a.chunks, G = a.row_groups, M = a.M;
   const int64_t g = (int64_t)blockIdx.x / C;
@@ -321,9 +324,10 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
     rw[k].zero();
     if (v < nin) rw[k].load(W + (int64_t)v * E);
 #pragma unroll
-    for (int e = 0; e < E; ++e) {
-      accw[k][e] = 0.0f;
-      if constexpr (LN) sdb[k * E + e][tid] = 0.0f;
+    for (int e = 0; e < E; ++e) accw[k][e] = 0.0f;
+    if constexpr (LN) {
+#pragma unroll
+      for (int h = 0; h < E4; ++h) sdb[k * E4 + h][tid] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
   }
   // px/pdy: in flight; xa/dya: the row being finished; xn/dyn: the next row (published)
@@ -440,7 +444,17 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
         const float xh = in ? ((xf[e] - m) - delta) * rstd : 0.0f;
         dx[e] = rstd * (df[e] * wf[e] - c1 - xh * c2);
         accw[k][e] += df[e] * xh;
-        if constexpr (LN) sdb[k * E + e][tid] += df[e];
+      }
+      if constexpr (LN) {
+#pragma unroll
+        for (int h = 0; h < E4; ++h) {
+          float4 b = sdb[k * E4 + h][tid];
+          b.x += df[4 * h];
+          b.y += df[4 * h + 1];
+          b.z += df[4 * h + 2];
+          b.w += df[4 * h + 3];
+          sdb[k * E4 + h][tid] = b;
+        }
       }
       if (in) {
         const int64_t off = (int64_t)v * E;
@@ -468,12 +482,14 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
   if (failed) {
     const float nan = __builtin_nanf("");
 #pragma unroll
-    for (int k = 0; k < VPT; ++k)
+    for (int k = 0; k < VPT; ++k) {
 #pragma unroll
-      for (int e = 0; e < E; ++e) {
-        accw[k][e] = nan;
-        if constexpr (LN) sdb[k * E + e][tid] = nan;
+      for (int e = 0; e < E; ++e) accw[k][e] = nan;
+      if constexpr (LN) {
+#pragma unroll
+        for (int h = 0; h < E4; ++h) sdb[k * E4 + h][tid] = make_float4(nan, nan, nan, nan);
       }
+    }
   }
   if (a.dw) {
     TW *dw = static_cast<TW *>(a.dw) + col0;
@@ -486,7 +502,13 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
         if constexpr (LN) {
           float bsum[E];
 #pragma unroll
-          for (int e = 0; e < E; ++e) bsum[e] = sdb[k * E + e][tid];
+          for (int h = 0; h < E4; ++h) {
+            const float4 b = sdb[k * E4 + h][tid];
+            bsum[4 * h] = b.x;
+            bsum[4 * h + 1] = b.y;
+            bsum[4 * h + 2] = b.z;
+            bsum[4 * h + 3] = b.w;
+          }
           if (db) WAcc<T, TW, EV>::store(db + (int64_t)v * E, bsum);
         }
       }
@@ -499,9 +521,16 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
       const int v = tid + k * XLB;
       if (v < nin) {
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          pw[(int64_t)v * E + e] = accw[k][e];
-          if constexpr (LN) pb[(int64_t)v * E + e] = sdb[k * E + e][tid];
+        for (int e = 0; e < E; ++e) pw[(int64_t)v * E + e] = accw[k][e];
+        if constexpr (LN) {
+#pragma unroll
+          for (int h = 0; h < E4; ++h) {
+            const float4 b = sdb[k * E4 + h][tid];
+            pb[(int64_t)v * E + 4 * h] = b.x;
+            pb[(int64_t)v * E + 4 * h + 1] = b.y;
+            pb[(int64_t)v * E + 4 * h + 2] = b.z;
+            pb[(int64_t)v * E + 4 * h + 3] = b.w;
+          }
         }
       }
     }
