@@ -370,6 +370,14 @@ __device__ __forceinline__ float rsqrt_f32(float v) { return __builtin_amdgcn_rs
 // through (fmaxf would turn it into 0 and give a NaN row the finite rstd eps^-1/2).
 __device__ __forceinline__ float clamp_var(float v) { return v < 0.0f ? 0.0f : v; }
 
+// Elements in chunk c of a split row of nacc accesses of E elements, chunk_acc accesses per
+// chunk (the last chunk may be short).
+__device__ __forceinline__ float split_chunk_elems(int64_t c, int32_t chunk_acc, int32_t nacc,
+                                                   int E) {
+  const int64_t left = (int64_t)nacc - c * chunk_acc;
+  return (float)((left < chunk_acc ? left : chunk_acc) * E);
+}
+
 // LayerNorm statistics of a row from its chunks' partials (the split scheme, both forms): chunk
 // c has n_c elements, mean m_c, q_c = sum (x - m_c)^2 and s_c = sum (x - m_c). With d_c = m_c -
 // shift (shift: chunk 0's mean), A = sum n_c d_c + s_c gives the row mean shift + A / N, and

@@ -37,12 +37,6 @@ __device__ __forceinline__ int64_t reverse_within_xcd(int64_t b, int64_t nb) {
   return ((nx - 1 - i) << 3) + x;
 }
 
-// Elements in chunk c of a row of nacc accesses.
-__device__ __forceinline__ float chunk_count(int64_t c, int32_t chunk_acc, int32_t nacc, int E) {
-  const int64_t left = (int64_t)nacc - c * chunk_acc;
-  return (float)((left < chunk_acc ? left : chunk_acc) * E);
-}
-
 // Per-(row, chunk) partials, RP floats each:
 //   forward  LayerNorm: [0] chunk mean m_c, [1] sum (x - m_c)^2, [2] sum (x - m_c)
 //            RMSNorm  : [0] sum x^2
@@ -64,7 +58,7 @@ __device__ __forceinline__ void combine_row_stats(const float *rp, int64_t C, in
     shift = rp[0];
     float ab[2] = {0.0f, 0.0f};
     for (int64_t c = tid; c < C; c += blockDim.x)
-      ln_chunk_terms(chunk_count(c, chunk_acc, nacc, E), rp[RP * c], rp[RP * c + 1],
+      ln_chunk_terms(split_chunk_elems(c, chunk_acc, nacc, E), rp[RP * c], rp[RP * c + 1],
                      rp[RP * c + 2], shift, ab[0], ab[1]);
     team_sum<2, SPLIT_LB / 64>(ab, red, slot, waves, 0, wave, lane);
     slot ^= 1;

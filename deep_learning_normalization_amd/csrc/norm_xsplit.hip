@@ -6,8 +6,8 @@
 // X (and dY) cross HBM once, which is the traffic of the single-workgroup schemes.
 //
 //   grid      G row groups x C chunks. Workgroup (g, c) owns column chunk c (its weight and
-//             bias stay in registers) and walks rows g, g + G, g + 2G, ...; the next row's
-//             inputs are requested before the current row is reduced.
+//             bias stay in registers) and walks rows g, g + G, g + 2G, ...; it publishes row
+//             r + G's partials before it waits for row r's, with row r + 2G's loads in flight.
 //   exchange  per (row, chunk) four 64-bit words: bit 32 marks the word as published, the low
 //             half holds an fp32 partial. They are written and read with relaxed atomics at
 //             agent scope, which the compiler makes coherent across the XCDs' separate L2s;
@@ -39,6 +39,8 @@ namespace {
 constexpr int XLB = 256;                // threads per workgroup
 constexpr int XMAXCH = 2;               // chunks per thread in the exchange (C <= 512)
 constexpr int kWordsPerChunk = 4;
+static_assert(kXchgMaxChunks <= (int64_t)XLB * XMAXCH, "the plan admits more chunks than a "
+                                                        "workgroup gathers");
 
 __device__ __forceinline__ void publish(uint64_t *p, float v) {
   const uint64_t w = (1ull << 32) | (uint64_t)__builtin_bit_cast(unsigned, v);
@@ -51,12 +53,6 @@ __device__ __forceinline__ uint64_t peek(uint64_t *p) {
 
 __device__ __forceinline__ float word_value(uint64_t w) {
   return __builtin_bit_cast(float, (unsigned)(w & 0xffffffffull));
-}
-
-// Elements in chunk c of a row of nacc accesses of E elements.
-__device__ __forceinline__ float chunk_elems(int64_t c, int32_t chunk_acc, int32_t nacc, int E) {
-  const int64_t left = (int64_t)nacc - c * chunk_acc;
-  return (float)((left < chunk_acc ? left : chunk_acc) * E);
 }
 
 // Wait until the NQ words of every chunk of one row (xp: the row's words) are published and
@@ -238,8 +234,8 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
       for (int j = 0; j < XMAXCH; ++j) {
         const int64_t cc = tid + (int64_t)j * XLB;
         if (cc < C)
-          ln_chunk_terms(chunk_elems(cc, a.chunk_acc, a.nacc, E), pv[j][0], pv[j][1], pv[j][2],
-                         shift, ab[0], ab[1]);
+          ln_chunk_terms(split_chunk_elems(cc, a.chunk_acc, a.nacc, E), pv[j][0], pv[j][1],
+                         pv[j][2], shift, ab[0], ab[1]);
       }
       team_sum<2, XLB / 64>(ab, red, slot, waves, 0, wave, lane);
       slot ^= 1;

@@ -101,7 +101,7 @@ typedef enum {
   NORM_SCHEME_SPLIT = 2, /* one row over several workgroups (very long rows): a single pass
                             in which the row's workgroups exchange their chunk partials through
                             the workspace, each chunk held in registers throughout (16-byte
-                            accesses, no residual input, up to 1024 chunks, saved statistics
+                            accesses, no residual input, up to 512 chunks, saved statistics
                             for the backward), else two passes, the second re-reading its
                             chunk */
   NORM_SCHEME_LOOP = 3   /* backward only: one row per workgroup in two sweeps, the second

@@ -99,7 +99,7 @@ def test_forced_scheme(name, scheme, Ns, dt, kind):
                 run_and_check(_small(kind, dt, M, N, seed=3 * M + N + 1), stats=False)
 
 
-# ---- the split scheme's two forms -----------------------------------------------------------------
+# ---- the split scheme's two forms ----------------------------------------------------------------
 # Single pass (the workgroups of a row exchange chunk partials, each chunk stays in registers)
 # and two passes (the second re-reads its chunk). The backward's single pass needs the saved
 # statistics; with stats=False it recomputes them and runs two passes either way.
