@@ -189,6 +189,25 @@ def test_nan_row_propagates(kind, N, knob):
     assert torch.isnan(dW.float()).all()
 
 
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_split_exchange_chunk_limits(kind):
+    """Rows at the single-pass form's limits: 384 chunks of 8192 (the most a forward takes:
+    two row groups of 3 workgroups per CU on 256 CUs), 512 (the most the backward takes), and
+    one chunk past each, which run two passes; every one must match the oracle. The chunk
+    counts follow the device's CU count."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    fwd_max = min(512, 3 * cu // 2)
+    bwd_max = min(512, 2 * cu)
+    for C, ragged in ((fwd_max, 0), (fwd_max + 1, 0), (bwd_max, 0), (bwd_max, 8)):
+        N = 8192 * C + ragged
+        _say("split exchange limits %s N=%d" % (kind, N))
+        f = _split_form(kind, "bf16", nl.PASS_FWD, 2, N)
+        b = _split_form(kind, "bf16", nl.PASS_BWD, 2, N)
+        nchunks = -(-N // 8192)
+        assert (f > 0) == (nchunks <= fwd_max) and (b > 0) == (nchunks <= bwd_max)
+        run_and_check(_small(kind, "bf16", 2, N, seed=C + ragged))
+
+
 def test_split_exchange_wait_is_bounded():
     """The exchange's wait gives up rather than hangs: with chunk 0 withholding its partials
     (a test-only flag) and a poll limit of 8, every row of the call comes out NaN, the kernels
