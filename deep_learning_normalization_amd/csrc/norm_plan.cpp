@@ -402,7 +402,7 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // 20.9 us). The statistics pass keeps the forward's plan and workspace but never runs it
     // (it writes no Y, so its second pass re-reads nothing).
     if (t.xchg != 0 && wc == kFull && vpt == 4 && !residual) {
-      const int64_t cap = (int64_t)cu * (bwd ? kXchgBwdPerCu : kXchgFwdPerCu);
+      const int64_t cap = (int64_t)cu * (bwd ? kXchgBwdPerCu : xchg_fwd_per_cu(dtype));
       if (p.chunks <= kXchgMaxChunks && p.chunks * (bwd ? 1 : 2) <= cap) {
         int64_t G = cap / p.chunks;
         if (bwd && t.row_groups > 0 && t.row_groups < G) G = t.row_groups;

@@ -48,8 +48,12 @@ constexpr int64_t kWsMagic = 0x4E4F524D50415254LL; // "NORMPART"
 
 // Split exchange form: workgroups per CU its kernels are compiled to keep resident (their
 // launch bounds), which bounds its grid, and the most chunks per row it exchanges.
-constexpr int kXchgFwdPerCu = 3;
+constexpr int kXchgFwdPerCu = 3;    // weights in registers (fp32 beside 16-bit activations)
+constexpr int kXchgFwdPerCuLds = 4; // weights in LDS (stored like the activations)
 constexpr int kXchgBwdPerCu = 2;
+constexpr int xchg_fwd_per_cu(norm_dtype_t d) {
+  return (d == NORM_BF16_F32W || d == NORM_F16_F32W) ? kXchgFwdPerCu : kXchgFwdPerCuLds;
+}
 constexpr int64_t kXchgPollsDefault = 1 << 19;
 constexpr int64_t kXchgPollsMax = 1 << 24;
 constexpr int64_t kXchgMaxChunks = 512;

@@ -106,8 +106,19 @@ __device__ bool gather_row(uint64_t *xp, int64_t C, unsigned polls, float (&v)[X
 // Two rows are in hand at a time: the partials of row r + G are published before the wait for
 // row r's, so the wait overlaps the other workgroups' progress on row r; the inputs of row
 // r + 2G are in flight meanwhile.
+//
+// The weight and bias of the chunk live in LDS when they are stored like the activations (16
+// bytes per access; each thread reads only its own slots, so no barrier guards them): that
+// frees 32 VGPRs and lets 4 workgroups share a CU. fp32 weights beside 16-bit activations
+// (32 bytes per access) would need 64 KB of LDS per workgroup and stay in registers, 3 per CU.
+template <typename T, typename TW, int EV> constexpr bool fwd_weights_in_lds() {
+  return sizeof(WAcc<T, TW, EV>) <= 16;
+}
+
 template <typename T, typename TW, int EV, int VPT, bool LN>
-__global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs a) {
+__global__ __launch_bounds__(XLB, (fwd_weights_in_lds<T, TW, EV>() ? kXchgFwdPerCuLds
+                                                                     : kXchgFwdPerCu))
+void xsplit_fwd_kernel(FwdArgs a) {
   using A = Acc<T, EV>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
@@ -127,15 +138,26 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
   const TW *__restrict__ W = static_cast<const TW *>(a.w) + col0;
   const TW *__restrict__ Bb = a.b ? static_cast<const TW *>(a.b) + col0 : nullptr;
 
-  WAcc<T, TW, EV> rw[VPT], rb[VPT];
+  constexpr bool WL = fwd_weights_in_lds<T, TW, EV>();
+  using WA = WAcc<T, TW, EV>;
+  __shared__ WA lw[WL ? VPT : 1][WL ? XLB : 1], lb[WL ? VPT : 1][WL ? XLB : 1];
+  WA rw[WL ? 1 : VPT], rb[WL ? 1 : VPT];
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = tid + k * XLB;
-    rw[k].zero();
-    rb[k].zero();
+    WA w, b;
+    w.zero();
+    b.zero();
     if (v < nin) {
-      rw[k].load(W + (int64_t)v * E);
-      if (Bb) rb[k].load(Bb + (int64_t)v * E);
+      w.load(W + (int64_t)v * E);
+      if (Bb) b.load(Bb + (int64_t)v * E);
+    }
+    if constexpr (WL) {
+      lw[k][tid] = w;
+      lb[k][tid] = b;
+    } else {
+      rw[k] = w;
+      rb[k] = b;
     }
   }
   raw px[VPT], ra[VPT], rn[VPT];
@@ -205,8 +227,10 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
   issue(g); // g < M: the plan makes G at most M
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
-    rw[k].settle();
-    rb[k].settle();
+    if constexpr (!WL) {
+      rw[k].settle();
+      rb[k].settle();
+    }
     ra[k] = px[k];
   }
   issue(g + G);
@@ -256,8 +280,13 @@ __global__ __launch_bounds__(XLB, kXchgFwdPerCu) void xsplit_fwd_kernel(FwdArgs 
       if (v < nin) {
         float xf[E], wf[E], bf[E], y[E];
         A::unpack(ra[k], xf);
-        rw[k].get(wf);
-        rb[k].get(bf);
+        if constexpr (WL) {
+          lw[k][tid].get(wf);
+          lb[k][tid].get(bf);
+        } else {
+          rw[k].get(wf);
+          rb[k].get(bf);
+        }
 #pragma unroll
         for (int e = 0; e < E; ++e) y[e] = ((xf[e] - shift) - delta) * rstd * wf[e] + bf[e];
         A::st(Y + row * a.ldy + (int64_t)v * E, A::pack(y));
@@ -572,7 +601,7 @@ template <typename T, typename TW, bool LN> int bwd_resident() {
 template <typename T, typename TW>
 norm_status_t xfwd_typed(const Plan &p, const FwdArgs &a, hipStream_t s) {
   constexpr int F = full_epv<T>();
-  const int need = (int)kXchgFwdPerCu;
+  const int need = fwd_weights_in_lds<T, TW, F>() ? kXchgFwdPerCuLds : kXchgFwdPerCu;
   const int have = a.layernorm ? fwd_resident<T, TW, true>() : fwd_resident<T, TW, false>();
   if (have < need) return NORM_ERR_UNSUPPORTED;
   norm_status_t st = clear_words(a.xpart, a.M, a.chunks, false, s);
@@ -602,7 +631,7 @@ norm_status_t xbwd_typed(const BwdArgs &a, hipStream_t s) {
 } // namespace
 
 bool xsplit_ready(norm_dtype_t dtype, bool layernorm, bool bwd) {
-  const int need = bwd ? (int)kXchgBwdPerCu : (int)kXchgFwdPerCu;
+  const int need = bwd ? (int)kXchgBwdPerCu : xchg_fwd_per_cu(dtype);
   int have = 0;
 #define DLN_XR(T, TW)                                                                           \
   have = bwd ? (layernorm ? bwd_resident<T, TW, true>() : bwd_resident<T, TW, false>())          \

@@ -331,11 +331,14 @@ def test_plan_tuning_overrides():
 
 def test_split_exchange_plan():
     """The single-pass split form: 16-byte accesses, the default chunk, no residual input, at
-    most 512 chunks, and a grid (row groups x chunks) the device keeps resident: 3 workgroups
-    per CU forward (with room for two row groups), 2 backward."""
+    most 512 chunks, and a grid (row groups x chunks) the device keeps resident: 4 workgroups
+    per CU forward (3 with fp32 weights beside 16-bit activations), with room for two row
+    groups, and 2 backward."""
     cu = 256
     try:
-        for kind, pass_, per_cu in ((0, 0, 3), (1, 0, 3), (0, 1, 2), (1, 1, 2)):
+        mixed = nl.norm_plan(0, nl.BF16_F32W, 0, 256, 262144, cu_count=cu)
+        assert mixed["exchange_row_groups"] == min(256, cu * 3 // 32)
+        for kind, pass_, per_cu in ((0, 0, 4), (1, 0, 4), (0, 1, 2), (1, 1, 2)):
             for M, N in ((256, 262144), (4, 4194304), (3, 20000), (1000, 65536)):
                 # more chunks than the device holds at once (forward: twice over)
                 if N // 8192 * (2 if pass_ == 0 else 1) > cu * per_cu:

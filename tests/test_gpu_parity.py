@@ -191,12 +191,12 @@ def test_nan_row_propagates(kind, N, knob):
 
 @pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
 def test_split_exchange_chunk_limits(kind):
-    """Rows at the single-pass form's limits: 384 chunks of 8192 (the most a forward takes:
-    two row groups of 3 workgroups per CU on 256 CUs), 512 (the most the backward takes), and
-    one chunk past each, which run two passes; every one must match the oracle. The chunk
-    counts follow the device's CU count."""
+    """Rows at the single-pass form's limits: the most chunks of 8192 a forward takes (two row
+    groups of 4 workgroups per CU, at most 512), 512 (the most the backward takes), and one
+    chunk past each, which run two passes; every one must match the oracle. The chunk counts
+    follow the device's CU count."""
     cu = torch.cuda.get_device_properties(0).multi_processor_count
-    fwd_max = min(512, 3 * cu // 2)
+    fwd_max = min(512, 4 * cu // 2)
     bwd_max = min(512, 2 * cu)
     for C, ragged in ((fwd_max, 0), (fwd_max + 1, 0), (bwd_max, 0), (bwd_max, 8)):
         N = 8192 * C + ragged
