@@ -274,7 +274,8 @@ typedef enum {
   NORM_TUNE_TEAM_THREADS = 3,   /* threads per row team (multiple of 64); ignored where a team
                                    of that size cannot hold the row */
   NORM_TUNE_SPLIT_CHUNK = 4,    /* split scheme: elements per chunk */
-  NORM_TUNE_ROW_GROUPS = 5,     /* split backward: number of row groups */
+  NORM_TUNE_ROW_GROUPS = 5,     /* split backward: number of row groups (the single-pass form
+                                   takes at most this many, and never more than fit) */
   NORM_TUNE_TEAMS_PER_WG = 6,   /* block scheme: row teams per workgroup (their dW/dB partials
                                    are merged in LDS, so fewer partial rows are written) */
   NORM_TUNE_ROW_ORDER = 7,      /* wave/block schemes: 0 = row groups interleaved across the
