@@ -696,6 +696,21 @@ def test_large_mean_rows_fp32(N):
     run_and_check(w)
 
 
+@pytest.mark.parametrize("form,flag", SPLIT_FORMS, ids=[f[0] for f in SPLIT_FORMS])
+def test_split_hard_rows(form, flag):
+    """Long rows on both split forms where the chunk combine does the most work: fp32 rows far
+    from zero mean (mean 1000, sd 1), and bf16 rows with 1% of their columns scaled by 20
+    (chunks whose variances differ by orders of magnitude)."""
+    with tuned(exchange=flag):
+        for N in (65536, 262144):
+            _say("split hard rows %s N=%d" % (form, N))
+            run_and_check(_small("layernorm", "f32", 9, N, seed=N, x=inputs.normal(1000.0, 1.0)))
+            for kind in ("layernorm", "rmsnorm"):
+                w = dataclasses.replace(_small(kind, "bf16", 33, N, seed=N + 1),
+                                        outlier_frac=0.01)
+                run_and_check(w)
+
+
 @pytest.mark.parametrize("dt", ["bf16", "f32"])
 def test_outlier_channels(dt):
     w = dataclasses.replace(inputs.rms_hidden(5120, M=512), dtype=dt)
