@@ -165,9 +165,11 @@ def timed_workload(w, steps, warmup, torch, nl, min_footprint=1 << 30, max_sets=
     ms, wall, marks = run(step, steps, timed_kernels=want_bwd)
     out["ms_per_step"], out["wall_s"] = ms, wall
     if want_bwd:
-        b = [m.elapsed_ms() for m in marks]
-        out["bwd_timed_us_mean"] = 1e3 * sum(b) / len(b)
-        out["bwd_timed_us_median"] = 1e3 * sorted(b)[len(b) // 2]
+        b = sorted(1e3 * m.elapsed_ms() for m in marks)
+        out["bwd_timed_us_mean"] = sum(b) / len(b)
+        out["bwd_timed_us_median"] = b[len(b) // 2]
+        out["bwd_timed_us_p10"] = b[len(b) // 10]
+        out["bwd_timed_us_p90"] = b[(9 * len(b)) // 10]
     ms, _, _ = run(lambda i, mk: fwd(sets[i % S]), steps)
     out["fwd_us"] = ms * 1e3
     if want_bwd:
@@ -314,7 +316,42 @@ def cpu_baseline(w, budget_s=10.0):
             "sample": "whole workload (%d x %d), forward + backward incl. dW/dB, repeated %d "
                       "times in %.1f s; median run %.4f s; %s" % (w.M, w.N, len(times), total, t,
                                                                   cpu),
-            "seconds": round(t, 4), "rows_per_s": round(w.M / t, 1)}
+            "seconds": round(t, 4), "rows_per_s": round(w.M / t, 1),
+            "single_thread": oracle_single_thread()}
+
+
+def oracle_single_thread(runs=3):
+    """The oracle on one host thread, median of `runs` runs each: the RMSNorm fp32 2048 x 1024
+    forward and the RMSNorm bf16 32768 x 2048 forward + backward (the hidden-size workload),
+    as GB/s over their algorithmic bytes."""
+    import oracle
+    from deep_learning_normalization_amd import inputs, traffic
+    threads = oracle.num_threads()
+    out = []
+    try:
+        oracle.set_num_threads(1)
+        for w, both in ((inputs.RMS_F32_2048x1024, False), (inputs.rms_hidden(2048), True)):
+            host = inputs.make(w)
+            bits = {k: inputs.host_bits(host[k]) for k in ("X", "W", "dY")}
+            dt = oracle.BF16 if w.dtype == "bf16" else oracle.F32
+            times = []
+            for _ in range(runs):
+                t0 = time.perf_counter()
+                oracle.fwd(oracle.RMSNORM, dt, bits["X"], bits["W"], eps=float(w.eps))
+                if both:
+                    oracle.bwd(oracle.RMSNORM, dt, bits["X"], bits["dY"], bits["W"],
+                               eps=float(w.eps))
+                times.append(time.perf_counter() - t0)
+            t = sorted(times)[len(times) // 2]
+            nbytes = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N)
+            if both:
+                nbytes += traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N)
+            out.append({"workload": w.name, "pass": "fwd+bwd" if both else "fwd",
+                        "seconds": round(t, 4), "GBps": round(nbytes / t / 1e9, 3),
+                        "rows_per_s": round(w.M / t, 1), "cores": 1})
+    finally:
+        oracle.set_num_threads(threads)
+    return out
 
 
 def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
@@ -528,7 +565,10 @@ def main():
         "roofline": {"bound": "hbm", "kernel": "team_bwd_kernel (fused dX + dW/dB partials)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_bytes,
-                     "algorithmic_bytes": bfb, "avg_launch_us": round(bwd_us, 3)},
+                     "algorithmic_bytes": bfb, "avg_launch_us": round(bwd_us, 3),
+                     "launch_us_p10_p50_p90": [round(r["bwd_timed_us_p10"], 3),
+                                               round(r["bwd_timed_us_median"], 3),
+                                               round(r["bwd_timed_us_p90"], 3)]},
         "fwd": {"us": round(r["fwd_us"], 3), "GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1),
                 "frac_peak": round(fb / (r["fwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                 "bytes": fb},
