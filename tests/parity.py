@@ -150,7 +150,8 @@ def check_stats(got_mean, got_rstd, ref_mean, ref_rstd):
 
 
 def sample_rows(M, k=24, seed=0):
-    """First, last and seeded random rows (sorted, unique)."""
+    """First, last and seeded random rows (sorted, unique). Only for checks that say why they
+    cannot compare every row; run_and_check compares every row."""
     if M <= 3 * k:
         return np.arange(M)
     g = np.random.default_rng(seed)
@@ -158,20 +159,32 @@ def sample_rows(M, k=24, seed=0):
     return np.array(sorted(rows))
 
 
+def row_blocks(M, N, block_elems=1 << 24):
+    """Consecutive row ranges [r0, r1) covering all M rows, each of at most block_elems
+    elements (at least one row): the oracle and the comparison stream through them, so host
+    memory stays at a few blocks of float64 whatever the workload's size."""
+    rb = max(1, block_elems // max(1, N))
+    return [(r0, min(M, r0 + rb)) for r0 in range(0, M, rb)]
+
+
 def _to_dev(t, dev):
     return None if t is None else t.to(dev)
 
 
-def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stats=True,
-                  dr="none", dh=False, stream=None):
+def _host_rows(a, r0, r1):
+    return a[r0:r1].double().cpu().numpy()
+
+
+def run_and_check(w, M=None, dev="cuda", want_bwd=True, stats=True, dr="none", dh=False,
+                  stream=None, block_elems=1 << 24):
     """Run forward (and backward) of workload w on the GPU and check every output against the
-    oracle. Rows are checked in full when M*N <= full_limit, else on sampled rows; dW/dB always
-    over all rows.
+    oracle: Y, H, mean, rstd and dX on every row, compared in blocks of rows that the oracle
+    computes one after another; dW and dB on every column, summed by the oracle over all rows.
 
     dr: "none" (no dR), "alias" (dR is dX), "separate" (its own buffer, must equal dX).
     dh: add a seeded incoming gradient of H (residual variant).
     stats: pass the forward's mean/rstd to the backward (else it recomputes them).
-    Returns the device outputs for further checks.
+    Returns the device outputs for further checks, and "rows_compared" (every row: M).
     """
     if dh and w.dh is None:
         w = dataclasses.replace(w, dh=inputs.normal(0, 0.5))
@@ -186,47 +199,36 @@ def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stat
     out = {"Y": Y, "H": H, "mean": mean, "rstd": rstd}
 
     bits = {k: inputs.host_bits(t[k]) for k in ("X", "W", "B", "R", "dY", "dH")}
-    rows = np.arange(M) if M * N <= full_limit else sample_rows(M)
-    idx = torch.as_tensor(rows, device=dev, dtype=torch.long)
-
-    def take(a):
-        return a.index_select(0, idx).double().cpu().numpy()
-
-    # oracle forward on the sampled rows (contiguous runs)
-    ref = {"y": [], "mean": [], "rstd": [], "h": []}
-    runs = np.split(rows, np.flatnonzero(np.diff(rows) != 1) + 1) if len(rows) else []
-    for run in runs:
+    blocks = row_blocks(M, N, block_elems)
+    rstd_ref = np.empty(M, np.float64)
+    compared = 0
+    # the oracle's own h (as input bits) for the residual backward, formed block by block
+    xbits = bits["X"]
+    if R is not None:
+        xbits = np.empty((M, N), np.float32 if w.dtype == "f32" else np.uint16)
+    for r0, r1 in blocks:
         f = oracle.fwd(kind, dtc, bits["X"], bits["W"], bits["B"], bits["R"], eps=eps,
-                       rows=(int(run[0]), int(run[-1]) + 1), want_h=R is not None)
-        for k in ref:
-            if f[k] is not None:
-                ref[k].append(f[k])
-    cat = {k: (np.concatenate(v) if v else None) for k, v in ref.items()}
-    if M:
-        check_values("Y", take(Y), cat["y"], w.dtype)
-        check_stats(mean.index_select(0, idx).double().cpu().numpy() if mean is not None else None,
-                    rstd.index_select(0, idx).double().cpu().numpy(),
-                    cat["mean"] if w.kind == "layernorm" else None, cat["rstd"])
+                       rows=(r0, r1), want_h=R is not None)
+        where = " rows %d-%d" % (r0, r1 - 1)
+        check_values("Y" + where, _host_rows(Y, r0, r1), f["y"], w.dtype)
+        check_stats(mean[r0:r1].double().cpu().numpy() if mean is not None else None,
+                    rstd[r0:r1].double().cpu().numpy(),
+                    f["mean"] if w.kind == "layernorm" else None, f["rstd"])
+        rstd_ref[r0:r1] = f["rstd"]
         if R is not None:
-            check_h(take(H), cat["h"], w.dtype)
+            check_h(_host_rows(H, r0, r1), f["h"], w.dtype)
+            h = f["h"]
+            xbits[r0:r1] = (oracle.round_bf16(h) if w.dtype == "bf16" else
+                            oracle.round_f16(h) if w.dtype == "f16" else h.astype(np.float32))
+        compared += r1 - r0
+        del f
+    out["rows_compared"] = compared
+    assert compared == M
     if not want_bwd or w.dy is None:
         return out
 
     dY, dH = _to_dev(t["dY"], dev), _to_dev(t["dH"], dev)
     Xin = H if R is not None else X
-    # the oracle's own h (as input bits) for the residual backward, formed block by block
-    if R is not None:
-        xbits = np.empty((M, N), np.float32 if w.dtype == "f32" else np.uint16)
-        for r0 in range(0, M, 4096):
-            r1 = min(M, r0 + 4096)
-            h = oracle.fwd(kind, dtc, bits["X"], bits["W"], None, bits["R"], eps=eps,
-                           rows=(r0, r1), want_h=True)["h"]
-            xbits[r0:r1] = (oracle.round_bf16(h) if w.dtype == "bf16" else
-                            oracle.round_f16(h) if w.dtype == "f16" else h.astype(np.float32))
-            del h
-    else:
-        xbits = bits["X"]
-
     dX = torch.empty_like(X)
     dW = torch.empty_like(W)
     dB = torch.empty_like(W) if w.kind == "layernorm" else None
@@ -241,17 +243,19 @@ def run_and_check(w, M=None, dev="cuda", full_limit=1 << 22, want_bwd=True, stat
     out.update({"dX": dX, "dW": dW, "dB": dB, "dR": dR, "ws": ws})
 
     g_full = oracle.bwd(kind, dtc, xbits, bits["dY"], bits["W"], eps=eps, want_dx=False)
-    dx_ref = []
-    for run in runs:
-        g = oracle.bwd(kind, dtc, xbits, bits["dY"], bits["W"], bits["dH"], eps=eps,
-                       rows=(int(run[0]), int(run[-1]) + 1), want_dw=False)
-        dx_ref.append(g["dx"])
-    if M:
-        fl = dx_floor(torch.as_tensor(rows), t["dY"], t["W"], cat["rstd"], N)
-        check_values("dX", take(dX), np.concatenate(dx_ref), w.dtype, floor=fl)
     check_colsums("dW", dW.double().cpu().numpy(), g_full["dw"], w.wdtype or w.dtype)
     if dB is not None:
         check_colsums("dB", dB.double().cpu().numpy(), g_full["db"], w.wdtype or w.dtype)
+    compared = 0
+    for r0, r1 in blocks:
+        g = oracle.bwd(kind, dtc, xbits, bits["dY"], bits["W"], bits["dH"], eps=eps,
+                       rows=(r0, r1), want_dw=False)
+        fl = dx_floor(torch.arange(r0, r1), t["dY"], t["W"], rstd_ref[r0:r1], N)
+        check_values("dX rows %d-%d" % (r0, r1 - 1), _host_rows(dX, r0, r1), g["dx"], w.dtype,
+                     floor=fl)
+        compared += r1 - r0
+        del g
+    assert compared == M
     if dr == "separate" and M:
         assert torch.equal(dR.view(torch.int16) if dR.dtype == torch.bfloat16 else dR,
                            dX.view(torch.int16) if dX.dtype == torch.bfloat16 else dX)

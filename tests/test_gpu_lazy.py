@@ -216,7 +216,10 @@ def test_lazy_linear_zero_rows():
                          ids=lambda p: p.name)
 def test_lazy_linear_full_size(proj):
     """The full-size projections in the configuration the benchmark times, on sampled rows
-    (first, last, tile edges and random ones) against the oracle."""
+    (first, last, the 128-row tile edges 127/128 and 8191/8192, and random ones) against the
+    oracle. Rows are sampled because every row would cost the double-precision oracle
+    2 * 16384 * 4096 * 4096 = 550 G multiply-adds in plain loops (many minutes on the host);
+    the smaller projection tests compare every row."""
     w = proj.norm
     _say("lazy full size %s" % proj.name)
     t = inputs.make(w)

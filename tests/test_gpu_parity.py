@@ -43,8 +43,11 @@ def _small(kind, dtype, M, N, seed=0, **kw):
 @pytest.mark.parametrize("w", inputs.all_workloads(), ids=lambda w: w.name)
 def test_full_size_workload(w):
     _say("full size %s (%d x %d, %s %s)" % (w.name, w.M, w.N, w.kind, w.dtype))
-    run_and_check(w)
+    out = run_and_check(w)
     torch.cuda.synchronize()
+    assert out["rows_compared"] == w.M
+    _say("full size %s: rows compared %d of %d (100%%), every column of dW/dB"
+         % (w.name, out["rows_compared"], w.M))
 
 
 # ---- sweep around tile and scheme boundaries ----------------------------------------------------
