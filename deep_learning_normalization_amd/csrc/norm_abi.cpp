@@ -4,6 +4,7 @@
 // (cached), build the launch plan, check the workspace, queue the kernels on the caller's
 // stream. Nothing here allocates or synchronises.
 #include <atomic>
+#include <cstdint>
 #include <new>
 
 #include "norm_internal.hpp"
@@ -43,6 +44,9 @@ norm_status_t current_cu_count(int *cu) {
 float *ws_region(void *ws, size_t off) {
   return reinterpret_cast<float *>(static_cast<char *>(ws) + off);
 }
+
+// 64-bit word i of the workspace header
+uint64_t *header_word(void *ws, int i) { return static_cast<uint64_t *>(ws) + i; }
 
 norm_status_t ws_ok(const dln::Plan &p, const void *ws, size_t ws_bytes) {
   if (p.ws_bytes == 0) return NORM_OK;
@@ -105,6 +109,8 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
                     dln::xsplit_ready(dtype, kind == NORM_LAYERNORM, true);
   b.xpart = xchg ? reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + plan->off_xpart)
                  : nullptr;
+  b.xerr = xchg ? header_word(workspace, dln::kWsErrWord) : nullptr;
+  b.tag = xchg ? dln::next_exchange_tag() : 0u;
   b.polls = (uint32_t)(dln::tuning().xchg_polls > 0 ? dln::tuning().xchg_polls
                                                      : dln::kXchgPollsDefault);
   b.withhold = dln::tuning().xchg_withhold == 1 ? 1 : 0;
@@ -316,6 +322,8 @@ norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const v
     // the single-pass exchange form where the plan allows it and Y is written
     if (p.xchg && Y && !R && dln::xsplit_ready(dtype, kind == NORM_LAYERNORM, false)) {
       a.xpart = reinterpret_cast<uint64_t *>(static_cast<char *>(workspace) + p.off_xpart);
+      a.xerr = header_word(workspace, dln::kWsErrWord);
+      a.tag = dln::next_exchange_tag();
       a.xgroups = p.xrow_groups;
       a.polls = (uint32_t)(dln::tuning().xchg_polls > 0 ? dln::tuning().xchg_polls
                                                          : dln::kXchgPollsDefault);
@@ -428,6 +436,34 @@ norm_status_t norm_workspace_size(norm_kind_t kind, norm_dtype_t dtype, norm_pas
   return dln::workspace_bytes(kind, dtype, pass, M, N, residual, cu, dln::tuning(), bytes);
 }
 
+size_t norm_workspace_bytes(norm_kind_t kind, int pass, int64_t M, int64_t N,
+                            norm_dtype_t dtype, int residual) {
+  if (M < 0 || N <= 0) return SIZE_MAX;
+  size_t b = 0;
+  if (dln::workspace_bytes_any_device(kind, dtype, static_cast<norm_pass_t>(pass), M, N,
+                                      residual, dln::tuning(), &b) != NORM_OK)
+    return SIZE_MAX;
+  return b;
+}
+
+norm_status_t norm_workspace_status(void *workspace, size_t workspace_bytes,
+                                    norm_stream_t stream) {
+  if (workspace_bytes < dln::kWsHeaderBytes) return NORM_OK;
+  if (!workspace || ((uintptr_t)workspace & 15u)) return NORM_ERR_WORKSPACE;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint64_t *word = header_word(workspace, dln::kWsErrWord);
+  uint64_t v = 0;
+  if (hipMemcpyAsync(&v, word, sizeof v, hipMemcpyDeviceToHost, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return NORM_ERR_HIP;
+  if (v != dln::kXchgFailWord) return NORM_OK;
+  const uint64_t zero = 0;
+  if (hipMemcpyAsync(word, &zero, sizeof zero, hipMemcpyHostToDevice, s) != hipSuccess ||
+      hipStreamSynchronize(s) != hipSuccess)
+    return NORM_ERR_HIP;
+  return NORM_ERR_EXCHANGE;
+}
+
 norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
                         int64_t N, int residual, int align, int cu_count, norm_plan_t *out) {
   if (!out) return NORM_ERR_INVALID_ARG;
@@ -476,6 +512,8 @@ const char *norm_status_string(norm_status_t status) {
   case NORM_ERR_UNSUPPORTED: return "NORM_ERR_UNSUPPORTED: shape or option not supported";
   case NORM_ERR_WORKSPACE: return "NORM_ERR_WORKSPACE: workspace missing or too small";
   case NORM_ERR_HIP: return "NORM_ERR_HIP: HIP runtime or launch failure";
+  case NORM_ERR_EXCHANGE:
+    return "NORM_ERR_EXCHANGE: a long-row call gave up waiting for partial sums (NaN outputs)";
   default: return "unknown norm status";
   }
 }

@@ -26,9 +26,11 @@ struct FwdArgs {
   float *mean;        // or nullptr
   float *rstd;        // or nullptr
   float *rowpart;     // split: [M][chunks][4]
-  uint64_t *xpart;    // split exchange form: [M][chunks][4] exchange words
+  uint64_t *xpart;    // split exchange form: [M][chunks][kXchgWordsPerChunk] exchange words
+  uint64_t *xerr;     // split exchange form: the workspace header's exchange-failure word
   int64_t xgroups;    // split exchange form: row groups
   uint32_t polls;     // split exchange form: polls before a row is given up
+  uint32_t tag;       // split exchange form: this call's tag (never 0 or ~0)
   int32_t withhold;   // split exchange form, tests only: chunk 0 publishes nothing
   int64_t ldx, ldr, ldy, ldh; // elements between row starts of X, R, Y, H (N when contiguous)
   int64_t M;
@@ -57,9 +59,11 @@ struct BwdArgs {
   int64_t *header;    // workspace header: magic, partials, N
   float *rowpart;     // split: [M][chunks][4]
   float *stats;       // split without saved stats: [2][M]
-  uint64_t *xpart;    // split exchange form: [M][chunks][4] exchange words, or nullptr when
-                      // the two-pass form runs
+  uint64_t *xpart;    // split exchange form: [M][chunks][kXchgWordsPerChunk] exchange words,
+                      // or nullptr when the two-pass form runs
+  uint64_t *xerr;     // split exchange form: the workspace header's exchange-failure word
   uint32_t polls;     // split exchange form: polls before a row is given up
+  uint32_t tag;       // split exchange form: this call's tag (never 0 or ~0)
   int32_t withhold;   // split exchange form, tests only: chunk 0 publishes nothing
   int64_t ldx, lddy, lddh, lddx, lddr; // elements between row starts (N when contiguous)
   int64_t M;
@@ -112,6 +116,9 @@ norm_status_t launch_split_bwd(const Plan &p, norm_dtype_t dtype, const BwdArgs 
 // the split scheme in one pass, chunk partials exchanged between the workgroups of a row;
 // xsplit_ready: whether the device keeps its kernels resident as the plan assumes
 bool xsplit_ready(norm_dtype_t dtype, bool layernorm, bool bwd);
+// A fresh tag for one call of the exchange form: a process-wide counter from a random start,
+// never 0 or ~0.
+uint32_t next_exchange_tag();
 norm_status_t launch_xsplit_fwd(const Plan &p, norm_dtype_t dtype, const FwdArgs &a,
                                 hipStream_t s);
 norm_status_t launch_xsplit_bwd(norm_dtype_t dtype, const BwdArgs &a, hipStream_t s);

@@ -415,11 +415,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
   }
   if (p.chunk_elems == 0) p.chunk_elems = N;
 
+  // Every workspace starts with the header; forwards of the wave and block schemes need none.
   size_t off = 0;
+  p.off_header = 0;
   if (bwd) {
     p.partials = scheme == NORM_SCHEME_SPLIT ? p.row_groups : p.grid;
     if (p.xchg && p.xrow_groups > p.partials) p.partials = p.xrow_groups;
-    p.off_header = 0;
     p.off_colpart = kWsHeaderBytes;
     off = align256(kWsHeaderBytes + (size_t)2 * (size_t)p.partials * (size_t)N * 4);
     if (scheme == NORM_SCHEME_SPLIT) {
@@ -429,12 +430,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       off = align256(off + (size_t)2 * (size_t)Mm * 4);
     }
   } else if (scheme == NORM_SCHEME_SPLIT) {
-    p.off_rowpart = 0;
-    off = align256((size_t)Mm * (size_t)p.chunks * 4 * 4);
+    p.off_rowpart = kWsHeaderBytes;
+    off = align256(kWsHeaderBytes + (size_t)Mm * (size_t)p.chunks * 4 * 4);
   }
   if (p.xchg) {
     p.off_xpart = off;
-    off = align256(off + (size_t)Mm * (size_t)p.chunks * 4 * 8);
+    off = align256(off + (size_t)Mm * (size_t)p.chunks * kXchgWordsPerChunk * 8);
   }
   p.ws_bytes = off;
   *out = p;
@@ -455,6 +456,21 @@ norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t 
     if (make_plan(kind, dtype, pass, M, N, residual, align, cu, t, &p) == NORM_OK &&
         p.ws_bytes > best)
       best = p.ws_bytes;
+  *bytes = best;
+  return NORM_OK;
+}
+
+norm_status_t workspace_bytes_any_device(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass,
+                                         int64_t M, int64_t N, int residual, const Tuning &t,
+                                         size_t *bytes) {
+  if (!bytes) return NORM_ERR_INVALID_ARG;
+  size_t best = 0;
+  for (int cu = 1; cu <= kMaxCuCount; ++cu) {
+    size_t b = 0;
+    const norm_status_t s = workspace_bytes(kind, dtype, pass, M, N, residual, cu, t, &b);
+    if (s != NORM_OK) return s;
+    if (b > best) best = b;
+  }
   *bytes = best;
   return NORM_OK;
 }

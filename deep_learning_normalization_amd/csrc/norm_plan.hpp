@@ -33,18 +33,25 @@ struct Plan {
   int xchg = 0;            // split: the single-pass exchange form may run (norm_xsplit.hip)
   int64_t xrow_groups = 0; // split exchange form: row groups (its grid is xrow_groups x chunks)
   // workspace layout (bytes from the workspace start; every region 256-byte aligned)
-  size_t off_header = 0;   // backward: kWsHeaderBytes describing the partials (see below)
+  size_t off_header = 0;   // kWsHeaderBytes at the workspace start (see below)
   size_t off_colpart = 0;  // [2][partials][N] fp32: dW partials then dB partials
   size_t off_rowpart = 0;  // split: [M][chunks][4] fp32 per-chunk row partials
   size_t off_stats = 0;    // split backward without saved stats: [M] mean then [M] rstd
-  size_t off_xpart = 0;    // split exchange form: [M][chunks][4] 64-bit exchange words
+  size_t off_xpart = 0;    // split exchange form: [M][chunks][kXchgWordsPerChunk] 64-bit words
   size_t ws_bytes = 0;
 };
 
-// The backward's fused pass writes this header at the start of its workspace so that the
-// column reduction (possibly a separate call) knows how many partial rows follow.
+// Every workspace starts with this header of 64-bit words. The backward's fused pass writes
+// words 0-2 (magic, partial rows, N) so that the column reduction (possibly a separate call)
+// knows how many partial rows follow; word 3 is set by a split-scheme exchange wait that gave
+// up, and read and cleared by norm_workspace_status.
 constexpr size_t kWsHeaderBytes = 256;
 constexpr int64_t kWsMagic = 0x4E4F524D50415254LL; // "NORMPART"
+constexpr int kWsErrWord = 3;
+constexpr uint64_t kXchgFailWord = 0x584348474641494CULL; // "XCHGFAIL"
+// Largest compute-unit count of a gfx950 device: norm_workspace_bytes sizes for every count up
+// to this one.
+constexpr int kMaxCuCount = 256;
 
 // Split exchange form: workgroups per CU its kernels are compiled to keep resident (their
 // launch bounds), which bounds its grid, and the most chunks per row it exchanges.
@@ -54,6 +61,9 @@ constexpr int kXchgBwdPerCu = 2;
 constexpr int xchg_fwd_per_cu(norm_dtype_t d) {
   return (d == NORM_BF16_F32W || d == NORM_F16_F32W) ? kXchgFwdPerCu : kXchgFwdPerCuLds;
 }
+// 64-bit exchange words per (row, chunk): each partial value (at most three) is published as a
+// pair of words, padded to eight (64 bytes).
+constexpr int kXchgWordsPerChunk = 8;
 constexpr int64_t kXchgPollsDefault = 1 << 19;
 constexpr int64_t kXchgPollsMax = 1 << 24;
 constexpr int64_t kXchgMaxChunks = 512;
@@ -85,6 +95,10 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
 norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
                               int64_t N, int residual, int cu_count, const Tuning &t,
                               size_t *bytes);
+// The largest of workspace_bytes over every compute-unit count 1 .. kMaxCuCount.
+norm_status_t workspace_bytes_any_device(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass,
+                                         int64_t M, int64_t N, int residual, const Tuning &t,
+                                         size_t *bytes);
 
 // Argument checks (no device access). They return NORM_OK or NORM_ERR_INVALID_ARG.
 struct FwdCheck {

@@ -8,20 +8,27 @@
 //   grid      G row groups x C chunks. Workgroup (g, c) owns column chunk c (its weight and
 //             bias stay in registers) and walks rows g, g + G, g + 2G, ...; it publishes row
 //             r + G's partials before it waits for row r's, with row r + 2G's loads in flight.
-//   exchange  per (row, chunk) four 64-bit words: bit 32 marks the word as published, the low
-//             half holds an fp32 partial. They are written and read with relaxed atomics at
-//             agent scope, which the compiler makes coherent across the XCDs' separate L2s;
-//             each word carries its own valid bit, so no fence orders anything. The launcher
-//             zeroes the words with a kernel before every call (no memset, so graph replays
-//             start clean too).
+//   exchange  per (row, chunk) eight 64-bit words: each fp32 partial goes out as a pair of
+//             words, (tag, value) and (~tag, value), where tag is a 32-bit number drawn for the
+//             call. A partial counts as published once both words of its pair carry this call's
+//             tag (and its complement) around the same value, so words left by earlier calls
+//             (other tags) or by whatever the memory held before (which would have to match 64
+//             bits of pattern) never pass, and no call needs the words cleared first. Words are
+//             written and read with relaxed atomics at agent scope, which the compiler makes
+//             coherent across the XCDs' separate L2s; each pair validates itself, so no fence
+//             orders anything. Tags come from a process-wide counter; a call captured into a
+//             HIP graph replays with its tag fixed, so under capture the launcher clears the
+//             words with a kernel first (no memset, so replays start clean).
 //   progress  workgroup (g, c) only waits for the other C - 1 workgroups of row group g, whose
-//             ids are adjacent to its own. Workgroups are dispatched in id order, so every
-//             group below the highest dispatched one is complete on the device and can finish;
-//             the plan keeps C within what the device holds at once (C <= G * C <= resident
-//             workgroups), so the group being dispatched fits too. The wait is bounded anyway:
-//             after a set number of polls (2^19 by default, a second or so) the workgroup gives
-//             up, writes NaN for the row and stops waiting for later rows, so a broken
-//             assumption shows up as NaN outputs, never as a hang.
+//             ids are adjacent to its own. The plan keeps the grid within what the device holds
+//             at once (G * C <= resident workgroups), so on an otherwise idle device every
+//             workgroup of a group is running while the others wait. Neither HIP nor the
+//             hardware promises that (dispatch order is not guaranteed, and other work may hold
+//             compute units), so the wait is bounded: after a set number of polls (2^19 by
+//             default, a second or so) the workgroup gives up, writes NaN for the row, stops
+//             waiting for later rows and sets the workspace header's exchange-failure word
+//             (reported by norm_workspace_status): a broken assumption shows up as NaN outputs
+//             and a status, never as a hang.
 //
 // Method (web page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
 // matsubara.tec.br): para. 6, very large shapes as a regression class; paras. 8-10, the split
@@ -30,6 +37,10 @@
 // (brifing.si), item 4: one row's norm spread over several thread blocks (multi-CTA). The
 // chunk combination is the parallel-variance one: the row mean from the chunk means, the
 // squared deviation from the chunk sums plus count * (chunk mean - row mean)^2.
+#include <atomic>
+#include <chrono>
+#include <random>
+
 #include "norm_device.hpp"
 #include "norm_internal.hpp"
 
@@ -38,38 +49,44 @@ namespace {
 
 constexpr int XLB = 256;                // threads per workgroup
 constexpr int XMAXCH = 2;               // chunks per thread in the exchange (C <= 512)
-constexpr int kWordsPerChunk = 4;
+constexpr int kWordsPerChunk = kXchgWordsPerChunk;
 static_assert(kXchgMaxChunks <= (int64_t)XLB * XMAXCH, "the plan admits more chunks than a "
                                                         "workgroup gathers");
+static_assert(kWordsPerChunk >= 2 * 3, "a word pair for each of up to three partials");
 
-__device__ __forceinline__ void publish(uint64_t *p, float v) {
-  const uint64_t w = (1ull << 32) | (uint64_t)__builtin_bit_cast(unsigned, v);
-  __hip_atomic_store(p, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+// Partial q of a chunk: the word pair at 2q, 2q + 1.
+__device__ __forceinline__ void publish(uint64_t *p, float v, uint32_t tag) {
+  const uint64_t bits = (uint64_t)__builtin_bit_cast(unsigned, v);
+  __hip_atomic_store(p, ((uint64_t)tag << 32) | bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
+  __hip_atomic_store(p + 1, ((uint64_t)(~tag) << 32) | bits, __ATOMIC_RELAXED,
+                     __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ uint64_t peek(uint64_t *p) {
+__device__ __forceinline__ uint64_t peek(const uint64_t *p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-__device__ __forceinline__ float word_value(uint64_t w) {
-  return __builtin_bit_cast(float, (unsigned)(w & 0xffffffffull));
+// Whether the pair (a, b) was published by this call (tag): a carries the tag, b its
+// complement, both the same value. Sets v to the value.
+__device__ __forceinline__ int pair_valid(uint64_t a, uint64_t b, uint32_t tag, float &v) {
+  v = __builtin_bit_cast(float, (unsigned)(a & 0xffffffffull));
+  return (int)((uint32_t)(a >> 32) == tag) & (int)((uint32_t)(b >> 32) == ~tag) &
+         (int)((uint32_t)a == (uint32_t)b);
 }
 
-// Wait until the NQ words of every chunk of one row (xp: the row's words) are published and
-// return this thread's chunks tid + XLB * j in v[j] (zeros past C), plus chunk 0's first word
-// in v0. Every thread of the workgroup calls it. Returns false, with NaN in every value, once a
-// wait has given up after `polls` polls (`failed` then stays set and later calls return at
-// once).
+// Wait until the NQ partials of every chunk of one row (xp: the row's words) are published and
+// return this thread's chunks tid + XLB * j in v[j] (zeros past C), plus chunk 0's first
+// partial in v0. Every thread of the workgroup calls it. Returns false, with NaN in every value,
+// once a wait has given up after `polls` polls (`failed` then stays set and later calls return
+// at once); the first give-up of a workgroup also sets the exchange-failure word `err`.
 template <int NQ>
-__device__ bool gather_row(uint64_t *xp, int64_t C, unsigned polls, float (&v)[XMAXCH][NQ],
-                           float &v0, bool &failed) {
+__device__ bool gather_row(const uint64_t *xp, int64_t C, unsigned polls, uint32_t tag,
+                           uint64_t *err, float (&v)[XMAXCH][NQ], float &v0, bool &failed) {
   const int tid = threadIdx.x;
   if (!failed) {
     for (unsigned spin = 0;; ++spin) {
-      int ok = 1;
-      const uint64_t w0 = peek(xp);
-      ok &= (int)(w0 >> 32);
-      v0 = word_value(w0);
+      int ok = pair_valid(peek(xp), peek(xp + 1), tag, v0);
 #pragma unroll
       for (int j = 0; j < XMAXCH; ++j) {
         const int64_t cc = tid + (int64_t)j * XLB;
@@ -77,9 +94,8 @@ __device__ bool gather_row(uint64_t *xp, int64_t C, unsigned polls, float (&v)[X
         for (int q = 0; q < NQ; ++q) {
           v[j][q] = 0.0f;
           if (cc < C) {
-            const uint64_t w = peek(xp + cc * kWordsPerChunk + q);
-            ok &= (int)(w >> 32);
-            v[j][q] = word_value(w);
+            const uint64_t *w = xp + cc * kWordsPerChunk + 2 * q;
+            ok &= pair_valid(peek(w), peek(w + 1), tag, v[j][q]);
           }
         }
       }
@@ -88,6 +104,8 @@ __device__ bool gather_row(uint64_t *xp, int64_t C, unsigned polls, float (&v)[X
       __builtin_amdgcn_s_sleep(4);
     }
     failed = true;
+    if (tid == 0 && err)
+      __hip_atomic_store(err, kXchgFailWord, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
   const float nan = __builtin_nanf("");
   v0 = nan;
@@ -203,9 +221,9 @@ void xsplit_fwd_kernel(FwdArgs a) {
       team_sum<2, XLB / 64>(qc, red, slot, waves, 0, wave, lane);
       slot ^= 1;
       if (tid == 0 && !(a.withhold && c == 0)) {
-        publish(xc + 0, mc);
-        publish(xc + 1, qc[0]);
-        publish(xc + 2, qc[1]);
+        publish(xc + 0, mc, a.tag);
+        publish(xc + 2, qc[0], a.tag);
+        publish(xc + 4, qc[1], a.tag);
       }
     } else {
       float q[1] = {0.0f};
@@ -218,7 +236,7 @@ void xsplit_fwd_kernel(FwdArgs a) {
       }
       team_sum<1, XLB / 64>(q, red, slot, waves, 0, wave, lane);
       slot ^= 1;
-      if (tid == 0 && !(a.withhold && c == 0)) publish(xc, q[0]);
+      if (tid == 0 && !(a.withhold && c == 0)) publish(xc, q[0], a.tag);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) settle(r[k]);
@@ -247,7 +265,8 @@ void xsplit_fwd_kernel(FwdArgs a) {
     // team sum (a fixed order; the two-pass form combines in the same order with the same
     // terms, ln_chunk_terms, so both forms give the same bits)
     float pv[XMAXCH][NQ], m0;
-    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, a.polls, pv, m0, failed);
+    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, a.polls, a.tag, a.xerr, pv, m0,
+                   failed);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) settle(ra[k]);
     float shift = 0.0f, delta = 0.0f, rstd;
@@ -402,7 +421,7 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
     if (tid == 0 && !(a.withhold && c == 0)) {
       uint64_t *xc = a.xpart + (row * C + c) * kWordsPerChunk;
 #pragma unroll
-      for (int q = 0; q < NQ; ++q) publish(xc + q, sums[q]);
+      for (int q = 0; q < NQ; ++q) publish(xc + 2 * q, sums[q], a.tag);
     }
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
@@ -436,7 +455,8 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
     if (next < M) publish_partials(xn, dyn, mn, next);
 
     float pv[XMAXCH][NQ], unused;
-    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, a.polls, pv, unused, failed);
+    gather_row<NQ>(a.xpart + row * C * kWordsPerChunk, C, a.polls, a.tag, a.xerr, pv, unused,
+                   failed);
 #pragma unroll
     for (int k = 0; k < VPT; ++k) {
       settle(xa[k]);
@@ -564,8 +584,9 @@ __global__ __launch_bounds__(XLB, kXchgBwdPerCu) void xsplit_bwd_kernel(BwdArgs 
 
 // ---- launchers -------------------------------------------------------------------------------
 
-// Clears n exchange words, with the same agent-scope stores that publish them. One kernel name
-// per pass, so that profiles attribute it.
+// Clears n exchange words, with the same agent-scope stores that publish them; run only before
+// a call captured into a HIP graph, whose replays reuse one tag. One kernel name per pass, so
+// that profiles attribute it.
 __device__ __forceinline__ void clear_n(uint64_t *p, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
     __hip_atomic_store(p + i, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -573,7 +594,20 @@ __device__ __forceinline__ void clear_n(uint64_t *p, int64_t n) {
 __global__ __launch_bounds__(256) void xclear_fwd_kernel(uint64_t *p, int64_t n) { clear_n(p, n); }
 __global__ __launch_bounds__(256) void xclear_bwd_kernel(uint64_t *p, int64_t n) { clear_n(p, n); }
 
+// Whether work queued on s now is being captured into a graph. A stream the runtime cannot
+// answer for counts as captured (the clear is then merely redundant); the error that query
+// leaves is consumed so that the caller's next error check does not see it.
+bool capturing(hipStream_t s) {
+  hipStreamCaptureStatus cs = hipStreamCaptureStatusNone;
+  if (hipStreamIsCapturing(s, &cs) != hipSuccess) {
+    (void)hipGetLastError();
+    return true;
+  }
+  return cs != hipStreamCaptureStatusNone;
+}
+
 norm_status_t clear_words(uint64_t *words, int64_t M, int64_t C, bool bwd, hipStream_t s) {
+  if (!capturing(s)) return NORM_OK; // eager calls: a fresh tag makes every old word stale
   const int64_t n = M * C * kWordsPerChunk;
   const int64_t blocks = (n + 255) / 256 < 1024 ? (n + 255) / 256 : 1024;
   const hipError_t e = launch(bwd ? xclear_bwd_kernel : xclear_fwd_kernel,
@@ -629,6 +663,17 @@ norm_status_t xbwd_typed(const BwdArgs &a, hipStream_t s) {
 }
 
 } // namespace
+
+uint32_t next_exchange_tag() {
+  static std::atomic<uint32_t> counter{[] {
+    std::random_device rd;
+    return (uint32_t)rd() ^ (uint32_t)std::chrono::steady_clock::now().time_since_epoch().count();
+  }()};
+  for (;;) {
+    const uint32_t t = counter.fetch_add(1, std::memory_order_relaxed);
+    if (t != 0u && t != ~0u) return t;
+  }
+}
 
 bool xsplit_ready(norm_dtype_t dtype, bool layernorm, bool bwd) {
   const int need = bwd ? (int)kXchgBwdPerCu : xchg_fwd_per_cu(dtype);

@@ -22,7 +22,8 @@ TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 
 TUNE_SPLIT_EXCHANGE, TUNE_EXCHANGE_POLLS, TUNE_EXCHANGE_WITHHOLD = 8, 9, 10
 N_TUNE_KEYS = 11
 
-OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = 0, 1, 2, 3, 4
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_EXCHANGE = 0, 1, 2, 3, 4, 5
+SIZE_MAX = (1 << 64) - 1
 
 KINDS = {"layernorm": LAYERNORM, "rmsnorm": RMSNORM}
 DTYPES = {torch.float32: F32, torch.bfloat16: BF16, torch.float16: F16}
@@ -41,7 +42,8 @@ def dtype_code(act, weight=None):
     raise ValueError("unsupported dtype pair: activations %s, weights %s" % (act, weight))
 
 SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fwd_ex",
-           "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats", "norm_workspace_size", "norm_plan",
+           "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats", "norm_workspace_size",
+           "norm_workspace_bytes", "norm_workspace_status", "norm_plan",
            "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version",
            "norm_fold_projection", "norm_lazy_linear")
 
@@ -95,6 +97,9 @@ def lib():
         L.norm_stats.argtypes = [i32, vp, vp, f32, i64, i64, i32, vp, vp, vp, vp, sz, ld, vp]
         L.norm_workspace_size.argtypes = [i32, i32, i32, i64, i64, i32,
                                           ctypes.POINTER(ctypes.c_size_t)]
+        L.norm_workspace_bytes.argtypes = [i32, i32, i64, i64, i32, i32]
+        L.norm_workspace_bytes.restype = sz
+        L.norm_workspace_status.argtypes = [vp, sz, vp]
         L.norm_plan.argtypes = [i32, i32, i32, i64, i64, i32, i32, i32, ctypes.POINTER(_Plan)]
         L.norm_set_tuning.argtypes = [i32, i64]
         L.norm_set_launch_events.argtypes = [vp, vp]
@@ -107,7 +112,8 @@ def lib():
                                        vp, vp, vp, vp, i64, vp]
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
                      "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats",
-                     "norm_workspace_size", "norm_plan", "norm_set_tuning",
+                     "norm_workspace_size", "norm_workspace_status", "norm_plan",
+                     "norm_set_tuning",
                      "norm_set_launch_events", "norm_fold_projection", "norm_lazy_linear"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
@@ -315,6 +321,20 @@ def norm_workspace_size(kind, dtype, pass_, M, N, residual=False):
                                    ctypes.byref(out))
     _raise(st, "norm_workspace_size")
     return out.value
+
+
+def norm_workspace_bytes(kind, pass_, M, N, dtype, residual=False):
+    """Workspace bytes enough for a call on any gfx950 device (host only, no GPU needed);
+    SIZE_MAX for arguments no call accepts."""
+    dt = dtype_code(dtype) if isinstance(dtype, torch.dtype) else int(dtype)
+    return lib().norm_workspace_bytes(_kind(kind), int(pass_), M, N, dt, int(bool(residual)))
+
+
+def norm_workspace_status(workspace, stream=None):
+    """Synchronise `stream`, read and clear the workspace's exchange-failure word: OK, or
+    ERR_EXCHANGE if a call on it gave up a wait (and wrote NaN) since the last query."""
+    wp, wb = _ws(workspace)
+    return lib().norm_workspace_status(wp, wb, _stream(stream))
 
 
 def norm_plan(kind, dtype, pass_, M, N, residual=False, align=16, cu_count=256):

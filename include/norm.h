@@ -83,7 +83,9 @@ typedef enum {
   NORM_ERR_INVALID_ARG = 1, /* a pointer, size, eps, kind or dtype is not acceptable */
   NORM_ERR_UNSUPPORTED = 2, /* valid request outside what the kernels handle */
   NORM_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than norm_workspace_size() */
-  NORM_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+  NORM_ERR_HIP = 4,         /* a HIP runtime call or kernel launch failed */
+  NORM_ERR_EXCHANGE = 5     /* norm_workspace_status only: a call on this workspace gave up
+                               waiting for the partial sums of a long row and wrote NaN */
 } norm_status_t;
 
 /* Which pass a workspace size or plan is asked for. */
@@ -132,9 +134,12 @@ typedef void *norm_stream_t; /* a hipStream_t */
  *          overlap in time.
  * Returns NORM_OK once the kernels are queued.
  * Very long rows (the split scheme's single-pass form) are spread over workgroups that wait
- * for each other's partial sums; the wait is bounded (NORM_TUNE_EXCHANGE_POLLS) and a wait that
- * gives up writes NaN into the call's outputs for the rows it could not finish, never hangs.
- * It can only give up if the device does not keep the call's workgroups resident.
+ * for each other's partial sums. The form assumes that every workgroup of a row group gets a
+ * compute unit while the others wait: the grid is sized to fit the device at once, but neither
+ * HIP nor the hardware promises that workgroups are dispatched in order or that other work on
+ * the device leaves room. So the wait is bounded (NORM_TUNE_EXCHANGE_POLLS): a wait that gives
+ * up writes NaN into the call's outputs for the rows it could not finish and sets the
+ * workspace's exchange-failure word, which norm_workspace_status reports; it never hangs.
  */
 norm_status_t norm_fwd(norm_kind_t kind, const void *X, const void *R, const void *W,
                        const void *B, float eps, int64_t M, int64_t N, norm_dtype_t dtype,
@@ -228,12 +233,49 @@ norm_status_t norm_bwd_reduce(norm_kind_t kind, int64_t M, int64_t N, norm_dtype
                               norm_stream_t stream);
 
 /*
+ * Workspace layout. A call that needs a workspace uses its first 256 bytes as a header of
+ * 64-bit words: 0 a magic value, 1 the number of column-partial rows and 2 N (all three written
+ * by the backward's fused pass for its column reduction), 3 the exchange-failure word (below).
+ * The rest holds fp32 partial sums and, for very long rows, the exchange words of the split
+ * scheme's single pass, which carry a tag of the call that wrote them (words of earlier calls,
+ * or memory the workspace held before, never pass for this call's). The workspace's contents
+ * need no initialisation and are not meaningful to the caller.
+ *
+ * Workspace bytes for a call, host only (no device needed) [P1 paras. 9-10: the workspace of
+ * per-block partial sums of the split reduction]: the largest size the dispatcher's plan for
+ * (kind, pass, M, N, dtype, residual) takes on any gfx950 device (1 to 256 compute units, the
+ * plan's grid depends on the count) and any pointer alignment, under the current tuning
+ * overrides. pass: NORM_PASS_FWD, NORM_PASS_BWD or NORM_PASS_STATS; residual: nonzero when R is
+ * given. A workspace of this size, 256-byte aligned, is enough for the call on any gfx950
+ * device. Returns SIZE_MAX for arguments no call accepts (kind, dtype or pass unknown, M < 0,
+ * N <= 0, N >= 2^31) or a shape no kernel handles. It evaluates the plan for every compute-unit
+ * count (about 0.1 ms on the host): size the workspace once per shape.
+ */
+size_t norm_workspace_bytes(norm_kind_t kind, int pass, int64_t M, int64_t N,
+                            norm_dtype_t dtype, int residual);
+
+/*
  * Workspace bytes a call needs on the CURRENT device (the size depends on its compute-unit
- * count). pass: NORM_PASS_FWD or NORM_PASS_BWD; residual: nonzero when R is given.
- * Writes the size to *bytes. Returns NORM_ERR_HIP if no device can be queried.
+ * count), at most norm_workspace_bytes(). pass: NORM_PASS_FWD or NORM_PASS_BWD; residual:
+ * nonzero when R is given. Writes the size to *bytes. Returns NORM_ERR_HIP if no device can be
+ * queried.
  */
 norm_status_t norm_workspace_size(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass,
                                   int64_t M, int64_t N, int residual, size_t *bytes);
+
+/*
+ * Whether a call on this workspace gave up an exchange wait ([P1] para. 9's workspace reduction,
+ * spread over workgroups that wait for each other's partial sums; see norm_fwd). A wait that
+ * gives up writes NaN into its rows' outputs and sets the header's exchange-failure word; this
+ * query waits for `stream` to finish (it synchronises the host), reads that word, clears it and
+ * returns NORM_ERR_EXCHANGE if it was set, else NORM_OK. The word stays set until queried, so one
+ * query covers every call on the workspace since the previous query. workspace_bytes below the
+ * 256-byte header (including 0) returns NORM_OK: such a workspace belongs to no call that waits.
+ * NORM_ERR_WORKSPACE for a NULL or unaligned workspace of 256 bytes or more, NORM_ERR_HIP if a
+ * copy or the synchronisation fails. Not for use inside a captured HIP graph.
+ */
+norm_status_t norm_workspace_status(void *workspace, size_t workspace_bytes,
+                                    norm_stream_t stream);
 
 /* Description of the launch plan for a shape, for tests and tuning. */
 typedef struct {

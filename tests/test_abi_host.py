@@ -52,7 +52,7 @@ def test_header_compiles_as_c():
 
 
 def test_status_strings():
-    for s in range(5):
+    for s in range(6):
         assert nl.status_string(s).startswith("NORM_")
     assert "unknown" in nl.status_string(99)
     assert nl.norm_version() >= 100
@@ -379,6 +379,54 @@ def test_split_exchange_plan():
     finally:
         for k in range(nl.N_TUNE_KEYS):
             nl.norm_set_tuning(k, -1)
+
+
+@pytest.mark.parametrize("kind", [0, 1])
+@pytest.mark.parametrize("pass_", [0, 1, 2])
+@pytest.mark.parametrize("M,N", [(1, 1), (3, 1000), (2048, 1024), (16384, 4096), (16384, 4100),
+                                 (32768, 8192), (65536, 7168), (16384, 16384), (256, 262144),
+                                 (4, 4194304), (2, 8192 * 513), (1000, 65536)])
+def test_workspace_bytes_on_the_host(kind, pass_, M, N):
+    """norm_workspace_bytes needs no device and covers the plan of every compute-unit count
+    (1 .. 256) and every pointer alignment."""
+    for dt in (BF, F, nl.BF16_F32W):
+        for res in ((0, 1) if (kind == 1 and pass_ != 1) else (0,)):
+            code = nl.dtype_code(dt) if isinstance(dt, torch.dtype) else dt
+            b = nl.lib().norm_workspace_bytes(kind, pass_, M, N, code, res)
+            assert b == nl.norm_workspace_bytes(kind, pass_, M, N, dt, bool(res))
+            assert b != nl.SIZE_MAX
+            most = 0
+            for cu in (1, 2, 3, 7, 32, 64, 80, 128, 200, 255, 256):
+                for align in (16, 8, 4, 2, 1):
+                    p = nl.norm_plan(kind, dt, pass_, M, N, residual=bool(res), align=align,
+                                     cu_count=cu)
+                    most = max(most, p["workspace_bytes"])
+            assert b >= most
+            # a workspace is either none at all or starts with the 256-byte header
+            assert b == 0 or b >= 256
+            if pass_ == 1:
+                assert b >= 256 + 2 * N * 4
+            assert b % 256 == 0
+
+
+def test_workspace_bytes_rejects():
+    L = nl.lib()
+    B16 = nl.BF16
+    for args in ((0, 0, -1, 16, B16, 0), (0, 0, 4, 0, B16, 0), (0, 0, 4, -5, B16, 0),
+                 (7, 0, 4, 16, B16, 0), (0, 7, 4, 16, B16, 0), (0, 0, 4, 16, 9, 0),
+                 (0, 1, 4, 1 << 31, B16, 0)):
+        assert L.norm_workspace_bytes(*args) == nl.SIZE_MAX, args
+    # M == 0 is a valid (empty) call
+    assert L.norm_workspace_bytes(0, 1, 0, 4096, B16, 0) != nl.SIZE_MAX
+
+
+def test_workspace_status_host_checks():
+    """Arguments the status query rejects (or answers) without touching a device."""
+    L = nl.lib()
+    assert L.norm_workspace_status(None, 0, None) == nl.OK      # no workspace: nothing waited
+    assert L.norm_workspace_status(None, 255, None) == nl.OK
+    assert L.norm_workspace_status(None, 256, None) == nl.ERR_WORKSPACE
+    assert L.norm_workspace_status(FAKE + 4, 4096, None) == nl.ERR_WORKSPACE  # unaligned
 
 
 def test_workspace_needs_a_device_here():

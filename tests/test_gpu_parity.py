@@ -214,28 +214,110 @@ def test_split_exchange_chunk_limits(kind):
 def test_split_exchange_wait_is_bounded():
     """The exchange's wait gives up rather than hangs: with chunk 0 withholding its partials
     (a test-only flag) and a poll limit of 8, every row of the call comes out NaN, the kernels
-    finish, and the next call without the flag is correct again."""
+    finish, the workspace reports the failure (once: the query clears it), and the next call on
+    the same workspaces without the flag is correct again and reports nothing."""
     M, N = 64, 65536
     for kind in ("layernorm", "rmsnorm"):
         _say("split exchange bounded wait %s %dx%d" % (kind, M, N))
         w = _small(kind, "bf16", M, N, seed=9)
         t = inputs.make(w)
         X, W, B, dY = (t[k].cuda() if t[k] is not None else None for k in ("X", "W", "B", "dY"))
+        ln = kind == "layernorm"
+        wsf = nl.workspace(kind, X.dtype, nl.PASS_FWD, M, N)
+        wsb = nl.workspace(kind, X.dtype, nl.PASS_BWD, M, N)
+
+        def fwd():
+            Y = torch.empty_like(X)
+            mean = torch.empty(M, device="cuda") if ln else None
+            rstd = torch.empty(M, device="cuda")
+            nl.norm_fwd(kind, X, None, W, B, w.eps, Y, None, mean, rstd, wsf)
+            return Y, mean, rstd
+
+        def bwd(mean, rstd):
+            dX, dW = torch.empty_like(X), torch.empty_like(W)
+            dB = torch.empty_like(W) if ln else None
+            nl.norm_bwd(kind, X, dY, None, W, mean, rstd, w.eps, dX, None, dW, dB, wsb)
+            return dX, dW, dB
+
         with tuned(exchange=1):
-            Y0, _, mean0, rstd0 = nl.forward(kind, X, W, B, w.eps)
+            Y0, mean0, rstd0 = fwd()
+            dX0, dW0, _ = bwd(mean0, rstd0)
             assert _split_form(kind, "bf16", nl.PASS_FWD, M, N) > 0
+            assert _split_form(kind, "bf16", nl.PASS_BWD, M, N) > 0
+        assert nl.norm_workspace_status(wsf) == nl.OK
+        assert nl.norm_workspace_status(wsb) == nl.OK
         with tuned(exchange=1, polls=8, withhold=1):
-            Y, _, _, rstd = nl.forward(kind, X, W, B, w.eps)
-            dX, dW, dB = nl.backward(kind, X, dY, W, mean0, rstd0, w.eps)
+            Y, _, rstd = fwd()
+            dX, dW, dB = bwd(mean0, rstd0)
             torch.cuda.synchronize()
         assert torch.isnan(Y.float()).all() and torch.isnan(rstd).all()
         assert torch.isnan(dX.float()).all() and torch.isnan(dW.float()).all()
+        assert nl.norm_workspace_status(wsf) == nl.ERR_EXCHANGE
+        assert nl.norm_workspace_status(wsf) == nl.OK  # the query cleared it
+        assert nl.norm_workspace_status(wsb) == nl.ERR_EXCHANGE
+        assert nl.norm_workspace_status(wsb) == nl.OK
         with tuned(exchange=1):
-            Y2, _, _, rstd2 = nl.forward(kind, X, W, B, w.eps)
+            Y2, _, rstd2 = fwd()
+            dX2, dW2, _ = bwd(mean0, rstd0)
             torch.cuda.synchronize()
         assert torch.equal(Y2.view(torch.int16), Y0.view(torch.int16))
         assert torch.equal(rstd2, rstd0)
+        assert torch.equal(dX2.view(torch.int16), dX0.view(torch.int16))
+        assert torch.equal(dW2.view(torch.int16), dW0.view(torch.int16))
+        assert nl.norm_workspace_status(wsf) == nl.OK
+        assert nl.norm_workspace_status(wsb) == nl.OK
         run_and_check(w)
+
+
+def test_split_exchange_needs_no_clean_workspace():
+    """The exchange words carry a tag of the call that wrote them, so no call needs its words
+    cleared first: a workspace full of random bits, one last used by a call of another shape
+    (whose words then sit where this call's go), and one reused call after call all give the
+    bits of a fresh workspace, and match the oracle."""
+    for kind in ("layernorm", "rmsnorm"):
+        for M, N in ((64, 65536), (3, 262144)):
+            _say("split exchange stale words %s %dx%d" % (kind, M, N))
+            w = _small(kind, "bf16", M, N, seed=M + N)
+            t = inputs.make(w)
+            X, W, B, dY = (t[k].cuda() if t[k] is not None else None
+                           for k in ("X", "W", "B", "dY"))
+            ln = kind == "layernorm"
+            nf = nl.norm_workspace_size(kind, X.dtype, nl.PASS_FWD, M, N)
+            nb = nl.norm_workspace_size(kind, X.dtype, nl.PASS_BWD, M, N)
+            big = max(nf, nb, nl.norm_workspace_size(kind, X.dtype, nl.PASS_BWD, 2 * M, N))
+
+            def run(ws):
+                Y = torch.empty_like(X)
+                mean = torch.empty(M, device="cuda") if ln else None
+                rstd = torch.empty(M, device="cuda")
+                nl.norm_fwd(kind, X, None, W, B, w.eps, Y, None, mean, rstd, ws[:nf])
+                dX, dW = torch.empty_like(X), torch.empty_like(W)
+                dB = torch.empty_like(W) if ln else None
+                nl.norm_bwd(kind, X, dY, None, W, mean, rstd, w.eps, dX, None, dW, dB, ws[:nb])
+                torch.cuda.synchronize()
+                return [v.view(torch.int16) if v.dtype == torch.bfloat16 else v
+                        for v in (Y, rstd, dX, dW, dB) if v is not None]
+
+            with tuned(exchange=1):
+                assert _split_form(kind, "bf16", nl.PASS_FWD, M, N) > 0
+                ref = run(torch.zeros(big, dtype=torch.uint8, device="cuda"))
+                g = torch.Generator(device="cuda").manual_seed(M + N)
+                noise = torch.randint(0, 256, (big,), dtype=torch.uint8, device="cuda",
+                                      generator=g)
+                for got in (run(noise), run(noise), run(noise)):
+                    assert all(torch.equal(a, b) for a, b in zip(got, ref))
+                # words of a call with twice the rows (another layout) left in the workspace
+                other = torch.zeros(big, dtype=torch.uint8, device="cuda")
+                X2 = torch.cat([X, X])
+                Y2 = torch.empty_like(X2)
+                nl.norm_bwd(kind, X2, torch.cat([dY, dY]), None, W,
+                            torch.zeros(2 * M, device="cuda") if ln else None,
+                            torch.ones(2 * M, device="cuda"), w.eps, Y2, None,
+                            torch.empty_like(W), torch.empty_like(W) if ln else None, other)
+                assert all(torch.equal(a, b) for a, b in zip(run(other), ref))
+                assert nl.norm_workspace_status(noise[:nf]) == nl.OK
+                assert nl.norm_workspace_status(other[:nb]) == nl.OK
+            run_and_check(w)
 
 
 # ---- bf16 activations with fp32 weight, bias, dW, dB --------------------------------------------
