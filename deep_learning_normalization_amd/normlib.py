@@ -377,7 +377,9 @@ class KernelTimer:
             h.hipEventDestroy.argtypes = [ctypes.c_void_p]
             h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
                                               ctypes.c_void_p]
-            for f in ("hipEventCreateWithFlags", "hipEventDestroy", "hipEventElapsedTime"):
+            h.hipGetLastError.argtypes = []
+            for f in ("hipEventCreateWithFlags", "hipEventDestroy", "hipEventElapsedTime",
+                      "hipGetLastError"):
                 getattr(h, f).restype = ctypes.c_int
             cls._hip = h
         return cls._hip
@@ -395,6 +397,9 @@ class KernelTimer:
     def elapsed_ms(self):
         ms = ctypes.c_float()
         if self._hip.hipEventElapsedTime(ctypes.byref(ms), self.start, self.stop) != 0:
+            # the failed call also left the runtime's per-thread last error set; consume it so
+            # that the next error check (torch's, after its own kernel launches) does not see it
+            self._hip.hipGetLastError()
             raise RuntimeError("hipEventElapsedTime failed (events not recorded?)")
         return ms.value
 

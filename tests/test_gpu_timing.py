@@ -59,3 +59,7 @@ def test_failing_call_disarms():
     torch.cuda.synchronize()
     with pytest.raises(RuntimeError):
         t.elapsed_ms()                                            # never recorded
+    # and that failed query leaves no error behind for the next kernel launch's check
+    z = torch.zeros(1024, device="cuda")
+    assert torch.equal(z + 1, torch.ones_like(z))
+    torch.cuda.synchronize()
