@@ -20,7 +20,7 @@ ARCH = os.environ.get("DLN_OFFLOAD_ARCH", "gfx950")
 SOURCES = [
     "norm_team.hip", "norm_team_f32.hip", "norm_team_bf16.hip", "norm_team_bf16w.hip",
     "norm_team_f16.hip", "norm_team_f16w.hip", "norm_looped.hip", "norm_split.hip",
-    "norm_xsplit.hip",
+    "norm_xsplit.hip", "norm_noalloc.hip",
     "norm_lazy.hip", "norm_lazy_check.cpp",
     "norm_abi.cpp", "norm_plan.cpp",
 ]

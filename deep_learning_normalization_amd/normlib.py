@@ -45,7 +45,7 @@ SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fw
            "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats", "norm_workspace_size",
            "norm_workspace_bytes", "norm_workspace_status", "norm_plan",
            "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version",
-           "norm_fold_projection", "norm_lazy_linear")
+           "norm_fold_projection", "norm_lazy_linear", "norm_bwd_noalloc")
 
 
 class NormError(RuntimeError):
@@ -90,6 +90,8 @@ def lib():
         L.norm_bwd_fused.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp,
                                      vp, sz, vp]
         L.norm_bwd_reduce.argtypes = [i32, i64, i64, i32, vp, vp, vp, sz, vp]
+        L.norm_bwd_noalloc.argtypes = [i32, vp, vp, vp, vp, vp, vp, f32, i64, i64, i32, vp, vp,
+                                       vp, vp, vp]
         ld = ctypes.POINTER(RowStrides)
         L.norm_fwd_ex.argtypes = L.norm_fwd.argtypes[:-1] + [ld, vp]
         L.norm_bwd_ex.argtypes = L.norm_bwd.argtypes[:-1] + [ld, vp]
@@ -114,7 +116,8 @@ def lib():
                      "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats",
                      "norm_workspace_size", "norm_workspace_status", "norm_plan",
                      "norm_set_tuning",
-                     "norm_set_launch_events", "norm_fold_projection", "norm_lazy_linear"):
+                     "norm_set_launch_events", "norm_fold_projection", "norm_lazy_linear",
+                     "norm_bwd_noalloc"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
         _lib = L
@@ -282,6 +285,25 @@ def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, str
                            _ptr(dW), _ptr(dB), wp, wb,
                            _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR), _stream(stream))
     _raise(st, "norm_bwd")
+
+
+def norm_bwd_noalloc(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, stream=None):
+    """Queue the backward with the library's own device scratch as its workspace (no
+    allocation anywhere). Contiguous [M, N] tensors only."""
+    M, N = X.shape
+    dt, wdt = X.dtype, W.dtype
+    for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
+        _check_mat(t, M, N, dt, nm)
+        if t is not None and not t.is_contiguous():
+            raise ValueError("%s must be contiguous" % nm)
+    for t, nm in ((W, "W"), (dW, "dW"), (dB, "dB")):
+        _check_vec(t, N, wdt, nm)
+    _check_vec(mean, M, torch.float32, "mean")
+    _check_vec(rstd, M, torch.float32, "rstd")
+    st = lib().norm_bwd_noalloc(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
+                                _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX),
+                                _ptr(dR), _ptr(dW), _ptr(dB), _stream(stream))
+    _raise(st, "norm_bwd_noalloc")
 
 
 def norm_bwd_fused(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, workspace, stream=None):

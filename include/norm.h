@@ -170,6 +170,24 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
                        void *dB, void *workspace, size_t workspace_bytes, norm_stream_t stream);
 
 /*
+ * norm_bwd without a caller workspace, for callers that cannot allocate device memory (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid allocation). Arguments,
+ * results and errors are those of norm_bwd; the workspace is the library's own device array of
+ * 64 MiB per device (zero-initialised data of the code object, held by every device the library
+ * runs on until the process ends), so the call allocates nothing and makes no allocating call.
+ * A shape whose backward needs more than 64 MiB of workspace on the current device (see
+ * norm_workspace_size) returns NORM_ERR_WORKSPACE and launches nothing. Every call on a device
+ * shares that array: calls that overlap in time on one device (different streams, or threads
+ * without ordering between their calls) race on it and must be serialised by the caller. An
+ * exchange wait that gives up writes NaN as for norm_bwd; its failure word stays in the array,
+ * which norm_workspace_status cannot read.
+ */
+norm_status_t norm_bwd_noalloc(norm_kind_t kind, const void *X, const void *dY, const void *dH,
+                               const void *W, const float *mean, const float *rstd, float eps,
+                               int64_t M, int64_t N, norm_dtype_t dtype, void *dX, void *dR,
+                               void *dW, void *dB, norm_stream_t stream);
+
+/*
  * Row strides for the _ex variants below: the number of elements between the starts of
  * consecutive rows of each [M, N] tensor, so a tensor may be a row-strided view (for example
  * the query rows inside a fused query/key/value buffer). 0 means N (contiguous rows); any other

@@ -1,0 +1,102 @@
+"""norm_bwd_noalloc (the backward with the library's own device scratch as its workspace)
+against norm_bwd with a caller workspace, through the C ABI: two calls in a row on each scheme,
+the second with fewer rows, must give the bits norm_bwd gives (the same kernels and plan on the
+same inputs), which match the oracle; a shape that needs more scratch than the array holds is
+refused before anything is launched."""
+import dataclasses
+
+import pytest
+import torch
+
+from deep_learning_normalization_amd import inputs, normlib as nl
+from tests.parity import run_and_check
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print("[gpu] " + msg, flush=True)
+
+
+def _bits(t):
+    return t.view(torch.int16) if t.dtype in (torch.bfloat16, torch.float16) else t
+
+
+def _workload(kind, dtype, M, N, seed):
+    eps = 1e-5 if kind == "layernorm" else 1e-6
+    return inputs.Workload("noalloc_%s_%s_%dx%d" % (kind, dtype, M, N), kind, dtype, M, N, eps,
+                           x=inputs.normal(0.2, 1.0), w=inputs.normal(1, 0.1),
+                           b=inputs.normal(0, 0.1) if kind == "layernorm" else None,
+                           dy=inputs.normal(0, 1), seed=seed)
+
+
+def _both(w, dh=False):
+    """norm_bwd_noalloc and norm_bwd on the same inputs; returns both results."""
+    if dh:
+        w = dataclasses.replace(w, dh=inputs.normal(0, 0.5))
+    t = inputs.make(w)
+    X, W, B, dY = (t[k].cuda() if t[k] is not None else None for k in ("X", "W", "B", "dY"))
+    dH = t["dH"].cuda() if t["dH"] is not None else None
+    Y, _, mean, rstd = nl.forward(w.kind, X, W, B, w.eps)
+    ln = w.kind == "layernorm"
+    out = []
+    for noalloc in (True, False):
+        dX, dW = torch.empty_like(X), torch.empty_like(W)
+        dB = torch.empty_like(W) if ln else None
+        if noalloc:
+            nl.norm_bwd_noalloc(w.kind, X, dY, dH, W, mean, rstd, w.eps, dX, None, dW, dB)
+        else:
+            ws = nl.workspace(w.kind, X.dtype, nl.PASS_BWD, w.M, w.N)
+            nl.norm_bwd(w.kind, X, dY, dH, W, mean, rstd, w.eps, dX, None, dW, dB, ws)
+        out.append([v for v in (dX, dW, dB) if v is not None])
+    torch.cuda.synchronize()
+    return out
+
+
+# (first call, second call with fewer rows): block, wave, looped and split (exchange) schemes
+CASES = [
+    (("layernorm", "bf16", 16384, 4096), ("layernorm", "bf16", 1000, 4096)),
+    (("rmsnorm", "bf16", 4096, 1024), ("rmsnorm", "bf16", 77, 1024)),
+    (("rmsnorm", "bf16", 2048, 16384), ("layernorm", "bf16", 300, 12288)),
+    (("layernorm", "bf16", 256, 262144), ("rmsnorm", "bf16", 64, 65536)),
+    (("layernorm", "f32", 1024, 5000), ("layernorm", "f32", 3, 5000)),
+]
+
+
+@pytest.mark.parametrize("first,second", CASES, ids=lambda c: "%s_%s_%dx%d" % c)
+def test_noalloc_matches_norm_bwd(first, second):
+    for i, shape in enumerate((first, second)):
+        w = _workload(*shape, seed=11 + i)
+        _say("noalloc call %d: %s" % (i + 1, w.name))
+        a, b = _both(w)
+        for x, y in zip(a, b):
+            assert torch.equal(_bits(x), _bits(y)), w.name
+    # and the second shape against the oracle, every row
+    run_and_check(_workload(*second, seed=12))
+
+
+def test_noalloc_with_incoming_gradient():
+    w = _workload("rmsnorm", "bf16", 512, 7168, seed=5)
+    _say("noalloc with dH: %s" % w.name)
+    a, b = _both(w, dh=True)
+    for x, y in zip(a, b):
+        assert torch.equal(_bits(x), _bits(y))
+
+
+def test_noalloc_refuses_oversized_shapes():
+    """A long-row backward whose row partials alone exceed the 64 MiB array (200000 rows x 32
+    chunks x 16 bytes = 102 MB) is refused with NORM_ERR_WORKSPACE after the host checks, before
+    any launch: the pointers below are never dereferenced (widely spaced fake addresses that the
+    argument checks accept as disjoint)."""
+    M, N = 200000, 262144
+    assert nl.norm_workspace_size("layernorm", torch.bfloat16, nl.PASS_BWD, M, N) > (64 << 20)
+    base = 1 << 44
+    X, dY, W, mean, rstd, dX, dW, dB = (base * (i + 1) for i in range(8))
+    st = nl.lib().norm_bwd_noalloc(nl.LAYERNORM, X, dY, None, W, mean, rstd, 1e-5, M, N, nl.BF16,
+                                   dX, None, dW, dB, None)
+    assert st == nl.ERR_WORKSPACE
+    # and an argument error is still an argument error
+    st = nl.lib().norm_bwd_noalloc(nl.LAYERNORM, X, dY, None, None, mean, rstd, 1e-5, M, N,
+                                   nl.BF16, dX, None, dW, dB, None)
+    assert st == nl.ERR_INVALID_ARG
+    torch.cuda.synchronize()
