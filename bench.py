@@ -4,18 +4,24 @@
 Headline workload: LayerNorm forward + backward, bf16 storage with fp32 arithmetic,
 M = 16384 rows x N = 4096, X ~ N(0,1), dY ~ N(0,1), gamma ~ N(1,0.1), beta ~ N(0,0.1),
 eps = 1e-5, synthetic seeded data. One step = norm_fwd on one buffer set, then the backward
-(norm_bwd_fused + norm_bwd_reduce, which is exactly what norm_bwd runs) on another set. Sets
-rotate over more than 1 GiB, so every pass starts with its inputs in HBM, not in the 256 MB
-memory-side cache, and the backward never finds what the forward just touched.
+(norm_bwd_fused + norm_bwd_reduce, which is exactly what norm_bwd runs) on another set.
 
-Printed (rank 0, one JSON line): achieved HBM GB/s of forward + backward (algorithmic bytes /
-measured time), with the forward and backward figures, a roofline entry for the dominant
-kernel (the fused backward pass: on every launch inside the timed region, HIP events take the
-kernel's own start and end timestamps) and the CPU oracle timed on this host as a reported
-baseline.
+Cache-cold protocol (deep_learning_normalization_amd/timing.py): every timed loop (step,
+forward only, backward only) cycles through buffer sets sized from that loop's own bytes per
+call, so that a set is used again only after at least 1 GiB (four times the 256 MB memory-side
+cache) of the loop's traffic, and the step's forward never reads what the backward before it
+touched.
 
---sweep also measures every workload shape (forward, backward, both) and writes the table to
-stderr and to --sweep-out.
+Printed (one JSON line): achieved HBM GB/s of forward + backward (algorithmic bytes / measured
+time) as `value`; the forward and backward figures; a roofline entry for the dominant kernel (the
+fused backward pass: on every launch inside the timed region, HIP events take the kernel's own
+start and end timestamps); `ceilings`, what hand-written streaming kernels (include/hbm_probe.h)
+reach for each stream mix in the same run; `shapes`, the same figures for every other workload
+the metric is quoted on (fractions of the 8 TB/s peak and of the measured ceiling of each pass's
+stream mix); and the CPU oracle timed on this host as a reported baseline.
+
+--sweep also times the registry's other workloads (ragged row, hidden 16384, fp16, fp32
+weights) into `shapes`.
 
 --projection instead measures the norm deferred into a following projection (norm_lazy_linear
 after norm_fold_projection) on its two workloads, next to the unfused pair (norm_fwd, then
@@ -51,135 +57,6 @@ def load_traffic(workload_name):
     return d, None
 
 
-class BufferSet:
-    """One set of device tensors for a workload (inputs copied from host, outputs empty)."""
-
-    def __init__(self, host, dev, torch):
-        self.t = {k: (v.to(dev) if v is not None else None) for k, v in host.items()}
-        X = self.t["X"]
-        M = X.shape[0]
-        self.Y = torch.empty_like(X)
-        self.H = torch.empty_like(X) if self.t["R"] is not None else None
-        self.mean = torch.empty(M, dtype=torch.float32, device=dev)
-        self.rstd = torch.empty(M, dtype=torch.float32, device=dev)
-        self.dX = torch.empty_like(X)
-
-
-def set_bytes(host):
-    n = sum(v.numel() * v.element_size() for v in host.values() if v is not None and v.dim() == 2)
-    X = host["X"]
-    outs = 2 if host["dY"] is not None else 1
-    if host["R"] is not None:
-        outs += 1
-    return n + outs * X.numel() * X.element_size()
-
-
-def timed_workload(w, steps, warmup, torch, nl, min_footprint=1 << 30, max_sets=64,
-                   two_stage=True):
-    """Cold-cache timing of one workload. Buffer sets rotate over more than min_footprint
-    bytes; the backward of a step uses a different set than its forward. Three loops:
-      step : forward, then the backward. two_stage: norm_bwd_fused (its kernels' own
-             timestamps recorded into HIP events on every launch, norm_set_launch_events)
-             followed by norm_bwd_reduce, which is what norm_bwd runs for the wave and block
-             schemes; else norm_bwd, timed the same way as a whole;
-      fwd  : forward only;   bwd : norm_bwd only.
-    Each loop is bracketed by a synchronize and a pair of events on the launch stream."""
-    from deep_learning_normalization_amd import inputs
-    dev = torch.device("cuda:0")
-    host = inputs.make(w)
-    sb = set_bytes(host)
-    S = max(2, min(max_sets, -(-min_footprint // sb)))
-    if S % 2:
-        S += 1
-    sets = [BufferSet(host, dev, torch) for _ in range(S)]
-    shared = sets[0].t
-    W, B = shared["W"], shared["B"]
-    M, N = w.M, w.N
-    kind = w.kind
-    eps = w.eps
-    want_bwd = w.dy is not None
-    wsf = nl.workspace(kind, host["X"].dtype, nl.PASS_FWD, M, N, w.r is not None)
-    wsb = nl.workspace(kind, host["X"].dtype, nl.PASS_BWD, M, N) if want_bwd else None
-    dW = torch.empty_like(W)
-    dB = torch.empty_like(W) if kind == "layernorm" else None
-    stream = torch.cuda.current_stream()
-
-    def fwd(s):
-        nl.norm_fwd(kind, s.t["X"], s.t["R"], W, B, eps, s.Y, s.H,
-                    s.mean if kind == "layernorm" else None, s.rstd, wsf)
-
-    def bwd_fused(s):
-        Xin = s.H if s.H is not None else s.t["X"]
-        nl.norm_bwd_fused(kind, Xin, s.t["dY"], None, W,
-                          s.mean if kind == "layernorm" else None, s.rstd, eps, s.dX, None, wsb)
-
-    def bwd_reduce():
-        nl.norm_bwd_reduce(kind, M, N, dW, dB, wsb)
-
-    def bwd_whole(s):
-        Xin = s.H if s.H is not None else s.t["X"]
-        nl.norm_bwd(kind, Xin, s.t["dY"], None, W, s.mean if kind == "layernorm" else None,
-                    s.rstd, eps, s.dX, None, dW, dB, wsb)
-
-    for s in sets:  # every set gets its statistics (and H) before the backward reads them
-        fwd(s)
-    ev = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
-
-    def run(body, n, timed_kernels=False):
-        for i in range(warmup):
-            body(i, None)
-        torch.cuda.synchronize()
-        marks = [nl.KernelTimer() for _ in range(n)] if timed_kernels else [None] * n
-        start, end = ev(), ev()
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        start.record(stream)
-        for i in range(n):
-            body(i, marks[i])
-        end.record(stream)
-        torch.cuda.synchronize()
-        wall = time.perf_counter() - t0
-        return start.elapsed_time(end) / n, wall, marks
-
-    out = {"sets": S, "set_bytes": sb}
-
-    def step(i, timer):
-        fwd(sets[i % S])
-        if want_bwd:
-            if timer:
-                timer.arm()  # the kernels' own start/end timestamps, no extra packets
-            if two_stage:
-                bwd_fused(sets[(i + S // 2) % S])
-                bwd_reduce()
-            else:
-                bwd_whole(sets[(i + S // 2) % S])
-
-    # the GPU clock settles within a few hundred ms of load: run steps for >= 0.3 s first
-    t_end = time.perf_counter() + 0.3
-    i = 0
-    while time.perf_counter() < t_end or i < warmup:
-        step(i, None)
-        i += 1
-        if i % 50 == 0:
-            torch.cuda.synchronize()
-    ms, wall, marks = run(step, steps, timed_kernels=want_bwd)
-    out["ms_per_step"], out["wall_s"] = ms, wall
-    if want_bwd:
-        b = sorted(1e3 * m.elapsed_ms() for m in marks)
-        out["bwd_timed_us_mean"] = sum(b) / len(b)
-        out["bwd_timed_us_median"] = b[len(b) // 2]
-        out["bwd_timed_us_p10"] = b[len(b) // 10]
-        out["bwd_timed_us_p90"] = b[(9 * len(b)) // 10]
-    ms, _, _ = run(lambda i, mk: fwd(sets[i % S]), steps)
-    out["fwd_us"] = ms * 1e3
-    if want_bwd:
-        ms, _, _ = run(lambda i, mk: bwd_whole(sets[i % S]), steps)
-        out["bwd_us"] = ms * 1e3
-    del sets
-    torch.cuda.empty_cache()
-    return out
-
-
 def stats_only(w, torch, nl, steps, warmup):
     """The statistics pass alone (norm_stats) on the workload's X: mean (LayerNorm) and rstd,
     no Y. X sets rotate over more than 1 GiB so every pass starts from HBM. Returns the mean
@@ -187,7 +64,7 @@ def stats_only(w, torch, nl, steps, warmup):
     from deep_learning_normalization_amd import inputs
     X0 = inputs.make(w)["X"].cuda()
     M, N = w.M, w.N
-    nsets = max(2, -(-(1 << 30) // (X0.numel() * X0.element_size())))
+    nsets = max(4, -(-(1 << 30) // (X0.numel() * X0.element_size())))
     xs = [X0] + [X0.clone() for _ in range(nsets - 1)]
     ln = w.kind == "layernorm"
     mean = torch.empty(M, device="cuda") if ln else None
@@ -210,73 +87,47 @@ def stats_only(w, torch, nl, steps, warmup):
     return us, nbytes
 
 
-def graph_fwd_us(w, torch, nl, replays=10):
-    """Forward calls replayed from a captured graph: one forward per buffer set, the sets
-    rotating over more than 1 GiB so that every call starts from HBM as in the eager loops,
-    replayed `replays` times; microseconds per forward. For shapes bound by the launch rather
-    than by HBM."""
-    from deep_learning_normalization_amd import inputs
-    host = inputs.make(w)
-    ln = w.kind == "layernorm"
-    set_bytes = 2 * host["X"].numel() * host["X"].element_size()
-    calls = max(20, -(-(1 << 30) // set_bytes))
-    sets = []
-    for _ in range(calls):
-        X = host["X"].cuda()
-        sets.append((X, torch.empty_like(X), torch.empty(w.M, device="cuda") if ln else None,
-                     torch.empty(w.M, device="cuda")))
-    W = host["W"].cuda()
-    B = host["B"].cuda() if ln and host["B"] is not None else None
-    ws = nl.workspace(w.kind, sets[0][0].dtype, nl.PASS_FWD, w.M, w.N)
-
-    def body():
-        for i in range(calls):
-            X, Y, mean, rstd = sets[i]
-            nl.norm_fwd(w.kind, X, None, W, B, w.eps, Y, None, mean, rstd, ws)
-    body()
-    torch.cuda.synchronize()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g):
-        body()
-    g.replay()
-    torch.cuda.synchronize()
-    a = torch.cuda.Event(enable_timing=True)
-    b = torch.cuda.Event(enable_timing=True)
-    a.record()
-    for _ in range(replays):
-        g.replay()
-    b.record()
-    torch.cuda.synchronize()
-    us = a.elapsed_time(b) * 1e3 / (replays * calls)
-    del g, sets
-    torch.cuda.empty_cache()
-    return us
+def ceiling_for(w, ceilings):
+    """The measured ceilings (GB/s) for a workload's forward and backward stream mixes: the
+    forward reads one [M, N] stream and writes one (two and two with the residual input), the
+    backward reads two and writes one."""
+    f = ceilings["2r2w" if w.r is not None else "copy"]
+    return f, ceilings["triad"]
 
 
-def copy_ceiling(torch, nbytes=1 << 30, iters=20):
-    """Achievable HBM bandwidth of a plain device copy (torch's copy kernel), GB/s moved
-    (read + write). Two buffer pairs alternate so neither copy starts in cache."""
-    n = nbytes // 2
-    bufs = [(torch.empty(n, dtype=torch.bfloat16, device="cuda").normal_(),
-             torch.empty(n, dtype=torch.bfloat16, device="cuda")) for _ in range(2)]
-    for s, d in bufs:
-        d.copy_(s)
-    torch.cuda.synchronize()
-    times = []
-    for i in range(iters):
-        s, d = bufs[i % 2]
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        a.record()
-        d.copy_(s)
-        b.record()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b))
-    del bufs
-    torch.cuda.empty_cache()
-    times.sort()
-    med = times[len(times) // 2]
-    return 2 * nbytes / (med * 1e-3) / 1e9, med * 1e3
+def shape_entry(w, r, ceilings):
+    """One workload's figures from timing.timed_workload: loop time per call, achieved GB/s
+    over the algorithmic bytes, its fraction of the 8 TB/s peak and of the measured ceiling for
+    its stream mix, and the per-launch kernel durations."""
+    fc, bc = ceiling_for(w, ceilings)
+    fb, bb = r["fwd_bytes"], r["bwd_bytes"]
+    e = {"workload": w.name, "kind": w.kind, "dtype": w.dtype, "M": w.M, "N": w.N,
+         "residual": w.r is not None, "buffer_sets": r["sets"],
+         "footprint_GiB": round(r["footprint_bytes"] / (1 << 30), 2)}
+    fg = fb / (r["fwd_us"] * 1e-6) / 1e9
+    e["fwd"] = {"us": round(r["fwd_us"], 2), "GBps": round(fg, 1),
+                "frac_peak": round(fg / PEAK_HBM_GBPS, 4),
+                "frac_ceiling": round(fg / fc["GBps"], 4), "ceiling": fc["streams"],
+                "kernel_us_mean_p50": [round(r["fwd_kernels_us"]["mean"], 2),
+                                       round(r["fwd_kernels_us"]["p50"], 2)],
+                "rows_per_s": round(w.M / (r["fwd_us"] * 1e-6), 1), "bytes": fb}
+    if bb:
+        bg = bb / (r["bwd_us"] * 1e-6) / 1e9
+        e["bwd"] = {"us": round(r["bwd_us"], 2), "GBps": round(bg, 1),
+                    "frac_peak": round(bg / PEAK_HBM_GBPS, 4),
+                    "frac_ceiling": round(bg / bc["GBps"], 4), "ceiling": bc["streams"],
+                    "kernel_us_mean_p50": [round(r["bwd_kernels_us"]["mean"], 2),
+                                           round(r["bwd_kernels_us"]["p50"], 2)],
+                    "bytes": bb}
+        step_us = r["ms_per_step"] * 1e3
+        sg = (fb + bb) / (step_us * 1e-6) / 1e9
+        # the ceiling of a step: each pass at its own mix's ceiling, back to back
+        t_ceil = fb / (fc["GBps"] * 1e9) + bb / (bc["GBps"] * 1e9)
+        e["fwd_bwd"] = {"us": round(step_us, 2), "GBps": round(sg, 1),
+                        "frac_peak": round(sg / PEAK_HBM_GBPS, 4),
+                        "frac_ceiling": round(sg * 1e9 * t_ceil / (fb + bb), 4),
+                        "rows_per_s": round(w.M / (step_us * 1e-6), 1), "bytes": fb + bb}
+    return e
 
 
 def cpu_baseline(w, budget_s=10.0):
@@ -352,41 +203,6 @@ def oracle_single_thread(runs=3):
     finally:
         oracle.set_num_threads(threads)
     return out
-
-
-def sweep(torch, nl, steps, warmup, out_path, copy_gbps):
-    from deep_learning_normalization_amd import inputs, traffic
-    rows = []
-    for w in inputs.all_workloads():
-        r = timed_workload(w, steps, warmup, torch, nl, two_stage=False)
-        res = w.r is not None
-        fb = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res, wdtype=w.wdtype)
-        row = {"workload": w.name, "kind": w.kind, "dtype": w.dtype,
-               "weight_dtype": w.wdtype or w.dtype, "M": w.M, "N": w.N,
-               "residual": res, "sets": r["sets"], "fwd_us": round(r["fwd_us"], 2),
-               "fwd_GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1)}
-        row["fwd_frac_peak"] = round(row["fwd_GBps"] / PEAK_HBM_GBPS, 4)
-        if w.M * w.N <= (1 << 22):  # launch-bound sizes: the rate from a replayed graph
-            gu = graph_fwd_us(w, torch, nl)
-            row["fwd_graph_us"] = round(gu, 2)
-            row["fwd_graph_GBps"] = round(fb / (gu * 1e-6) / 1e9, 1)
-        row["fwd_rows_per_s"] = round(w.M / (r["fwd_us"] * 1e-6), 1)
-        if w.dy is not None:
-            bb = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N, wdtype=w.wdtype)
-            step_us = r["ms_per_step"] * 1e3
-            row.update({"bwd_us": round(r["bwd_us"], 2),
-                        "bwd_GBps": round(bb / (r["bwd_us"] * 1e-6) / 1e9, 1),
-                        "bwd_kernels_us": round(r["bwd_timed_us_mean"], 2),
-                        "step_us": round(step_us, 2),
-                        "fwd_bwd_GBps": round((fb + bb) / (step_us * 1e-6) / 1e9, 1)})
-            row["fwd_bwd_frac_peak"] = round(row["fwd_bwd_GBps"] / PEAK_HBM_GBPS, 4)
-        rows.append(row)
-        sys.stderr.write(json.dumps(row) + "\n")
-        sys.stderr.flush()
-    if out_path:
-        with open(out_path, "w") as f:
-            json.dump({"copy_ceiling_GBps": copy_gbps, "rows": rows}, f, indent=1)
-    return rows
 
 
 def projection(p, torch, nl, steps, warmup):
@@ -505,8 +321,11 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--sweep", action="store_true", help="also time every workload shape")
-    ap.add_argument("--sweep-out", default=None)
+    ap.add_argument("--no-shapes", action="store_true",
+                    help="time only the headline workload (for profiling runs)")
+    ap.add_argument("--sweep", action="store_true",
+                    help="also time the other workloads of the registry (ragged, hidden 16384, "
+                         "fp16, fp32 weights)")
     ap.add_argument("--projection", action="store_true",
                     help="measure the norm deferred into a following projection instead")
     args = ap.parse_args()
@@ -518,34 +337,38 @@ def main():
         sys.exit(2)
 
     import torch
-    from deep_learning_normalization_amd import inputs, normlib as nl, traffic
+    from deep_learning_normalization_amd import inputs, normlib as nl, probes, timing
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     nl.lib()  # fails loudly if libnorm.so is missing
+    probes.lib()
 
     if args.projection:
         for p in (inputs.LN_LINEAR_BF16_16384x4096x4096, inputs.RMS_LINEAR_BF16_16384x4096x4096):
             print(json.dumps(projection(p, torch, nl, args.steps, args.warmup)), flush=True)
         return
 
+    def say(msg):
+        sys.stderr.write("[bench] %s\n" % msg)
+        sys.stderr.flush()
+
     w = inputs.LN_BF16_16384x4096
-    r = timed_workload(w, args.steps, args.warmup, torch, nl)
-    copy_gbps, copy_us = copy_ceiling(torch)
+    say("headline %s: %d steps" % (w.name, args.steps))
+    r = timing.timed_workload(w, args.steps, args.warmup, torch, nl)
+    say("ceilings: HBM probes")
+    ceilings = probes.ceilings()
     st_us, st_bytes = stats_only(w, torch, nl, args.steps, args.warmup)
     M, N = w.M, w.N
-    fb = traffic.fwd_bytes(w.kind, w.dtype, M, N)
-    bb = traffic.bwd_bytes(w.kind, w.dtype, M, N)
-    bfb = traffic.bwd_fused_bytes(w.kind, w.dtype, M, N)
+    fb, bb, bfb = r["fwd_bytes"], r["bwd_bytes"], r["bwd_fused_bytes"]
     ms = r["ms_per_step"]
     value = (fb + bb) / (ms * 1e-3) / 1e9
     # dominant kernel: the fused backward pass; mean launch duration over the timed steps
-    bwd_us = r["bwd_timed_us_mean"]
-    achieved = bfb / (bwd_us * 1e-6) / 1e9
+    k = r["step_bwd_kernels_us"]
+    achieved = bfb / (k["mean"] * 1e-6) / 1e9
     tr, why = load_traffic(w.name)
-    traffic_bytes = None
-    if tr is not None:
-        traffic_bytes = tr["hbm_bytes_per_launch"]
+    traffic_bytes = tr["hbm_bytes_per_launch"] if tr is not None else None
+    head = shape_entry(w, r, ceilings)
     line = {
         "metric": "achieved HBM GB/s (% of peak) for norm fwd and fwd+bwd, bf16, per MxN shape",
         "value": round(value, 1),
@@ -561,34 +384,46 @@ def main():
         "data": "synthetic (seeded; X~N(0,1), dY~N(0,1), gamma~N(1,0.1), beta~N(0,0.1))",
         "config": {"workload": "layernorm_fwd_bwd_bf16", "kind": "layernorm", "M": M, "N": N,
                    "eps": w.eps, "pass": "fwd+bwd", "buffer_sets": r["sets"],
-                   "bytes_per_step": fb + bb},
+                   "footprint_GiB": head["footprint_GiB"], "bytes_per_step": fb + bb},
         "roofline": {"bound": "hbm", "kernel": "team_bwd_kernel (fused dX + dW/dB partials)",
                      "achieved": round(achieved, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": traffic_bytes,
-                     "algorithmic_bytes": bfb, "avg_launch_us": round(bwd_us, 3),
-                     "launch_us_p10_p50_p90": [round(r["bwd_timed_us_p10"], 3),
-                                               round(r["bwd_timed_us_median"], 3),
-                                               round(r["bwd_timed_us_p90"], 3)]},
-        "fwd": {"us": round(r["fwd_us"], 3), "GBps": round(fb / (r["fwd_us"] * 1e-6) / 1e9, 1),
-                "frac_peak": round(fb / (r["fwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                "bytes": fb},
-        "bwd": {"us": round(r["bwd_us"], 3), "GBps": round(bb / (r["bwd_us"] * 1e-6) / 1e9, 1),
-                "frac_peak": round(bb / (r["bwd_us"] * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
-                "bytes": bb},
-        "fwd_bwd": {"GBps": round(value, 1), "frac_peak": round(value / PEAK_HBM_GBPS, 4),
-                    "rows_per_s": round(M / (ms * 1e-3), 1)},
-        "copy_ceiling": {"GBps": round(copy_gbps, 1), "us_per_GiB_copy": round(copy_us, 2),
-                         "kernel": "HIP runtime device copy of 1 GiB, read + write counted"},
+                     "algorithmic_bytes": bfb, "avg_launch_us": round(k["mean"], 3),
+                     "launch_us_p10_p50_p90": [round(k["p10"], 3), round(k["p50"], 3),
+                                               round(k["p90"], 3)],
+                     "frac_ceiling": round(achieved / ceilings["triad"]["GBps"], 4),
+                     "ceiling": "triad (2R1W)"},
+        "fwd": head["fwd"],
+        "bwd": head["bwd"],
+        "fwd_bwd": head["fwd_bwd"],
+        "ceilings": dict(ceilings, kernel="probe_kernel (libhbmprobe.so, include/hbm_probe.h): "
+                         "16-byte accesses, nontemporal stores; best of 12 access shapes, "
+                         "median of 12 launches each over a rotating 2 GiB pool"),
         "stats_only": {"us": round(st_us, 3), "GBps": round(st_bytes / (st_us * 1e-6) / 1e9, 1),
                        "bytes": st_bytes,
                        "what": "norm_stats: mean and rstd without Y (loop time per call)"},
     }
     if traffic_bytes is None:
         line["roofline"]["traffic_note"] = why
-    if args.sweep:
-        sweep(torch, nl, max(20, args.steps // 4), max(5, args.warmup // 4), args.sweep_out,
-              copy_gbps)
+    if not args.no_shapes:
+        shapes = []
+        extra = [x for x in inputs.all_workloads() if x.name not in inputs.CONFIG_WORKLOADS]
+        todo = [x for x in inputs.all_workloads() if x.name in inputs.CONFIG_WORKLOADS
+                and x.name != w.name] + (extra if args.sweep else [])
+        for x in todo:
+            say("shape %s" % x.name)
+            rx = timing.timed_workload(x, max(20, args.steps // 2), max(5, args.warmup // 2),
+                                       torch, nl)
+            e = shape_entry(x, rx, ceilings)
+            if x.M * x.N <= (1 << 22):  # launch-bound sizes: the rate from a replayed graph
+                gu = timing.graph_fwd_us(x, torch, nl)
+                e["fwd"]["graph_us"] = round(gu, 2)
+                e["fwd"]["graph_GBps"] = round(rx["fwd_bytes"] / (gu * 1e-6) / 1e9, 1)
+            shapes.append(e)
+            torch.cuda.empty_cache()
+        line["shapes"] = shapes
     if not args.no_cpu_baseline:
+        say("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(w)
     print(json.dumps(line), flush=True)
 

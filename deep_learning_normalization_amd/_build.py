@@ -1,7 +1,8 @@
-"""Build libnorm.so (the HIP kernels and the C ABI) in-tree for gfx950 with hipcc.
+"""Build libnorm.so (the HIP kernels and the C ABI) and libhbmprobe.so (the HBM bandwidth
+probes the benchmark compares against) in-tree for gfx950 with hipcc.
 
-Each source compiles to an object under _build/ in parallel, then one link step writes
-deep_learning_normalization_amd/libnorm.so next to this file.
+Each source compiles to an object under _build/ in parallel, then one link step per library
+writes it next to this file.
 """
 import concurrent.futures
 import os
@@ -15,6 +16,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libnorm.so")
+PROBE_LIB = os.path.join(PKG, "libhbmprobe.so")
+PROBE_SOURCES = ["hbm_probe.hip"]
 
 ARCH = os.environ.get("DLN_OFFLOAD_ARCH", "gfx950")
 SOURCES = [
@@ -54,18 +57,24 @@ def _compile(src, extra):
     return obj
 
 
-def build(extra_flags=(), jobs=None):
-    """Compile every source and link libnorm.so. Always recompiles."""
-    os.makedirs(BUILD, exist_ok=True)
-    jobs = jobs or min(len(SOURCES), os.cpu_count() or 1, 16)
-    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
-        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), SOURCES))
-    tmp = LIB + ".tmp%d" % os.getpid()
+def _link(objs, lib):
+    tmp = lib + ".tmp%d" % os.getpid()
     cmd = [hipcc(), "--offload-arch=" + ARCH, "-shared", "-fPIC", *objs, "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("link failed: %s\n%s" % (" ".join(cmd), r.stderr))
-    os.replace(tmp, LIB)
+    os.replace(tmp, lib)
+
+
+def build(extra_flags=(), jobs=None):
+    """Compile every source and link libnorm.so and libhbmprobe.so. Always recompiles."""
+    os.makedirs(BUILD, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    jobs = jobs or min(len(srcs), os.cpu_count() or 1, 16)
+    with concurrent.futures.ThreadPoolExecutor(jobs) as ex:
+        objs = list(ex.map(lambda s: _compile(s, list(extra_flags)), srcs))
+    _link(objs[:len(SOURCES)], LIB)
+    _link(objs[len(SOURCES):], PROBE_LIB)
     return LIB
 
 

@@ -1,0 +1,126 @@
+// hbm_probe.hip -- streaming probes of HBM bandwidth (read, write, copy, two reads and one
+// write, two reads and two writes), the ceilings for the norm passes' stream mixes.
+//
+// Each thread moves `U` 16-byte accesses per stream of one tile (256 threads x U accesses,
+// consecutive threads on consecutive 16-byte words, so every wavefront access is 1 KiB
+// contiguous); all of a tile's loads are issued before its first store. Stores are nontemporal,
+// as in the norm kernels.
+#include <hip/hip_ext.h>
+#include <hip/hip_runtime.h>
+
+#include "hbm_probe.h"
+
+namespace {
+
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool NT> __device__ __forceinline__ u32x4 load16(const u32x4 *p) {
+  if constexpr (NT) return __builtin_nontemporal_load(p);
+  else return *p;
+}
+
+template <int NIN, int NOUT, int U, bool NT>
+__global__ __launch_bounds__(256) void probe_kernel(const u32x4 *__restrict__ a,
+                                                    const u32x4 *__restrict__ b,
+                                                    u32x4 *__restrict__ c, u32x4 *__restrict__ d,
+                                                    int64_t nvec, int64_t ntiles, unsigned key) {
+  constexpr int64_t TILE = 256 * U;
+  unsigned acc = 0;
+  for (int64_t tile = blockIdx.x; tile < ntiles; tile += gridDim.x) {
+    const int64_t base = tile * TILE + threadIdx.x;
+    u32x4 va[U], vb[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      va[u] = u32x4{0u, 0u, 0u, 0u};
+      vb[u] = u32x4{0u, 0u, 0u, 0u};
+      if (i < nvec) {
+        if constexpr (NIN >= 1) va[u] = load16<NT>(a + i);
+        if constexpr (NIN >= 2) vb[u] = load16<NT>(b + i);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int64_t i = base + (int64_t)u * 256;
+      if (i >= nvec) continue;
+      u32x4 r;
+      if constexpr (NIN == 0) r = u32x4{key, (unsigned)i, key, (unsigned)i};
+      else if constexpr (NIN == 1) r = va[u];
+      else r = va[u] ^ vb[u];
+      if constexpr (NOUT >= 1) __builtin_nontemporal_store(r, c + i);
+      if constexpr (NOUT >= 2) __builtin_nontemporal_store(vb[u], d + i);
+      if constexpr (NOUT == 0) acc ^= r.x ^ r.y ^ r.z ^ r.w;
+    }
+  }
+  if constexpr (NOUT == 0) {
+    if (acc == key) c[0] = u32x4{acc, acc, acc, acc}; // keeps the loads; practically never taken
+  }
+}
+
+template <int NIN, int NOUT, int U, bool NT>
+hipError_t launch(const void *in0, const void *in1, void *out0, void *out1, int64_t nvec,
+                  int64_t grid, unsigned key, hipEvent_t e0, hipEvent_t e1, hipStream_t s) {
+  const int64_t ntiles = (nvec + 256 * U - 1) / (256 * U);
+  const int64_t g = grid > 0 ? (grid < ntiles ? grid : ntiles) : ntiles;
+  const u32x4 *a = static_cast<const u32x4 *>(in0);
+  const u32x4 *b = static_cast<const u32x4 *>(in1);
+  u32x4 *c = static_cast<u32x4 *>(out0);
+  u32x4 *d = static_cast<u32x4 *>(out1);
+  void *args[] = {&a, &b, &c, &d, &nvec, const_cast<int64_t *>(&ntiles), &key};
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(probe_kernel<NIN, NOUT, U, NT>),
+                            dim3((unsigned)g), dim3(256), args, 0, s, e0, e1, 0);
+}
+
+template <int NIN, int NOUT>
+hipError_t by_shape(int unroll, int nt, const void *in0, const void *in1, void *out0, void *out1,
+                    int64_t nvec, int64_t grid, unsigned key, hipEvent_t e0, hipEvent_t e1,
+                    hipStream_t s) {
+#define DLN_PROBE_U(U)                                                                         \
+  return nt ? launch<NIN, NOUT, U, true>(in0, in1, out0, out1, nvec, grid, key, e0, e1, s)     \
+            : launch<NIN, NOUT, U, false>(in0, in1, out0, out1, nvec, grid, key, e0, e1, s);
+  switch (unroll) {
+  case 1: DLN_PROBE_U(1)
+  case 2: DLN_PROBE_U(2)
+  case 4: DLN_PROBE_U(4)
+  default: DLN_PROBE_U(8)
+  }
+#undef DLN_PROBE_U
+}
+
+bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+
+} // namespace
+
+extern "C" int hbm_probe(int nin, int nout, const void *in0, const void *in1, void *out0,
+                         void *out1, size_t bytes, int unroll, int nt_loads, int64_t grid,
+                         uint32_t key, void *start_event, void *stop_event, void *stream) {
+  if (bytes == 0 || bytes % 16 || grid < 0 || (nt_loads != 0 && nt_loads != 1)) return -1;
+  if (unroll != 1 && unroll != 2 && unroll != 4 && unroll != 8) return -1;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return -1;
+  const bool shape_ok = (nin == 1 && nout == 0) || (nin == 0 && nout == 1) ||
+                        (nin == 1 && nout == 1) || (nin == 2 && nout == 1) ||
+                        (nin == 2 && nout == 2);
+  if (!shape_ok) return -1;
+  const void *ins[] = {in0, in1};
+  void *outs[] = {out0, out1};
+  for (int i = 0; i < nin; ++i)
+    if (!ins[i] || !aligned16(ins[i])) return -1;
+  if (!out0 || !aligned16(out0)) return -1; // the read probe's sink, or the first output
+  if (nout == 2 && (!out1 || !aligned16(out1))) return -1;
+  (void)outs;
+  const int64_t nvec = (int64_t)(bytes / 16);
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (nin == 1 && nout == 0)
+    e = by_shape<1, 0>(unroll, nt_loads, in0, in1, out0, out1, nvec, grid, key, e0, e1, s);
+  else if (nin == 0)
+    e = by_shape<0, 1>(unroll, nt_loads, in0, in1, out0, out1, nvec, grid, key, e0, e1, s);
+  else if (nin == 1)
+    e = by_shape<1, 1>(unroll, nt_loads, in0, in1, out0, out1, nvec, grid, key, e0, e1, s);
+  else if (nout == 1)
+    e = by_shape<2, 1>(unroll, nt_loads, in0, in1, out0, out1, nvec, grid, key, e0, e1, s);
+  else
+    e = by_shape<2, 2>(unroll, nt_loads, in0, in1, out0, out1, nvec, grid, key, e0, e1, s);
+  return e == hipSuccess ? 0 : -2;
+}

@@ -270,8 +270,20 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 // after the team sum, with per-row constants a = rstd, nd = -delta * rstd,
 // B = -rstd * c2, C = -rstd * c1: xhat = d * a + nd, dX = g * a + (xhat * B + C), and the
 // dW / dB column sums. d, g and dY stay in registers across the team sum when the thread holds
-// at most 16 elements of the row group (else they are formed again from the packed data).
-template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE, bool LN>
+// at most 16 elements of the row group (KEEP; else they are formed again from the packed data).
+//
+// Software pipeline ([P1] para. 12, done with registers): the next row group's X, dY and
+// saved statistics are requested before the current group is reduced and written.
+//
+// CLAMP (the RMSNorm kernels): every load is unconditional, from an address clamped into the
+// tensor (rows past M read row M - 1, columns past the row's end its last access); rows past M
+// are never stored or summed into dW / dB, and columns past the row's end are masked to zero
+// where unpacked. Otherwise (LayerNorm) loads past the row's end or past M are skipped and the
+// registers hold zeros. Both give the same results; they were measured on MI355X and each kind
+// keeps the faster one (RMSNorm 32768 x 4096: 141.0 -> 135.7 us, residual 65536 x 7168: 518 ->
+// 474 us with CLAMP; LayerNorm 16384 x 4096: 76.1 us without it, 81.5 us with it).
+template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE, bool LN,
+          bool CLAMP = !LN>
 __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_threads) {
   using A = Acc<T, EV>;
   using raw = typename A::raw;
@@ -309,58 +321,58 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   }
 
   const int64_t rows_per_group = (int64_t)gm.teams * ROWS;
-  // Software pipeline: X, dY and the saved statistics of the next row group are requested
-  // before this group's reductions and stores.
-  raw px[ROWS][VPT], pdy[ROWS][VPT];
-  float pm[ROWS], pr[ROWS];
-  auto issue = [&](int64_t g, bool live) {
+  // X, dY and the saved statistics of row group g into one register set
+  auto issue = [&](raw (&px)[ROWS][VPT], raw (&pdy)[ROWS][VPT], float (&pm)[ROWS],
+                   float (&pr)[ROWS], int64_t g, bool live) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = live && row0 + r < M;
-      const int64_t row = row0 + r;
+      const int64_t rowc = rv ? row0 + r : M - 1;
       pm[r] = 0.0f;
       pr[r] = 0.0f;
       if (have_stats) {
-        const int64_t row = rv ? row0 + r : M - 1;
-        if constexpr (LN) pm[r] = a.mean[row];
-        pr[r] = a.rstd[row];
+        if constexpr (LN) pm[r] = a.mean[rowc];
+        pr[r] = a.rstd[rowc];
       }
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
-        px[r][k] = A::zero();
-        pdy[r][k] = A::zero();
-        if (rv && v < nacc) {
-          px[r][k] = A::ld(X + row * a.ldx + (int64_t)v * E);
-          pdy[r][k] = A::ld(DY + row * a.lddy + (int64_t)v * E);
+        if constexpr (CLAMP) {
+          const int64_t off = (int64_t)(v < nacc ? v : nacc - 1) * E;
+          px[r][k] = A::ld(X + rowc * a.ldx + off);
+          pdy[r][k] = A::ld(DY + rowc * a.lddy + off);
+        } else {
+          px[r][k] = A::zero();
+          pdy[r][k] = A::zero();
+          if (rv && v < nacc) {
+            px[r][k] = A::ld(X + rowc * a.ldx + (int64_t)v * E);
+            pdy[r][k] = A::ld(DY + rowc * a.lddy + (int64_t)v * E);
+          }
         }
       }
     }
   };
+  // the raw access k of a set, zero for columns past the row's end (CLAMP loads hold the last
+  // access there; the others already hold zeros)
+  auto masked = [&](raw v, int k) {
+    if constexpr (CLAMP) return gm.t + k * gm.tt < nacc ? v : A::zero();
+    else return v;
+  };
   int slot = 0;
-  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
-  int64_t g = gr.first;
-  issue(g, g < gr.end);
-#pragma unroll
-  for (int k = 0; k < VPT; ++k) rw[k].settle();
-  for (; g < gr.end; g += gr.step) {
+
+  // One row group from its register set.
+  auto process = [&](raw (&rx)[ROWS][VPT], raw (&rdy)[ROWS][VPT], const float (&sm)[ROWS],
+                     const float (&sr)[ROWS], int64_t g) {
     const int64_t row0 = g * rows_per_group + (int64_t)gm.team * ROWS;
-    raw rx[ROWS][VPT], rdy[ROWS][VPT];
     // m: the row mean the forward saved (LayerNorm), or a first-pass mean when recomputing.
     // The reduction below also sums x - m, so the exact mean m + delta is used for xhat.
     float m[ROWS], rstd[ROWS];
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      m[r] = pm[r];
-      rstd[r] = pr[r];
-#pragma unroll
-      for (int k = 0; k < VPT; ++k) {
-        rx[r][k] = px[r][k];
-        rdy[r][k] = pdy[r][k];
-      }
+      m[r] = sm[r];
+      rstd[r] = sr[r];
     }
-    issue(g + gr.step, g + gr.step < gr.end);
     if (!have_stats) {
       // recompute the forward statistics from the register-resident rows
       if constexpr (LN) {
@@ -371,7 +383,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
           for (int k = 0; k < VPT; ++k) {
             float f[E];
-            A::unpack(rx[r][k], f);
+            A::unpack(masked(rx[r][k], k), f);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc += f[e];
           }
@@ -387,9 +399,9 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           float q = 0.0f, c = 0.0f;
 #pragma unroll
           for (int k = 0; k < VPT; ++k) {
-            if (gm.t + k * gm.tt < nacc) { // rows past M are all zeros
+            if (gm.t + k * gm.tt < nacc) { // columns past the row end add nothing
               float f[E];
-              A::unpack(rx[r][k], f);
+              A::unpack(masked(rx[r][k], k), f);
 #pragma unroll
               for (int e = 0; e < E; ++e) {
                 const float d = f[e] - m[r];
@@ -416,7 +428,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
           for (int k = 0; k < VPT; ++k) {
             float f[E];
-            A::unpack(rx[r][k], f);
+            A::unpack(masked(rx[r][k], k), f);
 #pragma unroll
             for (int e = 0; e < E; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
           }
@@ -450,8 +462,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         float xf[E], df[E];
-        A::unpack(rx[r][k], xf);
-        A::unpack(rdy[r][k], df);
+        A::unpack(masked(rx[r][k], k), xf);
+        A::unpack(masked(rdy[r][k], k), df);
         float d[E], gg[E];
 #pragma unroll
         for (int e = 0; e < E; ++e) {
@@ -504,8 +516,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           }
         } else {
           float xf[E], wf[E];
-          A::unpack(rx[r][k], xf);
-          A::unpack(rdy[r][k], df);
+          A::unpack(masked(rx[r][k], k), xf);
+          A::unpack(masked(rdy[r][k], k), df);
           rw[k].get(wf);
 #pragma unroll
           for (int e = 0; e < E; ++e) {
@@ -533,6 +545,30 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         if (DR) A::st(DR + row * a.lddr + off, p);
       }
     }
+  };
+
+  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
+  raw px[ROWS][VPT], pdy[ROWS][VPT];
+  float pm[ROWS], pr[ROWS];
+  int64_t g = gr.first;
+  issue(px, pdy, pm, pr, g, g < gr.end);
+#pragma unroll
+  for (int k = 0; k < VPT; ++k) rw[k].settle();
+  for (; g < gr.end; g += gr.step) {
+    raw rx[ROWS][VPT], rdy[ROWS][VPT];
+    float cm[ROWS], cr[ROWS];
+#pragma unroll
+    for (int r = 0; r < ROWS; ++r) {
+      cm[r] = pm[r];
+      cr[r] = pr[r];
+#pragma unroll
+      for (int k = 0; k < VPT; ++k) {
+        rx[r][k] = px[r][k];
+        rdy[r][k] = pdy[r][k];
+      }
+    }
+    issue(px, pdy, pm, pr, g + gr.step, g + gr.step < gr.end);
+    process(rx, rdy, cm, cr, g);
   }
 
   // Column partials of this workgroup: sum over its teams (fixed order) and write one row

@@ -228,3 +228,12 @@ def all_workloads():
         out += [long_rows("layernorm", M, N), long_rows("rmsnorm", M, N)]
     out += [LN_BF16_16384x4100, RMS_BF16_16384x16384, LN_F16_16384x4096]
     return out
+
+
+# The workloads the benchmark reports per shape: the 2048 x 1024 fp32 forward, the LayerNorm
+# 16384 x 4096, the four hidden sizes, the residual variant and the four long-row shapes (the
+# others above are parity and sweep cases).
+CONFIG_WORKLOADS = tuple(
+    [RMS_F32_2048x1024.name, LN_BF16_16384x4096.name]
+    + [rms_hidden(N).name for N in RMS_HIDDEN_SIZES] + [RESID_RMS_BF16_65536x7168.name]
+    + [long_rows(k, M, N).name for M, N in LONG_ROW_SHAPES for k in ("layernorm", "rmsnorm")])

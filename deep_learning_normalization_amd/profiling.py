@@ -8,8 +8,9 @@ and HBM traffic.
     python -m deep_learning_normalization_amd.profiling workloads --root DIR --out FILE --cmd "..."
     python -m deep_learning_normalization_amd.profiling summarize --root DIR --out DIR
 
-`drive` runs one workload's forward and backward K times on two rotating buffer sets (run it
-under rocprofv3); it first makes the 1 GiB device copies the counter calibration uses.
+`drive` runs one workload's step, forward and backward loops K times each with the benchmark's
+cache-cold buffer rotation (run it under rocprofv3); it first runs the copy probes the counter
+calibration uses.
 `workloads` summarises, for every workload, the three runs <root>/<name>/{trace,fetch,write}
 of `drive`: per kernel, its average duration, its calibrated HBM bytes and those bytes over
 the pass's algorithmic bytes.
@@ -19,9 +20,9 @@ the pass's algorithmic bytes.
 consecutive norm kernels.
 
 `traffic` reads the FETCH_SIZE and WRITE_SIZE counter collections of two rocprofv3 --pmc runs.
-Each counter is calibrated on the 1 GiB device-to-device copies the benchmark makes (a plain
-copy kernel of known size): factor = bytes the copy must read (write) / what the counter
-reports for it. The result, per launch of the selected kernel, is written as JSON together with
+Each counter is calibrated on the copy probes the run makes (include/hbm_probe.h: a plain copy
+kernel reading and writing 256 MiB per launch): factor = bytes the copy must read (write) /
+what the counter reports for it. The result, per launch of the selected kernel, is written as JSON together with
 a hash of the kernel sources, so a later change to the kernels invalidates it.
 """
 import argparse
@@ -36,8 +37,10 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(PKG, "csrc")
-COPY_BYTES = 1 << 30
-COPY_KERNEL = "__amd_rocclr_copyBuffer"
+# Counter calibration: the in-tree copy probe (include/hbm_probe.h) reads and writes exactly
+# CALIB_BYTES per launch.
+CALIB_KERNEL = "probe_kernel<1, 1,"
+CALIB_BYTES = 256 << 20
 
 
 # Sources of the norm kernels and their dispatcher (launch shapes). The entry-point layer and
@@ -93,7 +96,9 @@ def _short(name):
     return base.replace("void dln::", "").strip()
 
 
-def stats(trace_dir, out, cmd):
+def stats(trace_dir, out, cmd, algo=None):
+    """algo: {pass label: (kernel name substring, grid threads or None, algorithmic bytes per
+    launch)} for the rate table."""
     rows = list(csv.DictReader(open(_one(trace_dir, "_kernel_stats.csv"))))
     trace = list(csv.DictReader(open(_one(trace_dir, "_kernel_trace.csv"))))
     for r in rows:
@@ -119,6 +124,24 @@ def stats(trace_dir, out, cmd):
               "|---|---|---|"]
     for k, v in sorted(gaps.items()):
         lines.append("| %s | %.2f | %d |" % (k, statistics.median(v), len(v)))
+    if algo:
+        lines += ["", "Algorithmic bytes per launch over the launch's duration: the average, and "
+                  "at the fastest launch (above 8000 GB/s would mean a launch found its data "
+                  "in a cache). Launches are told apart by kernel and grid (threads), since the "
+                  "statistics pass runs the forward's kernel on a grid of its own:", "",
+                  "| pass | kernel | grid threads | algorithmic bytes | launches | average us | "
+                  "GB/s at average | fastest us | GB/s at fastest |",
+                  "|---|---|---|---|---|---|---|---|---|"]
+        for label, (sub, grid, nbytes) in algo.items():
+            d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0
+                 for r in trace if sub in r["Kernel_Name"] and
+                 (grid is None or int(r.get("Grid_Size_X", -1)) == grid)]
+            if not d:
+                continue
+            avg, fast = statistics.mean(d), min(d)
+            lines.append("| %s | %s | %s | %d | %d | %.2f | %.0f | %.2f | %.0f |" % (
+                label, sub, grid if grid is not None else "any", nbytes, len(d), avg,
+                nbytes / (avg * 1e3), fast, nbytes / (fast * 1e3)))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
     return rows
@@ -134,16 +157,20 @@ def _counter(directory, counter):
     return per
 
 
+def _calibration(fetch, write):
+    """Bytes per counter KiB for FETCH_SIZE and WRITE_SIZE, from the copy probes of the run."""
+    cf = [v for n, vs in fetch.items() if CALIB_KERNEL in n for v in vs]
+    cw = [v for n, vs in write.items() if CALIB_KERNEL in n for v in vs]
+    if not cf or not cw:
+        raise RuntimeError("no calibration copies (%s) in the counter runs" % CALIB_KERNEL)
+    return (CALIB_BYTES / (statistics.median(cf) * 1024.0),
+            CALIB_BYTES / (statistics.median(cw) * 1024.0))
+
+
 def traffic(fetch_dir, write_dir, workload, kernel, algo_bytes, out, cmd):
     fetch = _counter(fetch_dir, "FETCH_SIZE")
     write = _counter(write_dir, "WRITE_SIZE")
-    # calibration: the 1 GiB copies are the largest copy dispatches
-    cf = sorted(fetch.get(COPY_KERNEL, []))[-8:]
-    cw = sorted(write.get(COPY_KERNEL, []))[-8:]
-    if not cf or not cw:
-        raise RuntimeError("no calibration copies in the counter runs")
-    f_factor = COPY_BYTES / (statistics.median(cf) * 1024.0)
-    w_factor = COPY_BYTES / (statistics.median(cw) * 1024.0)
+    f_factor, w_factor = _calibration(fetch, write)
     names = [n for n in fetch if kernel in n]
     if len(names) != 1:
         raise RuntimeError("kernel filter %r matches %d kernels: %s" % (kernel, len(names), names))
@@ -167,44 +194,27 @@ def traffic(fetch_dir, write_dir, workload, kernel, algo_bytes, out, cmd):
 
 # ---- workload driver -------------------------------------------------------------------------
 
-def drive(name, steps):
-    """Forward then backward of one workload, `steps` times over two buffer sets."""
-    import torch
-    from deep_learning_normalization_amd import inputs, normlib as nl
-    w = {x.name: x for x in inputs.all_workloads()}[name]
-    nl.lib()
-    # calibration: 1 GiB device-to-device copies of known size
-    a = torch.empty(COPY_BYTES // 2, dtype=torch.bfloat16, device="cuda")
+def calibration_copies(torch, probes, n=4):
+    """n launches of the copy probe on fresh CALIB_BYTES buffers (the counter calibration)."""
+    a = torch.empty(CALIB_BYTES // 4, dtype=torch.int32, device="cuda").random_()
     b = torch.empty_like(a)
-    for _ in range(4):
-        b.copy_(a)
+    for _ in range(n):
+        probes.probe(1, 1, [a], [b], CALIB_BYTES)
     torch.cuda.synchronize()
     del a, b
     torch.cuda.empty_cache()
-    host = inputs.make(w)
-    dev = [{k: (v.cuda() if v is not None else None) for k, v in host.items()} for _ in range(2)]
-    ln = w.kind == "layernorm"
-    M, N = w.M, w.N
-    outs = []
-    for d in dev:
-        X = d["X"]
-        outs.append({"Y": torch.empty_like(X),
-                     "H": torch.empty_like(X) if d["R"] is not None else None,
-                     "mean": torch.empty(M, device="cuda") if ln else None,
-                     "rstd": torch.empty(M, device="cuda"), "dX": torch.empty_like(X)})
-    W, B = dev[0]["W"], dev[0]["B"]
-    dW = torch.empty_like(W)
-    dB = torch.empty_like(W) if ln else None
-    wsf = nl.workspace(w.kind, host["X"].dtype, nl.PASS_FWD, M, N, w.r is not None)
-    wsb = nl.workspace(w.kind, host["X"].dtype, nl.PASS_BWD, M, N)
-    for i in range(steps):
-        d, o = dev[i % 2], outs[i % 2]
-        nl.norm_fwd(w.kind, d["X"], d["R"], W, B, w.eps, o["Y"], o["H"], o["mean"], o["rstd"],
-                    wsf)
-        if w.dy is not None:
-            Xin = o["H"] if o["H"] is not None else d["X"]
-            nl.norm_bwd(w.kind, Xin, d["dY"], None, W, o["mean"], o["rstd"], w.eps, o["dX"],
-                        None, dW, dB, wsb)
+
+
+def drive(name, steps):
+    """One workload's step, forward and backward loops (timing.timed_workload: the benchmark's
+    cache-cold buffer rotation), `steps` calls each, after the copy probes the counter
+    calibration uses."""
+    import torch
+    from deep_learning_normalization_amd import inputs, normlib as nl, probes, timing
+    w = {x.name: x for x in inputs.all_workloads()}[name]
+    nl.lib()
+    calibration_copies(torch, probes)
+    timing.timed_workload(w, steps, 2, torch, nl, settle_s=0.1)
     torch.cuda.synchronize()
 
 
@@ -226,10 +236,12 @@ def workloads(root, out, cmd):
     lines = ["# Norm kernels per workload: duration and HBM traffic (rocprofv3)", "",
              "command (per workload NAME): %s" % cmd, "",
              "HBM bytes = FETCH_SIZE x fetch calibration + WRITE_SIZE x write calibration, the "
-             "factors taken from 1 GiB device copies in the same run. 'algorithmic' is the "
+             "factors taken from the copy probes (256 MiB read and written) in the same run. "
+             "'algorithmic' is the "
              "pass's minimum traffic; the backward's dW/dB partials are extra by design.", "",
-             "| workload | kernel | launches | avg us | HBM MB/launch | pass | algorithmic MB | "
-             "HBM / algorithmic | GB/s (HBM) |", "|---|---|---|---|---|---|---|---|---|"]
+             "| workload | kernel | launches | avg us | fastest us | HBM MB/launch | pass | "
+             "algorithmic MB | HBM / algorithmic | GB/s (HBM) | pass GB/s at fastest launch |",
+             "|---|---|---|---|---|---|---|---|---|---|---|"]
     for w in inputs.all_workloads():
         d = os.path.join(root, w.name)
         if not os.path.isdir(d):
@@ -237,10 +249,7 @@ def workloads(root, out, cmd):
         dur = _kernel_rows(os.path.join(d, "trace"))
         fetch = _counter(os.path.join(d, "fetch"), "FETCH_SIZE")
         write = _counter(os.path.join(d, "write"), "WRITE_SIZE")
-        cf = sorted(fetch.get(COPY_KERNEL, []))[-4:]
-        cw = sorted(write.get(COPY_KERNEL, []))[-4:]
-        f_factor = COPY_BYTES / (statistics.median(cf) * 1024.0)
-        w_factor = COPY_BYTES / (statistics.median(cw) * 1024.0)
+        f_factor, w_factor = _calibration(fetch, write)
         res = w.r is not None
         fwd_alg = traffic.fwd_bytes(w.kind, w.dtype, w.M, w.N, residual=res, wdtype=w.wdtype)
         bwd_alg = traffic.bwd_bytes(w.kind, w.dtype, w.M, w.N, wdtype=w.wdtype) \
@@ -252,11 +261,16 @@ def workloads(root, out, cmd):
             fb = statistics.median(fetch[full]) * 1024.0 * f_factor
             wb = statistics.median(write.get(full, [0.0])) * 1024.0 * w_factor
             us = statistics.mean(dur.get(short, [float("nan")]))
+            fast = min(dur.get(short, [float("nan")]))
             bwd_kernel = any(t in short for t in ("bwd", "colsum", "partial", "dx_kernel"))
             alg = bwd_alg if bwd_kernel else fwd_alg
-            lines.append("| %s | %s | %d | %.2f | %.1f | %s | %.1f | | %.0f |" % (
-                w.name, short, len(dur.get(short, [])), us, (fb + wb) / 1e6,
-                "bwd" if bwd_kernel else "fwd", alg / 1e6, (fb + wb) / (us * 1e-6) / 1e9))
+            # the pass's bytes over the fastest launch, for the kernel that moves the pass's
+            # data (its HBM traffic at least half the pass's algorithmic bytes)
+            main = (fb + wb) >= 0.5 * alg
+            lines.append("| %s | %s | %d | %.2f | %.2f | %.1f | %s | %.1f | | %.0f | %s |" % (
+                w.name, short, len(dur.get(short, [])), us, fast, (fb + wb) / 1e6,
+                "bwd" if bwd_kernel else "fwd", alg / 1e6, (fb + wb) / (us * 1e-6) / 1e9,
+                "%.0f" % (alg / (fast * 1e-6) / 1e9) if main else ""))
         # per pass totals: all kernels of the pass
         for pname, alg, sel in (("fwd", fwd_alg, False), ("bwd", bwd_alg, True)):
             if not alg:
@@ -269,20 +283,20 @@ def workloads(root, out, cmd):
                 tot_b += (statistics.median(fetch[full]) * f_factor +
                           statistics.median(write.get(full, [0.0])) * w_factor) * 1024.0
                 tot_us += statistics.mean(dur.get(short, [0.0]))
-            lines.append("| %s | **%s pass, all kernels** | | %.2f | %.1f | %s | %.1f | %.3f | "
-                         "%.0f |" % (w.name, pname, tot_us, tot_b / 1e6, pname, alg / 1e6,
-                                     tot_b / alg, alg / (tot_us * 1e-6) / 1e9))
+            lines.append("| %s | **%s pass, all kernels** | | %.2f | | %.1f | %s | %.1f | %.3f | "
+                         "%.0f | |" % (w.name, pname, tot_us, tot_b / 1e6, pname, alg / 1e6,
+                                       tot_b / alg, alg / (tot_us * 1e-6) / 1e9))
     with open(out, "w") as f:
         f.write("\n".join(lines) + "\n")
 
 
 HEADLINE_TRACE_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --kernel-trace --stats -d $REPO/gpurun_out/prof_trace "
                       "-o trace --output-format csv -- python3 $REPO/bench.py --steps 50 --warmup 10 "
-                      "--no-cpu-baseline")
+                      "--no-cpu-baseline --no-shapes")
 HEADLINE_PMC_CMD = ("cd /tmp && TMPDIR=/tmp rocprofv3 --pmc FETCH_SIZE -d $REPO/gpurun_out/prof_fetch -o fetch "
                     "--output-format csv -- python3 $REPO/bench.py --steps 20 --warmup 5 "
-                    "--no-cpu-baseline; the same with --pmc WRITE_SIZE -d $REPO/gpurun_out/prof_write "
-                    "-o write")
+                    "--no-cpu-baseline --no-shapes; the same with --pmc WRITE_SIZE -d "
+                    "$REPO/gpurun_out/prof_write -o write")
 WORKLOAD_CMD = ("cd /tmp && PYTHONPATH=$REPO rocprofv3 {--kernel-trace | --pmc FETCH_SIZE | --pmc "
                 "WRITE_SIZE} -d $REPO/gpurun_out/wl/NAME/{trace|fetch|write} -o run --output-format csv "
                 "-- python3 -m deep_learning_normalization_amd.profiling drive --workload NAME")
@@ -294,8 +308,21 @@ def summarize(root, out):
     per-workload table (under root/wl)."""
     from deep_learning_normalization_amd import inputs, traffic as model
     w = inputs.LN_BF16_16384x4096
+    from deep_learning_normalization_amd import normlib as nl
+
+    def grid_threads(pass_):
+        p = nl.norm_plan(w.kind, nl.BF16, pass_, w.M, w.N, cu_count=256)
+        return p["grid"] * p["threads"]
+    stats_bytes = w.M * w.N * 2 + 8 * w.M
     stats(os.path.join(root, "prof_trace"), os.path.join(out, "kernel_stats_%s.md" % w.name),
-          HEADLINE_TRACE_CMD)
+          HEADLINE_TRACE_CMD,
+          {"fused backward": ("team_bwd_kernel", grid_threads(nl.PASS_BWD),
+                              model.bwd_fused_bytes(w.kind, w.dtype, w.M, w.N)),
+           "forward": ("team_fwd_kernel", grid_threads(nl.PASS_FWD),
+                       model.fwd_bytes(w.kind, w.dtype, w.M, w.N)),
+           "statistics alone": ("team_fwd_kernel", grid_threads(nl.PASS_STATS), stats_bytes),
+           "copy probe": ("probe_kernel<1, 1", None, 2 * (256 << 20)),
+           "triad probe": ("probe_kernel<2, 1", None, 3 * (256 << 20))})
     fetch, write = os.path.join(root, "prof_fetch"), os.path.join(root, "prof_write")
     traffic(fetch, write, w.name, "team_bwd_kernel",
             model.bwd_fused_bytes(w.kind, w.dtype, w.M, w.N),

@@ -535,6 +535,27 @@ def test_tuning_knobs(knob, kind, dt, M, N):
         run_and_check(_small(kind, dt, M, N, seed=M))
 
 
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+@pytest.mark.parametrize("dt,wdt", [("bf16", None), ("f32", None), ("f16", None),
+                                    ("bf16", "f32")])
+def test_backward_ragged_row_groups(kind, dt, wdt):
+    """The wave and block backwards on row counts that end a workgroup's walk part-way through
+    a row group (rows past M load a clamped row in the RMSNorm kernels and must leave no trace),
+    on rows shorter than a team (columns past the row end masked), with grids that leave
+    workgroups one, two or many groups; the statistics recomputed, an incoming dH and a separate
+    dR."""
+    for N in (1024, 4096, 1000):
+        for M in (1, 2, 3, 5, 257, 1000):
+            for gpc in (-1, 1, 64):
+                _say("ragged row groups %s %s/%s %dx%d grid/cu %d" % (kind, dt, wdt, M, N, gpc))
+                w = dataclasses.replace(_small(kind, dt, M, N, seed=M * N + gpc), wdtype=wdt)
+                with tuned(grid_per_cu=gpc):
+                    run_and_check(w)
+                    if M == 257:
+                        run_and_check(dataclasses.replace(w, seed=M + 1), stats=False)
+                        run_and_check(dataclasses.replace(w, seed=M + 2), dr="separate", dh=True)
+
+
 # ---- residual variant -----------------------------------------------------------------------
 
 @pytest.mark.parametrize("dr", ["none", "alias", "separate"])

@@ -1,0 +1,59 @@
+"""The HBM probes move the data they claim to (needs a gfx950 GPU): the copy reproduces its
+input bit for bit, the two-input probes write the XOR of their inputs (and the second input),
+the write probe its pattern, and the read probe leaves its sink alone; sizes that end inside a
+tile and every access shape and grid are covered."""
+import pytest
+import torch
+
+from deep_learning_normalization_amd import probes
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 16 * 1000 + 16 * 3, (8 << 20) + 16 * 37])
+@pytest.mark.parametrize("unroll,nt,grid", [(1, 0, 0), (2, 1, 0), (4, 0, 64), (8, 1, 3)])
+def test_probe_moves_its_streams(nbytes, unroll, nt, grid):
+    print("[gpu] probe %d bytes unroll %d nt %d grid %d" % (nbytes, unroll, nt, grid), flush=True)
+    n = nbytes // 4
+    g = torch.Generator(device="cuda").manual_seed(nbytes + unroll)
+    a = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda", generator=g)
+    b = torch.randint(-2 ** 31, 2 ** 31 - 1, (n,), dtype=torch.int32, device="cuda", generator=g)
+    guard = 64
+    c = torch.full((n + guard,), 7, dtype=torch.int32, device="cuda")
+    d = torch.full((n + guard,), 9, dtype=torch.int32, device="cuda")
+    probes.probe(1, 1, [a], [c], nbytes, unroll, nt, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(c[:n], a) and (c[n:] == 7).all()
+    probes.probe(2, 1, [a, b], [c], nbytes, unroll, nt, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(c[:n], a ^ b)
+    probes.probe(2, 2, [a, b], [c, d], nbytes, unroll, nt, grid)
+    torch.cuda.synchronize()
+    assert torch.equal(c[:n], a ^ b) and torch.equal(d[:n], b) and (d[n:] == 9).all()
+    key = 0x12345
+    probes.probe(0, 1, [], [c], nbytes, unroll, nt, grid, key=key)
+    torch.cuda.synchronize()
+    v = c[:n].view(-1, 4)
+    assert (v[:, 0] == key).all() and (v[:, 2] == key).all()
+    assert torch.equal(v[:, 1], torch.arange(n // 4, device="cuda", dtype=torch.int32))
+    # the read probe writes its sink only where a thread's XOR of what it read equals the key:
+    # over zeros every thread's XOR is 0
+    z = torch.zeros(n, dtype=torch.int32, device="cuda")
+    sink = torch.full((4,), 5, dtype=torch.int32, device="cuda")
+    probes.probe(1, 0, [z], [sink], nbytes, unroll, nt, grid, key=1)
+    torch.cuda.synchronize()
+    assert (sink == 5).all()
+    probes.probe(1, 0, [z], [sink], nbytes, unroll, nt, grid, key=0)
+    torch.cuda.synchronize()
+    assert (sink == 0).all()
+
+
+def test_ceilings_report_every_mix():
+    print("[gpu] ceilings", flush=True)
+    c = probes.ceilings(stream_bytes=64 << 20, pool=8, iters=3,
+                        variants=[(4, 0, 0), (8, 1, 0)])
+    assert set(c) == set(probes.MIXES)
+    for name, e in c.items():
+        nin, nout = probes.MIXES[name]
+        assert e["streams"] == "%dR%dW" % (nin, nout)
+        assert 100.0 < e["GBps"] < 8000.0 * 1.05, (name, e)
