@@ -94,6 +94,7 @@ bool block_menu(int wc, bool bwd, int vpt, int rows, int lb, int sc = 1, bool re
   case 512:
     return (vpt == 1 && (rows == 1 || rows == 2 || rows == 4)) ||
            (vpt == 2 && (rows == 1 || rows == 2)) || (vpt == 4 && rows == 1);
+  case 768: return vpt == 1 && (rows == 1 || rows == 2);
   case 1024:
     return (vpt == 1 && (rows == 1 || rows == 2)) || (vpt == 2 && rows == 1);
   default: return false;
@@ -111,7 +112,7 @@ bool block_fits_registers(int wc, bool bwd, int vpt, int rows, int lb) {
     if (lb >= 512) return slots <= 4;
     return slots <= 8;
   }
-  if (lb >= 1024) return vpt == 1 && slots <= 2;
+  if (lb >= 768) return vpt == 1 && slots <= 2;
   if (lb >= 512) return vpt <= 2 && slots <= 4;
   return vpt <= 4 && slots <= 8;
 }
@@ -281,11 +282,19 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
                               ? (vec ? (bwd ? kBlockTeamTargetBwd : fwd_limit) : 1024)
                               : 1024;
         if (cand > limit) continue;
-        const int lb = vec ? lb_of(cand) : 1024;
+        // Backward teams of 513-768 threads with one full-width access per thread are compiled
+        // for 768 threads (3 wavefronts per SIMD, about 170 VGPRs), which holds two rows without
+        // spilling; a 1024-thread bound leaves 128 VGPRs, and the two-row kernel spilled there.
+        const bool mid = bwd && wc == kFull && v == 1 && cand > 512 && cand <= 768;
+        const int lb = mid ? 768 : vec ? lb_of(cand) : 1024;
         // Backward teams of up to 512 threads with one access per thread hold two rows at
         // once by default (measured on MI355X, with the saved statistics prefetched as well:
-        // fewer, fuller workgroups; wider teams or more accesses per thread do better with one)
-        int r = t.rows > 0 ? t.rows : ((bwd && v == 1 && cand <= 512) ? 2 : 1);
+        // fewer, fuller workgroups; wider teams or more accesses per thread do better with one).
+        // Teams of 513-768 threads: two rows for RMSNorm, one for LayerNorm (measured on one
+        // GPU at 640 threads: RMSNorm 32768 x 5120 197 against 202 us; LayerNorm 32768 x 5120
+        // 228 against 188 us, fp32 32768 x 2560 200 against 174 us)
+        const int two_upto = kind == NORM_RMSNORM ? 768 : 512;
+        int r = t.rows > 0 ? t.rows : ((bwd && v == 1 && cand <= two_upto) ? 2 : 1);
         const bool res = residual != 0;
         auto ok = [&](int rr) {
           return block_menu(wc, bwd, v, rr, lb, sc, res) &&

@@ -22,7 +22,7 @@ namespace dln {
 #define DLN_BLOCK_MENU(X)                                                                       \
   X(1, 1, 256) X(1, 2, 256) X(1, 4, 256) X(2, 1, 256) X(2, 2, 256) X(2, 4, 256) X(4, 1, 256)       \
       X(8, 1, 256) X(1, 1, 512) X(1, 2, 512) X(1, 4, 512) X(2, 1, 512) X(2, 2, 512) X(4, 1, 512)   \
-          X(1, 1, 1024) X(1, 2, 1024) X(2, 1, 1024)
+          X(1, 1, 768) X(1, 2, 768) X(1, 1, 1024) X(1, 2, 1024) X(2, 1, 1024)
 #define DLN_BLOCK_MENU_SCALAR(X) X(4, 1, 1024) X(8, 1, 1024)
 
 template <typename T, typename TW>

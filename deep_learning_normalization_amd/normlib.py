@@ -140,22 +140,36 @@ def _ptr(t):
     return t.data_ptr() or None
 
 
-def _stream(stream):
+_raw_stream = torch._C._cuda_getCurrentRawStream
+
+
+def _stream(stream, like=None):
+    """The hipStream_t of `stream`; None: the current stream of `like`'s device (or of the
+    current device)."""
     if stream is None:
-        return torch.cuda.current_stream().cuda_stream
+        return _raw_stream(like.get_device() if like is not None else torch.cuda.current_device())
     if isinstance(stream, int):
         return stream
     return stream.cuda_stream
 
 
+def _mat_err(name, dtype, M, N):
+    return ValueError("%s must be a CUDA %s tensor of %d x %d elements with contiguous rows"
+                      % (name, dtype, M, N))
+
+
 def _check_mat(t, M, N, dtype, name):
-    """A CUDA [M, N] tensor of `dtype` whose rows are contiguous (row stride >= N allowed)."""
+    """A CUDA [M, N] tensor of `dtype` whose rows are contiguous (row stride >= N allowed).
+    Returns whether its row stride differs from N (False for None)."""
     if t is None:
-        return
-    if (t.dtype != dtype or tuple(t.shape) != (M, N) or not t.is_cuda or
-            (M > 1 and t.stride(0) < N) or (N > 1 and t.stride(1) != 1)):
-        raise ValueError("%s must be a CUDA %s tensor of %d x %d elements with contiguous rows"
-                         % (name, dtype, M, N))
+        return False
+    if t.dtype is not dtype or t.shape != (M, N) or not t.is_cuda:
+        raise _mat_err(name, dtype, M, N)
+    if t.is_contiguous():
+        return False
+    if (N > 1 and t.stride(1) != 1) or (M > 1 and t.stride(0) < N):
+        raise _mat_err(name, dtype, M, N)
+    return M > 1 and t.stride(0) != N
 
 
 def _strides(**mats):
@@ -173,7 +187,7 @@ def _strides(**mats):
 def _check_vec(t, n, dtype, name):
     if t is None:
         return
-    if t.dtype != dtype or t.numel() != n or not t.is_contiguous() or not t.is_cuda:
+    if t.dtype is not dtype or t.numel() != n or not t.is_cuda or not t.is_contiguous():
         raise ValueError("%s must be a contiguous CUDA %s tensor of %d elements" % (name, dtype, n))
 
 
@@ -193,8 +207,10 @@ def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=N
     """Queue the forward. X, R, Y, H are [M, N]; W, B are [N]; mean, rstd are [M] fp32."""
     M, N = X.shape
     dt, wdt = X.dtype, W.dtype
-    for t, nm in ((X, "X"), (R, "R"), (Y, "Y"), (H, "H")):
-        _check_mat(t, M, N, dt, nm)
+    strided = _check_mat(X, M, N, dt, "X")
+    strided |= _check_mat(R, M, N, dt, "R")
+    strided |= _check_mat(Y, M, N, dt, "Y")
+    strided |= _check_mat(H, M, N, dt, "H")
     _check_vec(W, N, wdt, "W")
     _check_vec(B, N, wdt, "B")
     _check_vec(mean, M, torch.float32, "mean")
@@ -202,7 +218,8 @@ def norm_fwd(kind, X, R, W, B, eps, Y, H=None, mean=None, rstd=None, workspace=N
     wp, wb = _ws(workspace)
     st = lib().norm_fwd_ex(_kind(kind), _ptr(X), _ptr(R), _ptr(W), _ptr(B), float(eps), M, N,
                            dtype_code(dt, wdt), _ptr(Y), _ptr(H), _ptr(mean), _ptr(rstd), wp, wb,
-                           _strides(x=X, r=R, y=Y, h=H), _stream(stream))
+                           _strides(x=X, r=R, y=Y, h=H) if strided else None,
+                           _stream(stream, X))
     _raise(st, "norm_fwd")
 
 
@@ -210,14 +227,15 @@ def norm_stats(kind, X, R, eps, H=None, mean=None, rstd=None, workspace=None, st
     """Queue the statistics pass alone: mean (LayerNorm) and rstd, and H = R + X with R."""
     M, N = X.shape
     dt = X.dtype
-    for t, nm in ((X, "X"), (R, "R"), (H, "H")):
-        _check_mat(t, M, N, dt, nm)
+    strided = _check_mat(X, M, N, dt, "X")
+    strided |= _check_mat(R, M, N, dt, "R")
+    strided |= _check_mat(H, M, N, dt, "H")
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
     st = lib().norm_stats(_kind(kind), _ptr(X), _ptr(R), float(eps), M, N, DTYPES[dt], _ptr(H),
-                          _ptr(mean), _ptr(rstd), wp, wb, _strides(x=X, r=R, h=H),
-                          _stream(stream))
+                          _ptr(mean), _ptr(rstd), wp, wb,
+                          _strides(x=X, r=R, h=H) if strided else None, _stream(stream, X))
     _raise(st, "norm_stats")
 
 
@@ -273,8 +291,11 @@ def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, str
     """Queue the backward (fused pass, then the column reduction)."""
     M, N = X.shape
     dt, wdt = X.dtype, W.dtype
-    for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
-        _check_mat(t, M, N, dt, nm)
+    strided = _check_mat(X, M, N, dt, "X")
+    strided |= _check_mat(dY, M, N, dt, "dY")
+    strided |= _check_mat(dH, M, N, dt, "dH")
+    strided |= _check_mat(dX, M, N, dt, "dX")
+    strided |= _check_mat(dR, M, N, dt, "dR")
     for t, nm in ((W, "W"), (dW, "dW"), (dB, "dB")):
         _check_vec(t, N, wdt, nm)
     _check_vec(mean, M, torch.float32, "mean")
@@ -283,7 +304,8 @@ def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, str
     st = lib().norm_bwd_ex(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
                            _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX), _ptr(dR),
                            _ptr(dW), _ptr(dB), wp, wb,
-                           _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR), _stream(stream))
+                           _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR) if strided else None,
+                           _stream(stream, X))
     _raise(st, "norm_bwd")
 
 
@@ -310,16 +332,20 @@ def norm_bwd_fused(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, workspace, strea
     """Queue the backward's fused pass: dX (and dR), column partials into the workspace."""
     M, N = X.shape
     dt, wdt = X.dtype, W.dtype
-    for t, nm in ((X, "X"), (dY, "dY"), (dH, "dH"), (dX, "dX"), (dR, "dR")):
-        _check_mat(t, M, N, dt, nm)
+    strided = _check_mat(X, M, N, dt, "X")
+    strided |= _check_mat(dY, M, N, dt, "dY")
+    strided |= _check_mat(dH, M, N, dt, "dH")
+    strided |= _check_mat(dX, M, N, dt, "dX")
+    strided |= _check_mat(dR, M, N, dt, "dR")
     _check_vec(W, N, wdt, "W")
     _check_vec(mean, M, torch.float32, "mean")
     _check_vec(rstd, M, torch.float32, "rstd")
     wp, wb = _ws(workspace)
     st = lib().norm_bwd_fused_ex(_kind(kind), _ptr(X), _ptr(dY), _ptr(dH), _ptr(W), _ptr(mean),
                                  _ptr(rstd), float(eps), M, N, dtype_code(dt, wdt), _ptr(dX),
-                                 _ptr(dR), wp, wb, _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR),
-                                 _stream(stream))
+                                 _ptr(dR), wp, wb,
+                                 _strides(x=X, dy=dY, dh=dH, dx=dX, dr=dR) if strided else None,
+                                 _stream(stream, X))
     _raise(st, "norm_bwd_fused")
 
 

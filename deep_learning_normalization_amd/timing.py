@@ -75,6 +75,12 @@ class Rotation:
         self.dW = torch.empty_like(self.W)
         self.dB = torch.empty_like(self.W) if ln else None
         adt = host["X"].dtype
+        # the split scheme's norm_bwd may sum its column partials inside the fused pass, which
+        # the two-stage calls (norm_bwd_fused, then norm_bwd_reduce) cannot
+        self.split = (w.dy is not None and nl.norm_plan(
+            w.kind, nl.dtype_code(adt, self.W.dtype), nl.PASS_BWD, M, N,
+            cu_count=torch.cuda.get_device_properties(0).multi_processor_count)["scheme"]
+            == nl.SCHEME_SPLIT)
         self.wsf = nl.workspace(w.kind, adt, nl.PASS_FWD, M, N, res)
         self.wsb = nl.workspace(w.kind, adt, nl.PASS_BWD, M, N) if w.dy is not None else None
         for s in self.sets:  # every set gets its statistics (and H) before a backward reads it
@@ -113,9 +119,11 @@ def timed_workload(w, steps, warmup, torch, nl, two_stage=True, settle_s=0.3, ro
 
     two_stage: the step's backward is norm_bwd_fused (its kernels' timestamps taken on every
     launch) followed by norm_bwd_reduce, which is what norm_bwd runs for the wave, block and
-    looped schemes; else norm_bwd as a whole (timed the same way). Returns loop times per call
-    and per-launch kernel statistics (mean, p10, median, p90 in microseconds)."""
+    looped schemes; else, and always for the split scheme, norm_bwd as a whole (timed the same
+    way). Returns loop times per call and per-launch kernel statistics (mean, p10, median, p90 in
+    microseconds)."""
     rot = rot or Rotation(w, torch, nl)
+    two_stage = two_stage and not rot.split
     S = rot.S
     want_bwd = w.dy is not None
     stream = torch.cuda.current_stream()

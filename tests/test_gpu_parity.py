@@ -1002,7 +1002,9 @@ def test_workspace_too_small_is_rejected():
 
 
 @pytest.mark.parametrize("kind,M,N", [("layernorm", 2048, 4096), ("rmsnorm", 256, 262144),
-                                      ("rmsnorm", 4, 1 << 20), ("layernorm", 999, 777)])
+                                      ("rmsnorm", 4, 1 << 20), ("layernorm", 999, 777),
+                                      ("layernorm", 256, 262144), ("layernorm", 17, 262144),
+                                      ("rmsnorm", 3, 20000), ("layernorm", 64, 65536)])
 def test_two_stage_backward_matches_norm_bwd(kind, M, N):
     w = _small(kind, "bf16", M, N, seed=2)
     t = inputs.make(w)
@@ -1023,6 +1025,41 @@ def test_two_stage_backward_matches_norm_bwd(kind, M, N):
         assert torch.equal(dB1.view(torch.int16), dB2.view(torch.int16))
 
 
+@pytest.mark.parametrize("dt,wdt", [("bf16", None), ("f32", None), ("f16", None),
+                                    ("bf16", "f32")])
+@pytest.mark.parametrize("kind", ["layernorm", "rmsnorm"])
+def test_split_row_group_counts(kind, dt, wdt):
+    """The single-pass split backward with 2, 3, 7, 16, 32 and 33 row groups (each writes a
+    partial row of column sums that the reduction pass adds): norm_bwd matches the oracle and
+    gives the same bits as the two-stage calls; ragged last chunks, rows per group uneven."""
+    for N in (20000, 65536, 8192 * 5 + 8):
+        for M, groups in ((40, 2), (40, 3), (45, 7), (80, 16), (64, 32), (70, 33)):
+            _say("split row groups %s %s/%s %dx%d groups %d" % (kind, dt, wdt, M, N, groups))
+            w = dataclasses.replace(_small(kind, dt, M, N, seed=M + N + groups), wdtype=wdt)
+            with tuned(exchange=1, row_groups=groups):
+                p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_BWD, M, N,
+                                 cu_count=torch.cuda.get_device_properties(0).multi_processor_count)
+                if p["exchange_row_groups"] == 0:
+                    continue  # this width runs two passes
+                out = run_and_check(w)
+                X = inputs.make(w)["X"].cuda()
+                t = inputs.make(w)
+                W, dY = t["W"].cuda(), t["dY"].cuda()
+                ws = nl.workspace(kind, X.dtype, nl.PASS_BWD, M, N)
+                dX2, dW2 = torch.empty_like(X), torch.empty_like(W)
+                dB2 = torch.empty_like(W) if kind == "layernorm" else None
+                nl.norm_bwd_fused(kind, X, dY, None, W, out["mean"], out["rstd"], w.eps, dX2,
+                                  None, ws)
+                nl.norm_bwd_reduce(kind, M, N, dW2, dB2, ws)
+                torch.cuda.synchronize()
+                bits = (lambda v: v.view(torch.int16) if v.element_size() == 2 else v)
+                assert torch.equal(bits(out["dX"]), bits(dX2))
+                assert torch.equal(bits(out["dW"]), bits(dW2))
+                if dB2 is not None:
+                    assert torch.equal(bits(out["dB"]), bits(dB2))
+                assert nl.norm_workspace_status(out["ws"]) == nl.OK
+
+
 def test_reduce_on_a_foreign_workspace_gives_nan():
     """The reduce stage reads the partial count from the header the fused pass wrote; on a
     workspace that holds no such header it writes NaN rather than reading past the partials."""
@@ -1032,3 +1069,33 @@ def test_reduce_on_a_foreign_workspace_gives_nan():
     nl.norm_bwd_reduce("rmsnorm", 100, N, dW, None, ws)
     torch.cuda.synchronize()
     assert torch.isnan(dW.float()).all()
+
+
+def test_binding_checks_tensors():
+    """The Python binding refuses tensors the C ABI cannot check (wrong dtype, shape, device,
+    columns not contiguous) before calling the library, and passes row-strided views with their
+    strides."""
+    _say("binding checks")
+    M, N = 64, 1024
+    w = _small("layernorm", "bf16", M, N, seed=5)
+    t = inputs.make(w)
+    X, W, B = (t[k].cuda() for k in ("X", "W", "B"))
+    Y = torch.empty_like(X)
+    bad_y = [torch.empty(M, N, dtype=torch.float16, device="cuda"),       # dtype
+             torch.empty(M, N + 1, dtype=torch.bfloat16, device="cuda"),  # shape
+             torch.empty(M, N, dtype=torch.bfloat16),                     # host memory
+             torch.empty(N, M, dtype=torch.bfloat16, device="cuda").t()]  # columns strided
+    for y in bad_y:
+        with pytest.raises(ValueError):
+            nl.norm_fwd("layernorm", X, None, W, B, w.eps, y)
+    with pytest.raises(ValueError):
+        nl.norm_fwd("layernorm", X, None, W[:-1], B, w.eps, Y)
+    # row-strided views: the slices of a wider buffer
+    big = torch.zeros(M, 3 * N, dtype=torch.bfloat16, device="cuda")
+    big[:, N:2 * N] = X
+    out = torch.full((M, 2 * N), 7.0, dtype=torch.bfloat16, device="cuda")
+    nl.norm_fwd("layernorm", big[:, N:2 * N], None, W, B, w.eps, out[:, :N])
+    nl.norm_fwd("layernorm", X, None, W, B, w.eps, Y)
+    torch.cuda.synchronize()
+    assert torch.equal(out[:, :N].view(torch.int16), Y.view(torch.int16))
+    assert (out[:, N:] == 7.0).all()
