@@ -19,8 +19,8 @@ typedef uint16_t bf16_bits;
 typedef _Float16 f16_t;
 
 // Input loads and output stores of the streamed [M, N] tensors. Each element is touched once
-// per pass, so stores bypass the caches' allocate-on-write (nontemporal). Loads stay ordinary:
-// the split scheme re-reads its chunks and wants them cached.
+// per pass, so stores bypass the caches' allocate-on-write (nontemporal). ld_stream loads stay
+// ordinary: the looped and split schemes re-read their chunks and want them cached.
 #ifndef DLN_STORE_NT
 #define DLN_STORE_NT 1
 #endif
@@ -34,6 +34,14 @@ template <typename V> __device__ __forceinline__ V ld_stream(const V *p) {
 #else
   return *p;
 #endif
+}
+
+// Loads of data that a kernel reads exactly once (X, R, dY and dH in the wave and block
+// schemes, which hold their rows in registers): nontemporal. Measured on MI355X, cache-cold,
+// against ordinary loads: LayerNorm bf16 16384 x 4096 backward 76.6 -> 73.0 us, RMSNorm bf16
+// 32768 x 4096 backward 135.7 -> 129.5 us, residual RMSNorm 65536 x 7168 forward 646 -> 618 us.
+template <typename V> __device__ __forceinline__ V ld_once(const V *p) {
+  return __builtin_nontemporal_load(p);
 }
 
 template <typename V> __device__ __forceinline__ void st_stream(V *p, V v) {
@@ -115,6 +123,7 @@ template <typename T, int E> struct Acc {
   static constexpr bool B16 = sizeof(T) == 2; // bf16 or fp16
   typedef typename Words<NW>::type raw;
   __device__ static raw ld(const T *p) { return ld_stream(reinterpret_cast<const raw *>(p)); }
+  __device__ static raw ld_once(const T *p) { return dln::ld_once(reinterpret_cast<const raw *>(p)); }
   __device__ static raw ld_cached(const T *p) { return *reinterpret_cast<const raw *>(p); }
   __device__ static void st(T *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
   __device__ static void unpack(raw v, float *f) {
@@ -156,6 +165,7 @@ template <> struct Acc<float, 1> {
   static constexpr int EPV = 1;
   typedef float raw;
   __device__ static raw ld(const float *p) { return *p; }
+  __device__ static raw ld_once(const float *p) { return dln::ld_once(p); }
   __device__ static raw ld_cached(const float *p) { return *p; }
   __device__ static void st(float *p, raw v) { *p = v; }
   __device__ static void unpack(raw v, float *f) { f[0] = v; }
@@ -168,6 +178,7 @@ template <> struct Acc<bf16_bits, 1> {
   static constexpr int EPV = 1;
   typedef bf16_bits raw;
   __device__ static raw ld(const bf16_bits *p) { return *p; }
+  __device__ static raw ld_once(const bf16_bits *p) { return dln::ld_once(p); }
   __device__ static raw ld_cached(const bf16_bits *p) { return *p; }
   __device__ static void st(bf16_bits *p, raw v) { *p = v; }
   __device__ static void unpack(raw v, float *f) {
@@ -182,6 +193,9 @@ template <> struct Acc<f16_t, 1> {
   static constexpr int EPV = 1;
   typedef uint16_t raw; // the element's bits
   __device__ static raw ld(const f16_t *p) { return *reinterpret_cast<const raw *>(p); }
+  __device__ static raw ld_once(const f16_t *p) {
+    return dln::ld_once(reinterpret_cast<const raw *>(p));
+  }
   __device__ static raw ld_cached(const f16_t *p) { return *reinterpret_cast<const raw *>(p); }
   __device__ static void st(f16_t *p, raw v) { *reinterpret_cast<raw *>(p) = v; }
   __device__ static void unpack(raw v, float *f) { f[0] = (float)__builtin_bit_cast(f16_t, v); }

@@ -121,8 +121,8 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
         px[r][k] = A::zero();
         if (RESID) pr[r][k] = A::zero();
         if (rv && v < nacc) {
-          px[r][k] = A::ld(X + row * a.ldx + (int64_t)v * E);
-          if (RESID) pr[r][k] = A::ld(Rr + row * a.ldr + (int64_t)v * E);
+          px[r][k] = A::ld_once(X + row * a.ldx + (int64_t)v * E);
+          if (RESID) pr[r][k] = A::ld_once(Rr + row * a.ldr + (int64_t)v * E);
         }
       }
     }
@@ -340,14 +340,14 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         const int v = gm.t + k * gm.tt;
         if constexpr (CLAMP) {
           const int64_t off = (int64_t)(v < nacc ? v : nacc - 1) * E;
-          px[r][k] = A::ld(X + rowc * a.ldx + off);
-          pdy[r][k] = A::ld(DY + rowc * a.lddy + off);
+          px[r][k] = A::ld_once(X + rowc * a.ldx + off);
+          pdy[r][k] = A::ld_once(DY + rowc * a.lddy + off);
         } else {
           px[r][k] = A::zero();
           pdy[r][k] = A::zero();
           if (rv && v < nacc) {
-            px[r][k] = A::ld(X + rowc * a.ldx + (int64_t)v * E);
-            pdy[r][k] = A::ld(DY + rowc * a.lddy + (int64_t)v * E);
+            px[r][k] = A::ld_once(X + rowc * a.ldx + (int64_t)v * E);
+            pdy[r][k] = A::ld_once(DY + rowc * a.lddy + (int64_t)v * E);
           }
         }
       }
@@ -536,7 +536,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         const int64_t off = (int64_t)v * E;
         if (DH) {
           float hf[E];
-          A::unpack(A::ld(DH + row * a.lddh + off), hf);
+          A::unpack(A::ld_once(DH + row * a.lddh + off), hf);
 #pragma unroll
           for (int e = 0; e < E; ++e) dx[e] += hf[e];
         }

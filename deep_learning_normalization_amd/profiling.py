@@ -218,6 +218,118 @@ def drive(name, steps):
     torch.cuda.synchronize()
 
 
+# Counter passes for what bounds the streaming kernels (one rocprofv3 --pmc run each; a pass
+# stays within the per-block counter limits: 8 SQ, 4 TCC, 4 TCP, 2 TA, 2 GRBM).
+COUNTER_PASSES = {
+    "sq": ["SQ_WAVES", "SQ_WAVE_CYCLES", "SQ_BUSY_CYCLES", "SQ_LEVEL_WAVES",
+           "SQ_INST_LEVEL_VMEM", "SQ_INSTS_VMEM_RD", "SQ_INSTS_VMEM_WR", "SQ_WAIT_INST_ANY",
+           "GRBM_GUI_ACTIVE"],
+    "tcc": ["TCC_EA0_RDREQ_LEVEL_sum", "TCC_EA0_RDREQ_sum", "TCC_EA0_WRREQ_LEVEL_sum",
+            "TCC_EA0_WRREQ_sum", "GRBM_GUI_ACTIVE"],
+    "tcp": ["TCP_TCC_READ_REQ_LATENCY_sum", "TCP_TCC_READ_REQ_sum", "TCP_PENDING_STALL_CYCLES_sum",
+            "TA_BUSY_avr", "TA_ADDR_STALLED_BY_TC_CYCLES_sum", "GRBM_GUI_ACTIVE"],
+}
+
+
+def counters_drive(launches=20):
+    """The kernels the counter summary compares, `launches` times each with the cache-cold
+    rotation: the LayerNorm 16384 x 4096 fused backward and forward, the RMSNorm 32768 x 4096
+    fused backward, and the copy and triad probes."""
+    import torch
+    from deep_learning_normalization_amd import inputs, normlib as nl, probes, timing
+    nl.lib()
+    for w in (inputs.LN_BF16_16384x4096, inputs.rms_hidden(4096)):
+        rot = timing.Rotation(w, torch, nl)
+        for i in range(launches):
+            rot.bwd_fused(rot.sets[(i + rot.S // 2) % rot.S])
+            if w.kind == "layernorm":
+                rot.fwd(rot.sets[i % rot.S])
+        torch.cuda.synchronize()
+        rot.free()
+    nbytes = 256 << 20
+    bufs = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda") for _ in range(8)]
+    for i in range(launches):
+        probes.probe(2, 1, [bufs[(3 * i) % 8], bufs[(3 * i + 1) % 8]], [bufs[(3 * i + 2) % 8]],
+                     nbytes, 4, 1, 0)
+        probes.probe(1, 1, [bufs[(2 * i + 3) % 8]], [bufs[(2 * i + 4) % 8]], nbytes, 2, 1, 0)
+    torch.cuda.synchronize()
+
+
+def _pmc_rows(directory):
+    """{(kernel name, grid threads): {counter: [values per dispatch]}} of one --pmc run."""
+    path = _one(directory, "_counter_collection.csv")
+    per = {}
+    for r in csv.DictReader(open(path)):
+        key = (_name(r["Kernel_Name"]), int(r.get("Grid_Size", r.get("Grid_Size_X", 0)) or 0),
+               r.get("Dispatch_Id"))
+        per.setdefault(key, {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    out = {}
+    for (name, grid, _), cs in per.items():
+        d = out.setdefault((name, grid), {})
+        for c, v in cs.items():
+            d.setdefault(c, []).append(v)
+    return out
+
+
+def counters(root, out, cmd):
+    """Markdown summary of the counter passes under root/<pass>/ for the kernels of
+    counters_drive: occupancy, memory instructions in flight, DRAM requests in flight and their
+    latency."""
+    runs = {p: _pmc_rows(os.path.join(root, p)) for p in COUNTER_PASSES}
+
+    kernels = [("LayerNorm 16384x4096 fused backward", "team_bwd_kernel", "true, false"),
+               ("LayerNorm 16384x4096 forward", "team_fwd_kernel", None),
+               ("RMSNorm 32768x4096 fused backward", "team_bwd_kernel", "false, true"),
+               ("triad probe (2R1W)", "probe_kernel<2, 1", None),
+               ("copy probe (1R1W)", "probe_kernel<1, 1", None)]
+
+    def pick(run, sub, tail):
+        vals = {}
+        for (name, grid), cs in run.items():
+            if sub in name and (tail is None or tail in name):
+                for c, v in cs.items():
+                    vals.setdefault(c, []).extend(v)
+        return {c: statistics.median(v) for c, v in vals.items()}
+    lines = ["# What bounds the streaming kernels: rocprofv3 counters", "",
+             "command: %s" % cmd, "",
+             "Medians over the dispatches of each kernel. Derived columns: DRAM reads in "
+             "flight = TCC_EA0_RDREQ_LEVEL (summed over the L2 channels) / GRBM_GUI_ACTIVE "
+             "(summed over the 8 XCDs): a relative measure of the read requests outstanding "
+             "to memory; DRAM read latency = RDREQ_LEVEL / RDREQ in cycles; their ratio is "
+             "proportional to the read bandwidth; writes likewise; L2 read latency seen by the "
+             "vector caches = TCP_TCC_READ_REQ_LATENCY / TCP_TCC_READ_REQ. The SQ pass's "
+             "level counters (SQ_LEVEL_WAVES, SQ_INST_LEVEL_VMEM) read 0 or implausibly low on "
+             "this part and are listed raw only.", "",
+             "| kernel | GPU cycles (8 XCDs) | DRAM reads in flight | DRAM read latency | "
+             "reads in flight / latency | DRAM writes in flight | L2 read latency (TCP) | "
+             "TA busy (avg) | TCP pending-stall cycles |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for label, sub, tail in kernels:
+        sq, tcc, tcp = (pick(runs[p], sub, tail) for p in ("sq", "tcc", "tcp"))
+        if not sq or not tcc:
+            continue
+        g = tcc.get("GRBM_GUI_ACTIVE") or sq.get("GRBM_GUI_ACTIVE") or float("nan")
+        f = lambda a, b: a / b if b else float("nan")  # noqa: E731
+        rin = f(tcc.get("TCC_EA0_RDREQ_LEVEL_sum", 0), g)
+        rlat = f(tcc.get("TCC_EA0_RDREQ_LEVEL_sum", 0), tcc.get("TCC_EA0_RDREQ_sum", 0))
+        lines.append("| %s | %.0f | %.0f | %.0f | %.2f | %.0f | %.0f | %.0f | %.3g |"
+                     % (label, g, rin, rlat, f(rin, rlat),
+                        f(tcc.get("TCC_EA0_WRREQ_LEVEL_sum", 0), g),
+                        f(tcp.get("TCP_TCC_READ_REQ_LATENCY_sum", 0),
+                          tcp.get("TCP_TCC_READ_REQ_sum", 0)),
+                        tcp.get("TA_BUSY_avr", float("nan")),
+                        tcp.get("TCP_PENDING_STALL_CYCLES_sum", float("nan"))))
+    lines += ["", "Raw medians:", ""]
+    for label, sub, tail in kernels:
+        for p in COUNTER_PASSES:
+            d = pick(runs[p], sub, tail)
+            if d:
+                lines.append("- %s, %s pass: %s" % (label, p, ", ".join(
+                    "%s %.6g" % (k, v) for k, v in sorted(d.items()))))
+    with open(out, "w") as fh:
+        fh.write("\n".join(lines) + "\n")
+
+
 def _kernel_rows(trace_dir):
     rows = list(csv.DictReader(open(_one(trace_dir, "_kernel_trace.csv"))))
     per = {}
@@ -357,12 +469,21 @@ def main():
     wk.add_argument("--root", required=True)
     wk.add_argument("--out", required=True)
     wk.add_argument("--cmd", required=True)
+    sub.add_parser("counters-drive")
+    cn = sub.add_parser("counters")
+    cn.add_argument("--root", required=True)
+    cn.add_argument("--out", required=True)
+    cn.add_argument("--cmd", required=True)
     sm = sub.add_parser("summarize")
     sm.add_argument("--root", required=True, help="the capture's output folder")
     sm.add_argument("--out", required=True, help="where the summaries go")
     a = ap.parse_args()
     if a.what == "summarize":
         summarize(a.root, a.out)
+    elif a.what == "counters-drive":
+        counters_drive()
+    elif a.what == "counters":
+        counters(a.root, a.out, a.cmd)
     elif a.what == "drive":
         drive(a.workload, a.steps)
     elif a.what == "workloads":
