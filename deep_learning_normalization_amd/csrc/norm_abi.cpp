@@ -85,7 +85,11 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   const int64_t lds[] = {ld.x, ld.dy, dH ? ld.dh : N, ld.dx, dR ? ld.dr : N};
   const int align = dln::fold_stride_align(dln::common_align(ptrs, 6), lds, 5,
                                            dln::act_elem_size(dtype));
-  st = dln::make_plan(kind, dtype, NORM_PASS_BWD, M, N, 0, align, cu, dln::tuning(), plan);
+  const void *acts[] = {X, dY, dH, dX, dR};
+  int phase0 = -1, dphase = -1;
+  dln::common_phase(acts, lds, 5, dln::act_elem_size(dtype), &phase0, &dphase);
+  st = dln::make_plan(kind, dtype, NORM_PASS_BWD, M, N, 0, align, phase0, dphase, cu,
+                      dln::tuning(), plan);
   if (st != NORM_OK) return st;
   st = ws_ok(*plan, workspace, workspace_bytes);
   if (st != NORM_OK) return st;
@@ -121,7 +125,10 @@ norm_status_t bwd_setup(norm_kind_t kind, const void *X, const void *dY, const v
   b.lddr = ld.dr;
   b.M = M;
   b.N = (int32_t)N;
-  b.nacc = (int32_t)(N / plan->epv);
+  b.nacc = (int32_t)plan->nacc;
+  b.period = plan->period;
+  b.phase0 = phase0 < 0 ? 0 : phase0;
+  b.dphase = dphase < 0 ? 0 : dphase;
   b.chunks = plan->chunks;
   b.chunk_acc = (int32_t)(plan->chunk_elems / plan->epv);
   b.partials = plan->partials;
@@ -289,8 +296,12 @@ norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const v
   const int64_t lds[] = {ld.x, R ? ld.r : N, ld.y, H ? ld.h : N};
   const int align = dln::fold_stride_align(dln::common_align(ptrs, 6), lds, 4,
                                            dln::act_elem_size(dtype));
+  const void *acts[] = {X, R, Y, H};
+  int phase0 = -1, dphase = -1;
+  dln::common_phase(acts, lds, 4, dln::act_elem_size(dtype), &phase0, &dphase);
   dln::Plan p;
-  st = dln::make_plan(kind, dtype, pass, M, N, R != nullptr, align, cu, dln::tuning(), &p);
+  st = dln::make_plan(kind, dtype, pass, M, N, R != nullptr, align, phase0, dphase, cu,
+                      dln::tuning(), &p);
   if (st != NORM_OK) return st;
   st = ws_ok(p, workspace, workspace_bytes);
   if (st != NORM_OK) return st;
@@ -310,7 +321,10 @@ norm_status_t fwd_launch(norm_kind_t kind, const void *X, const void *R, const v
   a.ldh = ld.h;
   a.M = M;
   a.N = (int32_t)N;
-  a.nacc = (int32_t)(N / p.epv);
+  a.nacc = (int32_t)p.nacc;
+  a.period = p.period;
+  a.phase0 = phase0 < 0 ? 0 : phase0;
+  a.dphase = dphase < 0 ? 0 : dphase;
   a.chunks = p.chunks;
   a.chunk_acc = (int32_t)(p.chunk_elems / p.epv);
   a.layernorm = kind == NORM_LAYERNORM ? 1 : 0;
@@ -469,7 +483,10 @@ norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
   if (!out) return NORM_ERR_INVALID_ARG;
   dln::Plan p;
   norm_status_t st =
-      dln::make_plan(kind, dtype, pass, M, N, residual, align, cu_count, dln::tuning(), &p);
+      dln::make_plan(kind, dtype, pass, M, N, residual, align, align >= 16 ? 0 : -1,
+                     (int)((N * (int64_t)dln::act_elem_size(dtype)) % 16 /
+                           (int64_t)dln::act_elem_size(dtype)),
+                     cu_count, dln::tuning(), &p);
   if (st != NORM_OK) return st;
   norm_plan_t o{};
   o.scheme = p.scheme;
@@ -487,6 +504,7 @@ norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
   o.partials = p.partials;
   o.workspace_bytes = p.ws_bytes;
   o.exchange_row_groups = p.xchg ? p.xrow_groups : 0;
+  o.phase_classes = p.period;
   *out = o;
   return NORM_OK;
 }

@@ -123,7 +123,9 @@ template <typename T, int E> struct Acc {
   static constexpr bool B16 = sizeof(T) == 2; // bf16 or fp16
   typedef typename Words<NW>::type raw;
   __device__ static raw ld(const T *p) { return ld_stream(reinterpret_cast<const raw *>(p)); }
-  __device__ static raw ld_once(const T *p) { return dln::ld_once(reinterpret_cast<const raw *>(p)); }
+  __device__ static raw ld_once(const T *p) {
+    return dln::ld_once(reinterpret_cast<const raw *>(p));
+  }
   __device__ static raw ld_cached(const T *p) { return *reinterpret_cast<const raw *>(p); }
   __device__ static void st(T *p, raw v) { st_stream(reinterpret_cast<raw *>(p), v); }
   __device__ static void unpack(raw v, float *f) {
@@ -231,6 +233,8 @@ template <typename T, int EV> struct WAcc<T, T, EV> {
   typename A::raw r;
   __device__ void zero() { r = A::zero(); }
   __device__ void load(const T *p) { r = A::ld_cached(p); }
+  // E weights from p at any element alignment (one unaligned access)
+  __device__ void load_any(const T *p) { __builtin_memcpy(&r, p, sizeof(r)); }
   __device__ void get(float *f) const { A::unpack(r, f); }
   __device__ void settle() { dln::settle(r); }
   __device__ static void store(T *p, const float *f) { A::st(p, A::pack(f)); }
@@ -254,6 +258,7 @@ template <int EV> struct WAccF32 {
       for (int j = 0; j < LW; ++j) w[LW * i + j] = __builtin_bit_cast(float, word(v, j));
     }
   }
+  __device__ void load_any(const float *p) { __builtin_memcpy(w, p, sizeof(w)); }
   __device__ void get(float *f) const {
 #pragma unroll
     for (int e = 0; e < E; ++e) f[e] = w[e];

@@ -36,6 +36,10 @@ struct FwdArgs {
   int64_t M;
   int32_t N;
   int32_t nacc;       // accesses per row (N / epv)
+  int32_t period;     // wave/block at the full width, rows off 16-byte boundaries: the number
+                      // of row phase classes P (1, 2, 4 or 8); 0 for aligned rows
+  int32_t phase0;     // with period: elements by which row 0 starts past a 16-byte boundary
+  int32_t dphase;     // with period: the same for the step from one row to the next
   int64_t chunks;     // split
   int32_t chunk_acc;  // split: accesses per chunk
   int32_t layernorm;  // 1 LayerNorm, 0 RMSNorm
@@ -69,6 +73,9 @@ struct BwdArgs {
   int64_t M;
   int32_t N;
   int32_t nacc;
+  int32_t period;     // as in FwdArgs
+  int32_t phase0;
+  int32_t dphase;
   int64_t chunks;
   int32_t chunk_acc;
   int64_t partials;

@@ -185,13 +185,17 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
     if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
     g_tuning.xchg_withhold = (int)v;
     return NORM_OK;
+  case NORM_TUNE_UNALIGNED:
+    if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
+    g_tuning.unaligned = (int)v;
+    return NORM_OK;
   default: return NORM_ERR_INVALID_ARG;
   }
 }
 
 norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
-                        int64_t N, int residual, int align, int cu, const Tuning &t,
-                        Plan *out) {
+                        int64_t N, int residual, int align, int phase0, int dphase, int cu,
+                        const Tuning &t, Plan *out) {
   if (!out || !valid_kind(kind) || !valid_dtype(dtype) ||
       (pass != NORM_PASS_FWD && pass != NORM_PASS_BWD && pass != NORM_PASS_STATS) || M < 0 ||
       N <= 0 || N > kMaxN ||
@@ -209,13 +213,59 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       p.epv = e;
       break;
     }
+  // Rows off 16-byte boundaries (their length, stride or start) with every [M, N] tensor at
+  // one phase: the wave and block schemes still take 16-byte accesses, each workgroup on the
+  // rows of one phase class (see the team kernels), in place of element-wise and of 8- and
+  // 4-byte accesses unless tuned off (measured on MI355X against 8- / 4-byte accesses:
+  // LayerNorm 16384 x 4100 forward 61 / 57 us, backward 96 / 96-100 us; 16384 x 4098 61 / 66,
+  // 96 / 145 us; RMSNorm 32768 x 4100 92 / 105, 140 / 187 us; LayerNorm 65536 x 1002 56 / 56,
+  // 75 / 80 us).
+  int64_t nal = 0;
+  int period = 0;
+  // (rows of at least one access: a row's edge accesses load its first and last 16 bytes)
+  if (p.epv < ev && N >= ev && t.unaligned != 0 && phase0 >= 0 && dphase >= 0) {
+    int g = ev; // gcd(dphase, ev): rows repeat their phase every ev / g rows
+    if (dphase % ev) {
+      int x = dphase % ev, y = ev;
+      while (x) {
+        const int r = y % x;
+        y = x;
+        x = r;
+      }
+      g = y;
+    }
+    period = ev / g;
+    for (int c = 0; c < period; ++c) {
+      const int pe = (int)((phase0 + (int64_t)c * dphase) % ev);
+      const int64_t n = cdiv(N + pe, ev);
+      if (n > nal) nal = n;
+    }
+    // the scheme a full-width row of this length takes (below)
+    int sch = t.scheme == NORM_SCHEME_LOOP && !bwd ? NORM_SCHEME_AUTO : t.scheme;
+    if (sch == NORM_SCHEME_AUTO)
+      sch = N <= kWaveMaxRow ? NORM_SCHEME_WAVE
+            : nal <= (bwd ? 1024 : 2048) ? NORM_SCHEME_BLOCK
+                                         : NORM_SCHEME_SPLIT;
+    // (the wave backward over phase classes is compiled up to 4 accesses per thread only: its
+    // 8-access form gave wrong results on MI355X, cause not found, and is never launched)
+    const bool wave_ok = sch == NORM_SCHEME_WAVE && !(bwd && nal > 4 * 64);
+    if (wave_ok || sch == NORM_SCHEME_BLOCK) {
+      p.epv = ev;
+      p.period = period;
+    }
+  }
   p.vector = p.epv > 1 ? 1 : 0;
   p.scale = p.vector ? ev / p.epv : 1;
   p.access_bytes = (int)((size_t)p.epv * elem_size(dtype));
   const bool vec = p.vector != 0;
   const int wc = !vec ? kElem : p.scale == 1 ? kFull : kNarrow;
   const int sc = p.scale;
-  const int64_t nacc = N / p.epv;
+  const int64_t nacc = p.period ? nal : N / p.epv;
+  p.nacc = nacc;
+  // rows of the largest phase class (every row without classes); grids count its workgroups
+  // and are multiplied by the classes at the end
+  const int64_t PC = p.period ? p.period : 1;
+  const int64_t Mc = cdiv(M > 0 ? M : 1, PC);
   // accesses per row in full-width units: the narrow paths size teams and pick schemes as the
   // 16-byte path would for the same row
   const int64_t nacc_eq = cdiv(nacc, sc);
@@ -252,11 +302,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.threads = kWaveThreads;
     p.lb = kWaveThreads;
     p.team_threads = 64;
-    const int64_t groups = cdiv(Mm, (int64_t)(kWaveThreads / 64) * rows);
+    const int64_t groups = cdiv(Mc, (int64_t)(kWaveThreads / 64) * rows);
     // 8- and 4-byte forwards stream better from 16 workgroups per CU (measured on MI355X:
     // LayerNorm 65536 x 1002 57.8 -> 53.4 us)
     const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (bwd ? 2 : sc > 1 ? 16 : 8);
-    p.grid = groups < cu * gpc ? groups : cu * gpc;
+    const int64_t cap = cu * gpc / PC > 0 ? cu * gpc / PC : 1; // per phase class
+    p.grid = PC * (groups < cap ? groups : cap);
     p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_BLOCK) {
     static const int vmenu[] = {1, 2, 4, 8};
@@ -276,10 +327,17 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
           cand = t.team_threads;
         }
         // forward: teams up to 256 threads, or 512 with four accesses per thread rather than
-        // eight (measured on MI355X: 12288-16384 bf16 rows run 10-20% faster)
-        const int fwd_limit = v >= 4 ? 2 * kBlockTeamTarget : kBlockTeamTarget;
+        // eight (measured on MI355X: 12288-16384 bf16 rows run 10-20% faster). Rows over phase
+        // classes, which often need one access past a power of two (N = 4097: 513), take two
+        // accesses per thread up to 384 threads and, in the backward, one up to 512 (measured on
+        // MI355X, LayerNorm 16384 x 4097: forward 4 x 192 threads 68 us, 2 x 320 62 us;
+        // backward 1 x 576 121 us, 2 x 320 with two rows 96 us)
+        const bool part = p.period > 0;
+        const int fwd_limit = v >= 4 ? 2 * kBlockTeamTarget
+                              : (part && v == 2) ? kBlockTeamTarget + 128 : kBlockTeamTarget;
+        const int bwd_limit = part && v == 1 ? 512 : kBlockTeamTargetBwd;
         const int limit = (pass_i == 0 && !use_override)
-                              ? (vec ? (bwd ? kBlockTeamTargetBwd : fwd_limit) : 1024)
+                              ? (vec ? (bwd ? bwd_limit : fwd_limit) : 1024)
                               : 1024;
         if (cand > limit) continue;
         // Backward teams of 513-768 threads with one full-width access per thread are compiled
@@ -294,7 +352,8 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
         // GPU at 640 threads: RMSNorm 32768 x 5120 197 against 202 us; LayerNorm 32768 x 5120
         // 228 against 188 us, fp32 32768 x 2560 200 against 174 us)
         const int two_upto = kind == NORM_RMSNORM ? 768 : 512;
-        int r = t.rows > 0 ? t.rows : ((bwd && v == 1 && cand <= two_upto) ? 2 : 1);
+        const bool two = bwd && ((v == 1 && cand <= two_upto) || (part && v == 2 && cand <= 384));
+        int r = t.rows > 0 ? t.rows : (two ? 2 : 1);
         const bool res = residual != 0;
         auto ok = [&](int rr) {
           return block_menu(wc, bwd, v, rr, lb, sc, res) &&
@@ -327,25 +386,34 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.team_threads = tt;
     p.threads = tt * teams;
     p.lb = vec ? (teams > 1 ? lb_of(p.threads) : lb_pick) : 1024;
-    const int64_t groups = cdiv(Mm, (int64_t)rows * teams);
+    const int64_t groups = cdiv(Mc, (int64_t)rows * teams);
+    auto capped = [&](int64_t gpc) { // persistent: gpc workgroups per CU over all classes
+      const int64_t cap = cu * gpc / PC > 0 ? cu * gpc / PC : 1;
+      return PC * (groups < cap ? groups : cap);
+    };
     if (bwd) {
       // Backward: persistent, about 1024 16-byte accesses per tensor in flight per CU; every
       // workgroup writes one partial row, so fewer, longer-lived workgroups.
       const int64_t load = (int64_t)p.threads * vpt * rows; // full-width units
-      const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1);
-      p.grid = groups < cu * gpc ? groups : cu * gpc;
-    } else if (t.grid_per_cu > 0 || stats || sc > 1) {
+      p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1));
+    } else if (t.grid_per_cu > 0 || stats || sc > 1 || p.period) {
       // the statistics pass alone, with no stores to overlap, streams best from a persistent
       // grid of 8 workgroups per CU (measured on MI355X: LayerNorm 16384 x 4096 30.6 -> 28.7 us);
       // 8- and 4-byte forwards from 16 (LayerNorm 16384 x 4100 54.4 -> 49.8 us, 16384 x 4098
-      // 68.8 -> 60.4 us)
-      const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : stats ? 8 : 16;
-      p.grid = groups < cu * gpc ? groups : cu * gpc;
+      // 68.8 -> 60.4 us); forwards over phase classes, whose workgroups gather their weights
+      // first, from enough workgroups for about 12 wavefronts per CU (measured on MI355X,
+      // LayerNorm 16384 x 2049 / 3073 / 4097 with 3 / 4 / 5 wavefronts each: best at 4 / 3 / 2
+      // workgroups per CU, 35 / 44 / 62 us, against 50 / 54 / 108 us from short-lived ones)
+      // (4 accesses per thread take about 180 VGPRs, so 2 wavefronts per SIMD: 8 per CU;
+      // RMSNorm 16384 x 8185 99 us from 2 workgroups of 4 wavefronts, 108 us from 3)
+      const int64_t waves = (p.threads + 63) / 64, budget = vpt >= 4 ? 8 : 12;
+      const int64_t gpc_part = budget / waves > 0 ? budget / waves : 1;
+      p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : stats ? 8 : p.period ? gpc_part : 16);
     } else {
       // Forward (measured on MI355X): short-lived workgroups of two row groups each (the second
       // group's loads overlap the first's reductions), one for the residual variant, whose
       // four streams per row already keep enough requests in flight.
-      p.grid = residual ? groups : cdiv(groups, 2);
+      p.grid = PC * (residual ? groups : cdiv(groups, 2));
     }
     p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_LOOP) {
@@ -457,14 +525,22 @@ norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t 
   // Size for every pointer alignment (each may pick another access width). A tuning override
   // may leave a narrower width without a kernel; a call with such pointers then fails with
   // NORM_ERR_UNSUPPORTED anyway, so only the 16-byte-aligned plan has to succeed.
+  // (phase classes: 1, 2, 4 or 8 classes, their grids and row lengths differing; every phase
+  // pair that gives a class count is tried, with the alignments that still take that mode)
   Plan p;
-  norm_status_t s = make_plan(kind, dtype, pass, M, N, residual, 16, cu, t, &p);
+  norm_status_t s = make_plan(kind, dtype, pass, M, N, residual, 16, 0, 0, cu, t, &p);
   if (s != NORM_OK) return s;
   size_t best = p.ws_bytes;
-  for (int align : {8, 4, 2, 1})
-    if (make_plan(kind, dtype, pass, M, N, residual, align, cu, t, &p) == NORM_OK &&
-        p.ws_bytes > best)
-      best = p.ws_bytes;
+  // (a row step of d elements gives the classes of gcd(d, epv): steps 0, 1, 2 and 4 cover them)
+  const int ev = vec_epv(dtype);
+  for (int align : {16, 8, 4, 2, 1})
+    for (int ph0 = -1; ph0 < ev; ++ph0)
+      for (int dph : {-1, 0, 1, 2, 4})
+        if (dph < ev &&
+            make_plan(kind, dtype, pass, M, N, residual, align, ph0, dph, cu, t, &p) ==
+                NORM_OK &&
+            p.ws_bytes > best)
+          best = p.ws_bytes;
   *bytes = best;
   return NORM_OK;
 }
@@ -608,6 +684,30 @@ int fold_stride_align(int align, const int64_t *ld, int n, size_t elem_bytes) {
   uintptr_t bits = (uintptr_t)(align > 0 ? align : 1);
   for (int i = 0; i < n; ++i) bits |= (uintptr_t)((size_t)ld[i] * elem_bytes);
   return (int)(bits & (~bits + 1));
+}
+
+void common_phase(const void *const *ptrs, const int64_t *ld, int n, size_t elem_bytes,
+                  int *phase0, int *dphase) {
+  int b = -1, d = -1;
+  for (int i = 0; i < n; ++i) {
+    if (!ptrs[i]) continue;
+    const uintptr_t a = (uintptr_t)ptrs[i];
+    if (a % elem_bytes) { // not even element-aligned
+      b = d = -2;
+      break;
+    }
+    const int bi = (int)((a % 16) / elem_bytes);
+    const int di = (int)((((uint64_t)ld[i] * elem_bytes) % 16) / elem_bytes);
+    if (b == -1) {
+      b = bi;
+      d = di;
+    } else if (bi != b || di != d) {
+      b = d = -2;
+      break;
+    }
+  }
+  *phase0 = b < 0 ? -1 : b;
+  *dphase = d < 0 ? -1 : d;
 }
 
 size_t act_elem_size(norm_dtype_t d) { return elem_size(d); }

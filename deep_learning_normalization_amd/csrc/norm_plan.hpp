@@ -16,6 +16,10 @@ struct Plan {
   int scheme = NORM_SCHEME_BLOCK;
   int vector = 1;          // vector accesses of whole 32-bit words (1) or element-wise (0)
   int epv = 8;             // elements per access
+  int64_t nacc = 0;        // accesses per row: N / epv; with phase classes the most any class
+                           // needs, ceil((N + pe) / epv)
+  int period = 0;          // wave/block at the full width, rows off 16-byte boundaries: row phase
+                           // classes P (the grid is a multiple of P); 0 for aligned rows
   int scale = 1;           // full-width elements (16 bytes) / epv on the vector paths: 1, 2, 4
   int access_bytes = 16;   // bytes per access: 16, 8 or 4, or the element size
   int threads = 256;       // workgroup size
@@ -80,16 +84,25 @@ struct Tuning {
   int xchg = -1;
   int64_t xchg_polls = -1;
   int xchg_withhold = -1;
+  int unaligned = -1;
 };
 
 const Tuning &tuning();
 norm_status_t set_tuning(norm_tune_t key, int64_t value);
 
 // align: the largest power of two, up to 16, that divides the address of every tensor the call
-// touches (16 for buffers from an allocator; 1 when unknown or odd).
+// touches and (times the element size) every row stride (16 for buffers from an allocator; 1
+// when unknown or odd). phase0 / dphase: when every [M, N] tensor of the call starts the same
+// number of elements past a 16-byte boundary and its row stride moves the start by the same
+// number (modulo 16 bytes), those two numbers in elements; else -1.
 norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
-                        int64_t N, int residual, int align, int cu_count, const Tuning &t,
-                        Plan *out);
+                        int64_t N, int residual, int align, int phase0, int dphase, int cu_count,
+                        const Tuning &t, Plan *out);
+
+// The common phase of a call's [M, N] tensors (pointers and row strides, nullptr entries
+// ignored) in elements of elem_bytes: writes phase0 and dphase as make_plan takes them.
+void common_phase(const void *const *ptrs, const int64_t *ld, int n, size_t elem_bytes,
+                  int *phase0, int *dphase);
 
 // Largest workspace any pointer alignment can need for this call on cu_count CUs.
 norm_status_t workspace_bytes(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,

@@ -17,6 +17,22 @@
 //   paras. 8-10 -- one fused pass produces dX and per-block partial column sums (no atomics;
 //               several rows per block), and a second pass consolidates the partials;
 //   para. 12 -- several rows in flight per team (the software-pipelining knob).
+// Rows that do not start on 16-byte boundaries (an odd N, strides or pointers of that kind) keep
+// 16-byte accesses (the PART instantiations, launched for such rows only, so the others compile
+// without this code). With all activation tensors at one phase (the same address and stride
+// modulo 16 bytes), row r starts pe(r) elements past a boundary, and pe(r) depends only on
+// r mod P (P = 1, 2, 4 or 8 classes). Each workgroup takes the rows of one class, so its pe is
+// fixed: access v of a row covers columns v * E - pe ... v * E - pe + E - 1, aligned in memory,
+// except the first and the last access, which cover the row's first and last E columns (in
+// bounds, possibly unaligned; they overlap their neighbours). Every lane loads, computes and
+// stores all E columns of its access with its weights gathered once at those columns; a 0/1
+// factor per element, fixed per lane for the workgroup, keeps the columns an edge access shares
+// with its neighbour (and accesses past the row's end) out of the row sums and the dW / dB sums,
+// and the shared columns are stored twice with the same value (the same instructions on the same
+// inputs). So the rows take no branch and no element-wise access: measured on MI355X, a branch
+// around loads or around values of loads in flight makes the compiler wait for every load in
+// flight (LayerNorm 16384 x 4097 forward 240 us), and shifting the edge elements into an aligned
+// grid costs the VALU time these kernels do not have (they run 60-75% VALU-busy).
 // Memory: every [M, N] element moves through 16-byte coalesced accesses, exactly once per pass
 // (web page "Otimização de Performance de GPU: Maximizando Throughput para Treinamento e
 // Inferência de LLM", introl.com, sections on memory bandwidth and on kernel fusion), and all
@@ -64,25 +80,88 @@ struct GroupRange {
   int64_t first, step, end;
 };
 __device__ __forceinline__ GroupRange group_range(int64_t M, int64_t rows_per_group,
-                                                  int blocked) {
+                                                  int blocked, int64_t bid, int64_t nb) {
   const int64_t groups = (M + rows_per_group - 1) / rows_per_group;
-  if (!blocked) return GroupRange{(int64_t)blockIdx.x, (int64_t)gridDim.x, groups};
-  const int64_t per = (groups + gridDim.x - 1) / gridDim.x;
-  const int64_t first = (int64_t)blockIdx.x * per;
+  if (!blocked) return GroupRange{bid, nb, groups};
+  const int64_t per = (groups + nb - 1) / nb;
+  const int64_t first = bid * per;
   return GroupRange{first, 1, first + per < groups ? first + per : groups};
 }
 
+// The rows a workgroup walks and where their accesses fall. Without PART: every row, accesses
+// v * E ... v * E + E - 1 from the row start. With PART: the rows of class blockIdx.x mod P
+// (row = cls + P * i for i < Mv), workgroup blockIdx.x / P of gridDim.x / P on them; their
+// inner accesses start pe elements before their aligned block, nal accesses per row (see win).
+template <int E, bool PART> struct RowPhase {
+  int P = 1, cls = 0, pe = 0, nal = 0, lastn = E, n = 0;
+  int64_t Mv = 0, bid = 0, nb = 1, m = 0;
+  __device__ RowPhase(int nacc, int64_t M, int N, int period, int phase0, int dphase) {
+    n = N;
+    m = M;
+    if constexpr (PART) {
+      P = period;
+      cls = (int)(blockIdx.x % (unsigned)P);
+      bid = blockIdx.x / (unsigned)P;
+      nb = gridDim.x / (unsigned)P;
+      pe = (phase0 + cls * dphase) & (E - 1);
+      nal = (N + pe + E - 1) / E;
+      lastn = N + pe - (nal - 1) * E;
+      Mv = M > cls ? (M - cls + P - 1) / P : 0;
+    } else {
+      (void)N, (void)period, (void)phase0, (void)dphase;
+      nal = nacc;
+      Mv = M;
+      bid = blockIdx.x;
+      nb = gridDim.x;
+    }
+  }
+  __device__ int64_t row(int64_t i) const { return PART ? cls + (int64_t)P * i : i; }
+  // a row of the tensor to load from for row index i of this workgroup, valid or not (PART
+  // loads unconditionally: rows past the class's last read a real row, masked afterwards)
+  __device__ int64_t load_row(int64_t i, bool valid) const {
+    if (valid) return row(i);
+    const int64_t r = row(Mv > 0 ? Mv - 1 : 0);
+    return r < m ? r : m - 1;
+  }
+  // element offset, from the row's start, of the E columns access v loads and stores: v * E
+  // without PART; with PART v * E - pe (aligned) for the inner accesses, 0 and N - E (N >= E)
+  // for the first and the last
+  __device__ int64_t win(int v) const {
+    if constexpr (!PART) return (int64_t)v * E;
+    // (arithmetic rather than a choice, which the compiler turns into a branch around the load)
+    const int o = v * E - pe; // N < 2^31
+    const int first = v == 0, last = v == nal - 1;
+    return (int64_t)(o + first * pe + last * (n - E - o - first * pe));
+  }
+  // 1 for element e of access v if this access owns its column, 0 if the neighbouring access
+  // owns it (the first access's last pe columns, the last access's first E - lastn) or v is past
+  // the row's end
+  __device__ float own(int v, int e) const {
+    if constexpr (!PART) return 1.0f;
+    const int olo = v == nal - 1 ? E - lastn : 0;
+    const int ohi = v >= nal ? 0 : v == 0 ? E - pe : E;
+    return (e >= olo && e < ohi) ? 1.0f : 0.0f;
+  }
+  // weights at access v's columns (once per workgroup; zero past the row's end)
+  template <typename WA, typename TW> __device__ void gather(WA &w, const TW *p, int v) const {
+    w.load_any(p + win(v < nal ? v : nal - 1));
+    if (v >= nal) w.zero();
+  }
+};
+
 // ---- forward ------------------------------------------------------------------------------
 
-template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE, bool RESID>
+template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE, bool RESID,
+          bool PART = false>
 __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_threads) {
   using A = Acc<T, EV>;
   using raw = typename A::raw;
   constexpr int E = A::EPV;
   __shared__ __align__(16) float red[RED_FLOATS];
   const TeamGeom gm = team_geom<WAVE>(team_threads);
-  const int nacc = a.nacc;
-  const int64_t M = a.M;
+  const RowPhase<E, PART> ph(a.nacc, a.M, a.N, a.period, a.phase0, a.dphase);
+  const int nacc = ph.nal;
+  const int64_t M = ph.Mv; // rows walked below are indices among this workgroup's rows
   const T *__restrict__ X = static_cast<const T *>(a.x);
   const T *__restrict__ Rr = static_cast<const T *>(a.r);
   const TW *__restrict__ W = static_cast<const TW *>(a.w);
@@ -91,13 +170,23 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
   T *__restrict__ H = static_cast<T *>(a.h);
 
   float w[VPT][E], b[VPT][E];
+  float own[PART ? VPT : 1][E]; // see RowPhase::own
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = gm.t + k * gm.tt;
+    if constexpr (PART) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) own[k][e] = ph.own(v, e);
+    }
     WAcc<T, TW, EV> rw, rb;
     rw.zero();
     rb.zero();
-    if (W && v < nacc) { // no weight: the statistics-only pass
+    if constexpr (PART) { // the class's columns (once per workgroup)
+      if (W) {
+        ph.gather(rw, W, v);
+        if (Bb) ph.gather(rb, Bb, v);
+      }
+    } else if (W && v < nacc) { // no weight: the statistics-only pass
       rw.load(W + (int64_t)v * E);
       if (Bb) rb.load(Bb + (int64_t)v * E);
     }
@@ -114,13 +203,20 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = live && row0 + r < M;
-      const int64_t row = row0 + r;
+      const int64_t row = ph.row(row0 + r);
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
-        px[r][k] = A::zero();
-        if (RESID) pr[r][k] = A::zero();
-        if (rv && v < nacc) {
+        if constexpr (!PART) {
+          px[r][k] = A::zero();
+          if (RESID) pr[r][k] = A::zero();
+        }
+        if constexpr (PART) { // every slot loads (see RowPhase::load_row and own)
+          const int64_t rl = ph.load_row(row0 + r, rv);
+          const int64_t o = ph.win(v < nacc ? v : nacc - 1);
+          px[r][k] = A::ld_once(X + rl * a.ldx + o);
+          if (RESID) pr[r][k] = A::ld_once(Rr + rl * a.ldr + o);
+        } else if (rv && v < nacc) {
           px[r][k] = A::ld_once(X + row * a.ldx + (int64_t)v * E);
           if (RESID) pr[r][k] = A::ld_once(Rr + row * a.ldr + (int64_t)v * E);
         }
@@ -128,7 +224,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
     }
   };
   int slot = 0;
-  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
+  const GroupRange gr = group_range(M, rows_per_group, a.blocked, ph.bid, ph.nb);
   int64_t g = gr.first;
   issue(g, g < gr.end);
 #pragma unroll
@@ -155,7 +251,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
       for (int r = 0; r < ROWS; ++r) {
         const bool rv = row0 + r < M;
-        const int64_t hbase = (row0 + r) * a.ldh;
+        const int64_t hbase = ph.row(row0 + r) * a.ldh;
 #pragma unroll
         for (int k = 0; k < VPT; ++k) {
           A::unpack(rx[r][k], x[r][k]);
@@ -168,7 +264,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
             const raw hp = A::pack(f);
             A::unpack(hp, x[r][k]);
             const int v = gm.t + k * gm.tt;
-            if (rv && v < nacc) A::st(H + hbase + (int64_t)v * E, hp);
+            if (rv && v < nacc) A::st(H + hbase + ph.win(v), hp);
           }
         }
       }
@@ -187,7 +283,10 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
         for (int k = 0; k < VPT; ++k)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc += x[r][k][e];
+          for (int e = 0; e < E; ++e) {
+            if constexpr (PART) acc = __builtin_fmaf(x[r][k][e], own[k][e], acc);
+            else acc += x[r][k][e];
+          }
         s[r] = acc;
       }
       team_sum<ROWS, (WAVE ? 1 : LB / 64)>(s, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
@@ -203,7 +302,9 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
           const bool in = gm.t + k * gm.tt < nacc;
 #pragma unroll
           for (int e = 0; e < E; ++e) {
-            const float d = in ? x[r][k][e] - mean1[r] : 0.0f;
+            float d;
+            if constexpr (PART) d = (x[r][k][e] - mean1[r]) * own[k][e];
+            else d = in ? x[r][k][e] - mean1[r] : 0.0f;
             q += d * d;
             c += d;
           }
@@ -227,7 +328,10 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
         for (int k = 0; k < VPT; ++k)
 #pragma unroll
-          for (int e = 0; e < E; ++e) acc += x[r][k][e] * x[r][k][e];
+          for (int e = 0; e < E; ++e) {
+            if constexpr (PART) acc += (x[r][k][e] * own[k][e]) * x[r][k][e];
+            else acc += x[r][k][e] * x[r][k][e];
+          }
         q[r] = acc;
       }
       team_sum<ROWS, (WAVE ? 1 : LB / 64)>(q, red, slot, gm.waves, gm.wave0, gm.wave, gm.lane);
@@ -242,8 +346,8 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      const int64_t row = row0 + r;
-      if (row >= M) continue;
+      if (row0 + r >= M) continue;
+      const int64_t row = ph.row(row0 + r);
       const int64_t ybase = row * a.ldy;
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
@@ -253,7 +357,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 #pragma unroll
           for (int e = 0; e < E; ++e)
             y[e] = ((x[r][k][e] - mean1[r]) - delta[r]) * rstd[r] * w[k][e] + b[k][e];
-          A::st(Y + ybase + (int64_t)v * E, A::pack(y));
+          A::st(Y + ybase + ph.win(v), A::pack(y));
         }
       }
       if (gm.t == 0) {
@@ -283,7 +387,7 @@ __global__ __launch_bounds__(LB) void team_fwd_kernel(FwdArgs a, int team_thread
 // keeps the faster one (RMSNorm 32768 x 4096: 141.0 -> 135.7 us, residual 65536 x 7168: 518 ->
 // 474 us with CLAMP; LayerNorm 16384 x 4096: 76.1 us without it, 81.5 us with it).
 template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE, bool LN,
-          bool CLAMP = !LN>
+          bool PART = false, bool CLAMP = !LN && !PART>
 __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_threads) {
   using A = Acc<T, EV>;
   using raw = typename A::raw;
@@ -293,8 +397,9 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   __shared__ __align__(16) float red[RED_FLOATS];
   __shared__ float merge[MERGE_FLOATS];
   const TeamGeom gm = team_geom<WAVE>(team_threads);
-  const int nacc = a.nacc;
-  const int64_t M = a.M;
+  const RowPhase<E, PART> ph(a.nacc, a.M, a.N, a.period, a.phase0, a.dphase);
+  const int nacc = ph.nal;
+  const int64_t M = ph.Mv; // rows walked below are indices among this workgroup's rows
   const int64_t N = a.N;
   const T *__restrict__ X = static_cast<const T *>(a.x);
   const T *__restrict__ DY = static_cast<const T *>(a.dy);
@@ -308,11 +413,20 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
   // the weight stays in its storage format (half the registers for bf16), unpacked at use
   WAcc<T, TW, EV> rw[VPT];
   float accw[VPT][E], accb[LN ? VPT : 1][E];
+  float own[PART ? VPT : 1][E]; // see RowPhase::own
 #pragma unroll
   for (int k = 0; k < VPT; ++k) {
     const int v = gm.t + k * gm.tt;
+    if constexpr (PART) {
+#pragma unroll
+      for (int e = 0; e < E; ++e) own[k][e] = ph.own(v, e);
+    }
     rw[k].zero();
-    if (v < nacc) rw[k].load(W + (int64_t)v * E);
+    if constexpr (PART) { // the class's columns (once per workgroup)
+      ph.gather(rw[k], W, v);
+    } else if (v < nacc) {
+      rw[k].load(W + (int64_t)v * E);
+    }
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       accw[k][e] = 0.0f;
@@ -328,7 +442,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
       const bool rv = live && row0 + r < M;
-      const int64_t rowc = rv ? row0 + r : M - 1;
+      const int64_t rowc = PART ? ph.load_row(row0 + r, rv) : (rv ? row0 + r : M - 1);
       pm[r] = 0.0f;
       pr[r] = 0.0f;
       if (have_stats) {
@@ -338,7 +452,11 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 #pragma unroll
       for (int k = 0; k < VPT; ++k) {
         const int v = gm.t + k * gm.tt;
-        if constexpr (CLAMP) {
+        if constexpr (PART) { // every slot loads (see RowPhase::load_row and own)
+          const int64_t o = ph.win(v < nacc ? v : nacc - 1);
+          px[r][k] = A::ld_once(X + rowc * a.ldx + o);
+          pdy[r][k] = A::ld_once(DY + rowc * a.lddy + o);
+        } else if constexpr (CLAMP) {
           const int64_t off = (int64_t)(v < nacc ? v : nacc - 1) * E;
           px[r][k] = A::ld_once(X + rowc * a.ldx + off);
           pdy[r][k] = A::ld_once(DY + rowc * a.lddy + off);
@@ -385,7 +503,10 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
             float f[E];
             A::unpack(masked(rx[r][k], k), f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc += f[e];
+            for (int e = 0; e < E; ++e) {
+              if constexpr (PART) acc = __builtin_fmaf(f[e], own[k][e], acc);
+              else acc += f[e];
+            }
           }
           s[r] = acc;
         }
@@ -404,7 +525,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
               A::unpack(masked(rx[r][k], k), f);
 #pragma unroll
               for (int e = 0; e < E; ++e) {
-                const float d = f[e] - m[r];
+                float d = f[e] - m[r];
+                if constexpr (PART) d *= own[k][e];
                 q = __builtin_fmaf(d, d, q);
                 c += d;
               }
@@ -430,7 +552,10 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
             float f[E];
             A::unpack(masked(rx[r][k], k), f);
 #pragma unroll
-            for (int e = 0; e < E; ++e) acc = __builtin_fmaf(f[e], f[e], acc);
+            for (int e = 0; e < E; ++e) {
+              if constexpr (PART) acc = __builtin_fmaf(f[e] * own[k][e], f[e], acc);
+              else acc = __builtin_fmaf(f[e], f[e], acc);
+            }
           }
           q[r] = acc;
         }
@@ -470,11 +595,16 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
           d[e] = LN ? xf[e] - m[r] : xf[e];
           gg[e] = df[e] * wf[e];
           // columns past N hold x = dY = 0: g * d adds nothing there
-          sums[r] = __builtin_fmaf(gg[e], d[e], sums[r]);
-          if constexpr (LN) sums[ROWS + r] += gg[e];
+          const float gs = PART ? gg[e] * own[k][e] : gg[e];
+          sums[r] = __builtin_fmaf(gs, d[e], sums[r]);
+          if constexpr (LN) sums[ROWS + r] += gs;
         }
         if constexpr (LN) {
-          if (in) {
+          if constexpr (PART) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              sums[2 * ROWS + r] = __builtin_fmaf(d[e], own[k][e], sums[2 * ROWS + r]);
+          } else if (in) {
 #pragma unroll
             for (int e = 0; e < E; ++e) sums[2 * ROWS + r] += d[e];
           }
@@ -494,8 +624,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 
 #pragma unroll
     for (int r = 0; r < ROWS; ++r) {
-      const int64_t row = row0 + r;
-      if (row >= M) continue; // rows past M add nothing to dW / dB and write nothing
+      if (row0 + r >= M) continue; // rows past M add nothing to dW / dB and write nothing
+      const int64_t row = ph.row(row0 + r);
       const float delta = LN ? sums[2 * ROWS + r] * a.inv_n : 0.0f;
       const float c1 = LN ? sums[ROWS + r] * a.inv_n : 0.0f;
       const float c2 =
@@ -530,10 +660,11 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         for (int e = 0; e < E; ++e) {
           const float xh = __builtin_fmaf(d[e], ra, nd);
           dx[e] = __builtin_fmaf(gg[e], ra, __builtin_fmaf(xh, cB, cC));
-          accw[k][e] = __builtin_fmaf(df[e], xh, accw[k][e]);
-          if constexpr (LN) accb[k][e] += df[e];
+          const float dfs = PART ? df[e] * own[k][e] : df[e];
+          accw[k][e] = __builtin_fmaf(dfs, xh, accw[k][e]);
+          if constexpr (LN) accb[k][e] += dfs;
         }
-        const int64_t off = (int64_t)v * E;
+        const int64_t off = ph.win(v);
         if (DH) {
           float hf[E];
           A::unpack(A::ld_once(DH + row * a.lddh + off), hf);
@@ -547,7 +678,7 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
     }
   };
 
-  const GroupRange gr = group_range(M, rows_per_group, a.blocked);
+  const GroupRange gr = group_range(M, rows_per_group, a.blocked, ph.bid, ph.nb);
   raw px[ROWS][VPT], pdy[ROWS][VPT];
   float pm[ROWS], pr[ROWS];
   int64_t g = gr.first;
@@ -582,8 +713,9 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
       if (v < nacc) {
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          pw[(int64_t)v * E + e] = accw[k][e];
-          if constexpr (LN) pb[(int64_t)v * E + e] = accb[k][e];
+          if (PART && own[k][e] == 0.0f) continue; // the neighbouring access writes it
+          pw[ph.win(v) + e] = accw[k][e];
+          if constexpr (LN) pb[ph.win(v) + e] = accb[k][e];
         }
       }
     }
@@ -599,8 +731,8 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
         const int v = gm.t + k * gm.tt;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
-          const int64_t col = (int64_t)v * E + e;
-          if (v < nacc && col >= c0 && col < c1)
+          const int64_t col = ph.win(v) + e;
+          if (v < nacc && col >= c0 && col < c1 && !(PART && own[k][e] == 0.0f))
             merge[gm.team * cols_per_block + (int)(col - c0)] =
                 q == 0 ? accw[k][e] : accb[LN ? k : 0][e];
         }
@@ -621,6 +753,15 @@ __global__ __launch_bounds__(LB) void team_bwd_kernel(BwdArgs a, int team_thread
 template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE>
 hipError_t fwd_launch(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s) {
   dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if constexpr (EV == full_epv<T>()) { // rows in phase classes only at the full width
+    if (a.period) {
+      if (resid)
+        return launch(team_fwd_kernel<T, TW, EV, VPT, ROWS, LB, WAVE, true, true>, grid, block,
+                      s, a, p.team_threads);
+      return launch(team_fwd_kernel<T, TW, EV, VPT, ROWS, LB, WAVE, false, true>, grid, block, s,
+                    a, p.team_threads);
+    }
+  }
   if (resid)
     return launch(team_fwd_kernel<T, TW, EV, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
                   p.team_threads);
@@ -631,6 +772,15 @@ hipError_t fwd_launch(const Plan &p, const FwdArgs &a, bool resid, hipStream_t s
 template <typename T, typename TW, int EV, int VPT, int ROWS, int LB, bool WAVE>
 hipError_t bwd_launch(const Plan &p, const BwdArgs &a, hipStream_t s) {
   dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if constexpr (EV == full_epv<T>()) {
+    if (a.period) {
+      if (a.layernorm)
+        return launch(team_bwd_kernel<T, TW, EV, VPT, ROWS, LB, WAVE, true, true>, grid, block, s,
+                      a, p.team_threads);
+      return launch(team_bwd_kernel<T, TW, EV, VPT, ROWS, LB, WAVE, false, true>, grid, block, s,
+                    a, p.team_threads);
+    }
+  }
   if (a.layernorm)
     return launch(team_bwd_kernel<T, TW, EV, VPT, ROWS, LB, WAVE, true>, grid, block, s, a,
                   p.team_threads);

@@ -20,7 +20,8 @@ SCHEME_AUTO, SCHEME_WAVE, SCHEME_BLOCK, SCHEME_SPLIT, SCHEME_LOOP = -1, 0, 1, 2,
 TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 3
 TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
 TUNE_SPLIT_EXCHANGE, TUNE_EXCHANGE_POLLS, TUNE_EXCHANGE_WITHHOLD = 8, 9, 10
-N_TUNE_KEYS = 11
+TUNE_UNALIGNED = 11
+N_TUNE_KEYS = 12
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_EXCHANGE = 0, 1, 2, 3, 4, 5
 SIZE_MAX = (1 << 64) - 1
@@ -67,7 +68,8 @@ class _Plan(ctypes.Structure):
                 ("grid", ctypes.c_int64), ("chunks", ctypes.c_int64),
                 ("chunk_elems", ctypes.c_int64), ("row_groups", ctypes.c_int64),
                 ("partials", ctypes.c_int64), ("workspace_bytes", ctypes.c_uint64),
-                ("exchange_row_groups", ctypes.c_int64)]
+                ("exchange_row_groups", ctypes.c_int64), ("phase_classes", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 _lib = None

@@ -314,13 +314,20 @@ typedef struct {
   int64_t exchange_row_groups; /* split scheme: row groups of the single-pass exchange form
                                   when it applies (the backward's also needs the saved
                                   statistics), else 0 */
+  int32_t phase_classes;  /* wave/block with 16-byte accesses to rows off 16-byte boundaries:
+                             the row phase classes (1, 2, 4 or 8), each workgroup taking the
+                             rows of one; 0 for aligned rows (NORM_TUNE_UNALIGNED) */
+  int32_t reserved;
 } norm_plan_t;
 
 /*
  * The plan the dispatcher picks for a shape on a device with cu_count compute units. align is
  * the largest power of two, up to 16, that divides the address of every tensor of the call
  * (16 for buffers straight from an allocator; values above 16 count as 16; 0 or 1 when
- * unknown). Pure host logic: needs no GPU.
+ * unknown). Rows are taken as contiguous, so a row starts N elements after the previous one,
+ * and below 16 the tensors' phases as unknown (a call whose tensors share one phase can take
+ * 16-byte accesses over row phase classes where this plan shows narrower ones). Pure host
+ * logic: needs no GPU.
  */
 norm_status_t norm_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, int64_t M,
                         int64_t N, int residual, int align, int cu_count, norm_plan_t *out);
@@ -346,8 +353,13 @@ typedef enum {
                                    before a workgroup gives up on the row and writes NaN for
                                    it and for its later rows (1 .. 2^24; default 2^19, about a
                                    second) */
-  NORM_TUNE_EXCHANGE_WITHHOLD = 10 /* for tests of that bounded wait only: 1 = chunk 0 never
-                                      publishes its partials, so every row gives up */
+  NORM_TUNE_EXCHANGE_WITHHOLD = 10, /* for tests of that bounded wait only: 1 = chunk 0 never
+                                       publishes its partials, so every row gives up */
+  NORM_TUNE_UNALIGNED = 11      /* wave/block schemes, rows off 16-byte boundaries (their
+                                   length, stride or start) with every [M, N] tensor at one
+                                   phase: -1 (default) or 1, 16-byte accesses over row phase
+                                   classes in place of 8-byte, 4-byte and element-wise ones;
+                                   0 never */
 } norm_tune_t;
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);

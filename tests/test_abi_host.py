@@ -2,6 +2,7 @@
 rejects bad arguments before touching a device, and its dispatcher picks the documented
 schemes and workspace layouts."""
 import ctypes
+import math
 import os
 import re
 import subprocess
@@ -239,8 +240,21 @@ def test_scheme_boundaries():
     assert nl.norm_plan(0, BF, 1, 16384, 16392)["scheme"] == nl.SCHEME_SPLIT
     assert nl.norm_plan(0, F, 1, 16384, 8192)["scheme"] == nl.SCHEME_LOOP
     assert nl.norm_plan(0, F, 1, 16384, 8196)["scheme"] == nl.SCHEME_SPLIT
-    assert nl.norm_plan(0, BF, 1, 16384, 4095)["scheme"] == nl.SCHEME_BLOCK   # element-wise
-    assert nl.norm_plan(0, BF, 1, 16384, 4097)["scheme"] == nl.SCHEME_SPLIT   # element-wise
+    # odd rows: 16-byte accesses over row phase classes in the block scheme while the class
+    # whose rows start 7 elements past a boundary needs at most 1024 accesses (N <= 8185 bf16),
+    # element-wise in the split scheme beyond
+    assert nl.norm_plan(0, BF, 1, 16384, 4095)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 1, 16384, 4097)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 1, 16384, 8185)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 1, 16384, 8187)["scheme"] == nl.SCHEME_SPLIT   # element-wise
+    assert nl.norm_plan(0, BF, 0, 16384, 16377)["scheme"] == nl.SCHEME_BLOCK
+    assert nl.norm_plan(0, BF, 0, 16384, 16379)["scheme"] == nl.SCHEME_SPLIT   # element-wise
+    try:
+        nl.norm_set_tuning(nl.TUNE_UNALIGNED, 0)
+        assert nl.norm_plan(0, BF, 1, 16384, 4095)["scheme"] == nl.SCHEME_BLOCK   # element-wise
+        assert nl.norm_plan(0, BF, 1, 16384, 4097)["scheme"] == nl.SCHEME_SPLIT   # element-wise
+    finally:
+        nl.norm_set_tuning(nl.TUNE_UNALIGNED, -1)
     # forcing the looped scheme leaves the forward to the dispatcher
     try:
         nl.norm_set_tuning(nl.TUNE_SCHEME, nl.SCHEME_LOOP)
@@ -257,16 +271,43 @@ def test_access_width_follows_row_length_and_alignment():
         p = nl.norm_plan(0, dt, pass_, 64, N, align=align)
         assert p["access_bytes"] == p["elems_per_access"] * (4 if dt == F else 2)
         return p["access_bytes"]
-    # bf16: 16 bytes when N % 8 == 0, else 8 (N % 4 == 0), else 4 (N even), else one element
-    assert [width(BF, N) for N in (4096, 4100, 4098, 4097)] == [16, 8, 4, 2]
-    # fp32: 16 bytes when N % 4 == 0, else 8 (N even), else one element
-    assert [width(F, N) for N in (4096, 4098, 4097)] == [16, 8, 4]
+    # 16 bytes when N is a multiple of the 16-byte access, else 16 bytes over row phase classes:
+    # row r of contiguous rows starts at phase r * N mod 8 (bf16), so N % 8 = 4, 2 or odd gives
+    # 2, 4 or 8 classes (fp32: N % 4 = 2 or odd gives 2 or 4)
+    assert [width(BF, N) for N in (4096, 4100, 4098, 4097)] == [16, 16, 16, 16]
+    assert [nl.norm_plan(0, BF, 0, 64, N)["phase_classes"] for N in (4096, 4100, 4098, 4097)] \
+        == [0, 2, 4, 8]
+    assert [width(F, N) for N in (4096, 4098, 4097)] == [16, 16, 16]
+    assert [nl.norm_plan(0, F, 0, 64, N)["phase_classes"] for N in (4096, 4098, 4097)] \
+        == [0, 2, 4]
+    for dt, N, classes in ((BF, 4097, 8), (BF, 4103, 8), (F, 4093, 4), (F, 1027, 4),
+                           (BF, 1001, 8), (BF, 9, 8), (F, 5, 4)):
+        p = nl.norm_plan(0, dt, 1, 64, N)
+        assert p["phase_classes"] == classes and p["elems_per_access"] == (8 if dt == BF else 4)
+        assert p["grid"] % classes == 0
+    assert nl.norm_plan(0, BF, 1, 64, 4096)["phase_classes"] == 0
+    # pointers whose phase is unknown (align below 16), and rows shorter than one 16-byte
+    # access: the widest aligned access, element-wise for odd rows
+    assert width(BF, 4097, 8) == 2 and width(F, 4097, 8) == 4 and width(BF, 4100, 8) == 8
+    assert width(BF, 7) == 2 and width(F, 3) == 4
+    try:
+        # without phase classes: 8 bytes (N % 4 == 0), 4 (N even) or one element
+        nl.norm_set_tuning(nl.TUNE_UNALIGNED, 0)
+        assert [width(BF, N) for N in (4100, 4098, 4097)] == [8, 4, 2]
+        assert [width(F, N) for N in (4098, 4097)] == [8, 4]
+        # fp32 weights beside bf16 activations: 4 bf16 need 16-byte weight loads, 2 need 8
+        assert [width(BF32W, N) for N in (4096, 4100, 4098)] == [16, 8, 4]
+        assert [width(BF32W, 4100, a) for a in (16, 8, 4)] == [8, 4, 2]
+        nl.norm_set_tuning(nl.TUNE_UNALIGNED, 1)     # the same as the default
+        assert [width(BF, N) for N in (4100, 4098, 4097)] == [16, 16, 16]
+    finally:
+        nl.norm_set_tuning(nl.TUNE_UNALIGNED, -1)
     # the pointers' common alignment caps the width
     assert [width(BF, 4096, a) for a in (16, 8, 4, 2, 1, 0)] == [16, 8, 4, 2, 2, 2]
     assert [width(F, 4096, a) for a in (16, 8, 4)] == [16, 8, 4]
-    # fp32 weights beside bf16 activations: 4 bf16 need 16-byte weight loads, 2 need 8 bytes
-    assert [width(BF32W, N) for N in (4096, 4100, 4098)] == [16, 8, 4]
-    assert [width(BF32W, 4100, a) for a in (16, 8, 4)] == [8, 4, 2]
+    # fp32 weights: the phase classes gather them at any alignment
+    assert [width(BF32W, N) for N in (4096, 4100, 4098)] == [16, 16, 16]
+    assert [width(BF32W, 4100, a) for a in (16, 8, 4)] == [16, 4, 2]
     # the narrow paths size their teams like the 16-byte path: same scheme, same threads
     for pass_ in (0, 1):
         full = nl.norm_plan(0, BF, pass_, 16384, 4096)
@@ -286,8 +327,17 @@ def test_plan_covers_every_row_and_column(dt, N, M, pass_):
     for align in (16, 8, 4, 2, 1):
         p = nl.norm_plan(0, dt, pass_, M, N, align=align)
         epv = p["elems_per_access"]
-        assert N % epv == 0 and p["access_bytes"] <= max(align, 4 if dt == F else 2)
-        nacc = N // epv
+        P = p["phase_classes"]
+        if P:
+            # 16-byte accesses over row phase classes (contiguous rows of N elements from a
+            # 16-byte aligned start: row r at phase r * N mod epv), a team scheme
+            assert align == 16 and p["access_bytes"] == 16 and N % epv and N >= epv
+            assert p["scheme"] in (nl.SCHEME_WAVE, nl.SCHEME_BLOCK)
+            assert P == epv // math.gcd(N % epv, epv) and p["grid"] % P == 0
+            nacc = max(-(-(N + (c * N) % epv) // epv) for c in range(P))
+        else:
+            assert N % epv == 0 and p["access_bytes"] <= max(align, 4 if dt == F else 2)
+            nacc = N // epv
         assert p["threads"] % 64 == 0 and 64 <= p["threads"] <= 1024
         assert p["grid"] >= 1
         if p["scheme"] == nl.SCHEME_SPLIT:

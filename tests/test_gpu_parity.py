@@ -472,14 +472,19 @@ def _access_bytes(kind, dt, wdt, M, N, residual=False, align=16):
     return nl.norm_plan(kind, code, 0, M, N, residual, align=align)["access_bytes"]
 
 
+# (The default takes 16-byte accesses over row phase classes for these rows when all tensors
+# share a phase; these tests switch that off to cover the 8- and 4-byte kernels, which serve
+# tensors at mixed phases.)
+
 @pytest.mark.parametrize("kind,dt,wdt,M,N", _narrow_cases(), ids=lambda v: str(v))
 def test_narrow_access_widths(kind, dt, wdt, M, N):
-    width = _access_bytes(kind, dt, wdt, M, N)
-    assert width == (8 if (dt == "f32" or N % 4 == 0) else 4)
-    _say("narrow %d-byte %s %s w=%s %dx%d" % (width, kind, dt, wdt, M, N))
-    w = dataclasses.replace(_small(kind, dt, M, N, seed=M + N), wdtype=wdt)
-    run_and_check(w)
-    run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
+    with tuned(unaligned=0):
+        width = _access_bytes(kind, dt, wdt, M, N)
+        assert width == (8 if (dt == "f32" or N % 4 == 0) else 4)
+        _say("narrow %d-byte %s %s w=%s %dx%d" % (width, kind, dt, wdt, M, N))
+        w = dataclasses.replace(_small(kind, dt, M, N, seed=M + N), wdtype=wdt)
+        run_and_check(w)
+        run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
 
 
 @pytest.mark.parametrize("N", [1002, 4098, 4100, 7170, 8194, 16386])
@@ -487,8 +492,9 @@ def test_narrow_access_widths(kind, dt, wdt, M, N):
 def test_narrow_residual(kind, N):
     _say("narrow residual %s N=%d" % (kind, N))
     w = _small(kind, "bf16", 65, N, seed=N, x=inputs.normal(0, 0.5), r=inputs.normal(0, 1))
-    run_and_check(w, dr="alias", dh=True)
-    run_and_check(dataclasses.replace(w, seed=N + 1), dr="separate")
+    with tuned(unaligned=0):
+        run_and_check(w, dr="alias", dh=True)
+        run_and_check(dataclasses.replace(w, seed=N + 1), dr="separate")
 
 
 @pytest.mark.parametrize("N", [4098, 4100, 8196])
@@ -503,7 +509,7 @@ def test_narrow_forced(knob, N):
         pytest.skip("the looped backward has no 4-byte kernels")
     for kind in ("layernorm", "rmsnorm"):
         _say("narrow knob %s %s N=%d" % (knob, kind, N))
-        with tuned(**knob):
+        with tuned(unaligned=0, **knob):
             run_and_check(_small(kind, "bf16", 77, N, seed=N))
 
 
@@ -749,9 +755,17 @@ SHIFTS = [("bf16", None, 1, 2), ("bf16", None, 2, 4), ("bf16", None, 4, 8),
 
 @pytest.mark.parametrize("dt,wdt,shift,width", SHIFTS, ids=lambda v: str(v))
 @pytest.mark.parametrize("N", [100, 1000, 4096, 9000])
-def test_pointer_alignment_sets_width(dt, wdt, shift, width, N):
-    """Every tensor placed `shift` elements past a 16-byte boundary: the plan takes the widest
-    access that alignment allows, and the results still match the oracle."""
+@pytest.mark.parametrize("unaligned", [0, -1], ids=["narrow", "phase_classes"])
+def test_pointer_alignment_sets_width(dt, wdt, shift, width, N, unaligned):
+    """Every tensor placed `shift` elements past a 16-byte boundary: without phase classes the
+    plan takes the widest access that alignment allows; with them (the default; all tensors at
+    one phase) 16-byte accesses over the classes where a team scheme holds the row. The results
+    match the oracle either way."""
+    with tuned(unaligned=unaligned):
+        _pointer_shift_case(dt, wdt, shift, width, N, check_width=unaligned == 0)
+
+
+def _pointer_shift_case(dt, wdt, shift, width, N, check_width):
     kind = "layernorm"
     w = dataclasses.replace(_small(kind, dt, 61, N, seed=N), wdtype=wdt)
     t = inputs.make(w)
@@ -769,8 +783,9 @@ def test_pointer_alignment_sets_width(dt, wdt, shift, width, N):
     expect = min(width, (N & -N) * X.element_size())
     if expect < 4:
         expect = X.element_size()
-    assert _access_bytes(kind, dt, wdt, 61, N, align=min(align, W.data_ptr() & -W.data_ptr())) \
-        == expect
+    if check_width:
+        assert _access_bytes(kind, dt, wdt, 61, N,
+                             align=min(align, W.data_ptr() & -W.data_ptr())) == expect
     _say("pointer shift %d (%s, w=%s) N=%d: %d-byte accesses" % (shift, dt, wdt, N, expect))
     Y = shifted(torch.zeros(61, N, dtype=X.dtype))
     mean = torch.empty(61, dtype=torch.float32, device="cuda")
