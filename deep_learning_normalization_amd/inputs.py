@@ -176,11 +176,13 @@ def long_rows(kind: str, M: int, N: int) -> Workload:
 LONG_ROW_SHAPES = ((256, 262144), (4, 4194304))
 
 
-# Beyond the shapes above: a row length that rules out 16-byte accesses (LayerNorm 16384 x
-# 4100, 8-byte accesses), a hidden size whose backward rows no longer fit a team's registers
+# Beyond the shapes above: row lengths that are not a multiple of the 16-byte access (LayerNorm
+# 16384 x 4100 and 16384 x 4097), a hidden size whose backward rows no longer fit a team's registers
 # (RMSNorm 16384 x 16384, the looped backward), and fp16 storage, with the same draws as their
 # neighbours.
 LN_BF16_16384x4100 = LN_BF16_16384x4096.with_shape(16384, 4100, "layernorm_bf16_16384x4100")
+# An odd row length (rows at eight different 16-byte phases).
+LN_BF16_16384x4097 = LN_BF16_16384x4096.with_shape(16384, 4097, "layernorm_bf16_16384x4097")
 # The LayerNorm in fp16 storage.
 LN_F16_16384x4096 = replace(LN_BF16_16384x4096, name="layernorm_f16_16384x4096", dtype="f16")
 RMS_BF16_16384x16384 = rms_hidden(16384, M=16384)
@@ -226,7 +228,7 @@ def all_workloads():
     out.append(RESID_RMS_BF16_65536x7168)
     for M, N in LONG_ROW_SHAPES:
         out += [long_rows("layernorm", M, N), long_rows("rmsnorm", M, N)]
-    out += [LN_BF16_16384x4100, RMS_BF16_16384x16384, LN_F16_16384x4096]
+    out += [LN_BF16_16384x4100, LN_BF16_16384x4097, RMS_BF16_16384x16384, LN_F16_16384x4096]
     return out
 
 
