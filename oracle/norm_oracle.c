@@ -25,6 +25,8 @@
  *   [P3] "Towards Free Normalization: Fusing Normalization into GEMM and Attention Kernels"
  *        (brifing.si): items 3-4 and 9-10 -- a norm whose output is the input of a matrix
  *        product, fused into that product; the oracle evaluates the unfused composition.
+ *        Item 5 -- norms fused around an attention kernel; the oracle normalises the query
+ *        and key vectors, then evaluates softmax attention from its definition.
  *
  *   Readings taken where the pages say nothing (each is also listed in the design notes):
  *     - variance is the biased estimator (divide by N);
@@ -52,6 +54,8 @@
 #endif
 
 enum { OR_LAYERNORM = 0, OR_RMSNORM = 1 };
+/* attention without a norm on its queries and keys (the unfused composition's second step) */
+enum { OR_NO_NORM = -1 };
 /* dtype: the storage type of every tensor, or OR_BF16_F32W / OR_F16_F32W = bf16 / fp16
  * activations and gradients (X, R, dY, dH) with fp32 weight and bias (their gradients are then
  * fp32 too). */
@@ -425,6 +429,103 @@ int oracle_norm_linear_rows(int kind, int dtype, int64_t M, int64_t K, int64_t N
   }
   free(y);
   return OR_OK;
+}
+
+/* ---- norms on the queries and keys of an attention ----------------------------------- */
+
+/* One query or key vector of D bf16 values at Xb + off, normalised like a row of length D
+ * (or copied, for OR_NO_NORM) with the D-entry gamma W and beta B (bf16 bits; B may be NULL). */
+static void or_qk_row(int kind, int64_t D, const void *Xb, int64_t off, const void *W,
+                      const void *B, double eps, double *out) {
+  for (int64_t d = 0; d < D; ++d) out[d] = or_load(OR_BF16, Xb, off + d);
+  if (kind == OR_NO_NORM) return;
+  double mu, rs;
+  or_row_stats(kind, D, out, eps, &mu, &rs);
+  for (int64_t d = 0; d < D; ++d) {
+    double w = or_load(OR_BF16, W, d);
+    double b = B ? or_load(OR_BF16, B, d) : 0.0;
+    out[d] = (kind == OR_LAYERNORM) ? (out[d] - mu) * rs * w + b : out[d] * rs * w;
+  }
+}
+
+/*
+ * Attention whose queries and keys are normalised first [P3 item 5: norms fused around an
+ * attention kernel]. Reading: the norm applies to every query vector and every key vector of
+ * every head along the head dimension D (QK-norm), with one gamma (and, for LayerNorm, beta)
+ * of D entries for the queries and one for the keys, shared by all heads; V is used as given.
+ * Then, per query head, softmax attention by its definition:
+ *   logit(i, j) = scale * sum_d q'(i, d) k'(j, d),  over keys j visible to query i
+ *                 (all S keys, or j <= i when causal),
+ *   O(i, :)     = sum_j softmax_j(logit(i, .)) V(j, :),
+ *   lse(i)      = log sum_j exp(logit(i, j)).
+ * Grouped heads: query head h reads key and value head h / (Hq / Hk).
+ *
+ * Layout: Q [B][S][Hq][D], K and V [B][S][Hk][D], all bf16 bits; Wq, Bq, Wk, Bk D bf16 bits
+ * each (Bq, Bk NULL for RMSNorm; all four NULL for OR_NO_NORM). Computes query positions
+ * s0 .. s1-1 of batch b and query head h:
+ *   O   : out, (s1-s0)*D doubles, unrounded
+ *   lse : out, (s1-s0) doubles, or NULL
+ * Returns 0, or nonzero on a bad argument / allocation failure.
+ */
+int oracle_norm_attention(int kind, int64_t B, int64_t S, int64_t Hq, int64_t Hk, int64_t D,
+                          int64_t b, int64_t h, int64_t s0, int64_t s1, const void *Q,
+                          const void *K, const void *V, const void *Wq, const void *Bq,
+                          const void *Wk, const void *Bk, double eps, double scale, int causal,
+                          double *O, double *lse) {
+  if (kind != OR_LAYERNORM && kind != OR_RMSNORM && kind != OR_NO_NORM) return OR_BAD_ARG;
+  if (B <= 0 || S <= 0 || Hq <= 0 || Hk <= 0 || D <= 0 || Hq % Hk != 0) return OR_BAD_ARG;
+  if (b < 0 || b >= B || h < 0 || h >= Hq || s0 < 0 || s1 < s0 || s1 > S) return OR_BAD_ARG;
+  if (!Q || !K || !V || !O || !(eps >= 0.0)) return OR_BAD_ARG;
+  if (kind == OR_NO_NORM && (Wq || Bq || Wk || Bk)) return OR_BAD_ARG;
+  if (kind != OR_NO_NORM && (!Wq || !Wk)) return OR_BAD_ARG;
+  if (kind == OR_RMSNORM && (Bq || Bk)) return OR_BAD_ARG;
+  const int64_t hk = h / (Hq / Hk);
+  const int64_t nk = causal ? s1 : S; /* keys any of these queries sees */
+  double *kn = (double *)malloc((size_t)(nk ? nk : 1) * (size_t)D * sizeof(double));
+  if (!kn) return OR_NO_MEMORY;
+#pragma omp parallel for schedule(static)
+  for (int64_t j = 0; j < nk; ++j)
+    or_qk_row(kind, D, K, ((b * S + j) * Hk + hk) * D, Wk, Bk, eps, kn + j * D);
+  int fail = 0;
+#pragma omp parallel
+  {
+    double *qn = (double *)malloc((size_t)D * sizeof(double));
+    double *p = (double *)malloc((size_t)(nk ? nk : 1) * sizeof(double));
+    if (!qn || !p) {
+#pragma omp atomic write
+      fail = 1;
+    }
+#pragma omp for schedule(static)
+    for (int64_t i = s0; i < s1; ++i) {
+      if (!qn || !p) continue;
+      or_qk_row(kind, D, Q, ((b * S + i) * Hq + h) * D, Wq, Bq, eps, qn);
+      const int64_t n = causal ? i + 1 : S;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < n; ++j) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < D; ++d) dot += qn[d] * kn[j * D + d];
+        p[j] = scale * dot;
+        if (p[j] > mx) mx = p[j];
+      }
+      /* softmax with its largest logit taken out of every exponent (the same ratios) */
+      double z = 0.0;
+      for (int64_t j = 0; j < n; ++j) {
+        p[j] = exp(p[j] - mx);
+        z += p[j];
+      }
+      for (int64_t d = 0; d < D; ++d) {
+        double acc = 0.0;
+        for (int64_t j = 0; j < n; ++j)
+          acc += p[j] * or_load(OR_BF16, V, ((b * S + j) * Hk + hk) * D + d);
+        O[(i - s0) * D + d] = acc / z;
+      }
+      if (lse) lse[i - s0] = mx + log(z);
+    }
+    free(qn);
+    free(p);
+  }
+  free(kn);
+  return fail ? OR_NO_MEMORY : OR_OK;
 }
 
 /* ---- helpers exposed for pins ---------------------------------------------------------- */

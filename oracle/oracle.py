@@ -9,7 +9,8 @@ Definitions followed (web page "PyTorch atinge desempenho SOTA em normalização
 torch.compile", matsubara.tec.br): para. 2 for what LayerNorm and RMSNorm compute, para. 3 for
 the reduction along the contiguous dimension, para. 7 for the gradients dX, dW and dB; and
 (web page "Towards Free Normalization: Fusing Normalization into GEMM and Attention Kernels",
-brifing.si) items 3-4 and 9-10 for a norm whose output feeds a matrix product.
+brifing.si) items 3-4 and 9-10 for a norm whose output feeds a matrix product, and item 5 for
+norms on the queries and keys of an attention.
 """
 import ctypes
 import os
@@ -19,6 +20,7 @@ import numpy as np
 from . import build as _build
 
 LAYERNORM, RMSNORM = 0, 1
+NO_NORM = -1  # attention with its queries and keys used as given
 # storage types: every tensor fp32, bf16 or fp16, or bf16 / fp16 activations and gradients
 # with fp32 weight and bias
 F32, BF16, BF16_F32W, F16, F16_F32W = 0, 1, 2, 3, 4
@@ -53,6 +55,10 @@ class Oracle:
         lib.oracle_norm_linear_rows.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64,
                                                 i64, i64, vp, vp, vp, vp, vp, dbl, dp]
         lib.oracle_norm_linear_rows.restype = ctypes.c_int
+        lib.oracle_norm_attention.argtypes = [ctypes.c_int, i64, i64, i64, i64, i64, i64, i64,
+                                              i64, i64, vp, vp, vp, vp, vp, vp, vp, dbl, dbl,
+                                              ctypes.c_int, dp, dp]
+        lib.oracle_norm_attention.restype = ctypes.c_int
         lib.oracle_decode.argtypes = [ctypes.c_int, vp, i64, dp]
         lib.oracle_decode.restype = ctypes.c_int
         lib.oracle_round_bf16.argtypes = [dp, i64, vp]
@@ -75,6 +81,11 @@ class Oracle:
 
     def norm_linear(self, kind, dtype, X, W, B, L, c=None, eps=1e-5, rows=None):
         return _norm_linear(self.lib, kind, dtype, X, W, B, L, c, eps, rows)
+
+    def norm_attention(self, kind, Q, K, V, Wq=None, Bq=None, Wk=None, Bk=None, eps=1e-6,
+                       scale=None, causal=False, b=0, h=0, rows=None):
+        return _norm_attention(self.lib, kind, Q, K, V, Wq, Bq, Wk, Bk, eps, scale, causal, b,
+                               h, rows)
 
     def decode(self, dtype, bits):
         return _decode(self.lib, dtype, bits)
@@ -198,6 +209,36 @@ def _norm_linear(lib, kind, dtype, X, W, B, L, c, eps, rows):
     return out
 
 
+def _norm_attention(lib, kind, Q, K, V, Wq, Bq, Wk, Bk, eps, scale, causal, b, h, rows):
+    """Attention of query head h of batch b over query positions [s0, s1) (all by default),
+    with the queries and keys normalised first (kind LAYERNORM or RMSNORM) or used as given
+    (NO_NORM). Q is B x S x Hq x D, K and V B x S x Hk x D, the four norm vectors D each, all
+    bf16 bits (uint16). scale defaults to D ** -0.5. Returns (O, lse): (s1-s0) x D and (s1-s0)
+    unrounded float64 arrays. Definition: the page "Towards Free Normalization: Fusing
+    Normalization into GEMM and Attention Kernels" (brifing.si), item 5.
+    """
+    Q = _bits(Q, BF16)
+    if Q.ndim != 4:
+        raise ValueError("Q must be B x S x Hq x D")
+    Bn, S, Hq, D = Q.shape
+    K = _bits(K, BF16)
+    if K.ndim != 4 or K.shape[:2] != (Bn, S) or K.shape[3] != D:
+        raise ValueError("K must be %d x %d x Hk x %d, got %s" % (Bn, S, D, K.shape))
+    Hk = K.shape[2]
+    V = _bits(V, BF16, K.shape)
+    Wq, Bq, Wk, Bk = (_bits(t, BF16, (D,)) for t in (Wq, Bq, Wk, Bk))
+    s0, s1 = (0, S) if rows is None else rows
+    O = np.empty((s1 - s0, D), np.float64)
+    lse = np.empty(s1 - s0, np.float64)
+    scale = D ** -0.5 if scale is None else scale
+    st = lib.oracle_norm_attention(kind, Bn, S, Hq, Hk, D, b, h, s0, s1, _ptr(Q), _ptr(K),
+                                   _ptr(V), _ptr(Wq), _ptr(Bq), _ptr(Wk), _ptr(Bk), float(eps),
+                                   float(scale), int(bool(causal)), _ptr(O), _ptr(lse))
+    if st:
+        raise ValueError("oracle_norm_attention failed with status %d" % st)
+    return O, lse
+
+
 def _decode(lib, dtype, bits):
     """Widen an array of bf16 or fp16 (uint16) or fp32 bits to float64 with the oracle's
     decoder."""
@@ -236,6 +277,12 @@ def bwd(kind, dtype, X, dY, W, dH=None, eps=1e-5, rows=None, want_dx=True, want_
 
 def norm_linear(kind, dtype, X, W, B, L, c=None, eps=1e-5, rows=None):
     return default().norm_linear(kind, dtype, X, W, B, L, c, eps, rows)
+
+
+def norm_attention(kind, Q, K, V, Wq=None, Bq=None, Wk=None, Bk=None, eps=1e-6, scale=None,
+                   causal=False, b=0, h=0, rows=None):
+    return default().norm_attention(kind, Q, K, V, Wq, Bq, Wk, Bk, eps, scale, causal, b, h,
+                                    rows)
 
 
 def decode(dtype, bits):

@@ -11,7 +11,10 @@ What pins what:
   - mathematics: row invariants of the normalised output, shift / scale invariance of the
     gradient, central finite differences of the oracle's own forward;
   - hand-derived exact cases in tests/golden/exact_cases.json;
-  - number formats: bf16 widening and round-to-nearest-even against torch's conversions.
+  - number formats: bf16 widening and round-to-nearest-even against torch's conversions;
+  - attention with normalised queries and keys: torch float64 layer_norm / rms_norm followed
+    by scaled_dot_product_attention and logsumexp, closed forms (uniform weights, one key) and
+    the exact invariance of RMSNorm / LayerNorm under scaling by a power of two.
 
 Definitions (page "PyTorch atinge desempenho SOTA em normalização com torch.compile",
 matsubara.tec.br): para. 2 (LayerNorm, RMSNorm), para. 3 (reduction along the contiguous
@@ -623,6 +626,128 @@ def pin_norm_linear_deferred_form(orc):
             _close(got, lazy, 1e-11, 1e-11, "deferred form")
 
 
+# ---- attention over normalised queries and keys ---------------------------------------------
+# Page "Towards Free Normalization: Fusing Normalization into GEMM and Attention Kernels"
+# (brifing.si), item 5: norms fused around an attention kernel, read as the norm of every query
+# and key vector along the head dimension.
+
+NO_NORM = -1
+# (B, S, Hq, Hk, D)
+ATT_SHAPES = [(1, 1, 1, 1, 8), (2, 5, 4, 2, 16), (1, 33, 3, 1, 24), (2, 19, 2, 2, 128)]
+
+
+def _att_case(kind, Bn, S, Hq, Hk, D, seed):
+    q = (torch.randn(Bn, S, Hq, D, generator=_rng(seed)) * 1.3 + 0.4).to(torch.bfloat16)
+    k = (torch.randn(Bn, S, Hk, D, generator=_rng(seed + 1)) * 0.8 - 0.3).to(torch.bfloat16)
+    v = torch.randn(Bn, S, Hk, D, generator=_rng(seed + 2)).to(torch.bfloat16)
+    if kind == NO_NORM:
+        return q, k, v, None, None, None, None
+    wq = _vec(D, BF16, seed + 3, mean=1.5, std=0.5)
+    wk = _vec(D, BF16, seed + 4, mean=1.5, std=0.5)
+    bq = _vec(D, BF16, seed + 5, mean=0.0, std=0.3) if kind == LN else None
+    bk = _vec(D, BF16, seed + 6, mean=0.0, std=0.3) if kind == LN else None
+    return q, k, v, wq, bq, wk, bk
+
+
+def _att_oracle(orc, kind, t, eps, scale, causal, b, h, rows=None):
+    q, k, v, wq, bq, wk, bk = t
+    hb = inputs.host_bits
+    return orc.norm_attention(kind, hb(q), hb(k), hb(v), hb(wq), hb(bq), hb(wk), hb(bk), eps=eps,
+                              scale=scale, causal=causal, b=b, h=h, rows=rows)
+
+
+def pin_norm_attention_vs_torch(orc):
+    """O and lse against torch float64: layer_norm / rms_norm of the query and key vectors
+    over D, key and value heads repeated for grouped query heads, then
+    scaled_dot_product_attention and logsumexp of the masked logits."""
+    for kind in (LN, RMS, NO_NORM):
+        for causal in (False, True):
+            for i, (Bn, S, Hq, Hk, D) in enumerate(ATT_SHAPES):
+                t = _att_case(kind, Bn, S, Hq, Hk, D, 1100 + 10 * i)
+                q, k, v, wq, bq, wk, bk = (_d(x) for x in t)
+                eps = _eps32(1e-6)
+                scale = 0.7 * D ** -0.5
+                if kind == LN:
+                    q = F.layer_norm(q, (D,), wq, bq, eps)
+                    k = F.layer_norm(k, (D,), wk, bk, eps)
+                elif kind == RMS:
+                    q = F.rms_norm(q, (D,), wq, eps)
+                    k = F.rms_norm(k, (D,), wk, eps)
+                g = Hq // Hk
+                k = k.repeat_interleave(g, dim=2)
+                v = v.repeat_interleave(g, dim=2)
+                qh, kh, vh = (x.transpose(1, 2) for x in (q, k, v))   # B x H x S x D
+                want = F.scaled_dot_product_attention(qh, kh, vh, is_causal=causal, scale=scale)
+                logits = scale * (qh @ kh.transpose(-1, -2))
+                if causal:
+                    logits = logits.masked_fill(
+                        torch.ones(S, S, dtype=torch.bool).triu(1), float("-inf"))
+                want_lse = torch.logsumexp(logits, dim=-1)
+                for b in range(Bn):
+                    for h in range(Hq):
+                        O, lse = _att_oracle(orc, kind, t, eps, scale, causal, b, h)
+                        what = "attention kind %d causal %d %s b %d h %d" % (
+                            kind, causal, (Bn, S, Hq, Hk, D), b, h)
+                        _close(O, want[b, h].numpy(), 1e-11, 1e-11, what + " O")
+                        _close(lse, want_lse[b, h].numpy(), 1e-11, 1e-11, what + " lse")
+
+
+def pin_norm_attention_closed_forms(orc):
+    """Cases with a closed form: equal logits give the plain mean of the visible value rows
+    (all S, or the first i + 1 when causal) and lse = log(count) + the common logit; a single
+    key gives its value row. Equal logits come from zero queries without a norm, and from
+    identical key vectors with either norm."""
+    Bn, S, Hq, Hk, D = 2, 9, 4, 2, 16
+    for kind in (NO_NORM, RMS, LN):
+        for causal in (False, True):
+            q, k, v, wq, bq, wk, bk = _att_case(kind, Bn, S, Hq, Hk, D, 1300)
+            if kind == NO_NORM:
+                q = torch.zeros_like(q)
+            else:
+                k = k[:, :1].expand(Bn, S, Hk, D).contiguous()
+            t = (q, k, v, wq, bq, wk, bk)
+            vd = v.double()
+            for b in range(Bn):
+                for h in range(Hq):
+                    O, lse = _att_oracle(orc, kind, t, 1e-6, 0.3, causal, b, h)
+                    hk = h // (Hq // Hk)
+                    for i in range(S):
+                        n = i + 1 if causal else S
+                        want = vd[b, :n, hk].mean(dim=0).numpy()
+                        _close(O[i], want, 1e-12, 1e-12, "equal logits O kind %d" % kind)
+                        if kind == NO_NORM:
+                            _close([lse[i]], [np.log(n)], 1e-12, 1e-12, "equal logits lse")
+    t = _att_case(RMS, 1, 1, 2, 1, 24, 1310)
+    for h in range(2):
+        O, _ = _att_oracle(orc, RMS, t, 1e-6, 0.2, False, 0, h)
+        assert np.array_equal(O[0], t[2][0, 0, 0].double().numpy()), "one key: O = its value"
+
+
+def pin_norm_attention_scale_invariance(orc):
+    """With eps = 0 both norms are invariant to scaling a vector by a power of two, and every
+    step of the definition scales exactly: scaling all queries by 2 and all keys by 1/4 leaves
+    O and lse bit for bit unchanged; without a norm it scales the logits instead. Query rows
+    computed in pieces equal the rows computed together."""
+    Bn, S, Hq, Hk, D = 1, 21, 2, 1, 32
+    for kind in (LN, RMS):
+        for causal in (False, True):
+            t = _att_case(kind, Bn, S, Hq, Hk, D, 1400)
+            t2 = (t[0] * 2, t[1] * 0.25) + t[2:]
+            for h in range(Hq):
+                O, lse = _att_oracle(orc, kind, t, 0.0, 0.25, causal, 0, h)
+                O2, lse2 = _att_oracle(orc, kind, t2, 0.0, 0.25, causal, 0, h)
+                assert np.array_equal(O, O2) and np.array_equal(lse, lse2), "scale invariance"
+                Oa, la = _att_oracle(orc, kind, t, 0.0, 0.25, causal, 0, h, rows=(0, 8))
+                Ob, lb = _att_oracle(orc, kind, t, 0.0, 0.25, causal, 0, h, rows=(8, S))
+                assert np.array_equal(np.concatenate([Oa, Ob]), O), "row ranges"
+                assert np.array_equal(np.concatenate([la, lb]), lse), "row ranges lse"
+    t = _att_case(NO_NORM, Bn, S, Hq, Hk, D, 1410)
+    t2 = (t[0] * 2,) + t[1:]
+    O, lse = _att_oracle(orc, NO_NORM, t, 0.0, 0.25, True, 0, 1)
+    O2, lse2 = _att_oracle(orc, NO_NORM, t2, 0.0, 0.125, True, 0, 1)
+    assert np.array_equal(O, O2) and np.array_equal(lse, lse2), "query scale against scale"
+
+
 ALL_PINS = [
     pin_bf16_decode,
     pin_bf16_rounding,
@@ -644,4 +769,7 @@ ALL_PINS = [
     pin_norm_linear_vs_torch,
     pin_norm_linear_permutation,
     pin_norm_linear_deferred_form,
+    pin_norm_attention_vs_torch,
+    pin_norm_attention_closed_forms,
+    pin_norm_attention_scale_invariance,
 ]

@@ -78,6 +78,34 @@ MUTATIONS = [
      "st = oracle_fwd_rows(kind, dtype, M, K, r0, r1, X, NULL, W, NULL, eps, y, NULL, NULL, NULL);"),
     ("projection of the first row only", "acc += y[o * K + k] * or_load(act, L, j * K + k);",
      "acc += y[k] * or_load(act, L, j * K + k);"),
+    ("attention scale dropped", "p[j] = scale * dot;", "p[j] = dot;"),
+    ("causal window without the diagonal", "const int64_t n = causal ? i + 1 : S;",
+     "const int64_t n = causal ? (i > 0 ? i : 1) : S;"),
+    ("grouped heads interleaved", "const int64_t hk = h / (Hq / Hk);",
+     "const int64_t hk = h % Hk;"),
+    ("key norm with the query gamma and beta",
+     "or_qk_row(kind, D, K, ((b * S + j) * Hk + hk) * D, Wk, Bk, eps, kn + j * D);",
+     "or_qk_row(kind, D, K, ((b * S + j) * Hk + hk) * D, Wq, Bq, eps, kn + j * D);"),
+    ("key norm dropped",
+     "or_qk_row(kind, D, K, ((b * S + j) * Hk + hk) * D, Wk, Bk, eps, kn + j * D);",
+     "or_qk_row(OR_NO_NORM, D, K, ((b * S + j) * Hk + hk) * D, Wk, Bk, eps, kn + j * D);"),
+    ("query beta dropped", "or_qk_row(kind, D, Q, ((b * S + i) * Hq + h) * D, Wq, Bq, eps, qn);",
+     "or_qk_row(kind, D, Q, ((b * S + i) * Hq + h) * D, Wq, NULL, eps, qn);"),
+    ("keys of the first batch only",
+     "or_qk_row(kind, D, K, ((b * S + j) * Hk + hk) * D, Wk, Bk, eps, kn + j * D);",
+     "or_qk_row(kind, D, K, ((0 * S + j) * Hk + hk) * D, Wk, Bk, eps, kn + j * D);"),
+    ("value row of the query position",
+     "acc += p[j] * or_load(OR_BF16, V, ((b * S + j) * Hk + hk) * D + d);",
+     "acc += p[j] * or_load(OR_BF16, V, ((b * S + i) * Hk + hk) * D + d);"),
+    ("value read from the query head", "acc += p[j] * or_load(OR_BF16, V, ((b * S + j) * Hk + hk) * D + d);",
+     "acc += p[j] * or_load(OR_BF16, V, ((b * S + j) * Hk + h % Hk) * D + d);"),
+    ("softmax normaliser dropped", "O[(i - s0) * D + d] = acc / z;", "O[(i - s0) * D + d] = acc;"),
+    ("lse without the largest logit", "if (lse) lse[i - s0] = mx + log(z);",
+     "if (lse) lse[i - s0] = log(z);"),
+    ("query norm weight index reversed", "double w = or_load(OR_BF16, W, d);",
+     "double w = or_load(OR_BF16, W, D - 1 - d);"),
+    ("QK LayerNorm bias sign", "(out[d] - mu) * rs * w + b : out[d] * rs * w;",
+     "(out[d] - mu) * rs * w - b : out[d] * rs * w;"),
 ]
 
 
