@@ -24,7 +24,7 @@ SOURCES = [
     "norm_team.hip", "norm_team_f32.hip", "norm_team_bf16.hip", "norm_team_bf16w.hip",
     "norm_team_f16.hip", "norm_team_f16w.hip", "norm_looped.hip", "norm_split.hip",
     "norm_xsplit.hip", "norm_noalloc.hip",
-    "norm_lazy.hip", "norm_lazy_check.cpp",
+    "norm_lazy.hip", "norm_lazy_check.cpp", "norm_attn.hip",
     "norm_abi.cpp", "norm_plan.cpp",
 ]
 

@@ -8,6 +8,7 @@
 #include <new>
 
 #include "norm_internal.hpp"
+#include "norm_attn.hpp"
 #include "norm_lazy.hpp"
 
 namespace {
@@ -276,6 +277,45 @@ norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int
   a.eps = eps;
   a.inv_k = 1.0f / (float)K;
   return dln::launch_lazy_linear(kind == NORM_LAYERNORM, a, static_cast<hipStream_t>(stream));
+}
+
+norm_status_t norm_attention_fwd(norm_kind_t kind, uint32_t flags, int64_t B, int64_t S,
+                                 int64_t Hq, int64_t Hk, int64_t D, const void *Q, int64_t ldq,
+                                 const void *K, int64_t ldk, const void *V, int64_t ldv,
+                                 const void *wq, const void *bq, const void *wk, const void *bk,
+                                 float eps, float scale, void *O, int64_t ldo, float *lse,
+                                 norm_stream_t stream) {
+  const EventsDisarm disarm;
+  const dln::AttnCheck ac{kind, flags, B, S, Hq, Hk, D, Q, K, V, ldq, ldk, ldv,
+                          wq, bq, wk, bk, eps, scale, O, ldo, lse};
+  const norm_status_t st = dln::check_attention(ac);
+  if (st != NORM_OK || B == 0 || S == 0) return st;
+  dln::AttnArgs a{};
+  a.q = static_cast<const uint16_t *>(Q);
+  a.k = static_cast<const uint16_t *>(K);
+  a.v = static_cast<const uint16_t *>(V);
+  a.wq = static_cast<const uint16_t *>(wq);
+  a.bq = static_cast<const uint16_t *>(bq);
+  a.wk = static_cast<const uint16_t *>(wk);
+  a.bk = static_cast<const uint16_t *>(bk);
+  a.o = static_cast<uint16_t *>(O);
+  a.lse = lse;
+  a.ldq = ldq;
+  a.ldk = ldk;
+  a.ldv = ldv;
+  a.ldo = ldo;
+  a.B = (int32_t)B;
+  a.S = (int32_t)S;
+  a.Hq = (int32_t)Hq;
+  a.Hk = (int32_t)Hk;
+  a.qblocks = (int32_t)((S + dln::kAttnBQ - 1) / dln::kAttnBQ);
+  a.eps = eps;
+  a.scale_log2 = (float)((double)scale * 1.4426950408889634);
+  const int norm = (flags & NORM_ATTN_NO_NORM) ? dln::ATTN_NO_NORM
+                   : kind == NORM_LAYERNORM    ? dln::ATTN_LAYERNORM
+                                               : dln::ATTN_RMSNORM;
+  return dln::launch_attention(norm, (flags & NORM_ATTN_CAUSAL) != 0, a,
+                               static_cast<hipStream_t>(stream));
 }
 
 } // extern "C"

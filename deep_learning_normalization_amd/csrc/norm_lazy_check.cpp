@@ -1,8 +1,10 @@
-// norm_lazy_check.cpp -- argument checks of norm_fold_projection and norm_lazy_linear (host
-// only, no device access): sizes, NULL pointers, overlaps and the layouts the product reads.
+// norm_lazy_check.cpp -- argument checks of the fused entry points, norm_fold_projection,
+// norm_lazy_linear and norm_attention_fwd (host only, no device access): sizes, NULL pointers,
+// overlaps and the layouts the kernels read.
 #include <cmath>
 #include <cstdint>
 
+#include "norm_attn.hpp"
 #include "norm_lazy.hpp"
 
 namespace dln {
@@ -102,6 +104,43 @@ norm_status_t check_lazy(const LazyCheck &c) {
   const void *ptrs[] = {c.X, c.G};
   if (c.K % 8 || c.ldx % 8 || c.ldg % 8 || common_align(ptrs, 2) < 16)
     return NORM_ERR_UNSUPPORTED;
+  return NORM_OK;
+}
+
+norm_status_t check_attention(const AttnCheck &c) {
+  const bool nonorm = (c.flags & NORM_ATTN_NO_NORM) != 0;
+  if (c.flags & ~(uint32_t)(NORM_ATTN_CAUSAL | NORM_ATTN_NO_NORM)) return NORM_ERR_INVALID_ARG;
+  if (!nonorm && !valid_kind(c.kind)) return NORM_ERR_INVALID_ARG;
+  if (c.B < 0 || c.S < 0 || c.Hq <= 0 || c.Hk <= 0 || c.D <= 0 || c.Hq % c.Hk != 0)
+    return NORM_ERR_INVALID_ARG;
+  if (c.B > kMaxN || c.S > kMaxN || c.Hq > kMaxN || c.D > kMaxN || c.Hq > kMaxN / c.D)
+    return NORM_ERR_INVALID_ARG;
+  if (!(c.eps >= 0.0f) || c.eps == INFINITY) return NORM_ERR_INVALID_ARG;
+  if (!(c.scale > 0.0f) || c.scale == INFINITY) return NORM_ERR_INVALID_ARG;
+  if (nonorm ? (c.wq || c.bq || c.wk || c.bk) : (!c.wq || !c.wk)) return NORM_ERR_INVALID_ARG;
+  if (!nonorm && c.kind == NORM_RMSNORM && (c.bq || c.bk)) return NORM_ERR_INVALID_ARG;
+  if (c.B == 0 || c.S == 0) return NORM_OK; // nothing to read or write
+  if (!c.Q || !c.K || !c.V || !c.O) return NORM_ERR_INVALID_ARG;
+  const int64_t T = c.B * c.S; // tokens
+  if (!stride_ok(T, c.Hq * c.D, c.ldq) || !stride_ok(T, c.Hk * c.D, c.ldk) ||
+      !stride_ok(T, c.Hk * c.D, c.ldv) || !stride_ok(T, c.Hq * c.D, c.ldo))
+    return NORM_ERR_INVALID_ARG;
+  const size_t nd = (size_t)c.D * 2;
+  const Span in[] = {{c.Q, span(T, c.Hq * c.D, c.ldq, 2)}, {c.K, span(T, c.Hk * c.D, c.ldk, 2)},
+                     {c.V, span(T, c.Hk * c.D, c.ldv, 2)}, {c.wq, nd}, {c.bq, nd},
+                     {c.wk, nd}, {c.bk, nd}};
+  const Span out[] = {{c.O, span(T, c.Hq * c.D, c.ldo, 2)},
+                      {c.lse, (size_t)c.B * (size_t)c.Hq * (size_t)c.S * 4}};
+  if (!disjoint(in, 7, out, 2)) return NORM_ERR_INVALID_ARG;
+  if ((uintptr_t)c.lse & 3u) return NORM_ERR_INVALID_ARG;
+  // the kernel: head size 128, 16-byte loads and stores of 8 values, a grid of one workgroup
+  // per 256 queries of each (batch, query head)
+  if (c.D != kAttnD) return NORM_ERR_UNSUPPORTED;
+  const void *ptrs[] = {c.Q, c.K, c.V, c.O, c.wq, c.bq, c.wk, c.bk};
+  if (c.ldq % 8 || c.ldk % 8 || c.ldv % 8 || c.ldo % 8 || common_align(ptrs, 8) < 16)
+    return NORM_ERR_UNSUPPORTED;
+  const int64_t qblocks = (c.S + kAttnBQ - 1) / kAttnBQ;
+  if (c.B * c.Hq > 0x7fffffffLL / qblocks) return NORM_ERR_UNSUPPORTED;
   return NORM_OK;
 }
 

@@ -5,7 +5,8 @@ arithmetic. The device path and the CPU oracle both receive exactly the tensors 
 (sampled in fp32 on the CPU, then cast to the storage dtype with round-to-nearest-even).
 
 Every tensor has its own generator, seeded with ``seed + offset``:
-X 0, W 1, B 2, dY 3, R 4, outlier-channel permutation 5, dH 6, projection L 7, its bias c 8.
+X 0, W 1, B 2, dY 3, R 4, outlier-channel permutation 5, dH 6, projection L 7, its bias c 8;
+attention Q 10, K 11, V 12, query gamma 13 and beta 14, key gamma 15 and beta 16.
 
 The pages print no data set for these kernels; the shapes follow the workloads they discuss
 (LLM hidden sizes, and the very-large-row regression class named on the page "PyTorch atinge
@@ -19,6 +20,7 @@ import numpy as np
 import torch
 
 OFF_X, OFF_W, OFF_B, OFF_DY, OFF_R, OFF_PERM, OFF_DH, OFF_L, OFF_C = 0, 1, 2, 3, 4, 5, 6, 7, 8
+OFF_Q, OFF_K, OFF_V, OFF_WQ, OFF_BQ, OFF_WK, OFF_BK = 10, 11, 12, 13, 14, 15, 16
 
 TORCH_DTYPES = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
@@ -219,6 +221,57 @@ RMS_LINEAR_BF16_16384x4096x4096 = Projection(
     "rmsnorm_linear_bf16_16384x4096x4096",
     replace(rms_hidden(4096, M=16384), name="rmsnorm_bf16_16384x4096_proj", dy=None), 4096,
     c=None)
+
+
+@dataclass(frozen=True)
+class Attention:
+    """Attention over B sequences of S tokens: Hq query heads of D dims reading Hk key/value
+    heads, with the query and key vectors normalised by `kind` ("layernorm", "rmsnorm" or
+    "none") before the scores. Gammas near 1.5 spread the logits over a few units, so the
+    softmax weights are neither flat nor one-hot."""
+    name: str
+    kind: str
+    B: int
+    S: int
+    Hq: int
+    Hk: int
+    D: int = 128
+    causal: bool = True
+    eps: float = 1e-6
+    q: Dist = normal(0.4, 1.3)
+    k: Dist = normal(-0.3, 0.8)
+    v: Dist = normal(0.0, 1.0)
+    gamma: Dist = normal(1.5, 0.5)
+    beta: Dist = normal(0.0, 0.3)
+    seed: int = 0
+
+    def with_shape(self, B, S, Hq, Hk, name=None, **kw):
+        return replace(self, B=B, S=S, Hq=Hq, Hk=Hk,
+                       name=name or "%s[%d,%d,%d,%d]" % (self.name, B, S, Hq, Hk), **kw)
+
+
+def make_attention(a: Attention) -> dict:
+    """CPU bf16 tensors Q [B, S, Hq, D], K and V [B, S, Hk, D], and the norm vectors wq, wk
+    (None without a norm), bq, bk (LayerNorm only, else None), each [D]."""
+    s = a.seed
+    bf = torch.bfloat16
+    out = {"Q": _draw(a.q, (a.B, a.S, a.Hq, a.D), s + OFF_Q).to(bf),
+           "K": _draw(a.k, (a.B, a.S, a.Hk, a.D), s + OFF_K).to(bf),
+           "V": _draw(a.v, (a.B, a.S, a.Hk, a.D), s + OFF_V).to(bf),
+           "wq": None, "bq": None, "wk": None, "bk": None}
+    if a.kind != "none":
+        out["wq"] = _draw(a.gamma, (a.D,), s + OFF_WQ).to(bf)
+        out["wk"] = _draw(a.gamma, (a.D,), s + OFF_WK).to(bf)
+    if a.kind == "layernorm":
+        out["bq"] = _draw(a.beta, (a.D,), s + OFF_BQ).to(bf)
+        out["bk"] = _draw(a.beta, (a.D,), s + OFF_BK).to(bf)
+    return out
+
+
+# A QK-norm attention layer at 4096 tokens: 2 sequences, 32 query heads of 128 dims over 8
+# key/value heads (grouped), RMSNorm on queries and keys, causal.
+ATTN_QKNORM_B2_S4096 = Attention("qknorm_attention_bf16_b2_s4096_hq32_hk8_d128_causal",
+                                 "rmsnorm", 2, 4096, 32, 8)
 
 
 def all_workloads():

@@ -46,7 +46,8 @@ SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fw
            "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats", "norm_workspace_size",
            "norm_workspace_bytes", "norm_workspace_status", "norm_plan",
            "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version",
-           "norm_fold_projection", "norm_lazy_linear", "norm_bwd_noalloc")
+           "norm_fold_projection", "norm_lazy_linear", "norm_bwd_noalloc",
+           "norm_attention_fwd")
 
 
 class NormError(RuntimeError):
@@ -114,12 +115,15 @@ def lib():
                                            vp, vp]
         L.norm_lazy_linear.argtypes = [i32, vp, i64, i64, i64, f32, vp, i64, i64, vp, vp, vp,
                                        vp, vp, vp, vp, i64, vp]
+        L.norm_attention_fwd.argtypes = [i32, ctypes.c_uint32, i64, i64, i64, i64, i64, vp, i64,
+                                         vp, i64, vp, i64, vp, vp, vp, vp, f32, f32, vp, i64, vp,
+                                         vp]
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
                      "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats",
                      "norm_workspace_size", "norm_workspace_status", "norm_plan",
                      "norm_set_tuning",
                      "norm_set_launch_events", "norm_fold_projection", "norm_lazy_linear",
-                     "norm_bwd_noalloc"):
+                     "norm_bwd_noalloc", "norm_attention_fwd"):
             getattr(L, name).restype = ctypes.c_int
         L.norm_version.restype = ctypes.c_int
         _lib = L
@@ -287,6 +291,49 @@ def norm_lazy_linear(kind, X, eps, G, s, t, Y, mean_in=None, rstd_in=None, mean_
                                 _ptr(mean_out), _ptr(rstd_out), _ptr(Y), _ld(Y),
                                 _stream(stream))
     _raise(st, "norm_lazy_linear")
+
+
+ATTN_CAUSAL, ATTN_NO_NORM = 1, 2
+
+
+def _token_stride(t, B, S, H, D, name):
+    """Elements between consecutive tokens of a CUDA bf16 [B, S, H, D] tensor whose tokens are
+    evenly spaced and whose (head, dim) block is contiguous."""
+    if t.dtype is not torch.bfloat16 or tuple(t.shape) != (B, S, H, D) or not t.is_cuda:
+        raise ValueError("%s must be a CUDA bfloat16 tensor of shape %s" % (name, (B, S, H, D)))
+    ld = t.stride(1) if S > 1 else (t.stride(0) if B > 1 else H * D)
+    if ((D > 1 and t.stride(3) != 1) or (H > 1 and t.stride(2) != D) or
+            (S > 1 and t.stride(1) != ld) or (B > 1 and t.stride(0) != S * ld)):
+        raise ValueError("%s: tokens must be evenly spaced with contiguous heads" % name)
+    return ld
+
+
+def norm_attention_fwd(kind, Q, K, V, wq, bq, wk, bk, eps, scale, O, lse=None, causal=False,
+                       normalize=True, stream=None):
+    """Queue attention over normalised queries and keys: Q, O [B, S, Hq, D], K, V
+    [B, S, Hk, D] (bf16, evenly spaced tokens, e.g. slices of one packed QKV tensor), gammas
+    wq, wk and betas bq, bk [D] bf16, lse [B, Hq, S] fp32 or None. normalize=False: the
+    queries and keys as given (the norm vectors must be None), as does kind "none"."""
+    Bn, S, Hq, D = Q.shape
+    Hk = K.shape[2]
+    ldq = _token_stride(Q, Bn, S, Hq, D, "Q")
+    ldk = _token_stride(K, Bn, S, Hk, D, "K")
+    ldv = _token_stride(V, Bn, S, Hk, D, "V")
+    ldo = _token_stride(O, Bn, S, Hq, D, "O")
+    for v, nm in ((wq, "wq"), (bq, "bq"), (wk, "wk"), (bk, "bk")):
+        _check_vec(v, D, torch.bfloat16, nm)
+    if lse is not None and (lse.dtype is not torch.float32 or tuple(lse.shape) != (Bn, Hq, S)
+                            or not lse.is_cuda or not lse.is_contiguous()):
+        raise ValueError("lse must be a contiguous CUDA float32 tensor of shape %s"
+                         % ((Bn, Hq, S),))
+    if kind == "none":
+        kind, normalize = RMSNORM, False
+    flags = (ATTN_CAUSAL if causal else 0) | (0 if normalize else ATTN_NO_NORM)
+    st = lib().norm_attention_fwd(_kind(kind), flags, Bn, S, Hq, Hk, D, _ptr(Q), ldq, _ptr(K),
+                                  ldk, _ptr(V), ldv, _ptr(wq), _ptr(bq), _ptr(wk), _ptr(bk),
+                                  float(eps), float(scale), _ptr(O), ldo, _ptr(lse),
+                                  _stream(stream, Q))
+    _raise(st, "norm_attention_fwd")
 
 
 def norm_bwd(kind, X, dY, dH, W, mean, rstd, eps, dX, dR, dW, dB, workspace, stream=None):
@@ -499,6 +546,21 @@ def lazy_linear(kind, X, eps, G, s=None, t=None, mean=None, rstd=None, stream=No
     Y = torch.empty(X.shape[0], G.shape[0], dtype=torch.bfloat16, device=X.device)
     norm_lazy_linear(kind, X, eps, G, s, t, Y, mean, rstd, None, None, stream)
     return Y
+
+
+def attention(kind, Q, K, V, wq=None, bq=None, wk=None, bk=None, eps=1e-6, scale=None,
+              causal=False, want_lse=False, stream=None):
+    """O (and lse when want_lse) of attention over queries and keys normalised by `kind` with
+    the given gammas (and betas); with wq and wk None (or kind "none") the queries and keys are
+    used as given."""
+    normalize = kind != "none" and (wq is not None or wk is not None)
+    D = Q.shape[3]
+    O = torch.empty(Q.shape, dtype=torch.bfloat16, device=Q.device)
+    lse = (torch.empty(Q.shape[0], Q.shape[2], Q.shape[1], dtype=torch.float32, device=Q.device)
+           if want_lse else None)
+    norm_attention_fwd(kind, Q, K, V, wq, bq, wk, bk, eps, D ** -0.5 if scale is None else scale,
+                       O, lse, causal, normalize, stream)
+    return (O, lse) if want_lse else O
 
 
 def backward(kind, X, dY, W, mean=None, rstd=None, eps=1e-5, dH=None, stream=None):

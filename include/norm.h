@@ -418,9 +418,49 @@ norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int
                                int64_t ldy, norm_stream_t stream);
 
 /*
+ * Attention over normalised queries and keys, in one kernel (web page "Towards Free
+ * Normalization: Fusing Normalization into GEMM and Attention Kernels", item 5: several norms
+ * fused around an attention kernel; the page gives no formulas, so the form below is this
+ * library's reading, QK-norm). Per batch b and query head h, with g = Hq / Hk query heads per
+ * key/value head (head h reads key/value head h / g):
+ *     q'_i = Norm_q(Q[b, i, h, :]),   k'_j = Norm_k(K[b, j, h / g, :])
+ *     O[b, i, h, :] = sum_j softmax_j(scale * q'_i . k'_j) V[b, j, h / g, :]
+ *     lse[b, h, i]  = ln sum_j exp(scale * q'_i . k'_j)
+ * over the keys j visible to query i: all S, or j <= i with NORM_ATTN_CAUSAL. Norm_q and Norm_k
+ * are the row norm of `kind` along the head dimension D (LayerNorm: (x - mean) * rstd * gamma
+ * + beta; RMSNorm: x * rstd * gamma; rstd = 1 / sqrt(var or mean square + eps)), with gamma
+ * wq, wk and beta bq, bk of D entries shared by all heads. With NORM_ATTN_NO_NORM the queries
+ * and keys are used as given (kind is ignored; the four vectors must be NULL): the attention
+ * half of the same computation done in two passes.
+ *   Q       [B, S, Hq, D] bf16: element (b, s, h, d) at (b * S + s) * ldq + h * D + d.
+ *   K, V    [B, S, Hk, D] bf16 with token strides ldk, ldv.
+ *   wq, wk  [D] bf16 gammas; bq, bk [D] bf16 betas or NULL (zero; LayerNorm only).
+ *   eps     added inside the square root, >= 0 and finite. scale > 0 and finite (usually
+ *           1 / sqrt(D)).
+ *   O       [B, S, Hq, D] bf16 out, token stride ldo; must not overlap any input.
+ *   lse     [B, Hq, S] fp32 out, or NULL.
+ *   Numerics: the normalised vectors are rounded once to bf16, scores and O accumulate in fp32
+ *   on the matrix cores, the softmax weights enter the second product as bf16, O is rounded
+ *   once to bf16 (nearest even).
+ *   Requirements: D == 128; ldq, ldk, ldv, ldo multiples of 8 and at least Hq * D (Hk * D for
+ *   K and V); Q, K, V, O and the norm vectors 16-byte aligned. Otherwise NORM_ERR_UNSUPPORTED
+ *   (head size, alignment) or NORM_ERR_INVALID_ARG (sizes, Hq not a multiple of Hk, NULL
+ *   pointers, eps, scale, flags, overlaps). B == 0 or S == 0: NORM_OK once the rest passes,
+ *   nothing launched and no pointer read. The launch allocates nothing.
+ */
+#define NORM_ATTN_CAUSAL 1u
+#define NORM_ATTN_NO_NORM 2u
+norm_status_t norm_attention_fwd(norm_kind_t kind, uint32_t flags, int64_t B, int64_t S,
+                                 int64_t Hq, int64_t Hk, int64_t D, const void *Q, int64_t ldq,
+                                 const void *K, int64_t ldk, const void *V, int64_t ldv,
+                                 const void *wq, const void *bq, const void *wk, const void *bk,
+                                 float eps, float scale, void *O, int64_t ldo, float *lse,
+                                 norm_stream_t stream);
+
+/*
  * Kernel timing for profilers and benchmarks. Arms two HIP events (hipEvent_t, created by the
  * caller on the device of the stream that will be used) for the calling thread's next call of
- * norm_fwd, norm_bwd, norm_bwd_fused or norm_bwd_reduce: `start_event` takes the start
+ * norm_fwd, norm_bwd, norm_bwd_fused, norm_bwd_reduce or norm_attention_fwd: `start_event` takes the start
  * timestamp of the first kernel that call launches and `stop_event` the end timestamp of its
  * last one (hipExtLaunchKernel; no extra packets are queued, so the stream runs as it would
  * without timing). hipEventElapsedTime of the pair is then the GPU time of that call's kernels.
