@@ -23,6 +23,11 @@ stream mix); and the CPU oracle timed on this host as a reported baseline.
 --sweep also times the registry's other workloads (ragged row, hidden 16384, fp16, fp32
 weights) into `shapes`.
 
+`attention`: attention over RMSNorm-normalised queries and keys (2 sequences x 4096 tokens, 32
+query heads over 8 key/value heads of 128, causal) fused into one call (norm_attention_fwd),
+against the same computation in two passes; --attention prints that for causal and full masks,
+4096 and 1024 tokens, RMSNorm and LayerNorm, one JSON line each.
+
 --projection instead measures the norm deferred into a following projection (norm_lazy_linear
 after norm_fold_projection) on its two workloads, next to the unfused pair (norm_fwd, then
 torch's 2-D product with the bias, which is hipBLASLt) and the bare hipBLASLt product, and
@@ -315,6 +320,114 @@ def projection(p, torch, nl, steps, warmup):
     return out
 
 
+def attention_flops(a):
+    """Matrix-product flops of one call: 2 * D per (query, visible key) pair for each of the two
+    products, every query head of every sequence."""
+    pairs = a.S * (a.S + 1) // 2 if a.causal else a.S * a.S
+    return 4 * a.B * a.Hq * a.D * pairs
+
+
+def attention_cpu_baseline(a, rows=32):
+    """The oracle on `rows` queries at the end of one head (each sees all S keys), scaled to
+    the whole call's flops per second; single-threaded cost measured with the oracle's
+    threads."""
+    import oracle
+    from deep_learning_normalization_amd import inputs
+    t = inputs.make_attention(a)
+    hb = inputs.host_bits
+    kind = {"rmsnorm": oracle.RMSNORM, "layernorm": oracle.LAYERNORM, "none": oracle.NO_NORM}
+    args = [hb(t[n]) for n in ("Q", "K", "V", "wq", "bq", "wk", "bk")]
+    t0 = time.perf_counter()
+    oracle.norm_attention(kind[a.kind], *args, eps=a.eps, scale=a.D ** -0.5, causal=a.causal,
+                          b=0, h=0, rows=(a.S - rows, a.S))
+    sec = time.perf_counter() - t0
+    flops = 4 * a.D * sum((s + 1) if a.causal else a.S for s in range(a.S - rows, a.S))
+    return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
+            "cores": oracle.num_threads(), "seconds": round(sec, 3),
+            "sample": "%d queries of one head at the end of the sequence (each against %s keys), "
+                      "key norms of that head included" % (rows, "its preceding" if a.causal
+                                                           else "all %d" % a.S)}
+
+
+def attention_bench(a, torch, nl, steps, warmup, cpu=False):
+    """Attention over normalised queries and keys (norm_attention_fwd with a workspace: the key
+    pass, then the attention kernel with the queries normalised inside it) against the same
+    computation in two passes (norm_fwd on the query vectors and on the key vectors, then the
+    attention kernel without a norm), and that attention kernel alone on the normalised
+    inputs. Inputs stay resident (Q, K, V: 100 MB at 2 x 4096 x (32 + 8 + 8) heads x 128). The
+    forms alternate call by call, each call bracketed by its own pair of HIP events on the
+    stream, because the clock drifts by several percent over seconds of matrix-core load; the
+    figures are medians over `steps` calls of each form."""
+    from deep_learning_normalization_amd import inputs
+    dev = "cuda"
+    t = {k: (v.to(dev) if v is not None else None) for k, v in inputs.make_attention(a).items()}
+    Q, K, V = t["Q"], t["K"], t["V"]
+    O = torch.empty_like(Q)
+    ws = torch.empty(nl.attention_workspace_bytes(a.B, a.S, a.Hk, a.D), dtype=torch.uint8,
+                     device=dev)
+    Qn, Kn = torch.empty_like(Q), torch.empty_like(K)
+    rq = torch.empty(Q.numel() // a.D, device=dev)
+    rk = torch.empty(K.numel() // a.D, device=dev)
+    mq = torch.empty_like(rq) if a.kind == "layernorm" else None
+    mk = torch.empty_like(rk) if a.kind == "layernorm" else None
+    scale = a.D ** -0.5
+
+    def fused():
+        nl.norm_attention_fwd(a.kind, Q, K, V, t["wq"], t["bq"], t["wk"], t["bk"], a.eps, scale,
+                              O, None, a.causal, workspace=ws)
+
+    def alone():
+        nl.norm_attention_fwd("none", Qn, Kn, V, None, None, None, None, a.eps, scale, O, None,
+                              a.causal)
+
+    def unfused():
+        nl.norm_fwd(a.kind, Q.view(-1, a.D), None, t["wq"], t["bq"], a.eps, Qn.view(-1, a.D),
+                    None, mq, rq)
+        nl.norm_fwd(a.kind, K.view(-1, a.D), None, t["wk"], t["bk"], a.eps, Kn.view(-1, a.D),
+                    None, mk, rk)
+        alone()
+
+    forms = {"fused": fused, "unfused": unfused, "attention_alone": alone}
+    evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)] for k in forms}
+    t_end = time.perf_counter() + 0.5  # the clock settles under load
+    i = 0
+    while time.perf_counter() < t_end or i < warmup:
+        for f in forms.values():
+            f()
+        i += 1
+        torch.cuda.synchronize()
+    for j in range(steps):
+        for k, f in forms.items():
+            evs[k][j][0].record()
+            f()
+            evs[k][j][1].record()
+    torch.cuda.synchronize()
+    med = {}
+    for k in forms:
+        d = sorted(a0.elapsed_time(a1) * 1e3 for a0, a1 in evs[k])
+        med[k] = d[len(d) // 2]
+    flops = attention_flops(a)
+    tf = flops / (med["fused"] * 1e-6) / 1e12
+    out = {"workload": a.name, "kind": a.kind, "B": a.B, "S": a.S, "Hq": a.Hq, "Hk": a.Hk,
+           "D": a.D, "causal": a.causal, "dtype": "bf16", "flops_per_call": flops,
+           "fused_us": round(med["fused"], 2), "unfused_us": round(med["unfused"], 2),
+           "attention_alone_us": round(med["attention_alone"], 2),
+           "fused_speedup_vs_unfused": round(med["unfused"] / med["fused"], 4),
+           "what": "norm_attention_fwd (key pass + attention with in-kernel query norm) vs "
+                   "norm_fwd(Q) + norm_fwd(K) + attention; medians of alternating calls",
+           "roofline": {"bound": "mfma", "kernel": "attn_fwd_kernel (whole fused call: key pass "
+                        "included)", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
+                        "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
+                        "traffic": None}}
+    out["attention_alone_TFLOPs"] = round(flops / (med["attention_alone"] * 1e-6) / 1e12, 1)
+    if cpu:
+        out["cpu_baseline"] = attention_cpu_baseline(a)
+    del t, Q, K, V, O, ws, Qn, Kn
+    torch.cuda.empty_cache()
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -328,6 +441,9 @@ def main():
                          "fp16, fp32 weights)")
     ap.add_argument("--projection", action="store_true",
                     help="measure the norm deferred into a following projection instead")
+    ap.add_argument("--attention", action="store_true",
+                    help="measure attention over normalised queries and keys instead (causal "
+                         "and full, 4096 and 1024 tokens)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -347,6 +463,19 @@ def main():
     if args.projection:
         for p in (inputs.LN_LINEAR_BF16_16384x4096x4096, inputs.RMS_LINEAR_BF16_16384x4096x4096):
             print(json.dumps(projection(p, torch, nl, args.steps, args.warmup)), flush=True)
+        return
+    if args.attention:
+        from dataclasses import replace
+        base = inputs.ATTN_QKNORM_B2_S4096
+        for S in (4096, 1024):
+            for causal in (True, False):
+                for kind in ("rmsnorm", "layernorm"):
+                    a = replace(base, S=S, causal=causal, kind=kind,
+                                name="qknorm_attention_bf16_b2_s%d_hq32_hk8_d128_%s_%s" % (
+                                    S, "causal" if causal else "full", kind))
+                    print(json.dumps(attention_bench(a, torch, nl, min(args.steps, 50),
+                                                     args.warmup, cpu=(S == 4096 and causal))),
+                          flush=True)
         return
 
     def say(msg):
@@ -422,6 +551,9 @@ def main():
             shapes.append(e)
             torch.cuda.empty_cache()
         line["shapes"] = shapes
+        say("attention %s" % inputs.ATTN_QKNORM_B2_S4096.name)
+        line["attention"] = attention_bench(inputs.ATTN_QKNORM_B2_S4096, torch, nl, 30,
+                                            args.warmup, cpu=not args.no_cpu_baseline)
     if not args.no_cpu_baseline:
         say("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(w)

@@ -284,12 +284,14 @@ norm_status_t norm_attention_fwd(norm_kind_t kind, uint32_t flags, int64_t B, in
                                  const void *K, int64_t ldk, const void *V, int64_t ldv,
                                  const void *wq, const void *bq, const void *wk, const void *bk,
                                  float eps, float scale, void *O, int64_t ldo, float *lse,
+                                 void *workspace, size_t workspace_bytes,
                                  norm_stream_t stream) {
   const EventsDisarm disarm;
   const dln::AttnCheck ac{kind, flags, B, S, Hq, Hk, D, Q, K, V, ldq, ldk, ldv,
-                          wq, bq, wk, bk, eps, scale, O, ldo, lse};
+                          wq, bq, wk, bk, eps, scale, O, ldo, lse, workspace, workspace_bytes};
   const norm_status_t st = dln::check_attention(ac);
   if (st != NORM_OK || B == 0 || S == 0) return st;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
   dln::AttnArgs a{};
   a.q = static_cast<const uint16_t *>(Q);
   a.k = static_cast<const uint16_t *>(K);
@@ -310,12 +312,38 @@ norm_status_t norm_attention_fwd(norm_kind_t kind, uint32_t flags, int64_t B, in
   a.Hk = (int32_t)Hk;
   a.qblocks = (int32_t)((S + dln::kAttnBQ - 1) / dln::kAttnBQ);
   a.eps = eps;
+  a.scale = scale;
   a.scale_log2 = (float)((double)scale * 1.4426950408889634);
   const int norm = (flags & NORM_ATTN_NO_NORM) ? dln::ATTN_NO_NORM
                    : kind == NORM_LAYERNORM    ? dln::ATTN_LAYERNORM
                                                : dln::ATTN_RMSNORM;
-  return dln::launch_attention(norm, (flags & NORM_ATTN_CAUSAL) != 0, a,
-                               static_cast<hipStream_t>(stream));
+  // keys read by many (query block, query head) pairs: normalise them once, into the
+  // workspace, instead of in every query block
+  const size_t kbytes = dln::attention_workspace_bytes(B, S, Hk, D);
+  const int force = dln::tuning().attn_key_pass;
+  const bool key_pass = norm != dln::ATTN_NO_NORM && workspace && kbytes &&
+                        workspace_bytes >= kbytes && force != 0 &&
+                        (force == 1 || (int64_t)a.qblocks * (Hq / Hk) >= dln::kAttnKeyPassReuse);
+  if (key_pass) {
+    dln::KnormArgs ka{};
+    ka.k = a.k;
+    ka.wk = a.wk;
+    ka.bk = a.bk;
+    ka.out = static_cast<uint16_t *>(workspace);
+    ka.nkeys = B * S * Hk;
+    ka.ldk = ldk;
+    ka.Hk = (int32_t)Hk;
+    ka.eps = eps;
+    const norm_status_t ks = dln::launch_key_norm(norm == dln::ATTN_LAYERNORM, ka, hs);
+    if (ks != NORM_OK) return ks;
+    a.k = ka.out;
+    a.ldk = Hk * D;
+  }
+  return dln::launch_attention(norm, key_pass, (flags & NORM_ATTN_CAUSAL) != 0, a, hs);
+}
+
+size_t norm_attention_workspace_bytes(int64_t B, int64_t S, int64_t Hk, int64_t D) {
+  return dln::attention_workspace_bytes(B, S, Hk, D);
 }
 
 } // extern "C"

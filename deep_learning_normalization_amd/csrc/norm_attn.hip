@@ -18,16 +18,22 @@
 //              queries' normalised vectors (bf16) in registers as the B operand of S^T = K Q^T:
 //              lane l then owns query l % 32 and half (l / 32) of the keys of each 32-key MFMA
 //              block, so a query's running maximum and sum stay in its two lanes.
-//   key tiles  64 keys at a time through double-buffered LDS. Wavefronts 4-7 load K, normalise
-//              each key vector (16 lanes per key, DPP row sums) and store it as bf16; wavefronts
-//              0-3 load V and store it transposed, so that O^T = V^T P^T takes its B operand P
+//   key tiles  64 keys at a time through double-buffered LDS. Wavefronts 4-7 copy K as it is
+//              and form each key's statistics (16 lanes per key, DPP row sums); wavefronts 0-3
+//              load V and store it transposed, so that O^T = V^T P^T takes its B operand P
 //              straight from the score registers (MFMA 32x32x16 bf16, fp32 accumulation, for
 //              both products). The next tile's global loads are in flight during the products.
+//   key norm   deferred past the product, as a norm into a matrix product can be (the page's
+//              items 3-4): the key gamma is folded into each query once, and each key's rstd
+//              (and, for LayerNorm, -rstd * mean) scales its column of scores in fp32. A key is
+//              read by every query block of every query head of its group; normalising it
+//              there in full would repeat that vector work for each of them.
 //
-// Numerics: the normalised vectors are rounded once to bf16 (as a separate norm pass would
-// store them), the scores and the output accumulate in fp32, the weights P are rounded to bf16
-// for the second product, and O is rounded once to bf16.
+// Numerics: the normalised queries, times the key gamma, are rounded once to bf16; the keys
+// enter the product exactly; scores and output accumulate in fp32, the weights P are rounded to
+// bf16 for the second product, and O is rounded once to bf16.
 #include <cmath>
+#include <type_traits>
 
 #include "norm_attn.hpp"
 #include "norm_device.hpp"
@@ -83,12 +89,16 @@ __device__ __forceinline__ uint4 pack8(const float (&f)[8]) {
                     pack_bf16x2(f[6], f[7]));
 }
 
-template <int NORM, bool CAUSAL>
+template <int NORM, bool KPRE, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t sk[2][BK * kKRow];
   __shared__ __align__(16) uint16_t svt[2][D * kVRow];
+  __shared__ __align__(16) float srs[2][BK];  // per key of the tile: rstd
+  __shared__ __align__(16) float snm[2][BK];  // per key: -rstd * mean (LayerNorm)
   constexpr bool LN = NORM == ATTN_LAYERNORM;
   constexpr bool NORMED = NORM != ATTN_NO_NORM;
+  // KPRE: the keys arrive normalised (by attn_knorm_kernel); else their norm is deferred
+  constexpr bool DEFER = NORMED && !KPRE;
   constexpr float kInvD = 1.0f / (float)D;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int half = lane >> 5, col = lane & 31;
@@ -109,64 +119,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   const bool wactive = wq0 < S;
   const int wlast = min(wq0 + 31, S - 1);
 
-  // ---- this wavefront's queries, normalised, as MFMA B operands: lane l holds dims
-  // 16ks + 8h .. 16ks + 8h + 7 of query l % 32 in qf[ks]
   bf16x8_t qf[8];
-  {
-    const int qrow = myq < S ? myq : S - 1;
-    const uint16_t *qp = a.q + ((int64_t)b * S + qrow) * a.ldq + (int64_t)head * D + half * 8;
-    float x[8][8];
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) unpack8(*reinterpret_cast<const uint4 *>(qp + ks * 16), x[ks]);
-    if constexpr (NORMED) {
-      float mean = 0.0f;
-      if constexpr (LN) {
-        float s = 0.0f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-          for (int i = 0; i < 8; ++i) s += x[ks][i];
-        s += __shfl_xor(s, 32);
-        mean = s * kInvD;
-      }
-      float q2 = 0.0f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float d = x[ks][i] - mean;
-          q2 = __builtin_fmaf(d, d, q2);
-        }
-      q2 += __shfl_xor(q2, 32);
-      const float rstd = rsqrt_f32(q2 * kInvD + a.eps);
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        float g[8], be[8];
-        unpack8(*reinterpret_cast<const uint4 *>(a.wq + ks * 16 + half * 8), g);
-        if constexpr (LN)
-          unpack8(a.bq ? *reinterpret_cast<const uint4 *>(a.bq + ks * 16 + half * 8)
-                       : make_uint4(0u, 0u, 0u, 0u),
-                  be);
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const float y = (x[ks][i] - mean) * rstd * g[i];
-          x[ks][i] = LN ? y + be[i] : y;
-        }
-      }
-    }
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, pack8(x[ks]));
-  }
+  float c1 = 0.0f, c2 = 0.0f;
 
   // ---- staging roles: wavefronts 4-7 stage K, 0-3 stage V. Thread st of a role owns the
   // 16-byte chunk sc (dims 8sc .. 8sc+7) of K rows srow + 16i, or of V keys 4srow + i, i < 4.
   const bool kstage = wave >= 4;
   const int st = t & 255, sc = st & 15, srow = st >> 4;
-  uint4 gk = make_uint4(0u, 0u, 0u, 0u), bk = gk;
-  if (NORMED && kstage) {
-    gk = *reinterpret_cast<const uint4 *>(a.wk + sc * 8);
-    if (LN && a.bk) bk = *reinterpret_cast<const uint4 *>(a.bk + sc * 8);
-  }
   const uint16_t *sbase = kstage ? a.k : a.v;
   const int64_t sld = kstage ? a.ldk : a.ldv;
   sbase += (int64_t)b * S * sld + (int64_t)hk * D + sc * 8;
@@ -182,34 +141,43 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   auto stage_tile = [&](int buf) {
     if (kstage) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float x[8];
-        unpack8(pre[i], x);
-        if constexpr (NORMED) {
-          float mean = 0.0f;
-          if constexpr (LN) {
-            float s = 0.0f;
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<uint4 *>(&sk[buf][(srow + 16 * i) * kKRow + sc * 8]) = pre[i];
+      if constexpr (DEFER) {
+        // the statistics of the four keys, two passes over each key's 128 values (16 lanes,
+        // DPP row sums; the four rows interleaved)
+        float x[4][8], mean[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q2[4];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) s += x[e];
-            mean = row16_sum(s) * kInvD;
+        for (int i = 0; i < 4; ++i) unpack8(pre[i], x[i]);
+        if constexpr (LN) {
+          float sm[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            sm[i] = 0.0f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) sm[i] += x[i][e];
           }
-          float q2 = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) mean[i] = row16_sum(sm[i]) * kInvD;
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          q2[i] = 0.0f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float d = x[e] - mean;
-            q2 = __builtin_fmaf(d, d, q2);
-          }
-          const float rstd = rsqrt_f32(row16_sum(q2) * kInvD + a.eps);
-          float g[8], be[8];
-          unpack8(gk, g);
-          if constexpr (LN) unpack8(bk, be);
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float y = (x[e] - mean) * rstd * g[e];
-            x[e] = LN ? y + be[e] : y;
+            const float d = x[i][e] - mean[i];
+            q2[i] = __builtin_fmaf(d, d, q2[i]);
           }
         }
-        *reinterpret_cast<uint4 *>(&sk[buf][(srow + 16 * i) * kKRow + sc * 8]) = pack8(x);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) q2[i] = rsqrt_f32(row16_sum(q2[i]) * kInvD + a.eps);
+        if (sc == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            srs[buf][srow + 16 * i] = q2[i];
+            if (LN) snm[buf][srow + 16 * i] = -q2[i] * mean[i];
+          }
+        }
       }
     } else {
       // keys 4srow .. 4srow+3 land in four consecutive slots (see vt_off)
@@ -241,16 +209,22 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   for (int dt = 0; dt < 4; ++dt)
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
-  float m = -INFINITY, l = 0.0f;  // running maximum (log2 units) and this lane's share of the sum
+  // m: the exponent offset (log2 units) of this query's weights, kept within kSlack of the
+  // running maximum: O and l are rescaled only when the maximum outgrows it, so the weights
+  // stay below 2^kSlack. l: this lane's share of the sum of the weights.
+  constexpr float kSlack = 8.0f;
+  float m = -INFINITY, l = 0.0f;
 
-  load_tile(0);
-  stage_tile(0);
-  __syncthreads();
-  for (int kb = 0; kb < nkt; ++kb) {
+  // One key tile: the two products and the softmax update between them. MASK: the tile holds
+  // keys past the end or (causal) after some query of the workgroup; only those tiles pay for
+  // the per-score test, and only there do wavefronts whose queries all precede the tile skip
+  // it. Every wavefront of the workgroup takes part in the staging and the barrier.
+  auto tile = [&](int kb, auto mask_tag) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     const int buf = kb & 1;
     if (kb + 1 < nkt) load_tile(kb + 1);
     const int k0 = kb * BK;
-    if (wactive && (!CAUSAL || k0 <= wlast)) {
+    if (!MASK || (wactive && (!CAUSAL || k0 <= wlast))) {
       f32x16_t s[2];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
@@ -264,8 +238,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
           const bf16x8_t kf = *reinterpret_cast<const bf16x8_t *>(kp + j * 32 * kKRow + ks * 16);
           s[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[j], 0, 0, 0);
         }
-      // keys past the end, and (causal) keys after the query
-      if (k0 + BK > S || (CAUSAL && k0 + BK - 1 > wq0)) {
+      // the key statistics: register r of block j is key 32j + 8(r/4) + 4h + r%4
+      if constexpr (DEFER) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int g = 0; g < 4; ++g) {
+            const int k4 = 32 * j + 8 * g + 4 * half;
+            const float4 rs = *reinterpret_cast<const float4 *>(&srs[buf][k4]);
+            const float rv[4] = {rs.x, rs.y, rs.z, rs.w};
+            if constexpr (LN) {
+              const float4 nm = *reinterpret_cast<const float4 *>(&snm[buf][k4]);
+              const float nv[4] = {nm.x, nm.y, nm.z, nm.w};
+#pragma unroll
+              for (int i = 0; i < 4; ++i)
+                s[j][4 * g + i] = __builtin_fmaf(s[j][4 * g + i], rv[i], nv[i] * c1);
+            } else {
+#pragma unroll
+              for (int i = 0; i < 4; ++i) s[j][4 * g + i] *= rv[i];
+            }
+          }
+      }
+      if constexpr (MASK) {
 #pragma unroll
         for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -279,25 +273,28 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[j][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, 32)) * c;
       // key 0 is in the first tile of every query, so m is finite from the first tile on
-      const float mnew = fmaxf(m, mx * c);
-      const float alpha = __builtin_amdgcn_exp2f(m - mnew);
-      m = mnew;
-      float ls = 0.0f;
+      if (__any(mx > m + kSlack)) {
+        // a real branch: the compiler would otherwise turn it into 64 multiplies by 1
+        asm volatile("" ::: "memory");
+        const float mnew = fmaxf(m, mx);
+        const float alpha = __builtin_amdgcn_exp2f(m - mnew);
+        m = mnew;
+        l *= alpha;
+#pragma unroll
+        for (int dt = 0; dt < 4; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
+      }
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -mnew));
+          const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[j][r], c, -m));
           s[j][r] = p;
-          ls += p;
+          l += p;
         }
-      l = __builtin_fmaf(l, alpha, ls);
-#pragma unroll
-      for (int dt = 0; dt < 4; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] *= alpha;
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
         const int j = ss >> 1, r0 = 8 * (ss & 1);
@@ -316,9 +313,94 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     }
     if (kb + 1 < nkt) stage_tile(buf ^ 1);
     __syncthreads();
+  };
+
+  // Tiles before kb_mask need no test for any query of the workgroup: they end at or before
+  // the last whole tile of the sequence and (causal) before the workgroup's first query.
+  int kb_mask = S / BK;
+  if (CAUSAL && q0 / BK < kb_mask) kb_mask = q0 / BK;
+  if (kb_mask > nkt) kb_mask = nkt;
+  load_tile(0);  // in flight while the queries are normalised
+  // ---- this wavefront's queries as MFMA B operands: lane l holds dims 16ks + 8h .. +7 of
+  // query l % 32 in qf[ks]. With a norm, the query is normalised (q') and the key gamma is
+  // folded in: qf = bf16(q' * gamma_k). The keys then enter the product as they are and their
+  // own statistics scale the scores (the key norm deferred past the product):
+  //   q' . k'_j = rstd_j * (qf . k_j) [- rstd_j * mean_j * sum_d qf_d + q' . beta_k]
+  // (bracket: LayerNorm). The last term is the same for every key of the query, so the softmax
+  // drops it; it returns in lse (c2).
+  {
+    const int qrow = myq < S ? myq : S - 1;
+    const uint16_t *qp = a.q + ((int64_t)b * S + qrow) * a.ldq + (int64_t)head * D + half * 8;
+    float x[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) unpack8(*reinterpret_cast<const uint4 *>(qp + ks * 16), x[ks]);
+    if constexpr (NORMED) {
+      float mean = 0.0f;
+      if constexpr (LN) {
+        float s = 0.0f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int i = 0; i < 8; ++i) s += x[ks][i];
+        s += __shfl_xor(s, 32);
+        mean = s * kInvD;
+      }
+      float q2 = 0.0f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const float d = x[ks][i] - mean;
+          q2 = __builtin_fmaf(d, d, q2);
+        }
+      q2 += __shfl_xor(q2, 32);
+      const float rstd = rsqrt_f32(q2 * kInvD + a.eps);
+      const uint4 zero = make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        const int d0 = ks * 16 + half * 8;
+        float g[8], be[8], gk[8], bk[8];
+        unpack8(*reinterpret_cast<const uint4 *>(a.wq + d0), g);
+        if constexpr (LN) unpack8(a.bq ? *reinterpret_cast<const uint4 *>(a.bq + d0) : zero, be);
+        if constexpr (DEFER) {
+          unpack8(*reinterpret_cast<const uint4 *>(a.wk + d0), gk);
+          if constexpr (LN) unpack8(a.bk ? *reinterpret_cast<const uint4 *>(a.bk + d0) : zero, bk);
+        }
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          float y = (x[ks][i] - mean) * rstd * g[i];  // q'
+          if constexpr (LN) y += be[i];
+          if constexpr (DEFER) {
+            if constexpr (LN) c2 = __builtin_fmaf(y, bk[i], c2);
+            y *= gk[i];
+          }
+          x[ks][i] = y;
+        }
+      }
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 w = pack8(x[ks]);
+      qf[ks] = __builtin_bit_cast(bf16x8_t, w);
+      if constexpr (LN && DEFER) {  // the sum of the rounded values the product sees
+        const unsigned u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c1 += bf16_lo(u[i]) + bf16_hi(u[i]);
+      }
+    }
+    if constexpr (LN && DEFER) {
+      c1 += __shfl_xor(c1, 32);
+      c2 += __shfl_xor(c2, 32);
+    }
   }
 
-  // ---- O = O^T's column / sum, rounded once; lse = ln(sum) + max
+  stage_tile(0);
+  __syncthreads();
+  int kb = 0;
+  for (; kb < kb_mask; ++kb) tile(kb, std::false_type{});
+  for (; kb < nkt; ++kb) tile(kb, std::true_type{});
+
+  // ---- O = O^T's column / sum, rounded once; lse = ln(sum) + offset (+ the dropped term)
   const float lt = l + __shfl_xor(l, 32);
   if (wactive && myq < S) {
     const float inv = 1.0f / lt;
@@ -332,28 +414,86 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
                                    pack_bf16x2(o[dt][4 * g + 2] * inv, o[dt][4 * g + 3] * inv));
         *reinterpret_cast<uint2 *>(op + 32 * dt + 8 * g) = w;
       }
-    if (a.lse && half == 0)
-      a.lse[((int64_t)b * a.Hq + head) * S + myq] = (m + __log2f(lt)) * 0.69314718055994531f;
+    if (a.lse && half == 0) {
+      float v = (m + __log2f(lt)) * 0.69314718055994531f;
+      if constexpr (LN && DEFER) v = __builtin_fmaf(a.scale, c2, v);
+      a.lse[((int64_t)b * a.Hq + head) * S + myq] = v;
+    }
   }
 }
 
-template <int NORM>
+// The key norm as a pass of its own, for calls whose keys are each read by many query blocks
+// and heads: 16 lanes per key vector (8 values each; two passes over the values in registers,
+// DPP row sums), y = (x - mean) * rstd * gamma (+ beta), rounded once to bf16, stored densely
+// as [B * S][Hk][D].
+template <bool LN>
+__global__ __launch_bounds__(256) void attn_knorm_kernel(KnormArgs a) {
+  constexpr float kInvD = 1.0f / (float)D;
+  const int t = threadIdx.x, sc = t & 15;
+  const int64_t kv = (int64_t)blockIdx.x * 16 + (t >> 4);
+  const int64_t kvc = kv < a.nkeys ? kv : a.nkeys - 1;
+  const int64_t tok = kvc / a.Hk, h = kvc - tok * a.Hk;
+  float x[8], g[8], be[8];
+  unpack8(*reinterpret_cast<const uint4 *>(a.k + tok * a.ldk + h * D + sc * 8), x);
+  unpack8(*reinterpret_cast<const uint4 *>(a.wk + sc * 8), g);
+  if constexpr (LN)
+    unpack8(a.bk ? *reinterpret_cast<const uint4 *>(a.bk + sc * 8) : make_uint4(0u, 0u, 0u, 0u),
+            be);
+  float mean = 0.0f;
+  if constexpr (LN) {
+    float sm = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sm += x[e];
+    mean = row16_sum(sm) * kInvD;
+  }
+  float q2 = 0.0f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float d = x[e] - mean;
+    q2 = __builtin_fmaf(d, d, q2);
+  }
+  const float rstd = rsqrt_f32(row16_sum(q2) * kInvD + a.eps);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    const float y = (x[e] - mean) * rstd * g[e];
+    x[e] = LN ? y + be[e] : y;
+  }
+  if (kv < a.nkeys) *reinterpret_cast<uint4 *>(a.out + kv * D + sc * 8) = pack8(x);
+}
+
+template <int NORM, bool KPRE>
 hipError_t launch_norm(bool causal, dim3 grid, dim3 block, hipStream_t s, const AttnArgs &a) {
-  return causal ? launch(attn_fwd_kernel<NORM, true>, grid, block, s, a)
-                : launch(attn_fwd_kernel<NORM, false>, grid, block, s, a);
+  return causal ? launch(attn_fwd_kernel<NORM, KPRE, true>, grid, block, s, a)
+                : launch(attn_fwd_kernel<NORM, KPRE, false>, grid, block, s, a);
 }
 
 } // namespace
 
-norm_status_t launch_attention(int norm, bool causal, const AttnArgs &a, hipStream_t s) {
+norm_status_t launch_key_norm(bool layernorm, const KnormArgs &a, hipStream_t s) {
+  const int64_t wg = (a.nkeys + 15) / 16;
+  if (wg <= 0 || wg > 0x7fffffffLL) return NORM_ERR_UNSUPPORTED;
+  const dim3 grid((unsigned)wg), block(256);
+  const hipError_t e = layernorm ? launch(attn_knorm_kernel<true>, grid, block, s, a)
+                                 : launch(attn_knorm_kernel<false>, grid, block, s, a);
+  return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+}
+
+norm_status_t launch_attention(int norm, bool keys_normed, bool causal, const AttnArgs &a,
+                               hipStream_t s) {
   const int64_t wg = (int64_t)a.B * a.Hq * a.qblocks;
   if (wg <= 0 || wg > 0x7fffffffLL) return NORM_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)wg), block(kThreads);
   hipError_t e;
   switch (norm) {
-  case ATTN_LAYERNORM: e = launch_norm<ATTN_LAYERNORM>(causal, grid, block, s, a); break;
-  case ATTN_RMSNORM: e = launch_norm<ATTN_RMSNORM>(causal, grid, block, s, a); break;
-  case ATTN_NO_NORM: e = launch_norm<ATTN_NO_NORM>(causal, grid, block, s, a); break;
+  case ATTN_LAYERNORM:
+    e = keys_normed ? launch_norm<ATTN_LAYERNORM, true>(causal, grid, block, s, a)
+                    : launch_norm<ATTN_LAYERNORM, false>(causal, grid, block, s, a);
+    break;
+  case ATTN_RMSNORM:
+    e = keys_normed ? launch_norm<ATTN_RMSNORM, true>(causal, grid, block, s, a)
+                    : launch_norm<ATTN_RMSNORM, false>(causal, grid, block, s, a);
+    break;
+  case ATTN_NO_NORM: e = launch_norm<ATTN_NO_NORM, false>(causal, grid, block, s, a); break;
   default: return NORM_ERR_INVALID_ARG;
   }
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;

@@ -23,10 +23,30 @@ struct AttnArgs {
   int32_t B, S, Hq, Hk;
   int32_t qblocks;                    // ceil(S / kAttnBQ)
   float eps;
+  float scale;                        // the logit scale
   float scale_log2;                   // the logit scale times log2(e)
 };
 
-norm_status_t launch_attention(int norm, bool causal, const AttnArgs &a, hipStream_t s);
+// The keys normalised by a pass of their own into a dense [B * S][Hk][D] bf16 buffer.
+struct KnormArgs {
+  const uint16_t *k;                  // bf16 [B][S][Hk][D], token stride ldk
+  const uint16_t *wk, *bk;            // bf16 [D]; bk nullptr: no beta
+  uint16_t *out;                      // bf16 [B * S * Hk][D]
+  int64_t nkeys;                      // B * S * Hk
+  int64_t ldk;
+  int32_t Hk;
+  float eps;
+};
+
+// A call whose keys are each read by at least this many (query block, query head) pairs
+// normalises them in a pass of its own when the caller gives a workspace.
+constexpr int64_t kAttnKeyPassReuse = 8;
+
+norm_status_t launch_key_norm(bool layernorm, const KnormArgs &a, hipStream_t s);
+// keys_normed: a.k holds keys normalised by launch_key_norm (the queries are still normalised
+// by the attention kernel).
+norm_status_t launch_attention(int norm, bool keys_normed, bool causal, const AttnArgs &a,
+                               hipStream_t s);
 
 // norm_attention_fwd's checks (NORM_OK, NORM_ERR_INVALID_ARG, or NORM_ERR_UNSUPPORTED for a
 // head size or layout the kernel does not read).
@@ -41,7 +61,12 @@ struct AttnCheck {
   const void *O;
   int64_t ldo;
   const float *lse;
+  const void *workspace;
+  size_t workspace_bytes;
 };
+
+// Bytes of workspace the key-norm pass needs (0 for sizes past what it addresses).
+size_t attention_workspace_bytes(int64_t B, int64_t S, int64_t Hk, int64_t D);
 norm_status_t check_attention(const AttnCheck &c);
 
 } // namespace dln

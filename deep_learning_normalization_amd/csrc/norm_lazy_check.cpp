@@ -129,19 +129,30 @@ norm_status_t check_attention(const AttnCheck &c) {
   const Span in[] = {{c.Q, span(T, c.Hq * c.D, c.ldq, 2)}, {c.K, span(T, c.Hk * c.D, c.ldk, 2)},
                      {c.V, span(T, c.Hk * c.D, c.ldv, 2)}, {c.wq, nd}, {c.bq, nd},
                      {c.wk, nd}, {c.bk, nd}};
+  if (!c.workspace != !c.workspace_bytes) return NORM_ERR_INVALID_ARG;
   const Span out[] = {{c.O, span(T, c.Hq * c.D, c.ldo, 2)},
-                      {c.lse, (size_t)c.B * (size_t)c.Hq * (size_t)c.S * 4}};
-  if (!disjoint(in, 7, out, 2)) return NORM_ERR_INVALID_ARG;
+                      {c.lse, (size_t)c.B * (size_t)c.Hq * (size_t)c.S * 4},
+                      {c.workspace, c.workspace_bytes}};
+  if (!disjoint(in, 7, out, 3)) return NORM_ERR_INVALID_ARG;
   if ((uintptr_t)c.lse & 3u) return NORM_ERR_INVALID_ARG;
   // the kernel: head size 128, 16-byte loads and stores of 8 values, a grid of one workgroup
   // per 256 queries of each (batch, query head)
   if (c.D != kAttnD) return NORM_ERR_UNSUPPORTED;
-  const void *ptrs[] = {c.Q, c.K, c.V, c.O, c.wq, c.bq, c.wk, c.bk};
-  if (c.ldq % 8 || c.ldk % 8 || c.ldv % 8 || c.ldo % 8 || common_align(ptrs, 8) < 16)
+  const void *ptrs[] = {c.Q, c.K, c.V, c.O, c.wq, c.bq, c.wk, c.bk, c.workspace};
+  if (c.ldq % 8 || c.ldk % 8 || c.ldv % 8 || c.ldo % 8 || common_align(ptrs, 9) < 16)
     return NORM_ERR_UNSUPPORTED;
   const int64_t qblocks = (c.S + kAttnBQ - 1) / kAttnBQ;
   if (c.B * c.Hq > 0x7fffffffLL / qblocks) return NORM_ERR_UNSUPPORTED;
   return NORM_OK;
+}
+
+size_t attention_workspace_bytes(int64_t B, int64_t S, int64_t Hk, int64_t D) {
+  if (B <= 0 || S <= 0 || Hk <= 0 || D <= 0 || B > kMaxN || S > kMaxN || Hk > kMaxN ||
+      D > kMaxN)
+    return 0;
+  const int64_t keys = B * S; // < 2^62
+  if (keys > INT64_MAX / 2 / D / Hk) return 0;
+  return (size_t)(keys * Hk * D * 2);
 }
 
 } // namespace dln

@@ -189,6 +189,10 @@ norm_status_t set_tuning(norm_tune_t key, int64_t v) {
     if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
     g_tuning.unaligned = (int)v;
     return NORM_OK;
+  case NORM_TUNE_ATTN_KEY_PASS:
+    if (v != -1 && v != 0 && v != 1) return NORM_ERR_INVALID_ARG;
+    g_tuning.attn_key_pass = (int)v;
+    return NORM_OK;
   default: return NORM_ERR_INVALID_ARG;
   }
 }

@@ -85,6 +85,7 @@ struct Tuning {
   int64_t xchg_polls = -1;
   int xchg_withhold = -1;
   int unaligned = -1;
+  int attn_key_pass = -1;
 };
 
 const Tuning &tuning();

@@ -21,7 +21,8 @@ TUNE_SCHEME, TUNE_GRID_PER_CU, TUNE_ROWS_PER_ITER, TUNE_TEAM_THREADS = 0, 1, 2, 
 TUNE_SPLIT_CHUNK, TUNE_ROW_GROUPS, TUNE_TEAMS_PER_WG, TUNE_ROW_ORDER = 4, 5, 6, 7
 TUNE_SPLIT_EXCHANGE, TUNE_EXCHANGE_POLLS, TUNE_EXCHANGE_WITHHOLD = 8, 9, 10
 TUNE_UNALIGNED = 11
-N_TUNE_KEYS = 12
+TUNE_ATTN_KEY_PASS = 12
+N_TUNE_KEYS = 13
 
 OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP, ERR_EXCHANGE = 0, 1, 2, 3, 4, 5
 SIZE_MAX = (1 << 64) - 1
@@ -47,7 +48,7 @@ SYMBOLS = ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce", "norm_fw
            "norm_workspace_bytes", "norm_workspace_status", "norm_plan",
            "norm_set_tuning", "norm_set_launch_events", "norm_status_string", "norm_version",
            "norm_fold_projection", "norm_lazy_linear", "norm_bwd_noalloc",
-           "norm_attention_fwd")
+           "norm_attention_fwd", "norm_attention_workspace_bytes")
 
 
 class NormError(RuntimeError):
@@ -117,7 +118,9 @@ def lib():
                                        vp, vp, vp, vp, i64, vp]
         L.norm_attention_fwd.argtypes = [i32, ctypes.c_uint32, i64, i64, i64, i64, i64, vp, i64,
                                          vp, i64, vp, i64, vp, vp, vp, vp, f32, f32, vp, i64, vp,
-                                         vp]
+                                         vp, sz, vp]
+        L.norm_attention_workspace_bytes.argtypes = [i64, i64, i64, i64]
+        L.norm_attention_workspace_bytes.restype = sz
         for name in ("norm_fwd", "norm_bwd", "norm_bwd_fused", "norm_bwd_reduce",
                      "norm_fwd_ex", "norm_bwd_ex", "norm_bwd_fused_ex", "norm_stats",
                      "norm_workspace_size", "norm_workspace_status", "norm_plan",
@@ -308,12 +311,18 @@ def _token_stride(t, B, S, H, D, name):
     return ld
 
 
+def attention_workspace_bytes(B, S, Hk, D):
+    """Bytes of workspace norm_attention_fwd's key pass uses."""
+    return lib().norm_attention_workspace_bytes(B, S, Hk, D)
+
+
 def norm_attention_fwd(kind, Q, K, V, wq, bq, wk, bk, eps, scale, O, lse=None, causal=False,
-                       normalize=True, stream=None):
+                       normalize=True, workspace=None, stream=None):
     """Queue attention over normalised queries and keys: Q, O [B, S, Hq, D], K, V
     [B, S, Hk, D] (bf16, evenly spaced tokens, e.g. slices of one packed QKV tensor), gammas
     wq, wk and betas bq, bk [D] bf16, lse [B, Hq, S] fp32 or None. normalize=False: the
-    queries and keys as given (the norm vectors must be None), as does kind "none"."""
+    queries and keys as given (the norm vectors must be None), as does kind "none". workspace:
+    a CUDA tensor of at least attention_workspace_bytes() bytes for the key pass, or None."""
     Bn, S, Hq, D = Q.shape
     Hk = K.shape[2]
     ldq = _token_stride(Q, Bn, S, Hq, D, "Q")
@@ -332,7 +341,7 @@ def norm_attention_fwd(kind, Q, K, V, wq, bq, wk, bk, eps, scale, O, lse=None, c
     st = lib().norm_attention_fwd(_kind(kind), flags, Bn, S, Hq, Hk, D, _ptr(Q), ldq, _ptr(K),
                                   ldk, _ptr(V), ldv, _ptr(wq), _ptr(bq), _ptr(wk), _ptr(bk),
                                   float(eps), float(scale), _ptr(O), ldo, _ptr(lse),
-                                  _stream(stream, Q))
+                                  *_ws(workspace), _stream(stream, Q))
     _raise(st, "norm_attention_fwd")
 
 
@@ -549,17 +558,21 @@ def lazy_linear(kind, X, eps, G, s=None, t=None, mean=None, rstd=None, stream=No
 
 
 def attention(kind, Q, K, V, wq=None, bq=None, wk=None, bk=None, eps=1e-6, scale=None,
-              causal=False, want_lse=False, stream=None):
+              causal=False, want_lse=False, key_pass=True, stream=None):
     """O (and lse when want_lse) of attention over queries and keys normalised by `kind` with
     the given gammas (and betas); with wq and wk None (or kind "none") the queries and keys are
-    used as given."""
+    used as given. key_pass: give the call a workspace for its key pass."""
     normalize = kind != "none" and (wq is not None or wk is not None)
-    D = Q.shape[3]
+    Bn, S, _, D = Q.shape
+    ws = None
+    if normalize and key_pass:
+        ws = torch.empty(attention_workspace_bytes(Bn, S, K.shape[2], D), dtype=torch.uint8,
+                         device=Q.device)
     O = torch.empty(Q.shape, dtype=torch.bfloat16, device=Q.device)
     lse = (torch.empty(Q.shape[0], Q.shape[2], Q.shape[1], dtype=torch.float32, device=Q.device)
            if want_lse else None)
     norm_attention_fwd(kind, Q, K, V, wq, bq, wk, bk, eps, D ** -0.5 if scale is None else scale,
-                       O, lse, causal, normalize, stream)
+                       O, lse, causal, normalize, ws, stream)
     return (O, lse) if want_lse else O
 
 

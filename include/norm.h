@@ -355,11 +355,15 @@ typedef enum {
                                    second) */
   NORM_TUNE_EXCHANGE_WITHHOLD = 10, /* for tests of that bounded wait only: 1 = chunk 0 never
                                        publishes its partials, so every row gives up */
-  NORM_TUNE_UNALIGNED = 11      /* wave/block schemes, rows off 16-byte boundaries (their
+  NORM_TUNE_UNALIGNED = 11,     /* wave/block schemes, rows off 16-byte boundaries (their
                                    length, stride or start) with every [M, N] tensor at one
                                    phase: -1 (default) or 1, 16-byte accesses over row phase
                                    classes in place of 8-byte, 4-byte and element-wise ones;
                                    0 never */
+  NORM_TUNE_ATTN_KEY_PASS = 12  /* norm_attention_fwd with a large enough workspace: 1 = the
+                                   key pass always, 0 = never (the key norm deferred into the
+                                   attention kernel), -1 (default) = when each key is read by
+                                   at least 8 (query block, query head) pairs */
 } norm_tune_t;
 
 norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);
@@ -439,14 +443,25 @@ norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int
  *           1 / sqrt(D)).
  *   O       [B, S, Hq, D] bf16 out, token stride ldo; must not overlap any input.
  *   lse     [B, Hq, S] fp32 out, or NULL.
- *   Numerics: the normalised vectors are rounded once to bf16, scores and O accumulate in fp32
- *   on the matrix cores, the softmax weights enter the second product as bf16, O is rounded
- *   once to bf16 (nearest even).
+ *   workspace  device memory the call may use, or NULL (then workspace_bytes must be 0); it
+ *           must not overlap any argument. Each key vector is read by every query block of
+ *           every query head of its group. When that is at least 8 (query block, head) pairs
+ *           and workspace_bytes >= norm_attention_workspace_bytes(B, S, Hk, D), the keys are
+ *           normalised once, by a pass of their own into the workspace, and the attention
+ *           kernel reads them from there; the queries are always normalised inside the
+ *           attention kernel, which never stores them. Otherwise the key norm is deferred into
+ *           the attention kernel: the key gamma is folded into each query, and each key's
+ *           rstd (and, for LayerNorm, -rstd * mean) scales its scores.
+ *   Numerics: scores and O accumulate in fp32 on the matrix cores, the softmax weights enter
+ *   the second product as bf16, O is rounded once to bf16 (nearest even). With the key pass
+ *   the normalised queries and keys are each rounded once to bf16 (as two separate norm passes
+ *   would store them); with the deferred key norm the normalised queries times the key gamma
+ *   are rounded once to bf16 and the keys enter the product exactly.
  *   Requirements: D == 128; ldq, ldk, ldv, ldo multiples of 8 and at least Hq * D (Hk * D for
- *   K and V); Q, K, V, O and the norm vectors 16-byte aligned. Otherwise NORM_ERR_UNSUPPORTED
+ *   K and V); Q, K, V, O, the norm vectors and the workspace 16-byte aligned. Otherwise NORM_ERR_UNSUPPORTED
  *   (head size, alignment) or NORM_ERR_INVALID_ARG (sizes, Hq not a multiple of Hk, NULL
  *   pointers, eps, scale, flags, overlaps). B == 0 or S == 0: NORM_OK once the rest passes,
- *   nothing launched and no pointer read. The launch allocates nothing.
+ *   nothing launched and no pointer read. The call allocates nothing.
  */
 #define NORM_ATTN_CAUSAL 1u
 #define NORM_ATTN_NO_NORM 2u
@@ -455,7 +470,11 @@ norm_status_t norm_attention_fwd(norm_kind_t kind, uint32_t flags, int64_t B, in
                                  const void *K, int64_t ldk, const void *V, int64_t ldv,
                                  const void *wq, const void *bq, const void *wk, const void *bk,
                                  float eps, float scale, void *O, int64_t ldo, float *lse,
+                                 void *workspace, size_t workspace_bytes,
                                  norm_stream_t stream);
+/* Workspace bytes for norm_attention_fwd's key pass: B * S * Hk * D * 2 (0 for sizes it does
+ * not address). Host only. */
+size_t norm_attention_workspace_bytes(int64_t B, int64_t S, int64_t Hk, int64_t D);
 
 /*
  * Kernel timing for profilers and benchmarks. Arms two HIP events (hipEvent_t, created by the

@@ -271,7 +271,8 @@ class tuned:
                 "split_chunk": nl.TUNE_SPLIT_CHUNK, "row_groups": nl.TUNE_ROW_GROUPS,
                 "teams": nl.TUNE_TEAMS_PER_WG, "row_order": nl.TUNE_ROW_ORDER,
                 "exchange": nl.TUNE_SPLIT_EXCHANGE, "polls": nl.TUNE_EXCHANGE_POLLS,
-                "withhold": nl.TUNE_EXCHANGE_WITHHOLD, "unaligned": nl.TUNE_UNALIGNED}
+                "withhold": nl.TUNE_EXCHANGE_WITHHOLD, "unaligned": nl.TUNE_UNALIGNED,
+                "attn_key_pass": nl.TUNE_ATTN_KEY_PASS}
         self.items = [(keys[k], v) for k, v in kv.items()]
 
     def __enter__(self):

@@ -597,7 +597,8 @@ def _attn(**kw):
     ld = 8 * 128
     a = dict(kind=1, flags=0, B=2, S=300, Hq=4, Hk=2, D=128, Q=FAKE, ldq=ld, K=FAKE + 1024,
              ldk=ld, V=FAKE + 1536, ldv=ld, wq=FAKE * 2, bq=None, wk=FAKE * 2 + 256, bk=None,
-             eps=1e-6, scale=128 ** -0.5, O=FAKE * 3, ldo=512, lse=FAKE * 4, stream=None)
+             eps=1e-6, scale=128 ** -0.5, O=FAKE * 3, ldo=512, lse=FAKE * 4, workspace=None,
+             workspace_bytes=0, stream=None)
     a.update(kw)
     return nl.lib().norm_attention_fwd(*a.values())
 
@@ -610,6 +611,12 @@ def test_attention_checks():
     assert _attn(lse=None) == nl.ERR_HIP
     assert _attn(Hk=4, ldq=1536, ldk=1536, ldv=1536) == nl.ERR_HIP
     assert _attn(B=0) == nl.OK and _attn(S=0, Q=None, O=None) == nl.OK
+    ws = nl.attention_workspace_bytes(2, 300, 2, 128)
+    assert ws == 2 * 300 * 2 * 128 * 2
+    assert _attn(workspace=FAKE * 5, workspace_bytes=ws) == nl.ERR_HIP
+    assert _attn(workspace=FAKE * 5, workspace_bytes=16) == nl.ERR_HIP   # too small: not used
+    assert nl.attention_workspace_bytes(0, 300, 2, 128) == 0
+    assert nl.attention_workspace_bytes(1 << 31, 1 << 31, 2, 128) == 0
     for kw in (dict(kind=2), dict(flags=4), dict(Hk=3), dict(Hq=0), dict(D=0), dict(B=-1),
                dict(Q=None), dict(K=None), dict(V=None), dict(O=None), dict(wq=None),
                dict(wk=None), dict(bq=FAKE * 2 + 512),    # RMSNorm has no beta
@@ -619,11 +626,15 @@ def test_attention_checks():
                dict(ldq=511), dict(ldk=255), dict(ldo=256),  # strides below the heads
                dict(O=FAKE + 64),                         # O over Q
                dict(lse=FAKE * 3 + 8),                    # lse over O
-               dict(lse=FAKE * 4 + 2)):                   # misaligned lse
+               dict(lse=FAKE * 4 + 2),                    # misaligned lse
+               dict(workspace=FAKE * 5),                  # workspace without its size
+               dict(workspace_bytes=64),                  # a size without a workspace
+               dict(workspace=FAKE * 3 + 256, workspace_bytes=1024)):  # workspace over O
         assert _attn(**kw) == nl.ERR_INVALID_ARG, kw
     for kw in (dict(D=64, ldq=512, ldk=512, ldv=512, ldo=256),   # head size
                dict(ldq=8 * 128 + 4), dict(ldo=516),            # strides not multiples of 8
                dict(Q=FAKE + 8), dict(wk=FAKE * 2 + 264),       # not 16-byte aligned
+               dict(workspace=FAKE * 5 + 8, workspace_bytes=1024),
                dict(B=1 << 16, S=1 << 16, Hq=128, Hk=1,          # grid past 2^31 - 1
                     Q=1 << 48, ldq=1 << 14, K=2 << 48, ldk=128, V=3 << 48, ldv=128,
                     O=4 << 48, ldo=1 << 14, lse=5 << 48)):
