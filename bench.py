@@ -358,36 +358,8 @@ def attention_bench(a, torch, nl, steps, warmup, cpu=False):
     forms alternate call by call, each call bracketed by its own pair of HIP events on the
     stream, because the clock drifts by several percent over seconds of matrix-core load; the
     figures are medians over `steps` calls of each form."""
-    from deep_learning_normalization_amd import inputs
-    dev = "cuda"
-    t = {k: (v.to(dev) if v is not None else None) for k, v in inputs.make_attention(a).items()}
-    Q, K, V = t["Q"], t["K"], t["V"]
-    O = torch.empty_like(Q)
-    ws = torch.empty(nl.attention_workspace_bytes(a.B, a.S, a.Hk, a.D), dtype=torch.uint8,
-                     device=dev)
-    Qn, Kn = torch.empty_like(Q), torch.empty_like(K)
-    rq = torch.empty(Q.numel() // a.D, device=dev)
-    rk = torch.empty(K.numel() // a.D, device=dev)
-    mq = torch.empty_like(rq) if a.kind == "layernorm" else None
-    mk = torch.empty_like(rk) if a.kind == "layernorm" else None
-    scale = a.D ** -0.5
-
-    def fused():
-        nl.norm_attention_fwd(a.kind, Q, K, V, t["wq"], t["bq"], t["wk"], t["bk"], a.eps, scale,
-                              O, None, a.causal, workspace=ws)
-
-    def alone():
-        nl.norm_attention_fwd("none", Qn, Kn, V, None, None, None, None, a.eps, scale, O, None,
-                              a.causal)
-
-    def unfused():
-        nl.norm_fwd(a.kind, Q.view(-1, a.D), None, t["wq"], t["bq"], a.eps, Qn.view(-1, a.D),
-                    None, mq, rq)
-        nl.norm_fwd(a.kind, K.view(-1, a.D), None, t["wk"], t["bk"], a.eps, Kn.view(-1, a.D),
-                    None, mk, rk)
-        alone()
-
-    forms = {"fused": fused, "unfused": unfused, "attention_alone": alone}
+    from deep_learning_normalization_amd.profiling import attention_forms
+    forms = attention_forms(a, torch, nl)
     evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(steps)] for k in forms}
     t_end = time.perf_counter() + 0.5  # the clock settles under load
@@ -423,7 +395,7 @@ def attention_bench(a, torch, nl, steps, warmup, cpu=False):
     out["attention_alone_TFLOPs"] = round(flops / (med["attention_alone"] * 1e-6) / 1e12, 1)
     if cpu:
         out["cpu_baseline"] = attention_cpu_baseline(a)
-    del t, Q, K, V, O, ws, Qn, Kn
+    del forms
     torch.cuda.empty_cache()
     return out
 

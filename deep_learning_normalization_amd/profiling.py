@@ -7,6 +7,8 @@ and HBM traffic.
         --workload NAME --kernel SUBSTR --algo-bytes N --out FILE --cmd "..."
     python -m deep_learning_normalization_amd.profiling workloads --root DIR --out FILE --cmd "..."
     python -m deep_learning_normalization_amd.profiling summarize --root DIR --out DIR
+    python -m deep_learning_normalization_amd.profiling attention-drive [--steps K]
+    python -m deep_learning_normalization_amd.profiling attention-stats --trace DIR --out FILE
 
 `drive` runs one workload's step, forward and backward loops K times each with the benchmark's
 cache-cold buffer rotation (run it under rocprofv3); it first runs the copy probes the counter
@@ -414,6 +416,89 @@ WORKLOAD_CMD = ("cd /tmp && PYTHONPATH=$REPO rocprofv3 {--kernel-trace | --pmc F
                 "-- python3 -m deep_learning_normalization_amd.profiling drive --workload NAME")
 
 
+ATTENTION_CMD = ("cd /tmp && PYTHONPATH=$REPO rocprofv3 --kernel-trace --stats -d "
+                 "$REPO/gpurun_out/attn_trace -o run --output-format csv -- python3 -m "
+                 "deep_learning_normalization_amd.profiling attention-drive --steps 20")
+
+
+def attention_forms(a, torch, nl):
+    """The three forms the benchmark compares for attention workload a, on resident inputs:
+    the fused call (key pass into a workspace, then the attention kernel with the query norm
+    inside), the two-pass form (norm_fwd on the query vectors and on the key vectors, then the
+    attention kernel without a norm) and that attention kernel alone."""
+    from deep_learning_normalization_amd import inputs
+    t = {k: (v.to("cuda") if v is not None else None)
+         for k, v in inputs.make_attention(a).items()}
+    Q, K, V = t["Q"], t["K"], t["V"]
+    O = torch.empty_like(Q)
+    ws = torch.empty(nl.attention_workspace_bytes(a.B, a.S, a.Hk, a.D), dtype=torch.uint8,
+                     device="cuda")
+    Qn, Kn = torch.empty_like(Q), torch.empty_like(K)
+    rq = torch.empty(Q.numel() // a.D, device="cuda")
+    rk = torch.empty(K.numel() // a.D, device="cuda")
+    scale = a.D ** -0.5
+
+    def fused():
+        nl.norm_attention_fwd(a.kind, Q, K, V, t["wq"], t["bq"], t["wk"], t["bk"], a.eps, scale,
+                              O, None, a.causal, workspace=ws)
+
+    def alone():
+        nl.norm_attention_fwd("none", Qn, Kn, V, None, None, None, None, a.eps, scale, O, None,
+                              a.causal)
+
+    def unfused():
+        nl.norm_fwd(a.kind, Q.view(-1, a.D), None, t["wq"], t["bq"], a.eps, Qn.view(-1, a.D),
+                    None, None, rq)
+        nl.norm_fwd(a.kind, K.view(-1, a.D), None, t["wk"], t["bk"], a.eps, Kn.view(-1, a.D),
+                    None, None, rk)
+        alone()
+    return {"fused": fused, "unfused": unfused, "attention_alone": alone}
+
+
+def attention_drive(steps):
+    """The attention workload's three forms, alternating, `steps` calls each (run it under
+    rocprofv3)."""
+    import torch
+    from deep_learning_normalization_amd import inputs, normlib as nl
+    nl.lib()
+    forms = attention_forms(inputs.ATTN_QKNORM_B2_S4096, torch, nl)
+    for _ in range(steps):
+        for f in forms.values():
+            f()
+    torch.cuda.synchronize()
+
+
+def attention_stats(trace_dir, out, cmd):
+    """Kernel statistics of the attention capture, plus each attention kernel's matrix-core
+    rate at its average duration."""
+    from deep_learning_normalization_amd import inputs
+    a = inputs.ATTN_QKNORM_B2_S4096
+    stats(trace_dir, out, cmd)
+    trace = list(csv.DictReader(open(_one(trace_dir, "_kernel_trace.csv"))))
+    pairs = a.S * (a.S + 1) // 2 if a.causal else a.S * a.S
+    flops = 4 * a.B * a.Hq * a.D * pairs
+    by = {}
+    for r in trace:
+        n = _name(r["Kernel_Name"])
+        if "attn_fwd_kernel" in n:
+            key = n.replace("(anonymous namespace)::", "").split("(")[0].replace("void dln::", "")
+            by.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1000.0)
+    lines = ["", "Workload %s: B %d, S %d, Hq %d, Hk %d, D %d, %s, %s; %d matrix-product flops "
+             "per call (2 D per visible (query, key) pair and product). Template arguments: "
+             "<norm (0 LayerNorm, 1 RMSNorm, 2 none), keys normalised by the key pass, causal>."
+             % (a.name, a.B, a.S, a.Hq, a.Hk, a.D, a.kind, "causal" if a.causal else "full",
+                flops), "",
+             "| attention kernel | launches | average us | TFLOP/s at average | of 2500 |",
+             "|---|---|---|---|---|"]
+    for k, d in sorted(by.items()):
+        avg = statistics.mean(d)
+        tf = flops / (avg * 1e-6) / 1e12
+        lines.append("| %s | %d | %.2f | %.1f | %.3f |" % (k, len(d), avg, tf, tf / 2500.0))
+    with open(out, "a") as f:
+        f.write("\n".join(lines) + "\n")
+
+
 def summarize(root, out):
     """Every committed summary from one capture: the headline command's kernel statistics and
     its fused backward's and forward's traffic (under root/prof_{trace,fetch,write}), and the
@@ -474,12 +559,21 @@ def main():
     cn.add_argument("--root", required=True)
     cn.add_argument("--out", required=True)
     cn.add_argument("--cmd", required=True)
+    ad = sub.add_parser("attention-drive")
+    ad.add_argument("--steps", type=int, default=20)
+    ast = sub.add_parser("attention-stats")
+    ast.add_argument("--trace", required=True)
+    ast.add_argument("--out", required=True)
     sm = sub.add_parser("summarize")
     sm.add_argument("--root", required=True, help="the capture's output folder")
     sm.add_argument("--out", required=True, help="where the summaries go")
     a = ap.parse_args()
     if a.what == "summarize":
         summarize(a.root, a.out)
+    elif a.what == "attention-drive":
+        attention_drive(a.steps)
+    elif a.what == "attention-stats":
+        attention_stats(a.trace, a.out, ATTENTION_CMD)
     elif a.what == "counters-drive":
         counters_drive()
     elif a.what == "counters":
