@@ -23,15 +23,19 @@
 //              load V and store it transposed, so that O^T = V^T P^T takes its B operand P
 //              straight from the score registers (MFMA 32x32x16 bf16, fp32 accumulation, for
 //              both products). The next tile's global loads are in flight during the products.
-//   key norm   deferred past the product, as a norm into a matrix product can be (the page's
-//              items 3-4): the key gamma is folded into each query once, and each key's rstd
-//              (and, for LayerNorm, -rstd * mean) scales its column of scores in fp32. A key is
-//              read by every query block of every query head of its group; normalising it
-//              there in full would repeat that vector work for each of them.
+//   key norm   with a workspace, a pass of its own (attn_knorm_kernel) before the attention
+//              kernel; else deferred past the product, as a norm into a matrix product can be
+//              (the page's items 3-4): the key gamma is folded into each query once, the keys
+//              are staged as they are (LayerNorm: centred) and each key's rstd scales its
+//              column of scores in fp32. A key is read by every query block of every query
+//              head of its group; normalising it there in full would repeat that vector work
+//              for each of them.
 //
-// Numerics: the normalised queries, times the key gamma, are rounded once to bf16; the keys
-// enter the product exactly; scores and output accumulate in fp32, the weights P are rounded to
-// bf16 for the second product, and O is rounded once to bf16.
+// Numerics: with the key pass, the normalised queries and keys are each rounded once to bf16;
+// with the deferred key norm, the normalised queries times the key gamma are, and the keys
+// enter the product exactly (LayerNorm: centred, rounded once to bf16). Scores and output
+// accumulate in fp32, the weights P are rounded to bf16 for the second product, and O is
+// rounded once to bf16.
 #include <cmath>
 #include <type_traits>
 
@@ -48,7 +52,7 @@ constexpr int D = kAttnD, BQ = kAttnBQ, BK = kAttnBK;
 constexpr int kThreads = 512;
 constexpr int kKRow = D + 8;   // bf16 per staged key row: 272 bytes, so that the 16-byte operand
                                // reads of 16 consecutive keys start on distinct bank groups
-constexpr int kVRow = BK + 8;  // bf16 per staged row of V^T (one head dimension): 144 bytes
+constexpr int kVRow = BK + 16; // bf16 per staged row of V^T (one head dimension): 160 bytes
 static_assert(BQ == 8 * 32, "eight wavefronts of 32 queries");
 static_assert(D == 128 && BK == 64, "the staging maps below assume D = 128 and 64-key tiles");
 
@@ -59,11 +63,14 @@ static_assert(D == 128 && BK == 64, "the staging maps below assume D = 128 and 6
 // must list the same keys in the same order; so V^T stores key kk of the tile in slot
 // 16(kk/16) + swap of bits 2 and 3 of (kk % 16), and lane half h reads slots 16s + 8h .. +7.
 //
-// Element (dim d, slot p) of the staged V^T tile. Slots go in 16-byte units of 8; the unit
-// index is XORed with bits 4 and 5 of d, which spreads both the transposing 8-byte writes and
-// the 16-byte operand reads over the LDS banks.
+// Element (dim d, slot p) of the staged V^T tile. Slots go in 16-byte units of 8; rows are 160
+// bytes apart and the unit index is XORed with bits 4-6 of d. Chosen by measurement (the LDS
+// bank-conflict counter over candidate strides and XOR patterns, for these exact read and write
+// patterns): the 16-byte operand reads are conflict-free and the transposing 8-byte writes
+// lose 4 cycles each; the earlier 144-byte rows with bits 4-5 of d cost 4 cycles per read and
+// 12 per write.
 __device__ __forceinline__ int vt_off(int d, int p) {
-  return d * kVRow + ((((p >> 3) ^ ((d >> 3) & 6))) << 3) + (p & 7);
+  return d * kVRow + ((((p >> 3) ^ ((d >> 4) & 7))) << 3) + (p & 7);
 }
 
 // Sum over the 16 lanes of a DPP row; every lane of the row gets the same bits.
@@ -94,7 +101,6 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   __shared__ __align__(16) uint16_t sk[2][BK * kKRow];
   __shared__ __align__(16) uint16_t svt[2][D * kVRow];
   __shared__ __align__(16) float srs[2][BK];  // per key of the tile: rstd
-  __shared__ __align__(16) float snm[2][BK];  // per key: -rstd * mean (LayerNorm)
   constexpr bool LN = NORM == ATTN_LAYERNORM;
   constexpr bool NORMED = NORM != ATTN_NO_NORM;
   // KPRE: the keys arrive normalised (by attn_knorm_kernel); else their norm is deferred
@@ -120,7 +126,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   const int wlast = min(wq0 + 31, S - 1);
 
   bf16x8_t qf[8];
-  float c1 = 0.0f, c2 = 0.0f;
+  float c2 = 0.0f;
 
   // ---- staging roles: wavefronts 4-7 stage K, 0-3 stage V. Thread st of a role owns the
   // 16-byte chunk sc (dims 8sc .. 8sc+7) of K rows srow + 16i, or of V keys 4srow + i, i < 4.
@@ -140,43 +146,54 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   };
   auto stage_tile = [&](int buf) {
     if (kstage) {
+      if constexpr (!(DEFER && LN)) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        *reinterpret_cast<uint4 *>(&sk[buf][(srow + 16 * i) * kKRow + sc * 8]) = pre[i];
+        for (int i = 0; i < 4; ++i)
+          *reinterpret_cast<uint4 *>(&sk[buf][(srow + 16 * i) * kKRow + sc * 8]) = pre[i];
+      }
       if constexpr (DEFER) {
         // the statistics of the four keys, two passes over each key's 128 values (16 lanes,
-        // DPP row sums; the four rows interleaved)
-        float x[4][8], mean[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q2[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) unpack8(pre[i], x[i]);
+        // DPP row sums; the four rows interleaved), each pass unpacking the loaded values
+        float mean[4] = {0.0f, 0.0f, 0.0f, 0.0f}, q2[4];
         if constexpr (LN) {
           float sm[4];
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
+            float x[8];
+            unpack8(pre[i], x);
             sm[i] = 0.0f;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) sm[i] += x[i][e];
+            for (int e = 0; e < 8; ++e) sm[i] += x[e];
           }
 #pragma unroll
           for (int i = 0; i < 4; ++i) mean[i] = row16_sum(sm[i]) * kInvD;
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
+          float x[8];
+          unpack8(pre[i], x);
           q2[i] = 0.0f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
-            const float d = x[i][e] - mean[i];
+            const float d = x[e] - mean[i];
             q2[i] = __builtin_fmaf(d, d, q2[i]);
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) q2[i] = rsqrt_f32(row16_sum(q2[i]) * kInvD + a.eps);
-        if (sc == 0) {
+        if constexpr (LN) {  // the centred keys
 #pragma unroll
           for (int i = 0; i < 4; ++i) {
-            srs[buf][srow + 16 * i] = q2[i];
-            if (LN) snm[buf][srow + 16 * i] = -q2[i] * mean[i];
+            float x[8];
+            unpack8(pre[i], x);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] -= mean[i];
+            *reinterpret_cast<uint4 *>(&sk[buf][(srow + 16 * i) * kKRow + sc * 8]) = pack8(x);
           }
+        }
+        if (sc == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) srs[buf][srow + 16 * i] = q2[i];
         }
       }
     } else {
@@ -247,16 +264,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
             const int k4 = 32 * j + 8 * g + 4 * half;
             const float4 rs = *reinterpret_cast<const float4 *>(&srs[buf][k4]);
             const float rv[4] = {rs.x, rs.y, rs.z, rs.w};
-            if constexpr (LN) {
-              const float4 nm = *reinterpret_cast<const float4 *>(&snm[buf][k4]);
-              const float nv[4] = {nm.x, nm.y, nm.z, nm.w};
 #pragma unroll
-              for (int i = 0; i < 4; ++i)
-                s[j][4 * g + i] = __builtin_fmaf(s[j][4 * g + i], rv[i], nv[i] * c1);
-            } else {
-#pragma unroll
-              for (int i = 0; i < 4; ++i) s[j][4 * g + i] *= rv[i];
-            }
+            for (int i = 0; i < 4; ++i) s[j][4 * g + i] *= rv[i];
           }
       }
       if constexpr (MASK) {
@@ -295,6 +304,10 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
           s[j][r] = p;
           l += p;
         }
+      // V^T operand rows: vt_off(32dt + col, 16ss + 8h). With d = 32dt + col, bits 4-6 of d
+      // are 2dt + col/16, so the unit index (2ss + h) ^ (2dt + col/16) is
+      // 2(ss ^ dt) + (h ^ col/16): one per-lane base plus a constant per (dt, ss).
+      const uint16_t *vrow = &svt[buf][col * kVRow + 8 * (half ^ (col >> 4))];
 #pragma unroll
       for (int ss = 0; ss < 4; ++ss) {
         const int j = ss >> 1, r0 = 8 * (ss & 1);
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 #pragma unroll
         for (int dt = 0; dt < 4; ++dt) {
           const bf16x8_t vf = *reinterpret_cast<const bf16x8_t *>(
-              &svt[buf][vt_off(32 * dt + col, 16 * ss + 8 * half)]);
+              vrow + dt * 32 * kVRow + 16 * (ss ^ dt));
           o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pb, o[dt], 0, 0, 0);
         }
       }
@@ -322,12 +335,13 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   if (kb_mask > nkt) kb_mask = nkt;
   load_tile(0);  // in flight while the queries are normalised
   // ---- this wavefront's queries as MFMA B operands: lane l holds dims 16ks + 8h .. +7 of
-  // query l % 32 in qf[ks]. With a norm, the query is normalised (q') and the key gamma is
-  // folded in: qf = bf16(q' * gamma_k). The keys then enter the product as they are and their
-  // own statistics scale the scores (the key norm deferred past the product):
-  //   q' . k'_j = rstd_j * (qf . k_j) [- rstd_j * mean_j * sum_d qf_d + q' . beta_k]
-  // (bracket: LayerNorm). The last term is the same for every key of the query, so the softmax
-  // drops it; it returns in lse (c2).
+  // query l % 32 in qf[ks]. With a norm, the query is normalised (q'). When the key norm is
+  // deferred (DEFER), the key gamma is folded in, qf = bf16(q' * gamma_k), the keys enter the
+  // product as they are (LayerNorm: centred as they are staged, rounded once to bf16) and
+  // their own rstd scales the scores:
+  //   q' . k'_j = rstd_j * (qf . (k_j [- mean_j])) [+ q' . beta_k]
+  // (brackets: LayerNorm). The last term is the same for every key of the query, so the
+  // softmax drops it; it returns in lse (c2).
   {
     const int qrow = myq < S ? myq : S - 1;
     const uint16_t *qp = a.q + ((int64_t)b * S + qrow) * a.ldq + (int64_t)head * D + half * 8;
@@ -379,19 +393,8 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
       }
     }
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 w = pack8(x[ks]);
-      qf[ks] = __builtin_bit_cast(bf16x8_t, w);
-      if constexpr (LN && DEFER) {  // the sum of the rounded values the product sees
-        const unsigned u[4] = {w.x, w.y, w.z, w.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) c1 += bf16_lo(u[i]) + bf16_hi(u[i]);
-      }
-    }
-    if constexpr (LN && DEFER) {
-      c1 += __shfl_xor(c1, 32);
-      c2 += __shfl_xor(c2, 32);
-    }
+    for (int ks = 0; ks < 8; ++ks) qf[ks] = __builtin_bit_cast(bf16x8_t, pack8(x[ks]));
+    if constexpr (LN && DEFER) c2 += __shfl_xor(c2, 32);
   }
 
   stage_tile(0);

@@ -450,13 +450,14 @@ norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int
  *           normalised once, by a pass of their own into the workspace, and the attention
  *           kernel reads them from there; the queries are always normalised inside the
  *           attention kernel, which never stores them. Otherwise the key norm is deferred into
- *           the attention kernel: the key gamma is folded into each query, and each key's
- *           rstd (and, for LayerNorm, -rstd * mean) scales its scores.
+ *           the attention kernel: the key gamma is folded into each query, the keys are
+ *           staged as given (LayerNorm: centred) and each key's rstd scales its scores.
  *   Numerics: scores and O accumulate in fp32 on the matrix cores, the softmax weights enter
  *   the second product as bf16, O is rounded once to bf16 (nearest even). With the key pass
  *   the normalised queries and keys are each rounded once to bf16 (as two separate norm passes
  *   would store them); with the deferred key norm the normalised queries times the key gamma
- *   are rounded once to bf16 and the keys enter the product exactly.
+ *   are rounded once to bf16 and the keys enter the product exactly (LayerNorm: centred,
+ *   rounded once to bf16).
  *   Requirements: D == 128; ldq, ldk, ldv, ldo multiples of 8 and at least Hq * D (Hk * D for
  *   K and V); Q, K, V, O, the norm vectors and the workspace 16-byte aligned. Otherwise NORM_ERR_UNSUPPORTED
  *   (head size, alignment) or NORM_ERR_INVALID_ARG (sizes, Hq not a multiple of Hk, NULL
