@@ -10,9 +10,9 @@
 // scores nor the weights reach HBM either.
 //
 //   grid       one workgroup per (batch, query head, block of 256 queries). Workgroup ids are
-//              renumbered so that each XCD walks one contiguous range of them: the query heads
+//              renumbered so that each XCD takes a contiguous range of heads: the query heads
 //              that share a key/value head are adjacent, and their K and V tiles stay in that
-//              XCD's L2. With the causal mask, the longest blocks of each head go first.
+//              XCD's L2. With the causal mask, the longest blocks go first.
 //   workgroup  512 threads, eight wavefronts of 32 queries each, two per SIMD (one computes
 //              its softmax while the other's matrix products run). Each wavefront holds its
 //              queries' normalised vectors (bf16) in registers as the B operand of S^T = K Q^T:
@@ -109,12 +109,23 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int half = lane >> 5, col = lane & 31;
 
-  // workgroup -> (batch, query head, query block)
-  int bid = blockIdx.x;
-  const int nwg = gridDim.x;
-  if ((nwg & 7) == 0) bid = (bid & 7) * (nwg >> 3) + (bid >> 3);
-  const int qbr = bid % a.qblocks;
-  const int bh = bid / a.qblocks;
+  // workgroup -> (batch, query head, query block). Workgroup ids reach the eight XCDs in turn
+  // (id % 8); XCD x gets a contiguous eighth of the (batch, head) pairs, so the heads that
+  // share a key/value head share its L2. Without the mask, each head's query blocks follow one
+  // another. With it, a block's cost grows with its index, and the XCD takes its heads' longest
+  // blocks first, all heads at once, then the next longest (dispatch in decreasing cost leaves
+  // no long block for the end).
+  const int bid = blockIdx.x, nwg = gridDim.x, nbh = a.B * a.Hq;
+  int qbr, bh;
+  if (CAUSAL && (nbh & 7) == 0) {
+    const int hx = nbh >> 3, i = bid >> 3;
+    qbr = i / hx;
+    bh = (bid & 7) * hx + (i - qbr * hx);
+  } else {
+    const int idx = (nwg & 7) == 0 ? (bid & 7) * (nwg >> 3) + (bid >> 3) : bid;
+    qbr = idx % a.qblocks;
+    bh = idx / a.qblocks;
+  }
   const int head = bh % a.Hq, b = bh / a.Hq;
   const int qb = CAUSAL ? a.qblocks - 1 - qbr : qbr;
   const int hk = head / (a.Hq / a.Hk);
