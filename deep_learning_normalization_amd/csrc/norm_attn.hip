@@ -141,18 +141,33 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
 
   // ---- staging roles: wavefronts 4-7 stage K, 0-3 stage V. Thread st of a role owns the
   // 16-byte chunk sc (dims 8sc .. 8sc+7) of K rows srow + 16i, or of V keys 4srow + i, i < 4.
-  const bool kstage = wave >= 4;
+  // the role is uniform in the wavefront: the tile's base address is then a scalar, and each
+  // load adds this lane's 32-bit byte offset (token strides are below 2^24, checked on the host)
+  const bool kstage = __builtin_amdgcn_readfirstlane(wave) >= 4;
   const int st = t & 255, sc = st & 15, srow = st >> 4;
-  const uint16_t *sbase = kstage ? a.k : a.v;
   const int64_t sld = kstage ? a.ldk : a.ldv;
-  sbase += (int64_t)b * S * sld + (int64_t)hk * D + sc * 8;
+  const char *sbase = reinterpret_cast<const char *>((kstage ? a.k : a.v) +
+                                                     (int64_t)b * S * sld + (int64_t)hk * D);
+  int srows[4];
+  uint32_t soff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    srows[i] = kstage ? srow + 16 * i : 4 * srow + i;
+    soff[i] = (uint32_t)(((int64_t)srows[i] * sld + sc * 8) * 2);
+  }
   uint4 pre[4];
   auto load_tile = [&](int kb) {
+    const char *tb = sbase + (int64_t)kb * BK * sld * 2;
+    if (kb * BK + BK <= S) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int key = kb * BK + (kstage ? srow + 16 * i : 4 * srow + i);
-      key = key < S ? key : S - 1;  // rows past the end: a real row, masked out of the scores
-      pre[i] = *reinterpret_cast<const uint4 *>(sbase + (int64_t)key * sld);
+      for (int i = 0; i < 4; ++i) pre[i] = *reinterpret_cast<const uint4 *>(tb + soff[i]);
+    } else {  // the last tile: rows past the end read the last row, masked out of the scores
+      const int last = S - 1 - kb * BK;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = srows[i] < last ? srows[i] : last;
+        pre[i] = *reinterpret_cast<const uint4 *>(tb + (uint32_t)(((int64_t)r * sld + sc * 8) * 2));
+      }
     }
   };
   auto stage_tile = [&](int buf) {
@@ -239,7 +254,7 @@ __global__ __launch_bounds__(kThreads, 1) void attn_fwd_kernel(AttnArgs a) {
     for (int r = 0; r < 16; ++r) o[dt][r] = 0.0f;
   // m: the exponent offset (log2 units) of this query's weights, kept within kSlack of the
   // running maximum: O and l are rescaled only when the maximum outgrows it, so the weights
-  // stay below 2^kSlack. l: this lane's share of the sum of the weights.
+  // stay below 2^kSlack. l: this lane's share of the sum of the weights (fp32).
   constexpr float kSlack = 8.0f;
   float m = -INFINITY, l = 0.0f;
 

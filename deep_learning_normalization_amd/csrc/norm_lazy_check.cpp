@@ -141,6 +141,8 @@ norm_status_t check_attention(const AttnCheck &c) {
   const void *ptrs[] = {c.Q, c.K, c.V, c.O, c.wq, c.bq, c.wk, c.bk, c.workspace};
   if (c.ldq % 8 || c.ldk % 8 || c.ldv % 8 || c.ldo % 8 || common_align(ptrs, 9) < 16)
     return NORM_ERR_UNSUPPORTED;
+  // key and value rows are addressed by 32-bit byte offsets within a tile
+  if (c.ldk >= (1 << 24) || c.ldv >= (1 << 24)) return NORM_ERR_UNSUPPORTED;
   const int64_t qblocks = (c.S + kAttnBQ - 1) / kAttnBQ;
   if (c.B * c.Hq > 0x7fffffffLL / qblocks) return NORM_ERR_UNSUPPORTED;
   return NORM_OK;

@@ -459,7 +459,7 @@ norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int
  *   are rounded once to bf16 and the keys enter the product exactly (LayerNorm: centred,
  *   rounded once to bf16).
  *   Requirements: D == 128; ldq, ldk, ldv, ldo multiples of 8 and at least Hq * D (Hk * D for
- *   K and V); Q, K, V, O, the norm vectors and the workspace 16-byte aligned. Otherwise NORM_ERR_UNSUPPORTED
+ *   K and V); ldk and ldv below 2^24; Q, K, V, O, the norm vectors and the workspace 16-byte aligned. Otherwise NORM_ERR_UNSUPPORTED
  *   (head size, alignment) or NORM_ERR_INVALID_ARG (sizes, Hq not a multiple of Hk, NULL
  *   pointers, eps, scale, flags, overlaps). B == 0 or S == 0: NORM_OK once the rest passes,
  *   nothing launched and no pointer read. The call allocates nothing.
