@@ -327,16 +327,16 @@ def attention_flops(a):
     return 4 * a.B * a.Hq * a.D * pairs
 
 
-def attention_cpu_baseline(a, rows=32):
-    """The oracle on `rows` queries at the end of one head (each sees all S keys), scaled to
-    the whole call's flops per second; single-threaded cost measured with the oracle's
-    threads."""
+def attention_cpu_baseline(a, rows=None):
+    """The oracle on `rows` queries at the end of one head (default: the whole head, every
+    query of it), as matrix-product flops per second on the host's cores."""
     import oracle
     from deep_learning_normalization_amd import inputs
     t = inputs.make_attention(a)
     hb = inputs.host_bits
     kind = {"rmsnorm": oracle.RMSNORM, "layernorm": oracle.LAYERNORM, "none": oracle.NO_NORM}
     args = [hb(t[n]) for n in ("Q", "K", "V", "wq", "bq", "wk", "bk")]
+    rows = a.S if rows is None else rows
     t0 = time.perf_counter()
     oracle.norm_attention(kind[a.kind], *args, eps=a.eps, scale=a.D ** -0.5, causal=a.causal,
                           b=0, h=0, rows=(a.S - rows, a.S))
@@ -344,9 +344,9 @@ def attention_cpu_baseline(a, rows=32):
     flops = 4 * a.D * sum((s + 1) if a.causal else a.S for s in range(a.S - rows, a.S))
     return {"value": round(flops / sec / 1e12, 6), "unit": "TFLOP/s", "kind": "oracle",
             "cores": oracle.num_threads(), "seconds": round(sec, 3),
-            "sample": "%d queries of one head at the end of the sequence (each against %s keys), "
-                      "key norms of that head included" % (rows, "its preceding" if a.causal
-                                                           else "all %d" % a.S)}
+            "sample": "the last %d queries of one head (each against %s keys), the norms of "
+                      "that head's keys included" % (rows, "its preceding" if a.causal
+                                                      else "all %d" % a.S)}
 
 
 def attention_bench(a, torch, nl, steps, warmup, cpu=False):
