@@ -214,10 +214,11 @@ def projection(p, torch, nl, steps, warmup):
     """One projection workload: the fused product (statistics formed from the X tiles), the
     statistics pass plus the product with given statistics, the unfused pair (norm_fwd to a
     bf16 Y, then torch's 2-D product with the bias in bf16, i.e. hipBLASLt) and that product
-    alone. Two
-    buffer sets alternate (X, Y: 2 x 256 MiB at 16384 x 4096, beyond the memory-side cache).
-    Times are loop times per call over `steps` calls after `warmup`; the product kernel's own
-    duration is taken from HIP events on every launch (norm_set_launch_events)."""
+    alone. Two buffer sets alternate (X, Y: 2 x 256 MiB at 16384 x 4096, beyond the
+    memory-side cache). The forms alternate call by call, each call bracketed by its own pair
+    of HIP events, because the clock drifts by several percent over seconds of matrix-core
+    load; the figures are medians over `steps` calls of each form. The product kernel's own
+    duration is taken from HIP events on every fused launch (norm_set_launch_events)."""
     from deep_learning_normalization_amd import inputs
     w = p.norm
     host = inputs.make(w)
@@ -238,23 +239,6 @@ def projection(p, torch, nl, steps, warmup):
     ws = nl.workspace(w.kind, torch.bfloat16, nl.PASS_FWD, M, K)
     G, sv, tv = nl.fold_projection(w.kind, L, g, b, c)
 
-    def fold(i):
-        nl.norm_fold_projection(w.kind, L, g, b, c, G, sv, tv)
-
-    def fused(i):
-        nl.norm_lazy_linear(w.kind, Xs[i % 2], w.eps, G, sv, tv, Ys[i % 2])
-
-    def given(i):
-        nl.norm_stats(w.kind, Xs[i % 2], None, w.eps, None, mean, rstd, ws)
-        nl.norm_lazy_linear(w.kind, Xs[i % 2], w.eps, G, sv, tv, Ys[i % 2], mean_in=mean,
-                            rstd_in=rstd)
-
-    def stats(i):
-        nl.norm_stats(w.kind, Xs[i % 2], None, w.eps, None, mean, rstd, ws)
-
-    def norm(i):
-        nl.norm_fwd(w.kind, Xs[i % 2], None, g, b, w.eps, Ns[i % 2], None, mean, rstd, ws)
-
     def product(A, Y):
         # hipBLASLt through torch: the 2-D product with L transposed, bias in its epilogue
         if cb is None:
@@ -262,48 +246,50 @@ def projection(p, torch, nl, steps, warmup):
         else:
             torch.addmm(cb, A, Lt, out=Y)
 
-    def unfused(i):
-        norm(i)
-        product(Ns[i % 2], Ys[i % 2])
+    def norm(i):
+        nl.norm_fwd(w.kind, Xs[i % 2], None, g, b, w.eps, Ns[i % 2], None, mean, rstd, ws)
 
-    def linear(i):
-        product(Xs[i % 2], Ys[i % 2])
-
-    def loop(body, n, timers=None):
-        for i in range(warmup):
-            body(i)
+    forms = {
+        "fused": lambda i: nl.norm_lazy_linear(w.kind, Xs[i % 2], w.eps, G, sv, tv, Ys[i % 2]),
+        "given": lambda i: (nl.norm_stats(w.kind, Xs[i % 2], None, w.eps, None, mean, rstd, ws),
+                            nl.norm_lazy_linear(w.kind, Xs[i % 2], w.eps, G, sv, tv, Ys[i % 2],
+                                                mean_in=mean, rstd_in=rstd)),
+        "stats": lambda i: nl.norm_stats(w.kind, Xs[i % 2], None, w.eps, None, mean, rstd, ws),
+        "norm_fwd": norm,
+        "unfused": lambda i: (norm(i), product(Ns[i % 2], Ys[i % 2])),
+        "hipblaslt_linear": lambda i: product(Xs[i % 2], Ys[i % 2]),
+        "fold": lambda i: nl.norm_fold_projection(w.kind, L, g, b, c, G, sv, tv),
+    }
+    t_end = time.perf_counter() + 0.5  # the clock settles under load
+    i = 0
+    while time.perf_counter() < t_end or i < warmup:
+        for f in forms.values():
+            f(i)
+        i += 1
         torch.cuda.synchronize()
-        a = torch.cuda.Event(enable_timing=True)
-        e = torch.cuda.Event(enable_timing=True)
-        a.record()
-        for i in range(n):
-            if timers is not None:
-                timers[i].arm()
-            body(i)
-        e.record()
-        torch.cuda.synchronize()
-        return a.elapsed_time(e) / n * 1e3
-
-    # settle the clock under load
-    t_end = time.perf_counter() + 0.3
-    while time.perf_counter() < t_end:
-        fused(0)
-        torch.cuda.synchronize()
+    evs = {k: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(steps)] for k in forms}
     timers = [nl.KernelTimer() for _ in range(steps)]
-    r = {"fused_us": loop(fused, steps, timers)}
-    k_us = 1e3 * sum(t.elapsed_ms() for t in timers) / steps
-    r["given_us"] = loop(given, steps)
-    r["stats_us"] = loop(stats, steps)
-    r["norm_fwd_us"] = loop(norm, steps)
-    r["unfused_us"] = loop(unfused, steps)
-    r["hipblaslt_linear_us"] = loop(linear, steps)
-    r["fold_us"] = loop(fold, max(5, steps // 4))
+    for j in range(steps):
+        for k, f in forms.items():
+            evs[k][j][0].record()
+            if k == "fused":
+                timers[j].arm()
+            f(j)
+            evs[k][j][1].record()
+    torch.cuda.synchronize()
+    r = {}
+    for k in forms:
+        d = sorted(a0.elapsed_time(a1) * 1e3 for a0, a1 in evs[k])
+        r[k + "_us"] = d[len(d) // 2]
+    kd = sorted(1e3 * t.elapsed_ms() for t in timers)
+    k_us = kd[len(kd) // 2]
     flops = 2.0 * M * K * Nout
     achieved = flops / (k_us * 1e-6) / 1e12
     out = {
         "workload": p.name, "kind": w.kind, "M": M, "K": K, "Nout": Nout, "dtype": "bf16",
         "what": "Norm(X) L^T + c: rstd * (X G^T - mean * s) + t on the matrix cores, G = "
-                "bf16(L * gamma) from norm_fold_projection",
+                "bf16(L * gamma) from norm_fold_projection; medians of alternating calls",
         "flops_per_call": flops,
     }
     out.update({k: round(v, 2) for k, v in r.items()})

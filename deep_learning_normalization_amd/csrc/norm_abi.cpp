@@ -270,12 +270,14 @@ norm_status_t norm_lazy_linear(norm_kind_t kind, const void *X, int64_t ldx, int
   a.ldx = ldx;
   a.ldg = ldg;
   a.ldy = ldy;
-  const int64_t tm = (M + 127) / 128, tn = (Nout + 127) / 128;
+  const int64_t tm = (M + dln::kLazyTile - 1) / dln::kLazyTile;
+  const int64_t tn = (Nout + dln::kLazyTile - 1) / dln::kLazyTile;
   if (tm > 0x7fffffff || tn > 0x7fffffff) return NORM_ERR_UNSUPPORTED;
   a.tiles_m = (int32_t)tm;
   a.tiles_n = (int32_t)tn;
   a.eps = eps;
   a.inv_k = 1.0f / (float)K;
+  a.vec_store = ((uintptr_t)Y % 8 == 0 && ldy % 4 == 0) ? 1 : 0;
   return dln::launch_lazy_linear(kind == NORM_LAYERNORM, a, static_cast<hipStream_t>(stream));
 }
 

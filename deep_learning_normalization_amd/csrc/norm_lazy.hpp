@@ -7,6 +7,9 @@
 
 namespace dln {
 
+// output rows and columns per workgroup of the projection product
+constexpr int kLazyTile = 256;
+
 struct FoldArgs {
   const uint16_t *l;  // [Nout, K] bf16, row stride ldl
   const void *gamma;  // [K] bf16 or fp32
@@ -30,6 +33,7 @@ struct LazyArgs {
   int64_t ldx, ldg, ldy;
   int32_t tiles_m, tiles_n;
   float eps, inv_k;
+  int32_t vec_store;  // Y 8-byte aligned with ldy a multiple of 4: four columns per store
 };
 
 norm_status_t launch_fold_projection(bool f32_weights, const FoldArgs &a, int64_t nout,

@@ -104,6 +104,8 @@ norm_status_t check_lazy(const LazyCheck &c) {
   const void *ptrs[] = {c.X, c.G};
   if (c.K % 8 || c.ldx % 8 || c.ldg % 8 || common_align(ptrs, 2) < 16)
     return NORM_ERR_UNSUPPORTED;
+  // rows of a 256-row tile are addressed by 32-bit byte offsets from its first row
+  if (c.ldx >= (1 << 23) || c.ldg >= (1 << 23)) return NORM_ERR_UNSUPPORTED;
   return NORM_OK;
 }
 

@@ -403,13 +403,15 @@ norm_status_t norm_set_tuning(norm_tune_t key, int64_t value);
  *           row's first element; var = E[(x-x0)^2] - E[x-x0]^2, clamped at 0; rstd =
  *           1/sqrt(var + eps)) and, when mean_out / rstd_out are given, stores them [M] fp32.
  *   Y       [M, Nout] bf16 out, row stride ldy.
- *   Requirements: K a multiple of 8; ldx and ldg multiples of 8; X and G 16-byte aligned (the
- *   product reads 16-byte chunks of 8 values); ldy >= Nout. Otherwise NORM_ERR_UNSUPPORTED
- *   (alignment) or NORM_ERR_INVALID_ARG (sizes, NULL pointers, eps). M == 0: NORM_OK once the
- *   sizes and eps pass, nothing launched and no pointer read. Y must not overlap X, G, s, t
- *   or the statistics.
- *   The product runs on the matrix cores (bf16 inputs, fp32 accumulation) in 128 x 128 output
- *   tiles.
+ *   Requirements: K a multiple of 8; ldx and ldg multiples of 8 and below 2^23 (rows of a
+ *   256-row tile are addressed by 32-bit byte offsets); X and G 16-byte aligned (the product
+ *   reads 16-byte chunks of 8 values); ldy >= Nout. Otherwise NORM_ERR_UNSUPPORTED (layout)
+ *   or NORM_ERR_INVALID_ARG (sizes, NULL pointers, eps). M == 0: NORM_OK once the sizes and
+ *   eps pass, nothing launched and no pointer read. Y must not overlap X, G, s, t or the
+ *   statistics.
+ *   The product runs on the matrix cores (bf16 inputs, fp32 accumulation) in 256 x 256 output
+ *   tiles; Y is written four columns (8 bytes) at a time where Y is 8-byte aligned and ldy a
+ *   multiple of 4, else one value at a time.
  */
 norm_status_t norm_fold_projection(norm_kind_t kind, norm_dtype_t dtype, const void *L,
                                    int64_t ldl, const void *gamma, const void *beta,

@@ -564,6 +564,10 @@ def test_fold_projection_checks():
         assert _fold(**kw) == nl.ERR_INVALID_ARG, kw
 
 
+# fake operands far apart, for strides whose spans would overlap the packed fakes above
+FAR = dict(X=1 << 40, G=2 << 40, s=3 << 40, t=4 << 40, Y=5 << 40)
+
+
 def test_lazy_linear_checks():
     assert _lazy() == nl.ERR_HIP                           # statistics formed in the product
     assert _lazy(mean_out=FAKE * 6, rstd_out=FAKE * 7) == nl.ERR_HIP
@@ -586,8 +590,11 @@ def test_lazy_linear_checks():
         assert _lazy(**kw) == nl.ERR_INVALID_ARG, kw
     for kw in (dict(K=60, ldx=64, ldg=64),                 # K not a multiple of 8
                dict(ldx=68), dict(ldg=72 + 4),             # row strides not multiples of 8
-               dict(X=FAKE + 8), dict(G=FAKE * 2 + 2)):    # not 16-byte aligned
+               dict(X=FAKE + 8), dict(G=FAKE * 2 + 2),     # not 16-byte aligned
+               dict(FAR, M=2, ldx=1 << 23),                # tile rows past 32-bit offsets
+               dict(FAR, Nout=2, ldg=1 << 23, ldy=32)):
         assert _lazy(**kw) == nl.ERR_UNSUPPORTED, kw
+    assert _lazy(**dict(FAR, M=2, ldx=(1 << 23) - 8)) == nl.ERR_HIP
 
 
 # ---- attention over normalised queries and keys: argument checks ------------------------------

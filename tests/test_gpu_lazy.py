@@ -4,8 +4,8 @@ against the oracle's Norm(X) L^T + c, through the C ABI.
 The oracle evaluates the definition (the norm row in float64, then the dot products); the
 device evaluates rstd * (X G^T - mean * s) + t with G = bf16(L * gamma) on the matrix cores.
 The tolerance is the error bound of that arithmetic (tests/parity.py, norm_linear_bound).
-Shapes span several 128 x 128 output tiles with ragged edges in M, Nout and K (K = 200 ends in
-a partial 64-wide step)."""
+Shapes span several 256 x 256 output tiles with ragged edges in M, Nout and K (K = 200 and
+K = 520 end in a partial 64-wide step)."""
 import numpy as np
 import pytest
 import torch
@@ -100,7 +100,8 @@ def _bits(Y, rows=None):
     return inputs.host_bits(Y.contiguous())
 
 
-SHAPES = [(1, 8, 1), (5, 64, 7), (130, 200, 129), (257, 512, 300), (64, 4096, 256)]
+SHAPES = [(1, 8, 1), (5, 64, 7), (130, 200, 129), (257, 512, 300), (64, 4096, 256),
+          (600, 520, 530), (768, 128, 772)]
 
 
 @pytest.mark.parametrize("M,K,Nout", SHAPES, ids=lambda v: str(v))
@@ -216,7 +217,7 @@ def test_lazy_linear_zero_rows():
                          ids=lambda p: p.name)
 def test_lazy_linear_full_size(proj):
     """The full-size projections in the configuration the benchmark times, on sampled rows
-    (first, last, the 128-row tile edges 127/128 and 8191/8192, and random ones) against the
+    (first, last, the tile edges 255/256 and 8191/8192, and random ones) against the
     oracle. Rows are sampled because every row would cost the double-precision oracle
     2 * 16384 * 4096 * 4096 = 550 G multiply-adds in plain loops (many minutes on the host);
     the smaller projection tests compare every row."""
@@ -226,7 +227,7 @@ def test_lazy_linear_full_size(proj):
     p = inputs.make_projection(proj)
     X, g, b = t["X"], t["W"], t["B"]
     L, c = p["L"], p["c"]
-    rows = sorted(set(parity.sample_rows(w.M, k=16, seed=4).tolist()) | {127, 128, 8191, 8192})
+    rows = sorted(set(parity.sample_rows(w.M, k=16, seed=4).tolist()) | {255, 256, 8191, 8192})
     for mode in ("formed", "given"):
         Y, _, _, _ = _run(w.kind, X, g, b, L, c, w.eps, mode)
         ref, xd = _reference(w.kind, X, g, b, L, c, w.eps, rows)
