@@ -210,7 +210,19 @@ def oracle_single_thread(runs=3):
     return out
 
 
-def projection(p, torch, nl, steps, warmup):
+def add_mfma_ceiling(roof, mfma):
+    """The measured matrix-core ceiling (probes.mfma_ceiling) beside the published peak: these
+    kernels issue 32x32x16 bf16 operations, so that shape's best rate is their ceiling."""
+    if mfma is None:
+        return
+    c = mfma["32x32x16"]["TFLOPs"]
+    roof["ceiling_TFLOPs"] = c
+    roof["frac_ceiling"] = round(roof["achieved"] / c, 4)
+    roof["ceiling"] = ("mfma_probe (libhbmprobe.so, include/hbm_probe.h): 32x32x16 bf16 "
+                       "operations on register operands, no memory traffic")
+
+
+def projection(p, torch, nl, steps, warmup, mfma=None):
     """One projection workload: the fused product (statistics formed from the X tiles), the
     statistics pass plus the product with given statistics, the unfused pair (norm_fwd to a
     bf16 Y, then torch's 2-D product with the bias in bf16, i.e. hipBLASLt) and that product
@@ -297,6 +309,7 @@ def projection(p, torch, nl, steps, warmup):
     out["roofline"] = {"bound": "mfma", "kernel": "lazy_linear_kernel", "achieved":
                        round(achieved, 1), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                        "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": None}
+    add_mfma_ceiling(out["roofline"], mfma)
     out["hipblaslt_TFLOPs"] = round(flops / (r["hipblaslt_linear_us"] * 1e-6) / 1e12, 1)
     # what the norm adds on top of the bare product, unfused and fused
     out["norm_cost_unfused_us"] = round(r["unfused_us"] - r["hipblaslt_linear_us"], 2)
@@ -335,7 +348,7 @@ def attention_cpu_baseline(a, rows=None):
                                                       else "all %d" % a.S)}
 
 
-def attention_bench(a, torch, nl, steps, warmup, cpu=False):
+def attention_bench(a, torch, nl, steps, warmup, cpu=False, mfma=None):
     """Attention over normalised queries and keys (norm_attention_fwd with a workspace: the key
     pass, then the attention kernel with the queries normalised inside it) against the same
     computation in two passes (norm_fwd on the query vectors and on the key vectors, then the
@@ -378,6 +391,7 @@ def attention_bench(a, torch, nl, steps, warmup, cpu=False):
                         "included)", "achieved": round(tf, 1), "peak": PEAK_BF16_TFLOPS,
                         "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4),
                         "traffic": None}}
+    add_mfma_ceiling(out["roofline"], mfma)
     out["attention_alone_TFLOPs"] = round(flops / (med["attention_alone"] * 1e-6) / 1e12, 1)
     if cpu:
         out["cpu_baseline"] = attention_cpu_baseline(a)
@@ -418,9 +432,13 @@ def main():
     nl.lib()  # fails loudly if libnorm.so is missing
     probes.lib()
 
+    if args.projection or args.attention:
+        mfma = probes.mfma_ceiling()
+        print(json.dumps({"mfma_ceiling_TFLOPs": mfma, "peak_TFLOPs": PEAK_BF16_TFLOPS}),
+              flush=True)
     if args.projection:
         for p in (inputs.LN_LINEAR_BF16_16384x4096x4096, inputs.RMS_LINEAR_BF16_16384x4096x4096):
-            print(json.dumps(projection(p, torch, nl, args.steps, args.warmup)), flush=True)
+            print(json.dumps(projection(p, torch, nl, args.steps, args.warmup, mfma)), flush=True)
         return
     if args.attention:
         from dataclasses import replace
@@ -432,7 +450,8 @@ def main():
                                 name="qknorm_attention_bf16_b2_s%d_hq32_hk8_d128_%s_%s" % (
                                     S, "causal" if causal else "full", kind))
                     print(json.dumps(attention_bench(a, torch, nl, min(args.steps, 50),
-                                                     args.warmup, cpu=(S == 4096 and causal))),
+                                                     args.warmup, cpu=(S == 4096 and causal),
+                                                     mfma=mfma)),
                           flush=True)
         return
 
@@ -510,8 +529,11 @@ def main():
             torch.cuda.empty_cache()
         line["shapes"] = shapes
         say("attention %s" % inputs.ATTN_QKNORM_B2_S4096.name)
+        mfma = probes.mfma_ceiling()
         line["attention"] = attention_bench(inputs.ATTN_QKNORM_B2_S4096, torch, nl, 30,
-                                            args.warmup, cpu=not args.no_cpu_baseline)
+                                            args.warmup, cpu=not args.no_cpu_baseline,
+                                            mfma=mfma)
+        line["attention"]["mfma_ceilings_TFLOPs"] = mfma
     if not args.no_cpu_baseline:
         say("cpu baseline")
         line["cpu_baseline"] = cpu_baseline(w)

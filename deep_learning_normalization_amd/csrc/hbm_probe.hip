@@ -1,5 +1,6 @@
 // hbm_probe.hip -- streaming probes of HBM bandwidth (read, write, copy, two reads and one
-// write, two reads and two writes), the ceilings for the norm passes' stream mixes.
+// write, two reads and two writes), the ceilings for the norm passes' stream mixes, and a
+// matrix-core probe, the ceiling for the bf16 products.
 //
 // Each thread moves `U` 16-byte accesses per stream of one tile (256 threads x U accesses,
 // consecutive threads on consecutive 16-byte words, so every wavefront access is 1 KiB
@@ -89,7 +90,72 @@ hipError_t by_shape(int unroll, int nt, const void *in0, const void *in1, void *
 
 bool aligned16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
 
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Every wavefront runs `iters` rounds of eight independent bf16 matrix operations on operands
+// held in registers (no memory traffic), then stores one sum per lane so that none is dropped.
+template <int SHAPE, int NT>
+__global__ __launch_bounds__(NT) void mfma_probe_kernel(float *out, int iters) {
+  const int t = threadIdx.x;
+  bf16x8_t a, b;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = (__bf16)(float)((t + i) & 15);
+    b[i] = (__bf16)(float)((t ^ i) & 15);
+  }
+  float s = 0.0f;
+  if constexpr (SHAPE == 32) {
+    f32x16_t acc[8] = {};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) s += acc[u][r];
+  } else {
+    f32x4_t acc[8] = {};
+    for (int it = 0; it < iters; ++it)
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+        acc[u] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[u], 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) s += acc[u][r];
+  }
+  out[(int64_t)blockIdx.x * NT + t] = s;
+}
+
+template <int SHAPE, int NT>
+hipError_t launch_mfma(float *out, int64_t grid, int iters, hipEvent_t e0, hipEvent_t e1,
+                       hipStream_t s) {
+  void *args[] = {&out, &iters};
+  return hipExtLaunchKernel(reinterpret_cast<const void *>(mfma_probe_kernel<SHAPE, NT>),
+                            dim3((unsigned)grid), dim3(NT), args, 0, s, e0, e1, 0);
+}
+
 } // namespace
+
+extern "C" int mfma_probe(int shape, int waves_per_simd, int64_t grid, int iters, float *out,
+                          void *start_event, void *stop_event, void *stream) {
+  if ((shape != 32 && shape != 16) || (waves_per_simd != 1 && waves_per_simd != 2)) return -1;
+  if (grid <= 0 || grid > 0x7fffffff / 512 || iters <= 0 || !out) return -1;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return -1;
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  if (shape == 32)
+    e = waves_per_simd == 1 ? launch_mfma<32, 256>(out, grid, iters, e0, e1, s)
+                            : launch_mfma<32, 512>(out, grid, iters, e0, e1, s);
+  else
+    e = waves_per_simd == 1 ? launch_mfma<16, 256>(out, grid, iters, e0, e1, s)
+                            : launch_mfma<16, 512>(out, grid, iters, e0, e1, s);
+  return e == hipSuccess ? 0 : -2;
+}
 
 extern "C" int hbm_probe(int nin, int nout, const void *in0, const void *in1, void *out0,
                          void *out1, size_t bytes, int unroll, int nt_loads, int64_t grid,

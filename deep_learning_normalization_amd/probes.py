@@ -1,6 +1,7 @@
 """Binding of libhbmprobe.so (include/hbm_probe.h): streaming kernels that measure the HBM
 bandwidth a stream mix reaches on this device (read, write, copy, two reads and one write, two
-reads and two writes), the ceilings the benchmark reports beside the norm passes.
+reads and two writes), the ceilings the benchmark reports beside the norm passes, and a
+matrix-core probe, the ceiling for the bf16 products.
 
 ceilings() times every probe over buffers that rotate through more than 1 GiB (so no call finds
 its inputs in the 256 MB memory-side cache), each launch bracketed by its own kernel timestamps,
@@ -30,6 +31,9 @@ def lib():
                                 ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_uint32, vp,
                                 vp, vp]
         L.hbm_probe.restype = ctypes.c_int
+        L.mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, vp,
+                                 vp, vp, vp]
+        L.mfma_probe.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -93,3 +97,39 @@ def ceilings(stream_bytes=256 << 20, pool=8, iters=12, variants=None):
     del bufs
     torch.cuda.empty_cache()
     return out
+
+
+# flops of one matrix operation of each probed shape
+MFMA_FLOPS = {32: 2 * 32 * 32 * 16, 16: 2 * 16 * 16 * 32}
+
+
+def mfma_ceiling(iters=4096, launches=8):
+    """Measured bf16 matrix-core rate in TFLOP/s per operation shape (32x32x16, 16x16x32) and
+    occupancy (one or two wavefronts per SIMD): one workgroup per compute unit, each wavefront
+    running `iters` x 8 independent operations; the median of `launches` timed launches. The
+    best figure per shape is the ceiling for kernels built on that shape."""
+    from deep_learning_normalization_amd import normlib as nl
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cu * 512, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    timers = [nl.KernelTimer() for _ in range(launches)]
+    res = {}
+    for shape in (32, 16):
+        best = None
+        for waves in (1, 2):
+            for t in [None, None] + timers:
+                st = lib().mfma_probe(shape, waves, cu, iters, out.data_ptr(),
+                                      t.start.value if t else None,
+                                      t.stop.value if t else None, s)
+                if st != 0:
+                    raise RuntimeError("mfma_probe(%d, %d) failed: %d" % (shape, waves, st))
+            torch.cuda.synchronize()
+            us = sorted(1e3 * t.elapsed_ms() for t in timers)
+            med = us[len(us) // 2]
+            flops = cu * 4 * waves * iters * 8 * MFMA_FLOPS[shape]
+            tf = flops / (med * 1e-6) / 1e12
+            if best is None or tf > best["TFLOPs"]:
+                best = {"TFLOPs": round(tf, 1), "waves_per_simd": waves, "us": round(med, 2)}
+        res["%dx%dx%d" % ((32, 32, 16) if shape == 32 else (16, 16, 32))] = best
+    del out
+    return res

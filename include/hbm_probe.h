@@ -1,6 +1,6 @@
 /*
  * hbm_probe.h -- streaming kernels that measure what HBM delivers on this device, the ceilings
- * the norm kernels are compared against.
+ * the norm kernels are compared against, and a matrix-core probe for the bf16 products.
  *
  * The norm passes are streams: the forward reads one [M, N] tensor and writes one, the fused
  * backward reads two and writes one, the residual forward reads two and writes two. The share
@@ -43,6 +43,20 @@ extern "C" {
 int hbm_probe(int nin, int nout, const void *in0, const void *in1, void *out0, void *out1,
               size_t bytes, int unroll, int nt_loads, int64_t grid, uint32_t key,
               void *start_event, void *stop_event, void *stream);
+
+/*
+ * Queue the matrix-core probe on `stream`: `grid` workgroups of 64 * 4 * waves_per_simd threads
+ * (one or two wavefronts per SIMD), each wavefront running `iters` rounds of eight independent
+ * bf16 matrix operations (fp32 accumulation) on register operands, with no memory traffic
+ * beyond one float per thread written to out [grid * 64 * 4 * waves_per_simd] at the end. Its
+ * rate is the ceiling for the bf16 products (the attention kernel, the projection product):
+ *   shape   32: v_mfma_f32_32x32x16_bf16 (32768 flops per operation); 16:
+ *           v_mfma_f32_16x16x32_bf16 (16384 flops).
+ *   start_event, stop_event: NULL, or two hipEvent_t that take the kernel's timestamps.
+ * Returns 0 once queued, -1 for invalid arguments, -2 if the launch failed.
+ */
+int mfma_probe(int shape, int waves_per_simd, int64_t grid, int iters, float *out,
+               void *start_event, void *stop_event, void *stream);
 
 #ifdef __cplusplus
 }

@@ -57,3 +57,56 @@ def test_ceilings_report_every_mix():
         nin, nout = probes.MIXES[name]
         assert e["streams"] == "%dR%dW" % (nin, nout)
         assert 100.0 < e["GBps"] < 8000.0 * 1.05, (name, e)
+
+
+def _mfma_expected(shape, nt, iters):
+    """What every thread of the matrix-core probe stores, from the operand layouts: lane l of a
+    wavefront supplies row l % R of A and column l % R of B with the 8 values of k at
+    8 * (l // R) (R = 32 or 16), and holds the outputs of column l % R; for 32 x 32 blocks the
+    rows 8 * (j // 4) + 4 * (l // 32) + j % 4 of registers j, for 16 x 16 blocks the rows
+    4 * (l // 16) + j. Small integers keep every sum exact in fp32."""
+    import numpy as np
+    R, KB = (32, 16) if shape == 32 else (16, 32)
+    out = np.zeros(nt)
+    for w in range(nt // 64):
+        t = np.arange(64) + 64 * w
+        i = np.arange(8)
+        a = ((t[:, None] + i[None, :]) & 15).astype(np.float64)
+        b = ((t[:, None] ^ i[None, :]) & 15).astype(np.float64)
+        A = np.zeros((R, KB))
+        B = np.zeros((KB, R))
+        for l in range(64):
+            A[l % R, 8 * (l // R):8 * (l // R) + 8] = a[l]
+            B[8 * (l // R):8 * (l // R) + 8, l % R] = b[l]
+        D = A @ B
+        for l in range(64):
+            if shape == 32:
+                rows = [8 * (j // 4) + 4 * (l // 32) + j % 4 for j in range(16)]
+            else:
+                rows = [4 * (l // 16) + j for j in range(4)]
+            out[64 * w + l] = 8 * iters * D[rows, l % R].sum()
+    return out
+
+
+@pytest.mark.parametrize("shape,waves", [(32, 1), (32, 2), (16, 1), (16, 2)])
+def test_mfma_probe_computes_what_it_claims(shape, waves):
+    print("[gpu] mfma probe %d waves %d" % (shape, waves), flush=True)
+    import numpy as np
+    nt = 256 * waves
+    grid, iters = 3, 5
+    out = torch.full((grid * nt + 64,), -1.0, device="cuda")
+    assert probes.lib().mfma_probe(shape, waves, grid, iters, out.data_ptr(), None, None,
+                                   None) == 0
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = _mfma_expected(shape, nt, iters)
+    for g in range(grid):
+        assert np.array_equal(got[g * nt:(g + 1) * nt], want), (shape, waves, g)
+    assert (got[grid * nt:] == -1.0).all()
+
+
+def test_mfma_ceiling_is_plausible():
+    print("[gpu] mfma ceiling", flush=True)
+    c = probes.mfma_ceiling(iters=512, launches=4)
+    for k in ("32x32x16", "16x16x32"):
+        assert 100.0 < c[k]["TFLOPs"] <= 2500.0, c

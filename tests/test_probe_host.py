@@ -22,11 +22,11 @@ def _lib_built():
 
 def test_exports_what_the_header_declares():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    declared = set(re.findall(r"\b(hbm_[a-z_]+)\s*\(", text))
+    declared = set(re.findall(r"\b((?:hbm|mfma)_[a-z_]+)\s*\(", text))
     out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    assert declared == {"hbm_probe"}
-    assert declared <= set(re.findall(r"\bT (hbm_[a-z_]+)\b", out))
+    assert declared == {"hbm_probe", "mfma_probe"}
+    assert declared <= set(re.findall(r"\bT ((?:hbm|mfma)_[a-z_]+)\b", out))
 
 
 def test_header_compiles_as_c():
@@ -61,6 +61,20 @@ def test_probe_rejects(args):
                                   None, None) == -1
     # one event without the other
     assert probes.lib().hbm_probe(1, 1, A, None, C, None, 4096, 4, 0, 0, 0, A, None, None) == -1
+
+
+@pytest.mark.parametrize("args", [
+    (8, 1, 256, 16, A),        # no such shape
+    (32, 3, 256, 16, A),       # one or two wavefronts per SIMD only
+    (32, 1, 0, 16, A),         # no workgroups
+    (16, 2, 1 << 30, 16, A),   # grid past 32-bit thread counts
+    (32, 1, 256, 0, A),        # no iterations
+    (16, 1, 256, 16, None),    # no output
+])
+def test_mfma_probe_rejects(args):
+    shape, waves, grid, iters, out = args
+    assert probes.lib().mfma_probe(shape, waves, grid, iters, out, None, None, None) == -1
+    assert probes.lib().mfma_probe(32, 1, 256, 16, A, A, None, None) == -1
 
 
 @pytest.mark.parametrize("w", inputs.all_workloads(), ids=lambda w: w.name)
