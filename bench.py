@@ -434,7 +434,8 @@ def main():
 
     if args.projection or args.attention:
         mfma = probes.mfma_ceiling()
-        print(json.dumps({"mfma_ceiling_TFLOPs": mfma, "peak_TFLOPs": PEAK_BF16_TFLOPS}),
+        print(json.dumps({"mfma_ceiling_TFLOPs": mfma, "peak_TFLOPs": PEAK_BF16_TFLOPS,
+                          "lds_read_bytes_per_clk_per_cu": probes.lds_read_rate()}),
               flush=True)
     if args.projection:
         for p in (inputs.LN_LINEAR_BF16_16384x4096x4096, inputs.RMS_LINEAR_BF16_16384x4096x4096):

@@ -1,6 +1,6 @@
 // hbm_probe.hip -- streaming probes of HBM bandwidth (read, write, copy, two reads and one
-// write, two reads and two writes), the ceilings for the norm passes' stream mixes, and a
-// matrix-core probe, the ceiling for the bf16 products.
+// write, two reads and two writes), the ceilings for the norm passes' stream mixes, and
+// matrix-core and LDS read probes, the ceilings for the bf16 products.
 //
 // Each thread moves `U` 16-byte accesses per stream of one tile (256 threads x U accesses,
 // consecutive threads on consecutive 16-byte words, so every wavefront access is 1 KiB
@@ -138,7 +138,49 @@ hipError_t launch_mfma(float *out, int64_t grid, int iters, hipEvent_t e0, hipEv
                             dim3((unsigned)grid), dim3(NT), args, 0, s, e0, e1, 0);
 }
 
+// Every thread reads 16 bytes per access from a 64 KB LDS buffer (filled with a pattern
+// first); the 64 lanes of an access read one contiguous KB (no bank conflicts), and successive
+// accesses walk the buffer. The XOR of everything read goes to out[thread].
+template <int NT>
+__global__ __launch_bounds__(NT) void lds_probe_kernel(unsigned *out, int iters) {
+  typedef unsigned u4 __attribute__((ext_vector_type(4)));
+  __shared__ __align__(16) unsigned char buf[65536];
+  const int t = threadIdx.x;
+  for (int i = t; i < 65536 / 4; i += NT) reinterpret_cast<unsigned *>(buf)[i] = i * 2654435761u;
+  __syncthreads();
+  const int lane = t & 63, wave = t >> 6;
+  unsigned acc = 0;
+  int base = (wave * 1024) & 65535;
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int off = (base + u * 1024 + lane * 16) & 65520;
+      const u4 v = *reinterpret_cast<const u4 *>(buf + off);
+      acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    base = (base + 8192) & 65535;
+  }
+  out[(int64_t)blockIdx.x * NT + t] = acc;
+}
+
 } // namespace
+
+extern "C" int lds_probe(int waves_per_simd, int64_t grid, int iters, unsigned *out,
+                         void *start_event, void *stop_event, void *stream) {
+  if ((waves_per_simd != 1 && waves_per_simd != 2 && waves_per_simd != 4) || grid <= 0 ||
+      grid > 0x7fffffff / 1024 || iters <= 0 || !out)
+    return -1;
+  if ((start_event == nullptr) != (stop_event == nullptr)) return -1;
+  hipEvent_t e0 = static_cast<hipEvent_t>(start_event), e1 = static_cast<hipEvent_t>(stop_event);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  void *args[] = {&out, &iters};
+  const void *k = waves_per_simd == 1 ? reinterpret_cast<const void *>(lds_probe_kernel<256>)
+                  : waves_per_simd == 2 ? reinterpret_cast<const void *>(lds_probe_kernel<512>)
+                                        : reinterpret_cast<const void *>(lds_probe_kernel<1024>);
+  const hipError_t e = hipExtLaunchKernel(k, dim3((unsigned)grid), dim3(256 * waves_per_simd),
+                                          args, 0, s, e0, e1, 0);
+  return e == hipSuccess ? 0 : -2;
+}
 
 extern "C" int mfma_probe(int shape, int waves_per_simd, int64_t grid, int iters, float *out,
                           void *start_event, void *stop_event, void *stream) {

@@ -34,6 +34,8 @@ def lib():
         L.mfma_probe.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int64, ctypes.c_int, vp,
                                  vp, vp, vp]
         L.mfma_probe.restype = ctypes.c_int
+        L.lds_probe.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int, vp, vp, vp, vp]
+        L.lds_probe.restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -131,5 +133,32 @@ def mfma_ceiling(iters=4096, launches=8):
             if best is None or tf > best["TFLOPs"]:
                 best = {"TFLOPs": round(tf, 1), "waves_per_simd": waves, "us": round(med, 2)}
         res["%dx%dx%d" % ((32, 32, 16) if shape == 32 else (16, 16, 32))] = best
+    del out
+    return res
+
+
+def lds_read_rate(iters=4096, launches=8):
+    """Measured LDS read bandwidth in bytes per clock per compute unit (at the 2.4 GHz peak
+    clock) for 16-byte conflict-free reads, per occupancy (1, 2, 4 wavefronts per SIMD): one
+    workgroup per compute unit; the median of `launches` timed launches."""
+    from deep_learning_normalization_amd import normlib as nl
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cu * 1024, dtype=torch.int32, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+    timers = [nl.KernelTimer() for _ in range(launches)]
+    res = {}
+    for waves in (1, 2, 4):
+        for t in [None, None] + timers:
+            st = lib().lds_probe(waves, cu, iters, out.data_ptr(), t.start.value if t else None,
+                                 t.stop.value if t else None, s)
+            if st != 0:
+                raise RuntimeError("lds_probe(%d) failed: %d" % (waves, st))
+        torch.cuda.synchronize()
+        us = sorted(1e3 * t.elapsed_ms() for t in timers)
+        med = us[len(us) // 2]
+        nbytes = cu * 256 * waves * iters * 8 * 16
+        res["%d_waves_per_simd" % waves] = {
+            "bytes_per_clk_per_cu": round(nbytes / (med * 1e-6) / cu / 2.4e9, 1),
+            "us": round(med, 2)}
     del out
     return res

@@ -1,6 +1,7 @@
 /*
  * hbm_probe.h -- streaming kernels that measure what HBM delivers on this device, the ceilings
- * the norm kernels are compared against, and a matrix-core probe for the bf16 products.
+ * the norm kernels are compared against, and matrix-core and LDS read probes for the bf16
+ * products.
  *
  * The norm passes are streams: the forward reads one [M, N] tensor and writes one, the fused
  * backward reads two and writes one, the residual forward reads two and writes two. The share
@@ -57,6 +58,17 @@ int hbm_probe(int nin, int nout, const void *in0, const void *in1, void *out0, v
  */
 int mfma_probe(int shape, int waves_per_simd, int64_t grid, int iters, float *out,
                void *start_event, void *stop_event, void *stream);
+
+/*
+ * Queue the LDS read probe on `stream`: `grid` workgroups of 256 * waves_per_simd threads (1, 2
+ * or 4 wavefronts per SIMD), each with a 64 KB LDS buffer; every thread makes `iters` x 8
+ * reads of 16 bytes, each wavefront read one contiguous KB (conflict-free), and writes the XOR
+ * of what it read to out [grid * 256 * waves_per_simd]. Bytes read per launch:
+ * grid * 256 * waves_per_simd * iters * 8 * 16. Returns 0 once queued, -1 for invalid
+ * arguments, -2 if the launch failed.
+ */
+int lds_probe(int waves_per_simd, int64_t grid, int iters, unsigned *out, void *start_event,
+              void *stop_event, void *stream);
 
 #ifdef __cplusplus
 }

@@ -110,3 +110,37 @@ def test_mfma_ceiling_is_plausible():
     c = probes.mfma_ceiling(iters=512, launches=4)
     for k in ("32x32x16", "16x16x32"):
         assert 100.0 < c[k]["TFLOPs"] <= 2500.0, c
+
+
+@pytest.mark.parametrize("waves", [1, 2, 4])
+def test_lds_probe_reads_what_it_claims(waves):
+    """Every thread's XOR of its reads, recomputed on the host from the fill pattern and the
+    read schedule."""
+    print("[gpu] lds probe %d waves" % waves, flush=True)
+    import numpy as np
+    nt, grid, iters = 256 * waves, 2, 3
+    out = torch.zeros(grid * nt, dtype=torch.int32, device="cuda")
+    assert probes.lib().lds_probe(waves, grid, iters, out.data_ptr(), None, None, None) == 0
+    torch.cuda.synchronize()
+    words = (np.arange(16384, dtype=np.uint64) * 2654435761) & 0xFFFFFFFF
+    want = np.zeros(nt, dtype=np.uint64)
+    for t in range(nt):
+        lane, wave = t & 63, t >> 6
+        acc, base = 0, (wave * 1024) & 65535
+        for _ in range(iters):
+            for u in range(8):
+                off = (base + u * 1024 + lane * 16) & 65520
+                for k in range(4):
+                    acc ^= int(words[off // 4 + k])
+            base = (base + 8192) & 65535
+        want[t] = acc
+    got = out.cpu().numpy().view(np.uint32).astype(np.uint64)
+    for g in range(grid):
+        assert np.array_equal(got[g * nt:(g + 1) * nt], want), (waves, g)
+
+
+def test_lds_read_rate_is_plausible():
+    print("[gpu] lds read rate", flush=True)
+    r = probes.lds_read_rate(iters=512, launches=4)
+    for v in r.values():
+        assert 10.0 < v["bytes_per_clk_per_cu"] < 1024.0, r

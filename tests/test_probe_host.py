@@ -22,11 +22,11 @@ def _lib_built():
 
 def test_exports_what_the_header_declares():
     text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
-    declared = set(re.findall(r"\b((?:hbm|mfma)_[a-z_]+)\s*\(", text))
+    declared = set(re.findall(r"\b((?:hbm|mfma|lds)_[a-z_]+)\s*\(", text))
     out = subprocess.run(["nm", "-D", "--defined-only", probes.LIB_PATH], capture_output=True,
                          text=True, check=True).stdout
-    assert declared == {"hbm_probe", "mfma_probe"}
-    assert declared <= set(re.findall(r"\bT ((?:hbm|mfma)_[a-z_]+)\b", out))
+    assert declared == {"hbm_probe", "mfma_probe", "lds_probe"}
+    assert declared <= set(re.findall(r"\bT ((?:hbm|mfma|lds)_[a-z_]+)\b", out))
 
 
 def test_header_compiles_as_c():
@@ -75,6 +75,19 @@ def test_mfma_probe_rejects(args):
     shape, waves, grid, iters, out = args
     assert probes.lib().mfma_probe(shape, waves, grid, iters, out, None, None, None) == -1
     assert probes.lib().mfma_probe(32, 1, 256, 16, A, A, None, None) == -1
+
+
+@pytest.mark.parametrize("args", [
+    (3, 256, 16, A),           # 1, 2 or 4 wavefronts per SIMD only
+    (1, 0, 16, A),             # no workgroups
+    (4, 1 << 30, 16, A),       # grid past 32-bit thread counts
+    (2, 256, 0, A),            # no iterations
+    (2, 256, 16, None),        # no output
+])
+def test_lds_probe_rejects(args):
+    waves, grid, iters, out = args
+    assert probes.lib().lds_probe(waves, grid, iters, out, None, None, None) == -1
+    assert probes.lib().lds_probe(1, 256, 16, A, None, A, None) == -1
 
 
 @pytest.mark.parametrize("w", inputs.all_workloads(), ids=lambda w: w.name)
