@@ -480,9 +480,24 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // its whole grid must fit on the device at once, and a row group must hold every chunk of
     // a row. The forward also wants room for two row groups: with one, every workgroup walks
     // every row and the two-pass form streams faster (LayerNorm 4 x 4194304 bf16: 23.9 against
-    // 20.9 us). The statistics pass keeps the forward's plan and workspace but never runs it
-    // (it writes no Y, so its second pass re-reads nothing).
-    if (t.xchg != 0 && wc == kFull && vpt == 4 && !residual) {
+    // 20.9 us). Unless forced, a row also gathers at most 512 chunk partials forward and 640
+    // backward (LayerNorm three per chunk, RMSNorm one): every workgroup of a row polls them
+    // all, and beyond that the two-pass form is faster. Measured on MI355X, bf16, forward /
+    // backward in us, single pass against two passes:
+    //   LayerNorm 32 x 524288 (64 chunks)    17.7 / 40.8  against 18.4 / 48.0
+    //   LayerNorm 16 x 1048576 (128 chunks)  18.3 / 41.5  against 18.7 / 48.2
+    //   LayerNorm 12 x 1572864 (192 chunks)  22.8 / 50.2  against 20.8 / 59.1
+    //   LayerNorm 8 x 2097152 (256 chunks)   20.6 / 43.1  against 19.6 / 32.2
+    //   LayerNorm 4 x 4194304 (512 chunks)   27.6 / 34.7  against 21.0 / 31.8
+    //   RMSNorm 16 x 1048576 / 8 x 2097152 / 4 x 4194304: 15.4 / 32.0, 16.2 / 32.6,
+    //   17.3 / 26.0 against 17.4 / 35.5, 17.6 / 30.3, 18.6 / 30.3
+    // (256 x 262144, 32 chunks: the single pass wins for both kinds). The statistics pass
+    // keeps the forward's plan and workspace but never runs it (it writes no Y, so its second
+    // pass re-reads nothing).
+    const int64_t row_partials = p.chunks * (kind == NORM_LAYERNORM ? 3 : 1);
+    const int64_t auto_max = bwd ? kXchgAutoMaxPartialsBwd : kXchgAutoMaxPartialsFwd;
+    if (t.xchg != 0 && (t.xchg > 0 || row_partials <= auto_max) && wc == kFull && vpt == 4 &&
+        !residual) {
       const int64_t cap = (int64_t)cu * (bwd ? kXchgBwdPerCu : xchg_fwd_per_cu(dtype));
       if (p.chunks <= kXchgMaxChunks && p.chunks * (bwd ? 1 : 2) <= cap) {
         int64_t G = cap / p.chunks;

@@ -71,6 +71,11 @@ constexpr int kXchgWordsPerChunk = 8;
 constexpr int64_t kXchgPollsDefault = 1 << 19;
 constexpr int64_t kXchgPollsMax = 1 << 24;
 constexpr int64_t kXchgMaxChunks = 512;
+// By default the single-pass split form runs only where a row gathers at most this many chunk
+// partials (LayerNorm publishes three per chunk, RMSNorm one), forward and backward;
+// NORM_TUNE_SPLIT_EXCHANGE = 1 lifts the limit.
+constexpr int64_t kXchgAutoMaxPartialsFwd = 512;
+constexpr int64_t kXchgAutoMaxPartialsBwd = 640;
 
 struct Tuning {
   int scheme = NORM_SCHEME_AUTO;

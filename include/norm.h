@@ -347,8 +347,11 @@ typedef enum {
                                    are merged in LDS, so fewer partial rows are written) */
   NORM_TUNE_ROW_ORDER = 7,      /* wave/block schemes: 0 = row groups interleaved across the
                                    workgroups, 1 = each workgroup takes a contiguous block */
-  NORM_TUNE_SPLIT_EXCHANGE = 8, /* split scheme: 1 = the single-pass exchange form where it
-                                   applies (the default), 0 = always the two-pass form */
+  NORM_TUNE_SPLIT_EXCHANGE = 8, /* split scheme: 1 = the single-pass exchange form wherever it
+                                   applies, 0 = always the two-pass form, -1 (default) = the
+                                   single-pass form where it applies and a row gathers at
+                                   most 512 chunk partials forward, 640 backward (LayerNorm
+                                   three per chunk, RMSNorm one) */
   NORM_TUNE_EXCHANGE_POLLS = 9, /* single-pass split form: polls of a row's exchange words
                                    before a workgroup gives up on the row and writes NaN for
                                    it and for its later rows (1 .. 2^24; default 2^19, about a

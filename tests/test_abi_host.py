@@ -379,6 +379,25 @@ def test_plan_tuning_overrides():
             nl.norm_set_tuning(k, -1)
 
 
+def test_split_exchange_partial_limit():
+    """By default the single-pass split form needs a row to gather at most 512 chunk partials
+    forward and 640 backward: LayerNorm (three per chunk) keeps it up to 170 / 213 chunks of
+    8192, RMSNorm (one) up to the form's 512."""
+    try:
+        for kind, nq in ((0, 3), (1, 1)):
+            for pass_, limit in ((0, 512), (1, 640)):
+                for C in (64, 128, 170, 171, 192, 213, 214, 256, 512):
+                    M = 4 if C > 256 else 8
+                    p = nl.norm_plan(kind, BF, pass_, M, 8192 * C, cu_count=256)
+                    assert (p["exchange_row_groups"] > 0) == (C * nq <= limit), (kind, pass_, C)
+                    nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, 1)
+                    assert nl.norm_plan(kind, BF, pass_, M, 8192 * C,
+                                        cu_count=256)["exchange_row_groups"] > 0
+                    nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, -1)
+    finally:
+        nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, -1)
+
+
 def test_split_exchange_plan():
     """The single-pass split form: 16-byte accesses, the default chunk, no residual input, at
     most 512 chunks, and a grid (row groups x chunks) the device keeps resident: 4 workgroups
@@ -395,7 +414,15 @@ def test_split_exchange_plan():
                     assert nl.norm_plan(kind, BF, pass_, M, N,
                                         cu_count=cu)["exchange_row_groups"] == 0
                     continue
+                # by default a row gathers at most 512 chunk partials forward and 640
+                # backward (LayerNorm three per chunk, RMSNorm one); the knob at 1 lifts that
+                partials = -(-N // 8192) * (3 if kind == 0 else 1)
+                if partials > (512 if pass_ == 0 else 640):
+                    assert nl.norm_plan(kind, BF, pass_, M, N,
+                                        cu_count=cu)["exchange_row_groups"] == 0
+                    nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, 1)
                 p = nl.norm_plan(kind, BF, pass_, M, N, cu_count=cu)
+                nl.norm_set_tuning(nl.TUNE_SPLIT_EXCHANGE, -1)
                 assert p["scheme"] == nl.SCHEME_SPLIT and p["chunk_elems"] == 8192
                 G = p["exchange_row_groups"]
                 assert G == min(M, cu * per_cu // p["chunks"]) >= 1
