@@ -372,6 +372,21 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       }
     }
     if (!vpt) return NORM_ERR_UNSUPPORTED;
+    // RMSNorm backward over 16-bit rows (16-bit weights) of 576-768 full-width accesses
+    // (4608-6144 elements), aligned, no residual: 256-thread teams with four accesses each,
+    // one row at a time, beat the 576-768-thread teams with one access (measured on MI355X,
+    // bf16, 32768 rows: 4608 183.8 -> 179.5 us, 5120 190.3 -> 182.5, 6144 216.3 -> 198.6;
+    // 16384 x 5120 99.6 -> 95.4), but not at 4352 (175.8 against 179.4), at fp32 2560 (178
+    // against 189), for the residual form at 7168 or for LayerNorm (5120: 175 against 221).
+    if (bwd && kind == NORM_RMSNORM && !residual && vec && wc == kFull && !p.period &&
+        (dtype == NORM_BF16 || dtype == NORM_F16) && nacc >= 576 && nacc <= 768 &&
+        t.team_threads <= 0 && t.rows <= 0 && block_menu(wc, bwd, 4, 1, 256, sc, false) &&
+        block_fits_registers(wc, bwd, 4, 1, 256)) {
+      vpt = 4;
+      tt = 256;
+      rows = 1;
+      lb_pick = 256;
+    }
     // Backward: several row teams share a workgroup (up to 1024 threads) when the larger
     // workgroup still fits its registers; their dW/dB partials merge in LDS, so the partial
     // rows written (and re-read by the column reduction) drop by the team count.
