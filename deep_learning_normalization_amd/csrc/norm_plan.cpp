@@ -363,6 +363,14 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
           return block_menu(wc, bwd, v, rr, lb, sc, res) &&
                  block_fits_registers(wc, bwd, v, rr, lb);
         };
+        // RMSNorm backward over bf16 rows on 256-thread teams with one access each (rows of
+        // 1544-2048 elements): four rows at a time, so half the workgroups and half the dW
+        // partial rows (measured on MI355X, 32768 rows: 1600 68.8 -> 66.0 us, 1792 72.0 ->
+        // 66.2, 2048 75.2 -> 71.6; 65536 x 2048 143.2 -> 137.9; but fp16 2048 75.4 against
+        // 77.2, and no gain at 1536 or 1280 (192-thread teams) or for LayerNorm, which loses)
+        const bool four = bwd && kind == NORM_RMSNORM && dtype == NORM_BF16 && !res &&
+                          wc == kFull && !part && v == 1 && cand == 256 && t.rows <= 0;
+        if (four && ok(4)) r = 4;
         if (!ok(r)) r = 1;
         if (!ok(r)) continue;
         vpt = v;

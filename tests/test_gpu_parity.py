@@ -515,6 +515,19 @@ def test_narrow_forced(knob, N):
             run_and_check(_small(kind, "bf16", 77, N, seed=N))
 
 
+@pytest.mark.parametrize("N", [1600, 2048])
+def test_rms_bf16_four_row_backward(N):
+    """The default plan of bf16 RMSNorm backward rows of 1544-2048 elements holds four rows per
+    256-thread team; every row (ragged counts, one to a few hundred groups) against the
+    oracle."""
+    p = nl.norm_plan("rmsnorm", torch.bfloat16, nl.PASS_BWD, 32768, N)
+    assert (p["threads"], p["accesses_per_thread"], p["rows_per_iter"]) == (256, 1, 4)
+    for M in (1, 5, 1003):
+        _say("rms bf16 four-row backward %dx%d" % (M, N))
+        run_and_check(_small("rmsnorm", "bf16", M, N, seed=M + N))
+        run_and_check(_small("rmsnorm", "bf16", M, N, seed=M + N + 1), stats=False)
+
+
 # ---- tuning knobs ----------------------------------------------------------------------------
 
 KNOBS = [
