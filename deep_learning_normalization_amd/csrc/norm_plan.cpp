@@ -414,6 +414,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.threads = tt * teams;
     p.lb = vec ? (teams > 1 ? lb_of(p.threads) : lb_pick) : 1024;
     const int64_t groups = cdiv(Mc, (int64_t)rows * teams);
+    const bool wide_fwd = !bwd && !stats && !residual && vec && wc == kFull && !p.period &&
+                          (dtype == NORM_BF16 || dtype == NORM_F16) && vpt == 4 && tt > 256 &&
+                          (kind == NORM_LAYERNORM || tt <= 384);
     auto capped = [&](int64_t gpc) { // persistent: gpc workgroups per CU over all classes
       const int64_t cap = cu * gpc / PC > 0 ? cu * gpc / PC : 1;
       return PC * (groups < cap ? groups : cap);
@@ -423,7 +426,7 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // workgroup writes one partial row, so fewer, longer-lived workgroups.
       const int64_t load = (int64_t)p.threads * vpt * rows; // full-width units
       p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1));
-    } else if (t.grid_per_cu > 0 || stats || sc > 1 || p.period) {
+    } else if (t.grid_per_cu > 0 || stats || sc > 1 || p.period || wide_fwd) {
       // the statistics pass alone, with no stores to overlap, streams best from a persistent
       // grid of 8 workgroups per CU (measured on MI355X: LayerNorm 16384 x 4096 30.6 -> 28.7 us);
       // 8- and 4-byte forwards from 16 (LayerNorm 16384 x 4100 54.4 -> 49.8 us, 16384 x 4098
@@ -433,9 +436,20 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // workgroups per CU, 35 / 44 / 62 us, against 50 / 54 / 108 us from short-lived ones)
       // (4 accesses per thread take about 180 VGPRs, so 2 wavefronts per SIMD: 8 per CU;
       // RMSNorm 16384 x 8185 99 us from 2 workgroups of 4 wavefronts, 108 us from 3)
+      // Forwards of 16-bit rows on teams of 320-512 threads with four accesses each (rows of
+      // 8200-16384 elements) run from a persistent grid of 2 workgroups per CU (measured on
+      // MI355X, 16384 rows, short-lived against persistent: LayerNorm 10240 173.7 -> 130.9 us,
+      // 12288 181.4 -> 140.6, 14336 191.1 -> 170.2, 16384 211 -> 181; RMSNorm 10240 144.3 ->
+      // 112.0, 12288 150.0 -> 136.7, but 14336 161.2 against 167.1 and 16384 a tie, so RMSNorm
+      // keeps short-lived workgroups on teams of more than 384 threads; 8192, on 256 threads,
+      // ties either way)
       const int64_t waves = (p.threads + 63) / 64, budget = vpt >= 4 ? 8 : 12;
       const int64_t gpc_part = budget / waves > 0 ? budget / waves : 1;
-      p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : stats ? 8 : p.period ? gpc_part : 16);
+      p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu
+                      : stats                ? 8
+                      : p.period             ? gpc_part
+                      : wide_fwd             ? 2
+                                             : 16);
     } else {
       // Forward (measured on MI355X): short-lived workgroups of two row groups each (the second
       // group's loads overlap the first's reductions), one for the residual variant, whose

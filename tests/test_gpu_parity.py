@@ -528,6 +528,21 @@ def test_rms_bf16_four_row_backward(N):
         run_and_check(_small("rmsnorm", "bf16", M, N, seed=M + N + 1), stats=False)
 
 
+@pytest.mark.parametrize("kind,N", [("layernorm", 10240), ("layernorm", 16384),
+                                    ("rmsnorm", 12288), ("layernorm", 8200)])
+@pytest.mark.parametrize("dt", ["bf16", "f16"])
+def test_wide_forward_persistent_grid(kind, N, dt):
+    """The default forward plan of 16-bit rows on teams of more than 256 threads with four
+    accesses each runs a persistent grid of two workgroups per CU: row counts below, at and
+    past one row per workgroup, every row against the oracle."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_FWD, 16384, N, cu_count=cu)
+    assert p["threads"] > 256 and p["accesses_per_thread"] == 4 and p["grid"] == 2 * cu
+    for M in (1, 7, 2 * cu, 2 * cu + 1, 1500):
+        _say("wide forward %s %s %dx%d" % (kind, dt, M, N))
+        run_and_check(_small(kind, dt, M, N, seed=M + N))
+
+
 # ---- tuning knobs ----------------------------------------------------------------------------
 
 KNOBS = [
