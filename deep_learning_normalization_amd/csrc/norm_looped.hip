@@ -212,17 +212,28 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
 
 namespace {
 
-// Segments per row: 4 full-width (16-byte) accesses per thread, or 8 of 8 bytes. Workgroups of
-// up to 512 threads; at 150-240 VGPRs one workgroup per CU is resident.
+// Segments per row: 4 full-width (16-byte) accesses per thread, or 8 of 8 bytes; LayerNorm on
+// 16-bit rows also has a kernel of 3 full-width segments. Workgroups of up to 512 threads. Two
+// workgroups per CU are resident where a kernel takes at most 128 VGPRs (the compiler's report
+// for gfx950: 16-byte kernels of fp32 rows 72-93, of RMSNorm on 16-bit rows 124, of LayerNorm
+// on 16-bit rows 158 with four segments and 127 with three).
 constexpr int kLoopedLB = 512;
 
 template <typename T, typename TW, int EV>
 norm_status_t looped_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   constexpr int SEG = 4 * (full_epv<T>() / EV);
-  if (p.vpt != SEG || p.lb != kLoopedLB) return NORM_ERR_UNSUPPORTED;
+  constexpr bool kHas3 = EV == full_epv<T>() && sizeof(T) == 2;
+  const bool seg3 = kHas3 && a.layernorm && p.vpt == 3;
+  if ((p.vpt != SEG && !seg3) || p.lb != kLoopedLB) return NORM_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
-  const hipError_t e =
-      a.layernorm ? launch(looped_bwd_kernel<T, TW, EV, SEG, kLoopedLB, true>, grid, block, s, a)
+  hipError_t e;
+  if constexpr (kHas3) {
+    if (seg3) {
+      e = launch(looped_bwd_kernel<T, TW, EV, 3, kLoopedLB, true>, grid, block, s, a);
+      return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+    }
+  }
+  e = a.layernorm ? launch(looped_bwd_kernel<T, TW, EV, SEG, kLoopedLB, true>, grid, block, s, a)
                   : launch(looped_bwd_kernel<T, TW, EV, SEG, kLoopedLB, false>, grid, block, s, a);
   return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
 }

@@ -27,6 +27,10 @@ constexpr int kBlockTeamTarget = 256;    // preferred largest team for the block
 constexpr int kBlockTeamTargetBwd = 640; // the backward prefers one access per thread longer
 constexpr int kLoopThreads = 512;        // looped backward: workgroup (= team) size bound
 constexpr int kLoopSegFull = 4;          // looped backward: full-width accesses per thread
+constexpr int64_t kLoopTwoMaxAcc = 1792; // looped backward: longest row (16-byte accesses) run
+                                         // two workgroups per CU
+constexpr int kLoopSeg3 = 3;             // looped backward: segments of the short 16-bit
+                                         // LayerNorm kernel
 constexpr int kLoopMaxEq = kLoopThreads * kLoopSegFull; // longest row, full-width accesses
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -414,9 +418,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.threads = tt * teams;
     p.lb = vec ? (teams > 1 ? lb_of(p.threads) : lb_pick) : 1024;
     const int64_t groups = cdiv(Mc, (int64_t)rows * teams);
-    const bool wide_fwd = !bwd && !stats && !residual && vec && wc == kFull && !p.period &&
+    const bool wide_fwd = !bwd && !stats && vec && wc == kFull && !p.period &&
                           (dtype == NORM_BF16 || dtype == NORM_F16) && vpt == 4 && tt > 256 &&
-                          (kind == NORM_LAYERNORM || tt <= 384);
+                          ((kind == NORM_LAYERNORM && !residual) || tt <= 384);
     auto capped = [&](int64_t gpc) { // persistent: gpc workgroups per CU over all classes
       const int64_t cap = cu * gpc / PC > 0 ? cu * gpc / PC : 1;
       return PC * (groups < cap ? groups : cap);
@@ -442,7 +446,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // 12288 181.4 -> 140.6, 14336 191.1 -> 170.2, 16384 211 -> 181; RMSNorm 10240 144.3 ->
       // 112.0, 12288 150.0 -> 136.7, but 14336 161.2 against 167.1 and 16384 a tie, so RMSNorm
       // keeps short-lived workgroups on teams of more than 384 threads; 8192, on 256 threads,
-      // ties either way)
+      // ties either way). The residual form gains on 320-384 threads (16384 x 10240 289.7 ->
+      // 238.9 us, x 12288 333.5 -> 275.8) and ties on 512. fp32 rows lose 1-7% beside it (6144
+      // 132.5 -> 140.4) and keep short-lived workgroups.
       const int64_t waves = (p.threads + 63) / 64, budget = vpt >= 4 ? 8 : 12;
       const int64_t gpc_part = budget / waves > 0 ? budget / waves : 1;
       p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu
@@ -459,14 +465,18 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.row_order = t.row_order > 0 ? 1 : 0;
   } else if (scheme == NORM_SCHEME_LOOP) {
     // one row per workgroup, kLoopSegFull full-width accesses per thread (twice as many 8-byte
-    // ones; 4-byte accesses are not compiled for it); one resident workgroup per CU, each
-    // writing one partial row
+    // ones; 4-byte accesses are not compiled for it); one or two resident workgroups per CU,
+    // each writing one partial row
     if (!vec || sc > 2 || nacc_eq > kLoopMaxEq) return NORM_ERR_UNSUPPORTED;
     // Teams of the full 512 threads even where fewer would cover the row (the last segments
     // are then partly empty): with one resident workgroup per CU the team size is the CU's
     // whole parallelism (measured on MI355X: RMSNorm 16384 x 12288 297 -> 253 us, fp32
     // 32768 x 4098 705 -> 519 us). A smaller override is taken where it still covers the row.
-    const int seg = kLoopSegFull * sc;
+    // LayerNorm on 16-bit rows of at most 1536 accesses runs a kernel of three segments (127
+    // VGPRs against the four-segment kernel's 158), which leaves room for a second workgroup.
+    const bool seg3 = kind == NORM_LAYERNORM && dtype != NORM_F32 && sc == 1 && !p.period &&
+                      nacc <= kLoopSeg3 * kLoopThreads;
+    const int seg = seg3 ? kLoopSeg3 : kLoopSegFull * sc;
     const int need = (int)(cdiv(cdiv(nacc, seg), 64) * 64);
     int tt = kLoopThreads;
     if (t.team_threads > 0 && t.team_threads <= kLoopThreads && t.team_threads >= need)
@@ -476,7 +486,17 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.team_threads = tt;
     p.threads = tt;
     p.lb = kLoopThreads;
-    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : 1;
+    // Two workgroups per CU where the kernel's registers leave room for two 512-thread teams
+    // (at most 128 VGPRs: the 16-byte kernels of RMSNorm on 16-bit rows, 124, and of either
+    // kind on fp32 rows, 72-93; LayerNorm on 16-bit rows takes 158) and rows of at most 28 KB,
+    // so that two rows of X and dY per CU still stay in the L2 between the sweeps. Measured on
+    // MI355X, 16384 rows, one against two per CU: RMSNorm bf16 8200 210.2 -> 174.8 us, 10240
+    // 237.8 -> 198.0, 12288 258.9 -> 229.9, 14336 313.4 -> 277.5 (fp16, fp32 weights and the
+    // residual form alike); fp32 LayerNorm 4100 211.4 -> 175.0, 7168 313.3 -> 282.9; full 32 KB
+    // rows tie (bf16 16384) or lose (fp32 8192 309.8 -> 321.6).
+    const bool two = sc == 1 && !p.period && (dtype == NORM_F32 || kind == NORM_RMSNORM || seg3) &&
+                     nacc <= kLoopTwoMaxAcc;
+    const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : two ? 2 : 1;
     p.grid = Mm < cu * gpc ? Mm : cu * gpc;
     p.row_order = 0;
   } else if (scheme == NORM_SCHEME_SPLIT) {

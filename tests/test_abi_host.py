@@ -266,6 +266,45 @@ def test_scheme_boundaries():
         nl.norm_set_tuning(nl.TUNE_SCHEME, -1)
 
 
+def test_wide_row_grids():
+    """Grids of the wide-row plans, with 256 CUs."""
+    F16 = torch.float16
+    g = lambda *a, **k: nl.norm_plan(*a, cu_count=256, **k)
+    # forwards of 16-bit rows on 320-512-thread teams with four accesses: two persistent
+    # workgroups per CU (RMSNorm and the residual form up to 384 threads), short-lived otherwise
+    for kind, dt, N, res in [(0, BF, 8200, False), (0, BF, 16384, False), (0, F16, 10240, False),
+                             (1, BF, 12288, False), (1, BF, 10240, True), (0, F16, 12288, True)]:
+        p = g(kind, dt, 0, 16384, N, residual=res)
+        assert p["threads"] > 256 and p["accesses_per_thread"] == 4 and p["grid"] == 512, (kind, N)
+    # (short-lived: two row groups a workgroup, one in the residual form)
+    for kind, dt, N, res in [(1, BF, 14336, False), (1, BF, 16384, False), (0, BF, 16384, True),
+                             (1, BF, 7168, True), (0, F, 6144, False), (0, BF, 8192, False)]:
+        assert g(kind, dt, 0, 16384, N, residual=res)["grid"] == (16384 if res else 8192), (kind, N)
+    # looped backward: two workgroups per CU for rows of at most 1792 16-byte accesses whose
+    # kernel fits two 512-thread teams (RMSNorm on 16-bit rows, fp32 rows, and 16-bit LayerNorm
+    # rows of at most 1536 accesses through its three-segment kernel), one otherwise
+    for kind, dt, N, seg in [(1, BF, 8200, 4), (1, BF, 14336, 4), (0, F, 4100, 4), (1, F, 7168, 4),
+                             (0, BF, 8200, 3), (0, BF, 12288, 3), (0, F16, 10240, 3),
+                             (0, BF32W, 10240, 3)]:
+        p = g(kind, dt, 1, 16384, N)
+        assert (p["scheme"], p["accesses_per_thread"], p["grid"]) == (nl.SCHEME_LOOP, seg, 512), \
+            (kind, N)
+    for kind, dt, N, seg in [(1, BF, 16384, 4), (0, BF, 12296, 4), (0, BF, 16384, 4),
+                             (0, F, 8192, 4), (1, BF, 16380, 8)]:
+        p = g(kind, dt, 1, 16384, N)
+        assert (p["scheme"], p["accesses_per_thread"], p["grid"]) == (nl.SCHEME_LOOP, seg, 256), \
+            (kind, N)
+    # fewer rows than workgroups: one workgroup a row
+    assert g(0, BF, 1, 300, 10240)["grid"] == 300
+    # a grid override applies to the looped backward as given
+    try:
+        nl.norm_set_tuning(nl.TUNE_GRID_PER_CU, 1)
+        assert g(1, BF, 1, 16384, 10240)["grid"] == 256
+        assert g(0, BF, 1, 16384, 10240)["accesses_per_thread"] == 3
+    finally:
+        nl.norm_set_tuning(nl.TUNE_GRID_PER_CU, -1)
+
+
 def test_access_width_follows_row_length_and_alignment():
     def width(dt, N, align=16, pass_=0):
         p = nl.norm_plan(0, dt, pass_, 64, N, align=align)

@@ -528,19 +528,60 @@ def test_rms_bf16_four_row_backward(N):
         run_and_check(_small("rmsnorm", "bf16", M, N, seed=M + N + 1), stats=False)
 
 
-@pytest.mark.parametrize("kind,N", [("layernorm", 10240), ("layernorm", 16384),
-                                    ("rmsnorm", 12288), ("layernorm", 8200)])
+@pytest.mark.parametrize("kind,N,res", [("layernorm", 10240, False), ("layernorm", 16384, False),
+                                        ("rmsnorm", 12288, False), ("layernorm", 8200, False),
+                                        ("rmsnorm", 10240, True), ("layernorm", 12288, True)])
 @pytest.mark.parametrize("dt", ["bf16", "f16"])
-def test_wide_forward_persistent_grid(kind, N, dt):
+def test_wide_forward_persistent_grid(kind, N, res, dt):
     """The default forward plan of 16-bit rows on teams of more than 256 threads with four
-    accesses each runs a persistent grid of two workgroups per CU: row counts below, at and
-    past one row per workgroup, every row against the oracle."""
+    accesses each (320-384 threads for RMSNorm and the residual form) runs a persistent grid
+    of two workgroups per CU: row counts below, at and past one row per workgroup, every row
+    against the oracle."""
     cu = torch.cuda.get_device_properties(0).multi_processor_count
-    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_FWD, 16384, N, cu_count=cu)
+    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_FWD, 16384, N, residual=res,
+                     cu_count=cu)
     assert p["threads"] > 256 and p["accesses_per_thread"] == 4 and p["grid"] == 2 * cu
+    extra = dict(x=inputs.normal(0, 0.5), r=inputs.normal(0, 1)) if res else {}
     for M in (1, 7, 2 * cu, 2 * cu + 1, 1500):
-        _say("wide forward %s %s %dx%d" % (kind, dt, M, N))
-        run_and_check(_small(kind, dt, M, N, seed=M + N))
+        _say("wide forward %s %s residual=%s %dx%d" % (kind, dt, res, M, N))
+        w = _small(kind, dt, M, N, seed=M + N, **extra)
+        if res:
+            run_and_check(w, dr="alias", dh=True)
+        else:
+            run_and_check(w)
+
+
+@pytest.mark.parametrize("kind,dt,N,res,wdt,seg", [("rmsnorm", "bf16", 8200, False, None, 4),
+                                                   ("rmsnorm", "bf16", 14336, False, None, 4),
+                                                   ("rmsnorm", "f16", 10240, True, None, 4),
+                                                   ("layernorm", "f32", 4100, False, None, 4),
+                                                   ("layernorm", "f32", 7168, True, None, 4),
+                                                   ("rmsnorm", "f32", 6144, False, None, 4),
+                                                   ("layernorm", "bf16", 8200, False, None, 3),
+                                                   ("layernorm", "bf16", 12288, True, None, 3),
+                                                   ("layernorm", "f16", 10240, False, None, 3),
+                                                   ("layernorm", "bf16", 11264, False, "f32", 3)])
+def test_looped_backward_two_per_cu(kind, dt, N, res, wdt, seg):
+    """The default looped backward runs two workgroups per CU where its registers allow two
+    512-thread teams and rows are at most 28 KB (LayerNorm on 16-bit rows of at most 1536
+    accesses through its three-segment kernel): row counts below, at and past one row per
+    workgroup, with and without saved statistics, every row and every dW/dB column against the
+    oracle."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_BWD, 16384, N, residual=res,
+                     cu_count=cu)
+    assert p["scheme"] == nl.SCHEME_LOOP and p["grid"] == 2 * cu
+    assert (p["threads"], p["accesses_per_thread"]) == (512, seg)
+    extra = dict(x=inputs.normal(0, 0.5), r=inputs.normal(0, 1)) if res else {}
+    for M in (1, 7, 2 * cu, 2 * cu + 1, 1100):
+        _say("looped two per CU %s %s/%s residual=%s %dx%d" % (kind, dt, wdt, res, M, N))
+        w = dataclasses.replace(_small(kind, dt, M, N, seed=M + N, **extra), wdtype=wdt)
+        if res:
+            run_and_check(w, dr="alias", dh=True)
+            run_and_check(dataclasses.replace(w, seed=M + N + 1), dr="separate", stats=False)
+        else:
+            run_and_check(w)
+            run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
 
 
 # ---- tuning knobs ----------------------------------------------------------------------------
