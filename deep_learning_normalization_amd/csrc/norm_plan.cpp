@@ -418,9 +418,10 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     p.threads = tt * teams;
     p.lb = vec ? (teams > 1 ? lb_of(p.threads) : lb_pick) : 1024;
     const int64_t groups = cdiv(Mc, (int64_t)rows * teams);
-    const bool wide_fwd = !bwd && !stats && vec && wc == kFull && !p.period &&
-                          (dtype == NORM_BF16 || dtype == NORM_F16) && vpt == 4 && tt > 256 &&
-                          ((kind == NORM_LAYERNORM && !residual) || tt <= 384);
+    const bool wide_fwd =
+        !bwd && !stats && vec && wc == kFull && !p.period && vpt == 4 && tt > 256 &&
+        (dtype != NORM_F32 ? (kind == NORM_LAYERNORM && !residual) || tt <= 384
+                           : kind == NORM_LAYERNORM && !residual && tt <= 320);
     auto capped = [&](int64_t gpc) { // persistent: gpc workgroups per CU over all classes
       const int64_t cap = cu * gpc / PC > 0 ? cu * gpc / PC : 1;
       return PC * (groups < cap ? groups : cap);
@@ -447,7 +448,10 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // 112.0, 12288 150.0 -> 136.7, but 14336 161.2 against 167.1 and 16384 a tie, so RMSNorm
       // keeps short-lived workgroups on teams of more than 384 threads; 8192, on 256 threads,
       // ties either way). The residual form gains on 320-384 threads (16384 x 10240 289.7 ->
-      // 238.9 us, x 12288 333.5 -> 275.8) and ties on 512. fp32 rows lose 1-7% beside it (6144
+      // 238.9 us, x 12288 333.5 -> 275.8) and ties on 512. fp32 weights beside 16-bit rows
+      // gain alike (LayerNorm 8200 169.7 -> 114.1, 16384 208.1 -> 181.0; RMSNorm 10240 140.5
+      // -> 112.2). fp32 rows gain only for LayerNorm on 320 threads (4100 104.5 -> 95.1, 4608
+      // 109.0 -> 101.6, 5120 a tie); on more threads, and for RMSNorm, they lose 1-7% (6144
       // 132.5 -> 140.4) and keep short-lived workgroups.
       const int64_t waves = (p.threads + 63) / 64, budget = vpt >= 4 ? 8 : 12;
       const int64_t gpc_part = budget / waves > 0 ? budget / waves : 1;

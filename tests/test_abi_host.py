@@ -273,12 +273,15 @@ def test_wide_row_grids():
     # forwards of 16-bit rows on 320-512-thread teams with four accesses: two persistent
     # workgroups per CU (RMSNorm and the residual form up to 384 threads), short-lived otherwise
     for kind, dt, N, res in [(0, BF, 8200, False), (0, BF, 16384, False), (0, F16, 10240, False),
-                             (1, BF, 12288, False), (1, BF, 10240, True), (0, F16, 12288, True)]:
+                             (1, BF, 12288, False), (1, BF, 10240, True), (0, F16, 12288, True),
+                             (0, BF32W, 16384, False), (1, BF32W, 10240, False),
+                             (0, F, 4100, False), (0, F, 5120, False)]:
         p = g(kind, dt, 0, 16384, N, residual=res)
         assert p["threads"] > 256 and p["accesses_per_thread"] == 4 and p["grid"] == 512, (kind, N)
     # (short-lived: two row groups a workgroup, one in the residual form)
     for kind, dt, N, res in [(1, BF, 14336, False), (1, BF, 16384, False), (0, BF, 16384, True),
-                             (1, BF, 7168, True), (0, F, 6144, False), (0, BF, 8192, False)]:
+                             (1, BF, 7168, True), (0, F, 6144, False), (0, BF, 8192, False),
+                             (1, F, 4100, False), (0, F, 4100, True), (1, BF32W, 16384, False)]:
         assert g(kind, dt, 0, 16384, N, residual=res)["grid"] == (16384 if res else 8192), (kind, N)
     # looped backward: two workgroups per CU for rows of at most 1792 16-byte accesses whose
     # kernel fits two 512-thread teams (RMSNorm on 16-bit rows, fp32 rows, and 16-bit LayerNorm

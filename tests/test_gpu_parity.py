@@ -528,23 +528,30 @@ def test_rms_bf16_four_row_backward(N):
         run_and_check(_small("rmsnorm", "bf16", M, N, seed=M + N + 1), stats=False)
 
 
-@pytest.mark.parametrize("kind,N,res", [("layernorm", 10240, False), ("layernorm", 16384, False),
-                                        ("rmsnorm", 12288, False), ("layernorm", 8200, False),
-                                        ("rmsnorm", 10240, True), ("layernorm", 12288, True)])
-@pytest.mark.parametrize("dt", ["bf16", "f16"])
+_WIDE_FWD = [(kind, N, res, dt) for dt in ("bf16", "f16", "bf16_f32w")
+             for kind, N, res in [("layernorm", 10240, False), ("layernorm", 16384, False),
+                                  ("rmsnorm", 12288, False), ("layernorm", 8200, False),
+                                  ("rmsnorm", 10240, True), ("layernorm", 12288, True)]]
+_WIDE_FWD += [("layernorm", N, False, "f32") for N in (4100, 4608, 5120)]
+
+
+@pytest.mark.parametrize("kind,N,res,dt", _WIDE_FWD, ids=lambda v: str(v))
 def test_wide_forward_persistent_grid(kind, N, res, dt):
-    """The default forward plan of 16-bit rows on teams of more than 256 threads with four
-    accesses each (320-384 threads for RMSNorm and the residual form) runs a persistent grid
-    of two workgroups per CU: row counts below, at and past one row per workgroup, every row
-    against the oracle."""
+    """The default forward plan of 16-bit rows (either weight type) on teams of more than 256
+    threads with four accesses each (320-384 threads for RMSNorm and the residual form), and of
+    fp32 LayerNorm rows on 320 threads, runs a persistent grid of two workgroups per CU: row
+    counts below, at and past one row per workgroup, every row against the oracle."""
+    wdt = None
+    if dt == "bf16_f32w":
+        dt, wdt = "bf16", "f32"
     cu = torch.cuda.get_device_properties(0).multi_processor_count
-    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_FWD, 16384, N, residual=res,
-                     cu_count=cu)
+    pdt = nl.BF16_F32W if wdt else inputs.TORCH_DTYPES[dt]
+    p = nl.norm_plan(kind, pdt, nl.PASS_FWD, 16384, N, residual=res, cu_count=cu)
     assert p["threads"] > 256 and p["accesses_per_thread"] == 4 and p["grid"] == 2 * cu
     extra = dict(x=inputs.normal(0, 0.5), r=inputs.normal(0, 1)) if res else {}
     for M in (1, 7, 2 * cu, 2 * cu + 1, 1500):
-        _say("wide forward %s %s residual=%s %dx%d" % (kind, dt, res, M, N))
-        w = _small(kind, dt, M, N, seed=M + N, **extra)
+        _say("wide forward %s %s/%s residual=%s %dx%d" % (kind, dt, wdt, res, M, N))
+        w = dataclasses.replace(_small(kind, dt, M, N, seed=M + N, **extra), wdtype=wdt)
         if res:
             run_and_check(w, dr="alias", dh=True)
         else:
