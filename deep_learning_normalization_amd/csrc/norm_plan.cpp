@@ -372,8 +372,15 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
         // partial rows (measured on MI355X, 32768 rows: 1600 68.8 -> 66.0 us, 1792 72.0 ->
         // 66.2, 2048 75.2 -> 71.6; 65536 x 2048 143.2 -> 137.9; but fp16 2048 75.4 against
         // 77.2, and no gain at 1536 or 1280 (192-thread teams) or for LayerNorm, which loses)
-        const bool four = bwd && kind == NORM_RMSNORM && dtype == NORM_BF16 && !res &&
-                          wc == kFull && !part && v == 1 && cand == 256 && t.rows <= 0;
+        // Rows over phase classes on 320-384-thread teams with one access each hold four rows
+        // too (measured on MI355X: LayerNorm bf16 16384 x 2049 83.9 -> 77.0 us, fp16 87.9 ->
+        // 79.0, fp32 16384 x 1025 73.7 -> 65.3; RMSNorm 32768 x 2049 122.1 -> 111.9; 2561 a
+        // 1-4% gain; teams of 256 threads or fewer lose 1-8% and 448-512 threads tie)
+        const bool four = bwd && !res && v == 1 && t.rows <= 0 &&
+                          ((kind == NORM_RMSNORM && dtype == NORM_BF16 && wc == kFull && !part &&
+                            cand == 256) ||
+                           (part && cand >= 320 && cand <= 384 && dtype != NORM_BF16_F32W &&
+                            dtype != NORM_F16_F32W));
         if (four && ok(4)) r = 4;
         if (!ok(r)) r = 1;
         if (!ok(r)) continue;

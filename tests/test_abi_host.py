@@ -297,6 +297,13 @@ def test_wide_row_grids():
         p = g(kind, dt, 1, 16384, N)
         assert (p["scheme"], p["accesses_per_thread"], p["grid"]) == (nl.SCHEME_LOOP, seg, 256), \
             (kind, N)
+    # backward over phase classes: four rows at a time on 320-384-thread teams with one access
+    for kind, dt, N, rows in [(0, BF, 2049, 4), (1, BF, 2049, 4), (0, F, 1025, 4), (0, BF, 2561, 4),
+                              (0, BF, 1537, 2), (0, BF, 3073, 2), (0, BF, 4097, 2),
+                              (0, BF32W, 2049, 2)]:
+        p = g(kind, dt, 1, 16384, N)
+        assert p["phase_classes"] > 1 and p["rows_per_iter"] == rows, (kind, N)
+    assert g(0, BF, 1, 16384, 2049, residual=True)["rows_per_iter"] == 2
     # fewer rows than workgroups: one workgroup a row
     assert g(0, BF, 1, 300, 10240)["grid"] == 300
     # a grid override applies to the looped backward as given

@@ -591,6 +591,23 @@ def test_looped_backward_two_per_cu(kind, dt, N, res, wdt, seg):
             run_and_check(dataclasses.replace(w, seed=M + N + 1), stats=False)
 
 
+@pytest.mark.parametrize("kind,dt,N", [("layernorm", "bf16", 2049), ("rmsnorm", "bf16", 2049),
+                                       ("layernorm", "f16", 2561), ("layernorm", "f32", 1025),
+                                       ("rmsnorm", "f32", 1283)])
+def test_phase_class_four_row_backward(kind, dt, N):
+    """The default backward over phase classes on 320-384-thread teams with one access each
+    holds four rows: row counts below, at and past one row group per workgroup, every row and
+    every dW/dB column against the oracle, rows at every phase (odd N)."""
+    cu = torch.cuda.get_device_properties(0).multi_processor_count
+    p = nl.norm_plan(kind, inputs.TORCH_DTYPES[dt], nl.PASS_BWD, 16384, N, cu_count=cu)
+    assert p["phase_classes"] > 1 and p["accesses_per_thread"] == 1 and p["rows_per_iter"] == 4
+    assert 320 <= p["threads"] <= 384
+    for M in (1, 5, 4 * cu + 3, 3001):
+        _say("phase-class four-row backward %s %s %dx%d" % (kind, dt, M, N))
+        run_and_check(_small(kind, dt, M, N, seed=M + N))
+        run_and_check(_small(kind, dt, M, N, seed=M + N + 1), stats=False)
+
+
 # ---- tuning knobs ----------------------------------------------------------------------------
 
 KNOBS = [
