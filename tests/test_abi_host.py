@@ -511,7 +511,8 @@ def test_split_exchange_plan():
 @pytest.mark.parametrize("pass_", [0, 1, 2])
 @pytest.mark.parametrize("M,N", [(1, 1), (3, 1000), (2048, 1024), (16384, 4096), (16384, 4100),
                                  (32768, 8192), (65536, 7168), (16384, 16384), (256, 262144),
-                                 (4, 4194304), (2, 8192 * 513), (1000, 65536)])
+                                 (4, 4194304), (2, 8192 * 513), (1000, 65536), (16384, 10240),
+                                 (16384, 12288), (16384, 2049), (16384, 4100 * 2 + 1)])
 def test_workspace_bytes_on_the_host(kind, pass_, M, N):
     """norm_workspace_bytes needs no device and covers the plan of every compute-unit count
     (1 .. 256) and every pointer alignment."""
