@@ -304,6 +304,15 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       }
     if (!vpt) return NORM_ERR_UNSUPPORTED;
     int rows = t.rows > 0 ? t.rows : 1;
+    // Backwards of 16-bit rows of at most one 16-byte access per lane (N <= 512) hold several
+    // rows per wavefront: four for RMSNorm, two for LayerNorm (measured on MI355X, bf16, one
+    // row against four / two: RMSNorm 65536 x 256 43.4 -> 28.9 us, 65536 x 512 50.0 -> 40.2,
+    // 262144 x 512 177.8 -> 139.2, fp16 65536 x 512 49.3 -> 40.6; LayerNorm 65536 x 256 37.1 ->
+    // 35.7, 65536 x 512 44.2 -> 42.0, 262144 x 512 147.9 -> 140.4). Two accesses per lane
+    // (768, 1024) gain nothing from more rows and lose 10-40% with four.
+    if (t.rows <= 0 && bwd && vpt == 1 && sc == 1 && !p.period && !residual &&
+        (dtype == NORM_BF16 || dtype == NORM_F16))
+      rows = kind == NORM_RMSNORM ? 4 : 2;
     if (!wave_menu(wc, vpt, rows)) rows = 1;
     p.vpt = vpt * sc;
     p.rows = rows;
@@ -406,6 +415,20 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       rows = 1;
       lb_pick = 256;
     }
+    // LayerNorm backward over 16-bit rows of 257-384 accesses (2056-3072 elements): 256-thread
+    // teams with two accesses each and one row, two workgroups per CU, instead of 320-384
+    // threads with one access and two rows on one (measured on MI355X, bf16, 65536 rows: 2304
+    // 224.0 -> 187.6 us, 2560 228.7 -> 186.5, 2816 225.4 -> 193.6, 3072 230.6 -> 204.6; fp16
+    // 2560 234.7 -> 208.1; 16384 rows 4-7%)
+    if (bwd && kind == NORM_LAYERNORM && !residual && vec && wc == kFull && !p.period &&
+        (dtype == NORM_BF16 || dtype == NORM_F16) && nacc > 256 && nacc <= 384 &&
+        t.team_threads <= 0 && t.rows <= 0 && block_menu(wc, bwd, 2, 1, 256, sc, false) &&
+        block_fits_registers(wc, bwd, 2, 1, 256)) {
+      vpt = 2;
+      tt = 256;
+      rows = 1;
+      lb_pick = 256;
+    }
     // Backward: several row teams share a workgroup (up to 1024 threads) when the larger
     // workgroup still fits its registers; their dW/dB partials merge in LDS, so the partial
     // rows written (and re-read by the column reduction) drop by the team count.
@@ -437,7 +460,20 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // Backward: persistent, about 1024 16-byte accesses per tensor in flight per CU; every
       // workgroup writes one partial row, so fewer, longer-lived workgroups.
       const int64_t load = (int64_t)p.threads * vpt * rows; // full-width units
-      p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : (1024 / load > 0 ? 1024 / load : 1));
+      int64_t gpc = 1024 / load > 0 ? 1024 / load : 1;
+      // Two-row teams of 16-bit rows with one access per thread round up instead: teams of 192
+      // threads (rows of 1032-1536 elements) run three workgroups per CU, RMSNorm teams of
+      // 320-384 threads (2056-3072) two (measured on MI355X, bf16, 65536 rows: 1280 RMSNorm
+      // 119.8 -> 98.8 us, LayerNorm 126.6 -> 106.8; 1536 RMSNorm 127.1 -> 108.4, LayerNorm
+      // 131.3 -> 117.8, fp16 RMSNorm 126.5 -> 109.1; RMSNorm 2560 219.6 -> 168.1, 3072 230.5 ->
+      // 203.5; at 16384 rows 5-20% alike). RMSNorm on 448 threads (3584) loses 0-8% with two,
+      // and LayerNorm on 320-384 threads loses 4-5% (it takes 256-thread teams instead).
+      const bool up = bwd && vpt == 1 && rows == 2 && sc == 1 && !p.period && !residual &&
+                      (dtype == NORM_BF16 || dtype == NORM_F16) && p.threads == p.team_threads &&
+                      (p.threads == 192 ||
+                       (kind == NORM_RMSNORM && p.threads >= 320 && p.threads <= 384));
+      if (up) gpc = cdiv(1024, load);
+      p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : gpc);
     } else if (t.grid_per_cu > 0 || stats || sc > 1 || p.period || wide_fwd) {
       // the statistics pass alone, with no stores to overlap, streams best from a persistent
       // grid of 8 workgroups per CU (measured on MI355X: LayerNorm 16384 x 4096 30.6 -> 28.7 us);

@@ -315,6 +315,45 @@ def test_wide_row_grids():
         nl.norm_set_tuning(nl.TUNE_GRID_PER_CU, -1)
 
 
+def test_backward_team_rules():
+    """Backward plans of 16-bit rows up to 3584 elements, with 256 CUs: (threads, accesses per
+    thread, rows at a time, grid)."""
+    F16 = torch.float16
+    cases = [
+        ((1, BF, 65536, 256), (256, 1, 4, 512)),    # wave, one access: RMSNorm four rows
+        ((1, F16, 65536, 512), (256, 1, 4, 512)),
+        ((0, BF, 65536, 512), (256, 1, 2, 512)),    # LayerNorm two
+        ((1, BF, 65536, 768), (256, 2, 1, 512)),    # two accesses: one row
+        ((0, F, 65536, 512), (256, 2, 1, 512)),     # fp32 unchanged
+        ((1, BF, 65536, 1280), (192, 1, 2, 768)),   # 192-thread two-row teams: three per CU
+        ((0, BF, 65536, 1536), (192, 1, 2, 768)),
+        ((1, BF, 65536, 2560), (320, 1, 2, 512)),   # RMSNorm 320-384 threads: two per CU
+        ((1, F16, 65536, 3072), (384, 1, 2, 512)),
+        ((1, BF, 65536, 3584), (448, 1, 2, 256)),   # 448 threads: one
+        ((0, BF, 65536, 2304), (256, 2, 1, 512)),   # LayerNorm 257-384 accesses: 256 x 2
+        ((0, F16, 65536, 3072), (256, 2, 1, 512)),
+        ((0, BF, 65536, 3584), (448, 1, 2, 256)),
+        ((0, BF, 16384, 4096), (512, 1, 2, 256)),   # the 4096-element plan is unchanged
+        ((0, F, 65536, 1536), (384, 1, 2, 256)),
+    ]
+    for (kind, dt, M, N), want in cases:
+        p = nl.norm_plan(kind, dt, 1, M, N, cu_count=256)
+        got = (p["threads"], p["accesses_per_thread"], p["rows_per_iter"], p["grid"])
+        assert got == want, (kind, dt, N, got)
+    # the residual form keeps the earlier plans
+    p = nl.norm_plan(1, BF, 1, 65536, 2560, residual=True, cu_count=256)
+    assert p["grid"] == 256
+    p = nl.norm_plan(0, BF, 1, 65536, 2560, residual=True, cu_count=256)
+    assert p["threads"] == 320
+    # overrides win over the rules
+    try:
+        nl.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, 1)
+        assert nl.norm_plan(1, BF, 1, 65536, 512, cu_count=256)["rows_per_iter"] == 1
+        assert nl.norm_plan(0, BF, 1, 65536, 2560, cu_count=256)["threads"] == 320
+    finally:
+        nl.norm_set_tuning(nl.TUNE_ROWS_PER_ITER, -1)
+
+
 def test_access_width_follows_row_length_and_alignment():
     def width(dt, N, align=16, pass_=0):
         p = nl.norm_plan(0, dt, pass_, 64, N, align=align)

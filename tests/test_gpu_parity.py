@@ -608,6 +608,22 @@ def test_phase_class_four_row_backward(kind, dt, N):
         run_and_check(_small(kind, dt, M, N, seed=M + N + 1), stats=False)
 
 
+@pytest.mark.parametrize("kind,dt,N", [("rmsnorm", "bf16", 256), ("layernorm", "bf16", 512),
+                                       ("rmsnorm", "f16", 512), ("rmsnorm", "bf16", 1280),
+                                       ("layernorm", "bf16", 1536), ("rmsnorm", "bf16", 2560),
+                                       ("rmsnorm", "f16", 3072), ("layernorm", "bf16", 2304),
+                                       ("layernorm", "f16", 2560), ("layernorm", "bf16", 3072)])
+def test_backward_team_rules(kind, dt, N):
+    """The default backward plans of 16-bit rows of up to 3072 elements (several rows per
+    wavefront, three or two workgroups per CU, 256-thread LayerNorm teams of two accesses):
+    ragged row counts from one to several row groups per workgroup, with and without saved
+    statistics, every row and every dW/dB column against the oracle."""
+    for M in (1, 7, 1003, 4099):
+        _say("backward team rules %s %s %dx%d" % (kind, dt, M, N))
+        run_and_check(_small(kind, dt, M, N, seed=M + N))
+        run_and_check(_small(kind, dt, M, N, seed=M + N + 1), stats=False)
+
+
 # ---- tuning knobs ----------------------------------------------------------------------------
 
 KNOBS = [
