@@ -309,9 +309,10 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // row against four / two: RMSNorm 65536 x 256 43.4 -> 28.9 us, 65536 x 512 50.0 -> 40.2,
     // 262144 x 512 177.8 -> 139.2, fp16 65536 x 512 49.3 -> 40.6; LayerNorm 65536 x 256 37.1 ->
     // 35.7, 65536 x 512 44.2 -> 42.0, 262144 x 512 147.9 -> 140.4). Two accesses per lane
-    // (768, 1024) gain nothing from more rows and lose 10-40% with four.
+    // (768, 1024) gain nothing from more rows and lose 10-40% with four. fp32 rows of at most
+    // 256 elements alike (65536 rows: RMSNorm 48.6 -> 39.6 us, LayerNorm 43.4 -> 39.9).
     if (t.rows <= 0 && bwd && vpt == 1 && sc == 1 && !p.period && !residual &&
-        (dtype == NORM_BF16 || dtype == NORM_F16))
+        (dtype == NORM_BF16 || dtype == NORM_F16 || dtype == NORM_F32))
       rows = kind == NORM_RMSNORM ? 4 : 2;
     if (!wave_menu(wc, vpt, rows)) rows = 1;
     p.vpt = vpt * sc;
@@ -467,11 +468,18 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // 119.8 -> 98.8 us, LayerNorm 126.6 -> 106.8; 1536 RMSNorm 127.1 -> 108.4, LayerNorm
       // 131.3 -> 117.8, fp16 RMSNorm 126.5 -> 109.1; RMSNorm 2560 219.6 -> 168.1, 3072 230.5 ->
       // 203.5; at 16384 rows 5-20% alike). RMSNorm on 448 threads (3584) loses 0-8% with two,
-      // and LayerNorm on 320-384 threads loses 4-5% (it takes 256-thread teams instead).
-      const bool up = bwd && vpt == 1 && rows == 2 && sc == 1 && !p.period && !residual &&
-                      (dtype == NORM_BF16 || dtype == NORM_F16) && p.threads == p.team_threads &&
-                      (p.threads == 192 ||
-                       (kind == NORM_RMSNORM && p.threads >= 320 && p.threads <= 384));
+      // and LayerNorm on 320-384 threads loses 4-5% (it takes 256-thread teams instead). fp32
+      // rows: RMSNorm on 320-384 threads gains too (65536 x 1280 202.3 -> 166.6, x 1536 216.6
+      // -> 210.1), LayerNorm on 320 threads (1280: 192.9 -> 170.3) but not on 384 (1536: 196.6
+      // against 218.7).
+      const bool d16 = dtype == NORM_BF16 || dtype == NORM_F16;
+      const bool up =
+          bwd && vpt == 1 && rows == 2 && sc == 1 && !p.period && !residual &&
+          p.threads == p.team_threads &&
+          ((d16 && p.threads == 192) ||
+           ((d16 || dtype == NORM_F32) && kind == NORM_RMSNORM && p.threads >= 320 &&
+            p.threads <= 384) ||
+           (dtype == NORM_F32 && kind == NORM_LAYERNORM && p.threads == 320));
       if (up) gpc = cdiv(1024, load);
       p.grid = capped(t.grid_per_cu > 0 ? t.grid_per_cu : gpc);
     } else if (t.grid_per_cu > 0 || stats || sc > 1 || p.period || wide_fwd) {

@@ -334,7 +334,11 @@ def test_backward_team_rules():
         ((0, F16, 65536, 3072), (256, 2, 1, 512)),
         ((0, BF, 65536, 3584), (448, 1, 2, 256)),
         ((0, BF, 16384, 4096), (512, 1, 2, 256)),   # the 4096-element plan is unchanged
-        ((0, F, 65536, 1536), (384, 1, 2, 256)),
+        ((0, F, 65536, 1536), (384, 1, 2, 256)),   # fp32 LayerNorm on 384 threads: one per CU
+        ((1, F, 65536, 256), (256, 1, 4, 512)),     # fp32 wave, one access
+        ((0, F, 65536, 256), (256, 1, 2, 512)),
+        ((1, F, 65536, 1536), (384, 1, 2, 512)),    # fp32 RMSNorm 320-384 threads: two per CU
+        ((0, F, 65536, 1280), (320, 1, 2, 512)),    # fp32 LayerNorm 320 threads: two per CU
     ]
     for (kind, dt, M, N), want in cases:
         p = nl.norm_plan(kind, dt, 1, M, N, cu_count=256)

@@ -612,10 +612,12 @@ def test_phase_class_four_row_backward(kind, dt, N):
                                        ("rmsnorm", "f16", 512), ("rmsnorm", "bf16", 1280),
                                        ("layernorm", "bf16", 1536), ("rmsnorm", "bf16", 2560),
                                        ("rmsnorm", "f16", 3072), ("layernorm", "bf16", 2304),
-                                       ("layernorm", "f16", 2560), ("layernorm", "bf16", 3072)])
+                                       ("layernorm", "f16", 2560), ("layernorm", "bf16", 3072),
+                                       ("rmsnorm", "f32", 256), ("layernorm", "f32", 1280),
+                                       ("rmsnorm", "f32", 1536)])
 def test_backward_team_rules(kind, dt, N):
-    """The default backward plans of 16-bit rows of up to 3072 elements (several rows per
-    wavefront, three or two workgroups per CU, 256-thread LayerNorm teams of two accesses):
+    """The default backward plans of rows of up to 3072 elements (several rows per wavefront,
+    three or two workgroups per CU, 256-thread LayerNorm teams of two accesses):
     ragged row counts from one to several row groups per workgroup, with and without saved
     statistics, every row and every dW/dB column against the oracle."""
     for M in (1, 7, 1003, 4099):
