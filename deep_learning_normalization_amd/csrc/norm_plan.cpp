@@ -310,9 +310,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // 262144 x 512 177.8 -> 139.2, fp16 65536 x 512 49.3 -> 40.6; LayerNorm 65536 x 256 37.1 ->
     // 35.7, 65536 x 512 44.2 -> 42.0, 262144 x 512 147.9 -> 140.4). Two accesses per lane
     // (768, 1024) gain nothing from more rows and lose 10-40% with four. fp32 rows of at most
-    // 256 elements alike (65536 rows: RMSNorm 48.6 -> 39.6 us, LayerNorm 43.4 -> 39.9).
-    if (t.rows <= 0 && bwd && vpt == 1 && sc == 1 && !p.period && !residual &&
-        (dtype == NORM_BF16 || dtype == NORM_F16 || dtype == NORM_F32))
+    // 256 elements alike (65536 rows: RMSNorm 48.6 -> 39.6 us, LayerNorm 43.4 -> 39.9), and
+    // fp32 weights beside bf16 rows (RMSNorm 65536 x 512 51.1 -> 40.7).
+    if (t.rows <= 0 && bwd && vpt == 1 && sc == 1 && !p.period && !residual)
       rows = kind == NORM_RMSNORM ? 4 : 2;
     if (!wave_menu(wc, vpt, rows)) rows = 1;
     p.vpt = vpt * sc;
@@ -420,9 +420,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // teams with two accesses each and one row, two workgroups per CU, instead of 320-384
     // threads with one access and two rows on one (measured on MI355X, bf16, 65536 rows: 2304
     // 224.0 -> 187.6 us, 2560 228.7 -> 186.5, 2816 225.4 -> 193.6, 3072 230.6 -> 204.6; fp16
-    // 2560 234.7 -> 208.1; 16384 rows 4-7%)
+    // 2560 234.7 -> 208.1; fp32 weights 2560 226.3 -> 181.6; 16384 rows 4-10%)
     if (bwd && kind == NORM_LAYERNORM && !residual && vec && wc == kFull && !p.period &&
-        (dtype == NORM_BF16 || dtype == NORM_F16) && nacc > 256 && nacc <= 384 &&
+        dtype != NORM_F32 && nacc > 256 && nacc <= 384 &&
         t.team_threads <= 0 && t.rows <= 0 && block_menu(wc, bwd, 2, 1, 256, sc, false) &&
         block_fits_registers(wc, bwd, 2, 1, 256)) {
       vpt = 2;
@@ -471,8 +471,9 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
       // and LayerNorm on 320-384 threads loses 4-5% (it takes 256-thread teams instead). fp32
       // rows: RMSNorm on 320-384 threads gains too (65536 x 1280 202.3 -> 166.6, x 1536 216.6
       // -> 210.1), LayerNorm on 320 threads (1280: 192.9 -> 170.3) but not on 384 (1536: 196.6
-      // against 218.7).
-      const bool d16 = dtype == NORM_BF16 || dtype == NORM_F16;
+      // against 218.7). fp32 weights beside 16-bit rows follow the 16-bit rows (65536 rows,
+      // RMSNorm 1536 126.1 -> 109.5, 2560 218.0 -> 168.2; LayerNorm 1536 135.0 -> 115.1).
+      const bool d16 = dtype != NORM_F32;
       const bool up =
           bwd && vpt == 1 && rows == 2 && sc == 1 && !p.period && !residual &&
           p.threads == p.team_threads &&

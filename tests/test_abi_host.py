@@ -339,6 +339,10 @@ def test_backward_team_rules():
         ((0, F, 65536, 256), (256, 1, 2, 512)),
         ((1, F, 65536, 1536), (384, 1, 2, 512)),    # fp32 RMSNorm 320-384 threads: two per CU
         ((0, F, 65536, 1280), (320, 1, 2, 512)),    # fp32 LayerNorm 320 threads: two per CU
+        ((1, BF32W, 65536, 512), (256, 1, 4, 512)),  # fp32 weights follow the 16-bit rows
+        ((0, BF32W, 65536, 1536), (192, 1, 2, 768)),
+        ((1, BF32W, 65536, 2560), (320, 1, 2, 512)),
+        ((0, BF32W, 65536, 2560), (256, 2, 1, 512)),
     ]
     for (kind, dt, M, N), want in cases:
         p = nl.norm_plan(kind, dt, 1, M, N, cu_count=256)

@@ -614,16 +614,22 @@ def test_phase_class_four_row_backward(kind, dt, N):
                                        ("rmsnorm", "f16", 3072), ("layernorm", "bf16", 2304),
                                        ("layernorm", "f16", 2560), ("layernorm", "bf16", 3072),
                                        ("rmsnorm", "f32", 256), ("layernorm", "f32", 1280),
-                                       ("rmsnorm", "f32", 1536)])
+                                       ("rmsnorm", "f32", 1536), ("rmsnorm", "bf16_f32w", 512),
+                                       ("layernorm", "bf16_f32w", 1536),
+                                       ("layernorm", "bf16_f32w", 2560)])
 def test_backward_team_rules(kind, dt, N):
     """The default backward plans of rows of up to 3072 elements (several rows per wavefront,
     three or two workgroups per CU, 256-thread LayerNorm teams of two accesses):
     ragged row counts from one to several row groups per workgroup, with and without saved
     statistics, every row and every dW/dB column against the oracle."""
+    wdt = None
+    if dt == "bf16_f32w":
+        dt, wdt = "bf16", "f32"
     for M in (1, 7, 1003, 4099):
-        _say("backward team rules %s %s %dx%d" % (kind, dt, M, N))
-        run_and_check(_small(kind, dt, M, N, seed=M + N))
-        run_and_check(_small(kind, dt, M, N, seed=M + N + 1), stats=False)
+        _say("backward team rules %s %s/%s %dx%d" % (kind, dt, wdt, M, N))
+        run_and_check(dataclasses.replace(_small(kind, dt, M, N, seed=M + N), wdtype=wdt))
+        run_and_check(dataclasses.replace(_small(kind, dt, M, N, seed=M + N + 1), wdtype=wdt),
+                      stats=False)
 
 
 # ---- tuning knobs ----------------------------------------------------------------------------
