@@ -14,6 +14,8 @@
 // matsubara.tec.br): para. 5 -- reductions whose dimension is too large to hold on chip loop over
 // it; para. 7 -- the backward's gradients dX, dW, dB; paras. 8-10 -- dX and per-block partial
 // column sums from one fused pass, consolidated by a second pass over the partials.
+#include <type_traits>
+
 #include "norm_device.hpp"
 #include "norm_internal.hpp"
 
@@ -24,12 +26,20 @@ namespace dln {
 // which then holds the whole row in registers across the team sum.
 __device__ __forceinline__ void reload_barrier() { asm volatile("" ::: "memory"); }
 
-template <typename T, typename TW, int EV, int SEG, int LB, bool LN>
-__global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
+// DBL: the dB sums live in LDS instead of registers (each thread owns its own columns there, so
+// no barrier guards them), which takes the four-segment LayerNorm kernel of 16-bit rows from 158
+// to at most 128 VGPRs: two workgroups per CU (the bound's second argument is the wavefronts
+// per SIMD it must leave room for).
+template <typename T, typename TW, int EV, int SEG, int LB, bool LN, bool DBL = false>
+__global__ __launch_bounds__(LB, DBL ? LB / 128 : 1) void looped_bwd_kernel(BwdArgs a) {
   using A = Acc<T, EV>;
   constexpr int E = A::EPV;
   constexpr int MAXW = LB / 64;
+  static_assert(!DBL || (LN && E % 4 == 0), "dB in LDS: LayerNorm, whole float4 groups");
+  constexpr int E4 = E / 4 > 0 ? E / 4 : 1;
   __shared__ __align__(16) float red[RED_FLOATS];
+  // dB sums: elements 4h .. 4h + 3 of segment s of thread t at sdb[s * E4 + h][t]
+  __shared__ __align__(16) float4 sdb[DBL ? SEG * E4 : 1][DBL ? LB : 1];
   const int t = threadIdx.x;
   const int tt = blockDim.x;
   const int waves = tt >> 6, wave = t >> 6, lane = t & 63;
@@ -46,7 +56,7 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
   write_ws_header(a.header, a.partials, N);
 
   WAcc<T, TW, EV> rw[SEG];
-  float accw[SEG][E], accb[LN ? SEG : 1][E];
+  float accw[SEG][E], accb[(LN && !DBL) ? SEG : 1][E];
 #pragma unroll
   for (int s = 0; s < SEG; ++s) {
     const int v = t + s * tt;
@@ -56,7 +66,11 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       accw[s][e] = 0.0f;
-      if constexpr (LN) accb[s][e] = 0.0f;
+      if constexpr (LN && !DBL) accb[s][e] = 0.0f;
+    }
+    if constexpr (DBL) {
+#pragma unroll
+      for (int h = 0; h < E4; ++h) sdb[s * E4 + h][t] = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
     }
   }
 
@@ -179,7 +193,18 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
           const float xh = __builtin_fmaf(d, ra, nd);
           dx[e] = __builtin_fmaf(df[e] * wf[e], ra, __builtin_fmaf(xh, cB, cC));
           accw[s][e] = __builtin_fmaf(df[e], xh, accw[s][e]);
-          if constexpr (LN) accb[s][e] += df[e];
+          if constexpr (LN && !DBL) accb[s][e] += df[e];
+        }
+        if constexpr (DBL) {
+#pragma unroll
+          for (int h = 0; h < E4; ++h) {
+            float4 b = sdb[s * E4 + h][t];
+            b.x += df[4 * h];
+            b.y += df[4 * h + 1];
+            b.z += df[4 * h + 2];
+            b.w += df[4 * h + 3];
+            sdb[s * E4 + h][t] = b;
+          }
         }
         if (DH) {
           float hf[E];
@@ -204,7 +229,17 @@ __global__ __launch_bounds__(LB) void looped_bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int e = 0; e < E; ++e) {
         pw[(int64_t)v * E + e] = accw[s][e];
-        if constexpr (LN) pb[(int64_t)v * E + e] = accb[s][e];
+        if constexpr (LN && !DBL) pb[(int64_t)v * E + e] = accb[s][e];
+      }
+      if constexpr (DBL) {
+#pragma unroll
+        for (int h = 0; h < E4; ++h) {
+          const float4 b = sdb[s * E4 + h][t];
+          pb[(int64_t)v * E + 4 * h] = b.x;
+          pb[(int64_t)v * E + 4 * h + 1] = b.y;
+          pb[(int64_t)v * E + 4 * h + 2] = b.z;
+          pb[(int64_t)v * E + 4 * h + 3] = b.w;
+        }
       }
     }
   }
@@ -223,6 +258,8 @@ template <typename T, typename TW, int EV>
 norm_status_t looped_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   constexpr int SEG = 4 * (full_epv<T>() / EV);
   constexpr bool kHas3 = EV == full_epv<T>() && sizeof(T) == 2;
+  // bf16 LayerNorm with four full-width segments keeps its dB sums in LDS (fp16 would spill)
+  constexpr bool kDbl = EV == full_epv<T>() && std::is_same<T, bf16_bits>::value;
   const bool seg3 = kHas3 && a.layernorm && p.vpt == 3;
   if ((p.vpt != SEG && !seg3) || p.lb != kLoopedLB) return NORM_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
@@ -230,6 +267,12 @@ norm_status_t looped_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   if constexpr (kHas3) {
     if (seg3) {
       e = launch(looped_bwd_kernel<T, TW, EV, 3, kLoopedLB, true>, grid, block, s, a);
+      return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
+    }
+  }
+  if constexpr (kDbl) {
+    if (a.layernorm) {
+      e = launch(looped_bwd_kernel<T, TW, EV, SEG, kLoopedLB, true, true>, grid, block, s, a);
       return e == hipSuccess ? NORM_OK : NORM_ERR_HIP;
     }
   }

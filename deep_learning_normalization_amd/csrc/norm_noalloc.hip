@@ -21,7 +21,9 @@
 namespace dln {
 namespace {
 
-constexpr size_t kScratchBytes = (size_t)64 << 20;
+// 96 MiB: the looped LayerNorm backward of 16384-element bf16 rows (two workgroups per CU on up
+// to 256 CUs) needs 64 MiB of column partials plus the header
+constexpr size_t kScratchBytes = (size_t)96 << 20;
 constexpr int kMaxScratchDevices = 64;
 
 static __device__ __align__(256) unsigned char scratch[kScratchBytes];

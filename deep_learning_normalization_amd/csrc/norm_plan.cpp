@@ -550,8 +550,15 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // 237.8 -> 198.0, 12288 258.9 -> 229.9, 14336 313.4 -> 277.5 (fp16, fp32 weights and the
     // residual form alike); fp32 LayerNorm 4100 211.4 -> 175.0, 7168 313.3 -> 282.9; full 32 KB
     // rows tie (bf16 16384) or lose (fp32 8192 309.8 -> 321.6).
-    const bool two = sc == 1 && !p.period && (dtype == NORM_F32 || kind == NORM_RMSNORM || seg3) &&
-                     nacc <= kLoopTwoMaxAcc;
+    // LayerNorm on bf16 rows with four segments keeps its dB sums in LDS (127 VGPRs) and runs
+    // two per CU at every length (16384 rows, one against two: 12800 344.6 -> 277.6 us, 14336
+    // 353.3 -> 300.5, 16384 363.0 -> 350.5; fp32 weights alike; the LDS sums cost nothing at
+    // one per CU).
+    const bool dbl = kind == NORM_LAYERNORM && sc == 1 && !seg3 &&
+                     (dtype == NORM_BF16 || dtype == NORM_BF16_F32W);
+    const bool two = sc == 1 && !p.period &&
+                     (((dtype == NORM_F32 || kind == NORM_RMSNORM || seg3) &&
+                       nacc <= kLoopTwoMaxAcc) || dbl);
     const int64_t gpc = t.grid_per_cu > 0 ? t.grid_per_cu : two ? 2 : 1;
     p.grid = Mm < cu * gpc ? Mm : cu * gpc;
     p.row_order = 0;

@@ -173,9 +173,9 @@ norm_status_t norm_bwd(norm_kind_t kind, const void *X, const void *dY, const vo
  * norm_bwd without a caller workspace, for callers that cannot allocate device memory (code
  * under HIP graph capture, tight serving loops, harnesses that forbid allocation). Arguments,
  * results and errors are those of norm_bwd; the workspace is the library's own device array of
- * 64 MiB per device (zero-initialised data of the code object, held by every device the library
+ * 96 MiB per device (zero-initialised data of the code object, held by every device the library
  * runs on until the process ends), so the call allocates nothing and makes no allocating call.
- * A shape whose backward needs more than 64 MiB of workspace on the current device (see
+ * A shape whose backward needs more than 96 MiB of workspace on the current device (see
  * norm_workspace_size) returns NORM_ERR_WORKSPACE and launches nothing. Every call on a device
  * shares that array: calls that overlap in time on one device (different streams, or threads
  * without ordering between their calls) race on it and must be serialised by the caller. An
