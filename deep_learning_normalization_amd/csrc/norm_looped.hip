@@ -258,8 +258,9 @@ template <typename T, typename TW, int EV>
 norm_status_t looped_typed(const Plan &p, const BwdArgs &a, hipStream_t s) {
   constexpr int SEG = 4 * (full_epv<T>() / EV);
   constexpr bool kHas3 = EV == full_epv<T>() && sizeof(T) == 2;
-  // bf16 LayerNorm with four full-width segments keeps its dB sums in LDS (fp16 would spill)
-  constexpr bool kDbl = EV == full_epv<T>() && std::is_same<T, bf16_bits>::value;
+  // 16-bit LayerNorm with four full-width segments keeps its dB sums in LDS (the fp16 kernel
+  // spills 16 bytes per lane at the 128-VGPR bound, at no measured cost)
+  constexpr bool kDbl = EV == full_epv<T>() && sizeof(T) == 2;
   const bool seg3 = kHas3 && a.layernorm && p.vpt == 3;
   if ((p.vpt != SEG && !seg3) || p.lb != kLoopedLB) return NORM_ERR_UNSUPPORTED;
   const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);

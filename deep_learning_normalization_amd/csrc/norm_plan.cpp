@@ -550,12 +550,12 @@ norm_status_t make_plan(norm_kind_t kind, norm_dtype_t dtype, norm_pass_t pass, 
     // 237.8 -> 198.0, 12288 258.9 -> 229.9, 14336 313.4 -> 277.5 (fp16, fp32 weights and the
     // residual form alike); fp32 LayerNorm 4100 211.4 -> 175.0, 7168 313.3 -> 282.9; full 32 KB
     // rows tie (bf16 16384) or lose (fp32 8192 309.8 -> 321.6).
-    // LayerNorm on bf16 rows with four segments keeps its dB sums in LDS (127 VGPRs) and runs
-    // two per CU at every length (16384 rows, one against two: 12800 344.6 -> 277.6 us, 14336
-    // 353.3 -> 300.5, 16384 363.0 -> 350.5; fp32 weights alike; the LDS sums cost nothing at
-    // one per CU).
-    const bool dbl = kind == NORM_LAYERNORM && sc == 1 && !seg3 &&
-                     (dtype == NORM_BF16 || dtype == NORM_BF16_F32W);
+    // LayerNorm on 16-bit rows with four segments keeps its dB sums in LDS (127-128 VGPRs) and
+    // runs two per CU at every length (16384 rows, one against two: bf16 12800 344.6 -> 277.6
+    // us, 14336 353.3 -> 300.5, 16384 363.0 -> 350.5; fp16 12800 337.9 -> 272.2, 14336 347.7
+    // -> 295.5, 16384 370.8 -> 351.0; fp32 weights alike; the LDS sums cost nothing at one per
+    // CU).
+    const bool dbl = kind == NORM_LAYERNORM && sc == 1 && !seg3 && dtype != NORM_F32;
     const bool two = sc == 1 && !p.period &&
                      (((dtype == NORM_F32 || kind == NORM_RMSNORM || seg3) &&
                        nacc <= kLoopTwoMaxAcc) || dbl);

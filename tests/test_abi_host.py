@@ -285,17 +285,17 @@ def test_wide_row_grids():
         assert g(kind, dt, 0, 16384, N, residual=res)["grid"] == (16384 if res else 8192), (kind, N)
     # looped backward: two workgroups per CU for rows of at most 1792 16-byte accesses whose
     # kernel fits two 512-thread teams (RMSNorm on 16-bit rows, fp32 rows, and 16-bit LayerNorm
-    # rows of at most 1536 accesses through its three-segment kernel), for every bf16 LayerNorm
-    # row (its four-segment kernel keeps dB in LDS), one otherwise
+    # rows of at most 1536 accesses through its three-segment kernel), for every 16-bit
+    # LayerNorm row (its four-segment kernel keeps dB in LDS), one otherwise
     for kind, dt, N, seg in [(1, BF, 8200, 4), (1, BF, 14336, 4), (0, F, 4100, 4), (1, F, 7168, 4),
                              (0, BF, 8200, 3), (0, BF, 12288, 3), (0, F16, 10240, 3),
                              (0, BF32W, 10240, 3), (0, BF, 12296, 4), (0, BF, 16384, 4),
-                             (0, BF32W, 14336, 4)]:
+                             (0, BF32W, 14336, 4), (0, F16, 12296, 4), (0, F16, 16384, 4)]:
         p = g(kind, dt, 1, 16384, N)
         assert (p["scheme"], p["accesses_per_thread"], p["grid"]) == (nl.SCHEME_LOOP, seg, 512), \
             (kind, N)
-    for kind, dt, N, seg in [(1, BF, 16384, 4), (0, F16, 12296, 4), (0, F16, 16384, 4),
-                             (0, F, 8192, 4), (1, BF, 16380, 8), (0, BF, 16380, 8)]:
+    for kind, dt, N, seg in [(1, BF, 16384, 4), (1, F16, 16384, 4), (0, F, 8192, 4),
+                             (1, BF, 16380, 8), (0, BF, 16380, 8)]:
         p = g(kind, dt, 1, 16384, N)
         assert (p["scheme"], p["accesses_per_thread"], p["grid"]) == (nl.SCHEME_LOOP, seg, 256), \
             (kind, N)

@@ -570,11 +570,12 @@ def test_wide_forward_persistent_grid(kind, N, res, dt):
                                                    ("layernorm", "bf16", 11264, False, "f32", 3),
                                                    ("layernorm", "bf16", 14336, False, None, 4),
                                                    ("layernorm", "bf16", 16384, True, None, 4),
-                                                   ("layernorm", "bf16", 12800, False, "f32", 4)])
+                                                   ("layernorm", "bf16", 12800, False, "f32", 4),
+                                                   ("layernorm", "f16", 14336, False, None, 4)])
 def test_looped_backward_two_per_cu(kind, dt, N, res, wdt, seg):
     """The default looped backward runs two workgroups per CU where its registers allow two
     512-thread teams and rows are at most 28 KB (LayerNorm on 16-bit rows of at most 1536
-    accesses through its three-segment kernel), and for every bf16 LayerNorm row (its
+    accesses through its three-segment kernel), and for every 16-bit LayerNorm row (its
     four-segment kernel keeps the dB sums in LDS): row counts below, at and past one row per
     workgroup, with and without saved statistics, every row and every dW/dB column against the
     oracle."""
